@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Decode throughput of the constant-shape decode step on one MI355X.
+
+Workload (default): the 8B-shaped bf16 decoder (32 layers, d_model 4096, 32 q / 8 kv heads of 128, SwiGLU 14336,
+vocab 128256, RoPE theta 5e5), batch 1, contiguous KV of capacity 8192 pre-filled with N(0,1) keys and values up to
+position 2048; greedy decode from position 2048 (warm-up steps first, then the timed steps, 512 in total by
+default). Weights are seeded N(0, 0.02) draws rounded to bf16; nothing is trained or downloaded.
+
+One step = write the slot buffers, one HIP-graph replay of every kernel of the step, copy the logits back, pick
+the greedy token on the host. `value` is decode tokens/s over the timed steps (rows x steps / wall time).
+
+Printed as one JSON line, with:
+  roofline      the dominant kernel's achieved HBM bandwidth (algorithmic bytes per launch / mean launch time,
+                HIP events on the engine's stream) against MI355X's 8 TB/s;
+  step          whole-step device time (HIP events around the replay) and bytes, kernels per step, host submit
+                time for the graph replay and for one-launch-per-kernel;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s + % HBM roofline, batch 1, 8B-shaped bf16, cap 8192"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w) -> float:
+    """Bytes one step must move: all weights streamed once (layers, final norm, head), the embedding rows read,
+    the whole [cap] K and V sweep of every layer and row, and the K/V write."""
+    m = w.model
+    wb = 2 if m.weight_dtype == "bf16" else 4
+    kvb = 2 if w.kv_dtype == "bf16" else 4
+    d, hd, F, L, V, R = m.d_model, m.head_dim, m.ffn_dim, m.n_layers, m.vocab, w.rows
+    per_layer = d * (m.n_q_heads + 2 * m.n_kv_heads) * hd + m.n_q_heads * hd * d + 3 * d * F + 2 * d
+    return (wb * (L * per_layer + V * d + d) + R * d * wb + L * R * 2 * w.cap * m.n_kv_heads * hd * kvb
+            + L * R * 2 * m.n_kv_heads * hd * kvb)
+
+
+def engine_for(w, ws, exec_mode):
+    from decode_step_03_amd import Engine, make_config
+    m = w.model
+    cfg = make_config(n_layers=m.n_layers, d_model=m.d_model, n_q_heads=m.n_q_heads, n_kv_heads=m.n_kv_heads,
+                      head_dim=m.head_dim, ffn_dim=m.ffn_dim, vocab=m.vocab, rms_eps=m.rms_eps,
+                      rope_theta=m.rope_theta, rows=w.rows, cap=w.cap, kv_layout=w.kv_layout,
+                      page_size=w.page_size, pool_pages=w.pool_pages, weight_dtype=m.weight_dtype,
+                      kv_dtype=w.kv_dtype, exec_mode=exec_mode)
+    eng = Engine(cfg, "cuda:0")
+    eng.load_weights(ws.layers, ws.glob)
+    return eng
+
+
+def prefill(eng, w, start_pos):
+    import synth
+    for r in range(w.rows):
+        n = int(start_pos[r])
+        if n == 0:
+            continue
+        for li in range(w.model.n_layers):
+            eng.write_kv(li, r, 0, synth.kv_prefill(w, li, r, "k", n), synth.kv_prefill(w, li, r, "v", n))
+
+
+def cpu_baseline(w, ws, start_pos, start_tok, budget_s: float) -> dict:
+    """The oracle as it is, on this host's cores, over a bounded sample of the workload (whole decode steps)."""
+    import oracle
+    import synth
+    model = oracle.OracleModel.from_weightset(ws)
+    cache = oracle.RowCache(model, int(start_pos[0]) + 64, w.kv_dtype)
+    for li in range(w.model.n_layers):
+        n = int(start_pos[0])
+        cache.set(li, 0, synth.kv_prefill(w, li, 0, "k", n), synth.kv_prefill(w, li, 0, "v", n))
+    tok, p = int(start_tok[0]), int(start_pos[0])
+    steps, t0 = 0, time.time()
+    while True:
+        logits = oracle.decode_step(model, cache, tok, p)
+        tok, p, steps = int(np.argmax(logits)), p + 1, steps + 1
+        if time.time() - t0 >= budget_s or steps >= 32:
+            break
+    dt = time.time() - t0
+    return {"value": steps * w.rows / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{steps} greedy decode step(s) of row 0 from position {int(start_pos[0])}, all "
+                      f"{w.model.n_layers} layers and the head, float64, weights widened per 256-row block",
+            "seconds": round(dt, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=504)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="llama8b-bf16-cap8192")
+    ap.add_argument("--profile-iters", type=int, default=10)
+    ap.add_argument("--eager-steps", type=int, default=16, help="steps of the one-launch-per-kernel comparison")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (the decode step runs on a single MI355X with no sharding); "
+              f"asked for --gpus {args.gpus} / WORLD_SIZE {world}", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synth
+    w = synth.workload(args.workload)
+    m = w.model
+    t0 = time.time()
+    ws = synth.make_weights(m)
+    log(f"weights drawn in {time.time() - t0:.1f}s ({m.n_params() / 1e9:.2f} B parameters)")
+    start_pos = synth.start_positions(w)
+    start_tok = synth.start_tokens(w)
+    if w.start == "prefill_tokens":
+        raise SystemExit("bench.py times decode; use a workload that starts from pre-filled K/V or position 0")
+
+    t0 = time.time()
+    eng = engine_for(w, ws, "graph")
+    prefill(eng, w, start_pos)
+    log(f"engine loaded and K/V pre-filled in {time.time() - t0:.1f}s")
+
+    pos = start_pos.copy()
+    tok = start_tok.copy()
+    total = args.warmup + args.steps
+    if int(pos.max()) + total > w.cap:
+        raise SystemExit("warmup + steps run past the KV capacity")
+    wall, gpu_us, submit_us = [], [], []
+    torch.cuda.synchronize()
+    for i in range(total):
+        if i == args.warmup:
+            torch.cuda.synchronize()
+            t_start = time.perf_counter()
+        ts = time.perf_counter()
+        logits, flags = eng.step(tok, pos)
+        tok = logits.argmax(axis=1).astype(np.int32)
+        pos = pos + 1
+        if i >= args.warmup:
+            wall.append(time.perf_counter() - ts)
+            st = eng.stats()
+            gpu_us.append(st["last_gpu_us"])
+            submit_us.append(st["last_submit_us"])
+        if flags:
+            log(f"warning: non-finite logits at step {i}")
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    stats = eng.stats()
+    tok_s = w.rows * args.steps / elapsed
+    step_bytes = algorithmic_bytes(w)
+    gpu_ms = float(np.median(gpu_us)) / 1e3
+    log(f"{tok_s:.1f} tok/s, wall {1e3 * elapsed / args.steps:.3f} ms/step, GPU {gpu_ms:.3f} ms/step, "
+        f"{step_bytes / gpu_ms / 1e6:.0f} GB/s")
+
+    kernels = eng.profile_kernels(args.profile_iters)
+    dom = max(kernels, key=lambda k: k["us_per_step"])
+    per_launch_bytes = dom["bytes_per_step"] / dom["launches"]
+    per_launch_us = dom["us_per_step"] / dom["launches"]
+    achieved = per_launch_bytes / per_launch_us / 1e3
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom["name"],
+                "bytes_per_launch": per_launch_bytes, "us_per_launch": round(per_launch_us, 3)}
+    eng.close()
+    del eng
+    torch.cuda.empty_cache()
+
+    eager = {}
+    if args.eager_steps > 0:
+        e2 = engine_for(w, ws, "eager")
+        prefill(e2, w, start_pos)
+        sub, wl = [], []
+        p2, t2 = start_pos.copy(), start_tok.copy()
+        for i in range(args.eager_steps + 2):
+            ts = time.perf_counter()
+            lg, _ = e2.step(t2, p2)
+            t2 = lg.argmax(axis=1).astype(np.int32)
+            p2 = p2 + 1
+            if i >= 2:
+                wl.append(time.perf_counter() - ts)
+                sub.append(e2.stats()["last_submit_us"])
+        eager = {"host_submit_us": round(float(np.median(sub)), 1), "wall_ms": round(1e3 * float(np.median(wl)), 3)}
+        e2.close()
+        del e2
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, ws, start_pos, start_tok, args.cpu_baseline_seconds)
+        log(f"cpu oracle {cpu['value']:.4f} tok/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": m.weight_dtype,
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) K/V prefill, greedy tokens)",
+        "config": {"workload": w.name, "rows": w.rows, "layers": m.n_layers, "d_model": m.d_model,
+                   "heads": f"{m.n_q_heads}q/{m.n_kv_heads}kv x {m.head_dim}", "ffn": m.ffn_dim,
+                   "vocab": m.vocab, "cap": w.cap, "kv": f"{w.kv_layout} {w.kv_dtype}",
+                   "start_pos": int(start_pos[0])},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "step": {"bytes": step_bytes, "gpu_ms": round(gpu_ms, 4),
+                 "hbm_gbs": round(step_bytes / gpu_ms / 1e6, 1),
+                 "hbm_frac": round(step_bytes / gpu_ms / 1e6 / HBM_PEAK_GBS, 4),
+                 "wall_ms_p10_p50_p90": [round(1e3 * float(np.percentile(wall, q)), 4) for q in (10, 50, 90)],
+                 "kernels_per_step": stats["kernels_per_step"], "graph_replays_per_step": 1,
+                 "host_submit_us_graph": round(float(np.median(submit_us)), 1),
+                 "eager": eager, "attn_splits": stats["attn_splits"]},
+        "kernels": [{"name": k["name"], "launches": k["launches"], "us_per_step": round(k["us_per_step"], 2),
+                     "gbs": round(k["bytes_per_step"] / k["us_per_step"] / 1e3, 1) if k["us_per_step"] else None}
+                    for k in kernels],
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,914 @@
+// Host side of the decode-step library: configuration checks, buffer plan, weight packing, slot buffers,
+// HIP-graph capture and replay, bounded waits and the engine's error state machine. See include/ds3.h.
+#include "ds3.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "ds3_kernels.h"
+
+using namespace ds3;
+
+namespace {
+
+enum EngineState { ST_READY = 0, ST_NOT_LOADED = 1, ST_NEEDS_RESET = 2, ST_POISONED = 3 };
+constexpr uint32_t kDefaultTimeoutMs = 600000;  // "Execution" page, section "Failure handling": 600 s default
+constexpr size_t kAlign = 256;
+
+thread_local std::string g_last_error;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+size_t dtype_bytes(int dt) { return dt == DS3_BF16 ? 2 : 4; }
+
+struct WorkPlan {
+  size_t slots, status, x, q, attn, act, part, counters, rope, slot_map, total;
+};
+
+struct KernelKind {
+  const char* name;
+};
+enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN, K_HEAD, K_NUM };
+const char* kKindNames[K_NUM] = {"embed", "qkv_rope_kvwrite", "attention_splitk", "o_proj_residual",
+                                 "gateup_swiglu", "down_proj_residual", "lm_head"};
+
+struct Launch {
+  int kind;
+  int layer;
+};
+
+}  // namespace
+
+struct ds3_engine {
+  ds3_config cfg{};
+  void* buf[DS3_NUM_BUFFERS]{};
+  hipStream_t stream = nullptr;
+  bool own_stream = false;
+  int device = 0;
+
+  // work buffer views
+  int* slots = nullptr;
+  StatusWords* status = nullptr;
+  float *x = nullptr, *q = nullptr, *attn = nullptr, *act = nullptr, *part = nullptr, *rope = nullptr;
+  unsigned* counters = nullptr;
+  int* slot_map = nullptr;
+  float* logits = nullptr;
+  size_t work_bytes = 0;
+
+  // weights
+  struct LayerW {
+    float* attn_norm;
+    void* wqkv;
+    void* wo;
+    float* ffn_norm;
+    void* wgu;
+    void* wd;
+  };
+  std::vector<LayerW> L;
+  void* embed = nullptr;
+  float* final_norm = nullptr;
+  void* lm_head = nullptr;
+
+  KvView kv{};
+  size_t kv_bytes = 0;
+  int splits = 1, split_len = 1;
+  int blocks[K_NUM]{};
+
+  // host state
+  int32_t* h_slots = nullptr;   // pinned: slot words followed by the two status words (zeroed every step)
+  StatusWords* h_status = nullptr;
+  std::vector<int32_t> h_slot_map;
+  bool slot_map_set = false;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  bool captured = false;
+  int graph_nodes = 0;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr, ev_done = nullptr;
+  bool pending = false;   // work was enqueued that may still be running (after a timeout)
+  int state = ST_NOT_LOADED;
+  bool inject_check = false;
+  bool inject_timeout = false;
+  ds3_stats stats{};
+  std::string err;
+  void* kv_staging = nullptr;
+  size_t kv_staging_bytes = 0;
+  std::vector<Launch> sequence;
+};
+
+namespace {
+
+ds3_status fail(ds3_engine* e, ds3_status st, const std::string& msg) {
+  if (e) e->err = msg;
+  else g_last_error = msg;
+  return st;
+}
+
+ds3_status poison(ds3_engine* e, ds3_status st, const std::string& msg) {
+  e->state = ST_POISONED;
+  return fail(e, st, msg);
+}
+
+#define HIP_OR_POISON(e, call)                                                                          \
+  do {                                                                                                  \
+    hipError_t _h = (call);                                                                             \
+    if (_h != hipSuccess)                                                                               \
+      return poison((e), DS3_E_DEVICE_LOST, std::string(#call) + ": " + hipGetErrorString(_h));         \
+  } while (0)
+
+std::string check_config(const ds3_config* c) {
+  if (!c) return "config is NULL";
+  if (c->abi_version != DS3_ABI_VERSION) return "abi_version mismatch";
+  if (c->n_layers < 1) return "n_layers must be >= 1";
+  if (c->d_model < 8 || c->d_model % 8) return "d_model must be a positive multiple of 8";
+  if (c->head_dim != 64 && c->head_dim != 128) return "head_dim must be 64 or 128";
+  if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads) return "n_q_heads must be a multiple of n_kv_heads";
+  {
+    const int G = c->n_q_heads / c->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return "n_q_heads / n_kv_heads must be 1, 2, 4 or 8";
+  }
+  if (c->ffn_dim < 8 || c->ffn_dim % 8) return "ffn_dim must be a positive multiple of 8";
+  if (c->vocab < 2 || c->vocab % 2) return "vocab must be even and >= 2";
+  if (!(c->rms_eps >= 0.f)) return "rms_eps must be >= 0";
+  if (!(c->rope_theta > 1.0)) return "rope_theta must be > 1";
+  if (c->rows < 1 || c->rows > kMaxGemvRows) return "rows must be in 1..4";
+  if (c->cap < 1) return "cap must be >= 1";
+  if (c->weight_dtype != DS3_F32 && c->weight_dtype != DS3_BF16) return "weight_dtype must be DS3_F32 or DS3_BF16";
+  if (c->kv_dtype != DS3_F32 && c->kv_dtype != DS3_BF16) return "kv_dtype must be DS3_F32 or DS3_BF16";
+  if (c->exec_mode != DS3_GRAPH && c->exec_mode != DS3_EAGER) return "exec_mode must be DS3_GRAPH or DS3_EAGER";
+  if (c->kv_layout == DS3_KV_PAGED) {
+    if (c->page_size < 1) return "page_size must be >= 1";
+    if (c->cap % c->page_size) return "cap must be a multiple of page_size";
+    if (c->pool_pages < 1) return "pool_pages must be >= 1";
+    if ((int64_t)c->pool_pages * c->page_size > INT32_MAX) return "pool_pages * page_size must fit int32";
+  } else if (c->kv_layout != DS3_KV_CONTIGUOUS) {
+    return "kv_layout must be DS3_KV_CONTIGUOUS or DS3_KV_PAGED";
+  }
+  const int kmax = std::max(std::max(c->d_model, c->ffn_dim), c->n_q_heads * c->head_dim);
+  if (gemv_lds_bytes(c->rows, kmax) > 160 * 1024) return "rows * max(d_model, ffn_dim, q width) * 4 exceeds 160 KB LDS";
+  return "";
+}
+
+// attention split plan: ~2 blocks per CU, each split a multiple of the positions one block pass covers
+void plan_splits(const ds3_config& c, int* splits, int* split_len) {
+  const int ppp = attn_positions_per_pass(c.head_dim, c.kv_dtype);
+  const int units = (c.cap + ppp - 1) / ppp;         // passes over the whole capacity
+  const int target_blocks = 512;
+  int s = std::max(1, target_blocks / (c.rows * c.n_kv_heads));
+  s = std::min(s, units);
+  int per = (units + s - 1) / s;                     // passes per split
+  int len = per * ppp;
+  // keep the LDS of one block small (scores for G heads)
+  const int G = c.n_q_heads / c.n_kv_heads;
+  while ((size_t)G * len * 4 > 64 * 1024 && per > 1) {
+    --per;
+    len = per * ppp;
+  }
+  *split_len = len;
+  *splits = (c.cap + len - 1) / len;
+}
+
+WorkPlan plan_work(const ds3_config& c, int splits) {
+  WorkPlan w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + bytes, kAlign);
+    return at;
+  };
+  const SlotLayout sl{c.rows};
+  const int G = c.n_q_heads / c.n_kv_heads;
+  w.slots = take((size_t)sl.words() * 4);
+  w.status = take(sizeof(StatusWords));
+  w.x = take((size_t)c.rows * c.d_model * 4);
+  w.q = take((size_t)c.rows * c.n_q_heads * c.head_dim * 4);
+  w.attn = take((size_t)c.rows * c.n_q_heads * c.head_dim * 4);
+  w.act = take((size_t)c.rows * c.ffn_dim * 4);
+  w.part = take((size_t)c.rows * c.n_kv_heads * splits * G * (c.head_dim + 2) * 4);
+  w.counters = take((size_t)c.rows * c.n_kv_heads * 4);
+  w.rope = take((size_t)c.cap * (c.head_dim / 2) * 2 * 4);
+  w.slot_map = take(c.kv_layout == DS3_KV_PAGED ? (size_t)c.rows * (c.cap / c.page_size) * 4 : 4);
+  w.total = off;
+  return w;
+}
+
+size_t kv_state_bytes(const ds3_config& c) {
+  const size_t per_layer = c.kv_layout == DS3_KV_PAGED
+                               ? (size_t)c.pool_pages * c.n_kv_heads * c.page_size * c.head_dim
+                               : (size_t)c.rows * c.n_kv_heads * c.cap * c.head_dim;
+  return 2 * (size_t)c.n_layers * per_layer * dtype_bytes(c.kv_dtype);
+}
+
+struct WeightPlan {
+  struct L {
+    size_t attn_norm, wqkv, wo, ffn_norm, wgu, wd;
+  };
+  std::vector<L> layers;
+  size_t embed, final_norm, lm_head, total;
+};
+
+WeightPlan plan_weights(const ds3_config& c) {
+  WeightPlan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + bytes, kAlign);
+    return at;
+  };
+  const size_t wb = dtype_bytes(c.weight_dtype);
+  const size_t d = c.d_model, F = c.ffn_dim, qw = (size_t)c.n_q_heads * c.head_dim,
+               kvw = (size_t)c.n_kv_heads * c.head_dim;
+  for (int l = 0; l < c.n_layers; ++l) {
+    WeightPlan::L L;
+    L.attn_norm = take(d * 4);
+    L.wqkv = take((qw + 2 * kvw) * d * wb);
+    L.wo = take(d * qw * wb);
+    L.ffn_norm = take(d * 4);
+    L.wgu = take(2 * F * d * wb);
+    L.wd = take(d * F * wb);
+    p.layers.push_back(L);
+  }
+  p.embed = take((size_t)c.vocab * d * wb);
+  p.final_norm = take(d * 4);
+  p.lm_head = take((size_t)c.vocab * d * wb);
+  p.total = off;
+  return p;
+}
+
+// bytes a kind of kernel moves per step by the algorithm's count (streamed weights, swept and written K/V)
+double kind_bytes(const ds3_config& c, int kind) {
+  const double wb = (double)dtype_bytes(c.weight_dtype), kvb = (double)dtype_bytes(c.kv_dtype);
+  const double d = c.d_model, F = c.ffn_dim, qw = (double)c.n_q_heads * c.head_dim,
+               kvw = (double)c.n_kv_heads * c.head_dim, Lc = c.n_layers, R = c.rows;
+  switch (kind) {
+    case K_EMBED: return R * d * wb;
+    case K_QKV: return Lc * ((qw + 2 * kvw) * d * wb + d * wb + R * 2 * kvw * kvb);
+    case K_ATTN: return Lc * R * 2 * (double)c.cap * kvw * kvb;
+    case K_OPROJ: return Lc * d * qw * wb;
+    case K_GATEUP: return Lc * (2 * F * d * wb + d * wb);
+    case K_DOWN: return Lc * d * F * wb;
+    case K_HEAD: return (double)c.vocab * d * wb + d * wb;
+  }
+  return 0;
+}
+
+int gemv_blocks(int n_pairs, int max_blocks) {
+  const int waves = 4;
+  int b = (n_pairs + waves - 1) / waves;
+  return std::max(1, std::min(b, max_blocks));
+}
+
+ds3_status wait_done(ds3_engine* e, hipEvent_t ev, uint32_t timeout_ms) {
+  const auto t0 = std::chrono::steady_clock::now();
+  int spins = 0;
+  for (;;) {
+    hipError_t q = hipEventQuery(ev);
+    if (q == hipSuccess) {
+      e->pending = false;
+      return DS3_OK;
+    }
+    if (q != hipErrorNotReady) return poison(e, DS3_E_DEVICE_LOST, std::string("device wait: ") + hipGetErrorString(q));
+    const double ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    if (ms >= (double)timeout_ms)
+      return poison(e, DS3_E_TIMEOUT, "device wait exceeded " + std::to_string(timeout_ms) + " ms");
+    if (++spins > 2000) std::this_thread::sleep_for(std::chrono::microseconds(50));
+    else std::this_thread::yield();
+  }
+}
+
+hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
+  const ds3_config& c = e->cfg;
+  const int R = c.rows;
+  auto base = [&](GemvParams& p) {
+    p.rows = R;
+    p.eps = c.rms_eps;
+    p.nq = c.n_q_heads;
+    p.nkv = c.n_kv_heads;
+    p.hd = c.head_dim;
+    p.rope = e->rope;
+    p.kv = e->kv;
+    p.layer = l.layer;
+    p.slots = e->slots;
+    p.status = e->status;
+  };
+  switch (l.kind) {
+    case K_EMBED: {
+      EmbedParams p{e->embed, e->x, c.d_model, c.vocab, R, e->slots, e->status};
+      return launch_embed(p, c.weight_dtype, e->stream);
+    }
+    case K_QKV: {
+      GemvParams p{};
+      base(p);
+      const auto& W = e->L[l.layer];
+      p.w = W.wqkv;
+      p.in = e->x;
+      p.gain = W.attn_norm;
+      p.out = e->q;
+      p.K = c.d_model;
+      p.n_pairs = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim / 2;
+      return launch_gemv(p, GEMV_QKV, c.weight_dtype, c.kv_dtype, e->blocks[K_QKV], e->stream);
+    }
+    case K_ATTN: {
+      AttnParams p{};
+      p.q = e->q;
+      p.out = e->attn;
+      p.part = e->part;
+      p.counters = e->counters;
+      p.kv = e->kv;
+      p.layer = l.layer;
+      p.nq = c.n_q_heads;
+      p.nkv = c.n_kv_heads;
+      p.hd = c.head_dim;
+      p.splits = e->splits;
+      p.split_len = e->split_len;
+      p.scale = (float)(1.0 / std::sqrt((double)c.head_dim));
+      p.slots = e->slots;
+      p.status = e->status;
+      return launch_attention(p, c.kv_dtype, R, e->stream);
+    }
+    case K_OPROJ: {
+      GemvParams p{};
+      base(p);
+      p.w = e->L[l.layer].wo;
+      p.in = e->attn;
+      p.out = e->x;
+      p.K = c.n_q_heads * c.head_dim;
+      p.n_pairs = c.d_model / 2;
+      return launch_gemv(p, GEMV_RESID, c.weight_dtype, c.kv_dtype, e->blocks[K_OPROJ], e->stream);
+    }
+    case K_GATEUP: {
+      GemvParams p{};
+      base(p);
+      const auto& W = e->L[l.layer];
+      p.w = W.wgu;
+      p.in = e->x;
+      p.gain = W.ffn_norm;
+      p.out = e->act;
+      p.K = c.d_model;
+      p.n_pairs = c.ffn_dim;
+      p.up_offset = c.ffn_dim;
+      return launch_gemv(p, GEMV_GATEUP, c.weight_dtype, c.kv_dtype, e->blocks[K_GATEUP], e->stream);
+    }
+    case K_DOWN: {
+      GemvParams p{};
+      base(p);
+      p.w = e->L[l.layer].wd;
+      p.in = e->act;
+      p.out = e->x;
+      p.K = c.ffn_dim;
+      p.n_pairs = c.d_model / 2;
+      return launch_gemv(p, GEMV_RESID, c.weight_dtype, c.kv_dtype, e->blocks[K_DOWN], e->stream);
+    }
+    case K_HEAD: {
+      GemvParams p{};
+      base(p);
+      p.w = e->lm_head;
+      p.in = e->x;
+      p.gain = e->final_norm;
+      p.out = e->logits;
+      p.K = c.d_model;
+      p.n_pairs = c.vocab / 2;
+      return launch_gemv(p, GEMV_HEAD, c.weight_dtype, c.kv_dtype, e->blocks[K_HEAD], e->stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t enqueue_step(ds3_engine* e) {
+  for (const Launch& l : e->sequence) {
+    hipError_t h = enqueue_kernel(e, l);
+    if (h != hipSuccess) return h;
+  }
+  return hipSuccess;
+}
+
+ds3_status ensure_captured(ds3_engine* e) {
+  if (e->captured) return DS3_OK;
+  HIP_OR_POISON(e, hipStreamBeginCapture(e->stream, hipStreamCaptureModeThreadLocal));
+  hipError_t h = enqueue_step(e);
+  hipGraph_t g = nullptr;
+  hipError_t h2 = hipStreamEndCapture(e->stream, &g);
+  if (h != hipSuccess || h2 != hipSuccess) {
+    if (g) hipGraphDestroy(g);
+    return poison(e, DS3_E_DEVICE_LOST,
+                  std::string("graph capture: ") + hipGetErrorString(h != hipSuccess ? h : h2));
+  }
+  e->graph = g;
+  HIP_OR_POISON(e, hipGraphInstantiate(&e->exec, e->graph, nullptr, nullptr, 0));
+  size_t n = 0;
+  HIP_OR_POISON(e, hipGraphGetNodes(e->graph, nullptr, &n));
+  e->graph_nodes = (int)n;
+  e->captured = true;
+  e->stats.captures++;
+  return DS3_OK;
+}
+
+ds3_status refuse_if_unusable(ds3_engine* e) {
+  if (!e) return fail(nullptr, DS3_E_INVALID, "engine is NULL");
+  if (e->state == ST_POISONED) return fail(e, DS3_E_POISONED, "engine is poisoned: " + e->err);
+  return DS3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ds3_status ds3_query_buffers(const ds3_config* cfg, ds3_buffer_req* out, int32_t* n_inout) {
+  std::string why = check_config(cfg);
+  if (!why.empty()) return fail(nullptr, cfg ? DS3_E_UNSUPPORTED : DS3_E_INVALID, why);
+  if (!out || !n_inout || *n_inout < DS3_NUM_BUFFERS) return fail(nullptr, DS3_E_INVALID, "need room for 4 buffers");
+  int splits, split_len;
+  plan_splits(*cfg, &splits, &split_len);
+  const size_t sizes[DS3_NUM_BUFFERS] = {plan_weights(*cfg).total, kv_state_bytes(*cfg),
+                                         plan_work(*cfg, splits).total,
+                                         (size_t)cfg->rows * cfg->vocab * sizeof(float)};
+  const char* names[DS3_NUM_BUFFERS] = {"weights", "kv", "work", "logits"};
+  for (int i = 0; i < DS3_NUM_BUFFERS; ++i) {
+    out[i].id = i;
+    std::snprintf(out[i].name, sizeof(out[i].name), "%s", names[i]);
+    out[i].bytes = sizes[i];
+    out[i].align = kAlign;
+  }
+  *n_inout = DS3_NUM_BUFFERS;
+  return DS3_OK;
+}
+
+ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, void* hip_stream, ds3_engine** out) {
+  std::string why = check_config(cfg);
+  if (!why.empty()) return fail(nullptr, cfg ? DS3_E_UNSUPPORTED : DS3_E_INVALID, why);
+  if (!dev_ptrs || n != DS3_NUM_BUFFERS || !out) return fail(nullptr, DS3_E_INVALID, "need 4 device buffers and out");
+  for (int i = 0; i < DS3_NUM_BUFFERS; ++i)
+    if (!dev_ptrs[i] || (reinterpret_cast<uintptr_t>(dev_ptrs[i]) % kAlign))
+      return fail(nullptr, DS3_E_INVALID, "device buffer " + std::to_string(i) + " is NULL or not 256-byte aligned");
+  *out = nullptr;
+  ds3_engine* e = new ds3_engine();
+  e->cfg = *cfg;
+  if (e->cfg.timeout_ms == 0) e->cfg.timeout_ms = kDefaultTimeoutMs;
+  const ds3_config& c = e->cfg;
+  for (int i = 0; i < DS3_NUM_BUFFERS; ++i) e->buf[i] = dev_ptrs[i];
+  auto bail = [&](ds3_status st, const std::string& msg) {
+    g_last_error = msg;
+    ds3_destroy(e);
+    return st;
+  };
+  hipError_t h = hipGetDevice(&e->device);
+  if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("hipGetDevice: ") + hipGetErrorString(h));
+  if (hip_stream) {
+    e->stream = reinterpret_cast<hipStream_t>(hip_stream);
+  } else {
+    h = hipStreamCreateWithFlags(&e->stream, hipStreamNonBlocking);
+    if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("hipStreamCreate: ") + hipGetErrorString(h));
+    e->own_stream = true;
+  }
+  plan_splits(c, &e->splits, &e->split_len);
+  const WorkPlan wp = plan_work(c, e->splits);
+  char* work = reinterpret_cast<char*>(e->buf[DS3_BUF_WORK]);
+  e->slots = reinterpret_cast<int*>(work + wp.slots);
+  e->status = reinterpret_cast<StatusWords*>(work + wp.status);
+  e->x = reinterpret_cast<float*>(work + wp.x);
+  e->q = reinterpret_cast<float*>(work + wp.q);
+  e->attn = reinterpret_cast<float*>(work + wp.attn);
+  e->act = reinterpret_cast<float*>(work + wp.act);
+  e->part = reinterpret_cast<float*>(work + wp.part);
+  e->counters = reinterpret_cast<unsigned*>(work + wp.counters);
+  e->rope = reinterpret_cast<float*>(work + wp.rope);
+  e->slot_map = reinterpret_cast<int*>(work + wp.slot_map);
+  e->work_bytes = wp.total;
+  e->logits = reinterpret_cast<float*>(e->buf[DS3_BUF_LOGITS]);
+
+  const WeightPlan wpl = plan_weights(c);
+  char* wbase = reinterpret_cast<char*>(e->buf[DS3_BUF_WEIGHTS]);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const auto& P = wpl.layers[l];
+    e->L.push_back({reinterpret_cast<float*>(wbase + P.attn_norm), wbase + P.wqkv, wbase + P.wo,
+                    reinterpret_cast<float*>(wbase + P.ffn_norm), wbase + P.wgu, wbase + P.wd});
+  }
+  e->embed = wbase + wpl.embed;
+  e->final_norm = reinterpret_cast<float*>(wbase + wpl.final_norm);
+  e->lm_head = wbase + wpl.lm_head;
+
+  e->kv_bytes = kv_state_bytes(c);
+  const size_t kvb = dtype_bytes(c.kv_dtype);
+  e->kv.k = e->buf[DS3_BUF_KV];
+  e->kv.v = reinterpret_cast<char*>(e->buf[DS3_BUF_KV]) + e->kv_bytes / 2;
+  e->kv.layer_stride = (int64_t)(e->kv_bytes / 2 / kvb / c.n_layers);
+  e->kv.paged = c.kv_layout == DS3_KV_PAGED;
+  e->kv.cap = c.cap;
+  e->kv.page_size = e->kv.paged ? c.page_size : 1;
+  e->kv.pool_pages = e->kv.paged ? c.pool_pages : 0;
+  e->kv.slot_map = e->slot_map;
+
+  // launch shapes
+  const int max_blocks = 1024;
+  e->blocks[K_QKV] = gemv_blocks((c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim / 2, max_blocks);
+  e->blocks[K_OPROJ] = gemv_blocks(c.d_model / 2, max_blocks);
+  e->blocks[K_GATEUP] = gemv_blocks(c.ffn_dim, max_blocks);
+  e->blocks[K_DOWN] = gemv_blocks(c.d_model / 2, max_blocks);
+  e->blocks[K_HEAD] = gemv_blocks(c.vocab / 2, max_blocks);
+
+  e->sequence.push_back({K_EMBED, -1});
+  for (int l = 0; l < c.n_layers; ++l) {
+    e->sequence.push_back({K_QKV, l});
+    e->sequence.push_back({K_ATTN, l});
+    e->sequence.push_back({K_OPROJ, l});
+    e->sequence.push_back({K_GATEUP, l});
+    e->sequence.push_back({K_DOWN, l});
+  }
+  e->sequence.push_back({K_HEAD, -1});
+
+  const SlotLayout sl{c.rows};
+  h = hipHostMalloc(reinterpret_cast<void**>(&e->h_slots), (size_t)sl.words() * 4 + kAlign + sizeof(StatusWords),
+                    hipHostMallocDefault);
+  if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("hipHostMalloc: ") + hipGetErrorString(h));
+  std::memset(e->h_slots, 0, (size_t)sl.words() * 4);
+  e->h_status = reinterpret_cast<StatusWords*>(reinterpret_cast<char*>(e->h_slots) + align_up((size_t)sl.words() * 4, 16));
+  for (hipEvent_t* ev : {&e->ev0, &e->ev1, &e->ev_done}) {
+    h = hipEventCreate(ev);
+    if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("hipEventCreate: ") + hipGetErrorString(h));
+  }
+
+  // rotary table: angle p * theta^(-2i/hd) in double, stored as float32 (cos, sin)
+  {
+    const int half = c.head_dim / 2;
+    std::vector<float> tab((size_t)c.cap * half * 2);
+    for (int p = 0; p < c.cap; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double ang = (double)p * std::pow(c.rope_theta, -2.0 * i / c.head_dim);
+        tab[((size_t)p * half + i) * 2] = (float)std::cos(ang);
+        tab[((size_t)p * half + i) * 2 + 1] = (float)std::sin(ang);
+      }
+    h = hipMemcpyAsync(e->rope, tab.data(), tab.size() * 4, hipMemcpyHostToDevice, e->stream);
+    if (h == hipSuccess) h = hipMemsetAsync(e->slots, 0, wp.rope, e->stream);  // slots .. counters
+    if (h == hipSuccess) h = hipMemsetAsync(e->buf[DS3_BUF_KV], 0, e->kv_bytes, e->stream);
+    if (h == hipSuccess) h = hipStreamSynchronize(e->stream);
+    if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("create upload: ") + hipGetErrorString(h));
+  }
+  e->state = ST_NOT_LOADED;
+  e->stats.attn_splits = e->splits;
+  e->stats.state = e->state;
+  *out = e;
+  return DS3_OK;
+}
+
+ds3_status ds3_load_weights(ds3_engine* e, const ds3_weight_src* w, int32_t n) {
+  if (ds3_status st = refuse_if_unusable(e)) return st;
+  if (!w || n < 0) return fail(e, DS3_E_INVALID, "weights array is NULL");
+  const ds3_config& c = e->cfg;
+  const int64_t d = c.d_model, F = c.ffn_dim, qw = (int64_t)c.n_q_heads * c.head_dim,
+                kvw = (int64_t)c.n_kv_heads * c.head_dim, V = c.vocab;
+  auto expect = [&](int role, int64_t* rows, int64_t* cols) {
+    switch (role) {
+      case DS3_W_EMBED: case DS3_W_LM_HEAD: *rows = V; *cols = d; return;
+      case DS3_W_ATTN_NORM: case DS3_W_FFN_NORM: case DS3_W_FINAL_NORM: *rows = 1; *cols = d; return;
+      case DS3_W_Q: *rows = qw; *cols = d; return;
+      case DS3_W_K: case DS3_W_V: *rows = kvw; *cols = d; return;
+      case DS3_W_O: *rows = d; *cols = qw; return;
+      case DS3_W_GATE: case DS3_W_UP: *rows = F; *cols = d; return;
+      case DS3_W_DOWN: *rows = d; *cols = F; return;
+    }
+  };
+  static const char* role_names[DS3_W_NUM_ROLES] = {"EMBED", "ATTN_NORM", "Q", "K", "V", "O", "FFN_NORM",
+                                                    "GATE", "UP", "DOWN", "FINAL_NORM", "LM_HEAD"};
+  auto is_global = [](int role) { return role == DS3_W_EMBED || role == DS3_W_FINAL_NORM || role == DS3_W_LM_HEAD; };
+  // validate everything before touching the device
+  std::vector<const ds3_weight_src*> slot((size_t)DS3_W_NUM_ROLES * (c.n_layers + 1), nullptr);
+  for (int i = 0; i < n; ++i) {
+    const ds3_weight_src& s = w[i];
+    if (s.role < 0 || s.role >= DS3_W_NUM_ROLES) return fail(e, DS3_E_INVALID, "unknown role " + std::to_string(s.role));
+    const bool glob = is_global(s.role);
+    if (glob ? s.layer != -1 : (s.layer < 0 || s.layer >= c.n_layers))
+      return fail(e, DS3_E_INVALID, std::string("bad layer for role ") + role_names[s.role]);
+    int64_t er, ec;
+    expect(s.role, &er, &ec);
+    const bool is_norm = s.role == DS3_W_ATTN_NORM || s.role == DS3_W_FFN_NORM || s.role == DS3_W_FINAL_NORM;
+    if (!(s.rows == er && s.cols == ec) && !(is_norm && s.rows * s.cols == ec))
+      return fail(e, DS3_E_INVALID, std::string("wrong shape for ") + role_names[s.role]);
+    if (s.dtype != c.weight_dtype) return fail(e, DS3_E_INVALID, std::string("wrong dtype for ") + role_names[s.role]);
+    if (!s.data) return fail(e, DS3_E_INVALID, std::string("NULL data for ") + role_names[s.role]);
+    const size_t k = (size_t)s.role * (c.n_layers + 1) + (glob ? c.n_layers : s.layer);
+    if (slot[k]) return fail(e, DS3_E_INVALID, std::string("duplicate ") + role_names[s.role]);
+    slot[k] = &s;
+  }
+  for (int role = 0; role < DS3_W_NUM_ROLES; ++role) {
+    if (is_global(role)) {
+      if (!slot[(size_t)role * (c.n_layers + 1) + c.n_layers])
+        return fail(e, DS3_E_UNBOUND, std::string("unbound weight ") + role_names[role]);
+    } else {
+      for (int l = 0; l < c.n_layers; ++l)
+        if (!slot[(size_t)role * (c.n_layers + 1) + l])
+          return fail(e, DS3_E_UNBOUND, std::string("unbound weight ") + role_names[role] + " of layer " + std::to_string(l));
+    }
+  }
+  const size_t wb = dtype_bytes(c.weight_dtype);
+  auto src = [&](int role, int layer) { return slot[(size_t)role * (c.n_layers + 1) + (layer < 0 ? c.n_layers : layer)]; };
+  auto copy = [&](void* dst, const ds3_weight_src* s, size_t bytes) -> hipError_t {
+    return hipMemcpyAsync(dst, s->data, bytes, hipMemcpyDefault, e->stream);
+  };
+  // norm gains are kept as float32 on the device (exact widening of bf16 words)
+  std::vector<std::vector<float>> gains;
+  auto gain = [&](float* dst, const ds3_weight_src* s) -> hipError_t {
+    std::vector<float> g((size_t)d);
+    hipPointerAttribute_t attr{};
+    const bool on_device = hipPointerGetAttributes(&attr, s->data) == hipSuccess && attr.type == hipMemoryTypeDevice;
+    (void)!hipGetLastError();
+    std::vector<uint8_t> host((size_t)d * wb);
+    if (on_device) {
+      hipError_t h = hipMemcpy(host.data(), s->data, host.size(), hipMemcpyDeviceToHost);
+      if (h != hipSuccess) return h;
+    } else {
+      std::memcpy(host.data(), s->data, host.size());
+    }
+    for (int64_t i = 0; i < d; ++i) {
+      if (c.weight_dtype == DS3_BF16) {
+        uint16_t word;
+        std::memcpy(&word, host.data() + i * 2, 2);
+        uint32_t u = (uint32_t)word << 16;
+        std::memcpy(&g[i], &u, 4);
+      } else {
+        std::memcpy(&g[i], host.data() + i * 4, 4);
+      }
+    }
+    gains.push_back(std::move(g));
+    return hipMemcpyAsync(dst, gains.back().data(), (size_t)d * 4, hipMemcpyHostToDevice, e->stream);
+  };
+  gains.reserve((size_t)2 * c.n_layers + 1);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const auto& W = e->L[l];
+    char* qkv = reinterpret_cast<char*>(W.wqkv);
+    char* gu = reinterpret_cast<char*>(W.wgu);
+    HIP_OR_POISON(e, gain(W.attn_norm, src(DS3_W_ATTN_NORM, l)));
+    HIP_OR_POISON(e, copy(qkv, src(DS3_W_Q, l), (size_t)qw * d * wb));
+    HIP_OR_POISON(e, copy(qkv + (size_t)qw * d * wb, src(DS3_W_K, l), (size_t)kvw * d * wb));
+    HIP_OR_POISON(e, copy(qkv + (size_t)(qw + kvw) * d * wb, src(DS3_W_V, l), (size_t)kvw * d * wb));
+    HIP_OR_POISON(e, copy(W.wo, src(DS3_W_O, l), (size_t)d * qw * wb));
+    HIP_OR_POISON(e, gain(W.ffn_norm, src(DS3_W_FFN_NORM, l)));
+    HIP_OR_POISON(e, copy(gu, src(DS3_W_GATE, l), (size_t)F * d * wb));
+    HIP_OR_POISON(e, copy(gu + (size_t)F * d * wb, src(DS3_W_UP, l), (size_t)F * d * wb));
+    HIP_OR_POISON(e, copy(W.wd, src(DS3_W_DOWN, l), (size_t)d * F * wb));
+  }
+  HIP_OR_POISON(e, copy(e->embed, src(DS3_W_EMBED, -1), (size_t)V * d * wb));
+  HIP_OR_POISON(e, gain(e->final_norm, src(DS3_W_FINAL_NORM, -1)));
+  HIP_OR_POISON(e, copy(e->lm_head, src(DS3_W_LM_HEAD, -1), (size_t)V * d * wb));
+  HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
+  e->pending = true;
+  if (ds3_status st = wait_done(e, e->ev_done, e->cfg.timeout_ms)) return st;
+  if (e->state == ST_NOT_LOADED) e->state = ST_READY;
+  e->stats.state = e->state;
+  return DS3_OK;
+}
+
+ds3_status ds3_set_slot_map(ds3_engine* e, const int32_t* slot_map) {
+  if (ds3_status st = refuse_if_unusable(e)) return st;
+  const ds3_config& c = e->cfg;
+  if (c.kv_layout != DS3_KV_PAGED) return fail(e, DS3_E_INVALID, "slot map needs the paged KV layout");
+  if (!slot_map) return fail(e, DS3_E_INVALID, "slot map is NULL");
+  const size_t n = (size_t)c.rows * (c.cap / c.page_size);
+  std::vector<uint8_t> seen((size_t)c.pool_pages, 0);
+  for (size_t i = 0; i < n; ++i) {
+    const int32_t pg = slot_map[i];
+    if (pg < 0 || pg >= c.pool_pages) return fail(e, DS3_E_INVALID, "page id out of range at " + std::to_string(i));
+    if (seen[pg]) return fail(e, DS3_E_INVALID, "page " + std::to_string(pg) + " appears twice");
+    seen[pg] = 1;
+  }
+  e->h_slot_map.assign(slot_map, slot_map + n);
+  HIP_OR_POISON(e, hipMemcpyAsync(e->slot_map, e->h_slot_map.data(), n * 4, hipMemcpyHostToDevice, e->stream));
+  HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
+  e->pending = true;
+  if (ds3_status st = wait_done(e, e->ev_done, e->cfg.timeout_ms)) return st;
+  e->slot_map_set = true;
+  return DS3_OK;
+}
+
+ds3_status ds3_step(ds3_engine* e, const int32_t* tokens, const int32_t* pos, const int32_t* write_map,
+                    float* logits_host, uint32_t* flags) {
+  const auto t_start = std::chrono::steady_clock::now();
+  if (ds3_status st = refuse_if_unusable(e)) return st;
+  if (e->state == ST_NOT_LOADED) return fail(e, DS3_E_NOT_LOADED, "weights are not loaded");
+  if (e->state == ST_NEEDS_RESET) return fail(e, DS3_E_NEEDS_RESET, "a previous step failed; reset_state first");
+  const ds3_config& c = e->cfg;
+  if (!tokens || !pos) return fail(e, DS3_E_INVALID, "tokens or pos is NULL");
+  const SlotLayout sl{c.rows};
+  const bool paged = c.kv_layout == DS3_KV_PAGED;
+  if (paged && !write_map && !e->slot_map_set) return fail(e, DS3_E_INVALID, "paged step needs a slot map");
+  for (int r = 0; r < c.rows; ++r) {
+    if (tokens[r] < 0 || tokens[r] >= c.vocab) return fail(e, DS3_E_INVALID, "token out of range in row " + std::to_string(r));
+    if (pos[r] < 0 || pos[r] >= c.cap) return fail(e, DS3_E_INVALID, "pos out of range in row " + std::to_string(r));
+    if (paged && write_map &&
+        (write_map[r] < 0 || (int64_t)write_map[r] >= (int64_t)c.pool_pages * c.page_size))
+      return fail(e, DS3_E_INVALID, "write_map out of range in row " + std::to_string(r));
+  }
+  // slot words, then the status words (cleared every step by the same copy)
+  for (int r = 0; r < c.rows; ++r) {
+    e->h_slots[sl.token() + r] = tokens[r];
+    e->h_slots[sl.pos() + r] = pos[r];
+    int32_t wm = 0;
+    if (paged) {
+      const int ppr = c.cap / c.page_size;
+      wm = write_map ? write_map[r]
+                     : e->h_slot_map[(size_t)r * ppr + pos[r] / c.page_size] * c.page_size + pos[r] % c.page_size;
+    }
+    e->h_slots[sl.write_map() + r] = wm;
+  }
+  e->h_slots[sl.inject()] = e->inject_check ? 1 : 0;
+  e->inject_check = false;
+  const uint32_t timeout = e->inject_timeout ? 0u : e->cfg.timeout_ms;
+  e->inject_timeout = false;
+
+  HIP_OR_POISON(e, hipMemcpyAsync(e->slots, e->h_slots, (size_t)sl.words() * 4, hipMemcpyHostToDevice, e->stream));
+  e->h_status->err = 0;
+  e->h_status->nonfinite = 0;
+  HIP_OR_POISON(e, hipMemcpyAsync(e->status, e->h_status, sizeof(StatusWords), hipMemcpyHostToDevice, e->stream));
+  if (c.exec_mode == DS3_GRAPH) {
+    if (ds3_status st = ensure_captured(e)) return st;
+    HIP_OR_POISON(e, hipEventRecord(e->ev0, e->stream));
+    HIP_OR_POISON(e, hipGraphLaunch(e->exec, e->stream));
+    HIP_OR_POISON(e, hipEventRecord(e->ev1, e->stream));
+    e->stats.replays++;
+  } else {
+    HIP_OR_POISON(e, hipEventRecord(e->ev0, e->stream));
+    HIP_OR_POISON(e, enqueue_step(e));
+    HIP_OR_POISON(e, hipEventRecord(e->ev1, e->stream));
+  }
+  HIP_OR_POISON(e, hipMemcpyAsync(e->h_status, e->status, sizeof(StatusWords), hipMemcpyDeviceToHost, e->stream));
+  if (logits_host)
+    HIP_OR_POISON(e, hipMemcpyAsync(logits_host, e->logits, (size_t)c.rows * c.vocab * 4, hipMemcpyDeviceToHost,
+                                    e->stream));
+  HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
+  e->pending = true;
+  e->stats.last_submit_us =
+      std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t_start).count();
+  if (ds3_status st = wait_done(e, e->ev_done, timeout)) return st;
+  float gpu_ms = 0.f;
+  HIP_OR_POISON(e, hipEventElapsedTime(&gpu_ms, e->ev0, e->ev1));
+  e->stats.last_gpu_us = gpu_ms * 1e3;
+  e->stats.kernels_per_step = c.exec_mode == DS3_GRAPH ? e->graph_nodes : (int)e->sequence.size();
+  const uint32_t errbits = e->h_status->err;
+  if (flags) *flags = e->h_status->nonfinite ? 1u : 0u;
+  e->stats.last_host_us =
+      std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t_start).count();
+  if (errbits) {
+    e->state = ST_NEEDS_RESET;
+    e->stats.state = e->state;
+    return fail(e, DS3_E_KERNEL_CHECK, "in-kernel check failed, error bits 0x" + [&] {
+      char b[16];
+      std::snprintf(b, sizeof b, "%x", errbits);
+      return std::string(b);
+    }());
+  }
+  e->stats.steps++;
+  return DS3_OK;
+}
+
+ds3_status ds3_reset_state(ds3_engine* e) {
+  if (ds3_status st = refuse_if_unusable(e)) return st;
+  HIP_OR_POISON(e, hipMemsetAsync(e->buf[DS3_BUF_KV], 0, e->kv_bytes, e->stream));
+  HIP_OR_POISON(e, launch_fill_u32(e->counters, 0u, (size_t)e->cfg.rows * e->cfg.n_kv_heads, e->stream));
+  HIP_OR_POISON(e, launch_fill_u32(reinterpret_cast<uint32_t*>(e->status), 0u, 2, e->stream));
+  HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
+  e->pending = true;
+  if (ds3_status st = wait_done(e, e->ev_done, e->cfg.timeout_ms)) return st;
+  if (e->state == ST_NEEDS_RESET) e->state = ST_READY;
+  e->stats.state = e->state;
+  return DS3_OK;
+}
+
+static ds3_status kv_transfer(ds3_engine* e, int32_t layer, int32_t row, int32_t pos0, int32_t n, void* k, void* v,
+                              bool to_state) {
+  if (ds3_status st = refuse_if_unusable(e)) return st;
+  const ds3_config& c = e->cfg;
+  if (!k || !v) return fail(e, DS3_E_INVALID, "k or v is NULL");
+  if (layer < 0 || layer >= c.n_layers || row < 0 || row >= c.rows || pos0 < 0 || n < 0 || (int64_t)pos0 + n > c.cap)
+    return fail(e, DS3_E_INVALID, "layer/row/position range out of bounds");
+  if (c.kv_layout == DS3_KV_PAGED && !e->slot_map_set) return fail(e, DS3_E_INVALID, "paged KV needs a slot map");
+  if (n == 0) return DS3_OK;
+  const size_t kvb = dtype_bytes(c.kv_dtype);
+  const size_t half = (size_t)c.n_kv_heads * n * c.head_dim * kvb;
+  if (e->kv_staging_bytes < 2 * half) {
+    if (e->kv_staging) HIP_OR_POISON(e, hipFree(e->kv_staging));
+    e->kv_staging = nullptr;
+    e->kv_staging_bytes = 0;
+    HIP_OR_POISON(e, hipMalloc(&e->kv_staging, 2 * half));
+    e->kv_staging_bytes = 2 * half;
+  }
+  char* stg = reinterpret_cast<char*>(e->kv_staging);
+  if (to_state) {
+    HIP_OR_POISON(e, hipMemcpyAsync(stg, k, half, hipMemcpyHostToDevice, e->stream));
+    HIP_OR_POISON(e, hipMemcpyAsync(stg + half, v, half, hipMemcpyHostToDevice, e->stream));
+    HIP_OR_POISON(e, launch_kv_copy(e->kv, c.kv_dtype, layer, row, pos0, n, c.n_kv_heads, c.head_dim, stg, 1,
+                                    e->status, e->stream));
+  } else {
+    HIP_OR_POISON(e, launch_kv_copy(e->kv, c.kv_dtype, layer, row, pos0, n, c.n_kv_heads, c.head_dim, stg, 0,
+                                    e->status, e->stream));
+    HIP_OR_POISON(e, hipMemcpyAsync(k, stg, half, hipMemcpyDeviceToHost, e->stream));
+    HIP_OR_POISON(e, hipMemcpyAsync(v, stg + half, half, hipMemcpyDeviceToHost, e->stream));
+  }
+  HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
+  e->pending = true;
+  return wait_done(e, e->ev_done, e->cfg.timeout_ms);
+}
+
+ds3_status ds3_write_kv(ds3_engine* e, int32_t layer, int32_t row, int32_t pos0, int32_t n, const void* k,
+                        const void* v) {
+  return kv_transfer(e, layer, row, pos0, n, const_cast<void*>(k), const_cast<void*>(v), true);
+}
+
+ds3_status ds3_read_kv(ds3_engine* e, int32_t layer, int32_t row, int32_t pos0, int32_t n, void* k, void* v) {
+  return kv_transfer(e, layer, row, pos0, n, k, v, false);
+}
+
+ds3_status ds3_stats_get(const ds3_engine* e, ds3_stats* out) {
+  if (!e || !out) return DS3_E_INVALID;
+  *out = e->stats;
+  out->state = e->state;
+  out->attn_splits = e->splits;
+  if (out->kernels_per_step == 0) out->kernels_per_step = (int)e->sequence.size();
+  return DS3_OK;
+}
+
+ds3_status ds3_profile_kernels(ds3_engine* e, int32_t iters, ds3_kernel_time* out, int32_t* n_inout) {
+  if (ds3_status st = refuse_if_unusable(e)) return st;
+  if (e->state != ST_READY) return fail(e, DS3_E_NOT_LOADED, "engine is not ready");
+  if (!out || !n_inout || *n_inout < K_NUM || iters < 1) return fail(e, DS3_E_INVALID, "need room for the kernel kinds");
+  const size_t nk = e->sequence.size();
+  std::vector<hipEvent_t> evs(2 * nk, nullptr);
+  for (auto& ev : evs) HIP_OR_POISON(e, hipEventCreate(&ev));
+  std::vector<double> tot(K_NUM, 0.0);
+  std::vector<int> cnt(K_NUM, 0);
+  for (const Launch& l : e->sequence) cnt[l.kind]++;
+  ds3_status result = DS3_OK;
+  for (int it = 0; it < iters && result == DS3_OK; ++it) {
+    e->h_status->err = 0;
+    e->h_status->nonfinite = 0;
+    hipError_t h = hipMemcpyAsync(e->status, e->h_status, sizeof(StatusWords), hipMemcpyHostToDevice, e->stream);
+    for (size_t i = 0; i < nk && h == hipSuccess; ++i) {
+      h = hipEventRecord(evs[2 * i], e->stream);
+      if (h == hipSuccess) h = enqueue_kernel(e, e->sequence[i]);
+      if (h == hipSuccess) h = hipEventRecord(evs[2 * i + 1], e->stream);
+    }
+    if (h == hipSuccess) h = hipEventRecord(e->ev_done, e->stream);
+    if (h != hipSuccess) {
+      result = poison(e, DS3_E_DEVICE_LOST, std::string("profile: ") + hipGetErrorString(h));
+      break;
+    }
+    e->pending = true;
+    result = wait_done(e, e->ev_done, e->cfg.timeout_ms);
+    if (result != DS3_OK) break;
+    for (size_t i = 0; i < nk; ++i) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, evs[2 * i], evs[2 * i + 1]) != hipSuccess) {
+        result = poison(e, DS3_E_DEVICE_LOST, "profile: event timing failed");
+        break;
+      }
+      tot[e->sequence[i].kind] += ms * 1e3;
+    }
+  }
+  for (auto& ev : evs) (void)hipEventDestroy(ev);
+  if (result != DS3_OK) return result;
+  for (int k = 0; k < K_NUM; ++k) {
+    std::snprintf(out[k].name, sizeof(out[k].name), "%s", kKindNames[k]);
+    out[k].launches = cnt[k];
+    out[k].total_us = tot[k] / iters;
+    out[k].bytes = kind_bytes(e->cfg, k);
+  }
+  *n_inout = K_NUM;
+  return DS3_OK;
+}
+
+ds3_status ds3_debug_inject(ds3_engine* e, int32_t kind) {
+  if (ds3_status st = refuse_if_unusable(e)) return st;
+  if (kind == DS3_INJECT_KERNEL_CHECK) e->inject_check = true;
+  else if (kind == DS3_INJECT_TIMEOUT_NEXT) e->inject_timeout = true;
+  else return fail(e, DS3_E_INVALID, "unknown injection");
+  return DS3_OK;
+}
+
+const char* ds3_last_error(const ds3_engine* e) { return e ? e->err.c_str() : g_last_error.c_str(); }
+
+void ds3_destroy(ds3_engine* e) {
+  if (!e) return;
+  // Work from an earlier step may still be running after a timeout: wait for it (bounded) before releasing
+  // anything the kernels could touch.
+  if (e->pending && e->ev_done) {
+    const auto t0 = std::chrono::steady_clock::now();
+    while (hipEventQuery(e->ev_done) == hipErrorNotReady &&
+           std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count() <
+               (double)(e->cfg.timeout_ms ? e->cfg.timeout_ms : kDefaultTimeoutMs))
+      std::this_thread::sleep_for(std::chrono::microseconds(100));
+  }
+  if (e->exec) (void)hipGraphExecDestroy(e->exec);
+  if (e->graph) (void)hipGraphDestroy(e->graph);
+  for (hipEvent_t ev : {e->ev0, e->ev1, e->ev_done})
+    if (ev) (void)hipEventDestroy(ev);
+  if (e->h_slots) (void)hipHostFree(e->h_slots);
+  if (e->kv_staging) (void)hipFree(e->kv_staging);
+  if (e->own_stream && e->stream) (void)hipStreamDestroy(e->stream);
+  delete e;
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Internal interface between the engine (host) and the decode-step kernels (device). Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ds3 {
+
+// Bits of the device error word. A kernel that finds an out-of-range slot value sets its bit and substitutes a
+// safe value, so every access stays in bounds and every wave exits normally.
+enum : uint32_t {
+  ERR_TOKEN = 1u,       // Slot::Token outside [0, vocab)
+  ERR_POS = 2u,         // Slot::Pos outside [0, cap)
+  ERR_WRITE_MAP = 4u,   // Slot::WriteMap outside the pool
+  ERR_PAGE = 8u,        // a page id of the SlotMap outside [0, pool_pages)
+  ERR_INJECTED = 16u,   // test hook
+};
+
+// Slot buffer layout (int32 words at fixed device addresses; the host rewrites them before every replay).
+struct SlotLayout {
+  int rows;
+  __host__ __device__ int token() const { return 0; }
+  __host__ __device__ int pos() const { return rows; }
+  __host__ __device__ int write_map() const { return 2 * rows; }
+  __host__ __device__ int inject() const { return 3 * rows; }
+  __host__ __device__ int words() const { return 3 * rows + 1; }
+};
+
+// Status words written by kernels and read back after every step.
+struct StatusWords {
+  uint32_t err;        // ERR_* bits
+  uint32_t nonfinite;  // 1 if some logit is NaN or infinite
+};
+
+// Where the K/V state lives and how a (row, kv head, position) maps to an address.
+struct KvView {
+  void* k;               // layer 0 base of K (contiguous: [rows][nkv][cap][hd]; paged: [pages][nkv][ps][hd])
+  void* v;
+  int64_t layer_stride;  // elements between consecutive layers
+  int paged;             // 0 contiguous, 1 paged
+  int cap;
+  int page_size;
+  int pool_pages;
+  const int* slot_map;   // paged: [rows][cap/page_size]
+};
+
+enum GemvMode : int {
+  GEMV_QKV = 0,      // RMSNorm(x) -> [q;k;v] rows, rotary epilogue, K/V write at Slot::Pos
+  GEMV_GATEUP = 1,   // RMSNorm(x) -> gate/up rows, SwiGLU epilogue -> act
+  GEMV_RESID = 2,    // act -> rows, residual add into x
+  GEMV_HEAD = 3,     // RMSNorm(x) -> logits
+};
+
+struct GemvParams {
+  const void* w;         // weight rows [n_rows_total][K] (bf16 words or float32)
+  const float* in;       // activation input [rows][K] (fp32); RMSNorm input for the norm modes
+  const float* gain;     // RMSNorm gain [K] (fp32), norm modes only
+  float* out;            // QKV: q [rows][nq*hd]; GATEUP: act [rows][F]; RESID: x [rows][n_out]; HEAD: logits
+  int K;                 // input width
+  int n_pairs;           // output row pairs
+  int rows;              // activation rows (1..kMaxGemvRows)
+  float eps;
+  // QKV only
+  int nq, nkv, hd;
+  const float* rope;     // [cap][hd/2][2] cos, sin
+  KvView kv;
+  int layer;
+  // GATEUP: offset of the up rows after the gate rows (= F); HEAD/RESID: unused
+  int up_offset;
+  // shared
+  const int* slots;      // slot buffer
+  StatusWords* status;
+};
+
+struct AttnParams {
+  const float* q;        // [rows][nq][hd]
+  float* out;            // [rows][nq][hd]
+  float* part;           // partials: [rows][nkv][splits][G][hd + 2]
+  unsigned* counters;    // [rows][nkv], zero between launches
+  KvView kv;
+  int layer;
+  int nq, nkv, hd;
+  int splits;
+  int split_len;         // positions per split (multiple of the positions one block pass covers)
+  float scale;           // 1/sqrt(hd)
+  const int* slots;
+  StatusWords* status;
+};
+
+struct EmbedParams {
+  const void* table;     // [vocab][d]
+  float* x;              // [rows][d]
+  int d, vocab, rows;
+  const int* slots;
+  StatusWords* status;
+};
+
+constexpr int kMaxGemvRows = 4;
+
+// Host launchers (defined in ds3_kernels.hip). Each returns the launch error, if any.
+hipError_t launch_embed(const EmbedParams& p, int weight_dtype, hipStream_t s);
+hipError_t launch_gemv(const GemvParams& p, int mode, int weight_dtype, int kv_dtype, int blocks, hipStream_t s);
+hipError_t launch_attention(const AttnParams& p, int kv_dtype, int rows, hipStream_t s);
+hipError_t launch_kv_copy(const KvView& kv, int kv_dtype, int layer, int row, int pos0, int n, int nkv, int hd,
+                          void* staging, int to_state, StatusWords* status, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t s);
+
+size_t gemv_lds_bytes(int rows, int K);
+int attn_positions_per_pass(int hd, int kv_dtype);
+size_t attn_lds_bytes(int nq, int nkv, int hd, int split_len);
+
+}  // namespace ds3

@@ -1,0 +1,129 @@
+"""Python face of libds3.so: allocate the device buffers with PyTorch, hand them to the library, marshal calls.
+
+PyTorch provides device memory and a stream here and nothing else; every computation of the step runs inside the
+library's HIP kernels. The executor contract follows the poot documentation's "Execution" page, section
+"Per backend" (load_weights, step, reset_state, stats, unload).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _ds3 as C
+
+
+def make_config(*, n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, rms_eps, rope_theta, rows,
+                cap, kv_layout="contiguous", page_size=0, pool_pages=0, weight_dtype="bf16", kv_dtype="bf16",
+                exec_mode="graph", timeout_ms=0) -> C.ds3_config:
+    dt = {"f32": C.DS3_F32, "bf16": C.DS3_BF16}
+    return C.ds3_config(
+        C.DS3_ABI_VERSION, n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, rms_eps, rope_theta,
+        rows, cap, C.DS3_KV_PAGED if kv_layout == "paged" else C.DS3_KV_CONTIGUOUS, page_size, pool_pages,
+        dt[weight_dtype], dt[kv_dtype], C.DS3_EAGER if exec_mode == "eager" else C.DS3_GRAPH, timeout_ms)
+
+
+class Engine:
+    """One decode-step engine on one GPU: fixed rows, capacity and KV layout; weights loaded once."""
+
+    def __init__(self, cfg: C.ds3_config, device: str = "cuda:0"):
+        import torch
+        self.cfg = cfg
+        self.rows, self.vocab = cfg.rows, cfg.vocab
+        self.device = torch.device(device)
+        self._torch = torch
+        reqs = C.ds3_query_buffers(cfg)
+        with torch.cuda.device(self.device):
+            self.buffers = [torch.empty(max(int(r.bytes), 256), dtype=torch.uint8, device=self.device) for r in reqs]
+            self.stream = torch.cuda.Stream(self.device)
+            torch.cuda.synchronize(self.device)
+            self.handle = C.ds3_create(cfg, [b.data_ptr() for b in self.buffers], self.stream.cuda_stream)
+        self.logits_device = self.buffers[C.DS3_BUF_LOGITS][: 4 * self.rows * self.vocab].view(torch.float32).view(
+            self.rows, self.vocab)
+        self._logits_host = torch.empty((self.rows, self.vocab), dtype=torch.float32, pin_memory=True)
+        self._tok = np.zeros(self.rows, np.int32)
+        self._pos = np.zeros(self.rows, np.int32)
+        self._wm = np.zeros(self.rows, np.int32)
+
+    # -- contract ------------------------------------------------------------------------------------------
+
+    def load_weights(self, layers: list, glob: dict) -> None:
+        """Bind weights by role: `layers[l][role]` and `glob[role]` are numpy arrays (bf16 words or float32)."""
+        dtype = self.cfg.weight_dtype
+        srcs, keep = [], []
+
+        def add(role, layer, arr):
+            a = np.ascontiguousarray(arr)
+            keep.append(a)
+            rows, cols = (1, a.shape[0]) if a.ndim == 1 else a.shape
+            srcs.append(C.ds3_weight_src(C.ROLES[role], layer, dtype, rows, cols, a.ctypes.data))
+
+        for li, L in enumerate(layers):
+            for role, arr in L.items():
+                add(role, li, arr)
+        for role, arr in glob.items():
+            add(role, -1, arr)
+        C.ds3_load_weights(self.handle, srcs)
+
+    def set_slot_map(self, slot_map: np.ndarray) -> None:
+        a = np.ascontiguousarray(slot_map, dtype=np.int32)
+        C.ds3_set_slot_map(self.handle, a.ctypes.data)
+
+    def step(self, tokens, pos, write_map=None, copy_logits: bool = True):
+        """One decode step. Returns (logits float32 [rows, vocab] numpy view of pinned memory or None, flags)."""
+        self._tok[:] = tokens
+        self._pos[:] = pos
+        wm = None
+        if write_map is not None:
+            self._wm[:] = write_map
+            wm = self._wm.ctypes.data
+        out = self._logits_host.data_ptr() if copy_logits else None
+        flags = C.ds3_step(self.handle, self._tok.ctypes.data, self._pos.ctypes.data, wm, out)
+        return (self._logits_host.numpy() if copy_logits else None), flags
+
+    def reset_state(self) -> None:
+        C.ds3_reset_state(self.handle)
+
+    def write_kv(self, layer: int, row: int, pos0: int, k: np.ndarray, v: np.ndarray) -> None:
+        k = np.ascontiguousarray(k)
+        v = np.ascontiguousarray(v)
+        C.ds3_write_kv(self.handle, layer, row, pos0, k.shape[1], k.ctypes.data, v.ctypes.data)
+
+    def read_kv(self, layer: int, row: int, pos0: int, n: int):
+        dt = np.uint16 if self.cfg.kv_dtype == C.DS3_BF16 else np.float32
+        shape = (self.cfg.n_kv_heads, n, self.cfg.head_dim)
+        k, v = np.empty(shape, dt), np.empty(shape, dt)
+        C.ds3_read_kv(self.handle, layer, row, pos0, n, k.ctypes.data, v.ctypes.data)
+        return k, v
+
+    def stats(self) -> dict:
+        s = C.ds3_stats_get(self.handle)
+        return {f: getattr(s, f) for f, _ in s._fields_ if f != "reserved"}
+
+    def profile_kernels(self, iters: int = 5) -> list:
+        return [{"name": k.name.decode(), "launches": k.launches, "us_per_step": k.total_us, "bytes_per_step": k.bytes}
+                for k in C.ds3_profile_kernels(self.handle, iters)]
+
+    def debug_inject(self, kind: int) -> None:
+        C.ds3_debug_inject(self.handle, kind)
+
+    def last_error(self) -> str:
+        return C.ds3_last_error(self.handle)
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            C.ds3_destroy(self.handle)
+            self.handle = None
+            self.buffers = []
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,206 @@
+/*
+ * ds3.h -- C ABI of the constant-shape transformer decode step on MI355X (gfx950).
+ *
+ * The library exposes an executor shaped like the one on the poot documentation's "Execution" page (section
+ * "Per backend", the executor contract: load the weights once, step per token, reset the carried state, report
+ * statistics, unload): ds3_load_weights, ds3_step(tokens, pos) -> logits, ds3_reset_state, ds3_stats_get and
+ * ds3_destroy. Every call is extern "C" over plain pointers and sizes; no C++ or PyTorch type crosses it.
+ *
+ * Memory ownership: the CALLER allocates every device buffer the engine uses (sizes from ds3_query_buffers) and
+ * passes their addresses to ds3_create; the engine borrows them until ds3_destroy. The addresses must stay fixed,
+ * because the first step records a HIP graph whose kernel arguments point at them ("Execution" page, sections
+ * "A constant-shape decode graph" and "Slot buffers": grids and buffer addresses stay constant so one capture
+ * serves every position up to the capacity). The engine owns only its pinned host staging, its HIP events and
+ * its graph objects. The HIP stream is the caller's (borrowed), or the engine's own when NULL is passed.
+ *
+ * Errors ("Execution" page, section "Failure handling"): every call returns a ds3_status and never aborts the
+ * process. Argument errors leave the engine unchanged and touch no device state. A failed in-kernel check marks
+ * the engine NEEDS_RESET (ds3_step refuses until ds3_reset_state). A device error or a wait that outlasts the
+ * timeout POISONS the engine: every later call except ds3_last_error/ds3_destroy returns DS3_E_POISONED without
+ * a HIP call. ds3_last_error gives a message for the last failure.
+ *
+ * Threading: one engine is used by one host thread at a time.
+ */
+#ifndef DS3_H
+#define DS3_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DS3_ABI_VERSION 1u
+
+typedef struct ds3_engine ds3_engine;
+
+typedef enum {
+  DS3_OK = 0,
+  DS3_E_INVALID = 1,       /* bad argument (null pointer, token/pos/map out of range, wrong shape); no effect */
+  DS3_E_UNSUPPORTED = 2,   /* configuration outside what the kernels implement; the message names the field */
+  DS3_E_UNBOUND = 3,       /* ds3_load_weights: a (role, layer) the step needs was not supplied */
+  DS3_E_NOT_LOADED = 4,    /* ds3_step before a successful ds3_load_weights */
+  DS3_E_NEEDS_RESET = 5,   /* an earlier step failed after replay; call ds3_reset_state */
+  DS3_E_KERNEL_CHECK = 6,  /* an in-kernel check failed during this step; the engine now needs a reset */
+  DS3_E_TIMEOUT = 7,       /* a device wait outlasted timeout_ms; the engine is now poisoned */
+  DS3_E_DEVICE_LOST = 8,   /* a HIP call failed; the engine is now poisoned */
+  DS3_E_POISONED = 9       /* the engine was poisoned earlier; the call did not touch the device */
+} ds3_status;
+
+enum { DS3_F32 = 0, DS3_BF16 = 1 };                  /* weight and KV storage types */
+enum { DS3_KV_CONTIGUOUS = 0, DS3_KV_PAGED = 1 };    /* KV layouts */
+enum { DS3_GRAPH = 0, DS3_EAGER = 1 };               /* replay one captured graph, or launch every kernel */
+
+/*
+ * Model shape and step shape. Llama-style pre-norm decoder without biases: per layer RMSNorm, Q/K/V projection
+ * with rotary embedding on q and k, K/V write at the step's position, attention over the KV capacity with the
+ * positions after the current one hidden, o-projection, RMSNorm, SwiGLU feed-forward; then the final RMSNorm
+ * and the LM head ("Models, Registry and the Driver" page, section "Shared components": embed, one layer scope
+ * per layer with x += mixer(norm(x)); x += ffn(norm(x)), final norm, head).
+ *
+ * rows: sequences per step (1..16). cap: KV capacity per row (positions 0..cap-1). kv_layout CONTIGUOUS keeps
+ * K and V as [layer][row][kv_head][cap][head_dim]; PAGED keeps a pool [layer][page][kv_head][page_size][head_dim]
+ * of pool_pages pages addressed through a per-row page table (see ds3_set_slot_map). timeout_ms = 0 selects the
+ * default of 600000 ms ("Execution" page, section "Failure handling": every device wait is bounded).
+ */
+typedef struct {
+  uint32_t abi_version;        /* DS3_ABI_VERSION */
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+  float rms_eps;
+  double rope_theta;
+  int32_t rows, cap, kv_layout, page_size, pool_pages;
+  int32_t weight_dtype, kv_dtype, exec_mode;
+  uint32_t timeout_ms;
+} ds3_config;
+
+/* Device buffers the caller allocates for ds3_create, in this id order. */
+enum {
+  DS3_BUF_WEIGHTS = 0,   /* packed weights: filled by ds3_load_weights */
+  DS3_BUF_KV = 1,        /* K and V state of every layer (contiguous or pool) */
+  DS3_BUF_WORK = 2,      /* slot buffers, activations, attention partials, rotary table, error word */
+  DS3_BUF_LOGITS = 3,    /* float32 [rows][vocab]: the step's output */
+  DS3_NUM_BUFFERS = 4
+};
+
+typedef struct {
+  int32_t id;
+  char name[32];
+  uint64_t bytes;
+  uint32_t align;   /* required alignment of the device address, in bytes */
+} ds3_buffer_req;
+
+/* Weight roles: a weight is bound by what it is, not by a checkpoint's tensor name ("Execution" page, section
+ * "Per backend": load_weights binds each weight by its typed role; a weight nothing names stays unbound). */
+typedef enum {
+  DS3_W_EMBED = 0,       /* [vocab, d_model] */
+  DS3_W_ATTN_NORM = 1,   /* [d_model] per layer */
+  DS3_W_Q = 2,           /* [n_q_heads*head_dim, d_model] per layer */
+  DS3_W_K = 3,           /* [n_kv_heads*head_dim, d_model] per layer */
+  DS3_W_V = 4,           /* [n_kv_heads*head_dim, d_model] per layer */
+  DS3_W_O = 5,           /* [d_model, n_q_heads*head_dim] per layer */
+  DS3_W_FFN_NORM = 6,    /* [d_model] per layer */
+  DS3_W_GATE = 7,        /* [ffn_dim, d_model] per layer */
+  DS3_W_UP = 8,          /* [ffn_dim, d_model] per layer */
+  DS3_W_DOWN = 9,        /* [d_model, ffn_dim] per layer */
+  DS3_W_FINAL_NORM = 10, /* [d_model] */
+  DS3_W_LM_HEAD = 11,    /* [vocab, d_model] */
+  DS3_W_NUM_ROLES = 12
+} ds3_role;
+
+/* One weight tensor: row-major [rows, cols] ([out, in] for matrices; cols = length for norm gains) of dtype
+ * DS3_F32 or DS3_BF16 (bf16 words), equal to cfg.weight_dtype. `data` may be a host or a device address. */
+typedef struct {
+  int32_t role;
+  int32_t layer;     /* -1 for EMBED, FINAL_NORM and LM_HEAD */
+  int32_t dtype;
+  int64_t rows, cols;
+  const void* data;
+} ds3_weight_src;
+
+typedef struct {
+  uint64_t steps;            /* successful ds3_step calls */
+  uint64_t replays;          /* graph launches */
+  uint64_t captures;         /* graph captures (1 per engine in graph mode) */
+  int32_t kernels_per_step;  /* kernel launches (eager) or kernel nodes (graph) per step */
+  int32_t state;             /* 0 ready, 1 not loaded, 2 needs reset, 3 poisoned */
+  double last_host_us;       /* host time of the last ds3_step, slot write to logits ready */
+  double last_gpu_us;        /* device time of the last step's kernels (HIP events) */
+  int32_t attn_splits;       /* split count of the attention sweep over [cap] */
+  int32_t reserved;
+  double last_submit_us;     /* host time of the last ds3_step spent issuing work (slot copy, launch or replay,
+                                readback copies), without the wait for the device */
+} ds3_stats;
+
+/* Per-kernel device timing of one step, from HIP events around each launch on the engine's stream. */
+typedef struct {
+  char name[40];
+  int32_t launches;     /* launches of this kernel per step */
+  double total_us;      /* summed over the launches of one step, averaged over the iterations */
+  double bytes;         /* algorithmic bytes the launches move per step (weights, swept K/V, writes) */
+} ds3_kernel_time;
+
+/* Sizes of the device buffers for `cfg`. `out` has room for *n_inout entries; on return *n_inout is
+ * DS3_NUM_BUFFERS. Validates the configuration (DS3_E_UNSUPPORTED names the failing field). */
+ds3_status ds3_query_buffers(const ds3_config* cfg, ds3_buffer_req* out, int32_t* n_inout);
+
+/* Create an engine over caller-allocated device buffers (`dev_ptrs[i]` for buffer id i, n = DS3_NUM_BUFFERS),
+ * on HIP stream `hip_stream` (a hipStream_t; NULL = the engine creates its own). Uploads the rotary table and
+ * zeroes the work and KV buffers. On success *out owns the engine; release it with ds3_destroy. */
+ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, void* hip_stream, ds3_engine** out);
+
+/* Bind and pack all weights in one call. Every (role, layer) must be present exactly once with its shape and
+ * dtype; a missing one -> DS3_E_UNBOUND naming it; a duplicate, unknown role or wrong shape/dtype ->
+ * DS3_E_INVALID. Copies from `data` (host or device) and returns when the copies are done. */
+ds3_status ds3_load_weights(ds3_engine* e, const ds3_weight_src* w, int32_t n);
+
+/* Paged layout only: the per-row page table, int32 [rows][cap/page_size] of physical page ids in
+ * [0, pool_pages). Rows must not share pages. Copied to its slot buffer; it stays until the next call. */
+ds3_status ds3_set_slot_map(ds3_engine* e, const int32_t* slot_map);
+
+/* One decode step for every row r: take token tokens[r] at absolute position pos[r] (0 <= pos < cap), write its
+ * K/V at that position (contiguous: the position itself; paged: flat pool slot write_map[r], or, when write_map
+ * is NULL, slot_map[r][pos/page_size]*page_size + pos%page_size), attend over positions 0..pos[r], and produce
+ * logits float32 [rows][vocab] in the DS3_BUF_LOGITS buffer ("Execution" page, sections "A constant-shape decode
+ * graph" and "Slot buffers"; "Models, Registry and the Driver" page, section "The Model": positions are absolute,
+ * so positions need not be consecutive and a prefill is a sequence of steps). K/V of positions below pos[r] must
+ * already be in the state (earlier steps or ds3_write_kv). The first step in graph mode captures the kernel
+ * sequence into a HIP graph; every step replays it. If logits_host is not NULL the logits are also copied there.
+ * flags (may be NULL) receives bit 0 = some logit is NaN or infinite (not an error by itself). */
+ds3_status ds3_step(ds3_engine* e, const int32_t* tokens, const int32_t* pos, const int32_t* write_map,
+                    float* logits_host, uint32_t* flags);
+
+/* Zero every row's K/V state and the step's scratch state; clears NEEDS_RESET. Keeps weights and the graph. */
+ds3_status ds3_reset_state(ds3_engine* e);
+
+/* Write / read K and V of `n` logical positions pos0..pos0+n-1 of one row and layer. `k` and `v` are host arrays
+ * [n_kv_heads][n][head_dim] in the KV dtype (float32 or bf16 words). Paged layout maps positions through the
+ * row's page table. */
+ds3_status ds3_write_kv(ds3_engine* e, int32_t layer, int32_t row, int32_t pos0, int32_t n, const void* k,
+                        const void* v);
+ds3_status ds3_read_kv(ds3_engine* e, int32_t layer, int32_t row, int32_t pos0, int32_t n, void* k, void* v);
+
+ds3_status ds3_stats_get(const ds3_engine* e, ds3_stats* out);
+
+/* Run `iters` eager steps with the current slot contents (the last step's tokens and positions, re-written at
+ * the same positions) and report each kernel's device time per step, timed with HIP events on the engine's
+ * stream. `out` has room for *n_inout entries; on return *n_inout is the number of kernels. */
+ds3_status ds3_profile_kernels(ds3_engine* e, int32_t iters, ds3_kernel_time* out, int32_t* n_inout);
+
+/* Test hook for the failure path: DS3_INJECT_KERNEL_CHECK makes the next step's first kernel raise its check
+ * bit, so that step returns DS3_E_KERNEL_CHECK and the engine needs a reset. DS3_INJECT_TIMEOUT_NEXT sets the
+ * next step's wait limit to 0 ms so that it reports DS3_E_TIMEOUT (the kernels themselves run normally). */
+enum { DS3_INJECT_KERNEL_CHECK = 1, DS3_INJECT_TIMEOUT_NEXT = 2 };
+ds3_status ds3_debug_inject(ds3_engine* e, int32_t kind);
+
+/* Message of the engine's last failure ("" if none); engine-owned, valid until the next call. With e == NULL,
+ * the last failure of ds3_query_buffers/ds3_create on this thread. */
+const char* ds3_last_error(const ds3_engine* e);
+
+/* Release the engine (graph, events, staging). The caller's device buffers are not freed. */
+void ds3_destroy(ds3_engine* e);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DS3_H */

@@ -202,6 +202,17 @@ def make_weights(model: ModelShape, seed: int = 0, *, std: float = 0.02, gains: 
     """Draw every weight of `model`: matrices ~ N(0, std^2); RMSNorm gains = 1 ("ones") or 1 + N(0, gain_std^2)."""
     ws = WeightSet(model, [], {}, model.weight_dtype)
     dt = model.weight_dtype
+    import torch
+    torch_threads = torch.get_num_threads()
+    torch.set_num_threads(1)      # the chunk workers already use every core
+    try:
+        _draw_weights(ws, model, seed, std, gains, gain_std, dt)
+    finally:
+        torch.set_num_threads(torch_threads)
+    return ws
+
+
+def _draw_weights(ws, model, seed, std, gains, gain_std, dt):
     with ThreadPoolExecutor(_threads()) as pool:
         def gain(role, layer):
             if gains == "ones":
@@ -222,7 +233,6 @@ def make_weights(model: ModelShape, seed: int = 0, *, std: float = 0.02, gains: 
         ws.glob["embed"] = _normal_tensor(ws.shape_of("embed"), std, dt, (seed, model.name, "embed", -1), pool)
         ws.glob["lm_head"] = _normal_tensor(ws.shape_of("lm_head"), std, dt, (seed, model.name, "lm_head", -1), pool)
         ws.glob["final_norm"] = gain("final_norm", -1)
-    return ws
 
 
 # ----------------------------------------------------------------------------------------------------------

@@ -1,0 +1,119 @@
+"""Shared helpers of the GPU parity tests: build an engine and an oracle model from the same seeded inputs.
+
+Inputs come only from `synth` (seeded draws); expected values come only from `oracle`. The two sides share no
+arithmetic.
+"""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+
+import oracle
+import synth
+
+# Tolerances stated for the decode step: logits max-abs 1e-4 with fp32 weights, 2e-2 with bf16 weights (fp32
+# accumulate); greedy ids must match wherever the oracle's top-2 margin exceeds 5e-2.
+TOL_F32 = 1e-4
+TOL_BF16 = 2e-2
+GREEDY_MARGIN = 5e-2
+
+
+def log(*a):
+    print("[ds3-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def logits_tol(w: synth.Workload) -> float:
+    return TOL_F32 if w.model.weight_dtype == "f32" else TOL_BF16
+
+
+def engine_config(w: synth.Workload, exec_mode="graph", timeout_ms=0, rows=None, cap=None):
+    from decode_step_03_amd import make_config
+    m = w.model
+    return make_config(n_layers=m.n_layers, d_model=m.d_model, n_q_heads=m.n_q_heads, n_kv_heads=m.n_kv_heads,
+                       head_dim=m.head_dim, ffn_dim=m.ffn_dim, vocab=m.vocab, rms_eps=m.rms_eps,
+                       rope_theta=m.rope_theta, rows=rows or w.rows, cap=cap or w.cap, kv_layout=w.kv_layout,
+                       page_size=w.page_size, pool_pages=w.pool_pages, weight_dtype=m.weight_dtype,
+                       kv_dtype=w.kv_dtype, exec_mode=exec_mode, timeout_ms=timeout_ms)
+
+
+def make_engine(w: synth.Workload, ws: synth.WeightSet, exec_mode="graph", timeout_ms=0):
+    from decode_step_03_amd import Engine
+    eng = Engine(engine_config(w, exec_mode, timeout_ms))
+    eng.load_weights(ws.layers, ws.glob)
+    return eng
+
+
+def kv_value_tol(oracle_vals: np.ndarray, kv_dtype: str) -> np.ndarray:
+    """Per-element K/V state tolerance: 1e-4 for float32 state; for bf16 state max(2e-2, one bf16 ulp)."""
+    if kv_dtype == "f32":
+        return np.full(oracle_vals.shape, TOL_F32)
+    mag = np.abs(oracle_vals)
+    ulp = np.where(mag > 0, np.ldexp(1.0, np.frexp(mag)[1] - 8), 0.0)
+    return np.maximum(TOL_BF16, ulp)
+
+
+def kv_to_f64(a: np.ndarray) -> np.ndarray:
+    return oracle.widen(a)
+
+
+class Lockstep:
+    """Runs the engine and the oracle side by side, teacher-forced by the oracle's greedy token."""
+
+    def __init__(self, w: synth.Workload, ws: synth.WeightSet, engine, n_alloc: int | None = None):
+        self.w, self.ws, self.engine = w, ws, engine
+        self.model = oracle.OracleModel.from_weightset(ws)
+        self.caches = [oracle.RowCache(self.model, n_alloc or w.cap, w.kv_dtype) for _ in range(w.rows)]
+        self.max_err = 0.0
+        self.greedy_checked = 0
+        self.greedy_flips_inside_margin = 0
+
+    def prefill_random_kv(self, n_pos_per_row, seed=0):
+        """K/V contents ~ N(0,1) (stored in the KV dtype) at positions [0, n) of every row and layer, both sides."""
+        for r, n in enumerate(n_pos_per_row):
+            if n == 0:
+                continue
+            for li in range(self.w.model.n_layers):
+                K = synth.kv_prefill(self.w, li, r, "k", n, seed)
+                V = synth.kv_prefill(self.w, li, r, "v", n, seed)
+                self.engine.write_kv(li, r, 0, K, V)
+                self.caches[r].set(li, 0, K, V)
+
+    def step(self, tokens, pos, write_map=None, check=True):
+        t0 = time.time()
+        got, flags = self.engine.step(tokens, pos, write_map)
+        got = got.copy()
+        t1 = time.time()
+        ref = np.stack([oracle.decode_step(self.model, self.caches[r], int(tokens[r]), int(pos[r]))
+                        for r in range(self.w.rows)])
+        t2 = time.time()
+        if check:
+            self.check_logits(got, ref, flags)
+        return got, ref, (t1 - t0, t2 - t1)
+
+    def check_logits(self, got, ref, flags):
+        assert np.all(np.isfinite(ref)), "oracle logits not finite"
+        assert flags == 0 and np.all(np.isfinite(got)), "non-finite GPU logits where the oracle is finite"
+        err = float(np.max(np.abs(got.astype(np.float64) - ref)))
+        self.max_err = max(self.max_err, err)
+        tol = logits_tol(self.w)
+        assert err <= tol, f"logits max-abs error {err:.3e} > {tol:.1e}"
+        for r in range(ref.shape[0]):
+            gi, m = oracle.greedy(ref[r])
+            if m > GREEDY_MARGIN:
+                assert int(np.argmax(got[r])) == gi, f"greedy id differs with oracle margin {m:.3f}"
+                self.greedy_checked += 1
+            elif int(np.argmax(got[r])) != gi:
+                self.greedy_flips_inside_margin += 1
+
+    def check_kv(self, layer, row, pos0, n):
+        k, v = self.engine.read_kv(layer, row, pos0, n)
+        for got, ref in ((k, self.caches[row].K[layer][:, pos0:pos0 + n]), (v, self.caches[row].V[layer][:, pos0:pos0 + n])):
+            g = kv_to_f64(got)
+            rf = ref.astype(np.float64)
+            tol = kv_value_tol(rf, self.w.kv_dtype)
+            bad = np.abs(g - rf) > tol
+            assert not np.any(bad), f"KV state differs: max {np.max(np.abs(g - rf)):.3e}"
+            assert np.all(np.isfinite(g))

@@ -1,0 +1,41 @@
+"""Parity at the benchmark's full size: the 8B-shaped bf16 decoder, batch 1, cap 8192, K/V pre-filled with N(0,1)
+up to position 2048, in the launch configuration bench.py times (HIP-graph replay, same split plan).
+
+The oracle computes whole steps (every logit depends on every weight), so two consecutive steps are checked in
+full: every logit within 2e-2, greedy id equal where the oracle's margin exceeds 5e-2, and the K/V written at the
+step positions of the first and last layer within the bf16 state tolerance.
+"""
+import time
+
+import numpy as np
+import pytest
+
+import synth
+from tests.ds3_testlib import Lockstep, log, make_engine
+
+pytestmark = pytest.mark.gpu
+
+
+def test_llama8b_cap8192_two_steps_full_size():
+    w = synth.workload("llama8b-bf16-cap8192")
+    t0 = time.time()
+    ws = synth.make_weights(w.model)
+    log(f"8B-shaped weights drawn in {time.time() - t0:.1f}s")
+    eng = make_engine(w, ws, "graph")
+    try:
+        ls = Lockstep(w, ws, eng, n_alloc=w.prefill_len + 8)
+        t0 = time.time()
+        ls.prefill_random_kv([w.prefill_len])
+        log(f"K/V pre-filled to {w.prefill_len} in {time.time() - t0:.1f}s")
+        tok = synth.start_tokens(w)
+        pos = synth.start_positions(w)
+        for i in range(2):
+            got, ref, (tg, to) = ls.step(tok, pos)
+            log(f"step at {int(pos[0])}: GPU {tg * 1e3:.1f} ms, oracle {to:.1f} s, max err so far {ls.max_err:.3e}")
+            for li in (0, w.model.n_layers - 1):
+                ls.check_kv(li, 0, int(pos[0]), 1)
+            tok = ref.argmax(axis=1).astype(np.int32)
+            pos = pos + 1
+        assert eng.stats()["captures"] == 1
+    finally:
+        eng.close()

@@ -1,0 +1,177 @@
+"""GPU parity of the decode step against the CPU oracle, through the C ABI (libds3.so).
+
+Every case draws its inputs from `synth`, runs the HIP path and the oracle on the same inputs in lockstep
+(teacher-forced by the oracle's greedy token), and checks every logit of every step and the K/V state:
+max-abs <= 1e-4 with fp32 weights and state, <= 2e-2 with bf16 weights (fp32 accumulate); greedy ids equal
+wherever the oracle's top-2 margin exceeds 5e-2; any non-finite GPU value where the oracle is finite fails.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import synth
+from tests.ds3_testlib import Lockstep, log, make_engine
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_greedy(w, ws, steps, start_pos, exec_mode="graph", prefill_kv=0, check_kv_every=0):
+    eng = make_engine(w, ws, exec_mode)
+    try:
+        ls = Lockstep(w, ws, eng)
+        if prefill_kv:
+            ls.prefill_random_kv([prefill_kv] * w.rows)
+        tokens = synth.start_tokens(w)
+        pos = np.array(start_pos, dtype=np.int32)
+        for i in range(steps):
+            _, ref, _ = ls.step(tokens, pos)
+            tokens = np.array([int(np.argmax(ref[r])) for r in range(w.rows)], np.int32)
+            if check_kv_every and (i % check_kv_every == 0 or i == steps - 1):
+                for li in (0, w.model.n_layers - 1):
+                    for r in range(w.rows):
+                        ls.check_kv(li, r, int(pos[r]), 1)
+            pos = pos + 1
+        log(w.name, exec_mode, "steps", steps, "max logits err", f"{ls.max_err:.3e}", "greedy checked",
+            ls.greedy_checked, "flips inside margin", ls.greedy_flips_inside_margin)
+        return ls, eng
+    except BaseException:
+        eng.close()
+        raise
+
+
+@pytest.mark.parametrize("exec_mode", ["graph", "eager"])
+def test_tiny_fp32_64_greedy_steps(exec_mode):
+    """Tiny fp32 decoder: 64 greedy steps from position 0, every logit within 1e-4, KV state within 1e-4."""
+    w = synth.workload("tiny-fp32")
+    ws = synth.make_weights(w.model)
+    ls, eng = _run_greedy(w, ws, w.steps, synth.start_positions(w), exec_mode, check_kv_every=8)
+    try:
+        for li in range(w.model.n_layers):
+            ls.check_kv(li, 0, 0, w.steps)
+        assert ls.greedy_checked > 0
+    finally:
+        eng.close()
+
+
+def test_tiny_fp32_random_gains_and_tail_capacity():
+    """Gains 1 + N(0, 0.1) exercise the norm multiply; cap 100 leaves a ragged last split of the sweep."""
+    w = replace(synth.workload("tiny-fp32"), cap=100, name="tiny-fp32-cap100")
+    ws = synth.make_weights(w.model, gains="random")
+    ls, eng = _run_greedy(w, ws, 12, [86], prefill_kv=86)
+    try:
+        ls.check_kv(1, 0, 86, 12)
+        # maximum position: cap - 1
+        tok = np.array([3], np.int32)
+        ls.step(tok, np.array([99], np.int32))
+    finally:
+        eng.close()
+
+
+def test_llama1b_shape_two_layers():
+    """1B-shaped layers (GQA 32/8 x 64, FFN 8192, vocab 32000, cap 4096, bf16) with 2 layers: 40 steps."""
+    w = synth.small_variant(synth.workload("llama1b-bf16"), n_layers=2)
+    ws = synth.make_weights(w.model, gains="random")
+    ls, eng = _run_greedy(w, ws, 40, [300], prefill_kv=300, check_kv_every=10)
+    eng.close()
+
+
+def test_llama8b_shape_two_layers_multi_row():
+    """8B-shaped layers (hd 128, GQA 4) with 2 layers, 2 rows at different positions, small vocab."""
+    base = synth.workload("llama8b-bf16-cap8192")
+    w = replace(synth.small_variant(base, n_layers=2, vocab=4096), rows=2, name="llama8b-2l-2rows")
+    ws = synth.make_weights(w.model, gains="random")
+    eng = make_engine(w, ws)
+    try:
+        ls = Lockstep(w, ws, eng)
+        ls.prefill_random_kv([2048, 8000])
+        tokens = synth.start_tokens(w)
+        pos = np.array([2048, 8000], np.int32)
+        for _ in range(6):
+            _, ref, _ = ls.step(tokens, pos)
+            tokens = ref.argmax(axis=1).astype(np.int32)
+            for r in range(2):
+                ls.check_kv(1, r, int(pos[r]), 1)
+            pos += 1
+        log("llama8b-2l-2rows max err", f"{ls.max_err:.3e}")
+    finally:
+        eng.close()
+
+
+def _one_layer_case(cap=512, rows=1):
+    base = synth.workload("llama8b-bf16-cap8192")
+    w = replace(synth.small_variant(base, n_layers=1, vocab=2048, cap=cap), rows=rows, name="llama8b-1l")
+    ws = synth.make_weights(w.model, gains="random")
+    return w, ws
+
+
+def test_replay_equals_eager_bit_exact_and_no_stale_scalars():
+    """Capture at one position, replay at others: bit-identical to eager launches at those positions."""
+    w, ws = _one_layer_case()
+    g = make_engine(w, ws, "graph")
+    e = make_engine(w, ws, "eager")
+    try:
+        for eng in (g, e):
+            Lockstep(w, ws, eng).prefill_random_kv([200])
+        for p, t in [(200, 5), (201, 17), (350, 9), (0, 1), (511, 2047)]:
+            a, _ = g.step([t], [p])
+            a = a.copy()
+            b, _ = e.step([t], [p])
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"replay differs from eager at pos {p}"
+        assert g.stats()["captures"] == 1 and g.stats()["replays"] == 5
+    finally:
+        g.close()
+        e.close()
+
+
+def test_garbage_after_position_does_not_leak():
+    """K/V contents after pos (huge values, NaN, +-inf) leave the logits bit-identical."""
+    w, ws = _one_layer_case()
+    eng = make_engine(w, ws)
+    try:
+        ls = Lockstep(w, ws, eng)
+        ls.prefill_random_kv([300])
+        clean, _ = eng.step([7], [300])
+        clean = clean.copy()
+        rng = np.random.default_rng(0)
+        n = w.cap - 301
+        nkv, hd = w.model.n_kv_heads, w.model.head_dim
+        huge = synth.f32_to_bf16_words((rng.standard_normal((nkv, n, hd)) * 1e4).astype(np.float32))
+        specials = np.array([0x7fc0, 0x7f80, 0xff80], np.uint16)      # NaN, +inf, -inf
+        weird = rng.choice(specials, (nkv, n, hd))
+        for garbage in (huge, weird):
+            eng.write_kv(0, 0, 301, garbage, garbage)
+            # rewrite the prefix so the step at 300 sees the same visible state as before
+            ls.prefill_random_kv([300])
+            got, flags = eng.step([7], [300])
+            assert flags == 0
+            assert np.array_equal(got.view(np.uint32), clean.view(np.uint32))
+    finally:
+        eng.close()
+
+
+def test_positions_need_not_be_consecutive():
+    """Absolute positions: steps at 10, 400, 11 each attend over exactly 0..pos."""
+    w, ws = _one_layer_case()
+    eng = make_engine(w, ws)
+    try:
+        ls = Lockstep(w, ws, eng)
+        ls.prefill_random_kv([450])
+        for p in (10, 400, 11, 449):
+            ls.step(np.array([p % 97], np.int32), np.array([p], np.int32))
+    finally:
+        eng.close()
+
+
+def test_capacity_not_multiple_of_split():
+    """A capacity that is not a multiple of any split length: ragged last split, positions up to cap - 1."""
+    w, ws = _one_layer_case(cap=1000)
+    eng = make_engine(w, ws)
+    try:
+        ls = Lockstep(w, ws, eng)
+        ls.prefill_random_kv([997])
+        for p in (997, 998, 999):
+            ls.step(np.array([5], np.int32), np.array([p], np.int32))
+        ls.check_kv(0, 0, 997, 3)
+    finally:
+        eng.close()
