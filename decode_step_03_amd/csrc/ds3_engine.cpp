@@ -8,6 +8,7 @@
 #include <chrono>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <thread>
@@ -150,28 +151,38 @@ std::string check_config(const ds3_config* c) {
   } else if (c->kv_layout != DS3_KV_CONTIGUOUS) {
     return "kv_layout must be DS3_KV_CONTIGUOUS or DS3_KV_PAGED";
   }
-  const int kmax = std::max(std::max(c->d_model, c->ffn_dim), c->n_q_heads * c->head_dim);
-  if (gemv_lds_bytes(c->rows, kmax) > 160 * 1024) return "rows * max(d_model, ffn_dim, q width) * 4 exceeds 160 KB LDS";
+  const int kres = std::max(c->ffn_dim, c->n_q_heads * c->head_dim);
+  if (gemv_lds_bytes(c->rows, c->d_model, true) > 160 * 1024 || gemv_lds_bytes(c->rows, kres, false) > 160 * 1024)
+    return "rows: activations of rows x max(d_model, ffn_dim, q width) floats exceed the 160 KB LDS";
   return "";
 }
 
-// attention split plan: ~2 blocks per CU, each split a multiple of the positions one block pass covers
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  const int x = std::atoi(v);
+  return x > 0 ? x : dflt;
+}
+
+// Attention split plan: about DS3_ATTN_BLOCKS blocks (default 512, two per CU) over rows x kv heads x splits,
+// each split a whole number of the positions one block pass covers, LDS per block kept within 64 KB.
 void plan_splits(const ds3_config& c, int* splits, int* split_len) {
   const int ppp = attn_positions_per_pass(c.head_dim, c.kv_dtype);
   const int units = (c.cap + ppp - 1) / ppp;         // passes over the whole capacity
-  const int target_blocks = 512;
+  const int target_blocks = env_int("DS3_ATTN_BLOCKS", 512);
   int s = std::max(1, target_blocks / (c.rows * c.n_kv_heads));
   s = std::min(s, units);
   int per = (units + s - 1) / s;                     // passes per split
-  int len = per * ppp;
-  // keep the LDS of one block small (scores for G heads)
   const int G = c.n_q_heads / c.n_kv_heads;
-  while ((size_t)G * len * 4 > 64 * 1024 && per > 1) {
+  for (;;) {
+    const int len = per * ppp;
+    const int sp = (c.cap + len - 1) / len;
+    if (per == 1 || attn_lds_bytes(c.n_q_heads, c.n_kv_heads, c.head_dim, len, sp) <= 64 * 1024) break;
     --per;
-    len = per * ppp;
   }
-  *split_len = len;
-  *splits = (c.cap + len - 1) / len;
+  (void)G;
+  *split_len = per * ppp;
+  *splits = (c.cap + *split_len - 1) / *split_len;
 }
 
 WorkPlan plan_work(const ds3_config& c, int splits) {
@@ -395,7 +406,7 @@ ds3_status ensure_captured(ds3_engine* e) {
   hipGraph_t g = nullptr;
   hipError_t h2 = hipStreamEndCapture(e->stream, &g);
   if (h != hipSuccess || h2 != hipSuccess) {
-    if (g) hipGraphDestroy(g);
+    if (g) (void)hipGraphDestroy(g);
     return poison(e, DS3_E_DEVICE_LOST,
                   std::string("graph capture: ") + hipGetErrorString(h != hipSuccess ? h : h2));
   }
@@ -505,7 +516,7 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   e->kv.slot_map = e->slot_map;
 
   // launch shapes
-  const int max_blocks = 1024;
+  const int max_blocks = env_int("DS3_GEMV_BLOCKS", 1024);
   e->blocks[K_QKV] = gemv_blocks((c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim / 2, max_blocks);
   e->blocks[K_OPROJ] = gemv_blocks(c.d_model / 2, max_blocks);
   e->blocks[K_GATEUP] = gemv_blocks(c.ffn_dim, max_blocks);

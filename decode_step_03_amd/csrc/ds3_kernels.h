@@ -105,8 +105,8 @@ hipError_t launch_kv_copy(const KvView& kv, int kv_dtype, int layer, int row, in
                           void* staging, int to_state, StatusWords* status, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t s);
 
-size_t gemv_lds_bytes(int rows, int K);
+size_t gemv_lds_bytes(int rows, int K, bool norm);
 int attn_positions_per_pass(int hd, int kv_dtype);
-size_t attn_lds_bytes(int nq, int nkv, int hd, int split_len);
+size_t attn_lds_bytes(int nq, int nkv, int hd, int split_len, int splits);
 
 }  // namespace ds3

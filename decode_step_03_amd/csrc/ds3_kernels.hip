@@ -118,54 +118,28 @@ __global__ void __launch_bounds__(kBlock) embed_kernel(EmbedParams p) {
 // Each wave owns one pair of weight rows at a time and computes both rows' dot products with every activation
 // row (NR of them) held in LDS as fp32. A pair is the unit the epilogue needs: the two halves of a rotary pair
 // (element i and element i + hd/2 of a q or k head), a gate row and its up row, or two adjacent output rows.
-// The weight rows are read once per step with 16-byte non-temporal loads, kUnroll chunks of 64 lanes x 16 bytes
-// in flight per row; the reduction over the row is a fixed-order wave butterfly.
+//
+// Latency is what limits these short kernels, so the order of memory operations is deliberate:
+//   1. every thread loads its share of the activation (and, for the norm modes, the RMSNorm gain) into
+//      registers -- these loads go first because loads return in order;
+//   2. the wave starts streaming its first pair of weight rows (kUnroll x 16 bytes per lane per row) and the
+//      epilogue operands that live in memory;
+//   3. the activations (times the gain) go to LDS while the weights are in flight, and the RMSNorm sum of
+//      squares is reduced from the registers: one barrier, which waits for LDS traffic only;
+//   4. dot products as the weights arrive; fixed-order wave butterfly; the RMSNorm scale
+//      1/sqrt(mean(x^2) + eps) multiplies the two dot products in the epilogue.
+// No load sits behind a per-lane branch (indices are clamped instead), so nothing forces an early wait.
 
-template <typename WT, typename KT, int NR, int MODE>
-__global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
-  extern __shared__ float xs[];  // [NR][K]
-  __shared__ float red[NR][kBlock / 64];
-  constexpr int EPL = Pack<WT>::N;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int K = p.K;
-  const int chunk = 64 * EPL;
-  const int nchunks = (K + chunk - 1) / chunk;
-
-  // ---- prologue: activation rows -> LDS (RMSNorm for the norm modes)
-  if constexpr (MODE == GEMV_RESID) {
-    for (int i = tid; i < NR * K; i += kBlock) xs[i] = p.in[i];
-  } else {
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      float ss = 0.f;
-      for (int k = tid; k < K; k += kBlock) {
-        const float v = p.in[(size_t)r * K + k];
-        ss += v * v;
-      }
-      ss = wave_sum(ss);
-      if (lane == 0) red[r][wid] = ss;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const float tot = (red[r][0] + red[r][1]) + (red[r][2] + red[r][3]);
-      const float scale = 1.0f / sqrtf(tot / (float)K + p.eps);
-      for (int k = tid; k < K; k += kBlock) xs[r * K + k] = p.in[(size_t)r * K + k] * scale * p.gain[k];
-    }
-  }
-  __syncthreads();
-
-  const SlotLayout sl{p.rows};
-  const int nwaves = gridDim.x * (kBlock / 64);
-  for (int pair = blockIdx.x * (kBlock / 64) + wid; pair < p.n_pairs; pair += nwaves) {
-    // ---- which two weight rows this pair reads
-    int row0, row1;
-    int seg = 0, head = 0, idx = 0;   // QKV: segment 0 q / 1 k / 2 v, head, element index within the head
+template <int MODE>
+struct PairMap {
+  int row0, row1;
+  int seg, head, idx;   // QKV: segment 0 q / 1 k / 2 v, head, element within the head
+  __device__ __forceinline__ PairMap(const GemvParams& p, int pair) : seg(0), head(0), idx(0) {
     if constexpr (MODE == GEMV_QKV) {
       const int half = p.hd / 2;
       const int nqp = p.nq * half, nkp = p.nkv * half;
       if (pair < nqp) {
-        seg = 0; head = pair / half; idx = pair % half;
+        head = pair / half; idx = pair % half;
         row0 = head * p.hd + idx; row1 = row0 + half;
       } else if (pair < nqp + nkp) {
         const int pp = pair - nqp;
@@ -181,43 +155,187 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
     } else {
       row0 = 2 * pair; row1 = row0 + 1;
     }
-    const WT* w0 = reinterpret_cast<const WT*>(p.w) + (size_t)row0 * K;
-    const WT* w1 = reinterpret_cast<const WT*>(p.w) + (size_t)row1 * K;
+  }
+};
 
+// Loads of one group of kUnroll chunks of two weight rows. Past the row's end the chunk index is clamped to the
+// last chunk and the element index to the last 16 bytes: in bounds, no branches; fma_group zeroes them.
+template <typename WT>
+__device__ __forceinline__ void load_group(const WT* w0, const WT* w1, int c0, int nchunks, int K, int lane,
+                                           u32x4 (&b0)[kUnroll], u32x4 (&b1)[kUnroll]) {
+  constexpr int EPL = Pack<WT>::N;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int k = min(min(c0 + u, nchunks - 1) * (64 * EPL) + lane * EPL, K - EPL);
+    b0[u] = load_stream(w0 + k);
+    b1[u] = load_stream(w1 + k);
+  }
+}
+
+template <typename WT, int NR>
+__device__ __forceinline__ void fma_group(const u32x4 (&b0)[kUnroll], const u32x4 (&b1)[kUnroll], const float* xs,
+                                          int c0, int nchunks, int K, int lane, float (&a0)[NR], float (&a1)[NR]) {
+  constexpr int EPL = Pack<WT>::N;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int kr = (c0 + u) * (64 * EPL) + lane * EPL;
+    const bool valid = c0 + u < nchunks && kr < K;
+    const int k = min(min(c0 + u, nchunks - 1) * (64 * EPL) + lane * EPL, K - EPL);
+    float f0[EPL], f1[EPL];
+    Pack<WT>::widen(b0[u], f0);
+    Pack<WT>::widen(b1[u], f1);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      f0[e] = valid ? f0[e] : 0.f;
+      f1[e] = valid ? f1[e] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const float* xr = xs + r * K + k;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        a0[r] = fmaf(f0[e], xr[e], a0[r]);
+        a1[r] = fmaf(f1[e], xr[e], a1[r]);
+      }
+    }
+  }
+}
+
+template <typename WT, typename KT, int NR, int MODE, int XREG>
+__global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
+  extern __shared__ float xs[];  // [NR][K] activations (times the gain in the norm modes)
+  __shared__ float red[NR][kBlock / 64];
+  constexpr bool kNorm = MODE != GEMV_RESID;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int K = p.K;
+  const int K4 = K / 4;
+  const int nchunks = (K + 64 * Pack<WT>::N - 1) / (64 * Pack<WT>::N);
+  const int nwaves = gridDim.x * (kBlock / 64);
+  const SlotLayout sl{p.rows};
+
+  // ---- 1. slot positions, then activation (and gain) loads, first
+  int posr[NR];
+  bool pos_ok[NR];
+  if constexpr (MODE == GEMV_QKV) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int ps = p.slots[sl.pos() + r];
+      pos_ok[r] = ps >= 0 && ps < p.kv.cap;
+      posr[r] = pos_ok[r] ? ps : 0;
+    }
+  }
+  const int n4 = NR * K4;
+  const float4* in4 = reinterpret_cast<const float4*>(p.in);
+  const float4* g4 = reinterpret_cast<const float4*>(kNorm ? p.gain : p.in);
+  float4 xv[XREG], gv[kNorm ? XREG : 1];
+#pragma unroll
+  for (int u = 0; u < XREG; ++u) {
+    const int i = min(tid + u * kBlock, n4 - 1);
+    xv[u] = in4[i];
+    if constexpr (kNorm) gv[u] = g4[i % K4];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 2. the first pair's weights (they do not depend on the activations) and its epilogue operands
+  const WT* wbase = reinterpret_cast<const WT*>(p.w);
+  u32x4 b0[kUnroll], b1[kUnroll];
+  float ea[NR], eb[NR];
+  int pair = blockIdx.x * (kBlock / 64) + wid;
+  PairMap<MODE> pm(p, min(pair, p.n_pairs - 1));
+  const WT* w0 = wbase + (size_t)pm.row0 * K;
+  const WT* w1 = wbase + (size_t)pm.row1 * K;
+  auto fetch_epilogue = [&ea, &eb, &p, &posr](const PairMap<MODE>& m, int pr) {
+    (void)p;
+    (void)posr;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) { ea[r] = 0.f; eb[r] = 0.f; }
+    if constexpr (MODE == GEMV_QKV) {
+      if (m.seg != 2) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const float2 cs = reinterpret_cast<const float2*>(p.rope)[(size_t)posr[r] * (p.hd / 2) + m.idx];
+          ea[r] = cs.x;
+          eb[r] = cs.y;
+        }
+      }
+    } else if constexpr (MODE == GEMV_RESID) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const float2 xo = reinterpret_cast<const float2*>(p.out + (size_t)r * 2 * p.n_pairs)[pr];
+        ea[r] = xo.x;
+        eb[r] = xo.y;
+      }
+    }
+  };
+  // unconditional (the pair index is clamped): a branch here would make every later wait conservative
+  load_group<WT>(w0, w1, 0, nchunks, K, lane, b0, b1);
+  fetch_epilogue(pm, min(pair, p.n_pairs - 1));
+
+  // ---- 3. LDS fill (clamped lanes rewrite the same value) and the RMSNorm sums of squares
+  float4* xs4 = reinterpret_cast<float4*>(xs);
+  float ss[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) ss[r] = 0.f;
+#pragma unroll
+  for (int u = 0; u < XREG; ++u) {
+    const int iu = tid + u * kBlock;
+    const int i = min(iu, n4 - 1);
+    float4 v = xv[u];
+    if constexpr (kNorm) {
+      const float sq = (iu < n4) ? v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w : 0.f;
+      const int row = i / K4;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) ss[r] += (row == r) ? sq : 0.f;
+      v = make_float4(v.x * gv[u].x, v.y * gv[u].y, v.z * gv[u].z, v.w * gv[u].w);
+    }
+    xs4[i] = v;
+  }
+  for (int i = tid + XREG * kBlock; i < n4; i += kBlock) {   // activations beyond the register share, if any
+    float4 v = in4[i];
+    if constexpr (kNorm) {
+      const float4 gg = g4[i % K4];
+      const float sq = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) ss[r] += (i / K4 == r) ? sq : 0.f;
+      v = make_float4(v.x * gg.x, v.y * gg.y, v.z * gg.z, v.w * gg.w);
+    }
+    xs4[i] = v;
+  }
+  if constexpr (kNorm) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const float t = wave_sum(ss[r]);
+      if (lane == 0) red[r][wid] = t;
+    }
+  }
+  __syncthreads();
+  float scale[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    scale[r] = 1.f;
+    if constexpr (kNorm) {
+      const float tot = (red[r][0] + red[r][1]) + (red[r][2] + red[r][3]);
+      scale[r] = 1.0f / sqrtf(tot / (float)K + p.eps);
+    }
+  }
+
+  // ---- 4. pairs
+  bool first = true;
+  for (; pair < p.n_pairs; pair += nwaves) {
+    if (!first) {
+      pm = PairMap<MODE>(p, pair);
+      w0 = wbase + (size_t)pm.row0 * K;
+      w1 = wbase + (size_t)pm.row1 * K;
+      load_group<WT>(w0, w1, 0, nchunks, K, lane, b0, b1);
+      fetch_epilogue(pm, pair);
+    }
+    first = false;
     float a0[NR], a1[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) { a0[r] = 0.f; a1[r] = 0.f; }
-
     for (int c0 = 0; c0 < nchunks; c0 += kUnroll) {
-      u32x4 b0[kUnroll], b1[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int k = (c0 + u) * chunk + lane * EPL;
-        b0[u] = u32x4{0u, 0u, 0u, 0u};
-        b1[u] = u32x4{0u, 0u, 0u, 0u};
-        if (c0 + u < nchunks && k < K) {
-          b0[u] = load_stream(w0 + k);
-          b1[u] = load_stream(w1 + k);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int k = (c0 + u) * chunk + lane * EPL;
-        if (c0 + u < nchunks && k < K) {
-          float f0[EPL], f1[EPL];
-          Pack<WT>::widen(b0[u], f0);
-          Pack<WT>::widen(b1[u], f1);
-#pragma unroll
-          for (int r = 0; r < NR; ++r) {
-            const float* xr = xs + r * K + k;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-              a0[r] = fmaf(f0[e], xr[e], a0[r]);
-              a1[r] = fmaf(f1[e], xr[e], a1[r]);
-            }
-          }
-        }
-      }
+      if (c0 > 0) load_group<WT>(w0, w1, c0, nchunks, K, lane, b0, b1);
+      fma_group<WT, NR>(b0, b1, xs, c0, nchunks, K, lane, a0, a1);
     }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -229,61 +347,44 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
     // ---- epilogue (lane 0)
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      const float a = a0[r], b = a1[r];
+      const float a = a0[r] * scale[r], b = a1[r] * scale[r];
       if constexpr (MODE == GEMV_QKV) {
-        int pos = p.slots[sl.pos() + r];
-        bool ok = true;
-        if (pos < 0 || pos >= p.kv.cap) { raise_error(p.status, ERR_POS); pos = 0; ok = false; }
+        if (!pos_ok[r]) raise_error(p.status, ERR_POS);
         const int half = p.hd / 2;
-        if (seg == 2) {
-          // value rows: no rotation
-          if (ok) {
-            size_t off;
-            if (!p.kv.paged) {
-              off = ((size_t)(r * p.nkv + head) * p.kv.cap + pos) * p.hd;
-            } else {
-              const int slot = p.slots[sl.write_map() + r];
-              if (slot < 0 || slot >= p.kv.pool_pages * p.kv.page_size) { raise_error(p.status, ERR_WRITE_MAP); continue; }
-              off = ((size_t)((slot / p.kv.page_size) * p.nkv + head) * p.kv.page_size + slot % p.kv.page_size) * p.hd;
-            }
-            KT* vp = reinterpret_cast<KT*>(p.kv.v) + (size_t)p.layer * p.kv.layer_stride + off + idx;
-            store_kv(vp, a);
-            store_kv(vp + 1, b);
-          }
-        } else {
-          const float c = p.rope[((size_t)pos * half + idx) * 2];
-          const float s = p.rope[((size_t)pos * half + idx) * 2 + 1];
-          const float ra = a * c - b * s;
-          const float rb = a * s + b * c;
-          if (seg == 0) {
-            float* q = p.out + ((size_t)r * p.nq + head) * p.hd;
-            q[idx] = ra;
-            q[idx + half] = rb;
-          } else if (ok) {
-            size_t off;
-            if (!p.kv.paged) {
-              off = ((size_t)(r * p.nkv + head) * p.kv.cap + pos) * p.hd;
-            } else {
-              const int slot = p.slots[sl.write_map() + r];
-              if (slot < 0 || slot >= p.kv.pool_pages * p.kv.page_size) { raise_error(p.status, ERR_WRITE_MAP); continue; }
-              off = ((size_t)((slot / p.kv.page_size) * p.nkv + head) * p.kv.page_size + slot % p.kv.page_size) * p.hd;
-            }
-            KT* kp = reinterpret_cast<KT*>(p.kv.k) + (size_t)p.layer * p.kv.layer_stride + off + idx;
-            store_kv(kp, ra);
-            store_kv(kp + half, rb);
-          }
+        float va = a, vb = b;
+        if (pm.seg != 2) {   // rotate the pair (element idx, element idx + hd/2) by the angle of Slot::Pos
+          va = a * ea[r] - b * eb[r];
+          vb = a * eb[r] + b * ea[r];
         }
+        if (pm.seg == 0) {
+          float* q = p.out + ((size_t)r * p.nq + pm.head) * p.hd;
+          q[pm.idx] = va;
+          q[pm.idx + half] = vb;
+          continue;
+        }
+        if (!pos_ok[r]) continue;
+        size_t off;
+        if (!p.kv.paged) {
+          off = ((size_t)(r * p.nkv + pm.head) * p.kv.cap + posr[r]) * p.hd;
+        } else {
+          const int slot = p.slots[sl.write_map() + r];
+          if (slot < 0 || slot >= p.kv.pool_pages * p.kv.page_size) { raise_error(p.status, ERR_WRITE_MAP); continue; }
+          off = ((size_t)((slot / p.kv.page_size) * p.nkv + pm.head) * p.kv.page_size + slot % p.kv.page_size) * p.hd;
+        }
+        // k: the two halves of a rotary pair; v: two adjacent elements
+        KT* dst = reinterpret_cast<KT*>(pm.seg == 1 ? p.kv.k : p.kv.v) + (size_t)p.layer * p.kv.layer_stride + off +
+                  pm.idx;
+        store_kv(dst, va);
+        store_kv(dst + (pm.seg == 1 ? half : 1), vb);
       } else if constexpr (MODE == GEMV_GATEUP) {
         const float silu = a / (1.0f + expf(-a));
         p.out[(size_t)r * p.n_pairs + pair] = silu * b;
       } else if constexpr (MODE == GEMV_RESID) {
-        float* x = p.out + (size_t)r * 2 * p.n_pairs + 2 * pair;
-        x[0] += a;
-        x[1] += b;
+        float2* x = reinterpret_cast<float2*>(p.out + (size_t)r * 2 * p.n_pairs) + pair;
+        *x = make_float2(ea[r] + a, eb[r] + b);
       } else {  // GEMV_HEAD
-        float* lg = p.out + (size_t)r * 2 * p.n_pairs + 2 * pair;
-        lg[0] = a;
-        lg[1] = b;
+        float2* lg = reinterpret_cast<float2*>(p.out + (size_t)r * 2 * p.n_pairs) + pair;
+        *lg = make_float2(a, b);
         if (!isfinite(a) || !isfinite(b)) atomicOr(&p.status->nonfinite, 1u);
       }
     }
@@ -308,11 +409,13 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
   constexpr int EPL = Pack<KT>::N;
   constexpr int LPP = HD / EPL;         // lanes per position
   constexpr int PPP = kBlock / LPP;     // positions per block pass
-  constexpr int UA = 4;                 // passes in flight
+  constexpr int UA = 8;                 // passes in flight
   static_assert(LPP >= 1 && LPP <= 64 && (64 % LPP) == 0, "lanes per position must divide the wave");
   extern __shared__ float sm[];
   float* sc = sm;                       // [G][T] scores, then weights
   float* ow = sm + G * p.split_len;     // [4 waves][G][HD]
+  float* mstat = ow + 4 * G * HD;       // merge: [G][S] split maxima, then merge weights
+  float* lstat = mstat + G * p.splits;  // merge: [G][S] split sums
   __shared__ float s_m[G], s_l[G];
   __shared__ int s_last;
 
@@ -347,7 +450,10 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
       const int t = t0 + u * PPP + grp;
       const int j = j0 + t;
       kb[u] = u32x4{0u, 0u, 0u, 0u};
-      if (t < T && j < cap) kb[u] = load_stream(Kb + kv_offset(p.kv, r, p.nkv, g, j, HD, p.status) + sub * EPL);
+      if (t0 + u * PPP < T) {   // uniform: T is a whole number of passes
+        const int jj = min(j, cap - 1);   // past the capacity: a clamped, masked re-read
+        kb[u] = load_stream(Kb + kv_offset(p.kv, r, p.nkv, g, jj, HD, p.status) + sub * EPL);
+      }
     }
 #pragma unroll
     for (int u = 0; u < UA; ++u) {
@@ -403,7 +509,10 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
       const int t = t0 + u * PPP + grp;
       const int j = j0 + t;
       vb[u] = u32x4{0u, 0u, 0u, 0u};
-      if (t < T && j < cap) vb[u] = load_stream(Vb + kv_offset(p.kv, r, p.nkv, g, j, HD, p.status) + sub * EPL);
+      if (t0 + u * PPP < T) {
+        const int jj = min(j, cap - 1);
+        vb[u] = load_stream(Vb + kv_offset(p.kv, r, p.nkv, g, jj, HD, p.status) + sub * EPL);
+      }
     }
 #pragma unroll
     for (int u = 0; u < UA; ++u) {
@@ -466,24 +575,36 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
+  __threadfence();   // acquire: every split's partials are visible to plain loads from here on
+  for (int i = tid; i < G * S; i += kBlock) {
+    const int hh = i / S, s2 = i % S;
+    const float* ps = part + (size_t)s2 * (G * (HD + 2)) + hh * (HD + 2);
+    mstat[i] = ps[HD];
+    lstat[i] = ps[HD + 1];
+  }
+  __syncthreads();
+  for (int hh = wid; hh < G; hh += kBlock / 64) {
+    float M = -INFINITY;
+    for (int s2 = lane; s2 < S; s2 += 64) M = fmaxf(M, mstat[hh * S + s2]);
+    M = wave_max(M);
+    float L = 0.f;
+    for (int s2 = lane; s2 < S; s2 += 64) {
+      const float ms = mstat[hh * S + s2];
+      const float wgt = (ms == -INFINITY) ? 0.f : expf(ms - M);
+      mstat[hh * S + s2] = wgt;
+      L += wgt * lstat[hh * S + s2];
+    }
+    L = wave_sum(L);
+    if (lane == 0) s_l[hh] = L;
+  }
+  __syncthreads();
   for (int i = tid; i < G * HD; i += kBlock) {
     const int hh = i / HD, dd = i % HD;
-    float M = -INFINITY;
-    for (int s2 = 0; s2 < S; ++s2)
-      M = fmaxf(M, __hip_atomic_load(part + (size_t)s2 * (G * (HD + 2)) + hh * (HD + 2) + HD, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT));
-    float L = 0.f, acc = 0.f;
-    for (int s2 = 0; s2 < S; ++s2) {
-      const float* ps = part + (size_t)s2 * (G * (HD + 2)) + hh * (HD + 2);
-      const float ms = __hip_atomic_load(ps + HD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float ls = __hip_atomic_load(ps + HD + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float os = __hip_atomic_load(ps + dd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float w = (ms == -INFINITY) ? 0.f : expf(ms - M);
-      L += w * ls;
-      acc += w * os;
-    }
-    p.out[((size_t)r * p.nq + g * G + hh) * HD + dd] = acc / L;
+    const float* po = part + hh * (HD + 2) + dd;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int s2 = 0; s2 < S; ++s2) acc = fmaf(mstat[hh * S + s2], po[(size_t)s2 * (G * (HD + 2))], acc);
+    p.out[((size_t)r * p.nq + g * G + hh) * HD + dd] = acc / s_l[hh];
   }
   if (tid == 0) __hip_atomic_store(&p.counters[r * p.nkv + g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -517,16 +638,16 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t value, size_t n) {
 // ----------------------------------------------------------------------------------------------------------
 // host launchers
 
-size_t gemv_lds_bytes(int rows, int K) { return (size_t)rows * K * sizeof(float); }
+size_t gemv_lds_bytes(int rows, int K, bool norm) { (void)norm; return (size_t)rows * K * sizeof(float); }
 
 int attn_positions_per_pass(int hd, int kv_dtype) {
   const int epl = kv_dtype == 1 ? 8 : 4;
   return kBlock / (hd / epl);
 }
 
-size_t attn_lds_bytes(int nq, int nkv, int hd, int split_len) {
+size_t attn_lds_bytes(int nq, int nkv, int hd, int split_len, int splits) {
   const int G = nq / nkv;
-  return ((size_t)G * split_len + (size_t)4 * G * hd) * sizeof(float);
+  return ((size_t)G * split_len + (size_t)4 * G * hd + (size_t)2 * G * splits) * sizeof(float);
 }
 
 template <typename F>
@@ -542,35 +663,47 @@ hipError_t launch_embed(const EmbedParams& p, int weight_dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename WT, typename KT, int MODE, int NR, int XREG>
+static hipError_t gemv_go(const GemvParams& p, int blocks, hipStream_t s) {
+  auto* f = gemv_kernel<WT, KT, NR, MODE, XREG>;
+  const size_t lds = gemv_lds_bytes(p.rows, p.K, MODE != GEMV_RESID);
+  hipError_t e = set_lds(f, lds);
+  if (e != hipSuccess) return e;
+  f<<<blocks, kBlock, lds, s>>>(p);
+  return hipGetLastError();
+}
+
+// Register share of the activation per thread: the norm modes hold rows x d_model / 1024 float4 (4 per row for
+// d_model = 4096); the residual modes hold up to 16 float4 (K up to 16384 at one row). The rest, if any, is
+// loaded in a loop.
 template <typename WT, typename KT, int MODE>
 static hipError_t gemv_rows(const GemvParams& p, int blocks, hipStream_t s) {
-  const size_t lds = gemv_lds_bytes(p.rows, p.K);
-  switch (p.rows) {
-#define DS3_CASE(NR)                                                                 \
-  case NR: {                                                                         \
-    auto* f = gemv_kernel<WT, KT, NR, MODE>;                                         \
-    hipError_t e = set_lds(f, lds);                                                  \
-    if (e != hipSuccess) return e;                                                   \
-    f<<<blocks, kBlock, lds, s>>>(p);                                                \
-    return hipGetLastError();                                                        \
+  if constexpr (MODE != GEMV_RESID) {
+    switch (p.rows) {
+      case 1: return gemv_go<WT, KT, MODE, 1, 4>(p, blocks, s);
+      case 2: return gemv_go<WT, KT, MODE, 2, 8>(p, blocks, s);
+      case 3: return gemv_go<WT, KT, MODE, 3, 12>(p, blocks, s);
+      case 4: return gemv_go<WT, KT, MODE, 4, 16>(p, blocks, s);
+    }
+  } else {
+    const bool small = p.rows * p.K <= 4 * 4 * kBlock;   // fits 4 float4 per thread
+    switch (p.rows) {
+      case 1: return small ? gemv_go<WT, KT, MODE, 1, 4>(p, blocks, s) : gemv_go<WT, KT, MODE, 1, 16>(p, blocks, s);
+      case 2: return gemv_go<WT, KT, MODE, 2, 16>(p, blocks, s);
+      case 3: return gemv_go<WT, KT, MODE, 3, 16>(p, blocks, s);
+      case 4: return gemv_go<WT, KT, MODE, 4, 16>(p, blocks, s);
+    }
   }
-    DS3_CASE(1)
-    DS3_CASE(2)
-    DS3_CASE(3)
-    DS3_CASE(4)
-#undef DS3_CASE
-    default:
-      return hipErrorInvalidValue;
-  }
+  return hipErrorInvalidValue;
 }
 
 template <typename WT, typename KT>
 static hipError_t gemv_mode(const GemvParams& p, int mode, int blocks, hipStream_t s) {
   switch (mode) {
     case GEMV_QKV: return gemv_rows<WT, KT, GEMV_QKV>(p, blocks, s);
-    case GEMV_GATEUP: return gemv_rows<WT, KT, GEMV_GATEUP>(p, blocks, s);
-    case GEMV_RESID: return gemv_rows<WT, KT, GEMV_RESID>(p, blocks, s);
-    case GEMV_HEAD: return gemv_rows<WT, KT, GEMV_HEAD>(p, blocks, s);
+    case GEMV_GATEUP: return gemv_rows<WT, WT, GEMV_GATEUP>(p, blocks, s);
+    case GEMV_RESID: return gemv_rows<WT, WT, GEMV_RESID>(p, blocks, s);
+    case GEMV_HEAD: return gemv_rows<WT, WT, GEMV_HEAD>(p, blocks, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -586,7 +719,7 @@ hipError_t launch_gemv(const GemvParams& p, int mode, int weight_dtype, int kv_d
 template <typename KT, int HD>
 static hipError_t attn_g(const AttnParams& p, int rows, hipStream_t s) {
   const int G = p.nq / p.nkv;
-  const size_t lds = attn_lds_bytes(p.nq, p.nkv, HD, p.split_len);
+  const size_t lds = attn_lds_bytes(p.nq, p.nkv, HD, p.split_len, p.splits);
   dim3 grid(p.splits, p.nkv, rows);
   switch (G) {
 #define DS3_CASE(GG)                                      \
