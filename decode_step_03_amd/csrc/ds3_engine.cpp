@@ -164,24 +164,17 @@ int env_int(const char* name, int dflt) {
   return x > 0 ? x : dflt;
 }
 
-// Attention split plan: about DS3_ATTN_BLOCKS blocks (default 512, two per CU) over rows x kv heads x splits,
-// each split a whole number of the positions one block pass covers, LDS per block kept within 64 KB.
+// Attention split plan: about DS3_ATTN_BLOCKS blocks (default 512, two per CU) over rows x kv heads x splits.
+// A split is a whole number of LDS chunks, and there are no more splits than the in-kernel merge takes.
 void plan_splits(const ds3_config& c, int* splits, int* split_len) {
-  const int ppp = attn_positions_per_pass(c.head_dim, c.kv_dtype);
-  const int units = (c.cap + ppp - 1) / ppp;         // passes over the whole capacity
+  const int chunk = attn_positions_per_pass(c.head_dim, c.kv_dtype);
+  const int units = (c.cap + chunk - 1) / chunk;
   const int target_blocks = env_int("DS3_ATTN_BLOCKS", 512);
   int s = std::max(1, target_blocks / (c.rows * c.n_kv_heads));
   s = std::min(s, units);
-  int per = (units + s - 1) / s;                     // passes per split
-  const int G = c.n_q_heads / c.n_kv_heads;
-  for (;;) {
-    const int len = per * ppp;
-    const int sp = (c.cap + len - 1) / len;
-    if (per == 1 || attn_lds_bytes(c.n_q_heads, c.n_kv_heads, c.head_dim, len, sp) <= 64 * 1024) break;
-    --per;
-  }
-  (void)G;
-  *split_len = per * ppp;
+  s = std::min(s, attn_max_splits(c.n_q_heads, c.n_kv_heads, c.head_dim));
+  const int per = (units + s - 1) / s;
+  *split_len = per * chunk;
   *splits = (c.cap + *split_len - 1) / *split_len;
 }
 
@@ -201,7 +194,8 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
   w.q = take((size_t)c.rows * c.n_q_heads * c.head_dim * 4);
   w.attn = take((size_t)c.rows * c.n_q_heads * c.head_dim * 4);
   w.act = take((size_t)c.rows * c.ffn_dim * 4);
-  w.part = take((size_t)c.rows * c.n_kv_heads * splits * G * (c.head_dim + 2) * 4);
+  const size_t sp = splits <= 4 ? 4 : (splits <= 8 ? 8 : (splits <= 16 ? 16 : 32));   // padded split index
+  w.part = take((size_t)c.rows * c.n_kv_heads * G * (c.head_dim + 2) * sp * 4);
   w.counters = take((size_t)c.rows * c.n_kv_heads * 4);
   w.rope = take((size_t)c.cap * (c.head_dim / 2) * 2 * 4);
   w.slot_map = take(c.kv_layout == DS3_KV_PAGED ? (size_t)c.rows * (c.cap / c.page_size) * 4 : 4);

@@ -28,6 +28,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 256;
 constexpr int kUnroll = 8;   // 16-byte loads in flight per lane per weight row
+constexpr int kMaxSplitsPerLane = 32;   // attention split merge: partials one lane holds in registers
+constexpr int kAttnChunk = 128;         // attention: positions staged in LDS at a time
 
 __device__ __forceinline__ u32x4 load_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -79,6 +81,29 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
   return v;
 }
+
+// Sum over aligned groups of N lanes (N = 2, 4, 8, 16, 32, 64) that leaves the identical sum in every lane of
+// the group: every step adds a partner's value, and float addition is commutative, so partners agree bit for
+// bit. Steps within a row of 16 lanes use DPP lane permutations (quad swaps, half-row and row mirrors); wider
+// steps use cross-row shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (N >= 4) v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (N >= 8) v += dpp_mov<0x141>(v);   // row_half_mirror: pairs the two quads of each 8 lanes
+  if constexpr (N >= 16) v += dpp_mov<0x140>(v);  // row_mirror: pairs the two halves of each 16 lanes
+  if constexpr (N >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (N >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// 2^x with the hardware exp (results below the normal range flush to zero, which a softmax weight can afford)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ void raise_error(StatusWords* st, uint32_t bit) { atomicOr(&st->err, bit); }
 
@@ -394,29 +419,49 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
 // ----------------------------------------------------------------------------------------------------------
 // Attention: split sweep over the whole [cap] of one (row, kv head), all G query heads of the group at once.
 //
-// grid = (splits, nkv, rows); each block owns positions [s*T, s*T + T) of one kv head.
-// Phase A: LPP lanes share one position (16 bytes of the head each); scores for the G query heads are
-//          reduced over those lanes and kept in LDS. Positions j > pos (Slot::Pos) are hidden by selection:
-//          their score becomes -inf and their value row never reaches the accumulator, so whatever the buffer
-//          holds after pos (stale data, inf, NaN) cannot leak into the result.
-// Phase B: per head, the split's max m and the weights p_j = exp(s_j - m), sum l; then o = sum_j p_j v_j.
-// Merge:   the block that arrives last for its (row, kv head) -- an integer counter decides, the order of the
-//          merge does not depend on it -- merges the splits in split order s = 0..S-1:
-//          o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, M = max_s m_s.
+// grid = (splits, nkv, rows); block = 256 threads; each block owns positions [s*T, s*T + T) of one kv head and
+// walks them in LDS chunks of kAttnChunk positions. A chunk's K and V rows are staged in LDS with direct
+// global-to-LDS 16-byte loads (no registers involved, so every load of the chunk is in flight at once), then
+// one wait and one barrier. From LDS, LPP lanes share one position (16 bytes of the head each): the G scores of
+// a position are reduced over those lanes by a butterfly (bit-identical sums in every lane) and folded into a
+// running softmax state per lane group: max m, sum l, weighted value sum o (online softmax, one rescale per UA
+// positions).
+//
+// Masking (Slot::Pos against the position index, positions after pos hidden) is done by selection: a hidden
+// position's score is -inf and its value row never reaches the accumulator, so whatever the buffer holds after
+// pos -- stale data, inf, NaN -- cannot leak into the result.
+//
+// Merges, all in a fixed order: lane groups of a wave by butterfly, the 4 waves through LDS in wave order, and
+// the splits of a (row, kv head) by the block that finishes last -- an integer counter decides which block
+// merges, not the order of the merge: o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s with M = max_s m_s.
 
-template <typename KT, int HD, int G>
+struct Lse {   // merge of two (max, sum, weighted values) states (maxima in the log2 domain); symmetric, so
+               // butterfly partners agree
+  __device__ __forceinline__ static void weights(float m1, float m2, float& M, float& w1, float& w2) {
+    M = fmaxf(m1, m2);
+    w1 = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - M);
+    w2 = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - M);
+  }
+};
+
+typedef __attribute__((address_space(1))) const void* global_cptr;
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+template <typename KT, int HD, int G, bool PAGED>
 __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
-  constexpr int EPL = Pack<KT>::N;
-  constexpr int LPP = HD / EPL;         // lanes per position
-  constexpr int PPP = kBlock / LPP;     // positions per block pass
-  constexpr int UA = 8;                 // passes in flight
+  constexpr int EPL = Pack<KT>::N;               // elements per 16 bytes
+  constexpr int LPP = HD / EPL;                  // lanes per position
+  constexpr int PPP = kBlock / LPP;              // positions per block pass
+  constexpr int PB = HD * (int)sizeof(KT);       // bytes per position
+  constexpr int TC = kAttnChunk;                 // positions per LDS chunk
+  constexpr int NI = TC * PB / 1024;             // 1 KB global-to-LDS instructions per chunk and per K or V
+  constexpr int UA = G >= 4 ? 4 : 8;             // positions per lane group per softmax rescale
   static_assert(LPP >= 1 && LPP <= 64 && (64 % LPP) == 0, "lanes per position must divide the wave");
-  extern __shared__ float sm[];
-  float* sc = sm;                       // [G][T] scores, then weights
-  float* ow = sm + G * p.split_len;     // [4 waves][G][HD]
-  float* mstat = ow + 4 * G * HD;       // merge: [G][S] split maxima, then merge weights
-  float* lstat = mstat + G * p.splits;  // merge: [G][S] split sums
-  __shared__ float s_m[G], s_l[G];
+  static_assert(NI % (kBlock / 64) == 0 && TC % PPP == 0, "chunk must split evenly over the waves");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  KT* ks = reinterpret_cast<KT*>(smem);                       // [TC][HD]
+  KT* vs = reinterpret_cast<KT*>(smem + (size_t)TC * PB);     // [TC][HD]
+  float* wst = reinterpret_cast<float*>(smem + (size_t)2 * TC * PB);   // [4 waves][G][HD + 2]
   __shared__ int s_last;
 
   const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
@@ -435,6 +480,36 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
   }
   const KT* Kb = reinterpret_cast<const KT*>(p.kv.k) + (size_t)p.layer * p.kv.layer_stride;
   const KT* Vb = reinterpret_cast<const KT*>(p.kv.v) + (size_t)p.layer * p.kv.layer_stride;
+  const float scale2 = p.scale * 1.4426950408889634f;   // 1/sqrt(hd) * log2(e)
+
+  // ---- stage a chunk's K and V rows: instruction k of the block fills LDS bytes [k KB, k KB + 1 KB)
+  auto stage = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < NI / (kBlock / 64); ++i) {
+      const int k = i * (kBlock / 64) + wid;
+      const int byte = k * 1024 + lane * 16;
+      const int tc = byte / PB;                           // position within the chunk
+      const int t = c0 + tc;
+      const int jc = min(j0 + min(t, T - 1), cap - 1);    // past the split or the capacity: clamped, never visible
+      uint32_t off;
+      if constexpr (PAGED) {
+        const int ppr = cap / p.kv.page_size;
+        int page = p.kv.slot_map[r * ppr + jc / p.kv.page_size];
+        if (page < 0 || page >= p.kv.pool_pages) {
+          raise_error(p.status, ERR_PAGE);
+          page = 0;
+        }
+        off = (uint32_t)(((page * p.nkv + g) * p.kv.page_size + (jc % p.kv.page_size)) * HD);
+      } else {
+        off = (uint32_t)(((r * p.nkv + g) * cap + jc) * HD);
+      }
+      const int el = (byte % PB) / (int)sizeof(KT);
+      __builtin_amdgcn_global_load_lds((global_cptr)(Kb + off + el), (lds_ptr)(smem + (size_t)k * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_cptr)(Vb + off + el),
+                                       (lds_ptr)(smem + (size_t)TC * PB + (size_t)k * 1024), 16, 0, 0);
+    }
+  };
+  stage(0);   // the first chunk's rows go out before anything else
 
   float qv[G][EPL];
 #pragma unroll
@@ -442,169 +517,202 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qv[hh][e] = p.q[((size_t)r * p.nq + g * G + hh) * HD + sub * EPL + e];
 
-  // ---- phase A: scores
-  for (int t0 = 0; t0 < T; t0 += PPP * UA) {
-    u32x4 kb[UA];
+  float m[G], l[G], o[G][EPL];
 #pragma unroll
-    for (int u = 0; u < UA; ++u) {
-      const int t = t0 + u * PPP + grp;
-      const int j = j0 + t;
-      kb[u] = u32x4{0u, 0u, 0u, 0u};
-      if (t0 + u * PPP < T) {   // uniform: T is a whole number of passes
-        const int jj = min(j, cap - 1);   // past the capacity: a clamped, masked re-read
-        kb[u] = load_stream(Kb + kv_offset(p.kv, r, p.nkv, g, jj, HD, p.status) + sub * EPL);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < UA; ++u) {
-      const int t = t0 + u * PPP + grp;
-      const int j = j0 + t;
-      float kf[EPL];
-      Pack<KT>::widen(kb[u], kf);
-      float d[G];
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc = fmaf(qv[hh][e], kf[e], acc);
-#pragma unroll
-        for (int m = LPP / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-        d[hh] = acc;
-      }
-      if (sub == 0 && t < T) {
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) sc[hh * T + t] = (j <= pos) ? d[hh] * p.scale : -INFINITY;
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- per-head max and weights of this split
-  for (int hh = wid; hh < G; hh += kBlock / 64) {
-    float m = -INFINITY;
-    for (int t = lane; t < T; t += 64) m = fmaxf(m, sc[hh * T + t]);
-    m = wave_max(m);
-    float l = 0.f;
-    for (int t = lane; t < T; t += 64) {
-      const float sv = sc[hh * T + t];
-      const float pr = (sv == -INFINITY) ? 0.f : expf(sv - m);
-      sc[hh * T + t] = pr;
-      l += pr;
-    }
-    l = wave_sum(l);
-    if (lane == 0) { s_m[hh] = m; s_l[hh] = l; }
-  }
-  __syncthreads();
-
-  // ---- phase B: weighted values
-  float o[G][EPL];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh)
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[hh][e] = 0.f;
-  for (int t0 = 0; t0 < T; t0 += PPP * UA) {
-    u32x4 vb[UA];
+  }
+
+  for (int c0 = 0; c0 < T; c0 += TC) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // ---- scores and online softmax from LDS. Scores are kept in the log2 domain (q.k * scale * log2 e), so the
+    // weights are plain exp2: the same softmax, one hardware exp per weight.
+    for (int tb = grp; tb < TC; tb += PPP * UA) {
+      float sc[UA][G];
+      bool vis[UA];
 #pragma unroll
-    for (int u = 0; u < UA; ++u) {
-      const int t = t0 + u * PPP + grp;
-      const int j = j0 + t;
-      vb[u] = u32x4{0u, 0u, 0u, 0u};
-      if (t0 + u * PPP < T) {
-        const int jj = min(j, cap - 1);
-        vb[u] = load_stream(Vb + kv_offset(p.kv, r, p.nkv, g, jj, HD, p.status) + sub * EPL);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < UA; ++u) {
-      const int t = t0 + u * PPP + grp;
-      const int j = j0 + t;
-      if (t < T) {
-        const bool visible = j <= pos;
-        float vf[EPL];
-        Pack<KT>::widen(vb[u], vf);
+      for (int u = 0; u < UA; ++u) {
+        const int tc = min(tb + u * PPP, TC - 1);
+        const int t = c0 + tb + u * PPP;
+        vis[u] = tb + u * PPP < TC && t < T && j0 + t <= pos;
+        float kf[EPL];
+        Pack<KT>::widen(*reinterpret_cast<const u32x4*>(ks + (size_t)tc * HD + sub * EPL), kf);
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-          const float pr = sc[hh * T + t];
+          float acc = 0.f;
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) {
-            const float pv = pr * vf[e];
-            o[hh][e] += visible ? pv : 0.f;
-          }
+          for (int e = 0; e < EPL; ++e) acc = fmaf(qv[hh][e], kf[e], acc);
+          acc = group_sum<LPP>(acc);
+          sc[u][hh] = vis[u] ? acc * scale2 : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float bm = sc[0][hh];
+#pragma unroll
+        for (int u = 1; u < UA; ++u) bm = fmaxf(bm, sc[u][hh]);
+        const float mn = fmaxf(m[hh], bm);
+        const float corr = (mn == -INFINITY) ? 1.f : fast_exp2(m[hh] - mn);
+        l[hh] *= corr;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[hh][e] *= corr;
+        m[hh] = mn;
+      }
+#pragma unroll
+      for (int u = 0; u < UA; ++u) {
+        const int tc = min(tb + u * PPP, TC - 1);
+        float vf[EPL];
+        Pack<KT>::widen(*reinterpret_cast<const u32x4*>(vs + (size_t)tc * HD + sub * EPL), vf);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[e] = vis[u] ? vf[e] : 0.f;   // a hidden row never reaches o (no 0 * NaN)
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float pu = vis[u] ? fast_exp2(sc[u][hh] - m[hh]) : 0.f;
+          l[hh] += pu;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[hh][e] = fmaf(pu, vf[e], o[hh][e]);
         }
       }
     }
+    __syncthreads();   // the next chunk overwrites the staged rows
+    if (c0 + TC < T) stage(c0 + TC);
   }
-  // reduce over the position groups of the wave (lanes with the same `sub`), then over the 4 waves
+
+  // ---- merge the lane groups of the wave (butterfly over the lanes holding the same head elements)
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
+  for (int msk = LPP; msk < 64; msk <<= 1) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float v = o[hh][e];
+    for (int hh = 0; hh < G; ++hh) {
+      const float m2 = __shfl_xor(m[hh], msk, 64);
+      const float l2 = __shfl_xor(l[hh], msk, 64);
+      float M, w1, w2;
+      Lse::weights(m[hh], m2, M, w1, w2);
+      l[hh] = l[hh] * w1 + l2 * w2;
 #pragma unroll
-      for (int m = LPP; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
-      o[hh][e] = v;
+      for (int e = 0; e < EPL; ++e) {
+        const float o2 = __shfl_xor(o[hh][e], msk, 64);
+        o[hh][e] = o[hh][e] * w1 + o2 * w2;
+      }
+      m[hh] = M;
     }
+  }
   if (lane < LPP) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh)
+    for (int hh = 0; hh < G; ++hh) {
+      float* w = wst + (wid * G + hh) * (HD + 2);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) ow[(wid * G + hh) * HD + sub * EPL + e] = o[hh][e];
+      for (int e = 0; e < EPL; ++e) w[sub * EPL + e] = o[hh][e];
+      if (sub == 0) {
+        w[HD] = m[hh];
+        w[HD + 1] = l[hh];
+      }
+    }
   }
   __syncthreads();
 
+  // ---- merge the 4 waves in wave order and write this split's partial.
+  // Partials cross blocks (and XCDs, whose L2s are not coherent with each other), so they are written and read
+  // with agent-scope atomic accesses, which bypass the non-coherent caches; a cache-wide release/acquire fence
+  // per block (an L2 write-back) would serialize the blocks of an XCD. Layout per (row, kv head):
+  // [G][HD + 2][SP] with the split index fastest, so the merging block reads each output's splits contiguously.
   const int S = p.splits;
-  float* part = p.part + (((size_t)r * p.nkv + g) * S) * (G * (HD + 2));
-  float* mine = part + (size_t)s * (G * (HD + 2));
-  for (int i = tid; i < G * HD; i += kBlock) {
-    const int hh = i / HD, dd = i % HD;
-    const float v = ((ow[(0 * G + hh) * HD + dd] + ow[(1 * G + hh) * HD + dd]) + ow[(2 * G + hh) * HD + dd]) +
-                    ow[(3 * G + hh) * HD + dd];
-    mine[hh * (HD + 2) + dd] = v;
-  }
-  if (tid < G) {
-    mine[tid * (HD + 2) + HD] = s_m[tid];
-    mine[tid * (HD + 2) + HD + 1] = s_l[tid];
+  const int SP = S <= 4 ? 4 : (S <= 8 ? 8 : (S <= 16 ? 16 : 32));   // split index padded to 4, 8, 16 or 32
+  float* part = p.part + ((size_t)r * p.nkv + g) * (size_t)(G * (HD + 2)) * SP;
+  for (int i = tid; i < G * (HD + 2); i += kBlock) {
+    const int hh = i / (HD + 2), dd = i % (HD + 2);
+    float mm = wst[(0 * G + hh) * (HD + 2) + HD];
+    float ll = wst[(0 * G + hh) * (HD + 2) + HD + 1];
+    float oo = wst[(0 * G + hh) * (HD + 2) + min(dd, HD - 1)];
+#pragma unroll
+    for (int w = 1; w < kBlock / 64; ++w) {
+      const float* ws2 = wst + (w * G + hh) * (HD + 2);
+      float M, w1, w2;
+      Lse::weights(mm, ws2[HD], M, w1, w2);
+      ll = ll * w1 + ws2[HD + 1] * w2;
+      oo = oo * w1 + ws2[min(dd, HD - 1)] * w2;
+      mm = M;
+    }
+    __hip_atomic_store(part + (size_t)i * SP + s, dd < HD ? oo : (dd == HD ? mm : ll), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // ---- last arriving block merges the splits
+  // ---- the last arriving block of this (row, kv head) merges the splits.
+  // Every thread's partial stores have completed (waitcnt) before the barrier; only then does one thread count
+  // the block in. The block that sees S - 1 earlier arrivals reads every split's partial after its own count.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    __threadfence();
-    const unsigned prev = atomicAdd(&p.counters[r * p.nkv + g], 1u);
+    const unsigned prev = __hip_atomic_fetch_add(&p.counters[r * p.nkv + g], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == (unsigned)(S - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();   // acquire: every split's partials are visible to plain loads from here on
-  for (int i = tid; i < G * S; i += kBlock) {
-    const int hh = i / S, s2 = i % S;
-    const float* ps = part + (size_t)s2 * (G * (HD + 2)) + hh * (HD + 2);
-    mstat[i] = ps[HD];
-    lstat[i] = ps[HD + 1];
-  }
-  __syncthreads();
-  for (int hh = wid; hh < G; hh += kBlock / 64) {
-    float M = -INFINITY;
-    for (int s2 = lane; s2 < S; s2 += 64) M = fmaxf(M, mstat[hh * S + s2]);
-    M = wave_max(M);
-    float L = 0.f;
-    for (int s2 = lane; s2 < S; s2 += 64) {
-      const float ms = mstat[hh * S + s2];
-      const float wgt = (ms == -INFINITY) ? 0.f : expf(ms - M);
-      mstat[hh * S + s2] = wgt;
-      L += wgt * lstat[hh * S + s2];
+  // Only the merging block acquires (invalidating its stale cache lines); every split's partial was written
+  // through to memory before its block counted in, so plain loads from here on see it. Each output's SP split
+  // values are C = SP/4 float4; C consecutive lanes take one output, so a wave instruction reads ~1 KB of
+  // consecutive outputs.
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  {
+    const int C = SP / 4;                                   // float4 per output: 1, 2, 4 or 8
+    constexpr int NOUT = (G * HD * (kMaxSplitsPerLane / 4) + kBlock - 1) / kBlock;   // float4 per thread, max
+    const int c = tid % C;
+    float4 ov[NOUT];
+#pragma unroll
+    for (int k = 0; k < NOUT; ++k) {
+      const int o = min(tid / C + k * (kBlock / C), G * HD - 1);   // output index hh * HD + dd
+      const int hh = o / HD, dd = o % HD;
+      ov[k] = *reinterpret_cast<const float4*>(part + (size_t)(hh * (HD + 2) + dd) * SP + 4 * c);
     }
-    L = wave_sum(L);
-    if (lane == 0) s_l[hh] = L;
-  }
-  __syncthreads();
-  for (int i = tid; i < G * HD; i += kBlock) {
-    const int hh = i / HD, dd = i % HD;
-    const float* po = part + hh * (HD + 2) + dd;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int s2 = 0; s2 < S; ++s2) acc = fmaf(mstat[hh * S + s2], po[(size_t)s2 * (G * (HD + 2))], acc);
-    p.out[((size_t)r * p.nq + g * G + hh) * HD + dd] = acc / s_l[hh];
+    // per head: M = max_s m_s, weights 2^(m_s - M) into LDS (reusing the wave-merge area), L = sum_s w_s l_s
+    float* wts = wst;                       // [G][SP] weights, then [G][SP] sums
+    float* lsum = wst + G * SP;
+    __shared__ float s_L[G];
+    for (int i = tid; i < G * SP; i += kBlock) {
+      const int hh = i / SP, s2 = i % SP;
+      const float* ps = part + (size_t)(hh * (HD + 2) + HD) * SP;
+      wts[i] = s2 < S ? ps[s2] : -INFINITY;
+      lsum[i] = s2 < S ? ps[SP + s2] : 0.f;
+    }
+    __syncthreads();
+    for (int hh = wid; hh < G; hh += kBlock / 64) {
+      float M = -INFINITY;
+      for (int s2 = lane; s2 < SP; s2 += 64) M = fmaxf(M, wts[hh * SP + s2]);
+      M = wave_max(M);
+      float L = 0.f;
+      for (int s2 = lane; s2 < SP; s2 += 64) {
+        const float ms = wts[hh * SP + s2];
+        const float w = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+        wts[hh * SP + s2] = w;
+        L = fmaf(w, lsum[hh * SP + s2], L);
+      }
+      L = wave_sum(L);
+      if (lane == 0) s_L[hh] = L;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NOUT; ++k) {
+      const int o = min(tid / C + k * (kBlock / C), G * HD - 1);
+      const int hh = o / HD, dd = o % HD;
+      const float* w = wts + hh * SP + 4 * c;
+      // padded splits carry weight 0 and are selected out (never 0 * garbage)
+      float acc = w[0] * (4 * c + 0 < S ? ov[k].x : 0.f);
+      acc = fmaf(w[1], 4 * c + 1 < S ? ov[k].y : 0.f, acc);
+      acc = fmaf(w[2], 4 * c + 2 < S ? ov[k].z : 0.f, acc);
+      acc = fmaf(w[3], 4 * c + 3 < S ? ov[k].w : 0.f, acc);
+      switch (C) {   // sum over the C lanes of this output (they agree bit for bit)
+        case 2: acc = group_sum<2>(acc); break;
+        case 4: acc = group_sum<4>(acc); break;
+        case 8: acc = group_sum<8>(acc); break;
+        default: break;
+      }
+      if (c == 0 && tid / C + k * (kBlock / C) < G * HD) p.out[((size_t)r * p.nq + g * G + hh) * HD + dd] = acc / s_L[hh];
+    }
   }
   if (tid == 0) __hip_atomic_store(&p.counters[r * p.nkv + g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -641,13 +749,24 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t value, size_t n) {
 size_t gemv_lds_bytes(int rows, int K, bool norm) { (void)norm; return (size_t)rows * K * sizeof(float); }
 
 int attn_positions_per_pass(int hd, int kv_dtype) {
-  const int epl = kv_dtype == 1 ? 8 : 4;
-  return kBlock / (hd / epl);
+  (void)hd;
+  (void)kv_dtype;
+  return kAttnChunk;   // splits are whole LDS chunks
 }
 
-size_t attn_lds_bytes(int nq, int nkv, int hd, int split_len, int splits) {
+size_t attn_lds_bytes(int nq, int nkv, int hd, int split_len, int splits, int kv_dtype) {
+  (void)split_len;
+  (void)splits;
   const int G = nq / nkv;
-  return ((size_t)G * split_len + (size_t)4 * G * hd + (size_t)2 * G * splits) * sizeof(float);
+  const size_t pb = (size_t)hd * (kv_dtype == 1 ? 2 : 4);
+  return 2 * kAttnChunk * pb + (size_t)4 * G * (hd + 2) * sizeof(float);
+}
+
+int attn_max_splits(int nq, int nkv, int hd) {
+  (void)nq;
+  (void)nkv;
+  (void)hd;
+  return kMaxSplitsPerLane;
 }
 
 template <typename F>
@@ -716,27 +835,31 @@ hipError_t launch_gemv(const GemvParams& p, int mode, int weight_dtype, int kv_d
   return kv_dtype == 1 ? gemv_mode<float, uint16_t>(p, mode, blocks, s) : gemv_mode<float, float>(p, mode, blocks, s);
 }
 
+template <typename KT, int HD, int GG>
+static hipError_t attn_go(const AttnParams& p, int rows, hipStream_t s) {
+  const size_t lds = attn_lds_bytes(p.nq, p.nkv, HD, p.split_len, p.splits, sizeof(KT) == 2 ? 1 : 0);
+  dim3 grid(p.splits, p.nkv, rows);
+  hipError_t e;
+  if (p.kv.paged) {
+    auto* f = attn_kernel<KT, HD, GG, true>;
+    if ((e = set_lds(f, lds)) != hipSuccess) return e;
+    f<<<grid, kBlock, lds, s>>>(p);
+  } else {
+    auto* f = attn_kernel<KT, HD, GG, false>;
+    if ((e = set_lds(f, lds)) != hipSuccess) return e;
+    f<<<grid, kBlock, lds, s>>>(p);
+  }
+  return hipGetLastError();
+}
+
 template <typename KT, int HD>
 static hipError_t attn_g(const AttnParams& p, int rows, hipStream_t s) {
-  const int G = p.nq / p.nkv;
-  const size_t lds = attn_lds_bytes(p.nq, p.nkv, HD, p.split_len, p.splits);
-  dim3 grid(p.splits, p.nkv, rows);
-  switch (G) {
-#define DS3_CASE(GG)                                      \
-  case GG: {                                              \
-    auto* f = attn_kernel<KT, HD, GG>;                    \
-    hipError_t e = set_lds(f, lds);                       \
-    if (e != hipSuccess) return e;                        \
-    f<<<grid, kBlock, lds, s>>>(p);                       \
-    return hipGetLastError();                             \
-  }
-    DS3_CASE(1)
-    DS3_CASE(2)
-    DS3_CASE(4)
-    DS3_CASE(8)
-#undef DS3_CASE
-    default:
-      return hipErrorInvalidValue;
+  switch (p.nq / p.nkv) {
+    case 1: return attn_go<KT, HD, 1>(p, rows, s);
+    case 2: return attn_go<KT, HD, 2>(p, rows, s);
+    case 4: return attn_go<KT, HD, 4>(p, rows, s);
+    case 8: return attn_go<KT, HD, 8>(p, rows, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
