@@ -76,6 +76,10 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
   return v;
 }
+// Sum over the wave, identical in every lane: DPP sums within each row of 16 lanes, then the four row sums read
+// back in row order.
+__device__ __forceinline__ float wave_total(float v);
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
@@ -104,6 +108,15 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // 2^x with the hardware exp (results below the normal range flush to zero, which a softmax weight can afford)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_total(float v) {
+  v = group_sum<16>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
 
 __device__ __forceinline__ void raise_error(StatusWords* st, uint32_t bit) { atomicOr(&st->err, bit); }
 
@@ -344,17 +357,10 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
     }
   }
 
-  // ---- 4. pairs
-  bool first = true;
-  for (; pair < p.n_pairs; pair += nwaves) {
-    if (!first) {
-      pm = PairMap<MODE>(p, pair);
-      w0 = wbase + (size_t)pm.row0 * K;
-      w1 = wbase + (size_t)pm.row1 * K;
-      load_group<WT>(w0, w1, 0, nchunks, K, lane, b0, b1);
-      fetch_epilogue(pm, pair);
-    }
-    first = false;
+  // ---- 4. pairs. As soon as a pair's dot products have consumed its weights, the next pair's weights (and
+  // epilogue operands) are issued, so they are in flight during this pair's reduction and epilogue.
+  float na[NR], nb[NR];
+  for (; pair < p.n_pairs;) {
     float a0[NR], a1[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) { a0[r] = 0.f; a1[r] = 0.f; }
@@ -362,10 +368,22 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
       if (c0 > 0) load_group<WT>(w0, w1, c0, nchunks, K, lane, b0, b1);
       fma_group<WT, NR>(b0, b1, xs, c0, nchunks, K, lane, a0, a1);
     }
+    const PairMap<MODE> cur = pm;
+    const int cur_pair = pair;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) { na[r] = ea[r]; nb[r] = eb[r]; }
+    pair += nwaves;
+    if (pair < p.n_pairs) {
+      pm = PairMap<MODE>(p, pair);
+      w0 = wbase + (size_t)pm.row0 * K;
+      w1 = wbase + (size_t)pm.row1 * K;
+      load_group<WT>(w0, w1, 0, nchunks, K, lane, b0, b1);
+      fetch_epilogue(pm, pair);
+    }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      a0[r] = wave_sum(a0[r]);
-      a1[r] = wave_sum(a1[r]);
+      a0[r] = wave_total(a0[r]);
+      a1[r] = wave_total(a1[r]);
     }
     if (lane != 0) continue;
 
@@ -377,38 +395,38 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
         if (!pos_ok[r]) raise_error(p.status, ERR_POS);
         const int half = p.hd / 2;
         float va = a, vb = b;
-        if (pm.seg != 2) {   // rotate the pair (element idx, element idx + hd/2) by the angle of Slot::Pos
-          va = a * ea[r] - b * eb[r];
-          vb = a * eb[r] + b * ea[r];
+        if (cur.seg != 2) {   // rotate the pair (element idx, element idx + hd/2) by the angle of Slot::Pos
+          va = a * na[r] - b * nb[r];
+          vb = a * nb[r] + b * na[r];
         }
-        if (pm.seg == 0) {
-          float* q = p.out + ((size_t)r * p.nq + pm.head) * p.hd;
-          q[pm.idx] = va;
-          q[pm.idx + half] = vb;
+        if (cur.seg == 0) {
+          float* q = p.out + ((size_t)r * p.nq + cur.head) * p.hd;
+          q[cur.idx] = va;
+          q[cur.idx + half] = vb;
           continue;
         }
         if (!pos_ok[r]) continue;
         size_t off;
         if (!p.kv.paged) {
-          off = ((size_t)(r * p.nkv + pm.head) * p.kv.cap + posr[r]) * p.hd;
+          off = ((size_t)(r * p.nkv + cur.head) * p.kv.cap + posr[r]) * p.hd;
         } else {
           const int slot = p.slots[sl.write_map() + r];
           if (slot < 0 || slot >= p.kv.pool_pages * p.kv.page_size) { raise_error(p.status, ERR_WRITE_MAP); continue; }
-          off = ((size_t)((slot / p.kv.page_size) * p.nkv + pm.head) * p.kv.page_size + slot % p.kv.page_size) * p.hd;
+          off = ((size_t)((slot / p.kv.page_size) * p.nkv + cur.head) * p.kv.page_size + slot % p.kv.page_size) * p.hd;
         }
         // k: the two halves of a rotary pair; v: two adjacent elements
-        KT* dst = reinterpret_cast<KT*>(pm.seg == 1 ? p.kv.k : p.kv.v) + (size_t)p.layer * p.kv.layer_stride + off +
-                  pm.idx;
+        KT* dst = reinterpret_cast<KT*>(cur.seg == 1 ? p.kv.k : p.kv.v) + (size_t)p.layer * p.kv.layer_stride + off +
+                  cur.idx;
         store_kv(dst, va);
-        store_kv(dst + (pm.seg == 1 ? half : 1), vb);
+        store_kv(dst + (cur.seg == 1 ? half : 1), vb);
       } else if constexpr (MODE == GEMV_GATEUP) {
         const float silu = a / (1.0f + expf(-a));
-        p.out[(size_t)r * p.n_pairs + pair] = silu * b;
+        p.out[(size_t)r * p.n_pairs + cur_pair] = silu * b;
       } else if constexpr (MODE == GEMV_RESID) {
-        float2* x = reinterpret_cast<float2*>(p.out + (size_t)r * 2 * p.n_pairs) + pair;
-        *x = make_float2(ea[r] + a, eb[r] + b);
+        float2* x = reinterpret_cast<float2*>(p.out + (size_t)r * 2 * p.n_pairs) + cur_pair;
+        *x = make_float2(na[r] + a, nb[r] + b);
       } else {  // GEMV_HEAD
-        float2* lg = reinterpret_cast<float2*>(p.out + (size_t)r * 2 * p.n_pairs) + pair;
+        float2* lg = reinterpret_cast<float2*>(p.out + (size_t)r * 2 * p.n_pairs) + cur_pair;
         *lg = make_float2(a, b);
         if (!isfinite(a) || !isfinite(b)) atomicOr(&p.status->nonfinite, 1u);
       }
@@ -444,6 +462,14 @@ struct Lse {   // merge of two (max, sum, weighted values) states (maxima in the
   }
 };
 
+// s_waitcnt immediate (gfx9 encoding) that waits until at most N vector-memory operations are outstanding and
+// does not wait on the other counters
+template <int N>
+constexpr int kVmcntChunk() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
 typedef __attribute__((address_space(1))) const void* global_cptr;
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -459,9 +485,8 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
   static_assert(LPP >= 1 && LPP <= 64 && (64 % LPP) == 0, "lanes per position must divide the wave");
   static_assert(NI % (kBlock / 64) == 0 && TC % PPP == 0, "chunk must split evenly over the waves");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  KT* ks = reinterpret_cast<KT*>(smem);                       // [TC][HD]
-  KT* vs = reinterpret_cast<KT*>(smem + (size_t)TC * PB);     // [TC][HD]
-  float* wst = reinterpret_cast<float*>(smem + (size_t)2 * TC * PB);   // [4 waves][G][HD + 2]
+  constexpr int NBUF_MAX = 2;
+  float* wst = reinterpret_cast<float*>(smem + (size_t)NBUF_MAX * 2 * TC * PB);   // [4 waves][G][HD + 2]
   __shared__ int s_last;
 
   const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
@@ -469,7 +494,11 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int sub = tid % LPP, grp = tid / LPP;
   const int T = p.split_len;
-  const int j0 = s * T;
+  // Chunks of the capacity go to splits round-robin (split s takes chunks s, s + S, s + 2S, ...), so the visible
+  // positions 0..pos, and with them the arithmetic, spread over all splits; the merge does not depend on which
+  // positions a split holds.
+  const int S = p.splits;
+  auto chunk_base = [&](int c0) { return (s + (c0 / TC) * S) * TC; };
   const int cap = p.kv.cap;
   const SlotLayout sl{rows};
 
@@ -482,15 +511,24 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
   const KT* Vb = reinterpret_cast<const KT*>(p.kv.v) + (size_t)p.layer * p.kv.layer_stride;
   const float scale2 = p.scale * 1.4426950408889634f;   // 1/sqrt(hd) * log2(e)
 
-  // ---- stage a chunk's K and V rows: instruction k of the block fills LDS bytes [k KB, k KB + 1 KB)
-  auto stage = [&](int c0) {
+  // the query heads of this kv head (these loads go first: loads return in order)
+  float qv[G][EPL];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[hh][e] = p.q[((size_t)r * p.nq + g * G + hh) * HD + sub * EPL + e];
+
+  // ---- stage a chunk's K and V rows into LDS buffer `buf`: instruction k of the block fills bytes
+  // [k KB, k KB + 1 KB) of the buffer's K half and of its V half
+  auto stage = [&](int c0, int buf) {
+    unsigned char* kdst = smem + (size_t)buf * 2 * TC * PB;
+    unsigned char* vdst = kdst + (size_t)TC * PB;
 #pragma unroll
     for (int i = 0; i < NI / (kBlock / 64); ++i) {
       const int k = i * (kBlock / 64) + wid;
       const int byte = k * 1024 + lane * 16;
       const int tc = byte / PB;                           // position within the chunk
-      const int t = c0 + tc;
-      const int jc = min(j0 + min(t, T - 1), cap - 1);    // past the split or the capacity: clamped, never visible
+      const int jc = min(chunk_base(c0) + tc, cap - 1);   // past the capacity: clamped, never visible
       uint32_t off;
       if constexpr (PAGED) {
         const int ppr = cap / p.kv.page_size;
@@ -504,18 +542,16 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
         off = (uint32_t)(((r * p.nkv + g) * cap + jc) * HD);
       }
       const int el = (byte % PB) / (int)sizeof(KT);
-      __builtin_amdgcn_global_load_lds((global_cptr)(Kb + off + el), (lds_ptr)(smem + (size_t)k * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((global_cptr)(Vb + off + el),
-                                       (lds_ptr)(smem + (size_t)TC * PB + (size_t)k * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_cptr)(Kb + off + el), (lds_ptr)(kdst + (size_t)k * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_cptr)(Vb + off + el), (lds_ptr)(vdst + (size_t)k * 1024), 16, 0, 0);
     }
   };
-  stage(0);   // the first chunk's rows go out before anything else
-
-  float qv[G][EPL];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qv[hh][e] = p.q[((size_t)r * p.nq + g * G + hh) * HD + sub * EPL + e];
+  // Both buffers are filled up front; afterwards a buffer is refilled as soon as its chunk has been consumed.
+  // The paged layout reads page ids with ordinary loads, which would wait behind the previous chunk's rows,
+  // so it keeps one chunk in flight.
+  constexpr int NBUF = PAGED ? 1 : 2;
+  stage(0, 0);
+  if (NBUF == 2 && TC < T) stage(TC, 1);
 
   float m[G], l[G], o[G][EPL];
 #pragma unroll
@@ -526,10 +562,16 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
     for (int e = 0; e < EPL; ++e) o[hh][e] = 0.f;
   }
 
-  for (int c0 = 0; c0 < T; c0 += TC) {
-    __builtin_amdgcn_s_waitcnt(0);
+  for (int c0 = 0, buf = 0; c0 < T; c0 += TC, buf = (buf + 1) % NBUF) {
+    // wait for this chunk's rows only: a later chunk's rows (NI/4 K and NI/4 V loads per wave) may still fly
+    if (NBUF == 2 && c0 + TC < T) __builtin_amdgcn_s_waitcnt(kVmcntChunk<NI / (kBlock / 64) * 2>());
+    else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
+    const KT* ks = reinterpret_cast<const KT*>(smem + (size_t)buf * 2 * TC * PB);
+    const KT* vs = ks + (size_t)TC * HD;
+    // a chunk entirely after pos is swept (its rows were loaded) but holds no visible position: no arithmetic
+    const int jb = chunk_base(c0);
+    if (jb <= pos) {
     // ---- scores and online softmax from LDS. Scores are kept in the log2 domain (q.k * scale * log2 e), so the
     // weights are plain exp2: the same softmax, one hardware exp per weight.
     for (int tb = grp; tb < TC; tb += PPP * UA) {
@@ -538,8 +580,7 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
 #pragma unroll
       for (int u = 0; u < UA; ++u) {
         const int tc = min(tb + u * PPP, TC - 1);
-        const int t = c0 + tb + u * PPP;
-        vis[u] = tb + u * PPP < TC && t < T && j0 + t <= pos;
+        vis[u] = tb + u * PPP < TC && jb + tb + u * PPP <= pos;
         float kf[EPL];
         Pack<KT>::widen(*reinterpret_cast<const u32x4*>(ks + (size_t)tc * HD + sub * EPL), kf);
 #pragma unroll
@@ -579,8 +620,9 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
         }
       }
     }
-    __syncthreads();   // the next chunk overwrites the staged rows
-    if (c0 + TC < T) stage(c0 + TC);
+    }
+    __syncthreads();   // the buffer is refilled next
+    if (c0 + NBUF * TC < T) stage(c0 + NBUF * TC, buf);
   }
 
   // ---- merge the lane groups of the wave (butterfly over the lanes holding the same head elements)
@@ -620,7 +662,6 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
   // with agent-scope atomic accesses, which bypass the non-coherent caches; a cache-wide release/acquire fence
   // per block (an L2 write-back) would serialize the blocks of an XCD. Layout per (row, kv head):
   // [G][HD + 2][SP] with the split index fastest, so the merging block reads each output's splits contiguously.
-  const int S = p.splits;
   const int SP = S <= 4 ? 4 : (S <= 8 ? 8 : (S <= 16 ? 16 : 32));   // split index padded to 4, 8, 16 or 32
   float* part = p.part + ((size_t)r * p.nkv + g) * (size_t)(G * (HD + 2)) * SP;
   for (int i = tid; i < G * (HD + 2); i += kBlock) {
@@ -759,7 +800,7 @@ size_t attn_lds_bytes(int nq, int nkv, int hd, int split_len, int splits, int kv
   (void)splits;
   const int G = nq / nkv;
   const size_t pb = (size_t)hd * (kv_dtype == 1 ? 2 : 4);
-  return 2 * kAttnChunk * pb + (size_t)4 * G * (hd + 2) * sizeof(float);
+  return 2 * 2 * kAttnChunk * pb + (size_t)4 * G * (hd + 2) * sizeof(float);
 }
 
 int attn_max_splits(int nq, int nkv, int hd) {
