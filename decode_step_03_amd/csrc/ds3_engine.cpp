@@ -30,19 +30,23 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 size_t dtype_bytes(int dt) { return dt == DS3_BF16 ? 2 : 4; }
 
 struct WorkPlan {
-  size_t slots, status, x, q, attn, act, part, counters, rope, slot_map, total;
+  size_t slots, status, x, q, attn, act, part, counters, rope, slot_map, frag_hi, frag_lo, total;
 };
 
 struct KernelKind {
   const char* name;
 };
-enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN, K_HEAD, K_NUM };
+enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN, K_HEAD, K_SPLIT, K_NUM };
 const char* kKindNames[K_NUM] = {"embed", "qkv_rope_kvwrite", "attention_splitk", "o_proj_residual",
-                                 "gateup_swiglu", "down_proj_residual", "lm_head"};
+                                 "gateup_swiglu", "down_proj_residual", "lm_head", "act_split_mfma"};
+
+// activation sites the MFMA path splits into bf16 hi/lo operands
+enum Site { S_ATTN_NORM = 0, S_ATTN_OUT, S_FFN_NORM, S_ACT, S_FINAL_NORM };
 
 struct Launch {
   int kind;
   int layer;
+  int site;
 };
 
 }  // namespace
@@ -61,6 +65,8 @@ struct ds3_engine {
   unsigned* counters = nullptr;
   int* slot_map = nullptr;
   float* logits = nullptr;
+  uint16_t *frag_hi = nullptr, *frag_lo = nullptr;   // MFMA path: activation operands
+  bool mfma = false;                                 // rows > 4: projections on the matrix cores
   size_t work_bytes = 0;
 
   // weights
@@ -138,7 +144,7 @@ std::string check_config(const ds3_config* c) {
   if (c->vocab < 2 || c->vocab % 2) return "vocab must be even and >= 2";
   if (!(c->rms_eps >= 0.f)) return "rms_eps must be >= 0";
   if (!(c->rope_theta > 1.0)) return "rope_theta must be > 1";
-  if (c->rows < 1 || c->rows > kMaxGemvRows) return "rows must be in 1..4";
+  if (c->rows < 1 || c->rows > kMaxRows) return "rows must be in 1..16";
   if (c->cap < 1) return "cap must be >= 1";
   if (c->weight_dtype != DS3_F32 && c->weight_dtype != DS3_BF16) return "weight_dtype must be DS3_F32 or DS3_BF16";
   if (c->kv_dtype != DS3_F32 && c->kv_dtype != DS3_BF16) return "kv_dtype must be DS3_F32 or DS3_BF16";
@@ -151,9 +157,16 @@ std::string check_config(const ds3_config* c) {
   } else if (c->kv_layout != DS3_KV_CONTIGUOUS) {
     return "kv_layout must be DS3_KV_CONTIGUOUS or DS3_KV_PAGED";
   }
-  const int kres = std::max(c->ffn_dim, c->n_q_heads * c->head_dim);
-  if (gemv_lds_bytes(c->rows, c->d_model, true) > 160 * 1024 || gemv_lds_bytes(c->rows, kres, false) > 160 * 1024)
-    return "rows: activations of rows x max(d_model, ffn_dim, q width) floats exceed the 160 KB LDS";
+  if (c->rows <= kMaxGemvRows) {
+    const int kres = std::max(c->ffn_dim, c->n_q_heads * c->head_dim);
+    if (gemv_lds_bytes(c->rows, c->d_model, true) > 160 * 1024 || gemv_lds_bytes(c->rows, kres, false) > 160 * 1024)
+      return "rows: activations of rows x max(d_model, ffn_dim, q width) floats exceed the 160 KB LDS";
+  } else {
+    // matrix-core path: bf16 weights in whole 16-row tiles and 32-input steps
+    if (c->weight_dtype != DS3_BF16) return "weight_dtype: more than 4 rows needs bf16 weights (matrix-core path)";
+    if (c->d_model % 32 || c->ffn_dim % 32 || c->head_dim % 32 || c->vocab % 32)
+      return "d_model, ffn_dim, head_dim and vocab must be multiples of 32 for more than 4 rows";
+  }
   return "";
 }
 
@@ -199,6 +212,10 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
   w.counters = take((size_t)c.rows * c.n_kv_heads * 4);
   w.rope = take((size_t)c.cap * (c.head_dim / 2) * 2 * 4);
   w.slot_map = take(c.kv_layout == DS3_KV_PAGED ? (size_t)c.rows * (c.cap / c.page_size) * 4 : 4);
+  const size_t kmax = (size_t)std::max(std::max(c.d_model, c.ffn_dim), c.n_q_heads * c.head_dim);
+  const size_t frag = c.rows > kMaxGemvRows ? kmax * kMfmaRows * 2 : 16;
+  w.frag_hi = take(frag);
+  w.frag_lo = take(frag);
   w.total = off;
   return w;
 }
@@ -287,6 +304,22 @@ ds3_status wait_done(ds3_engine* e, hipEvent_t ev, uint32_t timeout_ms) {
   }
 }
 
+// One projection: the paired-row GEMV for up to 4 rows, the MFMA tile GEMM (on the split activations) beyond.
+hipError_t run_projection(ds3_engine* e, const GemvParams& p, int mode, int kind) {
+  const ds3_config& c = e->cfg;
+  if (!e->mfma) return launch_gemv(p, mode, c.weight_dtype, c.kv_dtype, e->blocks[kind], e->stream);
+  MfmaParams mp{};
+  mp.g = p;
+  mp.hi = e->frag_hi;
+  mp.lo = e->frag_lo;
+  switch (mode) {
+    case GEMV_QKV: mp.n_units = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim / 32; break;
+    case GEMV_GATEUP: mp.n_units = c.ffn_dim / 16; break;
+    default: mp.n_units = 2 * p.n_pairs / 32; break;
+  }
+  return launch_gemm_mfma(mp, mode, c.kv_dtype, e->stream);
+}
+
 hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
   const ds3_config& c = e->cfg;
   const int R = c.rows;
@@ -303,6 +336,22 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
     p.status = e->status;
   };
   switch (l.kind) {
+    case K_SPLIT: {
+      SplitParams sp{};
+      sp.hi = e->frag_hi;
+      sp.lo = e->frag_lo;
+      sp.rows = R;
+      sp.eps = c.rms_eps;
+      bool norm = true;
+      switch (l.site) {
+        case S_ATTN_NORM: sp.in = e->x; sp.gain = e->L[l.layer].attn_norm; sp.K = c.d_model; break;
+        case S_FFN_NORM: sp.in = e->x; sp.gain = e->L[l.layer].ffn_norm; sp.K = c.d_model; break;
+        case S_FINAL_NORM: sp.in = e->x; sp.gain = e->final_norm; sp.K = c.d_model; break;
+        case S_ATTN_OUT: sp.in = e->attn; sp.K = c.n_q_heads * c.head_dim; norm = false; break;
+        default: sp.in = e->act; sp.K = c.ffn_dim; norm = false; break;
+      }
+      return launch_split(sp, norm, e->stream);
+    }
     case K_EMBED: {
       EmbedParams p{e->embed, e->x, c.d_model, c.vocab, R, e->slots, e->status};
       return launch_embed(p, c.weight_dtype, e->stream);
@@ -317,7 +366,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.out = e->q;
       p.K = c.d_model;
       p.n_pairs = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim / 2;
-      return launch_gemv(p, GEMV_QKV, c.weight_dtype, c.kv_dtype, e->blocks[K_QKV], e->stream);
+      return run_projection(e, p, GEMV_QKV, K_QKV);
     }
     case K_ATTN: {
       AttnParams p{};
@@ -345,7 +394,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.out = e->x;
       p.K = c.n_q_heads * c.head_dim;
       p.n_pairs = c.d_model / 2;
-      return launch_gemv(p, GEMV_RESID, c.weight_dtype, c.kv_dtype, e->blocks[K_OPROJ], e->stream);
+      return run_projection(e, p, GEMV_RESID, K_OPROJ);
     }
     case K_GATEUP: {
       GemvParams p{};
@@ -358,7 +407,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.K = c.d_model;
       p.n_pairs = c.ffn_dim;
       p.up_offset = c.ffn_dim;
-      return launch_gemv(p, GEMV_GATEUP, c.weight_dtype, c.kv_dtype, e->blocks[K_GATEUP], e->stream);
+      return run_projection(e, p, GEMV_GATEUP, K_GATEUP);
     }
     case K_DOWN: {
       GemvParams p{};
@@ -368,7 +417,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.out = e->x;
       p.K = c.ffn_dim;
       p.n_pairs = c.d_model / 2;
-      return launch_gemv(p, GEMV_RESID, c.weight_dtype, c.kv_dtype, e->blocks[K_DOWN], e->stream);
+      return run_projection(e, p, GEMV_RESID, K_DOWN);
     }
     case K_HEAD: {
       GemvParams p{};
@@ -379,7 +428,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.out = e->logits;
       p.K = c.d_model;
       p.n_pairs = c.vocab / 2;
-      return launch_gemv(p, GEMV_HEAD, c.weight_dtype, c.kv_dtype, e->blocks[K_HEAD], e->stream);
+      return run_projection(e, p, GEMV_HEAD, K_HEAD);
     }
   }
   return hipErrorInvalidValue;
@@ -484,6 +533,9 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   e->counters = reinterpret_cast<unsigned*>(work + wp.counters);
   e->rope = reinterpret_cast<float*>(work + wp.rope);
   e->slot_map = reinterpret_cast<int*>(work + wp.slot_map);
+  e->frag_hi = reinterpret_cast<uint16_t*>(work + wp.frag_hi);
+  e->frag_lo = reinterpret_cast<uint16_t*>(work + wp.frag_lo);
+  e->mfma = c.rows > kMaxGemvRows;
   e->work_bytes = wp.total;
   e->logits = reinterpret_cast<float*>(e->buf[DS3_BUF_LOGITS]);
 
@@ -517,15 +569,20 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   e->blocks[K_DOWN] = gemv_blocks(c.d_model / 2, max_blocks);
   e->blocks[K_HEAD] = gemv_blocks(c.vocab / 2, max_blocks);
 
-  e->sequence.push_back({K_EMBED, -1});
+  e->sequence.push_back({K_EMBED, -1, 0});
   for (int l = 0; l < c.n_layers; ++l) {
-    e->sequence.push_back({K_QKV, l});
-    e->sequence.push_back({K_ATTN, l});
-    e->sequence.push_back({K_OPROJ, l});
-    e->sequence.push_back({K_GATEUP, l});
-    e->sequence.push_back({K_DOWN, l});
+    if (e->mfma) e->sequence.push_back({K_SPLIT, l, S_ATTN_NORM});
+    e->sequence.push_back({K_QKV, l, 0});
+    e->sequence.push_back({K_ATTN, l, 0});
+    if (e->mfma) e->sequence.push_back({K_SPLIT, l, S_ATTN_OUT});
+    e->sequence.push_back({K_OPROJ, l, 0});
+    if (e->mfma) e->sequence.push_back({K_SPLIT, l, S_FFN_NORM});
+    e->sequence.push_back({K_GATEUP, l, 0});
+    if (e->mfma) e->sequence.push_back({K_SPLIT, l, S_ACT});
+    e->sequence.push_back({K_DOWN, l, 0});
   }
-  e->sequence.push_back({K_HEAD, -1});
+  if (e->mfma) e->sequence.push_back({K_SPLIT, -1, S_FINAL_NORM});
+  e->sequence.push_back({K_HEAD, -1, 0});
 
   const SlotLayout sl{c.rows};
   h = hipHostMalloc(reinterpret_cast<void**>(&e->h_slots), (size_t)sl.words() * 4 + kAlign + sizeof(StatusWords),

@@ -95,9 +95,35 @@ struct EmbedParams {
   StatusWords* status;
 };
 
+// MFMA path (5..16 rows): activations are handed to the matrix cores as two bf16 parts, hi = bf16(a) and
+// lo = bf16(a - hi), stored in the operand order of v_mfma_f32_16x16x32_bf16 (step t of 32 inputs, lane l holds
+// inputs 32t + 8(l/16) .. +8 of activation row l % 16).
+struct SplitParams {
+  const float* in;       // [rows][K] fp32
+  const float* gain;     // RMSNorm gain [K] (norm only)
+  uint16_t* hi;          // [K/32][64][8] bf16
+  uint16_t* lo;
+  int K;
+  int rows;
+  float eps;
+};
+
 constexpr int kMaxGemvRows = 4;
+constexpr int kMaxRows = 16;
+constexpr int kMfmaRows = 16;   // activation rows of one MFMA tile (rows are zero-padded to it)
+
+// The same GEMM contract as GemvParams, for the MFMA path: `hi`/`lo` replace `in`/`gain` (the RMSNorm scale and
+// gain are already applied by the split kernel).
+struct MfmaParams {
+  GemvParams g;
+  const uint16_t* hi;
+  const uint16_t* lo;
+  int n_units;           // pairs of 16-row weight tiles
+};
 
 // Host launchers (defined in ds3_kernels.hip). Each returns the launch error, if any.
+hipError_t launch_split(const SplitParams& p, bool norm, hipStream_t s);
+hipError_t launch_gemm_mfma(const MfmaParams& p, int mode, int kv_dtype, hipStream_t s);
 hipError_t launch_embed(const EmbedParams& p, int weight_dtype, hipStream_t s);
 hipError_t launch_gemv(const GemvParams& p, int mode, int weight_dtype, int kv_dtype, int blocks, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, int kv_dtype, int rows, hipStream_t s);

@@ -435,6 +435,188 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
 }
 
 // ----------------------------------------------------------------------------------------------------------
+// MFMA path for 5..16 rows (batched decode). Each weight element now feeds up to 16 products, which is matrix
+// work: v_mfma_f32_16x16x32_bf16 multiplies a 16x32 bf16 weight tile by a 32x16 bf16 activation tile into fp32.
+// The activations are fp32, so they enter as two bf16 parts (hi and the remainder lo, about 16 significant bits
+// together): D = W.hi + W.lo. Weights are still read once per step.
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NORM>
+__global__ void __launch_bounds__(kBlock) split_kernel(SplitParams p) {
+  const int r = blockIdx.x;   // activation row of the tile (rows >= p.rows are zero padding)
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  __shared__ float red[kBlock / 64];
+  const bool live = r < p.rows;
+  const float* x = p.in + (size_t)(live ? r : 0) * p.K;
+  float scale = 1.f;
+  if constexpr (NORM) {
+    float ss = 0.f;
+    for (int k = tid; k < p.K; k += kBlock) {
+      const float v = x[k];
+      ss += v * v;
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red[wid] = ss;
+    __syncthreads();
+    scale = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)p.K + p.eps);
+  }
+  for (int k = tid; k < p.K; k += kBlock) {
+    float v = 0.f;
+    if (live) {
+      v = x[k] * scale;
+      if constexpr (NORM) v *= p.gain[k];
+    }
+    const uint16_t h = to_bf16(v);
+    const uint16_t l = to_bf16(v - widen1(h));
+    const size_t idx = ((size_t)(k >> 5) * 64 + ((k >> 3) & 3) * 16 + r) * 8 + (k & 7);
+    p.hi[idx] = h;
+    p.lo[idx] = l;
+  }
+}
+
+// A unit is a pair of 16-row weight tiles, chosen so the epilogue has what it needs (as PairMap for the GEMV):
+// rotary partners (rows i and i + hd/2 of a q or k head), a gate tile and its up tile, or two adjacent tiles.
+template <int MODE>
+struct TileMap {
+  int row0, row1;
+  int seg, head, idx0;   // QKV: segment 0 q / 1 k / 2 v, head, first element (within the head) of tile 0
+  __device__ __forceinline__ TileMap(const GemvParams& p, int unit) : seg(0), head(0), idx0(0) {
+    if constexpr (MODE == GEMV_QKV) {
+      const int per_head = p.hd / 32;              // units per q or k head
+      const int nqk = (p.nq + p.nkv) * per_head;
+      if (unit < nqk) {
+        head = unit / per_head;
+        idx0 = 16 * (unit % per_head);
+        seg = head < p.nq ? 0 : 1;
+        if (seg == 1) head -= p.nq;
+        row0 = (seg == 0 ? head : p.nq + head) * p.hd + idx0;
+        row1 = row0 + p.hd / 2;
+      } else {
+        const int v = 32 * (unit - nqk);            // first value row of the unit
+        seg = 2; head = v / p.hd; idx0 = v % p.hd;
+        row0 = (p.nq + p.nkv) * p.hd + v; row1 = row0 + 16;
+      }
+    } else if constexpr (MODE == GEMV_GATEUP) {
+      row0 = 16 * unit; row1 = p.up_offset + 16 * unit;
+    } else {
+      row0 = 32 * unit; row1 = row0 + 16;
+    }
+  }
+};
+
+template <typename KT, int MODE>
+__global__ void __launch_bounds__(kBlock) gemm_mfma_kernel(MfmaParams mp) {
+  const GemvParams& p = mp.g;
+  constexpr int U = 8;                       // k-steps of 32 inputs in flight per wave
+  __shared__ f32x4 red[kBlock / 64][2][64];  // split-K partials of the two tiles
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int K = p.K;
+  const int NS = K / 32;                     // k-steps
+  const int per = (NS + 3) / 4;              // k-steps per wave (split-K over the 4 waves)
+  const int t0 = wid * per, t1 = min(NS, t0 + per);
+  const TileMap<MODE> tm(p, blockIdx.x);
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(p.w);
+  const uint16_t* a0p = W + (size_t)(tm.row0 + lane % 16) * K + 8 * (lane / 16);
+  const uint16_t* a1p = W + (size_t)(tm.row1 + lane % 16) * K + 8 * (lane / 16);
+  const uint16_t* hp = mp.hi + (size_t)lane * 8;
+  const uint16_t* lp = mp.lo + (size_t)lane * 8;
+  f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+  for (int t = t0; t < t1; t += U) {
+    u32x4 a0[U], a1[U], bh[U], bl[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {   // steps past t1 are clamped (in bounds) and skipped below
+      const int tt = min(t + u, t1 - 1);
+      a0[u] = load_stream(a0p + 32 * tt);
+      a1[u] = load_stream(a1p + 32 * tt);
+      bh[u] = *reinterpret_cast<const u32x4*>(hp + (size_t)tt * 512);
+      bl[u] = *reinterpret_cast<const u32x4*>(lp + (size_t)tt * 512);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (t + u < t1) {
+        const bf16x8 A0 = __builtin_bit_cast(bf16x8, a0[u]);
+        const bf16x8 A1 = __builtin_bit_cast(bf16x8, a1[u]);
+        const bf16x8 BH = __builtin_bit_cast(bf16x8, bh[u]);
+        const bf16x8 BL = __builtin_bit_cast(bf16x8, bl[u]);
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BH, c0, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BL, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BH, c1, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BL, c1, 0, 0, 0);
+      }
+    }
+  }
+  red[wid][0][lane] = c0;
+  red[wid][1][lane] = c1;
+  __syncthreads();
+
+  // thread (l, i): lane l's element i of both tiles, summed over the waves in wave order.
+  // Tile element (l, i) is weight row tile_base + 4(l/16) + i and activation row l % 16.
+  const int l = tid >> 2, i = tid & 3;
+  float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int w = 0; w < kBlock / 64; ++w) {
+    a += red[w][0][l][i];
+    b += red[w][1][l][i];
+  }
+  const int r = l % 16;
+  if (r >= p.rows) return;
+  const int e = 4 * (l / 16) + i;           // row within the tile
+  const SlotLayout sl{p.rows};
+  if constexpr (MODE == GEMV_QKV) {
+    int pos = p.slots[sl.pos() + r];
+    const bool ok = pos >= 0 && pos < p.kv.cap;
+    if (!ok) {
+      raise_error(p.status, ERR_POS);
+      pos = 0;
+    }
+    const int half = p.hd / 2;
+    const int idx = tm.idx0 + e;
+    float va = a, vb = b;
+    if (tm.seg != 2) {
+      const float2 cs = reinterpret_cast<const float2*>(p.rope)[(size_t)pos * half + idx];
+      va = a * cs.x - b * cs.y;
+      vb = a * cs.y + b * cs.x;
+    }
+    if (tm.seg == 0) {
+      float* q = p.out + ((size_t)r * p.nq + tm.head) * p.hd;
+      q[idx] = va;
+      q[idx + half] = vb;
+      return;
+    }
+    if (!ok) return;
+    size_t off;
+    if (!p.kv.paged) {
+      off = ((size_t)(r * p.nkv + tm.head) * p.kv.cap + pos) * p.hd;
+    } else {
+      const int slot = p.slots[sl.write_map() + r];
+      if (slot < 0 || slot >= p.kv.pool_pages * p.kv.page_size) {
+        raise_error(p.status, ERR_WRITE_MAP);
+        return;
+      }
+      off = ((size_t)((slot / p.kv.page_size) * p.nkv + tm.head) * p.kv.page_size + slot % p.kv.page_size) * p.hd;
+    }
+    // k: rotary partners (element idx and idx + hd/2); v: elements idx and idx + 16 of the head
+    KT* dst = reinterpret_cast<KT*>(tm.seg == 1 ? p.kv.k : p.kv.v) + (size_t)p.layer * p.kv.layer_stride + off + idx;
+    store_kv(dst, va);
+    store_kv(dst + (tm.seg == 1 ? half : 16), vb);
+  } else if constexpr (MODE == GEMV_GATEUP) {
+    const float silu = a / (1.0f + expf(-a));
+    p.out[(size_t)r * p.n_pairs + tm.row0 + e] = silu * b;
+  } else if constexpr (MODE == GEMV_RESID) {
+    float* x = p.out + (size_t)r * 2 * p.n_pairs;
+    x[tm.row0 + e] += a;
+    x[tm.row1 + e] += b;
+  } else {  // GEMV_HEAD
+    float* lg = p.out + (size_t)r * 2 * p.n_pairs;
+    lg[tm.row0 + e] = a;
+    lg[tm.row1 + e] = b;
+    if (!isfinite(a) || !isfinite(b)) atomicOr(&p.status->nonfinite, 1u);
+  }
+}
+
+// ----------------------------------------------------------------------------------------------------------
 // Attention: split sweep over the whole [cap] of one (row, kv head), all G query heads of the group at once.
 //
 // grid = (splits, nkv, rows); block = 256 threads; each block owns positions [s*T, s*T + T) of one kv head and
@@ -913,6 +1095,29 @@ hipError_t launch_attention(const AttnParams& p, int kv_dtype, int rows, hipStre
     if (p.hd == 128) return attn_g<float, 128>(p, rows, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_split(const SplitParams& p, bool norm, hipStream_t s) {
+  if (norm) split_kernel<true><<<kMfmaRows, kBlock, 0, s>>>(p);
+  else split_kernel<false><<<kMfmaRows, kBlock, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <typename KT>
+static hipError_t gemm_go(const MfmaParams& p, int mode, hipStream_t s) {
+  switch (mode) {
+    case GEMV_QKV: gemm_mfma_kernel<KT, GEMV_QKV><<<p.n_units, kBlock, 0, s>>>(p); break;
+    case GEMV_GATEUP: gemm_mfma_kernel<KT, GEMV_GATEUP><<<p.n_units, kBlock, 0, s>>>(p); break;
+    case GEMV_RESID: gemm_mfma_kernel<KT, GEMV_RESID><<<p.n_units, kBlock, 0, s>>>(p); break;
+    case GEMV_HEAD: gemm_mfma_kernel<KT, GEMV_HEAD><<<p.n_units, kBlock, 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mfma(const MfmaParams& p, int mode, int kv_dtype, hipStream_t s) {
+  if (mode == GEMV_QKV && kv_dtype != 1) return gemm_go<float>(p, mode, s);
+  return gemm_go<uint16_t>(p, mode, s);
 }
 
 hipError_t launch_kv_copy(const KvView& kv, int kv_dtype, int layer, int row, int pos0, int n, int nkv, int hd,
