@@ -10,8 +10,11 @@ One step = write the slot buffers, one HIP-graph replay of every kernel of the s
 the greedy token on the host. `value` is decode tokens/s over the timed steps (rows x steps / wall time).
 
 Printed as one JSON line, with:
-  roofline      the dominant kernel's achieved HBM bandwidth (algorithmic bytes per launch / mean launch time,
-                HIP events on the engine's stream) against MI355X's 8 TB/s;
+  roofline      the dominant kernel's achieved HBM bandwidth against MI355X's 8 TB/s: algorithmic bytes per
+                launch / mean launch time, where each kernel kind's launches of a step are replayed as a graph of
+                their own between HIP events on the engine's stream; `traffic` is the HBM bytes per launch from
+                the committed rocprofv3 counter summary of that kernel (null if none, or if the kernel source
+                changed since);
   step          whole-step device time (HIP events around the replay) and bytes, kernels per step, host submit
                 time for the graph replay and for one-launch-per-kernel;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload on this host.
@@ -64,13 +67,30 @@ def engine_for(w, ws, exec_mode):
 
 
 def prefill(eng, w, start_pos):
+    """Initial state: the page table (paged layout) and N(0,1) K/V for positions [0, start) of every row; or, for
+    a workload that starts from a prompt, the prompt tokens fed as one-token steps (positions 0..len-1)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import synth
-    for r in range(w.rows):
-        n = int(start_pos[r])
-        if n == 0:
-            continue
-        for li in range(w.model.n_layers):
-            eng.write_kv(li, r, 0, synth.kv_prefill(w, li, r, "k", n), synth.kv_prefill(w, li, r, "v", n))
+    if w.kv_layout == "paged":
+        eng.set_slot_map(synth.page_table(w))
+    if w.start == "prefill_tokens":
+        toks = synth.prefill_tokens(w)
+        for p in range(w.prefill_len):
+            eng.step(toks[:, p], np.full(w.rows, p, np.int32), copy_logits=False)
+        return
+    jobs = [(li, r, int(start_pos[r])) for r in range(w.rows) for li in range(w.model.n_layers) if start_pos[r] > 0]
+
+    def gen(job):
+        li, r, n = job
+        return li, r, synth.kv_prefill(w, li, r, "k", n), synth.kv_prefill(w, li, r, "v", n)
+
+    t0 = time.time()
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        for i, (li, r, k, v) in enumerate(ex.map(gen, jobs)):
+            eng.write_kv(li, r, 0, k, v)
+            if (i + 1) % 64 == 0:
+                log(f"K/V prefill {i + 1}/{len(jobs)} (layer, row) pairs, {time.time() - t0:.0f}s")
 
 
 def cpu_baseline(w, ws, start_pos, start_tok, budget_s: float) -> dict:
@@ -90,10 +110,55 @@ def cpu_baseline(w, ws, start_pos, start_tok, budget_s: float) -> dict:
         if time.time() - t0 >= budget_s or steps >= 32:
             break
     dt = time.time() - t0
-    return {"value": steps * w.rows / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+    return {"value": steps / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": f"{steps} greedy decode step(s) of row 0 from position {int(start_pos[0])}, all "
                       f"{w.model.n_layers} layers and the head, float64, weights widened per 256-row block",
             "seconds": round(dt, 2)}
+
+
+KERNEL_SOURCE = os.path.join(ROOT, "decode_step_03_amd", "csrc", "ds3_kernels.hip")
+
+
+def pmc_traffic(kind: str, workload: str):
+    """HBM bytes per launch of kernel kind `kind` on `workload`, from the committed rocprofv3 counter summary
+    profiles/pmc_<kind>_<workload>.md (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the counter
+    reads for a plain copy of known size). None when there is no summary, or when the kernel source has changed
+    since the counters were taken (the summary records the source's SHA-256)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"pmc_{kind}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    try:
+        with open(KERNEL_SOURCE, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != vals["kernel_source_sha256"]:
+                return None
+        return (float(vals["fetch_kib_per_launch"]) * float(vals["fetch_scale"])
+                + float(vals["write_kib_per_launch"]) * float(vals["write_scale"])) * 1024.0
+    except (KeyError, ValueError, OSError):
+        return None
+
+
+def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 5) -> int:
+    """A plain copy kernel of known size: each launch reads and writes exactly `nbytes`. A hardware byte counter
+    read over these launches gives the factor that turns the counter's units into bytes."""
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda:0").fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / reps
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": reps,
+                      "us_per_launch": round(us, 1), "gbs": round(2 * nbytes / us / 1e3, 1)}), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -106,6 +171,8 @@ def main() -> int:
     ap.add_argument("--eager-steps", type=int, default=16, help="steps of the one-launch-per-kernel comparison")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device-to-device copy of known size (for scaling HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -116,6 +183,9 @@ def main() -> int:
 
     import torch
 
+    if args.copy_calibration:
+        return copy_calibration(torch)
+
     import synth
     w = synth.workload(args.workload)
     m = w.model
@@ -124,8 +194,6 @@ def main() -> int:
     log(f"weights drawn in {time.time() - t0:.1f}s ({m.n_params() / 1e9:.2f} B parameters)")
     start_pos = synth.start_positions(w)
     start_tok = synth.start_tokens(w)
-    if w.start == "prefill_tokens":
-        raise SystemExit("bench.py times decode; use a workload that starts from pre-filled K/V or position 0")
 
     t0 = time.time()
     eng = engine_for(w, ws, "graph")
@@ -136,7 +204,10 @@ def main() -> int:
     tok = start_tok.copy()
     total = args.warmup + args.steps
     if int(pos.max()) + total > w.cap:
-        raise SystemExit("warmup + steps run past the KV capacity")
+        total = w.cap - int(pos.max())
+        args.steps = max(1, total - args.warmup)
+        total = args.warmup + args.steps
+        log(f"steps limited to {args.steps} by the KV capacity")
     wall, gpu_us, submit_us = [], [], []
     torch.cuda.synchronize()
     for i in range(total):
@@ -168,8 +239,10 @@ def main() -> int:
     per_launch_bytes = dom["bytes_per_step"] / dom["launches"]
     per_launch_us = dom["us_per_step"] / dom["launches"]
     achieved = per_launch_bytes / per_launch_us / 1e3
+    traffic = pmc_traffic(dom["name"], w.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom["name"],
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": round(traffic) if traffic is not None else None, "kernel": dom["name"],
                 "bytes_per_launch": per_launch_bytes, "us_per_launch": round(per_launch_us, 3)}
     eng.close()
     del eng
@@ -199,8 +272,9 @@ def main() -> int:
         cpu = cpu_baseline(w, ws, start_pos, start_tok, args.cpu_baseline_seconds)
         log(f"cpu oracle {cpu['value']:.4f} tok/s on {cpu['cores']} threads")
 
+    metric = METRIC if w.name == "llama8b-bf16-cap8192" else f"decode tokens/s + % HBM roofline, {w.name}"
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(tok_s, 2),
         "unit": "tokens/s",
         "n_gpus": 1,

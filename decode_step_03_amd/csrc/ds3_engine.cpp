@@ -129,6 +129,8 @@ ds3_status poison(ds3_engine* e, ds3_status st, const std::string& msg) {
       return poison((e), DS3_E_DEVICE_LOST, std::string(#call) + ": " + hipGetErrorString(_h));         \
   } while (0)
 
+void plan_splits(const ds3_config& c, int* splits, int* split_len);
+
 std::string check_config(const ds3_config* c) {
   if (!c) return "config is NULL";
   if (c->abi_version != DS3_ABI_VERSION) return "abi_version mismatch";
@@ -154,8 +156,16 @@ std::string check_config(const ds3_config* c) {
     if (c->cap % c->page_size) return "cap must be a multiple of page_size";
     if (c->pool_pages < 1) return "pool_pages must be >= 1";
     if ((int64_t)c->pool_pages * c->page_size > INT32_MAX) return "pool_pages * page_size must fit int32";
+    if (c->page_size & (c->page_size - 1)) return "page_size must be a power of two";
   } else if (c->kv_layout != DS3_KV_CONTIGUOUS) {
     return "kv_layout must be DS3_KV_CONTIGUOUS or DS3_KV_PAGED";
+  }
+  {
+    int splits = 0, split_len = 0;
+    plan_splits(*c, &splits, &split_len);
+    if (attn_lds_bytes(c->n_q_heads, c->n_kv_heads, c->head_dim, split_len, c->kv_dtype,
+                       c->kv_layout == DS3_KV_PAGED ? c->page_size : 0) > 160 * 1024)
+      return "cap / page_size: the attention page table of a split does not fit the 160 KB LDS";
   }
   if (c->rows <= kMaxGemvRows) {
     const int kres = std::max(c->ffn_dim, c->n_q_heads * c->head_dim);
@@ -177,7 +187,7 @@ int env_int(const char* name, int dflt) {
   return x > 0 ? x : dflt;
 }
 
-// Attention split plan: about DS3_ATTN_BLOCKS blocks (default 512, two per CU) over rows x kv heads x splits.
+// Attention split plan: about DS3_ATTN_BLOCKS blocks (default 512) over rows x kv heads x splits.
 // A split is a whole number of LDS chunks, and there are no more splits than the in-kernel merge takes.
 void plan_splits(const ds3_config& c, int* splits, int* split_len) {
   const int chunk = attn_positions_per_pass(c.head_dim, c.kv_dtype);
@@ -893,49 +903,67 @@ ds3_status ds3_stats_get(const ds3_engine* e, ds3_stats* out) {
   return DS3_OK;
 }
 
+// Each kernel kind's launches of one step (in step order) are captured as a graph of their own and replayed
+// `iters` times between two HIP events: the device time of that kind per step, measured as the step graph runs
+// kernels (back to back, no host launch between them). A kind with fewer than 32 launches per step is captured
+// repeated up to at least 32 kernels, and its time divided accordingly. One whole step then runs again with the same slots, which
+// restores the K/V entries at the slot positions and the work buffers the replays overwrote.
 ds3_status ds3_profile_kernels(ds3_engine* e, int32_t iters, ds3_kernel_time* out, int32_t* n_inout) {
   if (ds3_status st = refuse_if_unusable(e)) return st;
   if (e->state != ST_READY) return fail(e, DS3_E_NOT_LOADED, "engine is not ready");
   if (!out || !n_inout || *n_inout < K_NUM || iters < 1) return fail(e, DS3_E_INVALID, "need room for the kernel kinds");
-  const size_t nk = e->sequence.size();
-  std::vector<hipEvent_t> evs(2 * nk, nullptr);
-  for (auto& ev : evs) HIP_OR_POISON(e, hipEventCreate(&ev));
   std::vector<double> tot(K_NUM, 0.0);
   std::vector<int> cnt(K_NUM, 0);
   for (const Launch& l : e->sequence) cnt[l.kind]++;
-  ds3_status result = DS3_OK;
-  for (int it = 0; it < iters && result == DS3_OK; ++it) {
-    e->h_status->err = 0;
-    e->h_status->nonfinite = 0;
-    hipError_t h = hipMemcpyAsync(e->status, e->h_status, sizeof(StatusWords), hipMemcpyHostToDevice, e->stream);
-    for (size_t i = 0; i < nk && h == hipSuccess; ++i) {
-      h = hipEventRecord(evs[2 * i], e->stream);
-      if (h == hipSuccess) h = enqueue_kernel(e, e->sequence[i]);
-      if (h == hipSuccess) h = hipEventRecord(evs[2 * i + 1], e->stream);
+  e->h_status->err = 0;
+  e->h_status->nonfinite = 0;
+  HIP_OR_POISON(e, hipMemcpyAsync(e->status, e->h_status, sizeof(StatusWords), hipMemcpyHostToDevice, e->stream));
+  for (int k = 0; k < K_NUM; ++k) {
+    if (!cnt[k]) continue;
+    // a kind with few launches per step (embed, LM head) is repeated so that the graph holds at least 32
+    // kernels and the replay's own launch latency is spread thin
+    const int reps = (32 + cnt[k] - 1) / cnt[k];
+    HIP_OR_POISON(e, hipStreamBeginCapture(e->stream, hipStreamCaptureModeThreadLocal));
+    hipError_t h = hipSuccess;
+    for (int rep = 0; rep < reps; ++rep)
+      for (const Launch& l : e->sequence)
+        if (l.kind == k && h == hipSuccess) h = enqueue_kernel(e, l);
+    hipGraph_t g = nullptr;
+    hipError_t h2 = hipStreamEndCapture(e->stream, &g);
+    if (h != hipSuccess || h2 != hipSuccess) {
+      if (g) (void)hipGraphDestroy(g);
+      return poison(e, DS3_E_DEVICE_LOST, std::string("profile capture: ") + hipGetErrorString(h != hipSuccess ? h : h2));
     }
+    hipGraphExec_t x = nullptr;
+    h = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+    if (h == hipSuccess) h = hipGraphLaunch(x, e->stream);   // warm-up replay
+    if (h == hipSuccess) h = hipEventRecord(e->ev0, e->stream);
+    for (int it = 0; it < iters && h == hipSuccess; ++it) h = hipGraphLaunch(x, e->stream);
+    if (h == hipSuccess) h = hipEventRecord(e->ev1, e->stream);
     if (h == hipSuccess) h = hipEventRecord(e->ev_done, e->stream);
+    ds3_status st = DS3_OK;
     if (h != hipSuccess) {
-      result = poison(e, DS3_E_DEVICE_LOST, std::string("profile: ") + hipGetErrorString(h));
-      break;
+      st = poison(e, DS3_E_DEVICE_LOST, std::string("profile: ") + hipGetErrorString(h));
+    } else {
+      e->pending = true;
+      st = wait_done(e, e->ev_done, e->cfg.timeout_ms);
     }
-    e->pending = true;
-    result = wait_done(e, e->ev_done, e->cfg.timeout_ms);
-    if (result != DS3_OK) break;
-    for (size_t i = 0; i < nk; ++i) {
-      float ms = 0.f;
-      if (hipEventElapsedTime(&ms, evs[2 * i], evs[2 * i + 1]) != hipSuccess) {
-        result = poison(e, DS3_E_DEVICE_LOST, "profile: event timing failed");
-        break;
-      }
-      tot[e->sequence[i].kind] += ms * 1e3;
-    }
+    float ms = 0.f;
+    if (st == DS3_OK && hipEventElapsedTime(&ms, e->ev0, e->ev1) != hipSuccess)
+      st = poison(e, DS3_E_DEVICE_LOST, "profile: event timing failed");
+    if (x) (void)hipGraphExecDestroy(x);
+    (void)hipGraphDestroy(g);
+    if (st != DS3_OK) return st;
+    tot[k] = ms * 1e3 / ((double)iters * reps);
   }
-  for (auto& ev : evs) (void)hipEventDestroy(ev);
-  if (result != DS3_OK) return result;
+  HIP_OR_POISON(e, enqueue_step(e));
+  HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
+  e->pending = true;
+  if (ds3_status st = wait_done(e, e->ev_done, e->cfg.timeout_ms)) return st;
   for (int k = 0; k < K_NUM; ++k) {
     std::snprintf(out[k].name, sizeof(out[k].name), "%s", kKindNames[k]);
     out[k].launches = cnt[k];
-    out[k].total_us = tot[k] / iters;
+    out[k].total_us = tot[k];
     out[k].bytes = kind_bytes(e->cfg, k);
   }
   *n_inout = K_NUM;

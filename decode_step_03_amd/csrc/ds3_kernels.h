@@ -133,7 +133,7 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t s)
 
 size_t gemv_lds_bytes(int rows, int K, bool norm);
 int attn_positions_per_pass(int hd, int kv_dtype);
-size_t attn_lds_bytes(int nq, int nkv, int hd, int split_len, int splits, int kv_dtype);
+size_t attn_lds_bytes(int nq, int nkv, int hd, int split_len, int kv_dtype, int page_size /* 0: contiguous */);
 int attn_max_splits(int nq, int nkv, int hd);   // splits the in-kernel merge can take
 
 }  // namespace ds3

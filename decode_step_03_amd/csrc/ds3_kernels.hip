@@ -29,7 +29,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBlock = 256;
 constexpr int kUnroll = 8;   // 16-byte loads in flight per lane per weight row
 constexpr int kMaxSplitsPerLane = 32;   // attention split merge: partials one lane holds in registers
-constexpr int kAttnChunk = 128;         // attention: positions staged in LDS at a time
+constexpr int kAttnChunk = 128;         // attention: positions staged in LDS per chunk, at most ...
+constexpr int kAttnChunkBytes = 32768;  // ... and at most this many bytes of K (and of V)
 
 __device__ __forceinline__ u32x4 load_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -136,18 +137,37 @@ __device__ __forceinline__ size_t kv_offset(const KvView& kv, int r, int nkv, in
 // ----------------------------------------------------------------------------------------------------------
 // embedding
 
+// grid = (d / (8 * kBlock) rounded up, rows): each thread moves 8 consecutive elements of the row with one
+// 16-byte (bf16) or two 16-byte (fp32) loads.
 template <typename WT>
 __global__ void __launch_bounds__(kBlock) embed_kernel(EmbedParams p) {
-  const int r = blockIdx.x;
+  const int r = blockIdx.y;
   SlotLayout sl{p.rows};
   int token = p.slots[sl.token() + r];
   if (token < 0 || token >= p.vocab) {
-    if (threadIdx.x == 0) raise_error(p.status, ERR_TOKEN);
+    if (threadIdx.x == 0 && blockIdx.x == 0) raise_error(p.status, ERR_TOKEN);
     token = 0;
   }
-  if (r == 0 && threadIdx.x == 0 && p.slots[sl.inject()] != 0) raise_error(p.status, ERR_INJECTED);
-  const WT* row = reinterpret_cast<const WT*>(p.table) + (size_t)token * p.d;
-  for (int k = threadIdx.x; k < p.d; k += kBlock) p.x[(size_t)r * p.d + k] = widen1(row[k]);
+  if (r == 0 && blockIdx.x == 0 && threadIdx.x == 0 && p.slots[sl.inject()] != 0) raise_error(p.status, ERR_INJECTED);
+  const int k0 = (blockIdx.x * kBlock + threadIdx.x) * 8;
+  if (k0 >= p.d) return;
+  const WT* row = reinterpret_cast<const WT*>(p.table) + (size_t)token * p.d + k0;
+  float v[8];
+  if constexpr (sizeof(WT) == 2) {
+    Pack<uint16_t>::widen(*reinterpret_cast<const u32x4*>(row), v);
+  } else {
+    float a[4], b[4];
+    Pack<float>::widen(*reinterpret_cast<const u32x4*>(row), a);
+    Pack<float>::widen(*reinterpret_cast<const u32x4*>(row + 4), b);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = a[e];
+      v[4 + e] = b[e];
+    }
+  }
+  float4* dst = reinterpret_cast<float4*>(p.x + (size_t)r * p.d + k0);
+  dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+  dst[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
 // ----------------------------------------------------------------------------------------------------------
@@ -443,37 +463,55 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// grid = (K / (8 * kBlock) rounded up, 16 rows): each thread turns 8 consecutive inputs of one row into one 16-byte
+// hi store and one 16-byte lo store in fragment order. With the RMSNorm, every block of a row first reduces that
+// row's sum of squares itself (the same order in every block, so the scale is identical across the row's blocks).
 template <bool NORM>
 __global__ void __launch_bounds__(kBlock) split_kernel(SplitParams p) {
-  const int r = blockIdx.x;   // activation row of the tile (rows >= p.rows are zero padding)
+  const int r = blockIdx.y;   // activation row of the tile (rows >= p.rows are zero padding)
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  __shared__ float red[kBlock / 64];
   const bool live = r < p.rows;
   const float* x = p.in + (size_t)(live ? r : 0) * p.K;
+  const int k0 = (blockIdx.x * kBlock + tid) * 8;
   float scale = 1.f;
   if constexpr (NORM) {
+    __shared__ float red[kBlock / 64];
     float ss = 0.f;
-    for (int k = tid; k < p.K; k += kBlock) {
-      const float v = x[k];
-      ss += v * v;
+    for (int k = tid * 4; k < p.K; k += kBlock * 4) {
+      const float4 v = *reinterpret_cast<const float4*>(x + k);
+      ss += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
     }
     ss = wave_sum(ss);
     if (lane == 0) red[wid] = ss;
     __syncthreads();
     scale = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)p.K + p.eps);
   }
-  for (int k = tid; k < p.K; k += kBlock) {
-    float v = 0.f;
-    if (live) {
-      v = x[k] * scale;
-      if constexpr (NORM) v *= p.gain[k];
-    }
-    const uint16_t h = to_bf16(v);
-    const uint16_t l = to_bf16(v - widen1(h));
-    const size_t idx = ((size_t)(k >> 5) * 64 + ((k >> 3) & 3) * 16 + r) * 8 + (k & 7);
-    p.hi[idx] = h;
-    p.lo[idx] = l;
+  if (k0 >= p.K) return;
+  float v[8];
+  {
+    const float4 a = *reinterpret_cast<const float4*>(x + k0);
+    const float4 b = *reinterpret_cast<const float4*>(x + k0 + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
+  if constexpr (NORM) {
+    const float4 a = *reinterpret_cast<const float4*>(p.gain + k0);
+    const float4 b = *reinterpret_cast<const float4*>(p.gain + k0 + 4);
+    const float gn[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * scale * gn[e];
+  }
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const float v0 = live ? v[e] : 0.f, v1 = live ? v[e + 1] : 0.f;
+    const uint16_t h0 = to_bf16(v0), h1 = to_bf16(v1);
+    const uint16_t l0 = to_bf16(v0 - widen1(h0)), l1 = to_bf16(v1 - widen1(h1));
+    hw[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    lw[e / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  }
+  const size_t idx = ((size_t)(k0 >> 5) * 64 + ((k0 >> 3) & 3) * 16 + r) * 8;
+  *reinterpret_cast<u32x4*>(p.hi + idx) = u32x4{hw[0], hw[1], hw[2], hw[3]};
+  *reinterpret_cast<u32x4*>(p.lo + idx) = u32x4{lw[0], lw[1], lw[2], lw[3]};
 }
 
 // A unit is a pair of 16-row weight tiles, chosen so the epilogue has what it needs (as PairMap for the GEMV):
@@ -506,15 +544,17 @@ struct TileMap {
   }
 };
 
-template <typename KT, int MODE>
-__global__ void __launch_bounds__(kBlock) gemm_mfma_kernel(MfmaParams mp) {
+// One block per unit; its NW waves split the inputs (split-K) and are summed in wave order. NW grows as the units
+// get fewer, so that a projection with few outputs (o-proj, down) still has enough waves per CU in flight.
+template <typename KT, int MODE, int NW>
+__global__ void __launch_bounds__(64 * NW) gemm_mfma_kernel(MfmaParams mp) {
   const GemvParams& p = mp.g;
   constexpr int U = 8;                       // k-steps of 32 inputs in flight per wave
-  __shared__ f32x4 red[kBlock / 64][2][64];  // split-K partials of the two tiles
+  __shared__ f32x4 red[NW][2][64];           // split-K partials of the two tiles
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int K = p.K;
   const int NS = K / 32;                     // k-steps
-  const int per = (NS + 3) / 4;              // k-steps per wave (split-K over the 4 waves)
+  const int per = (NS + NW - 1) / NW;        // k-steps per wave
   const int t0 = wid * per, t1 = min(NS, t0 + per);
   const TileMap<MODE> tm(p, blockIdx.x);
   const uint16_t* W = reinterpret_cast<const uint16_t*>(p.w);
@@ -550,13 +590,14 @@ __global__ void __launch_bounds__(kBlock) gemm_mfma_kernel(MfmaParams mp) {
   red[wid][0][lane] = c0;
   red[wid][1][lane] = c1;
   __syncthreads();
+  if (tid >= 256) return;
 
-  // thread (l, i): lane l's element i of both tiles, summed over the waves in wave order.
+  // thread (l, i) of the first 256: lane l's element i of both tiles, summed over the waves in wave order.
   // Tile element (l, i) is weight row tile_base + 4(l/16) + i and activation row l % 16.
   const int l = tid >> 2, i = tid & 3;
   float a = 0.f, b = 0.f;
 #pragma unroll
-  for (int w = 0; w < kBlock / 64; ++w) {
+  for (int w = 0; w < NW; ++w) {
     a += red[w][0][l][i];
     b += red[w][1][l][i];
   }
@@ -619,9 +660,9 @@ __global__ void __launch_bounds__(kBlock) gemm_mfma_kernel(MfmaParams mp) {
 // ----------------------------------------------------------------------------------------------------------
 // Attention: split sweep over the whole [cap] of one (row, kv head), all G query heads of the group at once.
 //
-// grid = (splits, nkv, rows); block = 256 threads; each block owns positions [s*T, s*T + T) of one kv head and
-// walks them in LDS chunks of kAttnChunk positions. A chunk's K and V rows are staged in LDS with direct
-// global-to-LDS 16-byte loads (no registers involved, so every load of the chunk is in flight at once), then
+// grid = (splits, nkv, rows); block = 256 threads; each block owns T positions of one kv head and walks them in
+// LDS chunks of TC positions (128, or 32 KB of K if that is fewer), two chunk buffers deep. A chunk's K and V
+// rows are staged in LDS with direct global-to-LDS 16-byte loads (no registers involved, so every load of the chunk is in flight at once), then
 // one wait and one barrier. From LDS, LPP lanes share one position (16 bytes of the head each): the G scores of
 // a position are reduced over those lanes by a butterfly (bit-identical sums in every lane) and folded into a
 // running softmax state per lane group: max m, sum l, weighted value sum o (online softmax, one rescale per UA
@@ -661,14 +702,15 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
   constexpr int LPP = HD / EPL;                  // lanes per position
   constexpr int PPP = kBlock / LPP;              // positions per block pass
   constexpr int PB = HD * (int)sizeof(KT);       // bytes per position
-  constexpr int TC = kAttnChunk;                 // positions per LDS chunk
+  constexpr int TC = kAttnChunkBytes / PB < kAttnChunk ? kAttnChunkBytes / PB : kAttnChunk;   // positions per chunk
   constexpr int NI = TC * PB / 1024;             // 1 KB global-to-LDS instructions per chunk and per K or V
   constexpr int UA = G >= 4 ? 4 : 8;             // positions per lane group per softmax rescale
   static_assert(LPP >= 1 && LPP <= 64 && (64 % LPP) == 0, "lanes per position must divide the wave");
   static_assert(NI % (kBlock / 64) == 0 && TC % PPP == 0, "chunk must split evenly over the waves");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  constexpr int NBUF_MAX = 2;
-  float* wst = reinterpret_cast<float*>(smem + (size_t)NBUF_MAX * 2 * TC * PB);   // [4 waves][G][HD + 2]
+  constexpr int NBUF = 2;
+  float* wst = reinterpret_cast<float*>(smem + (size_t)NBUF * 2 * TC * PB);   // [4 waves][G][HD + 2]
+  int* ptab = reinterpret_cast<int*>(wst + 4 * G * (HD + 2));                 // paged: pool page per chunk page
   __shared__ int s_last;
 
   const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
@@ -700,6 +742,27 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qv[hh][e] = p.q[((size_t)r * p.nq + g * G + hh) * HD + sub * EPL + e];
 
+  // ---- paged: the pool pages of every chunk this split sweeps go to LDS first, so staging a chunk needs no
+  // ordinary global load (which would have to wait behind the previous chunk's rows). Entry (chunk c, q) is the
+  // q-th logical page the chunk covers, clamped to the row's last page; an id outside the pool raises the error
+  // word and reads page 0 instead.
+  const int ps = PAGED ? p.kv.page_size : 1;
+  const int ppc = PAGED ? (ps <= TC ? TC / ps : 1) : 1;   // pages per chunk
+  if constexpr (PAGED) {
+    const int ppr = cap / ps;
+    const int n = ((T + TC - 1) / TC) * ppc;
+    for (int i = tid; i < n; i += kBlock) {
+      const int lp = min(chunk_base((i / ppc) * TC) / ps + i % ppc, ppr - 1);
+      int page = p.kv.slot_map[r * ppr + lp];
+      if (page < 0 || page >= p.kv.pool_pages) {
+        raise_error(p.status, ERR_PAGE);
+        page = 0;
+      }
+      ptab[i] = page;
+    }
+    __syncthreads();
+  }
+
   // ---- stage a chunk's K and V rows into LDS buffer `buf`: instruction k of the block fills bytes
   // [k KB, k KB + 1 KB) of the buffer's K half and of its V half
   auto stage = [&](int c0, int buf) {
@@ -713,13 +776,10 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
       const int jc = min(chunk_base(c0) + tc, cap - 1);   // past the capacity: clamped, never visible
       uint32_t off;
       if constexpr (PAGED) {
-        const int ppr = cap / p.kv.page_size;
-        int page = p.kv.slot_map[r * ppr + jc / p.kv.page_size];
-        if (page < 0 || page >= p.kv.pool_pages) {
-          raise_error(p.status, ERR_PAGE);
-          page = 0;
-        }
-        off = (uint32_t)(((page * p.nkv + g) * p.kv.page_size + (jc % p.kv.page_size)) * HD);
+        const int jb = chunk_base(c0);
+        const int q = min(max(jc / ps - jb / ps, 0), ppc - 1);
+        const int page = ptab[(c0 / TC) * ppc + q];
+        off = (uint32_t)(((page * p.nkv + g) * ps + (jc % ps)) * HD);
       } else {
         off = (uint32_t)(((r * p.nkv + g) * cap + jc) * HD);
       }
@@ -729,11 +789,8 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
     }
   };
   // Both buffers are filled up front; afterwards a buffer is refilled as soon as its chunk has been consumed.
-  // The paged layout reads page ids with ordinary loads, which would wait behind the previous chunk's rows,
-  // so it keeps one chunk in flight.
-  constexpr int NBUF = PAGED ? 1 : 2;
   stage(0, 0);
-  if (NBUF == 2 && TC < T) stage(TC, 1);
+  if (TC < T) stage(TC, 1);
 
   float m[G], l[G], o[G][EPL];
 #pragma unroll
@@ -746,7 +803,7 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
 
   for (int c0 = 0, buf = 0; c0 < T; c0 += TC, buf = (buf + 1) % NBUF) {
     // wait for this chunk's rows only: a later chunk's rows (NI/4 K and NI/4 V loads per wave) may still fly
-    if (NBUF == 2 && c0 + TC < T) __builtin_amdgcn_s_waitcnt(kVmcntChunk<NI / (kBlock / 64) * 2>());
+    if (c0 + TC < T) __builtin_amdgcn_s_waitcnt(kVmcntChunk<NI / (kBlock / 64) * 2>());
     else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const KT* ks = reinterpret_cast<const KT*>(smem + (size_t)buf * 2 * TC * PB);
@@ -972,17 +1029,16 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t value, size_t n) {
 size_t gemv_lds_bytes(int rows, int K, bool norm) { (void)norm; return (size_t)rows * K * sizeof(float); }
 
 int attn_positions_per_pass(int hd, int kv_dtype) {
-  (void)hd;
-  (void)kv_dtype;
-  return kAttnChunk;   // splits are whole LDS chunks
+  return std::min(kAttnChunk, kAttnChunkBytes / (hd * (kv_dtype == 1 ? 2 : 4)));   // splits are whole LDS chunks
 }
 
-size_t attn_lds_bytes(int nq, int nkv, int hd, int split_len, int splits, int kv_dtype) {
-  (void)split_len;
-  (void)splits;
+size_t attn_lds_bytes(int nq, int nkv, int hd, int split_len, int kv_dtype, int page_size) {
   const int G = nq / nkv;
   const size_t pb = (size_t)hd * (kv_dtype == 1 ? 2 : 4);
-  return 2 * 2 * kAttnChunk * pb + (size_t)4 * G * (hd + 2) * sizeof(float);
+  const int tc = attn_positions_per_pass(hd, kv_dtype);
+  size_t bytes = 2 * 2 * tc * pb + (size_t)4 * G * (hd + 2) * sizeof(float);
+  if (page_size > 0) bytes += (size_t)((split_len + tc - 1) / tc) * (page_size <= tc ? tc / page_size : 1) * 4;
+  return bytes;
 }
 
 int attn_max_splits(int nq, int nkv, int hd) {
@@ -1000,8 +1056,10 @@ static hipError_t set_lds(F* f, size_t bytes) {
 }
 
 hipError_t launch_embed(const EmbedParams& p, int weight_dtype, hipStream_t s) {
-  if (weight_dtype == 1) embed_kernel<uint16_t><<<p.rows, kBlock, 0, s>>>(p);
-  else embed_kernel<float><<<p.rows, kBlock, 0, s>>>(p);
+  if (p.d % 8) return hipErrorInvalidValue;
+  const dim3 grid((p.d + 8 * kBlock - 1) / (8 * kBlock), p.rows);
+  if (weight_dtype == 1) embed_kernel<uint16_t><<<grid, kBlock, 0, s>>>(p);
+  else embed_kernel<float><<<grid, kBlock, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -1060,7 +1118,8 @@ hipError_t launch_gemv(const GemvParams& p, int mode, int weight_dtype, int kv_d
 
 template <typename KT, int HD, int GG>
 static hipError_t attn_go(const AttnParams& p, int rows, hipStream_t s) {
-  const size_t lds = attn_lds_bytes(p.nq, p.nkv, HD, p.split_len, p.splits, sizeof(KT) == 2 ? 1 : 0);
+  const size_t lds = attn_lds_bytes(p.nq, p.nkv, HD, p.split_len, sizeof(KT) == 2 ? 1 : 0,
+                                    p.kv.paged ? p.kv.page_size : 0);
   dim3 grid(p.splits, p.nkv, rows);
   hipError_t e;
   if (p.kv.paged) {
@@ -1098,21 +1157,37 @@ hipError_t launch_attention(const AttnParams& p, int kv_dtype, int rows, hipStre
 }
 
 hipError_t launch_split(const SplitParams& p, bool norm, hipStream_t s) {
-  if (norm) split_kernel<true><<<kMfmaRows, kBlock, 0, s>>>(p);
-  else split_kernel<false><<<kMfmaRows, kBlock, 0, s>>>(p);
+  if (p.K % 32) return hipErrorInvalidValue;
+  const dim3 grid((p.K + 8 * kBlock - 1) / (8 * kBlock), kMfmaRows);
+  if (norm) split_kernel<true><<<grid, kBlock, 0, s>>>(p);
+  else split_kernel<false><<<grid, kBlock, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+int mfma_waves_per_unit(int n_units) {
+  // aim for about 8 waves per CU over the 256 CUs
+  return n_units >= 512 ? 4 : (n_units >= 256 ? 8 : 16);
+}
+
+template <typename KT, int NW>
+static hipError_t gemm_nw(const MfmaParams& p, int mode, hipStream_t s) {
+  switch (mode) {
+    case GEMV_QKV: gemm_mfma_kernel<KT, GEMV_QKV, NW><<<p.n_units, 64 * NW, 0, s>>>(p); break;
+    case GEMV_GATEUP: gemm_mfma_kernel<KT, GEMV_GATEUP, NW><<<p.n_units, 64 * NW, 0, s>>>(p); break;
+    case GEMV_RESID: gemm_mfma_kernel<KT, GEMV_RESID, NW><<<p.n_units, 64 * NW, 0, s>>>(p); break;
+    case GEMV_HEAD: gemm_mfma_kernel<KT, GEMV_HEAD, NW><<<p.n_units, 64 * NW, 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 template <typename KT>
 static hipError_t gemm_go(const MfmaParams& p, int mode, hipStream_t s) {
-  switch (mode) {
-    case GEMV_QKV: gemm_mfma_kernel<KT, GEMV_QKV><<<p.n_units, kBlock, 0, s>>>(p); break;
-    case GEMV_GATEUP: gemm_mfma_kernel<KT, GEMV_GATEUP><<<p.n_units, kBlock, 0, s>>>(p); break;
-    case GEMV_RESID: gemm_mfma_kernel<KT, GEMV_RESID><<<p.n_units, kBlock, 0, s>>>(p); break;
-    case GEMV_HEAD: gemm_mfma_kernel<KT, GEMV_HEAD><<<p.n_units, kBlock, 0, s>>>(p); break;
-    default: return hipErrorInvalidValue;
+  switch (mfma_waves_per_unit(p.n_units)) {
+    case 4: return gemm_nw<KT, 4>(p, mode, s);
+    case 8: return gemm_nw<KT, 8>(p, mode, s);
+    default: return gemm_nw<KT, 16>(p, mode, s);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_gemm_mfma(const MfmaParams& p, int mode, int kv_dtype, hipStream_t s) {

@@ -181,9 +181,11 @@ ds3_status ds3_read_kv(ds3_engine* e, int32_t layer, int32_t row, int32_t pos0, 
 
 ds3_status ds3_stats_get(const ds3_engine* e, ds3_stats* out);
 
-/* Run `iters` eager steps with the current slot contents (the last step's tokens and positions, re-written at
- * the same positions) and report each kernel's device time per step, timed with HIP events on the engine's
- * stream. `out` has room for *n_inout entries; on return *n_inout is the number of kernels. */
+/* Per kernel kind, the device time of one step's launches of that kind: they are captured as a graph of their
+ * own (in step order, with the current slot contents) and replayed `iters` times between two HIP events on the
+ * engine's stream. Afterwards one whole step runs again with the same slots, so the K/V entries at the slot
+ * positions and the work buffers hold what the last step left. `out` has room for *n_inout entries (at least the
+ * number of kinds); on return *n_inout is the number of kinds. A HIP failure poisons the engine. */
 ds3_status ds3_profile_kernels(ds3_engine* e, int32_t iters, ds3_kernel_time* out, int32_t* n_inout);
 
 /* Test hook for the failure path: DS3_INJECT_KERNEL_CHECK makes the next step's first kernel raise its check

@@ -175,3 +175,28 @@ def test_capacity_not_multiple_of_split():
         ls.check_kv(0, 0, 997, 3)
     finally:
         eng.close()
+
+
+def test_profile_kernels_times_every_kind_and_restores_state():
+    """Per-kind kernel timing (each kind's launches replayed as a graph of their own) reports every kernel kind
+    of the step with a positive time, and leaves the state as the last step left it: decoding continues in
+    parity with the oracle, and the K/V at the profiled position still match it."""
+    w = synth.workload("tiny-fp32")
+    ws = synth.make_weights(w.model)
+    ls, eng = _run_greedy(w, ws, 6, synth.start_positions(w))
+    try:
+        kinds = eng.profile_kernels(3)
+        names = {k["name"] for k in kinds if k["launches"]}
+        assert {"embed", "qkv_rope_kvwrite", "attention_splitk", "o_proj_residual", "gateup_swiglu",
+                "down_proj_residual", "lm_head"} <= names
+        for k in kinds:
+            if k["launches"]:
+                assert k["us_per_step"] > 0 and k["bytes_per_step"] > 0, k
+        for li in range(w.model.n_layers):
+            ls.check_kv(li, 0, 0, 6)
+        tokens = np.array([11], np.int32)
+        for p in range(6, 10):
+            _, ref, _ = ls.step(tokens, np.array([p], np.int32))
+            tokens = np.array([int(np.argmax(ref[0]))], np.int32)
+    finally:
+        eng.close()
