@@ -30,15 +30,16 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 size_t dtype_bytes(int dt) { return dt == DS3_BF16 ? 2 : 4; }
 
 struct WorkPlan {
-  size_t slots, status, x, q, attn, act, part, counters, rope, slot_map, frag_hi, frag_lo, total;
+  size_t slots, status, x, q, attn, act, part, rope, slot_map, frag_hi, frag_lo, total;
 };
 
 struct KernelKind {
   const char* name;
 };
-enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN, K_HEAD, K_SPLIT, K_NUM };
+enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN, K_HEAD, K_SPLIT, K_COMBINE, K_NUM };
 const char* kKindNames[K_NUM] = {"embed", "qkv_rope_kvwrite", "attention_splitk", "o_proj_residual",
-                                 "gateup_swiglu", "down_proj_residual", "lm_head", "act_split_mfma"};
+                                 "gateup_swiglu", "down_proj_residual", "lm_head", "act_split_mfma",
+                                 "attention_combine"};
 
 // activation sites the MFMA path splits into bf16 hi/lo operands
 enum Site { S_ATTN_NORM = 0, S_ATTN_OUT, S_FFN_NORM, S_ACT, S_FINAL_NORM };
@@ -62,7 +63,6 @@ struct ds3_engine {
   int* slots = nullptr;
   StatusWords* status = nullptr;
   float *x = nullptr, *q = nullptr, *attn = nullptr, *act = nullptr, *part = nullptr, *rope = nullptr;
-  unsigned* counters = nullptr;
   int* slot_map = nullptr;
   float* logits = nullptr;
   uint16_t *frag_hi = nullptr, *frag_lo = nullptr;   // MFMA path: activation operands
@@ -160,6 +160,17 @@ std::string check_config(const ds3_config* c) {
   } else if (c->kv_layout != DS3_KV_CONTIGUOUS) {
     return "kv_layout must be DS3_KV_CONTIGUOUS or DS3_KV_PAGED";
   }
+  if (c->kv_dtype == DS3_BF16) {
+    // matrix-core attention: V is stored transposed and read in groups of 8 positions
+    if (c->cap % 8) return "cap must be a multiple of 8 with bf16 K/V";
+    if (c->kv_layout == DS3_KV_PAGED && c->page_size < 8) return "page_size must be >= 8 with bf16 K/V";
+  }
+  {
+    const int64_t per_layer = c->kv_layout == DS3_KV_PAGED
+                                  ? (int64_t)c->pool_pages * c->n_kv_heads * c->page_size * c->head_dim
+                                  : (int64_t)c->rows * c->n_kv_heads * c->cap * c->head_dim;
+    if (per_layer > INT32_MAX) return "cap / pool_pages: one layer's K must hold fewer than 2^31 elements";
+  }
   {
     int splits = 0, split_len = 0;
     plan_splits(*c, &splits, &split_len);
@@ -217,9 +228,7 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
   w.q = take((size_t)c.rows * c.n_q_heads * c.head_dim * 4);
   w.attn = take((size_t)c.rows * c.n_q_heads * c.head_dim * 4);
   w.act = take((size_t)c.rows * c.ffn_dim * 4);
-  const size_t sp = splits <= 4 ? 4 : (splits <= 8 ? 8 : (splits <= 16 ? 16 : 32));   // padded split index
-  w.part = take((size_t)c.rows * c.n_kv_heads * G * (c.head_dim + 2) * sp * 4);
-  w.counters = take((size_t)c.rows * c.n_kv_heads * 4);
+  w.part = take((size_t)c.rows * c.n_kv_heads * splits * G * (c.head_dim + 2) * 4);
   w.rope = take((size_t)c.cap * (c.head_dim / 2) * 2 * 4);
   w.slot_map = take(c.kv_layout == DS3_KV_PAGED ? (size_t)c.rows * (c.cap / c.page_size) * 4 : 4);
   const size_t kmax = (size_t)std::max(std::max(c.d_model, c.ffn_dim), c.n_q_heads * c.head_dim);
@@ -378,12 +387,12 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.n_pairs = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim / 2;
       return run_projection(e, p, GEMV_QKV, K_QKV);
     }
-    case K_ATTN: {
+    case K_ATTN:
+    case K_COMBINE: {
       AttnParams p{};
       p.q = e->q;
       p.out = e->attn;
       p.part = e->part;
-      p.counters = e->counters;
       p.kv = e->kv;
       p.layer = l.layer;
       p.nq = c.n_q_heads;
@@ -394,7 +403,8 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.scale = (float)(1.0 / std::sqrt((double)c.head_dim));
       p.slots = e->slots;
       p.status = e->status;
-      return launch_attention(p, c.kv_dtype, R, e->stream);
+      return l.kind == K_ATTN ? launch_attention(p, c.kv_dtype, R, e->stream)
+                              : launch_attention_combine(p, R, e->stream);
     }
     case K_OPROJ: {
       GemvParams p{};
@@ -540,7 +550,6 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   e->attn = reinterpret_cast<float*>(work + wp.attn);
   e->act = reinterpret_cast<float*>(work + wp.act);
   e->part = reinterpret_cast<float*>(work + wp.part);
-  e->counters = reinterpret_cast<unsigned*>(work + wp.counters);
   e->rope = reinterpret_cast<float*>(work + wp.rope);
   e->slot_map = reinterpret_cast<int*>(work + wp.slot_map);
   e->frag_hi = reinterpret_cast<uint16_t*>(work + wp.frag_hi);
@@ -566,6 +575,7 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   e->kv.v = reinterpret_cast<char*>(e->buf[DS3_BUF_KV]) + e->kv_bytes / 2;
   e->kv.layer_stride = (int64_t)(e->kv_bytes / 2 / kvb / c.n_layers);
   e->kv.paged = c.kv_layout == DS3_KV_PAGED;
+  e->kv.v_t = c.kv_dtype == DS3_BF16;   // the matrix-core attention reads V position-contiguous
   e->kv.cap = c.cap;
   e->kv.page_size = e->kv.paged ? c.page_size : 1;
   e->kv.pool_pages = e->kv.paged ? c.pool_pages : 0;
@@ -584,6 +594,7 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
     if (e->mfma) e->sequence.push_back({K_SPLIT, l, S_ATTN_NORM});
     e->sequence.push_back({K_QKV, l, 0});
     e->sequence.push_back({K_ATTN, l, 0});
+    e->sequence.push_back({K_COMBINE, l, 0});
     if (e->mfma) e->sequence.push_back({K_SPLIT, l, S_ATTN_OUT});
     e->sequence.push_back({K_OPROJ, l, 0});
     if (e->mfma) e->sequence.push_back({K_SPLIT, l, S_FFN_NORM});
@@ -616,7 +627,7 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
         tab[((size_t)p * half + i) * 2 + 1] = (float)std::sin(ang);
       }
     h = hipMemcpyAsync(e->rope, tab.data(), tab.size() * 4, hipMemcpyHostToDevice, e->stream);
-    if (h == hipSuccess) h = hipMemsetAsync(e->slots, 0, wp.rope, e->stream);  // slots .. counters
+    if (h == hipSuccess) h = hipMemsetAsync(e->slots, 0, wp.rope, e->stream);  // slots .. partials
     if (h == hipSuccess) h = hipMemsetAsync(e->buf[DS3_BUF_KV], 0, e->kv_bytes, e->stream);
     if (h == hipSuccess) h = hipStreamSynchronize(e->stream);
     if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("create upload: ") + hipGetErrorString(h));
@@ -840,7 +851,6 @@ ds3_status ds3_step(ds3_engine* e, const int32_t* tokens, const int32_t* pos, co
 ds3_status ds3_reset_state(ds3_engine* e) {
   if (ds3_status st = refuse_if_unusable(e)) return st;
   HIP_OR_POISON(e, hipMemsetAsync(e->buf[DS3_BUF_KV], 0, e->kv_bytes, e->stream));
-  HIP_OR_POISON(e, launch_fill_u32(e->counters, 0u, (size_t)e->cfg.rows * e->cfg.n_kv_heads, e->stream));
   HIP_OR_POISON(e, launch_fill_u32(reinterpret_cast<uint32_t*>(e->status), 0u, 2, e->stream));
   HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
   e->pending = true;
@@ -869,20 +879,41 @@ static ds3_status kv_transfer(ds3_engine* e, int32_t layer, int32_t row, int32_t
     e->kv_staging_bytes = 2 * half;
   }
   char* stg = reinterpret_cast<char*>(e->kv_staging);
+  // A transposed V state is staged as [nkv][hd][n] (the copy kernel then walks the state contiguously); the host
+  // array is always [nkv][n][hd], so V is transposed on the host on the way in and on the way out.
+  const bool vt = e->kv.v_t;
+  const int nkv = c.n_kv_heads, hd = c.head_dim;
+  auto transpose = [&](const char* src, char* dst, bool to_t) {
+    // [nkv][n][hd] <-> [nkv][hd][n], in tiles of 64 positions so both sides stay cache-friendly
+    auto run = [&](auto* d, const auto* s2) {
+      for (int g = 0; g < nkv; ++g)
+        for (int t0 = 0; t0 < n; t0 += 64)
+          for (int x = 0; x < hd; ++x)
+            for (int t = t0; t < std::min(n, t0 + 64); ++t) {
+              const size_t a = ((size_t)g * n + t) * hd + x, b = ((size_t)g * hd + x) * n + t;
+              if (to_t) d[b] = s2[a];
+              else d[a] = s2[b];
+            }
+    };
+    if (kvb == 2) run(reinterpret_cast<uint16_t*>(dst), reinterpret_cast<const uint16_t*>(src));
+    else run(reinterpret_cast<uint32_t*>(dst), reinterpret_cast<const uint32_t*>(src));
+  };
+  std::vector<char> vtmp(vt ? half : 0);
   if (to_state) {
+    if (vt) transpose(reinterpret_cast<const char*>(v), vtmp.data(), true);
     HIP_OR_POISON(e, hipMemcpyAsync(stg, k, half, hipMemcpyHostToDevice, e->stream));
-    HIP_OR_POISON(e, hipMemcpyAsync(stg + half, v, half, hipMemcpyHostToDevice, e->stream));
-    HIP_OR_POISON(e, launch_kv_copy(e->kv, c.kv_dtype, layer, row, pos0, n, c.n_kv_heads, c.head_dim, stg, 1,
-                                    e->status, e->stream));
+    HIP_OR_POISON(e, hipMemcpyAsync(stg + half, vt ? vtmp.data() : v, half, hipMemcpyHostToDevice, e->stream));
+    HIP_OR_POISON(e, launch_kv_copy(e->kv, c.kv_dtype, layer, row, pos0, n, nkv, hd, stg, 1, e->status, e->stream));
   } else {
-    HIP_OR_POISON(e, launch_kv_copy(e->kv, c.kv_dtype, layer, row, pos0, n, c.n_kv_heads, c.head_dim, stg, 0,
-                                    e->status, e->stream));
+    HIP_OR_POISON(e, launch_kv_copy(e->kv, c.kv_dtype, layer, row, pos0, n, nkv, hd, stg, 0, e->status, e->stream));
     HIP_OR_POISON(e, hipMemcpyAsync(k, stg, half, hipMemcpyDeviceToHost, e->stream));
-    HIP_OR_POISON(e, hipMemcpyAsync(v, stg + half, half, hipMemcpyDeviceToHost, e->stream));
+    HIP_OR_POISON(e, hipMemcpyAsync(vt ? vtmp.data() : v, stg + half, half, hipMemcpyDeviceToHost, e->stream));
   }
   HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
   e->pending = true;
-  return wait_done(e, e->ev_done, e->cfg.timeout_ms);
+  if (ds3_status st = wait_done(e, e->ev_done, e->cfg.timeout_ms)) return st;
+  if (!to_state && vt) transpose(vtmp.data(), reinterpret_cast<char*>(v), false);
+  return DS3_OK;
 }
 
 ds3_status ds3_write_kv(ds3_engine* e, int32_t layer, int32_t row, int32_t pos0, int32_t n, const void* k,

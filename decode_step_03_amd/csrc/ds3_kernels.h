@@ -35,9 +35,11 @@ struct StatusWords {
 // Where the K/V state lives and how a (row, kv head, position) maps to an address.
 struct KvView {
   void* k;               // layer 0 base of K (contiguous: [rows][nkv][cap][hd]; paged: [pages][nkv][ps][hd])
-  void* v;
+  void* v;               // layer 0 base of V: as K, or transposed when v_t (contiguous: [rows][nkv][hd][cap];
+                         // paged: [pages][nkv][hd][ps]) -- the matrix-core attention reads V position-contiguous
   int64_t layer_stride;  // elements between consecutive layers
   int paged;             // 0 contiguous, 1 paged
+  int v_t;               // 1: V stored transposed (bf16 KV)
   int cap;
   int page_size;
   int pool_pages;
@@ -75,8 +77,7 @@ struct GemvParams {
 struct AttnParams {
   const float* q;        // [rows][nq][hd]
   float* out;            // [rows][nq][hd]
-  float* part;           // partials: [rows][nkv][splits][G][hd + 2]
-  unsigned* counters;    // [rows][nkv], zero between launches
+  float* part;           // split partials: [rows][nkv][splits][G][hd + 2] (weighted value sums, max, weight sum)
   KvView kv;
   int layer;
   int nq, nkv, hd;
@@ -127,6 +128,7 @@ hipError_t launch_gemm_mfma(const MfmaParams& p, int mode, int kv_dtype, hipStre
 hipError_t launch_embed(const EmbedParams& p, int weight_dtype, hipStream_t s);
 hipError_t launch_gemv(const GemvParams& p, int mode, int weight_dtype, int kv_dtype, int blocks, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, int kv_dtype, int rows, hipStream_t s);
+hipError_t launch_attention_combine(const AttnParams& p, int rows, hipStream_t s);
 hipError_t launch_kv_copy(const KvView& kv, int kv_dtype, int layer, int row, int pos0, int n, int nkv, int hd,
                           void* staging, int to_state, StatusWords* status, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t s);

@@ -28,7 +28,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 256;
 constexpr int kUnroll = 8;   // 16-byte loads in flight per lane per weight row
-constexpr int kMaxSplitsPerLane = 32;   // attention split merge: partials one lane holds in registers
+constexpr int kMaxSplits = 32;          // attention: splits per (row, kv head), merged by the combine kernel
 constexpr int kAttnChunk = 128;         // attention: positions staged in LDS per chunk, at most ...
 constexpr int kAttnChunkBytes = 32768;  // ... and at most this many bytes of K (and of V)
 
@@ -121,17 +121,29 @@ __device__ __forceinline__ float wave_total(float v) {
 
 __device__ __forceinline__ void raise_error(StatusWords* st, uint32_t bit) { atomicOr(&st->err, bit); }
 
-// Element offset of (row r, kv head g, position j, element 0) within one layer's K (or V) state.
-__device__ __forceinline__ size_t kv_offset(const KvView& kv, int r, int nkv, int g, int j, int hd,
-                                            StatusWords* st) {
-  if (!kv.paged) return ((size_t)(r * nkv + g) * kv.cap + j) * hd;
+// Location of logical position j of row r: the position itself (contiguous) or its pool slot page * ps + offset
+// (paged, through the row's page table; an id outside the pool raises the error word and reads page 0).
+__device__ __forceinline__ int kv_loc(const KvView& kv, int r, int j, StatusWords* st) {
+  if (!kv.paged) return j;
   const int ppr = kv.cap / kv.page_size;
   int page = kv.slot_map[r * ppr + j / kv.page_size];
   if (page < 0 || page >= kv.pool_pages) {
     raise_error(st, ERR_PAGE);
     page = 0;
   }
-  return ((size_t)(page * nkv + g) * kv.page_size + (j % kv.page_size)) * hd;
+  return page * kv.page_size + j % kv.page_size;
+}
+
+// Element offset, within one layer's K or V state, of element e of (row r, kv head g) at location loc (kv_loc).
+__device__ __forceinline__ size_t kv_at(const KvView& kv, bool is_v, int r, int nkv, int g, int hd, int loc, int e) {
+  const bool t = is_v && kv.v_t;
+  if (!kv.paged) {
+    const size_t head = (size_t)(r * nkv + g);
+    return t ? (head * hd + e) * kv.cap + loc : (head * kv.cap + loc) * hd + e;
+  }
+  const int ps = kv.page_size;
+  const size_t head = (size_t)(loc / ps) * nkv + g;
+  return t ? (head * hd + e) * ps + loc % ps : (head * ps + loc % ps) * hd + e;
 }
 
 // ----------------------------------------------------------------------------------------------------------
@@ -426,19 +438,16 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
           continue;
         }
         if (!pos_ok[r]) continue;
-        size_t off;
-        if (!p.kv.paged) {
-          off = ((size_t)(r * p.nkv + cur.head) * p.kv.cap + posr[r]) * p.hd;
-        } else {
-          const int slot = p.slots[sl.write_map() + r];
-          if (slot < 0 || slot >= p.kv.pool_pages * p.kv.page_size) { raise_error(p.status, ERR_WRITE_MAP); continue; }
-          off = ((size_t)((slot / p.kv.page_size) * p.nkv + cur.head) * p.kv.page_size + slot % p.kv.page_size) * p.hd;
+        int loc = posr[r];
+        if (p.kv.paged) {
+          loc = p.slots[sl.write_map() + r];
+          if (loc < 0 || loc >= p.kv.pool_pages * p.kv.page_size) { raise_error(p.status, ERR_WRITE_MAP); continue; }
         }
         // k: the two halves of a rotary pair; v: two adjacent elements
-        KT* dst = reinterpret_cast<KT*>(cur.seg == 1 ? p.kv.k : p.kv.v) + (size_t)p.layer * p.kv.layer_stride + off +
-                  cur.idx;
-        store_kv(dst, va);
-        store_kv(dst + (cur.seg == 1 ? half : 1), vb);
+        KT* base = reinterpret_cast<KT*>(cur.seg == 1 ? p.kv.k : p.kv.v) + (size_t)p.layer * p.kv.layer_stride;
+        const bool isv = cur.seg == 2;
+        store_kv(base + kv_at(p.kv, isv, r, p.nkv, cur.head, p.hd, loc, cur.idx), va);
+        store_kv(base + kv_at(p.kv, isv, r, p.nkv, cur.head, p.hd, loc, cur.idx + (isv ? 1 : half)), vb);
       } else if constexpr (MODE == GEMV_GATEUP) {
         const float silu = a / (1.0f + expf(-a));
         p.out[(size_t)r * p.n_pairs + cur_pair] = silu * b;
@@ -627,21 +636,19 @@ __global__ void __launch_bounds__(64 * NW) gemm_mfma_kernel(MfmaParams mp) {
       return;
     }
     if (!ok) return;
-    size_t off;
-    if (!p.kv.paged) {
-      off = ((size_t)(r * p.nkv + tm.head) * p.kv.cap + pos) * p.hd;
-    } else {
-      const int slot = p.slots[sl.write_map() + r];
-      if (slot < 0 || slot >= p.kv.pool_pages * p.kv.page_size) {
+    int loc = pos;
+    if (p.kv.paged) {
+      loc = p.slots[sl.write_map() + r];
+      if (loc < 0 || loc >= p.kv.pool_pages * p.kv.page_size) {
         raise_error(p.status, ERR_WRITE_MAP);
         return;
       }
-      off = ((size_t)((slot / p.kv.page_size) * p.nkv + tm.head) * p.kv.page_size + slot % p.kv.page_size) * p.hd;
     }
     // k: rotary partners (element idx and idx + hd/2); v: elements idx and idx + 16 of the head
-    KT* dst = reinterpret_cast<KT*>(tm.seg == 1 ? p.kv.k : p.kv.v) + (size_t)p.layer * p.kv.layer_stride + off + idx;
-    store_kv(dst, va);
-    store_kv(dst + (tm.seg == 1 ? half : 16), vb);
+    KT* base = reinterpret_cast<KT*>(tm.seg == 1 ? p.kv.k : p.kv.v) + (size_t)p.layer * p.kv.layer_stride;
+    const bool isv = tm.seg == 2;
+    store_kv(base + kv_at(p.kv, isv, r, p.nkv, tm.head, p.hd, loc, idx), va);
+    store_kv(base + kv_at(p.kv, isv, r, p.nkv, tm.head, p.hd, loc, idx + (isv ? 16 : half)), vb);
   } else if constexpr (MODE == GEMV_GATEUP) {
     const float silu = a / (1.0f + expf(-a));
     p.out[(size_t)r * p.n_pairs + tm.row0 + e] = silu * b;
@@ -696,6 +703,60 @@ constexpr int kVmcntChunk() {
 typedef __attribute__((address_space(1))) const void* global_cptr;
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// The end of an attention block: `wst` holds each wave's state [4 waves][G][HD + 2] (weighted value sums, then the
+// running max and the weight sum, maxima in the log2 domain). The 4 waves are merged in wave order into this
+// split's partial, stored with plain coalesced stores at part[row][kv head][split][G][HD + 2]; the combine kernel
+// that follows merges the splits (the kernel boundary makes the partials visible to every XCD).
+template <int G, int HD>
+__device__ __forceinline__ void attn_write_partial(const AttnParams& p, const float* wst, int r, int g, int s) {
+  float* part = p.part + (((size_t)r * p.nkv + g) * p.splits + s) * (size_t)(G * (HD + 2));
+  for (int i = threadIdx.x; i < G * (HD + 2); i += kBlock) {
+    const int hh = i / (HD + 2), dd = i % (HD + 2);
+    float mm = wst[(0 * G + hh) * (HD + 2) + HD];
+    float ll = wst[(0 * G + hh) * (HD + 2) + HD + 1];
+    float oo = wst[(0 * G + hh) * (HD + 2) + min(dd, HD - 1)];
+#pragma unroll
+    for (int w = 1; w < kBlock / 64; ++w) {
+      const float* ws2 = wst + (w * G + hh) * (HD + 2);
+      float M, w1, w2;
+      Lse::weights(mm, ws2[HD], M, w1, w2);
+      ll = ll * w1 + ws2[HD + 1] * w2;
+      oo = oo * w1 + ws2[min(dd, HD - 1)] * w2;
+      mm = M;
+    }
+    part[i] = dd < HD ? oo : (dd == HD ? mm : ll);
+  }
+}
+
+// Merge of the splits of one (row, q head): grid (nq, rows), HD threads, thread d owns output element d.
+// o[d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s with M = max_s m_s (a split that saw no visible position
+// has m_s = -inf and weight 0). Lane s of each wave loads split s's max and weight sum, so every load of the
+// kernel is a vector load issued up front (uniform addresses would become serialized scalar loads); the weights
+// reach every lane by readlane, and the value sum runs in split order.
+template <int G, int HD>
+__global__ void __launch_bounds__(128) attn_combine_kernel(AttnParams p) {
+  const int h = blockIdx.x, r = blockIdx.y, d = threadIdx.x, lane = d & 63;
+  const int g = h / G, hh = h % G, S = p.splits;
+  const size_t stride = (size_t)G * (HD + 2);   // between consecutive splits
+  const float* part = p.part + ((size_t)r * p.nkv + g) * S * stride + (size_t)hh * (HD + 2);
+  const int sl = min(lane, S - 1);
+  const float ms = part[(size_t)sl * stride + HD];
+  const float ls = part[(size_t)sl * stride + HD + 1];
+  float ov[kMaxSplits];
+#pragma unroll
+  for (int k = 0; k < kMaxSplits; ++k) ov[k] = part[(size_t)min(k, S - 1) * stride + d];
+  const float M = wave_max(lane < S ? ms : -INFINITY);
+  const float w = (lane < S && ms != -INFINITY) ? fast_exp2(ms - M) : 0.f;
+  const float L = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum(w * (lane < S ? ls : 0.f))), 0));
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxSplits; ++k) {
+    const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));   // 0 for k >= S
+    acc = fmaf(wk, k < S ? ov[k] : 0.f, acc);   // a padded split adds an exact zero, never 0 * garbage
+  }
+  p.out[((size_t)r * p.nq + h) * HD + d] = acc / L;
+}
+
 template <typename KT, int HD, int G, bool PAGED>
 __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
   constexpr int EPL = Pack<KT>::N;               // elements per 16 bytes
@@ -711,7 +772,6 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
   constexpr int NBUF = 2;
   float* wst = reinterpret_cast<float*>(smem + (size_t)NBUF * 2 * TC * PB);   // [4 waves][G][HD + 2]
   int* ptab = reinterpret_cast<int*>(wst + 4 * G * (HD + 2));                 // paged: pool page per chunk page
-  __shared__ int s_last;
 
   const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
   const int rows = gridDim.z;
@@ -896,109 +956,260 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
   }
   __syncthreads();
 
-  // ---- merge the 4 waves in wave order and write this split's partial.
-  // Partials cross blocks (and XCDs, whose L2s are not coherent with each other), so they are written and read
-  // with agent-scope atomic accesses, which bypass the non-coherent caches; a cache-wide release/acquire fence
-  // per block (an L2 write-back) would serialize the blocks of an XCD. Layout per (row, kv head):
-  // [G][HD + 2][SP] with the split index fastest, so the merging block reads each output's splits contiguously.
-  const int SP = S <= 4 ? 4 : (S <= 8 ? 8 : (S <= 16 ? 16 : 32));   // split index padded to 4, 8, 16 or 32
-  float* part = p.part + ((size_t)r * p.nkv + g) * (size_t)(G * (HD + 2)) * SP;
-  for (int i = tid; i < G * (HD + 2); i += kBlock) {
-    const int hh = i / (HD + 2), dd = i % (HD + 2);
-    float mm = wst[(0 * G + hh) * (HD + 2) + HD];
-    float ll = wst[(0 * G + hh) * (HD + 2) + HD + 1];
-    float oo = wst[(0 * G + hh) * (HD + 2) + min(dd, HD - 1)];
-#pragma unroll
-    for (int w = 1; w < kBlock / 64; ++w) {
-      const float* ws2 = wst + (w * G + hh) * (HD + 2);
-      float M, w1, w2;
-      Lse::weights(mm, ws2[HD], M, w1, w2);
-      ll = ll * w1 + ws2[HD + 1] * w2;
-      oo = oo * w1 + ws2[min(dd, HD - 1)] * w2;
-      mm = M;
-    }
-    __hip_atomic_store(part + (size_t)i * SP + s, dd < HD ? oo : (dd == HD ? mm : ll), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-  // ---- the last arriving block of this (row, kv head) merges the splits.
-  // Every thread's partial stores have completed (waitcnt) before the barrier; only then does one thread count
-  // the block in. The block that sees S - 1 earlier arrivals reads every split's partial after its own count.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(&p.counters[r * p.nkv + g], 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == (unsigned)(S - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  // Only the merging block acquires (invalidating its stale cache lines); every split's partial was written
-  // through to memory before its block counted in, so plain loads from here on see it. Each output's SP split
-  // values are C = SP/4 float4; C consecutive lanes take one output, so a wave instruction reads ~1 KB of
-  // consecutive outputs.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  {
-    const int C = SP / 4;                                   // float4 per output: 1, 2, 4 or 8
-    constexpr int NOUT = (G * HD * (kMaxSplitsPerLane / 4) + kBlock - 1) / kBlock;   // float4 per thread, max
-    const int c = tid % C;
-    float4 ov[NOUT];
-#pragma unroll
-    for (int k = 0; k < NOUT; ++k) {
-      const int o = min(tid / C + k * (kBlock / C), G * HD - 1);   // output index hh * HD + dd
-      const int hh = o / HD, dd = o % HD;
-      ov[k] = *reinterpret_cast<const float4*>(part + (size_t)(hh * (HD + 2) + dd) * SP + 4 * c);
-    }
-    // per head: M = max_s m_s, weights 2^(m_s - M) into LDS (reusing the wave-merge area), L = sum_s w_s l_s
-    float* wts = wst;                       // [G][SP] weights, then [G][SP] sums
-    float* lsum = wst + G * SP;
-    __shared__ float s_L[G];
-    for (int i = tid; i < G * SP; i += kBlock) {
-      const int hh = i / SP, s2 = i % SP;
-      const float* ps = part + (size_t)(hh * (HD + 2) + HD) * SP;
-      wts[i] = s2 < S ? ps[s2] : -INFINITY;
-      lsum[i] = s2 < S ? ps[SP + s2] : 0.f;
-    }
-    __syncthreads();
-    for (int hh = wid; hh < G; hh += kBlock / 64) {
-      float M = -INFINITY;
-      for (int s2 = lane; s2 < SP; s2 += 64) M = fmaxf(M, wts[hh * SP + s2]);
-      M = wave_max(M);
-      float L = 0.f;
-      for (int s2 = lane; s2 < SP; s2 += 64) {
-        const float ms = wts[hh * SP + s2];
-        const float w = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
-        wts[hh * SP + s2] = w;
-        L = fmaf(w, lsum[hh * SP + s2], L);
-      }
-      L = wave_sum(L);
-      if (lane == 0) s_L[hh] = L;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < NOUT; ++k) {
-      const int o = min(tid / C + k * (kBlock / C), G * HD - 1);
-      const int hh = o / HD, dd = o % HD;
-      const float* w = wts + hh * SP + 4 * c;
-      // padded splits carry weight 0 and are selected out (never 0 * garbage)
-      float acc = w[0] * (4 * c + 0 < S ? ov[k].x : 0.f);
-      acc = fmaf(w[1], 4 * c + 1 < S ? ov[k].y : 0.f, acc);
-      acc = fmaf(w[2], 4 * c + 2 < S ? ov[k].z : 0.f, acc);
-      acc = fmaf(w[3], 4 * c + 3 < S ? ov[k].w : 0.f, acc);
-      switch (C) {   // sum over the C lanes of this output (they agree bit for bit)
-        case 2: acc = group_sum<2>(acc); break;
-        case 4: acc = group_sum<4>(acc); break;
-        case 8: acc = group_sum<8>(acc); break;
-        default: break;
-      }
-      if (c == 0 && tid / C + k * (kBlock / C) < G * HD) p.out[((size_t)r * p.nq + g * G + hh) * HD + dd] = acc / s_L[hh];
-    }
-  }
-  if (tid == 0) __hip_atomic_store(&p.counters[r * p.nkv + g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  attn_write_partial<G, HD>(p, wst, r, g, s);
 }
 
 // ----------------------------------------------------------------------------------------------------------
-// K/V state copies for write_kv / read_kv: staging [nkv][n][hd] <-> state (contiguous or paged)
+// Matrix-core attention (bf16 K/V): the same split sweep, mask and merge as attn_kernel, with both products on
+// v_mfma_f32_16x16x32_bf16. Wave w of the block takes positions [32w, 32w + 32) of every 128-position chunk.
+//
+//   scores  S[position][head] = K[position][:] . q[head][:]  -- A = 16 K rows (from LDS), B = q^T (registers; the
+//           G heads of the group in columns 0..G-1, the rest zero), two 16-position tiles per wave;
+//   values  O[head][d] += P[head][position] V[position][d]   -- A = the softmax weights P, B = 16 d-columns of V
+//           (from the transposed V chunk in LDS), one 32-position k-step per wave.
+//
+// Tile t's rows are positions 8(m/4) + 4t + m%4 (m = row), so the score tile lands with lane (n, L) = (l%16, l/16)
+// holding head n at positions 8L..8L+7 of the wave's 32 -- exactly where the value product's A operand wants them:
+// no data moves between the two products. q and P enter as bf16 hi and lo parts (q: ~16 significant bits; P in
+// [0, 1]), K and V are bf16 already.
+//
+// LDS pieces are swizzled so that the 16 rows (or d-columns) one operand read touches fall in distinct banks:
+// K piece c of position pj sits at pj * HD/8 + (c ^ key(pj)); V^T group cv (8 positions) of element d at
+// d * 16 + (cv ^ (d % 16)). The global-to-LDS loads write the slots in order and pick the source per lane.
+//
+// Positions after pos: a score is selected to -inf and its weight to 0; in the one 32-position block per wave
+// that straddles pos, the hidden V rows are zeroed in the operand (an MFMA would turn 0 * NaN into NaN).
+
+template <int CPR>
+__device__ __forceinline__ int kswz(int pj) { return ((pj & 3) | ((pj >> 1) & 12)) & (CPR - 1); }
+
+__device__ __forceinline__ void split_hi_lo8(const float (&v)[8], bf16x8& hi, bf16x8& lo) {
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint16_t h0 = to_bf16(v[2 * e]), h1 = to_bf16(v[2 * e + 1]);
+    const uint16_t l0 = to_bf16(v[2 * e] - widen1(h0)), l1 = to_bf16(v[2 * e + 1] - widen1(h1));
+    hw[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    lw[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  }
+  hi = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+  lo = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+}
+
+template <int HD, int G, bool PAGED>
+__global__ void __launch_bounds__(kBlock) attn_mfma_kernel(AttnParams p) {
+  constexpr int TC = kAttnChunk;             // positions per chunk: 4 waves x 32
+  constexpr int CPR = HD / 8;                // 16-byte pieces per K row
+  constexpr int KB = TC * HD * 2;            // bytes of K, and of V^T, per chunk
+  constexpr int NIW = KB / 1024 / 4;         // 1 KB global-to-LDS instructions per wave, per K or V
+  constexpr int KS = HD / 32;                // k-steps of the score product
+  constexpr int DT = HD / 16;                // d tiles of the value product
+  static_assert(TC == 128 && G >= 1 && G <= 16 && (HD == 64 || HD == 128), "shape");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  float* wst = reinterpret_cast<float*>(smem + 2 * 2 * KB);   // [4 waves][G][HD + 2]
+  int* ptab = reinterpret_cast<int*>(wst + 4 * G * (HD + 2));  // paged: pool page per chunk page
+
+  const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+  const int rows = gridDim.z;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int n = lane & 15, L = lane >> 4;
+  const int T = p.split_len, S = p.splits, cap = p.kv.cap, nkv = p.nkv;
+  auto chunk_base = [&](int c0) { return (s + (c0 / TC) * S) * TC; };   // round-robin chunks, as attn_kernel
+  const SlotLayout sl{rows};
+  int pos = p.slots[sl.pos() + r];
+  if (pos < 0 || pos >= cap) {
+    if (tid == 0) raise_error(p.status, ERR_POS);
+    pos = 0;
+  }
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(p.kv.k) + (size_t)p.layer * p.kv.layer_stride;
+  const uint16_t* Vb = reinterpret_cast<const uint16_t*>(p.kv.v) + (size_t)p.layer * p.kv.layer_stride;
+  const float scale2 = p.scale * 1.4426950408889634f;   // 1/sqrt(hd) * log2(e): scores in the log2 domain
+
+  // ---- q loads first (loads return in order); they are turned into operands only after the K/V staging has
+  // been issued, so the sweep's loads do not wait behind them
+  float4 qa[KS], qb[KS];
+  {
+    const float* qrow = p.q + ((size_t)r * p.nq + g * G + min(n, G - 1)) * HD + 8 * L;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      qa[k] = *reinterpret_cast<const float4*>(qrow + 32 * k);
+      qb[k] = *reinterpret_cast<const float4*>(qrow + 32 * k + 4);
+    }
+  }
+
+  // ---- paged: the pool pages of every chunk of this split go to LDS first (as in attn_kernel)
+  const int ps = PAGED ? p.kv.page_size : 1;
+  const int ppc = PAGED ? (ps <= TC ? TC / ps : 1) : 1;
+  if constexpr (PAGED) {
+    const int ppr = cap / ps;
+    const int nt = ((T + TC - 1) / TC) * ppc;
+    for (int i = tid; i < nt; i += kBlock) {
+      const int lp = min(chunk_base((i / ppc) * TC) / ps + i % ppc, ppr - 1);
+      int page = p.kv.slot_map[r * ppr + lp];
+      if (page < 0 || page >= p.kv.pool_pages) {
+        raise_error(p.status, ERR_PAGE);
+        page = 0;
+      }
+      ptab[i] = page;
+    }
+    __syncthreads();
+  }
+
+  // ---- stage chunk c0 into buffer buf: instruction k of the block fills 16-byte slots [64k, 64k + 64) of the
+  // K half and of the V^T half; each lane picks the source of its slot (swizzled layouts above)
+  auto stage = [&](int c0, int buf) {
+    unsigned char* kdst = smem + (size_t)buf * 2 * KB;
+    unsigned char* vdst = kdst + KB;
+    const int jb = chunk_base(c0);
+#pragma unroll
+    for (int i = 0; i < NIW; ++i) {
+      const int k = i * 4 + wid;
+      const int slot = k * 64 + lane;
+      const int pj = slot / CPR;                          // K: position in the chunk and piece
+      const int c = (slot % CPR) ^ kswz<CPR>(pj);
+      const int jk = min(jb + pj, cap - 1);               // past the capacity: clamped, never visible
+      const int d = slot / (TC / 8);                      // V^T: element and 8-position group
+      const int cv = (slot % (TC / 8)) ^ (d & 15);
+      const int jv = min(jb + 8 * cv, cap - 8);
+      uint32_t koff, voff;
+      if constexpr (PAGED) {
+        const int q0 = (c0 / TC) * ppc;
+        const int pk = ptab[q0 + min(max(jk / ps - jb / ps, 0), ppc - 1)];
+        const int pv = ptab[q0 + min(max(jv / ps - jb / ps, 0), ppc - 1)];
+        koff = (uint32_t)(((pk * nkv + g) * ps + jk % ps) * HD + 8 * c);
+        voff = (uint32_t)(((pv * nkv + g) * HD + d) * ps + jv % ps);
+      } else {
+        koff = (uint32_t)(((r * nkv + g) * cap + jk) * HD + 8 * c);
+        voff = (uint32_t)(((r * nkv + g) * HD + d) * cap + jv);
+      }
+      __builtin_amdgcn_global_load_lds((global_cptr)(Kb + koff), (lds_ptr)(kdst + (size_t)k * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_cptr)(Vb + voff), (lds_ptr)(vdst + (size_t)k * 1024), 16, 0, 0);
+    }
+  };
+  stage(0, 0);
+  if (TC < T) stage(TC, 1);
+
+  // ---- q^T as B operand: lane (n, L) holds q[head n][32 ks + 8 L + e] * scale2, e = 0..7 (zero for n >= G)
+  bf16x8 qh[KS], ql[KS];
+  {
+    const float z = n < G ? scale2 : 0.f;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const float v[8] = {qa[k].x * z, qa[k].y * z, qa[k].z * z, qa[k].w * z,
+                          qb[k].x * z, qb[k].y * z, qb[k].z * z, qb[k].w * z};
+      split_hi_lo8(v, qh[k], ql[k]);
+    }
+  }
+
+  float m_run = -INFINITY;   // running max of head n (log2 domain), equal in the 4 lane groups
+  float lsum = 0.f;          // this lane's share of head n's weight sum
+  f32x4 acc[DT];             // O[head 4L + i][16 dt + n]
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = 0, buf = 0; c0 < T; c0 += TC, buf ^= 1) {
+    if (c0 + TC < T) __builtin_amdgcn_s_waitcnt(kVmcntChunk<2 * NIW>());
+    else __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int jw = chunk_base(c0) + 32 * wid;   // first position of this wave's block
+    if (jw <= pos) {                            // a block wholly after pos holds nothing visible
+      const uint16_t* kl = reinterpret_cast<const uint16_t*>(smem + (size_t)buf * 2 * KB);
+      const uint16_t* vl = kl + KB / 2;
+      f32x4 sc[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int pj = 32 * wid + 8 * (n >> 2) + 4 * t + (n & 3);
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          const int c = 4 * k + L;
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(kl + (size_t)(pj * CPR + (c ^ kswz<CPR>(pj))) * 8));
+          sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[k], sc[t], 0, 0, 0);
+          sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[k], sc[t], 0, 0, 0);
+        }
+      }
+      // lane (n, L): scores of head n at positions jw + 8L + e, e = 4t + i
+      float sv[8];
+      bool vis[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        vis[e] = jw + 8 * L + e <= pos;
+        sv[e] = vis[e] ? sc[e >> 2][e & 3] : -INFINITY;
+      }
+      float bm = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sv[e]);
+      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      const float mn = fmaxf(m_run, bm);
+      const float corr = (mn == -INFINITY) ? 1.f : fast_exp2(m_run - mn);
+      m_run = mn;
+      float pw[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pw[e] = vis[e] ? fast_exp2(sv[e] - mn) : 0.f;
+        psum += pw[e];
+      }
+      lsum = lsum * corr + psum;
+      bf16x8 ph, pl;
+      split_hi_lo8(pw, ph, pl);
+      // rescale the value sums: element i of acc[] belongs to head 4L + i, whose factor lane 4L + i holds
+      float cr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cr[i] = __shfl(corr, 4 * L + i, 64);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[dt][i] *= cr[i];
+      const bool partial = jw + 31 > pos;
+      uint32_t mk[4];
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2)
+        mk[q2] = (jw + 8 * L + 2 * q2 <= pos ? 0xFFFFu : 0u) | (jw + 8 * L + 2 * q2 + 1 <= pos ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 16 * dt + n;
+        u32x4 b = *reinterpret_cast<const u32x4*>(vl + (size_t)(d * 16 + ((4 * wid + L) ^ (d & 15))) * 8);
+        if (partial) {
+          b.x &= mk[0];
+          b.y &= mk[1];
+          b.z &= mk[2];
+          b.w &= mk[3];
+        }
+        const bf16x8 B = __builtin_bit_cast(bf16x8, b);
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, B, acc[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, B, acc[dt], 0, 0, 0);
+      }
+    }
+    __syncthreads();   // the buffer is refilled next
+    if (c0 + 2 * TC < T) stage(c0 + 2 * TC, buf);
+  }
+
+  // ---- this wave's state into LDS: the 4 lane groups of a head share its max; their weight sums add
+  float lt = lsum + __shfl_xor(lsum, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = 4 * L + i;
+    if (hh < G) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) wst[(wid * G + hh) * (HD + 2) + 16 * dt + n] = acc[dt][i];
+    }
+  }
+  if (L == 0 && n < G) {
+    wst[(wid * G + n) * (HD + 2) + HD] = m_run;
+    wst[(wid * G + n) * (HD + 2) + HD + 1] = lt;
+  }
+  __syncthreads();
+  attn_write_partial<G, HD>(p, wst, r, g, s);
+}
+
+// ----------------------------------------------------------------------------------------------------------
+// K/V state copies for write_kv / read_kv: staging <-> state (contiguous or paged). The staging holds K as
+// [nkv][n][hd] and V as [nkv][n][hd], or as [nkv][hd][n] when V is stored transposed, so that consecutive
+// threads touch consecutive elements of the state in either layout.
 
 template <typename KT>
 __global__ void __launch_bounds__(kBlock) kv_copy_kernel(KvView kv, int layer, int row, int pos0, int n, int nkv,
@@ -1009,10 +1220,11 @@ __global__ void __launch_bounds__(kBlock) kv_copy_kernel(KvView kv, int layer, i
     const int which = (int)(i / (nkv * per));
     const size_t rem = i % (nkv * per);
     const int g = (int)(rem / per);
-    const int t = (int)((rem / hd) % n);
-    const int e = (int)(rem % hd);
+    const bool t = which == 1 && kv.v_t;
+    const int pos = t ? (int)(rem % n) : (int)((rem / hd) % n);
+    const int e = t ? (int)((rem / n) % hd) : (int)(rem % hd);
     KT* base = reinterpret_cast<KT*>(which ? kv.v : kv.k) + (size_t)layer * kv.layer_stride;
-    KT* dst = base + kv_offset(kv, row, nkv, g, pos0 + t, hd, st) + e;
+    KT* dst = base + kv_at(kv, which == 1, row, nkv, g, hd, kv_loc(kv, row, pos0 + pos, st), e);
     if (to_state) *dst = staging[i];
     else staging[i] = *dst;
   }
@@ -1045,7 +1257,7 @@ int attn_max_splits(int nq, int nkv, int hd) {
   (void)nq;
   (void)nkv;
   (void)hd;
-  return kMaxSplitsPerLane;
+  return kMaxSplits;
 }
 
 template <typename F>
@@ -1122,16 +1334,17 @@ static hipError_t attn_go(const AttnParams& p, int rows, hipStream_t s) {
                                     p.kv.paged ? p.kv.page_size : 0);
   dim3 grid(p.splits, p.nkv, rows);
   hipError_t e;
-  if (p.kv.paged) {
-    auto* f = attn_kernel<KT, HD, GG, true>;
+  auto go = [&](auto* f) {
     if ((e = set_lds(f, lds)) != hipSuccess) return e;
     f<<<grid, kBlock, lds, s>>>(p);
+    return hipGetLastError();
+  };
+  if constexpr (sizeof(KT) == 2) {   // bf16 K/V (V transposed): matrix cores
+    if (!p.kv.v_t) return hipErrorInvalidValue;
+    return p.kv.paged ? go(attn_mfma_kernel<HD, GG, true>) : go(attn_mfma_kernel<HD, GG, false>);
   } else {
-    auto* f = attn_kernel<KT, HD, GG, false>;
-    if ((e = set_lds(f, lds)) != hipSuccess) return e;
-    f<<<grid, kBlock, lds, s>>>(p);
+    return p.kv.paged ? go(attn_kernel<KT, HD, GG, true>) : go(attn_kernel<KT, HD, GG, false>);
   }
-  return hipGetLastError();
 }
 
 template <typename KT, int HD>
@@ -1143,6 +1356,26 @@ static hipError_t attn_g(const AttnParams& p, int rows, hipStream_t s) {
     case 8: return attn_go<KT, HD, 8>(p, rows, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int HD>
+static hipError_t combine_g(const AttnParams& p, int rows, hipStream_t s) {
+  const dim3 grid(p.nq, rows);
+  switch (p.nq / p.nkv) {
+    case 1: attn_combine_kernel<1, HD><<<grid, HD, 0, s>>>(p); break;
+    case 2: attn_combine_kernel<2, HD><<<grid, HD, 0, s>>>(p); break;
+    case 4: attn_combine_kernel<4, HD><<<grid, HD, 0, s>>>(p); break;
+    case 8: attn_combine_kernel<8, HD><<<grid, HD, 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_combine(const AttnParams& p, int rows, hipStream_t s) {
+  if (p.splits < 1 || p.splits > kMaxSplits) return hipErrorInvalidValue;
+  if (p.hd == 64) return combine_g<64>(p, rows, s);
+  if (p.hd == 128) return combine_g<128>(p, rows, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attention(const AttnParams& p, int kv_dtype, int rows, hipStream_t s) {

@@ -187,11 +187,13 @@ def test_profile_kernels_times_every_kind_and_restores_state():
     try:
         kinds = eng.profile_kernels(3)
         names = {k["name"] for k in kinds if k["launches"]}
-        assert {"embed", "qkv_rope_kvwrite", "attention_splitk", "o_proj_residual", "gateup_swiglu",
-                "down_proj_residual", "lm_head"} <= names
+        assert {"embed", "qkv_rope_kvwrite", "attention_splitk", "attention_combine", "o_proj_residual",
+                "gateup_swiglu", "down_proj_residual", "lm_head"} <= names
         for k in kinds:
             if k["launches"]:
-                assert k["us_per_step"] > 0 and k["bytes_per_step"] > 0, k
+                assert k["us_per_step"] > 0, k
+                # the combine and split kernels move only work-buffer bytes, which the algorithmic count omits
+                assert k["bytes_per_step"] > 0 or k["name"] in ("attention_combine", "act_split_mfma"), k
         for li in range(w.model.n_layers):
             ls.check_kv(li, 0, 0, 6)
         tokens = np.array([11], np.int32)
