@@ -53,14 +53,14 @@ def algorithmic_bytes(w) -> float:
             + L * R * 2 * m.n_kv_heads * hd * kvb)
 
 
-def engine_for(w, ws, exec_mode):
+def engine_for(w, ws, exec_mode, kernel_plan="auto"):
     from decode_step_03_amd import Engine, make_config
     m = w.model
     cfg = make_config(n_layers=m.n_layers, d_model=m.d_model, n_q_heads=m.n_q_heads, n_kv_heads=m.n_kv_heads,
                       head_dim=m.head_dim, ffn_dim=m.ffn_dim, vocab=m.vocab, rms_eps=m.rms_eps,
                       rope_theta=m.rope_theta, rows=w.rows, cap=w.cap, kv_layout=w.kv_layout,
                       page_size=w.page_size, pool_pages=w.pool_pages, weight_dtype=m.weight_dtype,
-                      kv_dtype=w.kv_dtype, exec_mode=exec_mode)
+                      kv_dtype=w.kv_dtype, exec_mode=exec_mode, kernel_plan=kernel_plan)
     eng = Engine(cfg, "cuda:0")
     eng.load_weights(ws.layers, ws.glob)
     return eng
@@ -116,7 +116,11 @@ def cpu_baseline(w, ws, start_pos, start_tok, budget_s: float) -> dict:
             "seconds": round(dt, 2)}
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "decode_step_03_amd", "csrc", "ds3_kernels.hip")
+CSRC = os.path.join(ROOT, "decode_step_03_amd", "csrc")
+
+
+def kernel_source(kind: str) -> str:
+    return os.path.join(CSRC, "ds3_fused.hip" if kind == "decode_step_fused" else "ds3_kernels.hip")
 
 
 def pmc_traffic(kind: str, workload: str):
@@ -134,7 +138,7 @@ def pmc_traffic(kind: str, workload: str):
             k, v = line[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
     try:
-        with open(KERNEL_SOURCE, "rb") as f:
+        with open(kernel_source(kind), "rb") as f:
             if hashlib.sha256(f.read()).hexdigest() != vals["kernel_source_sha256"]:
                 return None
         return (float(vals["fetch_kib_per_launch"]) * float(vals["fetch_scale"])
@@ -168,7 +172,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="llama8b-bf16-cap8192")
     ap.add_argument("--profile-iters", type=int, default=10)
-    ap.add_argument("--eager-steps", type=int, default=16, help="steps of the one-launch-per-kernel comparison")
+    ap.add_argument("--eager-steps", type=int, default=16,
+                    help="steps of the per-operation kernels, as a graph replay and launched one by one")
+    ap.add_argument("--kernel-plan", default="auto", choices=["auto", "fused", "per_op"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -196,7 +202,7 @@ def main() -> int:
     start_tok = synth.start_tokens(w)
 
     t0 = time.time()
-    eng = engine_for(w, ws, "graph")
+    eng = engine_for(w, ws, "graph", args.kernel_plan)
     prefill(eng, w, start_pos)
     log(f"engine loaded and K/V pre-filled in {time.time() - t0:.1f}s")
 
@@ -248,24 +254,31 @@ def main() -> int:
     del eng
     torch.cuda.empty_cache()
 
-    eager = {}
+    # the per-operation kernels, replayed as one graph and launched one by one: host time per token
+    per_op = {}
     if args.eager_steps > 0:
-        e2 = engine_for(w, ws, "eager")
-        prefill(e2, w, start_pos)
-        sub, wl = [], []
-        p2, t2 = start_pos.copy(), start_tok.copy()
-        for i in range(args.eager_steps + 2):
-            ts = time.perf_counter()
-            lg, _ = e2.step(t2, p2)
-            t2 = lg.argmax(axis=1).astype(np.int32)
-            p2 = p2 + 1
-            if i >= 2:
-                wl.append(time.perf_counter() - ts)
-                sub.append(e2.stats()["last_submit_us"])
-        eager = {"host_submit_us": round(float(np.median(sub)), 1), "wall_ms": round(1e3 * float(np.median(wl)), 3)}
-        e2.close()
-        del e2
-        torch.cuda.empty_cache()
+        for mode in ("graph", "eager"):
+            e2 = engine_for(w, ws, mode, "per_op")
+            prefill(e2, w, start_pos)
+            sub, wl, gu = [], [], []
+            p2, t2 = start_pos.copy(), start_tok.copy()
+            for i in range(args.eager_steps + 2):
+                ts = time.perf_counter()
+                lg, _ = e2.step(t2, p2)
+                t2 = lg.argmax(axis=1).astype(np.int32)
+                p2 = p2 + 1
+                if i >= 2:
+                    wl.append(time.perf_counter() - ts)
+                    st2 = e2.stats()
+                    sub.append(st2["last_submit_us"])
+                    gu.append(st2["last_gpu_us"])
+            per_op[mode] = {"host_submit_us": round(float(np.median(sub)), 1),
+                            "wall_ms": round(1e3 * float(np.median(wl)), 3),
+                            "gpu_ms": round(float(np.median(gu)) / 1e3, 4),
+                            "kernels_per_step": e2.stats()["kernels_per_step"]}
+            e2.close()
+            del e2
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -296,9 +309,11 @@ def main() -> int:
                  "hbm_gbs": round(step_bytes / gpu_ms / 1e6, 1),
                  "hbm_frac": round(step_bytes / gpu_ms / 1e6 / HBM_PEAK_GBS, 4),
                  "wall_ms_p10_p50_p90": [round(1e3 * float(np.percentile(wall, q)), 4) for q in (10, 50, 90)],
+                 "kernel_plan": stats["kernel_plan"],
                  "kernels_per_step": stats["kernels_per_step"], "graph_replays_per_step": 1,
                  "host_submit_us_graph": round(float(np.median(submit_us)), 1),
-                 "eager": eager, "attn_splits": stats["attn_splits"]},
+                 "per_op_graph": per_op.get("graph", {}), "eager": per_op.get("eager", {}),
+                 "attn_splits": stats["attn_splits"]},
         "kernels": [{"name": k["name"], "launches": k["launches"], "us_per_step": round(k["us_per_step"], 2),
                      "gbs": round(k["bytes_per_step"] / k["us_per_step"] / 1e3, 1) if k["us_per_step"] else None}
                     for k in kernels],

@@ -11,7 +11,7 @@ from ctypes import POINTER, c_char, c_double, c_float, c_int32, c_int64, c_uint3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libds3.so")
 
-DS3_ABI_VERSION = 1
+DS3_ABI_VERSION = 2
 
 # ds3_status
 DS3_OK = 0
@@ -31,8 +31,9 @@ STATUS_NAMES = {0: "DS3_OK", 1: "DS3_E_INVALID", 2: "DS3_E_UNSUPPORTED", 3: "DS3
 DS3_F32, DS3_BF16 = 0, 1
 DS3_KV_CONTIGUOUS, DS3_KV_PAGED = 0, 1
 DS3_GRAPH, DS3_EAGER = 0, 1
+DS3_PLAN_AUTO, DS3_PLAN_PER_OP, DS3_PLAN_FUSED = 0, 1, 2
 DS3_BUF_WEIGHTS, DS3_BUF_KV, DS3_BUF_WORK, DS3_BUF_LOGITS, DS3_NUM_BUFFERS = 0, 1, 2, 3, 4
-DS3_INJECT_KERNEL_CHECK, DS3_INJECT_TIMEOUT_NEXT = 1, 2
+DS3_INJECT_KERNEL_CHECK, DS3_INJECT_TIMEOUT_NEXT, DS3_INJECT_BARRIER_TIMEOUT = 1, 2, 3
 
 ROLES = {"embed": 0, "attn_norm": 1, "wq": 2, "wk": 3, "wv": 4, "wo": 5, "ffn_norm": 6, "w_gate": 7, "w_up": 8,
          "w_down": 9, "final_norm": 10, "lm_head": 11}
@@ -43,7 +44,7 @@ class ds3_config(ctypes.Structure):
                 ("n_kv_heads", c_int32), ("head_dim", c_int32), ("ffn_dim", c_int32), ("vocab", c_int32),
                 ("rms_eps", c_float), ("rope_theta", c_double), ("rows", c_int32), ("cap", c_int32),
                 ("kv_layout", c_int32), ("page_size", c_int32), ("pool_pages", c_int32), ("weight_dtype", c_int32),
-                ("kv_dtype", c_int32), ("exec_mode", c_int32), ("timeout_ms", c_uint32)]
+                ("kv_dtype", c_int32), ("exec_mode", c_int32), ("timeout_ms", c_uint32), ("kernel_plan", c_int32)]
 
 
 class ds3_buffer_req(ctypes.Structure):
@@ -58,7 +59,7 @@ class ds3_weight_src(ctypes.Structure):
 class ds3_stats(ctypes.Structure):
     _fields_ = [("steps", c_uint64), ("replays", c_uint64), ("captures", c_uint64), ("kernels_per_step", c_int32),
                 ("state", c_int32), ("last_host_us", c_double), ("last_gpu_us", c_double),
-                ("attn_splits", c_int32), ("reserved", c_int32),
+                ("attn_splits", c_int32), ("kernel_plan", c_int32),
                 ("last_submit_us", c_double)]
 
 
@@ -78,6 +79,7 @@ SIGNATURES = [
     ("ds3_read_kv", c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     ("ds3_stats_get", c_int32, [c_void_p, POINTER(ds3_stats)]),
     ("ds3_profile_kernels", c_int32, [c_void_p, c_int32, POINTER(ds3_kernel_time), POINTER(c_int32)]),
+    ("ds3_phase_trace", c_int32, [c_void_p, POINTER(c_uint64), POINTER(c_int32)]),
     ("ds3_debug_inject", c_int32, [c_void_p, c_int32]),
     ("ds3_last_error", ctypes.c_char_p, [c_void_p]),
     ("ds3_destroy", None, [c_void_p]),
@@ -174,6 +176,13 @@ def ds3_profile_kernels(h: int, iters: int) -> list:
     n = c_int32(16)
     _check(load_library().ds3_profile_kernels(h, iters, out, ctypes.byref(n)), h)
     return list(out)[: n.value]
+
+
+def ds3_phase_trace(h: int, n: int):
+    out = (c_uint64 * n)()
+    k = c_int32(n)
+    _check(load_library().ds3_phase_trace(h, out, ctypes.byref(k)), h)
+    return list(out)[: k.value]
 
 
 def ds3_debug_inject(h: int, kind: int) -> None:

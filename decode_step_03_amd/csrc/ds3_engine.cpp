@@ -30,16 +30,18 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 size_t dtype_bytes(int dt) { return dt == DS3_BF16 ? 2 : 4; }
 
 struct WorkPlan {
-  size_t slots, status, x, q, attn, act, part, rope, slot_map, frag_hi, frag_lo, total;
+  size_t slots, status, x, q, attn, act, part, kvnew, sync, clocks, trace, rope, slot_map, frag_hi, frag_lo, total;
 };
 
 struct KernelKind {
   const char* name;
 };
-enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN, K_HEAD, K_SPLIT, K_COMBINE, K_NUM };
+enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN, K_HEAD, K_SPLIT, K_COMBINE, K_FUSED, K_NUM };
 const char* kKindNames[K_NUM] = {"embed", "qkv_rope_kvwrite", "attention_splitk", "o_proj_residual",
                                  "gateup_swiglu", "down_proj_residual", "lm_head", "act_split_mfma",
-                                 "attention_combine"};
+                                 "attention_combine", "decode_step_fused"};
+// fused plan: the operation kind of phase k of a layer (the grid barrier after it closes the phase)
+const int kPhaseKind[kFusedPhases] = {K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN};
 
 // activation sites the MFMA path splits into bf16 hi/lo operands
 enum Site { S_ATTN_NORM = 0, S_ATTN_OUT, S_FFN_NORM, S_ACT, S_FINAL_NORM };
@@ -67,6 +69,13 @@ struct ds3_engine {
   float* logits = nullptr;
   uint16_t *frag_hi = nullptr, *frag_lo = nullptr;   // MFMA path: activation operands
   bool mfma = false;                                 // rows > 4: projections on the matrix cores
+  bool fused = false;                                // the whole step as one persistent kernel
+  float* kvnew = nullptr;                            // fused: this step's k and v [nkv][2][hd]
+  unsigned* sync = nullptr;                          // fused: barrier and merge counters
+  unsigned long long* clocks = nullptr;              // fused: block 0's clock per barrier
+  unsigned long long* trace = nullptr;               // fused: every block's arrival and release per barrier
+  size_t sync_words = 0;
+  size_t weight_lstride = 0;                         // bytes between consecutive layers' weights
   size_t work_bytes = 0;
 
   // weights
@@ -102,6 +111,7 @@ struct ds3_engine {
   int state = ST_NOT_LOADED;
   bool inject_check = false;
   bool inject_timeout = false;
+  bool inject_barrier = false;
   ds3_stats stats{};
   std::string err;
   void* kv_staging = nullptr;
@@ -131,6 +141,19 @@ ds3_status poison(ds3_engine* e, ds3_status st, const std::string& msg) {
 
 void plan_splits(const ds3_config& c, int* splits, int* split_len);
 
+// Why the fused step kernel cannot run this configuration ("" if it can, device aside).
+std::string fused_refusal(const ds3_config& c) {
+  if (c.rows != 1) return "rows must be 1";
+  if (c.weight_dtype != DS3_BF16 || c.kv_dtype != DS3_BF16) return "weights and K/V must be bf16";
+  if (c.kv_layout != DS3_KV_CONTIGUOUS) return "K/V must be contiguous";
+  if (!fused_shape_supported(c.d_model, c.ffn_dim, c.head_dim, c.n_q_heads, c.n_kv_heads))
+    return "no compiled instantiation for this model shape";
+  const int S = kFusedBlocks / c.n_kv_heads;
+  if (c.cap != 128 * S && c.cap != 256 * S) return "cap must be 128 or 256 positions per split";
+  if (c.vocab < 16 * kFusedBlocks || c.vocab > 520 * kFusedBlocks) return "vocab out of the LM head's range";
+  return "";
+}
+
 std::string check_config(const ds3_config* c) {
   if (!c) return "config is NULL";
   if (c->abi_version != DS3_ABI_VERSION) return "abi_version mismatch";
@@ -151,6 +174,8 @@ std::string check_config(const ds3_config* c) {
   if (c->weight_dtype != DS3_F32 && c->weight_dtype != DS3_BF16) return "weight_dtype must be DS3_F32 or DS3_BF16";
   if (c->kv_dtype != DS3_F32 && c->kv_dtype != DS3_BF16) return "kv_dtype must be DS3_F32 or DS3_BF16";
   if (c->exec_mode != DS3_GRAPH && c->exec_mode != DS3_EAGER) return "exec_mode must be DS3_GRAPH or DS3_EAGER";
+  if (c->kernel_plan != DS3_PLAN_AUTO && c->kernel_plan != DS3_PLAN_PER_OP && c->kernel_plan != DS3_PLAN_FUSED)
+    return "kernel_plan must be DS3_PLAN_AUTO, DS3_PLAN_PER_OP or DS3_PLAN_FUSED";
   if (c->kv_layout == DS3_KV_PAGED) {
     if (c->page_size < 1) return "page_size must be >= 1";
     if (c->cap % c->page_size) return "cap must be a multiple of page_size";
@@ -177,6 +202,10 @@ std::string check_config(const ds3_config* c) {
     if (attn_lds_bytes(c->n_q_heads, c->n_kv_heads, c->head_dim, split_len, c->kv_dtype,
                        c->kv_layout == DS3_KV_PAGED ? c->page_size : 0) > 160 * 1024)
       return "cap / page_size: the attention page table of a split does not fit the 160 KB LDS";
+  }
+  if (c->kernel_plan == DS3_PLAN_FUSED) {
+    const std::string why = fused_refusal(*c);
+    if (!why.empty()) return "kernel_plan: the fused step kernel does not apply (" + why + ")";
   }
   if (c->rows <= kMaxGemvRows) {
     const int kres = std::max(c->ffn_dim, c->n_q_heads * c->head_dim);
@@ -228,7 +257,12 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
   w.q = take((size_t)c.rows * c.n_q_heads * c.head_dim * 4);
   w.attn = take((size_t)c.rows * c.n_q_heads * c.head_dim * 4);
   w.act = take((size_t)c.rows * c.ffn_dim * 4);
-  w.part = take((size_t)c.rows * c.n_kv_heads * splits * G * (c.head_dim + 2) * 4);
+  w.part = take((size_t)c.rows * c.n_kv_heads * std::max(splits, kFusedBlocks / c.n_kv_heads) * G *
+                (c.head_dim + 2) * 4);
+  w.kvnew = take((size_t)c.n_kv_heads * 2 * c.head_dim * 4);
+  w.sync = take(fused_sync_words(c.n_layers, c.n_kv_heads) * 4);
+  w.clocks = take(((size_t)kFusedPhases * c.n_layers + 2) * 8);
+  w.trace = take((size_t)kFusedPhases * c.n_layers * kFusedBlocks * 2 * 8);
   w.rope = take((size_t)c.cap * (c.head_dim / 2) * 2 * 4);
   w.slot_map = take(c.kv_layout == DS3_KV_PAGED ? (size_t)c.rows * (c.cap / c.page_size) * 4 : 4);
   const size_t kmax = (size_t)std::max(std::max(c.d_model, c.ffn_dim), c.n_q_heads * c.head_dim);
@@ -295,6 +329,11 @@ double kind_bytes(const ds3_config& c, int kind) {
     case K_GATEUP: return Lc * (2 * F * d * wb + d * wb);
     case K_DOWN: return Lc * d * F * wb;
     case K_HEAD: return (double)c.vocab * d * wb + d * wb;
+    case K_FUSED: {
+      double t = 0;
+      for (int k : {K_EMBED, K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN, K_HEAD}) t += kind_bytes(c, k);
+      return t;
+    }
   }
   return 0;
 }
@@ -355,6 +394,43 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
     p.status = e->status;
   };
   switch (l.kind) {
+    case K_FUSED: {
+      FusedParams p{};
+      const char* wb = reinterpret_cast<const char*>(e->buf[DS3_BUF_WEIGHTS]);
+      p.wbase = wb;
+      p.lstride = e->weight_lstride;
+      const auto& W0 = e->L[0];
+      p.o_attn_norm = reinterpret_cast<const char*>(W0.attn_norm) - wb;
+      p.o_wqkv = reinterpret_cast<const char*>(W0.wqkv) - wb;
+      p.o_wo = reinterpret_cast<const char*>(W0.wo) - wb;
+      p.o_ffn_norm = reinterpret_cast<const char*>(W0.ffn_norm) - wb;
+      p.o_wgu = reinterpret_cast<const char*>(W0.wgu) - wb;
+      p.o_wd = reinterpret_cast<const char*>(W0.wd) - wb;
+      p.embed = reinterpret_cast<const uint16_t*>(e->embed);
+      p.final_norm = e->final_norm;
+      p.lm_head = reinterpret_cast<const uint16_t*>(e->lm_head);
+      p.kv = e->kv;
+      p.rope = e->rope;
+      p.x = e->x;
+      p.q = e->q;
+      p.kvnew = e->kvnew;
+      p.attn = e->attn;
+      p.act = e->act;
+      p.part = e->part;
+      p.logits = e->logits;
+      p.sync = e->sync;
+      p.clocks = e->clocks;
+      p.trace = e->trace;
+      p.slots = e->slots;
+      p.status = e->status;
+      p.n_layers = c.n_layers;
+      p.vocab = c.vocab;
+      p.cap = c.cap;
+      p.split_len = c.cap / (kFusedBlocks / c.n_kv_heads);
+      p.eps = c.rms_eps;
+      p.scale = (float)(1.0 / std::sqrt((double)c.head_dim));
+      return launch_fused(p, c.d_model, c.ffn_dim, c.head_dim, c.n_q_heads, c.n_kv_heads, e->stream);
+    }
     case K_SPLIT: {
       SplitParams sp{};
       sp.hi = e->frag_hi;
@@ -552,6 +628,11 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   e->part = reinterpret_cast<float*>(work + wp.part);
   e->rope = reinterpret_cast<float*>(work + wp.rope);
   e->slot_map = reinterpret_cast<int*>(work + wp.slot_map);
+  e->kvnew = reinterpret_cast<float*>(work + wp.kvnew);
+  e->sync = reinterpret_cast<unsigned*>(work + wp.sync);
+  e->clocks = reinterpret_cast<unsigned long long*>(work + wp.clocks);
+  e->trace = reinterpret_cast<unsigned long long*>(work + wp.trace);
+  e->sync_words = fused_sync_words(c.n_layers, c.n_kv_heads);
   e->frag_hi = reinterpret_cast<uint16_t*>(work + wp.frag_hi);
   e->frag_lo = reinterpret_cast<uint16_t*>(work + wp.frag_lo);
   e->mfma = c.rows > kMaxGemvRows;
@@ -565,6 +646,7 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
     e->L.push_back({reinterpret_cast<float*>(wbase + P.attn_norm), wbase + P.wqkv, wbase + P.wo,
                     reinterpret_cast<float*>(wbase + P.ffn_norm), wbase + P.wgu, wbase + P.wd});
   }
+  e->weight_lstride = c.n_layers > 1 ? wpl.layers[1].attn_norm - wpl.layers[0].attn_norm : 0;
   e->embed = wbase + wpl.embed;
   e->final_norm = reinterpret_cast<float*>(wbase + wpl.final_norm);
   e->lm_head = wbase + wpl.lm_head;
@@ -589,8 +671,26 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   e->blocks[K_DOWN] = gemv_blocks(c.d_model / 2, max_blocks);
   e->blocks[K_HEAD] = gemv_blocks(c.vocab / 2, max_blocks);
 
-  e->sequence.push_back({K_EMBED, -1, 0});
-  for (int l = 0; l < c.n_layers; ++l) {
+  // kernel plan: the fused step kernel needs its shape, one block per CU of a 256-CU device, and co-residency.
+  // AUTO takes the per-operation kernels: on this GPU their kernel boundaries cost less than the fused kernel's
+  // grid barriers (device-scope atomics serialize under contention), so FUSED is chosen only on request.
+  if (c.kernel_plan == DS3_PLAN_FUSED && fused_refusal(c).empty()) {
+    int cus = 0;
+    h = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, e->device);
+    if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("hipDeviceGetAttribute: ") + hipGetErrorString(h));
+    int per_cu = 0;
+    h = fused_blocks_per_cu(c.d_model, c.ffn_dim, c.head_dim, c.n_q_heads, c.n_kv_heads,
+                            c.cap / (kFusedBlocks / c.n_kv_heads), &per_cu);
+    if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("fused occupancy: ") + hipGetErrorString(h));
+    e->fused = cus == kFusedBlocks && per_cu >= 1;
+    if (!e->fused && c.kernel_plan == DS3_PLAN_FUSED)
+      return bail(DS3_E_UNSUPPORTED, "kernel_plan: the fused step kernel needs " + std::to_string(kFusedBlocks) +
+                                         " compute units with one block each (device has " + std::to_string(cus) +
+                                         ", " + std::to_string(per_cu) + " block(s) per unit)");
+  }
+  if (e->fused) e->sequence.push_back({K_FUSED, -1, 0});
+  else e->sequence.push_back({K_EMBED, -1, 0});
+  for (int l = 0; l < c.n_layers && !e->fused; ++l) {
     if (e->mfma) e->sequence.push_back({K_SPLIT, l, S_ATTN_NORM});
     e->sequence.push_back({K_QKV, l, 0});
     e->sequence.push_back({K_ATTN, l, 0});
@@ -603,7 +703,7 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
     e->sequence.push_back({K_DOWN, l, 0});
   }
   if (e->mfma) e->sequence.push_back({K_SPLIT, -1, S_FINAL_NORM});
-  e->sequence.push_back({K_HEAD, -1, 0});
+  if (!e->fused) e->sequence.push_back({K_HEAD, -1, 0});
 
   const SlotLayout sl{c.rows};
   h = hipHostMalloc(reinterpret_cast<void**>(&e->h_slots), (size_t)sl.words() * 4 + kAlign + sizeof(StatusWords),
@@ -633,7 +733,8 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
     if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("create upload: ") + hipGetErrorString(h));
   }
   e->state = ST_NOT_LOADED;
-  e->stats.attn_splits = e->splits;
+  e->stats.attn_splits = e->fused ? kFusedBlocks / c.n_kv_heads : e->splits;
+  e->stats.kernel_plan = e->fused ? DS3_PLAN_FUSED : DS3_PLAN_PER_OP;
   e->stats.state = e->state;
   *out = e;
   return DS3_OK;
@@ -799,7 +900,9 @@ ds3_status ds3_step(ds3_engine* e, const int32_t* tokens, const int32_t* pos, co
     e->h_slots[sl.write_map() + r] = wm;
   }
   e->h_slots[sl.inject()] = e->inject_check ? 1 : 0;
+  e->h_slots[sl.spin()] = e->inject_barrier ? 1 : 0;   // fused kernel: 1 tick forces every barrier wait to time out
   e->inject_check = false;
+  e->inject_barrier = false;
   const uint32_t timeout = e->inject_timeout ? 0u : e->cfg.timeout_ms;
   e->inject_timeout = false;
 
@@ -852,6 +955,7 @@ ds3_status ds3_reset_state(ds3_engine* e) {
   if (ds3_status st = refuse_if_unusable(e)) return st;
   HIP_OR_POISON(e, hipMemsetAsync(e->buf[DS3_BUF_KV], 0, e->kv_bytes, e->stream));
   HIP_OR_POISON(e, launch_fill_u32(reinterpret_cast<uint32_t*>(e->status), 0u, 2, e->stream));
+  HIP_OR_POISON(e, launch_fill_u32(e->sync, 0u, e->sync_words, e->stream));
   HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
   e->pending = true;
   if (ds3_status st = wait_done(e, e->ev_done, e->cfg.timeout_ms)) return st;
@@ -929,7 +1033,8 @@ ds3_status ds3_stats_get(const ds3_engine* e, ds3_stats* out) {
   if (!e || !out) return DS3_E_INVALID;
   *out = e->stats;
   out->state = e->state;
-  out->attn_splits = e->splits;
+  out->attn_splits = e->fused ? kFusedBlocks / e->cfg.n_kv_heads : e->splits;
+  out->kernel_plan = e->fused ? DS3_PLAN_FUSED : DS3_PLAN_PER_OP;
   if (out->kernels_per_step == 0) out->kernels_per_step = (int)e->sequence.size();
   return DS3_OK;
 }
@@ -987,17 +1092,50 @@ ds3_status ds3_profile_kernels(ds3_engine* e, int32_t iters, ds3_kernel_time* ou
     if (st != DS3_OK) return st;
     tot[k] = ms * 1e3 / ((double)iters * reps);
   }
+  // fused plan: each operation's share of the kernel, from block 0's clock at the start, after every barrier
+  // and at the end (100 MHz), averaged over `iters` launches
+  std::vector<double> phase_us(K_NUM, 0.0);
+  std::vector<int> phases(K_NUM, 0);
+  if (e->fused) {
+    const int L = e->cfg.n_layers, nc = kFusedPhases * L + 2;
+    std::vector<unsigned long long> clk((size_t)nc);
+    for (int it = 0; it < iters; ++it) {
+      HIP_OR_POISON(e, enqueue_step(e));
+      HIP_OR_POISON(e, hipMemcpyAsync(clk.data(), e->clocks, (size_t)nc * 8, hipMemcpyDeviceToHost, e->stream));
+      HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
+      e->pending = true;
+      if (ds3_status st = wait_done(e, e->ev_done, e->cfg.timeout_ms)) return st;
+      for (int b = 0; b < kFusedPhases * L; ++b)
+        phase_us[kPhaseKind[b % kFusedPhases]] += (double)(clk[b + 1] - clk[b]) * 0.01 / iters;
+      phase_us[K_HEAD] += (double)(clk[nc - 1] - clk[nc - 2]) * 0.01 / iters;
+    }
+    for (int k : kPhaseKind) phases[k] = L;
+    phases[K_HEAD] = 1;
+  }
   HIP_OR_POISON(e, enqueue_step(e));
   HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
   e->pending = true;
   if (ds3_status st = wait_done(e, e->ev_done, e->cfg.timeout_ms)) return st;
   for (int k = 0; k < K_NUM; ++k) {
     std::snprintf(out[k].name, sizeof(out[k].name), "%s", kKindNames[k]);
-    out[k].launches = cnt[k];
-    out[k].total_us = tot[k];
+    out[k].launches = e->fused && k != K_FUSED ? phases[k] : cnt[k];
+    out[k].total_us = e->fused && k != K_FUSED ? phase_us[k] : tot[k];
     out[k].bytes = kind_bytes(e->cfg, k);
   }
   *n_inout = K_NUM;
+  return DS3_OK;
+}
+
+ds3_status ds3_phase_trace(ds3_engine* e, uint64_t* out, int32_t* n_inout) {
+  if (ds3_status st = refuse_if_unusable(e)) return st;
+  if (!e->fused) return fail(e, DS3_E_UNSUPPORTED, "phase trace needs the fused plan");
+  const int64_t n = (int64_t)kFusedPhases * e->cfg.n_layers * kFusedBlocks * 2;
+  if (!out || !n_inout || *n_inout < n) return fail(e, DS3_E_INVALID, "need room for " + std::to_string(n) + " words");
+  HIP_OR_POISON(e, hipMemcpyAsync(out, e->trace, (size_t)n * 8, hipMemcpyDeviceToHost, e->stream));
+  HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
+  e->pending = true;
+  if (ds3_status st = wait_done(e, e->ev_done, e->cfg.timeout_ms)) return st;
+  *n_inout = (int32_t)n;
   return DS3_OK;
 }
 
@@ -1005,6 +1143,7 @@ ds3_status ds3_debug_inject(ds3_engine* e, int32_t kind) {
   if (ds3_status st = refuse_if_unusable(e)) return st;
   if (kind == DS3_INJECT_KERNEL_CHECK) e->inject_check = true;
   else if (kind == DS3_INJECT_TIMEOUT_NEXT) e->inject_timeout = true;
+  else if (kind == DS3_INJECT_BARRIER_TIMEOUT) e->inject_barrier = true;
   else return fail(e, DS3_E_INVALID, "unknown injection");
   return DS3_OK;
 }

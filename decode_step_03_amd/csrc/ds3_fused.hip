@@ -1,0 +1,865 @@
+// The decode step of one row as ONE persistent kernel (gfx950).
+//
+// Batch-1 decode streams about half a gigabyte of weights per layer through five dependent steps: QKV
+// projection, attention sweep, o-projection, gate/up, down ("Models, Registry and the Driver" page, section
+// "Shared components"; "Execution" page, section "A constant-shape decode graph"). As separate kernels each step
+// pays a launch, a ramp-up and a drain of several microseconds against 5-40 us of streaming. Here one launch of
+// kFusedBlocks blocks (one per CU, 8 waves each) runs the whole step, and the steps become phases separated by
+// grid barriers. The weights do not depend on the activations, so every wave issues the loads of its first two
+// weight batches of the NEXT phase before it reaches the barrier: HBM keeps streaming while the grid
+// synchronizes. The K/V chunk a block sweeps in layer l + 1 is staged into LDS (direct global-to-LDS loads) while
+// layer l's gate/up phase streams.
+//
+// Coherence across the 8 XCDs, whose L2 caches are not coherent with each other: everything produced and consumed
+// within the launch (x, q, this step's k and v, the attention partials and output, the SwiGLU output) is written
+// with device-scope stores and read with device-scope loads (the sc1 cache policy), which do not hit a stale
+// line in a non-coherent L2. Weights and the K/V of earlier steps are read with ordinary loads. The K/V row at
+// the step's position is also stored to the cache, but the sweep takes this step's k and v from the device-scope
+// copy, so a chunk staged before they were written is patched in LDS.
+//
+// Grid barrier i: wave 0 of every block finishes its epilogue stores and waits for them (vmcnt 0); one lane
+// adds 1 to counter i and spins until the counter reads kFusedBlocks. Counters clear themselves (block 0 zeroes
+// counter i - 1 once it has passed barrier i; the last block to leave zeroes the last one), so a recorded graph
+// replays without host work. A block that waits longer than the limit (a slot word; 2 s by default) raises
+// ERR_BARRIER and the abort flag;
+// from then on no block waits at a barrier, so every wave exits (the step's results are then void).
+//
+// GEMV phases. A phase's outputs are split evenly over the blocks (units: output rows, or rotary / gate-up row
+// pairs). Within a block the 8 waves split the inputs into KS slices of whole 512-element chunks (KS = 8 when the
+// input width allows) and the rows into 8 / KS groups, so each lane holds the activation of its slice in
+// registers and every wave streams the same number of bytes. A wave streams its rows in batches of up to 16
+// 16-byte loads per lane, two batches in flight; after each batch a transposing butterfly leaves every row's
+// wave total in one set of lanes (RB - 1 + log2(64 / RB) shuffles for RB rows), and the KS slices are summed in
+// slice order from LDS in the epilogue. All orders are fixed, so a replay reproduces an eager launch bit for bit.
+#include "ds3_device.h"
+
+namespace ds3 {
+
+namespace {
+
+constexpr int kFW = 8;                 // waves per block
+constexpr int kFT = 64 * kFW;          // threads per block
+constexpr int kSc1 = 16;               // cache-policy bits of a buffer load: sc1 (device-scope coherent)
+constexpr int kNt = 2;                 // cache-policy bits of a buffer load: nt (streamed once)
+constexpr int kNL = 8;                 // 16-byte weight loads per lane per batch, at most (two batches in flight)
+constexpr int kRsrcWord3 = 0x00020000; // buffer resource word 3: raw 32-bit data (gfx9 family)
+
+enum { PH_QKV = 0, PH_ATTN, PH_O, PH_GU, PH_DOWN, PH_HEAD };
+
+template <int D_, int F_, int HD_, int NQ_, int NKV_, int TC_>
+struct Shape {
+  static constexpr int D = D_, F = F_, HD = HD_, NQ = NQ_, NKV = NKV_, G = NQ_ / NKV_, TC = TC_;
+  static constexpr int QW = NQ * HD;                 // q width, the o-projection's input
+  static constexpr int S = kFusedBlocks / NKV;       // attention splits per kv head: one (kv head, split) per block
+  static constexpr int KB = TC * HD * 2;             // bytes of one staged K chunk (and of its V^T chunk)
+  static constexpr int WST = kFW * G * (HD + 2);     // attention wave states
+  static constexpr int UNI = WST > kFW * 520 ? WST : kFW * 520;
+  static_assert(kFusedBlocks % NKV == 0 && S <= 64, "splits per kv head");
+  static_assert(TC % 32 == 0 && TC / 32 <= kFW && TC >= 128, "a chunk is 32 positions per wave");
+  static_assert(KB % (1024 * kFW) == 0, "a chunk's 1 KB staging instructions split evenly over the waves");
+  static_assert(G >= 1 && G <= 16 && (HD == 64 || HD == 128), "group and head width");
+};
+
+// Geometry of a GEMV phase (compile time).
+template <class SH, int PH>
+struct Geo {
+  static constexpr int K = PH == PH_O ? SH::QW : (PH == PH_DOWN ? SH::F : SH::D);
+  static constexpr int C = K / 512;                                  // 512-element chunks (64 lanes x 8)
+  static constexpr int KS = C % 8 == 0 ? 8 : (C % 4 == 0 ? 4 : (C % 2 == 0 ? 2 : 1));
+  static constexpr int RS = kFW / KS;                                // row groups
+  static constexpr int CW = C / KS;                                  // chunks per wave
+  static constexpr bool PAIRS = PH == PH_QKV || PH == PH_GU;
+  static constexpr bool NORM = PH == PH_QKV || PH == PH_GU || PH == PH_HEAD;
+  static constexpr int UNITS = PH == PH_QKV ? (SH::NQ + 2 * SH::NKV) * SH::HD / 2
+                                            : (PH == PH_GU ? SH::F : (PH == PH_HEAD ? 0 : SH::D));
+  static constexpr int RPB = PH == PH_HEAD ? 0 : UNITS / kFusedBlocks * (PAIRS ? 2 : 1);   // rows per block
+  static constexpr int RW = RPB / RS;                                                    // rows per wave
+  static constexpr int NBT = PH == PH_HEAD ? 0 : 2 * ((RW * CW + 2 * kNL - 1) / (2 * kNL));   // batches (even)
+  static constexpr int RB = PH == PH_HEAD ? kNL / CW : (RW + NBT - 1) / NBT;                 // rows per batch
+  static constexpr int NL = RB * CW;                                                     // loads per batch
+  static constexpr int RBP = RB <= 1 ? 1 : RB <= 2 ? 2 : RB <= 4 ? 4 : RB <= 8 ? 8 : 16;
+  static constexpr int LOG = RBP == 1 ? 0 : RBP == 2 ? 1 : RBP == 4 ? 2 : RBP == 8 ? 3 : 4;
+  static_assert(C * 512 == K && KS * CW == C, "input width must be whole 512-element chunks");
+  static_assert(NL >= 1 && NL <= kNL && RB <= 16, "a batch is at most kNL loads per lane");
+  static_assert(PH == PH_HEAD || UNITS % kFusedBlocks == 0, "units split evenly over the blocks");
+  static_assert(PH == PH_HEAD || (RPB % RS == 0 && RW >= 1), "rows split evenly over the row groups");
+  static_assert(PH == PH_HEAD || PH == PH_GU || UNITS / kFusedBlocks <= 64, "one epilogue lane per unit");
+  static_assert(PH != PH_GU || UNITS / kFusedBlocks <= 64, "one epilogue lane per gate/up pair");
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, kRsrcWord3);
+}
+// 16 bytes at a byte offset, read at device scope
+__device__ __forceinline__ u32x4 ld_dev16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kSc1);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned ld_dev(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// every memory operation this wave issued, the stores included, has completed
+__device__ __forceinline__ void wait_all() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// A value the compiler must treat as unknown at this point. Address arithmetic that repeats every layer is
+// otherwise hoisted out of the layer loop as hundreds of loop-invariant offsets, which do not fit the registers.
+__device__ __forceinline__ int opaque_v(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+__device__ __forceinline__ int opaque_s(int v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+template <class T>
+__device__ __forceinline__ T* opaque_p(T* v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+// RBP values per lane -> the wave total of value (lane >> (6 - log2 RBP)), identical in the lanes that hold it.
+// Halving steps (lanes differing in bit m exchange the half of the values the partner keeps) then a butterfly
+// over the remaining lane bits; every partial sum is formed in the same order on every run.
+template <int RBP>
+__device__ __forceinline__ float transpose_reduce(float (&a)[RBP], int lane) {
+  constexpr int LOG = RBP == 1 ? 0 : RBP == 2 ? 1 : RBP == 4 ? 2 : RBP == 8 ? 3 : 4;
+#pragma unroll
+  for (int s = 0; s < LOG; ++s) {
+    const int m = 32 >> s;
+    const int H = RBP >> (s + 1);
+    const bool up = (lane & m) != 0;
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+      const float send = up ? a[k] : a[k + H];
+      const float recv = __shfl_xor(send, m, 64);
+      a[k] = (up ? a[k + H] : a[k]) + recv;
+    }
+  }
+  float v = a[0];
+#pragma unroll
+  for (int m = 32 >> LOG; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+template <int KS>
+__device__ __forceinline__ float norm_scale(const float* ssq, int K, float eps) {
+  float t = 0.f;
+#pragma unroll
+  for (int k = 0; k < KS; ++k) t += ssq[k];
+  return 1.0f / sqrtf(t / (float)K + eps);
+}
+
+// QKV unit u: segment (0 q, 1 k, 2 v), head and element; rows of the packed Q|K|V matrix
+template <class SH>
+struct QkvUnit {
+  int seg, head, idx, row0, row1;
+  __device__ __forceinline__ explicit QkvUnit(int u) {
+    constexpr int half = SH::HD / 2, nqp = SH::NQ * half, nkp = SH::NKV * half;
+    if (u < nqp) {
+      seg = 0; head = u / half; idx = u % half;
+      row0 = head * SH::HD + idx; row1 = row0 + half;
+    } else if (u < nqp + nkp) {
+      const int pp = u - nqp;
+      seg = 1; head = pp / half; idx = pp % half;
+      row0 = SH::QW + head * SH::HD + idx; row1 = row0 + half;
+    } else {
+      const int pv = 2 * (u - nqp - nkp);
+      seg = 2; head = pv / SH::HD; idx = pv % SH::HD;
+      row0 = SH::QW + SH::NKV * SH::HD + pv; row1 = row0 + 1;
+    }
+  }
+};
+
+struct NoNext {
+  __device__ __forceinline__ void issue(int, u32x4 (&)[kNL]) const {}
+};
+
+// One GEMV phase as seen by one wave: its block's units, its rows and its input slice.
+template <class SH, int PH>
+struct GemvPhase {
+  using GE = Geo<SH, PH>;
+  const uint16_t* w;
+  int u0, nunits, rb;   // block: first unit, units, rows (2 per pair unit)
+  int r0, r1, ks;       // wave: rows [r0, r1) of the block, input slice
+  int nb;               // batches (even)
+  int lane;
+
+  __device__ __forceinline__ void init(const void* w_, int units_total, int b, int wid, int lane_) {
+    w = reinterpret_cast<const uint16_t*>(w_);
+    lane = lane_;
+    const int units = PH == PH_HEAD ? units_total : GE::UNITS;
+    u0 = (int)(((long long)b * units) / kFusedBlocks);
+    nunits = (int)(((long long)(b + 1) * units) / kFusedBlocks) - u0;
+    rb = nunits * (GE::PAIRS ? 2 : 1);
+    const int rg = wid / GE::KS;
+    ks = wid % GE::KS;
+    r0 = rg * rb / GE::RS;
+    r1 = (rg + 1) * rb / GE::RS;
+    nb = PH == PH_HEAD ? 2 * ((r1 - r0 + 2 * GE::RB - 1) / (2 * GE::RB)) : GE::NBT;
+  }
+
+  // weight row of block row br
+  __device__ __forceinline__ int row_of(int br) const {
+    if constexpr (PH == PH_QKV) {
+      const QkvUnit<SH> q(u0 + (br >> 1));
+      return (br & 1) ? q.row1 : q.row0;
+    } else if constexpr (PH == PH_GU) {
+      const int j = u0 + (br >> 1);
+      return (br & 1) ? SH::F + j : j;
+    } else {
+      return u0 + br;
+    }
+  }
+
+  // batch i into buf: rows past the wave's last are clamped to it (their sums are dropped)
+  // (buffer loads: the row offset rides in a scalar register, the lane offset is one vector register)
+  __device__ __forceinline__ void issue(int i, u32x4 (&buf)[kNL]) const {
+    const auto wr = make_rsrc(opaque_p(w));
+    const int lo = opaque_v(lane * 16 + ks * (GE::CW * 1024));
+    const int rfirst = opaque_s(r0 + i * GE::RB);
+#pragma unroll
+    for (int j = 0; j < GE::RB; ++j) {
+      const int br = min(rfirst + j, r1 - 1);
+      const int so = row_of(br) * (GE::K * 2);
+#pragma unroll
+      for (int c = 0; c < GE::CW; ++c)
+        buf[j * GE::CW + c] = __builtin_amdgcn_raw_buffer_load_b128(wr, lo, so + c * 1024, kNt);
+    }
+  }
+
+  // dot products of batch i's rows with the activation slice (per lane)
+  __device__ __forceinline__ void fma(const u32x4 (&buf)[kNL], const float (&xa)[GE::CW][8],
+                                     float (&acc)[GE::RBP]) const {
+#pragma unroll
+    for (int j = 0; j < GE::RBP; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int j = 0; j < GE::RB; ++j)
+#pragma unroll
+      for (int c = 0; c < GE::CW; ++c) {
+        float f[8];
+        Pack<uint16_t>::widen(buf[j * GE::CW + c], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j] = fmaf(f[e], xa[c][e], acc[j]);
+      }
+  }
+
+  // wave totals of batch i's rows -> red[ks][row]
+  __device__ __forceinline__ void reduce(int i, float (&acc)[GE::RBP], float* red) const {
+    const float v = transpose_reduce<GE::RBP>(acc, lane);
+    const int vi = lane >> (6 - GE::LOG);
+    const int br = r0 + i * GE::RB + vi;
+    if ((lane & ((64 >> GE::LOG) - 1)) == 0 && vi < GE::RB && br < r1) red[ks * rb + br] = v;
+  }
+};
+
+// Stage positions [jb, jb + TC) of kv head g (row 0) into LDS: K rows (16-byte pieces swizzled by position) and
+// the transposed V rows (8-position groups swizzled by element), with 1 KB global-to-LDS instructions; lane l of
+// instruction k fills slot 64 k + l and picks its source accordingly.
+template <class SH>
+__device__ __forceinline__ void stage_chunk(const FusedParams& p, int layer, int g, int jb, unsigned char* stage,
+                                            int wid, int lane) {
+  constexpr int HD = SH::HD, TC = SH::TC, CPR = HD / 8, NIW = SH::KB / 1024 / kFW;
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(p.kv.k) + (size_t)layer * p.kv.layer_stride;
+  const uint16_t* Vb = reinterpret_cast<const uint16_t*>(p.kv.v) + (size_t)layer * p.kv.layer_stride;
+  const int cap = p.cap;
+#pragma unroll
+  for (int i = 0; i < NIW; ++i) {
+    const int k = i * kFW + wid;
+    const int slot = opaque_v(k * 64 + lane);
+    const int pj = slot / CPR;
+    const int c = (slot % CPR) ^ kswz<CPR>(pj);
+    const int jk = min(jb + pj, cap - 1);
+    const int d = slot / (TC / 8);
+    const int cv = (slot % (TC / 8)) ^ (d & 15);
+    const int jv = min(jb + 8 * cv, cap - 8);
+    const uint16_t* ks = Kb + ((size_t)g * cap + jk) * HD + 8 * c;
+    const uint16_t* vs = Vb + ((size_t)g * HD + d) * cap + jv;
+    __builtin_amdgcn_global_load_lds((global_cptr)ks, (lds_ptr)(stage + (size_t)k * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((global_cptr)vs, (lds_ptr)(stage + SH::KB + (size_t)k * 1024), 16, 0, 0);
+  }
+}
+
+// Shared per-block state in LDS
+template <class SH>
+struct Smem {
+  unsigned char* stage;   // [K chunk | V^T chunk]
+  float* uni;             // GEMV row partials [KS][rows] / attention wave states [8][G][HD + 2]
+  float* ssq;             // [KS] RMSNorm sums of squares
+  int* flags;             // [0] abort seen, [1] this block merges the splits
+};
+
+// End of a phase, wave 0 only (after its epilogue stores): wait for them, count the block in at barrier `bar`,
+// wait for every block, then issue this wave's first batches of the next phase. (Wave 0 polls the counter with
+// vector loads, and a wave can only wait for its oldest loads first; so wave 0 has no weights in flight while it
+// polls, and the other 7 waves carry the prefetch across the barrier.)
+template <class PF>
+__device__ __forceinline__ void arrive_and_wait(const FusedParams& p, int bar, int lane, int* flags, PF&& prefetch) {
+  wait_all();
+  const unsigned sp = (unsigned)p.slots[SlotLayout{1}.spin()];
+  const long long spin_ticks = sp ? (long long)sp : kFusedSpinTicks;
+  const int nbar = kFusedPhases * p.n_layers;
+  const long long t0 = wall_clock64();
+  if (lane == 0 && !flags[0]) __hip_atomic_fetch_add(&p.sync[bar], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0 && !flags[0]) {
+    for (;;) {
+      if (ld_dev(&p.sync[bar]) >= (unsigned)kFusedBlocks) break;
+      if (ld_dev(&p.sync[nbar + 1]) != 0u) {
+        flags[0] = 1;
+        break;
+      }
+      if (wall_clock64() - t0 > spin_ticks) {
+        raise_error(p.status, ERR_BARRIER);
+        st_dev(&p.sync[nbar + 1], 1u);
+        flags[0] = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  if (lane == 0 && p.trace) {   // this block's arrival and release times at barrier `bar`
+    p.trace[((size_t)bar * kFusedBlocks + blockIdx.x) * 2] = (unsigned long long)t0;
+    p.trace[((size_t)bar * kFusedBlocks + blockIdx.x) * 2 + 1] = (unsigned long long)wall_clock64();
+  }
+  prefetch();
+}
+
+// After the block-wide barrier that follows arrive_and_wait: block 0 clears the previous counter and stamps
+// the clock.
+__device__ __forceinline__ void after_barrier(const FusedParams& p, int bar) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (bar > 0) st_dev(&p.sync[bar - 1], 0u);
+    if (p.clocks) p.clocks[bar + 1] = (unsigned long long)wall_clock64();
+  }
+}
+
+// A GEMV phase from the activation loads to the barrier. `x_embed` (layer 0 only): the residual stream is still
+// the embedding row, read from the (constant) table instead of x.
+template <class SH, int PH, class NX, class EXTRA>
+__device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<SH, PH>& ph, const NX& nx,
+                                         EXTRA&& extra, u32x4 (&A)[kNL], u32x4 (&B)[kNL], const Smem<SH>& sm,
+                                         const float* act, const float* gain, const uint16_t* x_embed, int layer,
+                                         int pos, bool pos_ok, int wid, int lane) {
+  using GE = Geo<SH, PH>;
+  constexpr int HD = SH::HD, half = SH::HD / 2;
+  float* red = sm.uni;
+  // (every buffer below is the same for each layer: opaque copies keep its addresses out of the layer loop)
+  act = opaque_p(act);
+  float* const xb = opaque_p(p.x);
+
+  // ---- 1. this wave's activation slice (times the RMSNorm gain), and its sum of squares
+  float xa[GE::CW][8];
+  {
+    const bool from_embed = PH == PH_QKV && x_embed != nullptr;
+    const auto rs = make_rsrc(act);
+    const int ebase = opaque_v(ph.ks * GE::CW * 512 + lane * 8);
+#pragma unroll
+    for (int c = 0; c < GE::CW; ++c) {
+      const int e0 = ebase + c * 512;
+      if (from_embed) {
+        Pack<uint16_t>::widen(*reinterpret_cast<const u32x4*>(x_embed + e0), xa[c]);
+      } else {
+        const u32x4 a = ld_dev16(rs, e0 * 4), b = ld_dev16(rs, e0 * 4 + 16);
+        xa[c][0] = __uint_as_float(a.x); xa[c][1] = __uint_as_float(a.y);
+        xa[c][2] = __uint_as_float(a.z); xa[c][3] = __uint_as_float(a.w);
+        xa[c][4] = __uint_as_float(b.x); xa[c][5] = __uint_as_float(b.y);
+        xa[c][6] = __uint_as_float(b.z); xa[c][7] = __uint_as_float(b.w);
+      }
+    }
+    if constexpr (GE::NORM) {
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < GE::CW; ++c) {
+        const int e0 = ebase + c * 512;
+        const float4 g0 = *reinterpret_cast<const float4*>(gain + e0);
+        const float4 g1 = *reinterpret_cast<const float4*>(gain + e0 + 4);
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ss = fmaf(xa[c][e], xa[c][e], ss);
+          xa[c][e] *= gv[e];
+        }
+      }
+      const float t = wave_total(ss);
+      if (wid < GE::KS && lane == 0) sm.ssq[ph.ks] = t;
+    }
+  }
+
+  // ---- 2. wave 0: operands of its epilogue (one unit per lane)
+  float eo_a = 0.f, eo_b = 0.f;
+  if constexpr (PH == PH_QKV) {
+    if (wid == 0 && lane < ph.nunits) {
+      const QkvUnit<SH> q(ph.u0 + lane);
+      if (q.seg != 2) {
+        const float2 cs = reinterpret_cast<const float2*>(opaque_p(p.rope))[(size_t)pos * half + q.idx];
+        eo_a = cs.x;
+        eo_b = cs.y;
+      }
+    }
+  } else if constexpr (PH == PH_O || PH == PH_DOWN) {
+    if (wid == 0 && lane < ph.nunits) {
+      const int row = ph.u0 + lane;
+      eo_a = (PH == PH_O && x_embed != nullptr) ? widen1(x_embed[row]) : ld_dev(xb + row);
+    }
+  }
+  extra();
+
+  // ---- 3. batches: two in flight; each freed buffer takes the next batch, past the end the next phase's
+  // first two (wave 0 issues those after its barrier arrival instead)
+  // (a buffer is refilled as soon as its dot products have read it, before the reduction's shuffles)
+  for (int i = 0; i < ph.nb; i += 2) {
+    float acc[GE::RBP];
+    ph.fma(A, xa, acc);
+    if (i + 2 < ph.nb) ph.issue(i + 2, A);
+    else if (wid != 0) nx.issue(0, A);
+    ph.reduce(i, acc, red);
+    ph.fma(B, xa, acc);
+    if (i + 3 < ph.nb) ph.issue(i + 3, B);
+    else if (wid != 0) nx.issue(1, B);
+    ph.reduce(i + 1, acc, red);
+  }
+  __syncthreads();
+
+  // ---- 4. wave 0: slice sums in slice order, epilogue, barrier
+  if (wid == 0) {
+    float scale = 1.f;
+    if constexpr (GE::NORM) scale = norm_scale<GE::KS>(sm.ssq, GE::K, p.eps);
+    auto total = [&](int br) __attribute__((always_inline)) {
+      float t = 0.f;
+#pragma unroll
+      for (int k = 0; k < GE::KS; ++k) t += red[k * ph.rb + br];
+      return t;
+    };
+    if constexpr (PH == PH_QKV) {
+      if (lane < ph.nunits) {
+        const QkvUnit<SH> q(ph.u0 + lane);
+        const float a = total(2 * lane) * scale, b = total(2 * lane + 1) * scale;
+        float va = a, vb = b;
+        if (q.seg != 2) {   // rotate the pair (element idx, element idx + hd/2) by the angles of pos
+          va = a * eo_a - b * eo_b;
+          vb = a * eo_b + b * eo_a;
+        }
+        if (q.seg == 0) {
+          float* qh = opaque_p(p.q) + q.head * HD;
+          st_dev(qh + q.idx, va);
+          st_dev(qh + q.idx + half, vb);
+        } else {
+          const int e1 = q.idx + (q.seg == 1 ? half : 1);
+          float* kn = opaque_p(p.kvnew) + (q.head * 2 + (q.seg - 1)) * HD;
+          st_dev(kn + q.idx, va);
+          st_dev(kn + e1, vb);
+          if (pos_ok) {   // the cache entry for later steps (DynamicUpdateSlice at pos)
+            uint16_t* base = reinterpret_cast<uint16_t*>(q.seg == 1 ? opaque_p(p.kv.k) : opaque_p(p.kv.v)) +
+                             (size_t)layer * p.kv.layer_stride;
+            if (q.seg == 1) {
+              uint16_t* kr = base + ((size_t)q.head * p.cap + pos) * HD;
+              kr[q.idx] = to_bf16(va);
+              kr[e1] = to_bf16(vb);
+            } else {
+              base[((size_t)q.head * HD + q.idx) * p.cap + pos] = to_bf16(va);
+              base[((size_t)q.head * HD + e1) * p.cap + pos] = to_bf16(vb);
+            }
+          }
+        }
+      }
+    } else if constexpr (PH == PH_GU) {
+      if (lane < ph.nunits) {
+        const float a = total(2 * lane) * scale, b = total(2 * lane + 1) * scale;
+        const float silu = a / (1.0f + expf(-a));
+        st_dev(opaque_p(p.act) + ph.u0 + lane, silu * b);
+      }
+    } else if constexpr (PH == PH_O || PH == PH_DOWN) {
+      if (lane < ph.nunits) st_dev(xb + ph.u0 + lane, eo_a + total(lane));
+    } else {   // PH_HEAD
+      bool bad = false;
+      for (int u = lane; u < ph.nunits; u += 64) {
+        const float v = total(u) * scale;
+        opaque_p(p.logits)[ph.u0 + u] = v;
+        bad |= !isfinite(v);
+      }
+      if (bad) atomicOr(&p.status->nonfinite, 1u);
+    }
+    if constexpr (PH != PH_HEAD) {
+      arrive_and_wait(p, kFusedPhases * layer + (PH == PH_QKV ? 0 : PH == PH_O ? 2 : PH == PH_GU ? 3 : 4), lane,
+                      sm.flags, [&]() __attribute__((always_inline)) {
+                        nx.issue(0, A);
+                        nx.issue(1, B);
+                      });
+    }
+  }
+  if constexpr (PH != PH_HEAD) {
+    __syncthreads();
+    after_barrier(p, kFusedPhases * layer + (PH == PH_QKV ? 0 : PH == PH_O ? 2 : PH == PH_GU ? 3 : 4));
+  }
+}
+
+// The attention phase: block b sweeps split s = b % S of kv head g = b / S (positions [s TC, s TC + TC))
+// for the G query heads of the group, on the matrix cores (as attn_mfma_kernel), then the last block of the kv
+// head to finish merges the S splits in split order.
+template <class SH, class NX>
+__device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, u32x4 (&A)[kNL], u32x4 (&B)[kNL],
+                                         const Smem<SH>& sm, int layer, int pos, bool pos_ok, int wid, int lane) {
+  constexpr int HD = SH::HD, G = SH::G, TC = SH::TC, S = SH::S, CPR = HD / 8, KSQ = HD / 32, DT = HD / 16;
+  const int tid = threadIdx.x, b = blockIdx.x;
+  const int g = b / S, s = b % S;
+  const int n = lane & 15, Lg = lane >> 4;
+  float* wst = sm.uni;
+  uint16_t* kl = reinterpret_cast<uint16_t*>(sm.stage);
+  uint16_t* vl = reinterpret_cast<uint16_t*>(sm.stage + SH::KB);
+
+  // ---- q (lane (n, Lg): head g G + n, elements 32 k + 8 Lg + 0..7) and this step's k and v
+  u32x4 qa[KSQ], qb[KSQ];
+  {
+    const auto rq = make_rsrc(opaque_p(p.q));
+    const int hq = g * G + min(n, G - 1);
+#pragma unroll
+    for (int k = 0; k < KSQ; ++k) {
+      const int off = (hq * HD + 8 * Lg + 32 * k) * 4;
+      qa[k] = ld_dev16(rq, off);
+      qb[k] = ld_dev16(rq, off + 16);
+    }
+  }
+  float kn = 0.f, vn = 0.f;
+  if (tid < HD) {
+    const float* kvn = opaque_p(p.kvnew);
+    kn = ld_dev(kvn + (g * 2 + 0) * HD + tid);
+    vn = ld_dev(kvn + (g * 2 + 1) * HD + tid);
+  }
+  wait_all();   // also the chunk staged during the previous phases
+
+  // ---- q^T as the B operand (columns 0..G-1 = the heads, times 1/sqrt(hd) log2(e); zero beyond G)
+  bf16x8 qh[KSQ], ql[KSQ];
+  {
+    const float z = n < G ? p.scale * 1.4426950408889634f : 0.f;
+#pragma unroll
+    for (int k = 0; k < KSQ; ++k) {
+      const float v[8] = {__uint_as_float(qa[k].x) * z, __uint_as_float(qa[k].y) * z,
+                          __uint_as_float(qa[k].z) * z, __uint_as_float(qa[k].w) * z,
+                          __uint_as_float(qb[k].x) * z, __uint_as_float(qb[k].y) * z,
+                          __uint_as_float(qb[k].z) * z, __uint_as_float(qb[k].w) * z};
+      split_hi_lo8(v, qh[k], ql[k]);
+    }
+  }
+
+  float m_run = -INFINITY;   // running max of head n (log2 domain)
+  float lsum = 0.f;          // this lane's share of head n's weight sum
+  f32x4 acc[DT];             // O[head 4 Lg + i][16 dt + n]
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  {
+    // one chunk per split (split_len == TC): staged during the previous layer's gate/up phase
+    const int jb = s * TC;
+    __syncthreads();     // the whole chunk is in LDS
+    // the row at pos: this step's k and v (the staged copy may predate their store)
+    if (pos_ok && pos >= jb && pos < jb + TC && tid < HD) {
+      const int pj = pos - jb;
+      kl[(pj * CPR + ((tid >> 3) ^ kswz<CPR>(pj))) * 8 + (tid & 7)] = to_bf16(kn);
+      vl[(tid * (TC / 8) + ((pj >> 3) ^ (tid & 15))) * 8 + (pj & 7)] = to_bf16(vn);
+    }
+    __syncthreads();
+    const int jw = jb + 32 * wid;   // first position of this wave's block of 32
+    if (32 * wid < TC && jw <= pos) {
+      f32x4 sc[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int pj = 32 * wid + 8 * (n >> 2) + 4 * t + (n & 3);
+#pragma unroll
+        for (int kk = 0; kk < KSQ; ++kk) {
+          const int c = 4 * kk + Lg;
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(kl + (size_t)(pj * CPR + (c ^ kswz<CPR>(pj))) * 8));
+          sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[kk], sc[t], 0, 0, 0);
+          sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[kk], sc[t], 0, 0, 0);
+        }
+      }
+      // lane (n, Lg): scores of head n at positions jw + 8 Lg + e, e = 4 t + i
+      float sv[8];
+      bool vis[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        vis[e] = jw + 8 * Lg + e <= pos;
+        sv[e] = vis[e] ? sc[e >> 2][e & 3] : -INFINITY;
+      }
+      float bm = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sv[e]);
+      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      const float mn = fmaxf(m_run, bm);
+      const float corr = (mn == -INFINITY) ? 1.f : fast_exp2(m_run - mn);
+      m_run = mn;
+      float pw[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pw[e] = vis[e] ? fast_exp2(sv[e] - mn) : 0.f;
+        psum += pw[e];
+      }
+      lsum = lsum * corr + psum;
+      bf16x8 ph, pl;
+      split_hi_lo8(pw, ph, pl);
+      float cr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cr[i] = __shfl(corr, 4 * Lg + i, 64);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[dt][i] *= cr[i];
+      const bool partial = jw + 31 > pos;
+      uint32_t mk[4];
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2)
+        mk[q2] = (jw + 8 * Lg + 2 * q2 <= pos ? 0xFFFFu : 0u) | (jw + 8 * Lg + 2 * q2 + 1 <= pos ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 16 * dt + n;
+        u32x4 bv = *reinterpret_cast<const u32x4*>(vl + (size_t)(d * (TC / 8) + ((4 * wid + Lg) ^ (d & 15))) * 8);
+        if (partial) {   // hidden V rows never meet the matrix core (0 x NaN would be NaN)
+          bv.x &= mk[0];
+          bv.y &= mk[1];
+          bv.z &= mk[2];
+          bv.w &= mk[3];
+        }
+        const bf16x8 Bv = __builtin_bit_cast(bf16x8, bv);
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, Bv, acc[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, Bv, acc[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // the next phase's first weights (waves 1-7; wave 0 after the barrier), in flight through the merge
+  if (wid != 0) {
+    nx.issue(0, A);
+    nx.issue(1, B);
+  }
+
+  // ---- wave states to LDS (idle waves contribute max -inf, weight 0)
+  {
+    float lt = lsum + __shfl_xor(lsum, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 4 * Lg + i;
+      if (hh < G) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) wst[(wid * G + hh) * (HD + 2) + 16 * dt + n] = acc[dt][i];
+      }
+    }
+    if (Lg == 0 && n < G) {
+      wst[(wid * G + n) * (HD + 2) + HD] = m_run;
+      wst[(wid * G + n) * (HD + 2) + HD + 1] = lt;
+    }
+  }
+  __syncthreads();
+
+  // ---- wave 0: the waves merged in wave order into this split's partial; count the split in
+  unsigned* mcnt = opaque_p(p.sync) + kFusedPhases * p.n_layers + 2 + layer * SH::NKV + g;
+  if (wid == 0) {
+    float* part = opaque_p(p.part) + ((size_t)g * S + s) * (G * (HD + 2));
+    for (int i = lane; i < G * (HD + 2); i += 64) {
+      const int hh = i / (HD + 2), dd = i % (HD + 2);
+      float mm = wst[hh * (HD + 2) + HD];
+      float ll = wst[hh * (HD + 2) + HD + 1];
+      float oo = wst[hh * (HD + 2) + min(dd, HD - 1)];
+#pragma unroll
+      for (int w = 1; w < kFW; ++w) {
+        const float* ws2 = wst + (w * G + hh) * (HD + 2);
+        float M, w1, w2;
+        Lse::weights(mm, ws2[HD], M, w1, w2);
+        ll = ll * w1 + ws2[HD + 1] * w2;
+        oo = oo * w1 + ws2[min(dd, HD - 1)] * w2;
+        mm = M;
+      }
+      st_dev(part + i, dd < HD ? oo : (dd == HD ? mm : ll));
+    }
+    wait_all();
+    if (lane == 0) sm.flags[1] = __hip_atomic_fetch_add(mcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(S - 1);
+  }
+  __syncthreads();
+
+  // ---- the last split of this kv head to finish merges all S in split order: wave w takes head w / (HD / 64),
+  // elements 64 (w % (HD / 64)) + lane
+  if (sm.flags[1]) {
+    constexpr int WPH = HD / 64;
+    const int hh = wid / WPH, d = (wid % WPH) * 64 + lane;
+    if (hh < G) {
+      constexpr int stride = G * (HD + 2);
+      const auto rp = make_rsrc(opaque_p(p.part) + (size_t)g * S * stride + hh * (HD + 2));
+      const int sl = min(lane, S - 1);
+      const float ms = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, (sl * stride + HD) * 4, 0, kSc1));
+      const float ls = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, (sl * stride + HD + 1) * 4, 0, kSc1));
+      float ov[S];
+      const int dv = opaque_v(d * 4);
+#pragma unroll
+      for (int k = 0; k < S; ++k)
+        ov[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, dv, k * stride * 4, kSc1));
+      const float M = wave_max(lane < S ? ms : -INFINITY);
+      const float w = (lane < S && ms != -INFINITY) ? fast_exp2(ms - M) : 0.f;
+      const float Lt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum(w * (lane < S ? ls : 0.f))), 0));
+      float o = 0.f;
+#pragma unroll
+      for (int k = 0; k < S; ++k) o = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k)), ov[k], o);
+      st_dev(opaque_p(p.attn) + (g * G + hh) * HD + d, o / Lt);
+    }
+    wait_all();
+    __syncthreads();
+    if (tid == 0) st_dev(mcnt, 0u);   // ready for the next step
+  }
+  if (wid == 0) {
+    arrive_and_wait(p, kFusedPhases * layer + 1, lane, sm.flags, [&]() __attribute__((always_inline)) {
+      nx.issue(0, A);
+      nx.issue(1, B);
+    });
+  }
+  __syncthreads();
+  after_barrier(p, kFusedPhases * layer + 1);
+}
+
+template <class SH>
+__global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_stage[2 * SH::KB];
+  __shared__ __attribute__((aligned(16))) float s_uni[SH::UNI];
+  __shared__ float s_ssq[kFW];
+  __shared__ int s_flags[2];
+  const Smem<SH> sm{s_stage, s_uni, s_ssq, s_flags};
+  const int tid = threadIdx.x, lane0 = tid & 63, wid0 = __builtin_amdgcn_readfirstlane(tid >> 6), b0 = blockIdx.x;
+  const int L = p.n_layers;
+  const int nbar = kFusedPhases * L;
+
+  const SlotLayout sl{1};
+  int token = p.slots[sl.token()];
+  int pos = p.slots[sl.pos()];
+  const bool tok_ok = token >= 0 && token < p.vocab;
+  const bool pos_ok = pos >= 0 && pos < p.cap;
+  if (!tok_ok) token = 0;
+  if (!pos_ok) pos = 0;
+  if (tid == 0) {
+    s_flags[0] = 0;
+    s_flags[1] = 0;
+    if (b0 == 0) {
+      if (!tok_ok) raise_error(p.status, ERR_TOKEN);
+      if (!pos_ok) raise_error(p.status, ERR_POS);
+      if (p.slots[sl.inject()] != 0) raise_error(p.status, ERR_INJECTED);
+      if (p.clocks) p.clocks[0] = (unsigned long long)wall_clock64();
+    }
+  }
+  const uint16_t* erow = p.embed + (size_t)token * SH::D;
+  auto W = [&](int l, size_t off) __attribute__((always_inline)) { return p.wbase + (size_t)l * p.lstride + off; };
+  auto GN = [&](int l, size_t off) __attribute__((always_inline)) { return reinterpret_cast<const float*>(W(l, off)); };
+  auto stage_layer = [&](int l, int b, int wid, int lane) __attribute__((always_inline)) {
+    stage_chunk<SH>(p, l, b / SH::S, (b % SH::S) * SH::TC, sm.stage, wid, lane);
+  };
+
+  u32x4 A[kNL], B[kNL];
+  GemvPhase<SH, PH_QKV> qkv;
+  qkv.init(W(0, p.o_wqkv), 0, b0, wid0, lane0);
+  stage_layer(0, b0, wid0, lane0);
+  qkv.issue(0, A);
+  qkv.issue(1, B);
+  __syncthreads();
+
+  for (int l = 0; l < L; ++l) {
+    // Per-iteration opaque copies: everything derived from the lane, wave and block index is recomputed in each
+    // layer instead of being hoisted out of the loop (which would keep hundreds of values live across it).
+    const int lane = opaque_v(lane0), wid = opaque_s(wid0), b = opaque_s(b0);
+    const uint16_t* xe = l == 0 ? erow : nullptr;
+    GemvPhase<SH, PH_O> ph_o;
+    ph_o.init(W(l, p.o_wo), 0, b, wid, lane);
+    GemvPhase<SH, PH_GU> ph_gu;
+    ph_gu.init(W(l, p.o_wgu), 0, b, wid, lane);
+    GemvPhase<SH, PH_DOWN> ph_down;
+    ph_down.init(W(l, p.o_wd), 0, b, wid, lane);
+
+    run_gemv<SH, PH_QKV>(p, qkv, NoNext{}, []() __attribute__((always_inline)) {}, A, B, sm, p.x, GN(l, p.o_attn_norm), xe, l, pos, pos_ok, wid, lane);
+    run_attn<SH>(p, ph_o, A, B, sm, l, pos, pos_ok, wid, lane);
+    run_gemv<SH, PH_O>(p, ph_o, ph_gu, []() __attribute__((always_inline)) {}, A, B, sm, p.attn, nullptr, xe, l, pos, pos_ok, wid, lane);
+    if (l + 1 < L) {
+      run_gemv<SH, PH_GU>(p, ph_gu, ph_down, [&]() __attribute__((always_inline)) { stage_layer(l + 1, b, wid, lane); }, A, B, sm, p.x, GN(l, p.o_ffn_norm),
+                          nullptr, l, pos, pos_ok, wid, lane);
+      qkv.init(W(l + 1, p.o_wqkv), 0, b, wid, lane);
+      run_gemv<SH, PH_DOWN>(p, ph_down, qkv, []() __attribute__((always_inline)) {}, A, B, sm, p.act, nullptr, nullptr, l, pos, pos_ok, wid, lane);
+    } else {
+      run_gemv<SH, PH_GU>(p, ph_gu, ph_down, []() __attribute__((always_inline)) {}, A, B, sm, p.x, GN(l, p.o_ffn_norm), nullptr, l, pos, pos_ok,
+                          wid, lane);
+      GemvPhase<SH, PH_HEAD> head;
+      head.init(p.lm_head, p.vocab, b, wid, lane);
+      run_gemv<SH, PH_DOWN>(p, ph_down, head, []() __attribute__((always_inline)) {}, A, B, sm, p.act, nullptr, nullptr, l, pos, pos_ok, wid,
+                            lane);
+      run_gemv<SH, PH_HEAD>(p, head, NoNext{}, []() __attribute__((always_inline)) {}, A, B, sm, p.x, p.final_norm, nullptr, l, pos, pos_ok, wid,
+                            lane);
+    }
+  }
+
+  // ---- leave: the last block out clears the last barrier's counter and the departure count
+  if (wid0 == 0) {
+    wait_all();
+    if (lane0 == 0 && !s_flags[0]) {
+      const unsigned prev = __hip_atomic_fetch_add(&p.sync[nbar], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == (unsigned)(kFusedBlocks - 1)) {
+        st_dev(&p.sync[nbar - 1], 0u);
+        st_dev(&p.sync[nbar], 0u);
+        if (p.clocks) p.clocks[nbar + 1] = (unsigned long long)wall_clock64();
+      }
+    }
+  }
+}
+
+template <class SH>
+hipError_t fused_go(const FusedParams& p, hipStream_t s) {
+  fused_step_kernel<SH><<<kFusedBlocks, kFT, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <class SH>
+hipError_t fused_occ(int* out) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, fused_step_kernel<SH>, kFT, 0);
+}
+
+}  // namespace
+
+bool fused_shape_supported(int d, int ffn, int hd, int nq, int nkv) {
+  return (d == 4096 && ffn == 14336 && hd == 128 && nq == 32 && nkv == 8) ||
+         (d == 2048 && ffn == 8192 && hd == 64 && nq == 32 && nkv == 8);
+}
+
+hipError_t fused_blocks_per_cu(int d, int ffn, int hd, int nq, int nkv, int split_len, int* out) {
+  *out = 0;
+  if (d == 4096 && ffn == 14336 && hd == 128 && nq == 32 && nkv == 8) {
+    return split_len == 256 ? fused_occ<Shape<4096, 14336, 128, 32, 8, 256>>(out)
+                            : fused_occ<Shape<4096, 14336, 128, 32, 8, 128>>(out);
+  }
+  if (d == 2048 && ffn == 8192 && hd == 64 && nq == 32 && nkv == 8) {
+    return split_len == 256 ? fused_occ<Shape<2048, 8192, 64, 32, 8, 256>>(out)
+                            : fused_occ<Shape<2048, 8192, 64, 32, 8, 128>>(out);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused(const FusedParams& p, int d, int ffn, int hd, int nq, int nkv, hipStream_t s) {
+  const int tc = p.split_len;   // one staged chunk per split
+  if ((tc != 256 && tc != 128) || p.cap != tc * (kFusedBlocks / nkv)) return hipErrorInvalidValue;
+  if (d == 4096 && ffn == 14336 && hd == 128 && nq == 32 && nkv == 8) {
+    return tc == 256 ? fused_go<Shape<4096, 14336, 128, 32, 8, 256>>(p, s)
+                     : fused_go<Shape<4096, 14336, 128, 32, 8, 128>>(p, s);
+  }
+  if (d == 2048 && ffn == 8192 && hd == 64 && nq == 32 && nkv == 8) {
+    return tc == 256 ? fused_go<Shape<2048, 8192, 64, 32, 8, 256>>(p, s)
+                     : fused_go<Shape<2048, 8192, 64, 32, 8, 128>>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ds3

@@ -14,6 +14,7 @@ enum : uint32_t {
   ERR_WRITE_MAP = 4u,   // Slot::WriteMap outside the pool
   ERR_PAGE = 8u,        // a page id of the SlotMap outside [0, pool_pages)
   ERR_INJECTED = 16u,   // test hook
+  ERR_BARRIER = 32u,    // fused step kernel: a grid barrier outlasted its spin limit (blocks not co-resident)
 };
 
 // Slot buffer layout (int32 words at fixed device addresses; the host rewrites them before every replay).
@@ -23,7 +24,8 @@ struct SlotLayout {
   __host__ __device__ int pos() const { return rows; }
   __host__ __device__ int write_map() const { return 2 * rows; }
   __host__ __device__ int inject() const { return 3 * rows; }
-  __host__ __device__ int words() const { return 3 * rows + 1; }
+  __host__ __device__ int spin() const { return 3 * rows + 1; }   // fused kernel: barrier wait limit, 0 = default
+  __host__ __device__ int words() const { return 3 * rows + 2; }
 };
 
 // Status words written by kernels and read back after every step.
@@ -122,6 +124,42 @@ struct MfmaParams {
   int n_units;           // pairs of 16-row weight tiles
 };
 
+// Fused step kernel (batch 1): the whole step as one persistent launch of kFusedBlocks blocks (one per CU),
+// its phases separated by grid barriers. Weight offsets are relative to `wbase`; layer l's tensors sit at
+// wbase + l * lstride + o_*.
+constexpr int kFusedBlocks = 256;
+constexpr int kFusedPhases = 5;   // per layer: qkv, attention, o-proj, gate/up, down (a grid barrier after each)
+
+struct FusedParams {
+  const char* wbase;
+  size_t lstride;
+  size_t o_attn_norm, o_wqkv, o_wo, o_ffn_norm, o_wgu, o_wd;
+  const uint16_t* embed;       // [vocab][d] bf16
+  const float* final_norm;     // [d]
+  const uint16_t* lm_head;     // [vocab][d] bf16
+  KvView kv;                   // contiguous bf16, V transposed
+  const float* rope;           // [cap][hd/2][2]
+  float* x;                    // [d] residual stream
+  float* q;                    // [nq][hd]
+  float* kvnew;                // [nkv][2][hd]: this step's k (rotated) and v, fp32
+  float* attn;                 // [nq][hd] attention output
+  float* act;                  // [ffn] SwiGLU output
+  float* part;                 // [nkv][splits][G][hd + 2] split partials
+  float* logits;               // [vocab]
+  unsigned* sync;              // [5 L] barrier counters, departures, abort flag, then [L][nkv] merge counters
+  unsigned long long* clocks;  // [5 L + 2] block 0's clock at the start, after every barrier, at the end
+  unsigned long long* trace;   // [5 L][kFusedBlocks][2] every block's arrival and release time per barrier
+  const int* slots;
+  StatusWords* status;
+  int n_layers, vocab, cap;
+  int split_len;               // positions per split
+  float eps, scale;            // RMSNorm eps, 1/sqrt(hd)
+};
+constexpr long long kFusedSpinTicks = 200000000LL;   // default grid-barrier wait limit: 2 s of the 100 MHz clock
+
+// Words of the fused kernel's sync region for `n_layers` layers and `nkv` kv heads.
+inline size_t fused_sync_words(int n_layers, int nkv) { return (size_t)kFusedPhases * n_layers + 2 + (size_t)n_layers * nkv; }
+
 // Host launchers (defined in ds3_kernels.hip). Each returns the launch error, if any.
 hipError_t launch_split(const SplitParams& p, bool norm, hipStream_t s);
 hipError_t launch_gemm_mfma(const MfmaParams& p, int mode, int kv_dtype, hipStream_t s);
@@ -132,6 +170,11 @@ hipError_t launch_attention_combine(const AttnParams& p, int rows, hipStream_t s
 hipError_t launch_kv_copy(const KvView& kv, int kv_dtype, int layer, int row, int pos0, int n, int nkv, int hd,
                           void* staging, int to_state, StatusWords* status, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t s);
+// Fused step kernel (ds3_fused.hip). fused_shape_supported: the model shape has a compiled instantiation.
+bool fused_shape_supported(int d, int ffn, int hd, int nq, int nkv);
+hipError_t launch_fused(const FusedParams& p, int d, int ffn, int hd, int nq, int nkv, hipStream_t s);
+// Blocks of the fused kernel one compute unit holds at once (its LDS and registers decide).
+hipError_t fused_blocks_per_cu(int d, int ffn, int hd, int nq, int nkv, int split_len, int* out);
 
 size_t gemv_lds_bytes(int rows, int K, bool norm);
 int attn_positions_per_pass(int hd, int kv_dtype);

@@ -15,12 +15,13 @@ from . import _ds3 as C
 
 def make_config(*, n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, rms_eps, rope_theta, rows,
                 cap, kv_layout="contiguous", page_size=0, pool_pages=0, weight_dtype="bf16", kv_dtype="bf16",
-                exec_mode="graph", timeout_ms=0) -> C.ds3_config:
+                exec_mode="graph", timeout_ms=0, kernel_plan="auto") -> C.ds3_config:
     dt = {"f32": C.DS3_F32, "bf16": C.DS3_BF16}
     return C.ds3_config(
         C.DS3_ABI_VERSION, n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, rms_eps, rope_theta,
         rows, cap, C.DS3_KV_PAGED if kv_layout == "paged" else C.DS3_KV_CONTIGUOUS, page_size, pool_pages,
-        dt[weight_dtype], dt[kv_dtype], C.DS3_EAGER if exec_mode == "eager" else C.DS3_GRAPH, timeout_ms)
+        dt[weight_dtype], dt[kv_dtype], C.DS3_EAGER if exec_mode == "eager" else C.DS3_GRAPH, timeout_ms,
+        {"auto": C.DS3_PLAN_AUTO, "per_op": C.DS3_PLAN_PER_OP, "fused": C.DS3_PLAN_FUSED}[kernel_plan])
 
 
 class Engine:
@@ -98,11 +99,18 @@ class Engine:
 
     def stats(self) -> dict:
         s = C.ds3_stats_get(self.handle)
-        return {f: getattr(s, f) for f, _ in s._fields_ if f != "reserved"}
+        d = {f: getattr(s, f) for f, _ in s._fields_}
+        d["kernel_plan"] = {C.DS3_PLAN_PER_OP: "per_op", C.DS3_PLAN_FUSED: "fused"}.get(d["kernel_plan"], "?")
+        return d
 
     def profile_kernels(self, iters: int = 5) -> list:
         return [{"name": k.name.decode(), "launches": k.launches, "us_per_step": k.total_us, "bytes_per_step": k.bytes}
                 for k in C.ds3_profile_kernels(self.handle, iters)]
+
+    def phase_trace(self) -> np.ndarray:
+        """Fused plan: [barriers, blocks, 2] arrival / release clock ticks (100 MHz) of the last step."""
+        n = 5 * self.cfg.n_layers * 256 * 2
+        return np.array(C.ds3_phase_trace(self.handle, n), dtype=np.uint64).reshape(5 * self.cfg.n_layers, 256, 2)
 
     def debug_inject(self, kind: int) -> None:
         C.ds3_debug_inject(self.handle, kind)

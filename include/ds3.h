@@ -30,7 +30,7 @@
 extern "C" {
 #endif
 
-#define DS3_ABI_VERSION 1u
+#define DS3_ABI_VERSION 2u
 
 typedef struct ds3_engine ds3_engine;
 
@@ -50,6 +50,12 @@ typedef enum {
 enum { DS3_F32 = 0, DS3_BF16 = 1 };                  /* weight and KV storage types */
 enum { DS3_KV_CONTIGUOUS = 0, DS3_KV_PAGED = 1 };    /* KV layouts */
 enum { DS3_GRAPH = 0, DS3_EAGER = 1 };               /* replay one captured graph, or launch every kernel */
+/* Kernel plan. PER_OP: one kernel per operation (embed, then per layer QKV, attention, split combine, o-proj,
+ * gate/up, down; then the LM head). FUSED: the whole step as one persistent kernel whose phases are those
+ * operations, separated by grid barriers (one block per compute unit; one row, bf16 weights and K/V, contiguous
+ * layout, the 1B and 8B model shapes, cap = 32 x 128 or 32 x 256 positions per 8 kv heads). AUTO picks PER_OP
+ * (the faster of the two on MI355X). Both compute the same step; the graph records whichever runs. */
+enum { DS3_PLAN_AUTO = 0, DS3_PLAN_PER_OP = 1, DS3_PLAN_FUSED = 2 };
 
 /*
  * Model shape and step shape. Llama-style pre-norm decoder without biases: per layer RMSNorm, Q/K/V projection
@@ -71,6 +77,7 @@ typedef struct {
   int32_t rows, cap, kv_layout, page_size, pool_pages;
   int32_t weight_dtype, kv_dtype, exec_mode;
   uint32_t timeout_ms;
+  int32_t kernel_plan;         /* DS3_PLAN_*; FUSED where it does not apply -> DS3_E_UNSUPPORTED */
 } ds3_config;
 
 /* Device buffers the caller allocates for ds3_create, in this id order. */
@@ -126,7 +133,7 @@ typedef struct {
   double last_host_us;       /* host time of the last ds3_step, slot write to logits ready */
   double last_gpu_us;        /* device time of the last step's kernels (HIP events) */
   int32_t attn_splits;       /* split count of the attention sweep over [cap] */
-  int32_t reserved;
+  int32_t kernel_plan;       /* the plan in use: DS3_PLAN_PER_OP or DS3_PLAN_FUSED */
   double last_submit_us;     /* host time of the last ds3_step spent issuing work (slot copy, launch or replay,
                                 readback copies), without the wait for the device */
 } ds3_stats;
@@ -183,15 +190,25 @@ ds3_status ds3_stats_get(const ds3_engine* e, ds3_stats* out);
 
 /* Per kernel kind, the device time of one step's launches of that kind: they are captured as a graph of their
  * own (in step order, with the current slot contents) and replayed `iters` times between two HIP events on the
- * engine's stream. Afterwards one whole step runs again with the same slots, so the K/V entries at the slot
+ * engine's stream. With the FUSED plan the one kernel is timed that way (kind "decode_step_fused"), and each
+ * operation kind reports its phases' share of it: the time between the grid barriers that close them, read from
+ * block 0's clock over `iters` further launches (launches = phases per step). Afterwards one whole step runs again with the same slots, so the K/V entries at the slot
  * positions and the work buffers hold what the last step left. `out` has room for *n_inout entries (at least the
  * number of kinds); on return *n_inout is the number of kinds. A HIP failure poisons the engine. */
 ds3_status ds3_profile_kernels(ds3_engine* e, int32_t iters, ds3_kernel_time* out, int32_t* n_inout);
 
+/* Fused plan only: the grid-barrier trace of the last step, uint64 [5 n_layers][256 blocks][2] = each block's
+ * wall-clock time (100 MHz ticks) when it arrived at the barrier and when it was released; the barriers close the
+ * QKV, attention, o-proj, gate/up and down phases of each layer in order. *n_inout: room in `out` on entry, words
+ * written on return. DS3_E_UNSUPPORTED with the per-operation plan. */
+ds3_status ds3_phase_trace(ds3_engine* e, uint64_t* out, int32_t* n_inout);
+
 /* Test hook for the failure path: DS3_INJECT_KERNEL_CHECK makes the next step's first kernel raise its check
  * bit, so that step returns DS3_E_KERNEL_CHECK and the engine needs a reset. DS3_INJECT_TIMEOUT_NEXT sets the
- * next step's wait limit to 0 ms so that it reports DS3_E_TIMEOUT (the kernels themselves run normally). */
-enum { DS3_INJECT_KERNEL_CHECK = 1, DS3_INJECT_TIMEOUT_NEXT = 2 };
+ * next step's wait limit to 0 ms so that it reports DS3_E_TIMEOUT (the kernels themselves run normally).
+ * DS3_INJECT_BARRIER_TIMEOUT (fused plan) sets the next step's grid-barrier wait limit to one clock tick: the
+ * blocks stop waiting for each other, the step's results are void, and it returns DS3_E_KERNEL_CHECK. */
+enum { DS3_INJECT_KERNEL_CHECK = 1, DS3_INJECT_TIMEOUT_NEXT = 2, DS3_INJECT_BARRIER_TIMEOUT = 3 };
 ds3_status ds3_debug_inject(ds3_engine* e, int32_t kind);
 
 /* Message of the engine's last failure ("" if none); engine-owned, valid until the next call. With e == NULL,

@@ -16,12 +16,13 @@ from tests.ds3_testlib import Lockstep, log, make_engine
 pytestmark = pytest.mark.gpu
 
 
-def test_llama8b_cap8192_two_steps_full_size():
+@pytest.mark.parametrize("plan", ["per_op", "fused"])
+def test_llama8b_cap8192_two_steps_full_size(plan):
     w = synth.workload("llama8b-bf16-cap8192")
     t0 = time.time()
     ws = synth.make_weights(w.model)
     log(f"8B-shaped weights drawn in {time.time() - t0:.1f}s")
-    eng = make_engine(w, ws, "graph")
+    eng = make_engine(w, ws, "graph", kernel_plan=plan)
     try:
         ls = Lockstep(w, ws, eng, n_alloc=w.prefill_len + 8)
         t0 = time.time()
@@ -36,6 +37,8 @@ def test_llama8b_cap8192_two_steps_full_size():
                 ls.check_kv(li, 0, int(pos[0]), 1)
             tok = ref.argmax(axis=1).astype(np.int32)
             pos = pos + 1
-        assert eng.stats()["captures"] == 1
+        st = eng.stats()
+        assert st["captures"] == 1 and st["kernel_plan"] == plan
+        assert plan != "fused" or st["kernels_per_step"] == 1
     finally:
         eng.close()

@@ -16,8 +16,8 @@ from tests.ds3_testlib import Lockstep, log, make_engine
 pytestmark = pytest.mark.gpu
 
 
-def _run_greedy(w, ws, steps, start_pos, exec_mode="graph", prefill_kv=0, check_kv_every=0):
-    eng = make_engine(w, ws, exec_mode)
+def _run_greedy(w, ws, steps, start_pos, exec_mode="graph", prefill_kv=0, check_kv_every=0, kernel_plan="auto"):
+    eng = make_engine(w, ws, exec_mode, kernel_plan=kernel_plan)
     try:
         ls = Lockstep(w, ws, eng)
         if prefill_kv:
@@ -68,12 +68,17 @@ def test_tiny_fp32_random_gains_and_tail_capacity():
         eng.close()
 
 
-def test_llama1b_shape_two_layers():
-    """1B-shaped layers (GQA 32/8 x 64, FFN 8192, vocab 32000, cap 4096, bf16) with 2 layers: 40 steps."""
+@pytest.mark.parametrize("plan", ["fused", "per_op"])
+def test_llama1b_shape_two_layers(plan):
+    """1B-shaped layers (GQA 32/8 x 64, FFN 8192, vocab 32000, cap 4096, bf16) with 2 layers: 40 steps, with the
+    fused step kernel and with one kernel per operation."""
     w = synth.small_variant(synth.workload("llama1b-bf16"), n_layers=2)
     ws = synth.make_weights(w.model, gains="random")
-    ls, eng = _run_greedy(w, ws, 40, [300], prefill_kv=300, check_kv_every=10)
-    eng.close()
+    ls, eng = _run_greedy(w, ws, 40, [300], prefill_kv=300, check_kv_every=10, kernel_plan=plan)
+    try:
+        assert eng.stats()["kernel_plan"] == plan
+    finally:
+        eng.close()
 
 
 def test_llama8b_shape_two_layers_multi_row():
