@@ -262,7 +262,7 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
   w.kvnew = take((size_t)c.n_kv_heads * 2 * c.head_dim * 4);
   w.sync = take(fused_sync_words(c.n_layers, c.n_kv_heads) * 4);
   w.clocks = take(((size_t)kFusedPhases * c.n_layers + 2) * 8);
-  w.trace = take((size_t)kFusedPhases * c.n_layers * kFusedBlocks * 2 * 8);
+  w.trace = take((size_t)kFusedPhases * c.n_layers * kFusedBlocks * 10 * 8);   // barrier trace, then sub-phases
   w.rope = take((size_t)c.cap * (c.head_dim / 2) * 2 * 4);
   w.slot_map = take(c.kv_layout == DS3_KV_PAGED ? (size_t)c.rows * (c.cap / c.page_size) * 4 : 4);
   const size_t kmax = (size_t)std::max(std::max(c.d_model, c.ffn_dim), c.n_q_heads * c.head_dim);
@@ -338,10 +338,12 @@ double kind_bytes(const ds3_config& c, int kind) {
   return 0;
 }
 
-int gemv_blocks(int n_pairs, int max_blocks) {
-  const int waves = 4;
-  int b = (n_pairs + waves - 1) / waves;
-  return std::max(1, std::min(b, max_blocks));
+// GEMV launch: one resident round of waves (2 per SIMD at these kernels' register use: 8 per CU, 2048 on 256
+// CUs, i.e. 2 blocks of 4 waves per CU); measured best among 256..4096 blocks. DS3_GEMV_BLOCKS overrides it.
+int gemv_blocks(int n_pairs, int cus) {
+  const int forced = env_int("DS3_GEMV_BLOCKS", 0);
+  const int target = forced > 0 ? forced : 2 * cus;
+  return std::max(1, std::min(target, (n_pairs + 3) / 4));
 }
 
 ds3_status wait_done(ds3_engine* e, hipEvent_t ev, uint32_t timeout_ms) {
@@ -392,6 +394,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
     p.layer = l.layer;
     p.slots = e->slots;
     p.status = e->status;
+    p.ping_pong = env_int("DS3_GEMV_PP", 1) == 1;
   };
   switch (l.kind) {
     case K_FUSED: {
@@ -421,6 +424,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.sync = e->sync;
       p.clocks = e->clocks;
       p.trace = e->trace;
+      p.trace2 = env_int("DS3_FUSED_TRACE2", 0) ? e->trace + (size_t)kFusedPhases * c.n_layers * kFusedBlocks * 2 : nullptr;
       p.slots = e->slots;
       p.status = e->status;
       p.n_layers = c.n_layers;
@@ -664,20 +668,19 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   e->kv.slot_map = e->slot_map;
 
   // launch shapes
-  const int max_blocks = env_int("DS3_GEMV_BLOCKS", 1024);
-  e->blocks[K_QKV] = gemv_blocks((c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim / 2, max_blocks);
-  e->blocks[K_OPROJ] = gemv_blocks(c.d_model / 2, max_blocks);
-  e->blocks[K_GATEUP] = gemv_blocks(c.ffn_dim, max_blocks);
-  e->blocks[K_DOWN] = gemv_blocks(c.d_model / 2, max_blocks);
-  e->blocks[K_HEAD] = gemv_blocks(c.vocab / 2, max_blocks);
+  int cus = 0;
+  h = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, e->device);
+  if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("hipDeviceGetAttribute: ") + hipGetErrorString(h));
+  e->blocks[K_QKV] = gemv_blocks((c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim / 2, cus);
+  e->blocks[K_OPROJ] = gemv_blocks(c.d_model / 2, cus);
+  e->blocks[K_GATEUP] = gemv_blocks(c.ffn_dim, cus);
+  e->blocks[K_DOWN] = gemv_blocks(c.d_model / 2, cus);
+  e->blocks[K_HEAD] = gemv_blocks(c.vocab / 2, cus);
 
   // kernel plan: the fused step kernel needs its shape, one block per CU of a 256-CU device, and co-residency.
   // AUTO takes the per-operation kernels: on this GPU their kernel boundaries cost less than the fused kernel's
   // grid barriers (device-scope atomics serialize under contention), so FUSED is chosen only on request.
   if (c.kernel_plan == DS3_PLAN_FUSED && fused_refusal(c).empty()) {
-    int cus = 0;
-    h = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, e->device);
-    if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("hipDeviceGetAttribute: ") + hipGetErrorString(h));
     int per_cu = 0;
     h = fused_blocks_per_cu(c.d_model, c.ffn_dim, c.head_dim, c.n_q_heads, c.n_kv_heads,
                             c.cap / (kFusedBlocks / c.n_kv_heads), &per_cu);
@@ -1129,8 +1132,9 @@ ds3_status ds3_profile_kernels(ds3_engine* e, int32_t iters, ds3_kernel_time* ou
 ds3_status ds3_phase_trace(ds3_engine* e, uint64_t* out, int32_t* n_inout) {
   if (ds3_status st = refuse_if_unusable(e)) return st;
   if (!e->fused) return fail(e, DS3_E_UNSUPPORTED, "phase trace needs the fused plan");
-  const int64_t n = (int64_t)kFusedPhases * e->cfg.n_layers * kFusedBlocks * 2;
-  if (!out || !n_inout || *n_inout < n) return fail(e, DS3_E_INVALID, "need room for " + std::to_string(n) + " words");
+  const int64_t n2 = (int64_t)kFusedPhases * e->cfg.n_layers * kFusedBlocks * 2;
+  if (!out || !n_inout || *n_inout < n2) return fail(e, DS3_E_INVALID, "need room for " + std::to_string(n2) + " words");
+  const int64_t n = *n_inout >= 5 * n2 ? 5 * n2 : n2;   // with room: the sub-phase clocks follow
   HIP_OR_POISON(e, hipMemcpyAsync(out, e->trace, (size_t)n * 8, hipMemcpyDeviceToHost, e->stream));
   HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
   e->pending = true;

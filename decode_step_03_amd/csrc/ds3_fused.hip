@@ -17,12 +17,14 @@
 // the step's position is also stored to the cache, but the sweep takes this step's k and v from the device-scope
 // copy, so a chunk staged before they were written is patched in LDS.
 //
-// Grid barrier i: wave 0 of every block finishes its epilogue stores and waits for them (vmcnt 0); one lane
-// adds 1 to counter i and spins until the counter reads kFusedBlocks. Counters clear themselves (block 0 zeroes
-// counter i - 1 once it has passed barrier i; the last block to leave zeroes the last one), so a recorded graph
-// replays without host work. A block that waits longer than the limit (a slot word; 2 s by default) raises
-// ERR_BARRIER and the abort flag;
-// from then on no block waits at a barrier, so every wave exits (the step's results are then void).
+// Grid barrier i, with flags and no atomics (device-scope atomics on one address serialize at close to a
+// microsecond each on this GPU): wave 0 of every block finishes its epilogue stores, waits for them (vmcnt 0)
+// and stores the barrier's generation into its arrival flag; block 0 polls all 256 flags (one 16-byte load per
+// lane) and then stores the generation into one release flag per XCD, which the other blocks poll. The
+// generation is epoch x (5 L + 1) + i + 1, with the epoch read at the start and advanced by block 0 at the end,
+// so flags never need clearing and a recorded graph replays without host work. A block that waits longer than the
+// limit (a slot word; 2 s by default) raises ERR_BARRIER and the abort flag; from then on no block waits, so
+// every wave exits (the step's results are then void).
 //
 // GEMV phases. A phase's outputs are split evenly over the blocks (units: output rows, or rotary / gate-up row
 // pairs). Within a block the 8 waves split the inputs into KS slices of whole 512-element chunks (KS = 8 when the
@@ -269,13 +271,14 @@ struct GemvPhase {
 // instruction k fills slot 64 k + l and picks its source accordingly.
 template <class SH>
 __device__ __forceinline__ void stage_chunk(const FusedParams& p, int layer, int g, int jb, unsigned char* stage,
-                                            int wid, int lane) {
+                                            int wid, int lane, int i0, int i1) {
   constexpr int HD = SH::HD, TC = SH::TC, CPR = HD / 8, NIW = SH::KB / 1024 / kFW;
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(p.kv.k) + (size_t)layer * p.kv.layer_stride;
   const uint16_t* Vb = reinterpret_cast<const uint16_t*>(p.kv.v) + (size_t)layer * p.kv.layer_stride;
   const int cap = p.cap;
 #pragma unroll
   for (int i = 0; i < NIW; ++i) {
+    if (i < i0 || i >= i1) continue;   // (uniform)
     const int k = i * kFW + wid;
     const int slot = opaque_v(k * 64 + lane);
     const int pj = slot / CPR;
@@ -300,60 +303,84 @@ struct Smem {
   int* flags;             // [0] abort seen, [1] this block merges the splits
 };
 
-// End of a phase, wave 0 only (after its epilogue stores): wait for them, count the block in at barrier `bar`,
-// wait for every block, then issue this wave's first batches of the next phase. (Wave 0 polls the counter with
-// vector loads, and a wave can only wait for its oldest loads first; so wave 0 has no weights in flight while it
-// polls, and the other 7 waves carry the prefetch across the barrier.)
-template <class PF>
-__device__ __forceinline__ void arrive_and_wait(const FusedParams& p, int bar, int lane, int* flags, PF&& prefetch) {
-  wait_all();
+// Bounded wait of wave 0 for `done()` (evaluated by every lane; the result must agree across the wave): false
+// when the wait gave up (abort flag seen, or the limit passed -- then the error bit and the abort flag are raised).
+template <class F>
+__device__ __forceinline__ bool spin_until(const FusedParams& p, int* flags, F&& done) {
   const unsigned sp = (unsigned)p.slots[SlotLayout{1}.spin()];
-  const long long spin_ticks = sp ? (long long)sp : kFusedSpinTicks;
-  const int nbar = kFusedPhases * p.n_layers;
+  const long long limit = sp ? (long long)sp : kFusedSpinTicks;
   const long long t0 = wall_clock64();
-  if (lane == 0 && !flags[0]) __hip_atomic_fetch_add(&p.sync[bar], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (lane == 0 && !flags[0]) {
-    for (;;) {
-      if (ld_dev(&p.sync[bar]) >= (unsigned)kFusedBlocks) break;
-      if (ld_dev(&p.sync[nbar + 1]) != 0u) {
-        flags[0] = 1;
-        break;
-      }
-      if (wall_clock64() - t0 > spin_ticks) {
+  for (;;) {
+    if (done()) return true;
+    if (ld_dev(&p.sync[1]) != 0u) break;
+    if (wall_clock64() - t0 > limit) {
+      if ((threadIdx.x & 63) == 0) {
         raise_error(p.status, ERR_BARRIER);
-        st_dev(&p.sync[nbar + 1], 1u);
-        flags[0] = 1;
-        break;
+        st_dev(&p.sync[1], 1u);
       }
-      __builtin_amdgcn_s_sleep(1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if ((threadIdx.x & 63) == 0) flags[0] = 1;
+  return false;
+}
+
+// End of a phase, wave 0 only (after its epilogue stores): wait for them, signal arrival at barrier `bar`, issue
+// this wave's first batches of the next phase and wait for every block. (Wave 0 polls with vector loads, and a
+// wave can only wait for its oldest loads first, so its polls also wait for those batches; block 0, whose polls
+// release everyone, issues them only after the barrier.)
+template <class PF>
+__device__ __forceinline__ void arrive_and_wait(const FusedParams& p, unsigned gen0, int bar, int lane, int* flags,
+                                                PF&& prefetch) {
+  wait_all();
+  const long long t0 = wall_clock64();
+  const unsigned gen = gen0 + (unsigned)bar + 1u;
+  if (!flags[0]) {
+    if (lane == 0) st_dev(&p.sync[kSyncArrive + blockIdx.x], gen);
+    if (blockIdx.x == 0) {
+      // the collector: every block's arrival flag, four per lane, then one release flag per XCD
+      const auto ra = make_rsrc(p.sync + kSyncArrive);
+      const bool ok = spin_until(p, flags, [&]() __attribute__((always_inline)) {
+        const u32x4 v = ld_dev16(ra, lane * 16);
+        return __all(v.x == gen && v.y == gen && v.z == gen && v.w == gen) != 0;
+      });
+      if (ok && lane < 8) st_dev(&p.sync[kSyncRelease + 32 * lane], gen);
+    } else {
+      // (the weights go out first: the polls then wait for them too, but the release rarely comes sooner)
+      prefetch();
+      const unsigned* rel = p.sync + kSyncRelease + 32 * (blockIdx.x & 7);
+      spin_until(p, flags, [&]() __attribute__((always_inline)) { return __all(ld_dev(rel) == gen) != 0; });
     }
   }
   if (lane == 0 && p.trace) {   // this block's arrival and release times at barrier `bar`
     p.trace[((size_t)bar * kFusedBlocks + blockIdx.x) * 2] = (unsigned long long)t0;
     p.trace[((size_t)bar * kFusedBlocks + blockIdx.x) * 2 + 1] = (unsigned long long)wall_clock64();
   }
-  prefetch();
+  if (blockIdx.x == 0 || flags[0]) prefetch();
 }
 
-// After the block-wide barrier that follows arrive_and_wait: block 0 clears the previous counter and stamps
-// the clock.
+// After the block-wide barrier that follows arrive_and_wait: block 0 stamps the clock.
 __device__ __forceinline__ void after_barrier(const FusedParams& p, int bar) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    if (bar > 0) st_dev(&p.sync[bar - 1], 0u);
-    if (p.clocks) p.clocks[bar + 1] = (unsigned long long)wall_clock64();
-  }
+  if (blockIdx.x == 0 && threadIdx.x == 0 && p.clocks) p.clocks[bar + 1] = (unsigned long long)wall_clock64();
 }
 
 // A GEMV phase from the activation loads to the barrier. `x_embed` (layer 0 only): the residual stream is still
-// the embedding row, read from the (constant) table instead of x.
+// the embedding row, read from the (constant) table instead of x. `extra(it)` runs after loop iteration `it`.
 template <class SH, int PH, class NX, class EXTRA>
 __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<SH, PH>& ph, const NX& nx,
                                          EXTRA&& extra, u32x4 (&A)[kNL], u32x4 (&B)[kNL], const Smem<SH>& sm,
                                          const float* act, const float* gain, const uint16_t* x_embed, int layer,
-                                         int pos, bool pos_ok, int wid, int lane) {
+                                         int pos, bool pos_ok, int wid, int lane, unsigned gen0) {
   using GE = Geo<SH, PH>;
   constexpr int HD = SH::HD, half = SH::HD / 2;
   float* red = sm.uni;
+  constexpr int BAR = PH == PH_QKV ? 0 : PH == PH_O ? 2 : PH == PH_GU ? 3 : 4;
+  // sub-phase clock (wave 0 of each block, when tracing): start, first batch consumed, batches done, block done
+  unsigned long long* st = (p.trace2 && wid == 0 && lane == 0 && PH != PH_HEAD)
+                               ? p.trace2 + ((size_t)(kFusedPhases * layer + BAR) * kFusedBlocks + blockIdx.x) * 8
+                               : nullptr;
+  if (st) st[0] = (unsigned long long)wall_clock64();
   // (every buffer below is the same for each layer: opaque copies keep its addresses out of the layer loop)
   act = opaque_p(act);
   float* const xb = opaque_p(p.x);
@@ -413,26 +440,30 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
       eo_a = (PH == PH_O && x_embed != nullptr) ? widen1(x_embed[row]) : ld_dev(xb + row);
     }
   }
-  extra();
-
-  // ---- 3. batches: two in flight; each freed buffer takes the next batch, past the end the next phase's
-  // first two (wave 0 issues those after its barrier arrival instead)
+  // ---- 3. batches: two in flight; each freed buffer takes the next batch
   // (a buffer is refilled as soon as its dot products have read it, before the reduction's shuffles)
   for (int i = 0; i < ph.nb; i += 2) {
     float acc[GE::RBP];
     ph.fma(A, xa, acc);
+    if (i == 0 && st) st[1] = (unsigned long long)wall_clock64();
     if (i + 2 < ph.nb) ph.issue(i + 2, A);
-    else if (wid != 0) nx.issue(0, A);
     ph.reduce(i, acc, red);
     ph.fma(B, xa, acc);
     if (i + 3 < ph.nb) ph.issue(i + 3, B);
-    else if (wid != 0) nx.issue(1, B);
     ph.reduce(i + 1, acc, red);
+    extra(i / 2);
   }
+  if (st) st[2] = (unsigned long long)wall_clock64();
   __syncthreads();
+  if (st) st[3] = (unsigned long long)wall_clock64();
 
-  // ---- 4. wave 0: slice sums in slice order, epilogue, barrier
-  if (wid == 0) {
+  // ---- 4. wave 0: slice sums in slice order, epilogue, barrier. Waves 1-7 meanwhile issue the next phase's
+  // first two batches (at a saturated memory system an issue can stall for microseconds, so they must not sit
+  // between wave 0 and its barrier arrival).
+  if (wid != 0) {
+    nx.issue(0, A);
+    nx.issue(1, B);
+  } else {
     float scale = 1.f;
     if constexpr (GE::NORM) scale = norm_scale<GE::KS>(sm.ssq, GE::K, p.eps);
     auto total = [&](int br) __attribute__((always_inline)) {
@@ -491,7 +522,7 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
       if (bad) atomicOr(&p.status->nonfinite, 1u);
     }
     if constexpr (PH != PH_HEAD) {
-      arrive_and_wait(p, kFusedPhases * layer + (PH == PH_QKV ? 0 : PH == PH_O ? 2 : PH == PH_GU ? 3 : 4), lane,
+      arrive_and_wait(p, gen0, kFusedPhases * layer + (PH == PH_QKV ? 0 : PH == PH_O ? 2 : PH == PH_GU ? 3 : 4), lane,
                       sm.flags, [&]() __attribute__((always_inline)) {
                         nx.issue(0, A);
                         nx.issue(1, B);
@@ -505,11 +536,12 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
 }
 
 // The attention phase: block b sweeps split s = b % S of kv head g = b / S (positions [s TC, s TC + TC))
-// for the G query heads of the group, on the matrix cores (as attn_mfma_kernel), then the last block of the kv
-// head to finish merges the S splits in split order.
+// for the G query heads of the group, on the matrix cores (as attn_mfma_kernel); each split stores its partial and
+// raises its flag, and split 0's block of the kv head waits for all S flags and merges the splits in split order.
 template <class SH, class NX>
 __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, u32x4 (&A)[kNL], u32x4 (&B)[kNL],
-                                         const Smem<SH>& sm, int layer, int pos, bool pos_ok, int wid, int lane) {
+                                         const Smem<SH>& sm, int layer, int pos, bool pos_ok, int wid, int lane,
+                                         unsigned gen0) {
   constexpr int HD = SH::HD, G = SH::G, TC = SH::TC, S = SH::S, CPR = HD / 8, KSQ = HD / 32, DT = HD / 16;
   const int tid = threadIdx.x, b = blockIdx.x;
   const int g = b / S, s = b % S;
@@ -518,39 +550,40 @@ __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, u32
   uint16_t* kl = reinterpret_cast<uint16_t*>(sm.stage);
   uint16_t* vl = reinterpret_cast<uint16_t*>(sm.stage + SH::KB);
 
-  // ---- q (lane (n, Lg): head g G + n, elements 32 k + 8 Lg + 0..7) and this step's k and v
-  u32x4 qa[KSQ], qb[KSQ];
-  {
-    const auto rq = make_rsrc(opaque_p(p.q));
-    const int hq = g * G + min(n, G - 1);
-#pragma unroll
-    for (int k = 0; k < KSQ; ++k) {
-      const int off = (hq * HD + 8 * Lg + 32 * k) * 4;
-      qa[k] = ld_dev16(rq, off);
-      qb[k] = ld_dev16(rq, off + 16);
-    }
+  unsigned long long* st = (p.trace2 && tid == 0)
+                               ? p.trace2 + ((size_t)(kFusedPhases * layer + 1) * kFusedBlocks + blockIdx.x) * 8
+                               : nullptr;
+  if (st) st[0] = (unsigned long long)wall_clock64();
+  // ---- wave 0 brings the group's q heads and this step's k and v into LDS once for the block (every block of the
+  // kv head reads the same device-scope lines, so one read per block, not one per wave)
+  float* qs = sm.uni;                  // [G][HD] q, then [2][HD] this step's k and v
+  if (wid == 0) {
+    const auto rq = make_rsrc(opaque_p(p.q) + g * G * HD);
+    const auto rk = make_rsrc(opaque_p(p.kvnew) + g * 2 * HD);
+    for (int i = lane; i < G * HD / 4; i += 64)
+      *reinterpret_cast<u32x4*>(qs + 4 * i) = ld_dev16(rq, 16 * i);
+    for (int i = lane; i < 2 * HD / 4; i += 64)
+      *reinterpret_cast<u32x4*>(qs + G * HD + 4 * i) = ld_dev16(rk, 16 * i);
   }
-  float kn = 0.f, vn = 0.f;
-  if (tid < HD) {
-    const float* kvn = opaque_p(p.kvnew);
-    kn = ld_dev(kvn + (g * 2 + 0) * HD + tid);
-    vn = ld_dev(kvn + (g * 2 + 1) * HD + tid);
-  }
-  wait_all();   // also the chunk staged during the previous phases
+  wait_all();   // (every wave: also its share of the chunk staged during the previous phases)
+  __syncthreads();
+  if (st) st[1] = (unsigned long long)wall_clock64();
 
-  // ---- q^T as the B operand (columns 0..G-1 = the heads, times 1/sqrt(hd) log2(e); zero beyond G)
+  // ---- q^T as the B operand (lane (n, Lg): head g G + n, elements 32 k + 8 Lg + 0..7, times 1/sqrt(hd) log2(e);
+  // zero beyond G)
   bf16x8 qh[KSQ], ql[KSQ];
   {
     const float z = n < G ? p.scale * 1.4426950408889634f : 0.f;
+    const float* qrow = qs + min(n, G - 1) * HD + 8 * Lg;
 #pragma unroll
     for (int k = 0; k < KSQ; ++k) {
-      const float v[8] = {__uint_as_float(qa[k].x) * z, __uint_as_float(qa[k].y) * z,
-                          __uint_as_float(qa[k].z) * z, __uint_as_float(qa[k].w) * z,
-                          __uint_as_float(qb[k].x) * z, __uint_as_float(qb[k].y) * z,
-                          __uint_as_float(qb[k].z) * z, __uint_as_float(qb[k].w) * z};
+      const float4 a = *reinterpret_cast<const float4*>(qrow + 32 * k);
+      const float4 c = *reinterpret_cast<const float4*>(qrow + 32 * k + 4);
+      const float v[8] = {a.x * z, a.y * z, a.z * z, a.w * z, c.x * z, c.y * z, c.z * z, c.w * z};
       split_hi_lo8(v, qh[k], ql[k]);
     }
   }
+  const float kn = tid < HD ? qs[G * HD + tid] : 0.f, vn = tid < HD ? qs[G * HD + HD + tid] : 0.f;
 
   float m_run = -INFINITY;   // running max of head n (log2 domain)
   float lsum = 0.f;          // this lane's share of head n's weight sum
@@ -560,8 +593,7 @@ __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, u32
 
   {
     // one chunk per split (split_len == TC): staged during the previous layer's gate/up phase
-    const int jb = s * TC;
-    __syncthreads();     // the whole chunk is in LDS
+    const int jb = s * TC;   // (the chunk is in LDS: every wave waited for its part, then the barrier above)
     // the row at pos: this step's k and v (the staged copy may predate their store)
     if (pos_ok && pos >= jb && pos < jb + TC && tid < HD) {
       const int pj = pos - jb;
@@ -640,12 +672,6 @@ __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, u32
     }
   }
 
-  // the next phase's first weights (waves 1-7; wave 0 after the barrier), in flight through the merge
-  if (wid != 0) {
-    nx.issue(0, A);
-    nx.issue(1, B);
-  }
-
   // ---- wave states to LDS (idle waves contribute max -inf, weight 0)
   {
     float lt = lsum + __shfl_xor(lsum, 16, 64);
@@ -665,11 +691,14 @@ __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, u32
   }
   __syncthreads();
 
-  // ---- wave 0: the waves merged in wave order into this split's partial; count the split in
-  unsigned* mcnt = opaque_p(p.sync) + kFusedPhases * p.n_layers + 2 + layer * SH::NKV + g;
-  if (wid == 0) {
+  if (st) st[2] = (unsigned long long)wall_clock64();
+  // ---- the 8 waves' states merged in wave order into this split's partial (outputs spread over all waves),
+  // then the split's flag
+  const unsigned gen = gen0 + (unsigned)(kFusedPhases * layer + 1) + 1u;
+  unsigned* sflag = opaque_p(p.sync) + kSyncSplit + 32 * g;
+  {
     float* part = opaque_p(p.part) + ((size_t)g * S + s) * (G * (HD + 2));
-    for (int i = lane; i < G * (HD + 2); i += 64) {
+    for (int i = tid; i < G * (HD + 2); i += kFT) {
       const int hh = i / (HD + 2), dd = i % (HD + 2);
       float mm = wst[hh * (HD + 2) + HD];
       float ll = wst[hh * (HD + 2) + HD + 1];
@@ -686,13 +715,20 @@ __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, u32
       st_dev(part + i, dd < HD ? oo : (dd == HD ? mm : ll));
     }
     wait_all();
-    if (lane == 0) sm.flags[1] = __hip_atomic_fetch_add(mcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(S - 1);
   }
   __syncthreads();
+  if (st) st[3] = (unsigned long long)wall_clock64();
+  if (wid == 0 && lane == 0) st_dev(sflag + s, gen);
 
-  // ---- the last split of this kv head to finish merges all S in split order: wave w takes head w / (HD / 64),
-  // elements 64 (w % (HD / 64)) + lane
-  if (sm.flags[1]) {
+  // ---- split 0 of each kv head merges all S splits in split order once every split's flag is up (lane k of
+  // wave 0 reads split k's): wave w takes head w / (HD / 64), elements 64 (w % (HD / 64)) + lane
+  if (s == 0) {
+    if (wid == 0 && !sm.flags[0])
+      spin_until(p, sm.flags, [&]() __attribute__((always_inline)) {
+        return __all(lane >= S || ld_dev(sflag + min(lane, S - 1)) == gen) != 0;
+      });
+    if (st) st[4] = (unsigned long long)wall_clock64();
+    __syncthreads();
     constexpr int WPH = HD / 64;
     const int hh = wid / WPH, d = (wid % WPH) * 64 + lane;
     if (hh < G) {
@@ -715,11 +751,15 @@ __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, u32
       st_dev(opaque_p(p.attn) + (g * G + hh) * HD + d, o / Lt);
     }
     wait_all();
+    if (st) st[5] = (unsigned long long)wall_clock64();
     __syncthreads();
-    if (tid == 0) st_dev(mcnt, 0u);   // ready for the next step
   }
-  if (wid == 0) {
-    arrive_and_wait(p, kFusedPhases * layer + 1, lane, sm.flags, [&]() __attribute__((always_inline)) {
+  // waves 1-7: the next phase's first weights, concurrent with wave 0's barrier
+  if (wid != 0) {
+    nx.issue(0, A);
+    nx.issue(1, B);
+  } else {
+    arrive_and_wait(p, gen0, kFusedPhases * layer + 1, lane, sm.flags, [&]() __attribute__((always_inline)) {
       nx.issue(0, A);
       nx.issue(1, B);
     });
@@ -740,6 +780,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedParams p) {
   const int nbar = kFusedPhases * L;
 
   const SlotLayout sl{1};
+  const unsigned gen0 = ld_dev(&p.sync[0]) * (unsigned)(nbar + 1);   // this launch's generations: gen0 + 1 ...
   int token = p.slots[sl.token()];
   int pos = p.slots[sl.pos()];
   const bool tok_ok = token >= 0 && token < p.vocab;
@@ -759,14 +800,18 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedParams p) {
   const uint16_t* erow = p.embed + (size_t)token * SH::D;
   auto W = [&](int l, size_t off) __attribute__((always_inline)) { return p.wbase + (size_t)l * p.lstride + off; };
   auto GN = [&](int l, size_t off) __attribute__((always_inline)) { return reinterpret_cast<const float*>(W(l, off)); };
-  auto stage_layer = [&](int l, int b, int wid, int lane) __attribute__((always_inline)) {
-    stage_chunk<SH>(p, l, b / SH::S, (b % SH::S) * SH::TC, sm.stage, wid, lane);
+  // stage layer l's K/V chunk; `it` >= 0: only the part for gate/up loop iteration `it` (2 instructions per wave
+  // each), so the staging does not arrive as one burst that stalls the waves' own loads
+  auto stage_layer = [&](int l, int b, int wid, int lane, int it) __attribute__((always_inline)) {
+    constexpr int NIW = SH::KB / 1024 / kFW;
+    const int i0 = it < 0 ? 0 : 2 * it, i1 = it < 0 ? NIW : 2 * it + 2;
+    if (i0 < NIW) stage_chunk<SH>(p, l, b / SH::S, (b % SH::S) * SH::TC, sm.stage, wid, lane, i0, i1);
   };
 
   u32x4 A[kNL], B[kNL];
   GemvPhase<SH, PH_QKV> qkv;
   qkv.init(W(0, p.o_wqkv), 0, b0, wid0, lane0);
-  stage_layer(0, b0, wid0, lane0);
+  stage_layer(0, b0, wid0, lane0, -1);
   qkv.issue(0, A);
   qkv.issue(1, B);
   __syncthreads();
@@ -783,37 +828,30 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedParams p) {
     GemvPhase<SH, PH_DOWN> ph_down;
     ph_down.init(W(l, p.o_wd), 0, b, wid, lane);
 
-    run_gemv<SH, PH_QKV>(p, qkv, NoNext{}, []() __attribute__((always_inline)) {}, A, B, sm, p.x, GN(l, p.o_attn_norm), xe, l, pos, pos_ok, wid, lane);
-    run_attn<SH>(p, ph_o, A, B, sm, l, pos, pos_ok, wid, lane);
-    run_gemv<SH, PH_O>(p, ph_o, ph_gu, []() __attribute__((always_inline)) {}, A, B, sm, p.attn, nullptr, xe, l, pos, pos_ok, wid, lane);
+    run_gemv<SH, PH_QKV>(p, qkv, NoNext{}, [](int) __attribute__((always_inline)) {}, A, B, sm, p.x, GN(l, p.o_attn_norm), xe, l, pos, pos_ok, wid, lane, gen0);
+    run_attn<SH>(p, ph_o, A, B, sm, l, pos, pos_ok, wid, lane, gen0);
+    run_gemv<SH, PH_O>(p, ph_o, ph_gu, [](int) __attribute__((always_inline)) {}, A, B, sm, p.attn, nullptr, xe, l, pos, pos_ok, wid, lane, gen0);
     if (l + 1 < L) {
-      run_gemv<SH, PH_GU>(p, ph_gu, ph_down, [&]() __attribute__((always_inline)) { stage_layer(l + 1, b, wid, lane); }, A, B, sm, p.x, GN(l, p.o_ffn_norm),
-                          nullptr, l, pos, pos_ok, wid, lane);
+      run_gemv<SH, PH_GU>(p, ph_gu, ph_down, [&](int it) __attribute__((always_inline)) { stage_layer(l + 1, b, wid, lane, it); }, A, B, sm, p.x, GN(l, p.o_ffn_norm),
+                          nullptr, l, pos, pos_ok, wid, lane, gen0);
       qkv.init(W(l + 1, p.o_wqkv), 0, b, wid, lane);
-      run_gemv<SH, PH_DOWN>(p, ph_down, qkv, []() __attribute__((always_inline)) {}, A, B, sm, p.act, nullptr, nullptr, l, pos, pos_ok, wid, lane);
+      run_gemv<SH, PH_DOWN>(p, ph_down, qkv, [](int) __attribute__((always_inline)) {}, A, B, sm, p.act, nullptr, nullptr, l, pos, pos_ok, wid, lane, gen0);
     } else {
-      run_gemv<SH, PH_GU>(p, ph_gu, ph_down, []() __attribute__((always_inline)) {}, A, B, sm, p.x, GN(l, p.o_ffn_norm), nullptr, l, pos, pos_ok,
-                          wid, lane);
+      run_gemv<SH, PH_GU>(p, ph_gu, ph_down, [](int) __attribute__((always_inline)) {}, A, B, sm, p.x, GN(l, p.o_ffn_norm), nullptr, l, pos, pos_ok,
+                          wid, lane, gen0);
       GemvPhase<SH, PH_HEAD> head;
       head.init(p.lm_head, p.vocab, b, wid, lane);
-      run_gemv<SH, PH_DOWN>(p, ph_down, head, []() __attribute__((always_inline)) {}, A, B, sm, p.act, nullptr, nullptr, l, pos, pos_ok, wid,
-                            lane);
-      run_gemv<SH, PH_HEAD>(p, head, NoNext{}, []() __attribute__((always_inline)) {}, A, B, sm, p.x, p.final_norm, nullptr, l, pos, pos_ok, wid,
-                            lane);
+      run_gemv<SH, PH_DOWN>(p, ph_down, head, [](int) __attribute__((always_inline)) {}, A, B, sm, p.act, nullptr, nullptr, l, pos, pos_ok, wid,
+                            lane, gen0);
+      run_gemv<SH, PH_HEAD>(p, head, NoNext{}, [](int) __attribute__((always_inline)) {}, A, B, sm, p.x, p.final_norm, nullptr, l, pos, pos_ok, wid,
+                            lane, gen0);
     }
   }
 
-  // ---- leave: the last block out clears the last barrier's counter and the departure count
-  if (wid0 == 0) {
-    wait_all();
-    if (lane0 == 0 && !s_flags[0]) {
-      const unsigned prev = __hip_atomic_fetch_add(&p.sync[nbar], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev == (unsigned)(kFusedBlocks - 1)) {
-        st_dev(&p.sync[nbar - 1], 0u);
-        st_dev(&p.sync[nbar], 0u);
-        if (p.clocks) p.clocks[nbar + 1] = (unsigned long long)wall_clock64();
-      }
-    }
+  // ---- leave: block 0 advances the epoch (every block read it at its start, before the first barrier)
+  if (b0 == 0 && tid == 0) {
+    st_dev(&p.sync[0], ld_dev(&p.sync[0]) + 1u);
+    if (p.clocks) p.clocks[nbar + 1] = (unsigned long long)wall_clock64();
   }
 }
 

@@ -74,6 +74,7 @@ struct GemvParams {
   // shared
   const int* slots;      // slot buffer
   StatusWords* status;
+  int ping_pong;         // rows longer than one group: two groups in flight per wave
 };
 
 struct AttnParams {
@@ -146,9 +147,10 @@ struct FusedParams {
   float* act;                  // [ffn] SwiGLU output
   float* part;                 // [nkv][splits][G][hd + 2] split partials
   float* logits;               // [vocab]
-  unsigned* sync;              // [5 L] barrier counters, departures, abort flag, then [L][nkv] merge counters
+  unsigned* sync;              // fused_sync_words: epoch, abort flag, arrival / release / split flags
   unsigned long long* clocks;  // [5 L + 2] block 0's clock at the start, after every barrier, at the end
   unsigned long long* trace;   // [5 L][kFusedBlocks][2] every block's arrival and release time per barrier
+  unsigned long long* trace2;  // optional [5 L][kFusedBlocks][4] GEMV sub-phase clocks of wave 0 (null: off)
   const int* slots;
   StatusWords* status;
   int n_layers, vocab, cap;
@@ -157,8 +159,12 @@ struct FusedParams {
 };
 constexpr long long kFusedSpinTicks = 200000000LL;   // default grid-barrier wait limit: 2 s of the 100 MHz clock
 
-// Words of the fused kernel's sync region for `n_layers` layers and `nkv` kv heads.
-inline size_t fused_sync_words(int n_layers, int nkv) { return (size_t)kFusedPhases * n_layers + 2 + (size_t)n_layers * nkv; }
+// The fused kernel's sync region (32-bit words): [0] launch epoch, [1] abort flag, [kSyncArrive..+256) each
+// block's barrier arrival flag, [kSyncRelease + 32 x] the release flag seen by XCD x (one 128-byte line each),
+// [kSyncSplit + 32 g + s] split s of kv head g has written its attention partial. No flag is ever reset: each
+// holds the generation (epoch x (5 L + 1) + barrier + 1) it last signalled.
+constexpr int kSyncArrive = 256, kSyncRelease = 512, kSyncSplit = 1024;
+inline size_t fused_sync_words(int n_layers, int nkv) { (void)n_layers; return (size_t)kSyncSplit + 32 * (size_t)nkv; }
 
 // Host launchers (defined in ds3_kernels.hip). Each returns the launch error, if any.
 hipError_t launch_split(const SplitParams& p, bool norm, hipStream_t s);

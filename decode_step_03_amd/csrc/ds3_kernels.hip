@@ -25,6 +25,7 @@ namespace ds3 {
 
 constexpr int kBlock = 256;
 constexpr int kUnroll = 8;   // 16-byte loads in flight per lane per weight row
+constexpr int kPP = 4;       // long rows: chunks per group, two groups in flight
 constexpr int kMaxSplits = 32;          // attention: splits per (row, kv head), merged by the combine kernel
 constexpr int kAttnChunk = 128;         // attention: positions staged in LDS per chunk, at most ...
 constexpr int kAttnChunkBytes = 32768;  // ... and at most this many bytes of K (and of V)
@@ -113,24 +114,24 @@ struct PairMap {
 
 // Loads of one group of kUnroll chunks of two weight rows. Past the row's end the chunk index is clamped to the
 // last chunk and the element index to the last 16 bytes: in bounds, no branches; fma_group zeroes them.
-template <typename WT>
+template <typename WT, int U = kUnroll>
 __device__ __forceinline__ void load_group(const WT* w0, const WT* w1, int c0, int nchunks, int K, int lane,
-                                           u32x4 (&b0)[kUnroll], u32x4 (&b1)[kUnroll]) {
+                                           u32x4 (&b0)[U], u32x4 (&b1)[U]) {
   constexpr int EPL = Pack<WT>::N;
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
+  for (int u = 0; u < U; ++u) {
     const int k = min(min(c0 + u, nchunks - 1) * (64 * EPL) + lane * EPL, K - EPL);
     b0[u] = load_stream(w0 + k);
     b1[u] = load_stream(w1 + k);
   }
 }
 
-template <typename WT, int NR>
-__device__ __forceinline__ void fma_group(const u32x4 (&b0)[kUnroll], const u32x4 (&b1)[kUnroll], const float* xs,
+template <typename WT, int NR, int U = kUnroll>
+__device__ __forceinline__ void fma_group(const u32x4 (&b0)[U], const u32x4 (&b1)[U], const float* xs,
                                           int c0, int nchunks, int K, int lane, float (&a0)[NR], float (&a1)[NR]) {
   constexpr int EPL = Pack<WT>::N;
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
+  for (int u = 0; u < U; ++u) {
     const int kr = (c0 + u) * (64 * EPL) + lane * EPL;
     const bool valid = c0 + u < nchunks && kr < K;
     const int k = min(min(c0 + u, nchunks - 1) * (64 * EPL) + lane * EPL, K - EPL);
@@ -154,7 +155,10 @@ __device__ __forceinline__ void fma_group(const u32x4 (&b0)[kUnroll], const u32x
   }
 }
 
-template <typename WT, typename KT, int NR, int MODE, int XREG>
+// PP (long rows): two groups of kPP chunks in flight per wave (ping-pong buffers), the second issued before the
+// first is consumed, so the wave always has loads in flight; groups are half as wide as kUnroll to keep the
+// register footprint (and with it two waves per SIMD).
+template <typename WT, typename KT, int NR, int MODE, int XREG, bool PP>
 __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
   extern __shared__ float xs[];  // [NR][K] activations (times the gain in the norm modes)
   __shared__ float red[NR][kBlock / 64];
@@ -191,7 +195,8 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
 
   // ---- 2. the first pair's weights (they do not depend on the activations) and its epilogue operands
   const WT* wbase = reinterpret_cast<const WT*>(p.w);
-  u32x4 b0[kUnroll], b1[kUnroll];
+  constexpr int GU = PP ? kPP : kUnroll;   // chunks per group
+  u32x4 b0[GU], b1[GU];
   float ea[NR], eb[NR];
   int pair = blockIdx.x * (kBlock / 64) + wid;
   PairMap<MODE> pm(p, min(pair, p.n_pairs - 1));
@@ -221,7 +226,7 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
     }
   };
   // unconditional (the pair index is clamped): a branch here would make every later wait conservative
-  load_group<WT>(w0, w1, 0, nchunks, K, lane, b0, b1);
+  load_group<WT, GU>(w0, w1, 0, nchunks, K, lane, b0, b1);
   fetch_epilogue(pm, min(pair, p.n_pairs - 1));
 
   // ---- 3. LDS fill (clamped lanes rewrite the same value) and the RMSNorm sums of squares
@@ -275,13 +280,29 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
   // ---- 4. pairs. As soon as a pair's dot products have consumed its weights, the next pair's weights (and
   // epilogue operands) are issued, so they are in flight during this pair's reduction and epilogue.
   float na[NR], nb[NR];
+  [[maybe_unused]] u32x4 d0[GU], d1[GU];
   for (; pair < p.n_pairs;) {
     float a0[NR], a1[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) { a0[r] = 0.f; a1[r] = 0.f; }
-    for (int c0 = 0; c0 < nchunks; c0 += kUnroll) {
-      if (c0 > 0) load_group<WT>(w0, w1, c0, nchunks, K, lane, b0, b1);
-      fma_group<WT, NR>(b0, b1, xs, c0, nchunks, K, lane, a0, a1);
+    int c_last = 0;   // PP: the group still to be consumed from d after the next pair's loads are out
+    if constexpr (PP) {
+      int c0 = 0;
+      for (; c0 + 2 * GU < nchunks; c0 += 2 * GU) {
+        load_group<WT, GU>(w0, w1, c0 + GU, nchunks, K, lane, d0, d1);
+        fma_group<WT, NR, GU>(b0, b1, xs, c0, nchunks, K, lane, a0, a1);
+        load_group<WT, GU>(w0, w1, c0 + 2 * GU, nchunks, K, lane, b0, b1);
+        fma_group<WT, NR, GU>(d0, d1, xs, c0 + GU, nchunks, K, lane, a0, a1);
+      }
+      // the last one or two groups (a group past the row end is clamped in bounds and masked to zero)
+      load_group<WT, GU>(w0, w1, c0 + GU, nchunks, K, lane, d0, d1);
+      fma_group<WT, NR, GU>(b0, b1, xs, c0, nchunks, K, lane, a0, a1);
+      c_last = c0 + GU;
+    } else {
+      for (int c0 = 0; c0 < nchunks; c0 += kUnroll) {
+        if (c0 > 0) load_group<WT>(w0, w1, c0, nchunks, K, lane, b0, b1);
+        fma_group<WT, NR>(b0, b1, xs, c0, nchunks, K, lane, a0, a1);
+      }
     }
     const PairMap<MODE> cur = pm;
     const int cur_pair = pair;
@@ -292,9 +313,10 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
       pm = PairMap<MODE>(p, pair);
       w0 = wbase + (size_t)pm.row0 * K;
       w1 = wbase + (size_t)pm.row1 * K;
-      load_group<WT>(w0, w1, 0, nchunks, K, lane, b0, b1);
+      load_group<WT, GU>(w0, w1, 0, nchunks, K, lane, b0, b1);
       fetch_epilogue(pm, pair);
     }
+    if constexpr (PP) fma_group<WT, NR, GU>(d0, d1, xs, c_last, nchunks, K, lane, a0, a1);
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       a0[r] = wave_total(a0[r]);
@@ -1124,7 +1146,12 @@ hipError_t launch_embed(const EmbedParams& p, int weight_dtype, hipStream_t s) {
 
 template <typename WT, typename KT, int MODE, int NR, int XREG>
 static hipError_t gemv_go(const GemvParams& p, int blocks, hipStream_t s) {
-  auto* f = gemv_kernel<WT, KT, NR, MODE, XREG>;
+  // long rows (more than one group of kUnroll chunks) get the ping-pong variant; only the residual GEMVs have them
+  const int nchunks = (p.K + 64 * Pack<WT>::N - 1) / (64 * Pack<WT>::N);
+  // (the ping-pong variant keeps only 4 float4 of the activation in registers: its second buffer needs the room)
+  auto* f = gemv_kernel<WT, KT, NR, MODE, XREG, false>;
+  if constexpr (MODE == GEMV_RESID)
+    if (nchunks > kUnroll && p.ping_pong) f = gemv_kernel<WT, KT, NR, MODE, 4, true>;
   const size_t lds = gemv_lds_bytes(p.rows, p.K, MODE != GEMV_RESID);
   hipError_t e = set_lds(f, lds);
   if (e != hipSuccess) return e;

@@ -107,10 +107,14 @@ class Engine:
         return [{"name": k.name.decode(), "launches": k.launches, "us_per_step": k.total_us, "bytes_per_step": k.bytes}
                 for k in C.ds3_profile_kernels(self.handle, iters)]
 
-    def phase_trace(self) -> np.ndarray:
-        """Fused plan: [barriers, blocks, 2] arrival / release clock ticks (100 MHz) of the last step."""
-        n = 5 * self.cfg.n_layers * 256 * 2
-        return np.array(C.ds3_phase_trace(self.handle, n), dtype=np.uint64).reshape(5 * self.cfg.n_layers, 256, 2)
+    def phase_trace(self, sub_phases: bool = False):
+        """Fused plan: [barriers, blocks, 2] arrival / release clock ticks (100 MHz) of the last step; with
+        sub_phases also [barriers, blocks, 8] sub-phase ticks of wave 0 (needs DS3_FUSED_TRACE2=1)."""
+        nb = 5 * self.cfg.n_layers
+        n = nb * 256 * 2
+        a = np.array(C.ds3_phase_trace(self.handle, 5 * n if sub_phases else n), dtype=np.uint64)
+        bar = a[:n].reshape(nb, 256, 2)
+        return (bar, a[n:].reshape(nb, 256, 8)) if sub_phases else bar
 
     def debug_inject(self, kind: int) -> None:
         C.ds3_debug_inject(self.handle, kind)

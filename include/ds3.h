@@ -199,8 +199,11 @@ ds3_status ds3_profile_kernels(ds3_engine* e, int32_t iters, ds3_kernel_time* ou
 
 /* Fused plan only: the grid-barrier trace of the last step, uint64 [5 n_layers][256 blocks][2] = each block's
  * wall-clock time (100 MHz ticks) when it arrived at the barrier and when it was released; the barriers close the
- * QKV, attention, o-proj, gate/up and down phases of each layer in order. *n_inout: room in `out` on entry, words
- * written on return. DS3_E_UNSUPPORTED with the per-operation plan. */
+ * QKV, attention, o-proj, gate/up and down phases of each layer in order. With room for five times as many words,
+ * [5 n_layers][256][8] sub-phase clocks follow (zero unless the engine was created with DS3_FUSED_TRACE2=1 in the
+ * environment): GEMV phases -- start, first batch consumed, batches done, block done; attention -- start, inputs
+ * in, sweep done, partial stored, all splits flagged (merging block), merge stored. *n_inout: room in `out` on entry, words written on return. DS3_E_UNSUPPORTED with the
+ * per-operation plan. */
 ds3_status ds3_phase_trace(ds3_engine* e, uint64_t* out, int32_t* n_inout);
 
 /* Test hook for the failure path: DS3_INJECT_KERNEL_CHECK makes the next step's first kernel raise its check
