@@ -150,14 +150,19 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 template <int CPR>
 __device__ __forceinline__ int kswz(int pj) { return ((pj & 3) | ((pj >> 1) & 12)) & (CPR - 1); }
 
+// Two floats -> two bf16 words (low word = a) with gfx950's packed convert, round to nearest, ties to even.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v{a, b}), bf16x2v));
+}
+
 __device__ __forceinline__ void split_hi_lo8(const float (&v)[8], bf16x8& hi, bf16x8& lo) {
   uint32_t hw[4], lw[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const uint16_t h0 = to_bf16(v[2 * e]), h1 = to_bf16(v[2 * e + 1]);
-    const uint16_t l0 = to_bf16(v[2 * e] - widen1(h0)), l1 = to_bf16(v[2 * e + 1] - widen1(h1));
-    hw[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    lw[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    hw[e] = cvt_pk_bf16(v[2 * e], v[2 * e + 1]);
+    lw[e] = cvt_pk_bf16(v[2 * e] - __uint_as_float(hw[e] << 16), v[2 * e + 1] - __uint_as_float(hw[e] & 0xffff0000u));
   }
   hi = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
   lo = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});

@@ -131,28 +131,48 @@ __device__ __forceinline__ T* opaque_p(T* v) {
   return v;
 }
 
+// Lanes l and l + 32 (swap32), or l and l + 16 within each half (swap16), exchange: after the swap, lanes below
+// the partner hold x of both lanes and lanes above hold y of both, so their sum is the pair's x total in the
+// lower lane and the pair's y total in the upper one (one permlane swap and one add per pair of values).
+__device__ __forceinline__ float swap_sum32(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_sum16(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // RBP values per lane -> the wave total of value (lane >> (6 - log2 RBP)), identical in the lanes that hold it.
-// Halving steps (lanes differing in bit m exchange the half of the values the partner keeps) then a butterfly
-// over the remaining lane bits; every partial sum is formed in the same order on every run.
+// Halving steps, from lane bit 5 down: the lanes whose bit is clear keep the lower half of the values and add the
+// partner's lower half, the others the upper half. Bits 5 and 4 use the permlane swaps; bits 3 and 2 the row and
+// half-row mirror DPP permutations (the partner differs in lower bits too, which the closing sum over those bits
+// absorbs). Every partial sum is formed in the same order on every run.
 template <int RBP>
 __device__ __forceinline__ float transpose_reduce(float (&a)[RBP], int lane) {
   constexpr int LOG = RBP == 1 ? 0 : RBP == 2 ? 1 : RBP == 4 ? 2 : RBP == 8 ? 3 : 4;
+  if constexpr (LOG >= 1) {
 #pragma unroll
-  for (int s = 0; s < LOG; ++s) {
-    const int m = 32 >> s;
-    const int H = RBP >> (s + 1);
-    const bool up = (lane & m) != 0;
+    for (int k = 0; k < RBP / 2; ++k) a[k] = swap_sum32(a[k], a[k + RBP / 2]);
+  }
+  if constexpr (LOG >= 2) {
 #pragma unroll
-    for (int k = 0; k < H; ++k) {
-      const float send = up ? a[k] : a[k + H];
-      const float recv = __shfl_xor(send, m, 64);
-      a[k] = (up ? a[k + H] : a[k]) + recv;
+    for (int k = 0; k < RBP / 4; ++k) a[k] = swap_sum16(a[k], a[k + RBP / 4]);
+  }
+  if constexpr (LOG >= 3) {
+    const bool up = (lane & 8) != 0;
+#pragma unroll
+    for (int k = 0; k < RBP / 8; ++k) {
+      const float send = up ? a[k] : a[k + RBP / 8];
+      a[k] = (up ? a[k + RBP / 8] : a[k]) + dpp_mov<0x140>(send);   // row_mirror: lane i <-> 15 - i
     }
   }
-  float v = a[0];
-#pragma unroll
-  for (int m = 32 >> LOG; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  if constexpr (LOG >= 4) {
+    const bool up = (lane & 4) != 0;
+    const float send = up ? a[0] : a[1];
+    a[0] = (up ? a[1] : a[0]) + dpp_mov<0x141>(send);   // row_half_mirror: lane i <-> 7 - i
+  }
+  return group_sum<(64 >> LOG)>(a[0]);
 }
 
 template <int KS>
@@ -197,9 +217,12 @@ struct GemvPhase {
   int r0, r1, ks;       // wave: rows [r0, r1) of the block, input slice
   int nb;               // batches (even)
   int lane;
+  const int* rtab;      // QKV: byte offsets of the block's weight rows (LDS, the same for every layer)
 
-  __device__ __forceinline__ void init(const void* w_, int units_total, int b, int wid, int lane_) {
+  __device__ __forceinline__ void init(const void* w_, int units_total, int b, int wid, int lane_,
+                                       const int* rtab_ = nullptr) {
     w = reinterpret_cast<const uint16_t*>(w_);
+    rtab = rtab_;
     lane = lane_;
     const int units = PH == PH_HEAD ? units_total : GE::UNITS;
     u0 = (int)(((long long)b * units) / kFusedBlocks);
@@ -233,11 +256,19 @@ struct GemvPhase {
     const int rfirst = opaque_s(r0 + i * GE::RB);
 #pragma unroll
     for (int j = 0; j < GE::RB; ++j) {
-      const int br = min(rfirst + j, r1 - 1);
-      const int so = row_of(br) * (GE::K * 2);
+      // (no clamp where the wave's rows are whole batches)
+      const int br = (PH != PH_HEAD && GE::NBT * GE::RB == GE::RW) ? rfirst + j : min(rfirst + j, r1 - 1);
+      if constexpr (PH == PH_QKV) {   // (the table's offset rides in the lane offset)
+        const int vo = lo + rtab[br];
 #pragma unroll
-      for (int c = 0; c < GE::CW; ++c)
-        buf[j * GE::CW + c] = __builtin_amdgcn_raw_buffer_load_b128(wr, lo, so + c * 1024, kNt);
+        for (int c = 0; c < GE::CW; ++c)
+          buf[j * GE::CW + c] = __builtin_amdgcn_raw_buffer_load_b128(wr, vo, c * 1024, kNt);
+      } else {
+        const int so = row_of(br) * (GE::K * 2);
+#pragma unroll
+        for (int c = 0; c < GE::CW; ++c)
+          buf[j * GE::CW + c] = __builtin_amdgcn_raw_buffer_load_b128(wr, lo, so + c * 1024, kNt);
+      }
     }
   }
 
@@ -336,28 +367,26 @@ __device__ __forceinline__ void arrive_and_wait(const FusedParams& p, unsigned g
   wait_all();
   const long long t0 = wall_clock64();
   const unsigned gen = gen0 + (unsigned)bar + 1u;
+  const bool col = blockIdx.x == 0;   // the collector
+  const bool early = !col && !flags[0];
   if (!flags[0]) {
     if (lane == 0) st_dev(&p.sync[kSyncArrive + blockIdx.x], gen);
-    if (blockIdx.x == 0) {
-      // the collector: every block's arrival flag, four per lane, then one release flag per XCD
-      const auto ra = make_rsrc(p.sync + kSyncArrive);
-      const bool ok = spin_until(p, flags, [&]() __attribute__((always_inline)) {
-        const u32x4 v = ld_dev16(ra, lane * 16);
-        return __all(v.x == gen && v.y == gen && v.z == gen && v.w == gen) != 0;
-      });
-      if (ok && lane < 8) st_dev(&p.sync[kSyncRelease + 32 * lane], gen);
-    } else {
-      // (the weights go out first: the polls then wait for them too, but the release rarely comes sooner)
-      prefetch();
-      const unsigned* rel = p.sync + kSyncRelease + 32 * (blockIdx.x & 7);
-      spin_until(p, flags, [&]() __attribute__((always_inline)) { return __all(ld_dev(rel) == gen) != 0; });
-    }
+    // (the weights go out first: the polls then wait for them too, but the release rarely comes sooner)
+    if (early) prefetch();
+    // the collector polls every block's arrival flag (four per lane), the others their XCD's release flag
+    const auto rf = make_rsrc(p.sync + (col ? kSyncArrive : kSyncRelease + 32 * (blockIdx.x & 7)));
+    const int off = col ? lane * 16 : 0;
+    const bool ok = spin_until(p, flags, [&]() __attribute__((always_inline)) {
+      const u32x4 v = ld_dev16(rf, off);
+      return __all(v.x == gen && (!col || (v.y == gen && v.z == gen && v.w == gen))) != 0;
+    });
+    if (col && ok && lane < 8) st_dev(&p.sync[kSyncRelease + 32 * lane], gen);
   }
   if (lane == 0 && p.trace) {   // this block's arrival and release times at barrier `bar`
     p.trace[((size_t)bar * kFusedBlocks + blockIdx.x) * 2] = (unsigned long long)t0;
     p.trace[((size_t)bar * kFusedBlocks + blockIdx.x) * 2 + 1] = (unsigned long long)wall_clock64();
   }
-  if (blockIdx.x == 0 || flags[0]) prefetch();
+  if (!early) prefetch();
 }
 
 // After the block-wide barrier that follows arrive_and_wait: block 0 stamps the clock.
@@ -442,7 +471,7 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
   }
   // ---- 3. batches: two in flight; each freed buffer takes the next batch
   // (a buffer is refilled as soon as its dot products have read it, before the reduction's shuffles)
-  for (int i = 0; i < ph.nb; i += 2) {
+  auto step = [&](int i) __attribute__((always_inline)) {
     float acc[GE::RBP];
     ph.fma(A, xa, acc);
     if (i == 0 && st) st[1] = (unsigned long long)wall_clock64();
@@ -452,6 +481,12 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
     if (i + 3 < ph.nb) ph.issue(i + 3, B);
     ph.reduce(i + 1, acc, red);
     extra(i / 2);
+  };
+  if constexpr (GE::NBT > 4) {   // (long loops stay rolled: one copy of the body in the instruction cache)
+#pragma nounroll
+    for (int i = 0; i < ph.nb; i += 2) step(i);
+  } else {
+    for (int i = 0; i < ph.nb; i += 2) step(i);
   }
   if (st) st[2] = (unsigned long long)wall_clock64();
   __syncthreads();
@@ -774,6 +809,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedParams p) {
   __shared__ __attribute__((aligned(16))) float s_uni[SH::UNI];
   __shared__ float s_ssq[kFW];
   __shared__ int s_flags[2];
+  __shared__ int s_qrow[Geo<SH, PH_QKV>::RPB];
   const Smem<SH> sm{s_stage, s_uni, s_ssq, s_flags};
   const int tid = threadIdx.x, lane0 = tid & 63, wid0 = __builtin_amdgcn_readfirstlane(tid >> 6), b0 = blockIdx.x;
   const int L = p.n_layers;
@@ -810,7 +846,9 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedParams p) {
 
   u32x4 A[kNL], B[kNL];
   GemvPhase<SH, PH_QKV> qkv;
-  qkv.init(W(0, p.o_wqkv), 0, b0, wid0, lane0);
+  qkv.init(W(0, p.o_wqkv), 0, b0, wid0, lane0, s_qrow);
+  if (tid < qkv.rb) s_qrow[tid] = qkv.row_of(tid) * (SH::D * 2);
+  __syncthreads();
   stage_layer(0, b0, wid0, lane0, -1);
   qkv.issue(0, A);
   qkv.issue(1, B);
@@ -834,7 +872,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedParams p) {
     if (l + 1 < L) {
       run_gemv<SH, PH_GU>(p, ph_gu, ph_down, [&](int it) __attribute__((always_inline)) { stage_layer(l + 1, b, wid, lane, it); }, A, B, sm, p.x, GN(l, p.o_ffn_norm),
                           nullptr, l, pos, pos_ok, wid, lane, gen0);
-      qkv.init(W(l + 1, p.o_wqkv), 0, b, wid, lane);
+      qkv.init(W(l + 1, p.o_wqkv), 0, b, wid, lane, s_qrow);
       run_gemv<SH, PH_DOWN>(p, ph_down, qkv, [](int) __attribute__((always_inline)) {}, A, B, sm, p.act, nullptr, nullptr, l, pos, pos_ok, wid, lane, gen0);
     } else {
       run_gemv<SH, PH_GU>(p, ph_gu, ph_down, [](int) __attribute__((always_inline)) {}, A, B, sm, p.x, GN(l, p.o_ffn_norm), nullptr, l, pos, pos_ok,
