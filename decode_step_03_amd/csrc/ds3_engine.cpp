@@ -678,9 +678,9 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   e->blocks[K_HEAD] = gemv_blocks(c.vocab / 2, cus);
 
   // kernel plan: the fused step kernel needs its shape, one block per CU of a 256-CU device, and co-residency.
-  // AUTO takes the per-operation kernels: on this GPU their kernel boundaries cost less than the fused kernel's
-  // grid barriers (device-scope atomics serialize under contention), so FUSED is chosen only on request.
-  if (c.kernel_plan == DS3_PLAN_FUSED && fused_refusal(c).empty()) {
+  // AUTO takes it wherever it applies (it is the faster plan at one row: no kernel boundaries, and the next
+  // phase's weights stream while the grid synchronizes), else the per-operation kernels.
+  if ((c.kernel_plan == DS3_PLAN_FUSED || c.kernel_plan == DS3_PLAN_AUTO) && fused_refusal(c).empty()) {
     int per_cu = 0;
     h = fused_blocks_per_cu(c.d_model, c.ffn_dim, c.head_dim, c.n_q_heads, c.n_kv_heads,
                             c.cap / (kFusedBlocks / c.n_kv_heads), &per_cu);
