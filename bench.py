@@ -119,16 +119,26 @@ def cpu_baseline(w, ws, start_pos, start_tok, budget_s: float) -> dict:
 CSRC = os.path.join(ROOT, "decode_step_03_amd", "csrc")
 
 
-def kernel_source(kind: str) -> str:
-    return os.path.join(CSRC, "ds3_fused.hip" if kind == "decode_step_fused" else "ds3_kernels.hip")
+def kernel_sources(kind: str) -> list:
+    """The source files a kernel kind is compiled from (its own file and the device headers it includes)."""
+    main = "ds3_fused.hip" if kind == "decode_step_fused" else "ds3_kernels.hip"
+    return [os.path.join(CSRC, f) for f in (main, "ds3_device.h", "ds3_kernels.h")]
+
+
+def sources_sha256(kind: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for path in kernel_sources(kind):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def pmc_traffic(kind: str, workload: str):
     """HBM bytes per launch of kernel kind `kind` on `workload`, from the committed rocprofv3 counter summary
     profiles/pmc_<kind>_<workload>.md (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the counter
     reads for a plain copy of known size). None when there is no summary, or when the kernel source has changed
-    since the counters were taken (the summary records the source's SHA-256)."""
-    import hashlib
+    since the counters were taken (the summary records the SHA-256 of its source files)."""
     path = os.path.join(ROOT, "profiles", f"pmc_{kind}_{workload}.md")
     if not os.path.exists(path):
         return None
@@ -138,9 +148,8 @@ def pmc_traffic(kind: str, workload: str):
             k, v = line[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
     try:
-        with open(kernel_source(kind), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != vals["kernel_source_sha256"]:
-                return None
+        if sources_sha256(kind) != vals["kernel_source_sha256"]:
+            return None
         return (float(vals["fetch_kib_per_launch"]) * float(vals["fetch_scale"])
                 + float(vals["write_kib_per_launch"]) * float(vals["write_scale"])) * 1024.0
     except (KeyError, ValueError, OSError):
