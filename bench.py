@@ -53,14 +53,14 @@ def algorithmic_bytes(w) -> float:
             + L * R * 2 * m.n_kv_heads * hd * kvb)
 
 
-def engine_for(w, ws, exec_mode, kernel_plan="auto"):
+def engine_for(w, ws, exec_mode, kernel_plan="auto", trace="off"):
     from decode_step_03_amd import Engine, make_config
     m = w.model
     cfg = make_config(n_layers=m.n_layers, d_model=m.d_model, n_q_heads=m.n_q_heads, n_kv_heads=m.n_kv_heads,
                       head_dim=m.head_dim, ffn_dim=m.ffn_dim, vocab=m.vocab, rms_eps=m.rms_eps,
                       rope_theta=m.rope_theta, rows=w.rows, cap=w.cap, kv_layout=w.kv_layout,
                       page_size=w.page_size, pool_pages=w.pool_pages, weight_dtype=m.weight_dtype,
-                      kv_dtype=w.kv_dtype, exec_mode=exec_mode, kernel_plan=kernel_plan)
+                      kv_dtype=w.kv_dtype, exec_mode=exec_mode, kernel_plan=kernel_plan, trace=trace)
     eng = Engine(cfg, "cuda:0")
     eng.load_weights(ws.layers, ws.glob)
     return eng

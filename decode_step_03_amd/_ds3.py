@@ -11,7 +11,7 @@ from ctypes import POINTER, c_char, c_double, c_float, c_int32, c_int64, c_uint3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libds3.so")
 
-DS3_ABI_VERSION = 2
+DS3_ABI_VERSION = 3
 
 # ds3_status
 DS3_OK = 0
@@ -32,6 +32,7 @@ DS3_F32, DS3_BF16 = 0, 1
 DS3_KV_CONTIGUOUS, DS3_KV_PAGED = 0, 1
 DS3_GRAPH, DS3_EAGER = 0, 1
 DS3_PLAN_AUTO, DS3_PLAN_PER_OP, DS3_PLAN_FUSED = 0, 1, 2
+DS3_TRACE_OFF, DS3_TRACE_BARRIERS, DS3_TRACE_PHASES = 0, 1, 2
 DS3_BUF_WEIGHTS, DS3_BUF_KV, DS3_BUF_WORK, DS3_BUF_LOGITS, DS3_NUM_BUFFERS = 0, 1, 2, 3, 4
 DS3_INJECT_KERNEL_CHECK, DS3_INJECT_TIMEOUT_NEXT, DS3_INJECT_BARRIER_TIMEOUT = 1, 2, 3
 
@@ -44,7 +45,8 @@ class ds3_config(ctypes.Structure):
                 ("n_kv_heads", c_int32), ("head_dim", c_int32), ("ffn_dim", c_int32), ("vocab", c_int32),
                 ("rms_eps", c_float), ("rope_theta", c_double), ("rows", c_int32), ("cap", c_int32),
                 ("kv_layout", c_int32), ("page_size", c_int32), ("pool_pages", c_int32), ("weight_dtype", c_int32),
-                ("kv_dtype", c_int32), ("exec_mode", c_int32), ("timeout_ms", c_uint32), ("kernel_plan", c_int32)]
+                ("kv_dtype", c_int32), ("exec_mode", c_int32), ("timeout_ms", c_uint32), ("kernel_plan", c_int32),
+                ("trace", c_int32)]
 
 
 class ds3_buffer_req(ctypes.Structure):

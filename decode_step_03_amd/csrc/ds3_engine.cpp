@@ -74,6 +74,7 @@ struct ds3_engine {
   unsigned* sync = nullptr;                          // fused: barrier and merge counters
   unsigned long long* clocks = nullptr;              // fused: block 0's clock per barrier
   unsigned long long* trace = nullptr;               // fused: every block's arrival and release per barrier
+  bool profiling = false;                            // fused: profile_kernels' own launches record the clocks
   size_t sync_words = 0;
   size_t weight_lstride = 0;                         // bytes between consecutive layers' weights
   size_t work_bytes = 0;
@@ -176,6 +177,8 @@ std::string check_config(const ds3_config* c) {
   if (c->exec_mode != DS3_GRAPH && c->exec_mode != DS3_EAGER) return "exec_mode must be DS3_GRAPH or DS3_EAGER";
   if (c->kernel_plan != DS3_PLAN_AUTO && c->kernel_plan != DS3_PLAN_PER_OP && c->kernel_plan != DS3_PLAN_FUSED)
     return "kernel_plan must be DS3_PLAN_AUTO, DS3_PLAN_PER_OP or DS3_PLAN_FUSED";
+  if (c->trace != DS3_TRACE_OFF && c->trace != DS3_TRACE_BARRIERS && c->trace != DS3_TRACE_PHASES)
+    return "trace must be DS3_TRACE_OFF, DS3_TRACE_BARRIERS or DS3_TRACE_PHASES";
   if (c->kv_layout == DS3_KV_PAGED) {
     if (c->page_size < 1) return "page_size must be >= 1";
     if (c->cap % c->page_size) return "cap must be a multiple of page_size";
@@ -258,7 +261,7 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
   w.attn = take((size_t)c.rows * c.n_q_heads * c.head_dim * 4);
   w.act = take((size_t)c.rows * c.ffn_dim * 4);
   w.part = take((size_t)c.rows * c.n_kv_heads * std::max(splits, kFusedBlocks / c.n_kv_heads) * G *
-                (c.head_dim + 2) * 4);
+                (c.head_dim + 4) * 4);
   w.kvnew = take((size_t)c.n_kv_heads * 2 * c.head_dim * 4);
   w.sync = take(fused_sync_words(c.n_layers, c.n_kv_heads) * 4);
   w.clocks = take(((size_t)kFusedPhases * c.n_layers + 2) * 8);
@@ -424,7 +427,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.sync = e->sync;
       p.clocks = e->clocks;
       p.trace = e->trace;
-      p.trace2 = env_int("DS3_FUSED_TRACE2", 0) ? e->trace + (size_t)kFusedPhases * c.n_layers * kFusedBlocks * 2 : nullptr;
+      p.trace2 = c.trace >= DS3_TRACE_PHASES ? e->trace + (size_t)kFusedPhases * c.n_layers * kFusedBlocks * 2 : nullptr;
       p.slots = e->slots;
       p.status = e->status;
       p.n_layers = c.n_layers;
@@ -433,7 +436,9 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.split_len = c.cap / (kFusedBlocks / c.n_kv_heads);
       p.eps = c.rms_eps;
       p.scale = (float)(1.0 / std::sqrt((double)c.head_dim));
-      return launch_fused(p, c.d_model, c.ffn_dim, c.head_dim, c.n_q_heads, c.n_kv_heads, e->stream);
+      // the traced variant only when a trace was asked for, or while profile_kernels reads the phase clocks
+      const bool trace = c.trace != DS3_TRACE_OFF || e->profiling;
+      return launch_fused(p, c.d_model, c.ffn_dim, c.head_dim, c.n_q_heads, c.n_kv_heads, trace, e->stream);
     }
     case K_SPLIT: {
       SplitParams sp{};
@@ -1103,7 +1108,10 @@ ds3_status ds3_profile_kernels(ds3_engine* e, int32_t iters, ds3_kernel_time* ou
     const int L = e->cfg.n_layers, nc = kFusedPhases * L + 2;
     std::vector<unsigned long long> clk((size_t)nc);
     for (int it = 0; it < iters; ++it) {
-      HIP_OR_POISON(e, enqueue_step(e));
+      e->profiling = true;
+      const hipError_t hp = enqueue_step(e);
+      e->profiling = false;
+      HIP_OR_POISON(e, hp);
       HIP_OR_POISON(e, hipMemcpyAsync(clk.data(), e->clocks, (size_t)nc * 8, hipMemcpyDeviceToHost, e->stream));
       HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
       e->pending = true;
@@ -1132,6 +1140,8 @@ ds3_status ds3_profile_kernels(ds3_engine* e, int32_t iters, ds3_kernel_time* ou
 ds3_status ds3_phase_trace(ds3_engine* e, uint64_t* out, int32_t* n_inout) {
   if (ds3_status st = refuse_if_unusable(e)) return st;
   if (!e->fused) return fail(e, DS3_E_UNSUPPORTED, "phase trace needs the fused plan");
+  if (e->cfg.trace == DS3_TRACE_OFF)
+    return fail(e, DS3_E_UNSUPPORTED, "phase trace needs an engine created with trace = DS3_TRACE_BARRIERS or above");
   const int64_t n2 = (int64_t)kFusedPhases * e->cfg.n_layers * kFusedBlocks * 2;
   if (!out || !n_inout || *n_inout < n2) return fail(e, DS3_E_INVALID, "need room for " + std::to_string(n2) + " words");
   const int64_t n = *n_inout >= 5 * n2 ? 5 * n2 : n2;   // with room: the sub-phase clocks follow

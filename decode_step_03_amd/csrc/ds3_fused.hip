@@ -81,6 +81,12 @@ struct Geo {
   static constexpr int NL = RB * CW;                                                     // loads per batch
   static constexpr int RBP = RB <= 1 ? 1 : RB <= 2 ? 2 : RB <= 4 ? 4 : RB <= 8 ? 8 : 16;
   static constexpr int LOG = RBP == 1 ? 0 : RBP == 2 ? 1 : RBP == 4 ? 2 : RBP == 8 ? 3 : 4;
+  // gate/up: batches 2 .. 2 + NLB - 1 of every wave travel through the LDS stage area (free between the attention
+  // sweep and the next layer's K/V staging), loaded while the attention and o-projection phases wait on their
+  // barriers, when HBM would otherwise idle. 1 KB slots; wave w's in slots w, w + 8, w + 16, ...
+  static constexpr int SLOTS_PER_WAVE = 2 * SH::KB / 1024 / kFW;
+  static constexpr int NLB = (PH == PH_GU && CW == 1) ? (SLOTS_PER_WAVE / RB < 2 ? SLOTS_PER_WAVE / RB : 2) : 0;
+  static_assert(NLB == 0 || NBT >= 2 + NLB + 1, "LDS batches leave streamed batches");
   static_assert(C * 512 == K && KS * CW == C, "input width must be whole 512-element chunks");
   static_assert(NL >= 1 && NL <= kNL && RB <= 16, "a batch is at most kNL loads per lane");
   static_assert(PH == PH_HEAD || UNITS % kFusedBlocks == 0, "units split evenly over the blocks");
@@ -272,6 +278,40 @@ struct GemvPhase {
     }
   }
 
+  // Gate/up only: load every wave's LDS batches (weights of batches 2 .. 2 + NLB - 1) into the stage area; wave
+  // `wid` (1..7) takes slots wid - 1, wid + 6, ... of the NLB RB 8 slots (slot w + 8 (bb RB + j): row j of LDS
+  // batch bb of wave w).
+  __device__ __forceinline__ void lds_prefetch(unsigned char* stage, int wid) const {
+    constexpr int NS = GE::NLB * GE::RB * kFW;
+    for (int k = wid - 1; k < NS; k += kFW - 1) {
+      const int w = k % kFW, m = k / kFW, bb = m / GE::RB, j = m % GE::RB;
+      const int rg = w / GE::KS, kw = w % GE::KS;
+      const int rw0 = rg * rb / GE::RS, rw1 = (rg + 1) * rb / GE::RS;
+      const int br = min(rw0 + (2 + bb) * GE::RB + j, rw1 - 1);
+      const uint16_t* src = w_row(br) + kw * (GE::CW * 512) + lane * 8;
+      __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(stage + (size_t)(w + kFW * m) * 1024), 16, 0,
+                                       kNt);
+    }
+  }
+  __device__ __forceinline__ const uint16_t* w_row(int br) const {
+    return opaque_p(w) + (size_t)row_of(br) * GE::K;
+  }
+
+  // dot products of LDS batch bb's rows (this wave's slots) with the activation slice
+  __device__ __forceinline__ void fma_lds(const unsigned char* stage, int bb, int wid, const float (&xa)[GE::CW][8],
+                                         float (&acc)[GE::RBP]) const {
+#pragma unroll
+    for (int j = 0; j < GE::RBP; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int j = 0; j < GE::RB; ++j) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + (size_t)(wid + kFW * (bb * GE::RB + j)) * 1024 + lane * 16);
+      float f[8];
+      Pack<uint16_t>::widen(v, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j] = fmaf(f[e], xa[0][e], acc[j]);
+    }
+  }
+
   // dot products of batch i's rows with the activation slice (per lane)
   __device__ __forceinline__ void fma(const u32x4 (&buf)[kNL], const float (&xa)[GE::CW][8],
                                      float (&acc)[GE::RBP]) const {
@@ -331,7 +371,7 @@ struct Smem {
   unsigned char* stage;   // [K chunk | V^T chunk]
   float* uni;             // GEMV row partials [KS][rows] / attention wave states [8][G][HD + 2]
   float* ssq;             // [KS] RMSNorm sums of squares
-  int* flags;             // [0] abort seen, [1] this block merges the splits
+  int* flags;             // [0] abort seen, [1] generation of the last attention merge done by wave 0
 };
 
 // Bounded wait of wave 0 for `done()` (evaluated by every lane; the result must agree across the wave): false
@@ -471,22 +511,41 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
   }
   // ---- 3. batches: two in flight; each freed buffer takes the next batch
   // (a buffer is refilled as soon as its dot products have read it, before the reduction's shuffles)
-  auto step = [&](int i) __attribute__((always_inline)) {
+  // (batch i in A and i + 1 in B; each is refilled with the batch two places on, skipping the LDS batches)
+  constexpr int NLB = GE::NLB;
+  auto step = [&](int i, int it) __attribute__((always_inline)) {
     float acc[GE::RBP];
     ph.fma(A, xa, acc);
     if (i == 0 && st) st[1] = (unsigned long long)wall_clock64();
-    if (i + 2 < ph.nb) ph.issue(i + 2, A);
+    const int nx_a = i + 2 + (i == 0 ? NLB : 0);
+    if (nx_a < ph.nb) ph.issue(nx_a, A);
     ph.reduce(i, acc, red);
-    ph.fma(B, xa, acc);
-    if (i + 3 < ph.nb) ph.issue(i + 3, B);
-    ph.reduce(i + 1, acc, red);
-    extra(i / 2);
+    if (i + 1 < ph.nb) {
+      ph.fma(B, xa, acc);
+      const int nx_b = i + 3 + (i == 0 ? NLB : 0);
+      if (nx_b < ph.nb) ph.issue(nx_b, B);
+      ph.reduce(i + 1, acc, red);
+    }
+    if constexpr (NLB > 0) {
+      if (i == 0) {   // the LDS batches, then the stage area is free for this wave's K/V staging
+#pragma unroll
+        for (int bb = 0; bb < NLB; ++bb) {
+          ph.fma_lds(sm.stage, bb, wid, xa, acc);
+          ph.reduce(2 + bb, acc, red);
+        }
+      }
+    }
+    extra(it);
   };
-  if constexpr (GE::NBT > 4) {   // (long loops stay rolled: one copy of the body in the instruction cache)
+  if constexpr (NLB > 0) {
+    step(0, 0);
 #pragma nounroll
-    for (int i = 0; i < ph.nb; i += 2) step(i);
+    for (int i = 2 + NLB, it = 1; i < ph.nb; i += 2, ++it) step(i, it);
+  } else if constexpr (GE::NBT > 4) {   // (long loops stay rolled: one copy of the body in the instruction cache)
+#pragma nounroll
+    for (int i = 0; i < ph.nb; i += 2) step(i, i / 2);
   } else {
-    for (int i = 0; i < ph.nb; i += 2) step(i);
+    for (int i = 0; i < ph.nb; i += 2) step(i, i / 2);
   }
   if (st) st[2] = (unsigned long long)wall_clock64();
   __syncthreads();
@@ -498,6 +557,8 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
   if (wid != 0) {
     nx.issue(0, A);
     nx.issue(1, B);
+    if constexpr (PH == PH_O && Geo<SH, PH_GU>::NLB > 0)   // the gate/up LDS batches (loaded during attention) have
+      __builtin_amdgcn_s_waitcnt(kVmcntChunk<2 * Geo<SH, PH_GU>::NL>());   // landed: the block barrier publishes them
   } else {
     float scale = 1.f;
     if constexpr (GE::NORM) scale = norm_scale<GE::KS>(sm.ssq, GE::K, p.eps);
@@ -573,8 +634,8 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
 // The attention phase: block b sweeps split s = b % S of kv head g = b / S (positions [s TC, s TC + TC))
 // for the G query heads of the group, on the matrix cores (as attn_mfma_kernel); each split stores its partial and
 // raises its flag, and split 0's block of the kv head waits for all S flags and merges the splits in split order.
-template <class SH, class NX>
-__device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, u32x4 (&A)[kNL], u32x4 (&B)[kNL],
+template <class SH, class NX, class GU>
+__device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, const GU& gu, u32x4 (&A)[kNL], u32x4 (&B)[kNL],
                                          const Smem<SH>& sm, int layer, int pos, bool pos_ok, int wid, int lane,
                                          unsigned gen0) {
   constexpr int HD = SH::HD, G = SH::G, TC = SH::TC, S = SH::S, CPR = HD / 8, KSQ = HD / 32, DT = HD / 16;
@@ -728,11 +789,13 @@ __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, u32
 
   if (st) st[2] = (unsigned long long)wall_clock64();
   // ---- the 8 waves' states merged in wave order into this split's partial (outputs spread over all waves),
-  // then the split's flag
+  // then the split's flag. Partial of split s: head hh at [hh (HD + 4), + HD) the output, + HD the max (log2
+  // domain), + HD + 1 the weight sum (16-byte aligned rows).
+  constexpr int PS = HD + 4, PSTRIDE = G * PS;
   const unsigned gen = gen0 + (unsigned)(kFusedPhases * layer + 1) + 1u;
   unsigned* sflag = opaque_p(p.sync) + kSyncSplit + 32 * g;
   {
-    float* part = opaque_p(p.part) + ((size_t)g * S + s) * (G * (HD + 2));
+    float* part = opaque_p(p.part) + ((size_t)g * S + s) * PSTRIDE;
     for (int i = tid; i < G * (HD + 2); i += kFT) {
       const int hh = i / (HD + 2), dd = i % (HD + 2);
       float mm = wst[hh * (HD + 2) + HD];
@@ -747,53 +810,61 @@ __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, u32
         oo = oo * w1 + ws2[min(dd, HD - 1)] * w2;
         mm = M;
       }
-      st_dev(part + i, dd < HD ? oo : (dd == HD ? mm : ll));
+      st_dev(part + hh * PS + dd, dd < HD ? oo : (dd == HD ? mm : ll));
     }
     wait_all();
   }
   __syncthreads();
   if (st) st[3] = (unsigned long long)wall_clock64();
-  if (wid == 0 && lane == 0) st_dev(sflag + s, gen);
 
-  // ---- split 0 of each kv head merges all S splits in split order once every split's flag is up (lane k of
-  // wave 0 reads split k's): wave w takes head w / (HD / 64), elements 64 (w % (HD / 64)) + lane
-  if (s == 0) {
-    if (wid == 0 && !sm.flags[0])
+  if (wid != 0) {
+    // waves 1-7: the next phase's first weights, concurrent with wave 0's merge and barrier; then, once wave 0 has
+    // its merge inputs (bulk loads issued earlier would queue ahead of them), the gate/up batches that go through
+    // LDS (the K/V chunk is no longer needed)
+    nx.issue(0, A);
+    nx.issue(1, B);
+    if constexpr (Geo<SH, PH_GU>::NLB > 0) {
+      while (__hip_atomic_load(&sm.flags[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != (int)gen)
+        __builtin_amdgcn_s_sleep(2);
+      gu.lds_prefetch(sm.stage, wid);
+    }
+  } else {
+    // ---- wave 0 of every split merges OPB of the kv head's G HD outputs, [s OPB, s OPB + OPB), over all S
+    // splits once their flags are up: lane k < S takes split k's max, sum and OPB outputs, and the weighted sums
+    // over the lanes come out of one transposing reduction (split order fixed, so every run forms them alike)
+    constexpr int OPB = G * HD / S;
+    static_assert(S <= 64 && OPB % 4 == 0 && OPB <= 16 && HD % OPB == 0, "merge slices of whole 16-byte groups");
+    if (lane == 0) st_dev(sflag + s, gen);
+    if (!sm.flags[0])
       spin_until(p, sm.flags, [&]() __attribute__((always_inline)) {
         return __all(lane >= S || ld_dev(sflag + min(lane, S - 1)) == gen) != 0;
       });
     if (st) st[4] = (unsigned long long)wall_clock64();
-    __syncthreads();
-    constexpr int WPH = HD / 64;
-    const int hh = wid / WPH, d = (wid % WPH) * 64 + lane;
-    if (hh < G) {
-      constexpr int stride = G * (HD + 2);
-      const auto rp = make_rsrc(opaque_p(p.part) + (size_t)g * S * stride + hh * (HD + 2));
-      const int sl = min(lane, S - 1);
-      const float ms = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, (sl * stride + HD) * 4, 0, kSc1));
-      const float ls = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, (sl * stride + HD + 1) * 4, 0, kSc1));
-      float ov[S];
-      const int dv = opaque_v(d * 4);
+    const int o0 = s * OPB, hh = o0 / HD, d0 = o0 % HD;
+    const auto rp = make_rsrc(opaque_p(p.part) + (size_t)g * S * PSTRIDE + hh * PS);
+    const int sl = opaque_v(min(lane, S - 1) * PSTRIDE * 4);
+    const u32x4 ml = ld_dev16(rp, sl + HD * 4);   // (max, sum, -, -)
+    u32x4 ov[OPB / 4];
 #pragma unroll
-      for (int k = 0; k < S; ++k)
-        ov[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, dv, k * stride * 4, kSc1));
-      const float M = wave_max(lane < S ? ms : -INFINITY);
-      const float w = (lane < S && ms != -INFINITY) ? fast_exp2(ms - M) : 0.f;
-      const float Lt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum(w * (lane < S ? ls : 0.f))), 0));
-      float o = 0.f;
+    for (int q4 = 0; q4 < OPB / 4; ++q4) ov[q4] = ld_dev16(rp, sl + (d0 + 4 * q4) * 4);
+    const float ms = lane < S ? __uint_as_float(ml.x) : -INFINITY;
+    const float M = wave_max(ms);
+    const float w = ms != -INFINITY ? fast_exp2(ms - M) : 0.f;
+    const float Lt = wave_total(w * __uint_as_float(ml.y));
+    float a[OPB];
 #pragma unroll
-      for (int k = 0; k < S; ++k) o = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k)), ov[k], o);
-      st_dev(opaque_p(p.attn) + (g * G + hh) * HD + d, o / Lt);
+    for (int q4 = 0; q4 < OPB / 4; ++q4) {
+      a[4 * q4] = w * __uint_as_float(ov[q4].x);
+      a[4 * q4 + 1] = w * __uint_as_float(ov[q4].y);
+      a[4 * q4 + 2] = w * __uint_as_float(ov[q4].z);
+      a[4 * q4 + 3] = w * __uint_as_float(ov[q4].w);
     }
-    wait_all();
+    const float o = transpose_reduce<OPB>(a, lane);
+    constexpr int LOGO = OPB == 4 ? 2 : OPB == 8 ? 3 : 4;
+    if ((lane & ((64 >> LOGO) - 1)) == 0)
+      st_dev(opaque_p(p.attn) + (g * G + hh) * HD + d0 + (lane >> (6 - LOGO)), o / Lt);
     if (st) st[5] = (unsigned long long)wall_clock64();
-    __syncthreads();
-  }
-  // waves 1-7: the next phase's first weights, concurrent with wave 0's barrier
-  if (wid != 0) {
-    nx.issue(0, A);
-    nx.issue(1, B);
-  } else {
+    if (lane == 0) __hip_atomic_store(&sm.flags[1], (int)gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     arrive_and_wait(p, gen0, kFusedPhases * layer + 1, lane, sm.flags, [&]() __attribute__((always_inline)) {
       nx.issue(0, A);
       nx.issue(1, B);
@@ -803,8 +874,17 @@ __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, u32
   after_barrier(p, kFusedPhases * layer + 1);
 }
 
-template <class SH>
-__global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedParams p) {
+// TRACE: record block 0's clock after every barrier, every block's barrier arrival and release times, and (with
+// trace2 set) the sub-phase clocks. Without it no trace code is compiled in: its pointers would hold scalar
+// registers for the whole launch, and the kernel's code must stay small enough for the instruction cache.
+template <class SH, bool TRACE>
+__global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedParams p_in) {
+  FusedParams p = p_in;
+  if constexpr (!TRACE) {
+    p.clocks = nullptr;
+    p.trace = nullptr;
+    p.trace2 = nullptr;
+  }
   __shared__ __attribute__((aligned(16))) unsigned char s_stage[2 * SH::KB];
   __shared__ __attribute__((aligned(16))) float s_uni[SH::UNI];
   __shared__ float s_ssq[kFW];
@@ -867,7 +947,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedParams p) {
     ph_down.init(W(l, p.o_wd), 0, b, wid, lane);
 
     run_gemv<SH, PH_QKV>(p, qkv, NoNext{}, [](int) __attribute__((always_inline)) {}, A, B, sm, p.x, GN(l, p.o_attn_norm), xe, l, pos, pos_ok, wid, lane, gen0);
-    run_attn<SH>(p, ph_o, A, B, sm, l, pos, pos_ok, wid, lane, gen0);
+    run_attn<SH>(p, ph_o, ph_gu, A, B, sm, l, pos, pos_ok, wid, lane, gen0);
     run_gemv<SH, PH_O>(p, ph_o, ph_gu, [](int) __attribute__((always_inline)) {}, A, B, sm, p.attn, nullptr, xe, l, pos, pos_ok, wid, lane, gen0);
     if (l + 1 < L) {
       run_gemv<SH, PH_GU>(p, ph_gu, ph_down, [&](int it) __attribute__((always_inline)) { stage_layer(l + 1, b, wid, lane, it); }, A, B, sm, p.x, GN(l, p.o_ffn_norm),
@@ -894,14 +974,19 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedParams p) {
 }
 
 template <class SH>
-hipError_t fused_go(const FusedParams& p, hipStream_t s) {
-  fused_step_kernel<SH><<<kFusedBlocks, kFT, 0, s>>>(p);
+hipError_t fused_go(const FusedParams& p, bool trace, hipStream_t s) {
+  if (trace) fused_step_kernel<SH, true><<<kFusedBlocks, kFT, 0, s>>>(p);
+  else fused_step_kernel<SH, false><<<kFusedBlocks, kFT, 0, s>>>(p);
   return hipGetLastError();
 }
 
 template <class SH>
 hipError_t fused_occ(int* out) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, fused_step_kernel<SH>, kFT, 0);
+  int a = 0, b = 0;
+  hipError_t h = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, fused_step_kernel<SH, false>, kFT, 0);
+  if (h == hipSuccess) h = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, fused_step_kernel<SH, true>, kFT, 0);
+  *out = a < b ? a : b;
+  return h;
 }
 
 }  // namespace
@@ -924,16 +1009,16 @@ hipError_t fused_blocks_per_cu(int d, int ffn, int hd, int nq, int nkv, int spli
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fused(const FusedParams& p, int d, int ffn, int hd, int nq, int nkv, hipStream_t s) {
+hipError_t launch_fused(const FusedParams& p, int d, int ffn, int hd, int nq, int nkv, bool trace, hipStream_t s) {
   const int tc = p.split_len;   // one staged chunk per split
   if ((tc != 256 && tc != 128) || p.cap != tc * (kFusedBlocks / nkv)) return hipErrorInvalidValue;
   if (d == 4096 && ffn == 14336 && hd == 128 && nq == 32 && nkv == 8) {
-    return tc == 256 ? fused_go<Shape<4096, 14336, 128, 32, 8, 256>>(p, s)
-                     : fused_go<Shape<4096, 14336, 128, 32, 8, 128>>(p, s);
+    return tc == 256 ? fused_go<Shape<4096, 14336, 128, 32, 8, 256>>(p, trace, s)
+                     : fused_go<Shape<4096, 14336, 128, 32, 8, 128>>(p, trace, s);
   }
   if (d == 2048 && ffn == 8192 && hd == 64 && nq == 32 && nkv == 8) {
-    return tc == 256 ? fused_go<Shape<2048, 8192, 64, 32, 8, 256>>(p, s)
-                     : fused_go<Shape<2048, 8192, 64, 32, 8, 128>>(p, s);
+    return tc == 256 ? fused_go<Shape<2048, 8192, 64, 32, 8, 256>>(p, trace, s)
+                     : fused_go<Shape<2048, 8192, 64, 32, 8, 128>>(p, trace, s);
   }
   return hipErrorInvalidValue;
 }

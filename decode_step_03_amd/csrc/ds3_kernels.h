@@ -178,7 +178,7 @@ hipError_t launch_kv_copy(const KvView& kv, int kv_dtype, int layer, int row, in
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t s);
 // Fused step kernel (ds3_fused.hip). fused_shape_supported: the model shape has a compiled instantiation.
 bool fused_shape_supported(int d, int ffn, int hd, int nq, int nkv);
-hipError_t launch_fused(const FusedParams& p, int d, int ffn, int hd, int nq, int nkv, hipStream_t s);
+hipError_t launch_fused(const FusedParams& p, int d, int ffn, int hd, int nq, int nkv, bool trace, hipStream_t s);
 // Blocks of the fused kernel one compute unit holds at once (its LDS and registers decide).
 hipError_t fused_blocks_per_cu(int d, int ffn, int hd, int nq, int nkv, int split_len, int* out);
 

@@ -15,13 +15,14 @@ from . import _ds3 as C
 
 def make_config(*, n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, rms_eps, rope_theta, rows,
                 cap, kv_layout="contiguous", page_size=0, pool_pages=0, weight_dtype="bf16", kv_dtype="bf16",
-                exec_mode="graph", timeout_ms=0, kernel_plan="auto") -> C.ds3_config:
+                exec_mode="graph", timeout_ms=0, kernel_plan="auto", trace="off") -> C.ds3_config:
     dt = {"f32": C.DS3_F32, "bf16": C.DS3_BF16}
     return C.ds3_config(
         C.DS3_ABI_VERSION, n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, rms_eps, rope_theta,
         rows, cap, C.DS3_KV_PAGED if kv_layout == "paged" else C.DS3_KV_CONTIGUOUS, page_size, pool_pages,
         dt[weight_dtype], dt[kv_dtype], C.DS3_EAGER if exec_mode == "eager" else C.DS3_GRAPH, timeout_ms,
-        {"auto": C.DS3_PLAN_AUTO, "per_op": C.DS3_PLAN_PER_OP, "fused": C.DS3_PLAN_FUSED}[kernel_plan])
+        {"auto": C.DS3_PLAN_AUTO, "per_op": C.DS3_PLAN_PER_OP, "fused": C.DS3_PLAN_FUSED}[kernel_plan],
+        {"off": C.DS3_TRACE_OFF, "barriers": C.DS3_TRACE_BARRIERS, "phases": C.DS3_TRACE_PHASES}[trace])
 
 
 class Engine:
@@ -109,7 +110,8 @@ class Engine:
 
     def phase_trace(self, sub_phases: bool = False):
         """Fused plan: [barriers, blocks, 2] arrival / release clock ticks (100 MHz) of the last step; with
-        sub_phases also [barriers, blocks, 8] sub-phase ticks of wave 0 (needs DS3_FUSED_TRACE2=1)."""
+        sub_phases also [barriers, blocks, 8] sub-phase ticks (zero unless created with trace="phases"). Needs an
+        engine created with trace="barriers" or "phases"."""
         nb = 5 * self.cfg.n_layers
         n = nb * 256 * 2
         a = np.array(C.ds3_phase_trace(self.handle, 5 * n if sub_phases else n), dtype=np.uint64)

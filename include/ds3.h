@@ -30,7 +30,7 @@
 extern "C" {
 #endif
 
-#define DS3_ABI_VERSION 2u
+#define DS3_ABI_VERSION 3u
 
 typedef struct ds3_engine ds3_engine;
 
@@ -59,6 +59,10 @@ enum { DS3_GRAPH = 0, DS3_EAGER = 1 };               /* replay one captured grap
  * concurrently on the device that keeps compute units busy makes its grid barriers wait, and a wait past the
  * barrier limit (2 s) ends the step with DS3_E_KERNEL_CHECK, never a hang. */
 enum { DS3_PLAN_AUTO = 0, DS3_PLAN_PER_OP = 1, DS3_PLAN_FUSED = 2 };
+/* Fused-plan tracing. OFF: the step kernel carries no trace code (the production build). BARRIERS: every step
+ * records each block's grid-barrier arrival and release times; PHASES: also each block's sub-phase clocks. Both
+ * run a separately compiled, traced variant of the step kernel, a little slower than the untraced one. */
+enum { DS3_TRACE_OFF = 0, DS3_TRACE_BARRIERS = 1, DS3_TRACE_PHASES = 2 };
 
 /*
  * Model shape and step shape. Llama-style pre-norm decoder without biases: per layer RMSNorm, Q/K/V projection
@@ -81,6 +85,7 @@ typedef struct {
   int32_t weight_dtype, kv_dtype, exec_mode;
   uint32_t timeout_ms;
   int32_t kernel_plan;         /* DS3_PLAN_*; FUSED where it does not apply -> DS3_E_UNSUPPORTED */
+  int32_t trace;               /* DS3_TRACE_*: fused plan, what every step records for ds3_phase_trace */
 } ds3_config;
 
 /* Device buffers the caller allocates for ds3_create, in this id order. */
@@ -203,10 +208,10 @@ ds3_status ds3_profile_kernels(ds3_engine* e, int32_t iters, ds3_kernel_time* ou
 /* Fused plan only: the grid-barrier trace of the last step, uint64 [5 n_layers][256 blocks][2] = each block's
  * wall-clock time (100 MHz ticks) when it arrived at the barrier and when it was released; the barriers close the
  * QKV, attention, o-proj, gate/up and down phases of each layer in order. With room for five times as many words,
- * [5 n_layers][256][8] sub-phase clocks follow (zero unless the engine was created with DS3_FUSED_TRACE2=1 in the
- * environment): GEMV phases -- start, first batch consumed, batches done, block done; attention -- start, inputs
- * in, sweep done, partial stored, all splits flagged (merging block), merge stored. *n_inout: room in `out` on entry, words written on return. DS3_E_UNSUPPORTED with the
- * per-operation plan. */
+ * [5 n_layers][256][8] sub-phase clocks follow (zero unless the engine was created with trace =
+ * DS3_TRACE_PHASES): GEMV phases -- start, first batch consumed, batches done, block done; attention -- start, inputs
+ * in, sweep done, partial stored, all splits flagged, merge stored. *n_inout: room in `out` on entry, words
+ * written on return. DS3_E_UNSUPPORTED with the per-operation plan or an engine created with trace = OFF. */
 ds3_status ds3_phase_trace(ds3_engine* e, uint64_t* out, int32_t* n_inout);
 
 /* Test hook for the failure path: DS3_INJECT_KERNEL_CHECK makes the next step's first kernel raise its check

@@ -29,19 +29,22 @@ def logits_tol(w: synth.Workload) -> float:
     return TOL_F32 if w.model.weight_dtype == "f32" else TOL_BF16
 
 
-def engine_config(w: synth.Workload, exec_mode="graph", timeout_ms=0, rows=None, cap=None, kernel_plan="auto"):
+def engine_config(w: synth.Workload, exec_mode="graph", timeout_ms=0, rows=None, cap=None, kernel_plan="auto",
+                  trace="off"):
     from decode_step_03_amd import make_config
     m = w.model
     return make_config(n_layers=m.n_layers, d_model=m.d_model, n_q_heads=m.n_q_heads, n_kv_heads=m.n_kv_heads,
                        head_dim=m.head_dim, ffn_dim=m.ffn_dim, vocab=m.vocab, rms_eps=m.rms_eps,
                        rope_theta=m.rope_theta, rows=rows or w.rows, cap=cap or w.cap, kv_layout=w.kv_layout,
                        page_size=w.page_size, pool_pages=w.pool_pages, weight_dtype=m.weight_dtype,
-                       kv_dtype=w.kv_dtype, exec_mode=exec_mode, timeout_ms=timeout_ms, kernel_plan=kernel_plan)
+                       kv_dtype=w.kv_dtype, exec_mode=exec_mode, timeout_ms=timeout_ms, kernel_plan=kernel_plan,
+                       trace=trace)
 
 
-def make_engine(w: synth.Workload, ws: synth.WeightSet, exec_mode="graph", timeout_ms=0, kernel_plan="auto"):
+def make_engine(w: synth.Workload, ws: synth.WeightSet, exec_mode="graph", timeout_ms=0, kernel_plan="auto",
+                trace="off"):
     from decode_step_03_amd import Engine
-    eng = Engine(engine_config(w, exec_mode, timeout_ms, kernel_plan=kernel_plan))
+    eng = Engine(engine_config(w, exec_mode, timeout_ms, kernel_plan=kernel_plan, trace=trace))
     eng.load_weights(ws.layers, ws.glob)
     return eng
 

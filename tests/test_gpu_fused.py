@@ -141,3 +141,39 @@ def test_fused_profile_reports_phases_and_restores_state():
         ls.step(tok, np.array([501], np.int32))
     finally:
         eng.close()
+
+
+def test_fused_phase_trace_records_barriers_and_leaves_results_alone():
+    """A traced engine (the separately compiled, traced step kernel) gives the untraced engine's logits bit for
+    bit; its grid-barrier trace has, for every block and barrier, arrival <= release, releases in barrier order,
+    and every block released only after the last block arrived; its GEMV sub-phase clocks are in order. An
+    untraced engine refuses the trace."""
+    w, ws = _case(n_layers=2)
+    plain = make_engine(w, ws, kernel_plan="fused")
+    traced = make_engine(w, ws, kernel_plan="fused", trace="phases")
+    try:
+        for eng in (plain, traced):
+            ls = Lockstep(w, ws, eng)
+            ls.prefill_random_kv([700])
+        tok = np.array([5], np.int32)
+        for p in (700, 701):
+            a, _ = plain.step(tok, np.array([p], np.int32))
+            b, _ = traced.step(tok, np.array([p], np.int32))
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"traced logits differ at pos {p}"
+            tok = np.array([int(np.argmax(a[0]))], np.int32)
+        bar, sub = traced.phase_trace(sub_phases=True)
+        nb = 5 * w.model.n_layers
+        assert bar.shape == (nb, 256, 2) and sub.shape == (nb, 256, 8)
+        arr, rel = bar[..., 0].astype(np.int64), bar[..., 1].astype(np.int64)
+        assert (arr > 0).all() and (arr <= rel).all()
+        assert (np.diff(rel, axis=0) >= 0).all(), "releases out of barrier order"
+        assert (rel.min(axis=1) >= arr.max(axis=1)).all(), "a block was released before every block arrived"
+        for ph in (0, 2, 3, 4):   # GEMV phases: start, first batch consumed, batches done, block done
+            st = sub[ph::5, :, :4].astype(np.int64)
+            assert (st > 0).all() and (np.diff(st, axis=2) >= 0).all()
+        with pytest.raises(DS3Error) as ei:
+            plain.phase_trace()
+        assert ei.value.status == C.DS3_E_UNSUPPORTED
+    finally:
+        plain.close()
+        traced.close()
