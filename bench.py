@@ -184,6 +184,9 @@ def main() -> int:
     ap.add_argument("--eager-steps", type=int, default=16,
                     help="steps of the per-operation kernels, as a graph replay and launched one by one")
     ap.add_argument("--kernel-plan", default="auto", choices=["auto", "fused", "per_op"])
+    ap.add_argument("--chain", type=int, default=32,
+                    help="steps per host wait, each step's token picked on the device (0: every step returns its "
+                         "logits and the host picks)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -225,21 +228,43 @@ def main() -> int:
         log(f"steps limited to {args.steps} by the KV capacity")
     wall, gpu_us, submit_us = [], [], []
     torch.cuda.synchronize()
-    for i in range(total):
-        if i == args.warmup:
-            torch.cuda.synchronize()
-            t_start = time.perf_counter()
-        ts = time.perf_counter()
-        logits, flags = eng.step(tok, pos)
-        tok = logits.argmax(axis=1).astype(np.int32)
-        pos = pos + 1
-        if i >= args.warmup:
-            wall.append(time.perf_counter() - ts)
-            st = eng.stats()
-            gpu_us.append(st["last_gpu_us"])
-            submit_us.append(st["last_submit_us"])
-        if flags:
-            log(f"warning: non-finite logits at step {i}")
+    if args.chain > 0:
+        # chained greedy steps: the device picks each token; one host wait per `chain` steps
+        def run(n_total, timed):
+            nonlocal tok, pos
+            done = 0
+            while done < n_total:
+                n = min(args.chain, n_total - done)
+                ts = time.perf_counter()
+                ids, flags = eng.step_greedy(tok, pos, n)
+                tok, pos, done = ids[-1].copy(), pos + n, done + n
+                if timed:
+                    wall.append((time.perf_counter() - ts) / n)
+                    st = eng.stats()
+                    gpu_us.append(st["last_gpu_us"])
+                    submit_us.append(st["last_submit_us"] / n)
+                if flags.any():
+                    log(f"warning: non-finite logits in {int(flags.sum())} of {n} chained steps")
+        run(args.warmup, False)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        run(args.steps, True)
+    else:
+        for i in range(total):
+            if i == args.warmup:
+                torch.cuda.synchronize()
+                t_start = time.perf_counter()
+            ts = time.perf_counter()
+            logits, flags = eng.step(tok, pos)
+            tok = logits.argmax(axis=1).astype(np.int32)
+            pos = pos + 1
+            if i >= args.warmup:
+                wall.append(time.perf_counter() - ts)
+                st = eng.stats()
+                gpu_us.append(st["last_gpu_us"])
+                submit_us.append(st["last_submit_us"])
+            if flags:
+                log(f"warning: non-finite logits at step {i}")
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     stats = eng.stats()
@@ -320,6 +345,8 @@ def main() -> int:
                  "wall_ms_p10_p50_p90": [round(1e3 * float(np.percentile(wall, q)), 4) for q in (10, 50, 90)],
                  "kernel_plan": stats["kernel_plan"],
                  "kernels_per_step": stats["kernels_per_step"], "graph_replays_per_step": 1,
+                 "steps_per_host_wait": args.chain if args.chain > 0 else 1,
+                 "token_pick": "device (greedy, chained)" if args.chain > 0 else "host argmax of copied logits",
                  "host_submit_us_graph": round(float(np.median(submit_us)), 1),
                  "per_op_graph": per_op.get("graph", {}), "eager": per_op.get("eager", {}),
                  "attn_splits": stats["attn_splits"]},

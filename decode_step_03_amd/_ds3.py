@@ -11,7 +11,7 @@ from ctypes import POINTER, c_char, c_double, c_float, c_int32, c_int64, c_uint3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libds3.so")
 
-DS3_ABI_VERSION = 3
+DS3_ABI_VERSION = 4
 
 # ds3_status
 DS3_OK = 0
@@ -33,6 +33,7 @@ DS3_KV_CONTIGUOUS, DS3_KV_PAGED = 0, 1
 DS3_GRAPH, DS3_EAGER = 0, 1
 DS3_PLAN_AUTO, DS3_PLAN_PER_OP, DS3_PLAN_FUSED = 0, 1, 2
 DS3_TRACE_OFF, DS3_TRACE_BARRIERS, DS3_TRACE_PHASES = 0, 1, 2
+DS3_MAX_CHAIN = 1024
 DS3_BUF_WEIGHTS, DS3_BUF_KV, DS3_BUF_WORK, DS3_BUF_LOGITS, DS3_NUM_BUFFERS = 0, 1, 2, 3, 4
 DS3_INJECT_KERNEL_CHECK, DS3_INJECT_TIMEOUT_NEXT, DS3_INJECT_BARRIER_TIMEOUT = 1, 2, 3
 
@@ -76,6 +77,7 @@ SIGNATURES = [
     ("ds3_load_weights", c_int32, [c_void_p, POINTER(ds3_weight_src), c_int32]),
     ("ds3_set_slot_map", c_int32, [c_void_p, c_void_p]),
     ("ds3_step", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, POINTER(c_uint32)]),
+    ("ds3_step_greedy", c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
     ("ds3_reset_state", c_int32, [c_void_p]),
     ("ds3_write_kv", c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     ("ds3_read_kv", c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
@@ -153,6 +155,10 @@ def ds3_step(h: int, tokens_ptr: int, pos_ptr: int, write_map_ptr: int | None, l
     flags = c_uint32(0)
     _check(load_library().ds3_step(h, tokens_ptr, pos_ptr, write_map_ptr, logits_ptr, ctypes.byref(flags)), h)
     return flags.value
+
+
+def ds3_step_greedy(h: int, tokens_ptr: int, pos_ptr: int, n_steps: int, ids_ptr: int, flags_ptr: int | None) -> None:
+    _check(load_library().ds3_step_greedy(h, tokens_ptr, pos_ptr, n_steps, ids_ptr, flags_ptr), h)
 
 
 def ds3_reset_state(h: int) -> None:

@@ -30,16 +30,18 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 size_t dtype_bytes(int dt) { return dt == DS3_BF16 ? 2 : 4; }
 
 struct WorkPlan {
-  size_t slots, status, x, q, attn, act, part, kvnew, sync, clocks, trace, rope, slot_map, frag_hi, frag_lo, total;
+  size_t slots, status, x, q, attn, act, part, kvnew, sync, clocks, trace, pick_val, pick_idx, pick_done, ids, chain_flags,
+      rope, slot_map, frag_hi, frag_lo, total;
 };
 
 struct KernelKind {
   const char* name;
 };
-enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN, K_HEAD, K_SPLIT, K_COMBINE, K_FUSED, K_NUM };
+enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN, K_HEAD, K_SPLIT, K_COMBINE, K_FUSED, K_PICK, K_NUM };
 const char* kKindNames[K_NUM] = {"embed", "qkv_rope_kvwrite", "attention_splitk", "o_proj_residual",
                                  "gateup_swiglu", "down_proj_residual", "lm_head", "act_split_mfma",
-                                 "attention_combine", "decode_step_fused"};
+                                 "attention_combine", "decode_step_fused", "greedy_pick"};
+constexpr int kMaxChain = DS3_MAX_CHAIN;   // steps of one ds3_step_greedy call
 // fused plan: the operation kind of phase k of a layer (the grid barrier after it closes the phase)
 const int kPhaseKind[kFusedPhases] = {K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN};
 
@@ -75,6 +77,11 @@ struct ds3_engine {
   unsigned long long* clocks = nullptr;              // fused: block 0's clock per barrier
   unsigned long long* trace = nullptr;               // fused: every block's arrival and release per barrier
   bool profiling = false;                            // fused: profile_kernels' own launches record the clocks
+  float* pick_val = nullptr;                         // greedy pick: per-slice maxima [rows][kPickSplit]
+  int* pick_idx = nullptr;
+  unsigned* pick_done = nullptr;
+  int32_t* ids = nullptr;                            // [kMaxChain][rows] picks of a chain of steps
+  uint32_t* chain_flags = nullptr;                   // [kMaxChain] non-finite flag of each step
   size_t sync_words = 0;
   size_t weight_lstride = 0;                         // bytes between consecutive layers' weights
   size_t work_bytes = 0;
@@ -101,6 +108,7 @@ struct ds3_engine {
   // host state
   int32_t* h_slots = nullptr;   // pinned: slot words followed by the two status words (zeroed every step)
   StatusWords* h_status = nullptr;
+  int32_t* h_chain = nullptr;   // pinned: [kMaxChain][rows] picks, then [kMaxChain] flags, of the last call
   std::vector<int32_t> h_slot_map;
   bool slot_map_set = false;
   hipGraph_t graph = nullptr;
@@ -266,6 +274,11 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
   w.sync = take(fused_sync_words(c.n_layers, c.n_kv_heads) * 4);
   w.clocks = take(((size_t)kFusedPhases * c.n_layers + 2) * 8);
   w.trace = take((size_t)kFusedPhases * c.n_layers * kFusedBlocks * 10 * 8);   // barrier trace, then sub-phases
+  w.pick_val = take((size_t)c.rows * kPickSplit * 4);
+  w.pick_idx = take((size_t)c.rows * kPickSplit * 4);
+  w.pick_done = take(4);
+  w.ids = take((size_t)kMaxChain * c.rows * 4);
+  w.chain_flags = take((size_t)kMaxChain * 4);
   w.rope = take((size_t)c.cap * (c.head_dim / 2) * 2 * 4);
   w.slot_map = take(c.kv_layout == DS3_KV_PAGED ? (size_t)c.rows * (c.cap / c.page_size) * 4 : 4);
   const size_t kmax = (size_t)std::max(std::max(c.d_model, c.ffn_dim), c.n_q_heads * c.head_dim);
@@ -332,6 +345,7 @@ double kind_bytes(const ds3_config& c, int kind) {
     case K_GATEUP: return Lc * (2 * F * d * wb + d * wb);
     case K_DOWN: return Lc * d * F * wb;
     case K_HEAD: return (double)c.vocab * d * wb + d * wb;
+    case K_PICK: return R * (double)c.vocab * 4;   // the logits, read once
     case K_FUSED: {
       double t = 0;
       for (int k : {K_EMBED, K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN, K_HEAD}) t += kind_bytes(c, k);
@@ -455,6 +469,24 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
         default: sp.in = e->act; sp.K = c.ffn_dim; norm = false; break;
       }
       return launch_split(sp, norm, e->stream);
+    }
+    case K_PICK: {
+      PickParams p{};
+      p.logits = e->logits;
+      p.vocab = c.vocab;
+      p.rows = R;
+      p.slots = e->slots;
+      p.page_table = c.kv_layout == DS3_KV_PAGED ? e->slot_map : nullptr;
+      p.page_size = c.page_size;
+      p.cap = c.cap;
+      p.part_val = e->pick_val;
+      p.part_idx = e->pick_idx;
+      p.done = e->pick_done;
+      p.ids = e->ids;
+      p.flags = e->chain_flags;
+      p.max_chain = kMaxChain;
+      p.status = e->status;
+      return launch_pick(p, e->stream);
     }
     case K_EMBED: {
       EmbedParams p{e->embed, e->x, c.d_model, c.vocab, R, e->slots, e->status};
@@ -641,6 +673,11 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   e->sync = reinterpret_cast<unsigned*>(work + wp.sync);
   e->clocks = reinterpret_cast<unsigned long long*>(work + wp.clocks);
   e->trace = reinterpret_cast<unsigned long long*>(work + wp.trace);
+  e->pick_val = reinterpret_cast<float*>(work + wp.pick_val);
+  e->pick_idx = reinterpret_cast<int*>(work + wp.pick_idx);
+  e->pick_done = reinterpret_cast<unsigned*>(work + wp.pick_done);
+  e->ids = reinterpret_cast<int32_t*>(work + wp.ids);
+  e->chain_flags = reinterpret_cast<uint32_t*>(work + wp.chain_flags);
   e->sync_words = fused_sync_words(c.n_layers, c.n_kv_heads);
   e->frag_hi = reinterpret_cast<uint16_t*>(work + wp.frag_hi);
   e->frag_lo = reinterpret_cast<uint16_t*>(work + wp.frag_lo);
@@ -712,6 +749,7 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   }
   if (e->mfma) e->sequence.push_back({K_SPLIT, -1, S_FINAL_NORM});
   if (!e->fused) e->sequence.push_back({K_HEAD, -1, 0});
+  e->sequence.push_back({K_PICK, -1, 0});
 
   const SlotLayout sl{c.rows};
   h = hipHostMalloc(reinterpret_cast<void**>(&e->h_slots), (size_t)sl.words() * 4 + kAlign + sizeof(StatusWords),
@@ -719,6 +757,8 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("hipHostMalloc: ") + hipGetErrorString(h));
   std::memset(e->h_slots, 0, (size_t)sl.words() * 4);
   e->h_status = reinterpret_cast<StatusWords*>(reinterpret_cast<char*>(e->h_slots) + align_up((size_t)sl.words() * 4, 16));
+  h = hipHostMalloc(reinterpret_cast<void**>(&e->h_chain), (size_t)kMaxChain * (c.rows + 1) * 4, hipHostMallocDefault);
+  if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("hipHostMalloc: ") + hipGetErrorString(h));
   for (hipEvent_t* ev : {&e->ev0, &e->ev1, &e->ev_done}) {
     h = hipEventCreate(ev);
     if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("hipEventCreate: ") + hipGetErrorString(h));
@@ -877,25 +917,32 @@ ds3_status ds3_set_slot_map(ds3_engine* e, const int32_t* slot_map) {
   return DS3_OK;
 }
 
-ds3_status ds3_step(ds3_engine* e, const int32_t* tokens, const int32_t* pos, const int32_t* write_map,
-                    float* logits_host, uint32_t* flags) {
+// n_steps steps from the given slots: the first from the host's words, each later one from the slots the
+// previous step's greedy pick advanced on the device (token = the pick, pos + 1). One host wait for all of them.
+static ds3_status run_steps(ds3_engine* e, const int32_t* tokens, const int32_t* pos, const int32_t* write_map,
+                            int32_t n_steps, float* logits_host, int32_t* ids_out, uint32_t* flags_out) {
   const auto t_start = std::chrono::steady_clock::now();
   if (ds3_status st = refuse_if_unusable(e)) return st;
   if (e->state == ST_NOT_LOADED) return fail(e, DS3_E_NOT_LOADED, "weights are not loaded");
   if (e->state == ST_NEEDS_RESET) return fail(e, DS3_E_NEEDS_RESET, "a previous step failed; reset_state first");
   const ds3_config& c = e->cfg;
   if (!tokens || !pos) return fail(e, DS3_E_INVALID, "tokens or pos is NULL");
+  if (n_steps < 1 || n_steps > kMaxChain)
+    return fail(e, DS3_E_INVALID, "n_steps must be in 1.." + std::to_string(kMaxChain));
   const SlotLayout sl{c.rows};
   const bool paged = c.kv_layout == DS3_KV_PAGED;
   if (paged && !write_map && !e->slot_map_set) return fail(e, DS3_E_INVALID, "paged step needs a slot map");
+  if (paged && n_steps > 1 && !e->slot_map_set) return fail(e, DS3_E_INVALID, "chained paged steps need a slot map");
   for (int r = 0; r < c.rows; ++r) {
     if (tokens[r] < 0 || tokens[r] >= c.vocab) return fail(e, DS3_E_INVALID, "token out of range in row " + std::to_string(r));
     if (pos[r] < 0 || pos[r] >= c.cap) return fail(e, DS3_E_INVALID, "pos out of range in row " + std::to_string(r));
+    if ((int64_t)pos[r] + n_steps > c.cap)
+      return fail(e, DS3_E_INVALID, "pos + n_steps passes the capacity in row " + std::to_string(r));
     if (paged && write_map &&
         (write_map[r] < 0 || (int64_t)write_map[r] >= (int64_t)c.pool_pages * c.page_size))
       return fail(e, DS3_E_INVALID, "write_map out of range in row " + std::to_string(r));
   }
-  // slot words, then the status words (cleared every step by the same copy)
+  // slot words, then the status words (cleared every call by the same copy)
   for (int r = 0; r < c.rows; ++r) {
     e->h_slots[sl.token() + r] = tokens[r];
     e->h_slots[sl.pos() + r] = pos[r];
@@ -909,6 +956,7 @@ ds3_status ds3_step(ds3_engine* e, const int32_t* tokens, const int32_t* pos, co
   }
   e->h_slots[sl.inject()] = e->inject_check ? 1 : 0;
   e->h_slots[sl.spin()] = e->inject_barrier ? 1 : 0;   // fused kernel: 1 tick forces every barrier wait to time out
+  e->h_slots[sl.chain()] = 0;
   e->inject_check = false;
   e->inject_barrier = false;
   const uint32_t timeout = e->inject_timeout ? 0u : e->cfg.timeout_ms;
@@ -921,15 +969,20 @@ ds3_status ds3_step(ds3_engine* e, const int32_t* tokens, const int32_t* pos, co
   if (c.exec_mode == DS3_GRAPH) {
     if (ds3_status st = ensure_captured(e)) return st;
     HIP_OR_POISON(e, hipEventRecord(e->ev0, e->stream));
-    HIP_OR_POISON(e, hipGraphLaunch(e->exec, e->stream));
+    for (int i = 0; i < n_steps; ++i) HIP_OR_POISON(e, hipGraphLaunch(e->exec, e->stream));
     HIP_OR_POISON(e, hipEventRecord(e->ev1, e->stream));
-    e->stats.replays++;
+    e->stats.replays += n_steps;
   } else {
     HIP_OR_POISON(e, hipEventRecord(e->ev0, e->stream));
-    HIP_OR_POISON(e, enqueue_step(e));
+    for (int i = 0; i < n_steps; ++i) HIP_OR_POISON(e, enqueue_step(e));
     HIP_OR_POISON(e, hipEventRecord(e->ev1, e->stream));
   }
   HIP_OR_POISON(e, hipMemcpyAsync(e->h_status, e->status, sizeof(StatusWords), hipMemcpyDeviceToHost, e->stream));
+  int32_t* h_ids = e->h_chain;
+  uint32_t* h_flags = reinterpret_cast<uint32_t*>(e->h_chain + (size_t)kMaxChain * c.rows);
+  if (ids_out)
+    HIP_OR_POISON(e, hipMemcpyAsync(h_ids, e->ids, (size_t)n_steps * c.rows * 4, hipMemcpyDeviceToHost, e->stream));
+  HIP_OR_POISON(e, hipMemcpyAsync(h_flags, e->chain_flags, (size_t)n_steps * 4, hipMemcpyDeviceToHost, e->stream));
   if (logits_host)
     HIP_OR_POISON(e, hipMemcpyAsync(logits_host, e->logits, (size_t)c.rows * c.vocab * 4, hipMemcpyDeviceToHost,
                                     e->stream));
@@ -940,10 +993,11 @@ ds3_status ds3_step(ds3_engine* e, const int32_t* tokens, const int32_t* pos, co
   if (ds3_status st = wait_done(e, e->ev_done, timeout)) return st;
   float gpu_ms = 0.f;
   HIP_OR_POISON(e, hipEventElapsedTime(&gpu_ms, e->ev0, e->ev1));
-  e->stats.last_gpu_us = gpu_ms * 1e3;
+  e->stats.last_gpu_us = gpu_ms * 1e3 / n_steps;
   e->stats.kernels_per_step = c.exec_mode == DS3_GRAPH ? e->graph_nodes : (int)e->sequence.size();
   const uint32_t errbits = e->h_status->err;
-  if (flags) *flags = e->h_status->nonfinite ? 1u : 0u;
+  if (ids_out) std::memcpy(ids_out, h_ids, (size_t)n_steps * c.rows * 4);
+  if (flags_out) std::memcpy(flags_out, h_flags, (size_t)n_steps * 4);
   e->stats.last_host_us =
       std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t_start).count();
   if (errbits) {
@@ -955,8 +1009,19 @@ ds3_status ds3_step(ds3_engine* e, const int32_t* tokens, const int32_t* pos, co
       return std::string(b);
     }());
   }
-  e->stats.steps++;
+  e->stats.steps += n_steps;
   return DS3_OK;
+}
+
+ds3_status ds3_step(ds3_engine* e, const int32_t* tokens, const int32_t* pos, const int32_t* write_map,
+                    float* logits_host, uint32_t* flags) {
+  return run_steps(e, tokens, pos, write_map, 1, logits_host, nullptr, flags);
+}
+
+ds3_status ds3_step_greedy(ds3_engine* e, const int32_t* tokens, const int32_t* pos, int32_t n_steps,
+                           int32_t* ids, uint32_t* flags) {
+  if (!ids) return fail(e, DS3_E_INVALID, "ids is NULL");
+  return run_steps(e, tokens, pos, nullptr, n_steps, nullptr, ids, flags);
 }
 
 ds3_status ds3_reset_state(ds3_engine* e) {
@@ -964,6 +1029,7 @@ ds3_status ds3_reset_state(ds3_engine* e) {
   HIP_OR_POISON(e, hipMemsetAsync(e->buf[DS3_BUF_KV], 0, e->kv_bytes, e->stream));
   HIP_OR_POISON(e, launch_fill_u32(reinterpret_cast<uint32_t*>(e->status), 0u, 2, e->stream));
   HIP_OR_POISON(e, launch_fill_u32(e->sync, 0u, e->sync_words, e->stream));
+  HIP_OR_POISON(e, launch_fill_u32(e->pick_done, 0u, 1, e->stream));
   HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
   e->pending = true;
   if (ds3_status st = wait_done(e, e->ev_done, e->cfg.timeout_ms)) return st;
@@ -1108,6 +1174,8 @@ ds3_status ds3_profile_kernels(ds3_engine* e, int32_t iters, ds3_kernel_time* ou
     const int L = e->cfg.n_layers, nc = kFusedPhases * L + 2;
     std::vector<unsigned long long> clk((size_t)nc);
     for (int it = 0; it < iters; ++it) {
+      HIP_OR_POISON(e, hipMemcpyAsync(e->slots, e->h_slots, (size_t)SlotLayout{e->cfg.rows}.words() * 4,
+                                      hipMemcpyHostToDevice, e->stream));   // (each step's pick advanced them)
       e->profiling = true;
       const hipError_t hp = enqueue_step(e);
       e->profiling = false;
@@ -1123,14 +1191,18 @@ ds3_status ds3_profile_kernels(ds3_engine* e, int32_t iters, ds3_kernel_time* ou
     for (int k : kPhaseKind) phases[k] = L;
     phases[K_HEAD] = 1;
   }
+  // the greedy pick's replays advanced the device slots: the closing step runs from the last call's words again
+  HIP_OR_POISON(e, hipMemcpyAsync(e->slots, e->h_slots, (size_t)SlotLayout{e->cfg.rows}.words() * 4,
+                                  hipMemcpyHostToDevice, e->stream));
   HIP_OR_POISON(e, enqueue_step(e));
   HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
   e->pending = true;
   if (ds3_status st = wait_done(e, e->ev_done, e->cfg.timeout_ms)) return st;
   for (int k = 0; k < K_NUM; ++k) {
     std::snprintf(out[k].name, sizeof(out[k].name), "%s", kKindNames[k]);
-    out[k].launches = e->fused && k != K_FUSED ? phases[k] : cnt[k];
-    out[k].total_us = e->fused && k != K_FUSED ? phase_us[k] : tot[k];
+    const bool phase = e->fused && k != K_FUSED && k != K_PICK;   // fused: a phase of the step kernel
+    out[k].launches = phase ? phases[k] : cnt[k];
+    out[k].total_us = phase ? phase_us[k] : tot[k];
     out[k].bytes = kind_bytes(e->cfg, k);
   }
   *n_inout = K_NUM;
@@ -1180,6 +1252,7 @@ void ds3_destroy(ds3_engine* e) {
   for (hipEvent_t ev : {e->ev0, e->ev1, e->ev_done})
     if (ev) (void)hipEventDestroy(ev);
   if (e->h_slots) (void)hipHostFree(e->h_slots);
+  if (e->h_chain) (void)hipHostFree(e->h_chain);
   if (e->kv_staging) (void)hipFree(e->kv_staging);
   if (e->own_stream && e->stream) (void)hipStreamDestroy(e->stream);
   delete e;

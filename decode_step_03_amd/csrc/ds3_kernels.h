@@ -25,7 +25,8 @@ struct SlotLayout {
   __host__ __device__ int write_map() const { return 2 * rows; }
   __host__ __device__ int inject() const { return 3 * rows; }
   __host__ __device__ int spin() const { return 3 * rows + 1; }   // fused kernel: barrier wait limit, 0 = default
-  __host__ __device__ int words() const { return 3 * rows + 2; }
+  __host__ __device__ int chain() const { return 3 * rows + 2; }  // greedy pick: steps since the host wrote slots
+  __host__ __device__ int words() const { return 3 * rows + 3; }
 };
 
 // Status words written by kernels and read back after every step.
@@ -88,6 +89,29 @@ struct AttnParams {
   int split_len;         // positions per split (multiple of the positions one block pass covers)
   float scale;           // 1/sqrt(hd)
   const int* slots;
+  StatusWords* status;
+};
+
+// Greedy pick after the LM head ("Execution" page, section "A constant-shape decode graph": the step's output
+// token is chosen on the device, so a run of steps needs no host round trip). Each row's logits are split over
+// kPickSplit blocks; every block writes the (value, index) of its slice's largest logit (first index on ties;
+// NaN never wins); the last block to finish (device-scope counter) combines the slices of every row and writes
+// the picks into the token slots, pos + 1 into the position slots (and the K/V write slot of pos + 1 from the
+// page table, paged layout), the picks into ids[step % max_chain] and the step's non-finite flag into
+// flags[step % max_chain] (then clears it for the next step), and advances the step counter.
+constexpr int kPickSplit = 16;
+struct PickParams {
+  const float* logits;     // [rows][vocab]
+  int vocab, rows;
+  int32_t* slots;          // SlotLayout{rows}
+  const int* page_table;   // paged: [rows][cap / page_size]; else null
+  int page_size, cap;
+  float* part_val;         // [rows][kPickSplit]
+  int* part_idx;           // [rows][kPickSplit]
+  unsigned* done;          // finished-block counter (back to 0 after every launch)
+  int32_t* ids;            // [max_chain][rows]
+  uint32_t* flags;         // [max_chain]
+  int max_chain;
   StatusWords* status;
 };
 
@@ -176,6 +200,7 @@ hipError_t launch_attention_combine(const AttnParams& p, int rows, hipStream_t s
 hipError_t launch_kv_copy(const KvView& kv, int kv_dtype, int layer, int row, int pos0, int n, int nkv, int hd,
                           void* staging, int to_state, StatusWords* status, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t s);
+hipError_t launch_pick(const PickParams& p, hipStream_t s);
 // Fused step kernel (ds3_fused.hip). fused_shape_supported: the model shape has a compiled instantiation.
 bool fused_shape_supported(int d, int ffn, int hd, int nq, int nkv);
 hipError_t launch_fused(const FusedParams& p, int d, int ffn, int hd, int nq, int nkv, bool trace, hipStream_t s);

@@ -1105,6 +1105,80 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t value, size_t n) {
 }
 
 // ----------------------------------------------------------------------------------------------------------
+// greedy pick
+
+// (value, index) order of the pick: larger value first, then lower index; NaN is never larger
+__device__ __forceinline__ bool pick_better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+
+constexpr int kPickThreads = 256;
+
+__global__ void __launch_bounds__(kPickThreads) pick_kernel(PickParams p) {
+  __shared__ float s_v[kPickThreads / 64];
+  __shared__ int s_i[kPickThreads / 64];
+  __shared__ int s_last;
+  const int r = blockIdx.x / kPickSplit, part = blockIdx.x % kPickSplit;
+  const int chunk = (p.vocab + kPickSplit - 1) / kPickSplit;
+  const int lo = part * chunk, hi = min(p.vocab, lo + chunk);
+  const float* lg = p.logits + (size_t)r * p.vocab;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = lo + (int)threadIdx.x; i < hi; i += kPickThreads) {
+    const float v = lg[i];
+    if (pick_better(v, i, bv, bi)) { bv = v; bi = i; }
+  }
+  // wave, then block: the order-independent (value, index) maximum
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float ov = __shfl_xor(bv, m, 64);
+    const int oi = __shfl_xor(bi, m, 64);
+    if (pick_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane == 0) { s_v[wv] = bv; s_i[wv] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kPickThreads / 64; ++w)
+      if (pick_better(s_v[w], s_i[w], bv, bi)) { bv = s_v[w]; bi = s_i[w]; }
+    __hip_atomic_store(&p.part_val[blockIdx.x], bv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&p.part_idx[blockIdx.x], bi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // release this block's slice result; the last block to arrive acquires everyone's
+    const unsigned prev = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  const SlotLayout sl{p.rows};
+  if (threadIdx.x < p.rows) {
+    const int rr = threadIdx.x;
+    float v = -INFINITY;
+    int idx = 0x7fffffff;
+    for (int k = 0; k < kPickSplit; ++k) {
+      const float ov = __hip_atomic_load(&p.part_val[rr * kPickSplit + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int oi = __hip_atomic_load(&p.part_idx[rr * kPickSplit + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (pick_better(ov, oi, v, idx)) { v = ov; idx = oi; }
+    }
+    if (idx >= p.vocab) idx = 0;   // every logit NaN
+    const int step = p.slots[sl.chain()];
+    p.ids[(size_t)(step % p.max_chain) * p.rows + rr] = idx;
+    const int np = p.slots[sl.pos() + rr] + 1;
+    p.slots[sl.token() + rr] = idx;
+    p.slots[sl.pos() + rr] = np;
+    if (p.page_table && np >= 0 && np < p.cap) {
+      const int ppr = p.cap / p.page_size;
+      p.slots[sl.write_map() + rr] = p.page_table[(size_t)rr * ppr + np / p.page_size] * p.page_size + np % p.page_size;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int step = p.slots[sl.chain()];
+    p.flags[step % p.max_chain] = p.status->nonfinite ? 1u : 0u;
+    p.status->nonfinite = 0;
+    p.slots[sl.chain()] = step + 1;
+    __hip_atomic_store(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ----------------------------------------------------------------------------------------------------------
 // host launchers
 
 size_t gemv_lds_bytes(int rows, int K, bool norm) { (void)norm; return (size_t)rows * K * sizeof(float); }
@@ -1314,6 +1388,12 @@ hipError_t launch_kv_copy(const KvView& kv, int kv_dtype, int layer, int row, in
   else
     kv_copy_kernel<float><<<blocks, kBlock, 0, s>>>(kv, layer, row, pos0, n, nkv, hd,
                                                     reinterpret_cast<float*>(staging), to_state, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_pick(const PickParams& p, hipStream_t s) {
+  if (p.rows < 1 || p.rows > kPickThreads || p.vocab < 1 || p.max_chain < 1) return hipErrorInvalidValue;
+  pick_kernel<<<p.rows * kPickSplit, kPickThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 

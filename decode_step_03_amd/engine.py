@@ -83,6 +83,17 @@ class Engine:
         flags = C.ds3_step(self.handle, self._tok.ctypes.data, self._pos.ctypes.data, wm, out)
         return (self._logits_host.numpy() if copy_logits else None), flags
 
+    def step_greedy(self, tokens, pos, n_steps: int):
+        """n_steps chained steps with the greedy pick on the device and one host wait. Returns (ids int32
+        [n_steps, rows], flags uint32 [n_steps]); step 0 takes `tokens` at `pos`, step i the previous pick at pos + i."""
+        self._tok[:] = tokens
+        self._pos[:] = pos
+        ids = np.empty((n_steps, self.cfg.rows), np.int32)
+        flags = np.empty(n_steps, np.uint32)
+        C.ds3_step_greedy(self.handle, self._tok.ctypes.data, self._pos.ctypes.data, n_steps, ids.ctypes.data,
+                          flags.ctypes.data)
+        return ids, flags
+
     def reset_state(self) -> None:
         C.ds3_reset_state(self.handle)
 

@@ -30,7 +30,7 @@
 extern "C" {
 #endif
 
-#define DS3_ABI_VERSION 3u
+#define DS3_ABI_VERSION 4u
 
 typedef struct ds3_engine ds3_engine;
 
@@ -183,6 +183,23 @@ ds3_status ds3_set_slot_map(ds3_engine* e, const int32_t* slot_map);
  * flags (may be NULL) receives bit 0 = some logit is NaN or infinite (not an error by itself). */
 ds3_status ds3_step(ds3_engine* e, const int32_t* tokens, const int32_t* pos, const int32_t* write_map,
                     float* logits_host, uint32_t* flags);
+
+/* Every step ends with the greedy pick on the device: for each row the index of its largest logit (the first
+ * such index on ties; a NaN logit is never picked; all NaN -> 0) is written into the row's token slot and
+ * pos + 1 into its position slot (paged: and the K/V write slot of pos + 1, from the page table), so the next
+ * step can run without the host ("Execution" page, section "A constant-shape decode graph": the token a step
+ * emits feeds the next step; "Slot buffers": a replay reads its inputs from device slots).
+ *
+ * ds3_step_greedy runs n_steps (1..DS3_MAX_CHAIN) such steps back to back with ONE host wait: the first from
+ * tokens[r] at pos[r], each later one from the previous step's pick at the next position; pos[r] + n_steps must
+ * not pass cap, and the paged layout needs the page table (ds3_set_slot_map) to cover those positions. ids
+ * (host, int32 [n_steps][rows]) receives the picks, step by step; flags (host, uint32 [n_steps], may be NULL)
+ * receives each step's non-finite bit (bit 0: some logit of that step is NaN or infinite). The logits of the last
+ * step stay in the DS3_BUF_LOGITS buffer. Errors as for ds3_step; after an in-kernel check failure the whole run's
+ * results are void (DS3_E_KERNEL_CHECK). */
+#define DS3_MAX_CHAIN 1024
+ds3_status ds3_step_greedy(ds3_engine* e, const int32_t* tokens, const int32_t* pos, int32_t n_steps,
+                           int32_t* ids, uint32_t* flags);
 
 /* Zero every row's K/V state and the step's scratch state; clears NEEDS_RESET. Keeps weights and the graph. */
 ds3_status ds3_reset_state(ds3_engine* e);
