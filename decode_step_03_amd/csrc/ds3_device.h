@@ -86,6 +86,9 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// (value, index) order of the greedy pick: larger value first, then lower index; NaN is never larger
+__device__ __forceinline__ bool pick_better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+
 // 2^x with the hardware exp (results below the normal range flush to zero, which a softmax weight can afford)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -444,6 +444,9 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.trace2 = c.trace >= DS3_TRACE_PHASES ? e->trace + (size_t)kFusedPhases * c.n_layers * kFusedBlocks * 2 : nullptr;
       p.slots = e->slots;
       p.status = e->status;
+      p.ids = e->ids;
+      p.chain_flags = e->chain_flags;
+      p.max_chain = kMaxChain;
       p.n_layers = c.n_layers;
       p.vocab = c.vocab;
       p.cap = c.cap;
@@ -749,7 +752,7 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   }
   if (e->mfma) e->sequence.push_back({K_SPLIT, -1, S_FINAL_NORM});
   if (!e->fused) e->sequence.push_back({K_HEAD, -1, 0});
-  e->sequence.push_back({K_PICK, -1, 0});
+  if (!e->fused) e->sequence.push_back({K_PICK, -1, 0});   // (the fused kernel picks in its own last phase)
 
   const SlotLayout sl{c.rows};
   h = hipHostMalloc(reinterpret_cast<void**>(&e->h_slots), (size_t)sl.words() * 4 + kAlign + sizeof(StatusWords),

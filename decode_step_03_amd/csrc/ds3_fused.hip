@@ -429,6 +429,58 @@ __device__ __forceinline__ void arrive_and_wait(const FusedParams& p, unsigned g
   if (!early) prefetch();
 }
 
+// Greedy candidate of the wave: the (value, index) maximum over its lanes, in every lane.
+__device__ __forceinline__ void pick_reduce(float& bv, int& bi) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float ov = __shfl_xor(bv, m, 64);
+    const int oi = __shfl_xor(bi, m, 64);
+    if (pick_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+}
+
+// After the head, wave 0 of every block (its candidate stored): arrive at the closing barrier (generation
+// gen0 + 5 L + 1); block 0 waits for every block, picks the step's token from the 256 candidates (the first index
+// of the largest logit; all NaN -> 0), writes it into the token slot and pos + 1 into the position slot for the
+// next launch (every block read the slots at its start), records the pick and the non-finite flag under the
+// chain counter, clears the flag and advances the counter. The other blocks just leave.
+__device__ __forceinline__ void final_pick(const FusedParams& p, unsigned gen0, int lane, int* flags) {
+  wait_all();
+  const unsigned gen = gen0 + (unsigned)(kFusedPhases * p.n_layers) + 1u;
+  if (flags[0]) return;
+  if (lane == 0) st_dev(&p.sync[kSyncArrive + blockIdx.x], gen);
+  if (blockIdx.x != 0) return;
+  const auto ra = make_rsrc(p.sync + kSyncArrive);
+  const bool ok = spin_until(p, flags, [&]() __attribute__((always_inline)) {
+    const u32x4 v = ld_dev16(ra, lane * 16);
+    return __all(v.x == gen && v.y == gen && v.z == gen && v.w == gen) != 0;
+  });
+  if (!ok) return;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  const float* pv = p.part;
+  const unsigned* pi = reinterpret_cast<const unsigned*>(p.part) + kFusedBlocks;
+#pragma unroll
+  for (int k = 0; k < kFusedBlocks / 64; ++k) {
+    const int blk = lane * (kFusedBlocks / 64) + k;
+    const float v = ld_dev(pv + blk);
+    const int i = (int)ld_dev(pi + blk);
+    if (pick_better(v, i, bv, bi)) { bv = v; bi = i; }
+  }
+  pick_reduce(bv, bi);
+  if (lane == 0) {
+    if (bi >= p.vocab) bi = 0;
+    const SlotLayout sl{1};
+    const int step = p.slots[sl.chain()];
+    p.ids[step % p.max_chain] = bi;
+    p.chain_flags[step % p.max_chain] = ld_dev(&p.status->nonfinite) ? 1u : 0u;
+    st_dev(&p.status->nonfinite, 0u);
+    p.slots[sl.token()] = bi;
+    p.slots[sl.pos()] = p.slots[sl.pos()] + 1;
+    p.slots[sl.chain()] = step + 1;
+  }
+}
+
 // After the block-wide barrier that follows arrive_and_wait: block 0 stamps the clock.
 __device__ __forceinline__ void after_barrier(const FusedParams& p, int bar) {
   if (blockIdx.x == 0 && threadIdx.x == 0 && p.clocks) p.clocks[bar + 1] = (unsigned long long)wall_clock64();
@@ -608,14 +660,23 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
       }
     } else if constexpr (PH == PH_O || PH == PH_DOWN) {
       if (lane < ph.nunits) st_dev(xb + ph.u0 + lane, eo_a + total(lane));
-    } else {   // PH_HEAD
+    } else {   // PH_HEAD: the logits, the non-finite flag, and this block's greedy candidate
       bool bad = false;
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
       for (int u = lane; u < ph.nunits; u += 64) {
         const float v = total(u) * scale;
         opaque_p(p.logits)[ph.u0 + u] = v;
         bad |= !isfinite(v);
+        if (pick_better(v, ph.u0 + u, bv, bi)) { bv = v; bi = ph.u0 + u; }
       }
       if (bad) atomicOr(&p.status->nonfinite, 1u);
+      pick_reduce(bv, bi);
+      if (lane == 0) {
+        st_dev(opaque_p(p.part) + blockIdx.x, bv);
+        st_dev(reinterpret_cast<unsigned*>(opaque_p(p.part)) + kFusedBlocks + blockIdx.x, (unsigned)bi);
+      }
+      final_pick(p, gen0, lane, sm.flags);
     }
     if constexpr (PH != PH_HEAD) {
       arrive_and_wait(p, gen0, kFusedPhases * layer + (PH == PH_QKV ? 0 : PH == PH_O ? 2 : PH == PH_GU ? 3 : 4), lane,

@@ -175,8 +175,11 @@ struct FusedParams {
   unsigned long long* clocks;  // [5 L + 2] block 0's clock at the start, after every barrier, at the end
   unsigned long long* trace;   // [5 L][kFusedBlocks][2] every block's arrival and release time per barrier
   unsigned long long* trace2;  // optional [5 L][kFusedBlocks][4] GEMV sub-phase clocks of wave 0 (null: off)
-  const int* slots;
+  int* slots;                  // read at the start; the greedy pick advances token and pos at the end
   StatusWords* status;
+  int32_t* ids;                // greedy pick: [max_chain][1] picks and [max_chain] non-finite flags of a chain
+  uint32_t* chain_flags;
+  int max_chain;
   int n_layers, vocab, cap;
   int split_len;               // positions per split
   float eps, scale;            // RMSNorm eps, 1/sqrt(hd)

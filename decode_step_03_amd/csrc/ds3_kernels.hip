@@ -1107,9 +1107,6 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t value, size_t n) {
 // ----------------------------------------------------------------------------------------------------------
 // greedy pick
 
-// (value, index) order of the pick: larger value first, then lower index; NaN is never larger
-__device__ __forceinline__ bool pick_better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
-
 constexpr int kPickThreads = 256;
 
 __global__ void __launch_bounds__(kPickThreads) pick_kernel(PickParams p) {
