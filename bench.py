@@ -189,6 +189,8 @@ def main() -> int:
                          "logits and the host picks)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--visible-steps", type=int, default=64,
+                    help="also time this many steps with the visible K/V sweep (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of known size (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -284,6 +286,29 @@ def main() -> int:
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": round(traffic) if traffic is not None else None, "kernel": dom["name"],
                 "bytes_per_launch": per_launch_bytes, "us_per_launch": round(per_launch_us, 3)}
+
+    # beyond the method: the visible K/V sweep (chunks wholly after pos not loaded; outputs bit-identical), timed
+    # on the same engine and capture from where the timed steps ended; fewer bytes than the formula's count
+    visible = None
+    n_vis = min(64, w.cap - int(pos.max()))
+    if args.visible_steps > 0 and n_vis >= 8:
+        n_vis = min(n_vis, args.visible_steps)
+        eng.set_kv_sweep("visible")
+        torch.cuda.synchronize()
+        tv = time.perf_counter()
+        gv = []
+        done = 0
+        while done < n_vis:
+            n = min(32, n_vis - done)
+            ids, _ = eng.step_greedy(tok, pos, n)
+            tok, pos, done = ids[-1].copy(), pos + n, done + n
+            gv.append(eng.stats()["last_gpu_us"])
+        torch.cuda.synchronize()
+        ev = time.perf_counter() - tv
+        eng.set_kv_sweep("full")
+        visible = {"tok_s": round(w.rows * n_vis / ev, 2), "gpu_ms": round(float(np.median(gv)) / 1e3, 4),
+                   "steps": n_vis, "note": "K/V chunks wholly after pos skipped; not the method's full sweep"}
+        log(f"visible sweep: {visible['tok_s']} tok/s, GPU {visible['gpu_ms']} ms/step")
     eng.close()
     del eng
     torch.cuda.empty_cache()
@@ -349,7 +374,7 @@ def main() -> int:
                  "token_pick": "device (greedy, chained)" if args.chain > 0 else "host argmax of copied logits",
                  "host_submit_us_graph": round(float(np.median(submit_us)), 1),
                  "per_op_graph": per_op.get("graph", {}), "eager": per_op.get("eager", {}),
-                 "attn_splits": stats["attn_splits"]},
+                 "attn_splits": stats["attn_splits"], "visible_sweep": visible},
         "kernels": [{"name": k["name"], "launches": k["launches"], "us_per_step": round(k["us_per_step"], 2),
                      "gbs": round(k["bytes_per_step"] / k["us_per_step"] / 1e3, 1) if k["us_per_step"] else None}
                     for k in kernels],

@@ -34,6 +34,7 @@ DS3_GRAPH, DS3_EAGER = 0, 1
 DS3_PLAN_AUTO, DS3_PLAN_PER_OP, DS3_PLAN_FUSED = 0, 1, 2
 DS3_TRACE_OFF, DS3_TRACE_BARRIERS, DS3_TRACE_PHASES = 0, 1, 2
 DS3_MAX_CHAIN = 1024
+DS3_SWEEP_FULL, DS3_SWEEP_VISIBLE = 0, 1
 DS3_BUF_WEIGHTS, DS3_BUF_KV, DS3_BUF_WORK, DS3_BUF_LOGITS, DS3_NUM_BUFFERS = 0, 1, 2, 3, 4
 DS3_INJECT_KERNEL_CHECK, DS3_INJECT_TIMEOUT_NEXT, DS3_INJECT_BARRIER_TIMEOUT = 1, 2, 3
 
@@ -78,6 +79,7 @@ SIGNATURES = [
     ("ds3_set_slot_map", c_int32, [c_void_p, c_void_p]),
     ("ds3_step", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, POINTER(c_uint32)]),
     ("ds3_step_greedy", c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
+    ("ds3_set_kv_sweep", c_int32, [c_void_p, c_int32]),
     ("ds3_reset_state", c_int32, [c_void_p]),
     ("ds3_write_kv", c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     ("ds3_read_kv", c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
@@ -159,6 +161,10 @@ def ds3_step(h: int, tokens_ptr: int, pos_ptr: int, write_map_ptr: int | None, l
 
 def ds3_step_greedy(h: int, tokens_ptr: int, pos_ptr: int, n_steps: int, ids_ptr: int, flags_ptr: int | None) -> None:
     _check(load_library().ds3_step_greedy(h, tokens_ptr, pos_ptr, n_steps, ids_ptr, flags_ptr), h)
+
+
+def ds3_set_kv_sweep(h: int, mode: int) -> None:
+    _check(load_library().ds3_set_kv_sweep(h, mode), h)
 
 
 def ds3_reset_state(h: int) -> None:

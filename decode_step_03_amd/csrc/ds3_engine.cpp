@@ -77,6 +77,7 @@ struct ds3_engine {
   unsigned long long* clocks = nullptr;              // fused: block 0's clock per barrier
   unsigned long long* trace = nullptr;               // fused: every block's arrival and release per barrier
   bool profiling = false;                            // fused: profile_kernels' own launches record the clocks
+  int32_t kv_sweep = DS3_SWEEP_FULL;                 // written into the sweep slot word every step
   float* pick_val = nullptr;                         // greedy pick: per-slice maxima [rows][kPickSplit]
   int* pick_idx = nullptr;
   unsigned* pick_done = nullptr;
@@ -960,6 +961,7 @@ static ds3_status run_steps(ds3_engine* e, const int32_t* tokens, const int32_t*
   e->h_slots[sl.inject()] = e->inject_check ? 1 : 0;
   e->h_slots[sl.spin()] = e->inject_barrier ? 1 : 0;   // fused kernel: 1 tick forces every barrier wait to time out
   e->h_slots[sl.chain()] = 0;
+  e->h_slots[sl.sweep()] = e->kv_sweep;
   e->inject_check = false;
   e->inject_barrier = false;
   const uint32_t timeout = e->inject_timeout ? 0u : e->cfg.timeout_ms;
@@ -1025,6 +1027,14 @@ ds3_status ds3_step_greedy(ds3_engine* e, const int32_t* tokens, const int32_t* 
                            int32_t* ids, uint32_t* flags) {
   if (!ids) return fail(e, DS3_E_INVALID, "ids is NULL");
   return run_steps(e, tokens, pos, nullptr, n_steps, nullptr, ids, flags);
+}
+
+ds3_status ds3_set_kv_sweep(ds3_engine* e, int32_t mode) {
+  if (ds3_status st = refuse_if_unusable(e)) return st;
+  if (mode != DS3_SWEEP_FULL && mode != DS3_SWEEP_VISIBLE)
+    return fail(e, DS3_E_INVALID, "mode must be DS3_SWEEP_FULL or DS3_SWEEP_VISIBLE");
+  e->kv_sweep = mode;
+  return DS3_OK;
 }
 
 ds3_status ds3_reset_state(ds3_engine* e) {

@@ -979,10 +979,12 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedParams p_in) {
   auto GN = [&](int l, size_t off) __attribute__((always_inline)) { return reinterpret_cast<const float*>(W(l, off)); };
   // stage layer l's K/V chunk; `it` >= 0: only the part for gate/up loop iteration `it` (2 instructions per wave
   // each), so the staging does not arrive as one burst that stalls the waves' own loads
+  // (visible-sweep slot set: a split whose positions all lie after pos stages nothing and computes nothing)
+  const bool live = p.slots[sl.sweep()] == 0 || (b0 % SH::S) * SH::TC <= pos;
   auto stage_layer = [&](int l, int b, int wid, int lane, int it) __attribute__((always_inline)) {
     constexpr int NIW = SH::KB / 1024 / kFW;
     const int i0 = it < 0 ? 0 : 2 * it, i1 = it < 0 ? NIW : 2 * it + 2;
-    if (i0 < NIW) stage_chunk<SH>(p, l, b / SH::S, (b % SH::S) * SH::TC, sm.stage, wid, lane, i0, i1);
+    if (i0 < NIW && live) stage_chunk<SH>(p, l, b / SH::S, (b % SH::S) * SH::TC, sm.stage, wid, lane, i0, i1);
   };
 
   u32x4 A[kNL], B[kNL];

@@ -26,7 +26,8 @@ struct SlotLayout {
   __host__ __device__ int inject() const { return 3 * rows; }
   __host__ __device__ int spin() const { return 3 * rows + 1; }   // fused kernel: barrier wait limit, 0 = default
   __host__ __device__ int chain() const { return 3 * rows + 2; }  // greedy pick: steps since the host wrote slots
-  __host__ __device__ int words() const { return 3 * rows + 3; }
+  __host__ __device__ int sweep() const { return 3 * rows + 3; }  // 1: K/V chunks wholly after pos are not loaded
+  __host__ __device__ int words() const { return 3 * rows + 4; }
 };
 
 // Status words written by kernels and read back after every step.

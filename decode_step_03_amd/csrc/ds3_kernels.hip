@@ -675,6 +675,9 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
     if (tid == 0) raise_error(p.status, ERR_POS);
     pos = 0;
   }
+  // visible-sweep slot set: chunks wholly after pos (a suffix of this split's chunks) are not loaded
+  const bool vis_only = p.slots[sl.sweep()] != 0;
+  auto live = [&](int c0) { return !vis_only || chunk_base(c0) <= pos; };
   const KT* Kb = reinterpret_cast<const KT*>(p.kv.k) + (size_t)p.layer * p.kv.layer_stride;
   const KT* Vb = reinterpret_cast<const KT*>(p.kv.v) + (size_t)p.layer * p.kv.layer_stride;
   const float scale2 = p.scale * 1.4426950408889634f;   // 1/sqrt(hd) * log2(e)
@@ -733,8 +736,8 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
     }
   };
   // Both buffers are filled up front; afterwards a buffer is refilled as soon as its chunk has been consumed.
-  stage(0, 0);
-  if (TC < T) stage(TC, 1);
+  if (live(0)) stage(0, 0);
+  if (TC < T && live(TC)) stage(TC, 1);
 
   float m[G], l[G], o[G][EPL];
 #pragma unroll
@@ -745,9 +748,9 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
     for (int e = 0; e < EPL; ++e) o[hh][e] = 0.f;
   }
 
-  for (int c0 = 0, buf = 0; c0 < T; c0 += TC, buf = (buf + 1) % NBUF) {
+  for (int c0 = 0, buf = 0; c0 < T && live(c0); c0 += TC, buf = (buf + 1) % NBUF) {
     // wait for this chunk's rows only: a later chunk's rows (NI/4 K and NI/4 V loads per wave) may still fly
-    if (c0 + TC < T) __builtin_amdgcn_s_waitcnt(kVmcntChunk<NI / (kBlock / 64) * 2>());
+    if (c0 + TC < T && live(c0 + TC)) __builtin_amdgcn_s_waitcnt(kVmcntChunk<NI / (kBlock / 64) * 2>());
     else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const KT* ks = reinterpret_cast<const KT*>(smem + (size_t)buf * 2 * TC * PB);
@@ -805,7 +808,7 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
     }
     }
     __syncthreads();   // the buffer is refilled next
-    if (c0 + NBUF * TC < T) stage(c0 + NBUF * TC, buf);
+    if (c0 + NBUF * TC < T && live(c0 + NBUF * TC)) stage(c0 + NBUF * TC, buf);
   }
 
   // ---- merge the lane groups of the wave (butterfly over the lanes holding the same head elements)
@@ -890,6 +893,10 @@ __global__ void __launch_bounds__(kBlock) attn_mfma_kernel(AttnParams p) {
     if (tid == 0) raise_error(p.status, ERR_POS);
     pos = 0;
   }
+  // the method sweeps every chunk; with the visible-sweep slot set, chunks wholly after pos (a suffix of this
+  // split's chunks) are neither loaded nor computed
+  const bool vis_only = p.slots[sl.sweep()] != 0;
+  auto live = [&](int c0) { return !vis_only || chunk_base(c0) <= pos; };
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(p.kv.k) + (size_t)p.layer * p.kv.layer_stride;
   const uint16_t* Vb = reinterpret_cast<const uint16_t*>(p.kv.v) + (size_t)p.layer * p.kv.layer_stride;
   const float scale2 = p.scale * 1.4426950408889634f;   // 1/sqrt(hd) * log2(e): scores in the log2 domain
@@ -955,8 +962,8 @@ __global__ void __launch_bounds__(kBlock) attn_mfma_kernel(AttnParams p) {
       __builtin_amdgcn_global_load_lds((global_cptr)(Vb + voff), (lds_ptr)(vdst + (size_t)k * 1024), 16, 0, 0);
     }
   };
-  stage(0, 0);
-  if (TC < T) stage(TC, 1);
+  if (live(0)) stage(0, 0);
+  if (TC < T && live(TC)) stage(TC, 1);
 
   // ---- q^T as B operand: lane (n, L) holds q[head n][32 ks + 8 L + e] * scale2, e = 0..7 (zero for n >= G)
   bf16x8 qh[KS], ql[KS];
@@ -976,8 +983,8 @@ __global__ void __launch_bounds__(kBlock) attn_mfma_kernel(AttnParams p) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int c0 = 0, buf = 0; c0 < T; c0 += TC, buf ^= 1) {
-    if (c0 + TC < T) __builtin_amdgcn_s_waitcnt(kVmcntChunk<2 * NIW>());
+  for (int c0 = 0, buf = 0; c0 < T && live(c0); c0 += TC, buf ^= 1) {
+    if (c0 + TC < T && live(c0 + TC)) __builtin_amdgcn_s_waitcnt(kVmcntChunk<2 * NIW>());
     else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int jw = chunk_base(c0) + 32 * wid;   // first position of this wave's block
@@ -1053,7 +1060,7 @@ __global__ void __launch_bounds__(kBlock) attn_mfma_kernel(AttnParams p) {
       }
     }
     __syncthreads();   // the buffer is refilled next
-    if (c0 + 2 * TC < T) stage(c0 + 2 * TC, buf);
+    if (c0 + 2 * TC < T && live(c0 + 2 * TC)) stage(c0 + 2 * TC, buf);
   }
 
   // ---- this wave's state into LDS: the 4 lane groups of a head share its max; their weight sums add

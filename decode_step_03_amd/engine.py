@@ -94,6 +94,11 @@ class Engine:
                           flags.ctypes.data)
         return ids, flags
 
+    def set_kv_sweep(self, mode: str) -> None:
+        """"full" (the method: every position of [cap] is loaded) or "visible" (chunks wholly after pos are skipped;
+        outputs bit-identical)."""
+        C.ds3_set_kv_sweep(self.handle, {"full": C.DS3_SWEEP_FULL, "visible": C.DS3_SWEEP_VISIBLE}[mode])
+
     def reset_state(self) -> None:
         C.ds3_reset_state(self.handle)
 

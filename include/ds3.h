@@ -201,6 +201,16 @@ ds3_status ds3_step(ds3_engine* e, const int32_t* tokens, const int32_t* pos, co
 ds3_status ds3_step_greedy(ds3_engine* e, const int32_t* tokens, const int32_t* pos, int32_t n_steps,
                            int32_t* ids, uint32_t* flags);
 
+/* K/V sweep of the attention, from the next step on (a slot word: no recapture). FULL (the default) loads every
+ * position of [cap], as the method does ("Execution" page, section "A constant-shape decode graph": the sweep
+ * covers the whole preallocated capacity and the mask hides what lies after pos). VISIBLE skips loading (and
+ * computing) the K/V chunks whose positions all lie after pos: the grid and every address stay the same, so the
+ * captured graph still serves every position, and the outputs are bit-identical to FULL (a hidden position
+ * contributes nothing either way). It goes beyond the pages and moves fewer bytes than the method's count.
+ * DS3_E_INVALID for any other mode. */
+enum { DS3_SWEEP_FULL = 0, DS3_SWEEP_VISIBLE = 1 };
+ds3_status ds3_set_kv_sweep(ds3_engine* e, int32_t mode);
+
 /* Zero every row's K/V state and the step's scratch state; clears NEEDS_RESET. Keeps weights and the graph. */
 ds3_status ds3_reset_state(ds3_engine* e);
 

@@ -1,0 +1,67 @@
+"""The visible K/V sweep (ds3_set_kv_sweep VISIBLE): chunks wholly after pos are neither loaded nor computed. A
+hidden position contributes nothing under the mask, so every output must be bit-identical to the full sweep of
+the method, on every attention kernel: the vector one (fp32 K/V), the matrix-core one (bf16, contiguous and
+paged) and the fused step kernel. Switching is a slot word: one capture serves both modes.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import bench
+import synth
+from decode_step_03_amd import DS3Error, _ds3 as C
+from tests.ds3_testlib import log, make_engine
+
+pytestmark = pytest.mark.gpu
+
+
+def _workload(name):
+    if name == "tiny-fp32":
+        return synth.workload("tiny-fp32")
+    if name == "8b-fused":
+        base = synth.workload("llama8b-bf16-cap8192")
+        return replace(synth.small_variant(base, n_layers=2, vocab=4096), name="llama8b-2l-sweep")
+    if name == "8b-r8":
+        base = synth.workload("llama8b-bf16-r8-cap32768")
+        return replace(synth.small_variant(base, n_layers=1, vocab=4096, cap=8192), name="llama8b-r8-sweep")
+    if name == "8b-r16-paged":
+        base = synth.workload("llama8b-bf16-r16-paged")
+        return replace(synth.small_variant(base, n_layers=1, vocab=4096), name="llama8b-r16-paged-sweep")
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name", ["tiny-fp32", "8b-fused", "8b-r8", "8b-r16-paged"])
+def test_visible_sweep_is_bit_identical(name):
+    w = _workload(name)
+    ws = synth.make_weights(w.model)
+    full = make_engine(w, ws)
+    vis = make_engine(w, ws)
+    try:
+        sp = np.minimum(synth.start_positions(w), w.cap - 8).astype(np.int32)
+        tok = synth.start_tokens(w)
+        for e in (full, vis):
+            bench.prefill(e, w, sp)
+        vis.set_kv_sweep("visible")
+        t = tok.copy()
+        for i in range(3):
+            a, fa = full.step(t, sp + i)
+            b, fb = vis.step(t, sp + i)
+            assert fa == fb == 0
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"step {i}: logits differ"
+            t = a.argmax(axis=1).astype(np.int32)
+        ia, _ = full.step_greedy(t, sp + 3, 4)
+        ib, _ = vis.step_greedy(t, sp + 3, 4)
+        assert np.array_equal(ia, ib)
+        vis.set_kv_sweep("full")   # and back, on the same capture
+        a, _ = full.step(ia[-1], sp + 7)
+        b, _ = vis.step(ib[-1], sp + 7)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+        assert vis.stats()["captures"] == 1
+        log(name, "plan", full.stats()["kernel_plan"], "positions", sp.tolist()[:4])
+        with pytest.raises(DS3Error) as ei:
+            C.ds3_set_kv_sweep(vis.handle, 7)
+        assert ei.value.status == C.DS3_E_INVALID
+    finally:
+        full.close()
+        vis.close()
