@@ -53,14 +53,15 @@ def algorithmic_bytes(w) -> float:
             + L * R * 2 * m.n_kv_heads * hd * kvb)
 
 
-def engine_for(w, ws, exec_mode, kernel_plan="auto", trace="off"):
+def engine_for(w, ws, exec_mode, kernel_plan="auto", trace="off", prefill_rows=None):
     from decode_step_03_amd import Engine, make_config
     m = w.model
     cfg = make_config(n_layers=m.n_layers, d_model=m.d_model, n_q_heads=m.n_q_heads, n_kv_heads=m.n_kv_heads,
                       head_dim=m.head_dim, ffn_dim=m.ffn_dim, vocab=m.vocab, rms_eps=m.rms_eps,
                       rope_theta=m.rope_theta, rows=w.rows, cap=w.cap, kv_layout=w.kv_layout,
                       page_size=w.page_size, pool_pages=w.pool_pages, weight_dtype=m.weight_dtype,
-                      kv_dtype=w.kv_dtype, exec_mode=exec_mode, kernel_plan=kernel_plan, trace=trace)
+                      kv_dtype=w.kv_dtype, exec_mode=exec_mode, kernel_plan=kernel_plan, trace=trace,
+                      prefill_rows=(16 if w.start == "prefill_tokens" else 0) if prefill_rows is None else prefill_rows)
     eng = Engine(cfg, "cuda:0")
     eng.load_weights(ws.layers, ws.glob)
     return eng
@@ -76,6 +77,15 @@ def prefill(eng, w, start_pos):
         eng.set_slot_map(synth.page_table(w))
     if w.start == "prefill_tokens":
         toks = synth.prefill_tokens(w)
+        if eng.cfg.prefill_rows > 0:   # the prompt in chunks of prefill_rows tokens per launch sequence
+            t0 = time.perf_counter()
+            for r in range(w.rows):
+                eng.prefill(r, toks[r], 0)
+            dt = time.perf_counter() - t0
+            prefill.last = {"tokens": int(w.rows * w.prefill_len), "chunk": int(eng.cfg.prefill_rows),
+                            "ms": round(1e3 * dt, 3), "tok_s": round(w.rows * w.prefill_len / dt, 1),
+                            "gpu_ms": round(eng.stats()["last_prefill_gpu_us"] / 1e3, 3)}
+            return
         for p in range(w.prefill_len):
             eng.step(toks[:, p], np.full(w.rows, p, np.int32), copy_logits=False)
         return
@@ -91,6 +101,9 @@ def prefill(eng, w, start_pos):
             eng.write_kv(li, r, 0, k, v)
             if (i + 1) % 64 == 0:
                 log(f"K/V prefill {i + 1}/{len(jobs)} (layer, row) pairs, {time.time() - t0:.0f}s")
+
+
+prefill.last = None
 
 
 def cpu_baseline(w, ws, start_pos, start_tok, budget_s: float) -> dict:
@@ -374,7 +387,7 @@ def main() -> int:
                  "token_pick": "device (greedy, chained)" if args.chain > 0 else "host argmax of copied logits",
                  "host_submit_us_graph": round(float(np.median(submit_us)), 1),
                  "per_op_graph": per_op.get("graph", {}), "eager": per_op.get("eager", {}),
-                 "attn_splits": stats["attn_splits"], "visible_sweep": visible},
+                 "attn_splits": stats["attn_splits"], "visible_sweep": visible, "prompt_prefill": prefill.last},
         "kernels": [{"name": k["name"], "launches": k["launches"], "us_per_step": round(k["us_per_step"], 2),
                      "gbs": round(k["bytes_per_step"] / k["us_per_step"] / 1e3, 1) if k["us_per_step"] else None}
                     for k in kernels],

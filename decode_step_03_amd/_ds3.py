@@ -11,7 +11,7 @@ from ctypes import POINTER, c_char, c_double, c_float, c_int32, c_int64, c_uint3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libds3.so")
 
-DS3_ABI_VERSION = 4
+DS3_ABI_VERSION = 5
 
 # ds3_status
 DS3_OK = 0
@@ -35,6 +35,7 @@ DS3_PLAN_AUTO, DS3_PLAN_PER_OP, DS3_PLAN_FUSED = 0, 1, 2
 DS3_TRACE_OFF, DS3_TRACE_BARRIERS, DS3_TRACE_PHASES = 0, 1, 2
 DS3_MAX_CHAIN = 1024
 DS3_SWEEP_FULL, DS3_SWEEP_VISIBLE = 0, 1
+DS3_MAX_PREFILL = 8192
 DS3_BUF_WEIGHTS, DS3_BUF_KV, DS3_BUF_WORK, DS3_BUF_LOGITS, DS3_NUM_BUFFERS = 0, 1, 2, 3, 4
 DS3_INJECT_KERNEL_CHECK, DS3_INJECT_TIMEOUT_NEXT, DS3_INJECT_BARRIER_TIMEOUT = 1, 2, 3
 
@@ -48,7 +49,7 @@ class ds3_config(ctypes.Structure):
                 ("rms_eps", c_float), ("rope_theta", c_double), ("rows", c_int32), ("cap", c_int32),
                 ("kv_layout", c_int32), ("page_size", c_int32), ("pool_pages", c_int32), ("weight_dtype", c_int32),
                 ("kv_dtype", c_int32), ("exec_mode", c_int32), ("timeout_ms", c_uint32), ("kernel_plan", c_int32),
-                ("trace", c_int32)]
+                ("trace", c_int32), ("prefill_rows", c_int32)]
 
 
 class ds3_buffer_req(ctypes.Structure):
@@ -64,7 +65,7 @@ class ds3_stats(ctypes.Structure):
     _fields_ = [("steps", c_uint64), ("replays", c_uint64), ("captures", c_uint64), ("kernels_per_step", c_int32),
                 ("state", c_int32), ("last_host_us", c_double), ("last_gpu_us", c_double),
                 ("attn_splits", c_int32), ("kernel_plan", c_int32),
-                ("last_submit_us", c_double)]
+                ("last_submit_us", c_double), ("prefill_tokens", c_uint64), ("last_prefill_gpu_us", c_double)]
 
 
 class ds3_kernel_time(ctypes.Structure):
@@ -80,6 +81,7 @@ SIGNATURES = [
     ("ds3_step", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, POINTER(c_uint32)]),
     ("ds3_step_greedy", c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
     ("ds3_set_kv_sweep", c_int32, [c_void_p, c_int32]),
+    ("ds3_prefill", c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, POINTER(c_uint32)]),
     ("ds3_reset_state", c_int32, [c_void_p]),
     ("ds3_write_kv", c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     ("ds3_read_kv", c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
@@ -161,6 +163,12 @@ def ds3_step(h: int, tokens_ptr: int, pos_ptr: int, write_map_ptr: int | None, l
 
 def ds3_step_greedy(h: int, tokens_ptr: int, pos_ptr: int, n_steps: int, ids_ptr: int, flags_ptr: int | None) -> None:
     _check(load_library().ds3_step_greedy(h, tokens_ptr, pos_ptr, n_steps, ids_ptr, flags_ptr), h)
+
+
+def ds3_prefill(h: int, row: int, tokens_ptr: int, pos0: int, n: int, logits_ptr: int | None) -> int:
+    flags = c_uint32(0)
+    _check(load_library().ds3_prefill(h, row, tokens_ptr, pos0, n, logits_ptr, ctypes.byref(flags)), h)
+    return flags.value
 
 
 def ds3_set_kv_sweep(h: int, mode: int) -> None:

@@ -103,12 +103,16 @@ __device__ __forceinline__ float wave_total(float v) {
 
 __device__ __forceinline__ void raise_error(StatusWords* st, uint32_t bit) { atomicOr(&st->err, bit); }
 
-// Location of logical position j of row r: the position itself (contiguous) or its pool slot page * ps + offset
-// (paged, through the row's page table; an id outside the pool raises the error word and reads page 0).
+// K/V row of activation row r
+__device__ __forceinline__ int kv_row(const KvView& kv, int r) { return kv.row_map ? kv.row_map[r] : r; }
+
+// Location of logical position j of activation row r: the position itself (contiguous) or its pool slot
+// page * ps + offset (paged, through its K/V row's page table; an id outside the pool raises the error word and
+// reads page 0).
 __device__ __forceinline__ int kv_loc(const KvView& kv, int r, int j, StatusWords* st) {
   if (!kv.paged) return j;
   const int ppr = kv.cap / kv.page_size;
-  int page = kv.slot_map[r * ppr + j / kv.page_size];
+  int page = kv.slot_map[kv_row(kv, r) * ppr + j / kv.page_size];
   if (page < 0 || page >= kv.pool_pages) {
     raise_error(st, ERR_PAGE);
     page = 0;
@@ -116,11 +120,12 @@ __device__ __forceinline__ int kv_loc(const KvView& kv, int r, int j, StatusWord
   return page * kv.page_size + j % kv.page_size;
 }
 
-// Element offset, within one layer's K or V state, of element e of (row r, kv head g) at location loc (kv_loc).
+// Element offset, within one layer's K or V state, of element e of (activation row r, kv head g) at location loc
+// (kv_loc).
 __device__ __forceinline__ size_t kv_at(const KvView& kv, bool is_v, int r, int nkv, int g, int hd, int loc, int e) {
   const bool t = is_v && kv.v_t;
   if (!kv.paged) {
-    const size_t head = (size_t)(r * nkv + g);
+    const size_t head = (size_t)(kv_row(kv, r) * nkv + g);
     return t ? (head * hd + e) * kv.cap + loc : (head * kv.cap + loc) * hd + e;
   }
   const int ps = kv.page_size;

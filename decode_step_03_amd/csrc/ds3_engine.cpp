@@ -30,8 +30,8 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 size_t dtype_bytes(int dt) { return dt == DS3_BF16 ? 2 : 4; }
 
 struct WorkPlan {
-  size_t slots, status, x, q, attn, act, part, kvnew, sync, clocks, trace, pick_val, pick_idx, pick_done, ids, chain_flags,
-      rope, slot_map, frag_hi, frag_lo, total;
+  size_t slots, status, x, q, attn, act, part, pre_slots, pre_logits, kvnew, sync, clocks, trace, pick_val, pick_idx,
+      pick_done, ids, chain_flags, rope, slot_map, frag_hi, frag_lo, total;
 };
 
 struct KernelKind {
@@ -42,6 +42,7 @@ const char* kKindNames[K_NUM] = {"embed", "qkv_rope_kvwrite", "attention_splitk"
                                  "gateup_swiglu", "down_proj_residual", "lm_head", "act_split_mfma",
                                  "attention_combine", "decode_step_fused", "greedy_pick"};
 constexpr int kMaxChain = DS3_MAX_CHAIN;   // steps of one ds3_step_greedy call
+constexpr int kMaxPrefill = DS3_MAX_PREFILL;   // tokens of one ds3_prefill call
 // fused plan: the operation kind of phase k of a layer (the grid barrier after it closes the phase)
 const int kPhaseKind[kFusedPhases] = {K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN};
 
@@ -127,6 +128,22 @@ struct ds3_engine {
   void* kv_staging = nullptr;
   size_t kv_staging_bytes = 0;
   std::vector<Launch> sequence;
+
+  // what enqueue_kernel launches for: the decode step (cfg.rows rows) or the prefill step (prefill_rows tokens
+  // of one K/V row); both share the work buffers, weights and K/V
+  struct RunCtx {
+    int rows = 0;
+    int* slots = nullptr;
+    float* logits = nullptr;
+    bool mfma = false;            // projections on the matrix cores (more than 4 rows)
+    const int* row_map = nullptr; // K/V row of each activation row (null: the row itself)
+  };
+  RunCtx dec, pre, cur;
+  std::vector<Launch> pre_sequence;
+  hipGraph_t pre_graph = nullptr;
+  hipGraphExec_t pre_exec = nullptr;
+  bool pre_captured = false;
+  int32_t* h_pre = nullptr;   // pinned: the slot words of every chunk of one ds3_prefill call
 };
 
 namespace {
@@ -219,15 +236,20 @@ std::string check_config(const ds3_config* c) {
     const std::string why = fused_refusal(*c);
     if (!why.empty()) return "kernel_plan: the fused step kernel does not apply (" + why + ")";
   }
-  if (c->rows <= kMaxGemvRows) {
-    const int kres = std::max(c->ffn_dim, c->n_q_heads * c->head_dim);
-    if (gemv_lds_bytes(c->rows, c->d_model, true) > 160 * 1024 || gemv_lds_bytes(c->rows, kres, false) > 160 * 1024)
-      return "rows: activations of rows x max(d_model, ffn_dim, q width) floats exceed the 160 KB LDS";
-  } else {
-    // matrix-core path: bf16 weights in whole 16-row tiles and 32-input steps
-    if (c->weight_dtype != DS3_BF16) return "weight_dtype: more than 4 rows needs bf16 weights (matrix-core path)";
-    if (c->d_model % 32 || c->ffn_dim % 32 || c->head_dim % 32 || c->vocab % 32)
-      return "d_model, ffn_dim, head_dim and vocab must be multiples of 32 for more than 4 rows";
+  if (c->prefill_rows < 0 || c->prefill_rows > kMaxRows) return "prefill_rows must be in 0..16";
+  for (const int R : {c->rows, c->prefill_rows}) {
+    if (R == 0) continue;
+    const char* what = R == c->rows ? "rows" : "prefill_rows";
+    if (R <= kMaxGemvRows) {
+      const int kres = std::max(c->ffn_dim, c->n_q_heads * c->head_dim);
+      if (gemv_lds_bytes(R, c->d_model, true) > 160 * 1024 || gemv_lds_bytes(R, kres, false) > 160 * 1024)
+        return std::string(what) + ": activations of rows x max(d_model, ffn_dim, q width) floats exceed the 160 KB LDS";
+    } else {
+      // matrix-core path: bf16 weights in whole 16-row tiles and 32-input steps
+      if (c->weight_dtype != DS3_BF16) return std::string(what) + ": more than 4 rows needs bf16 weights (matrix-core path)";
+      if (c->d_model % 32 || c->ffn_dim % 32 || c->head_dim % 32 || c->vocab % 32)
+        return "d_model, ffn_dim, head_dim and vocab must be multiples of 32 for more than 4 rows";
+    }
   }
   return "";
 }
@@ -263,14 +285,16 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
   };
   const SlotLayout sl{c.rows};
   const int G = c.n_q_heads / c.n_kv_heads;
+  const size_t RA = (size_t)std::max(c.rows, c.prefill_rows);   // activation rows of the larger step
   w.slots = take((size_t)sl.words() * 4);
   w.status = take(sizeof(StatusWords));
-  w.x = take((size_t)c.rows * c.d_model * 4);
-  w.q = take((size_t)c.rows * c.n_q_heads * c.head_dim * 4);
-  w.attn = take((size_t)c.rows * c.n_q_heads * c.head_dim * 4);
-  w.act = take((size_t)c.rows * c.ffn_dim * 4);
-  w.part = take((size_t)c.rows * c.n_kv_heads * std::max(splits, kFusedBlocks / c.n_kv_heads) * G *
-                (c.head_dim + 4) * 4);
+  w.x = take(RA * c.d_model * 4);
+  w.q = take(RA * c.n_q_heads * c.head_dim * 4);
+  w.attn = take(RA * c.n_q_heads * c.head_dim * 4);
+  w.act = take(RA * c.ffn_dim * 4);
+  w.part = take(RA * c.n_kv_heads * std::max(splits, kFusedBlocks / c.n_kv_heads) * G * (c.head_dim + 4) * 4);
+  w.pre_slots = take(c.prefill_rows ? (size_t)(SlotLayout{c.prefill_rows}.words() + c.prefill_rows) * 4 : 4);
+  w.pre_logits = take(c.prefill_rows ? (size_t)c.prefill_rows * c.vocab * 4 : 4);
   w.kvnew = take((size_t)c.n_kv_heads * 2 * c.head_dim * 4);
   w.sync = take(fused_sync_words(c.n_layers, c.n_kv_heads) * 4);
   w.clocks = take(((size_t)kFusedPhases * c.n_layers + 2) * 8);
@@ -283,7 +307,7 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
   w.rope = take((size_t)c.cap * (c.head_dim / 2) * 2 * 4);
   w.slot_map = take(c.kv_layout == DS3_KV_PAGED ? (size_t)c.rows * (c.cap / c.page_size) * 4 : 4);
   const size_t kmax = (size_t)std::max(std::max(c.d_model, c.ffn_dim), c.n_q_heads * c.head_dim);
-  const size_t frag = c.rows > kMaxGemvRows ? kmax * kMfmaRows * 2 : 16;
+  const size_t frag = RA > (size_t)kMaxGemvRows ? kmax * kMfmaRows * 2 : 16;
   w.frag_hi = take(frag);
   w.frag_lo = take(frag);
   w.total = off;
@@ -385,7 +409,7 @@ ds3_status wait_done(ds3_engine* e, hipEvent_t ev, uint32_t timeout_ms) {
 // One projection: the paired-row GEMV for up to 4 rows, the MFMA tile GEMM (on the split activations) beyond.
 hipError_t run_projection(ds3_engine* e, const GemvParams& p, int mode, int kind) {
   const ds3_config& c = e->cfg;
-  if (!e->mfma) return launch_gemv(p, mode, c.weight_dtype, c.kv_dtype, e->blocks[kind], e->stream);
+  if (!e->cur.mfma) return launch_gemv(p, mode, c.weight_dtype, c.kv_dtype, e->blocks[kind], e->stream);
   MfmaParams mp{};
   mp.g = p;
   mp.hi = e->frag_hi;
@@ -400,7 +424,9 @@ hipError_t run_projection(ds3_engine* e, const GemvParams& p, int mode, int kind
 
 hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
   const ds3_config& c = e->cfg;
-  const int R = c.rows;
+  const int R = e->cur.rows;
+  KvView kv = e->kv;
+  kv.row_map = e->cur.row_map;
   auto base = [&](GemvParams& p) {
     p.rows = R;
     p.eps = c.rms_eps;
@@ -408,9 +434,9 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
     p.nkv = c.n_kv_heads;
     p.hd = c.head_dim;
     p.rope = e->rope;
-    p.kv = e->kv;
+    p.kv = kv;
     p.layer = l.layer;
-    p.slots = e->slots;
+    p.slots = e->cur.slots;
     p.status = e->status;
     p.ping_pong = env_int("DS3_GEMV_PP", 1) == 1;
   };
@@ -493,7 +519,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       return launch_pick(p, e->stream);
     }
     case K_EMBED: {
-      EmbedParams p{e->embed, e->x, c.d_model, c.vocab, R, e->slots, e->status};
+      EmbedParams p{e->embed, e->x, c.d_model, c.vocab, R, e->cur.slots, e->status};
       return launch_embed(p, c.weight_dtype, e->stream);
     }
     case K_QKV: {
@@ -514,7 +540,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.q = e->q;
       p.out = e->attn;
       p.part = e->part;
-      p.kv = e->kv;
+      p.kv = kv;
       p.layer = l.layer;
       p.nq = c.n_q_heads;
       p.nkv = c.n_kv_heads;
@@ -522,7 +548,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.splits = e->splits;
       p.split_len = e->split_len;
       p.scale = (float)(1.0 / std::sqrt((double)c.head_dim));
-      p.slots = e->slots;
+      p.slots = e->cur.slots;
       p.status = e->status;
       return l.kind == K_ATTN ? launch_attention(p, c.kv_dtype, R, e->stream)
                               : launch_attention_combine(p, R, e->stream);
@@ -566,7 +592,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.w = e->lm_head;
       p.in = e->x;
       p.gain = e->final_norm;
-      p.out = e->logits;
+      p.out = e->cur.logits;
       p.K = c.d_model;
       p.n_pairs = c.vocab / 2;
       return run_projection(e, p, GEMV_HEAD, K_HEAD);
@@ -737,23 +763,44 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
                                          " compute units with one block each (device has " + std::to_string(cus) +
                                          ", " + std::to_string(per_cu) + " block(s) per unit)");
   }
-  if (e->fused) e->sequence.push_back({K_FUSED, -1, 0});
-  else e->sequence.push_back({K_EMBED, -1, 0});
-  for (int l = 0; l < c.n_layers && !e->fused; ++l) {
-    if (e->mfma) e->sequence.push_back({K_SPLIT, l, S_ATTN_NORM});
-    e->sequence.push_back({K_QKV, l, 0});
-    e->sequence.push_back({K_ATTN, l, 0});
-    e->sequence.push_back({K_COMBINE, l, 0});
-    if (e->mfma) e->sequence.push_back({K_SPLIT, l, S_ATTN_OUT});
-    e->sequence.push_back({K_OPROJ, l, 0});
-    if (e->mfma) e->sequence.push_back({K_SPLIT, l, S_FFN_NORM});
-    e->sequence.push_back({K_GATEUP, l, 0});
-    if (e->mfma) e->sequence.push_back({K_SPLIT, l, S_ACT});
-    e->sequence.push_back({K_DOWN, l, 0});
+  // the per-operation sequence of R rows (with the matrix-core split kernels above 4 rows)
+  auto per_op = [&](std::vector<Launch>& seq, bool mfma, bool pick) {
+    seq.push_back({K_EMBED, -1, 0});
+    for (int l = 0; l < c.n_layers; ++l) {
+      if (mfma) seq.push_back({K_SPLIT, l, S_ATTN_NORM});
+      seq.push_back({K_QKV, l, 0});
+      seq.push_back({K_ATTN, l, 0});
+      seq.push_back({K_COMBINE, l, 0});
+      if (mfma) seq.push_back({K_SPLIT, l, S_ATTN_OUT});
+      seq.push_back({K_OPROJ, l, 0});
+      if (mfma) seq.push_back({K_SPLIT, l, S_FFN_NORM});
+      seq.push_back({K_GATEUP, l, 0});
+      if (mfma) seq.push_back({K_SPLIT, l, S_ACT});
+      seq.push_back({K_DOWN, l, 0});
+    }
+    if (mfma) seq.push_back({K_SPLIT, -1, S_FINAL_NORM});
+    seq.push_back({K_HEAD, -1, 0});
+    if (pick) seq.push_back({K_PICK, -1, 0});
+  };
+  if (e->fused) e->sequence.push_back({K_FUSED, -1, 0});   // (the fused kernel picks in its own last phase)
+  else per_op(e->sequence, e->mfma, true);
+  e->dec.rows = c.rows;
+  e->dec.slots = e->slots;
+  e->dec.logits = e->logits;
+  e->dec.mfma = e->mfma;
+  e->cur = e->dec;
+  if (c.prefill_rows > 0) {
+    const int T = c.prefill_rows;
+    e->pre.rows = T;
+    e->pre.slots = reinterpret_cast<int*>(work + wp.pre_slots);
+    e->pre.logits = reinterpret_cast<float*>(work + wp.pre_logits);
+    e->pre.mfma = T > kMaxGemvRows;
+    e->pre.row_map = e->pre.slots + SlotLayout{T}.words();
+    per_op(e->pre_sequence, e->pre.mfma, false);
+    h = hipHostMalloc(reinterpret_cast<void**>(&e->h_pre),
+                      (size_t)(kMaxPrefill / T + 1) * (SlotLayout{T}.words() + T) * 4, hipHostMallocDefault);
+    if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("hipHostMalloc: ") + hipGetErrorString(h));
   }
-  if (e->mfma) e->sequence.push_back({K_SPLIT, -1, S_FINAL_NORM});
-  if (!e->fused) e->sequence.push_back({K_HEAD, -1, 0});
-  if (!e->fused) e->sequence.push_back({K_PICK, -1, 0});   // (the fused kernel picks in its own last phase)
 
   const SlotLayout sl{c.rows};
   h = hipHostMalloc(reinterpret_cast<void**>(&e->h_slots), (size_t)sl.words() * 4 + kAlign + sizeof(StatusWords),
@@ -1029,6 +1076,110 @@ ds3_status ds3_step_greedy(ds3_engine* e, const int32_t* tokens, const int32_t* 
   return run_steps(e, tokens, pos, nullptr, n_steps, nullptr, ids, flags);
 }
 
+ds3_status ds3_prefill(ds3_engine* e, int32_t row, const int32_t* tokens, int32_t pos0, int32_t n,
+                       float* logits_host, uint32_t* flags) {
+  if (ds3_status st = refuse_if_unusable(e)) return st;
+  if (e->state == ST_NOT_LOADED) return fail(e, DS3_E_NOT_LOADED, "weights are not loaded");
+  if (e->state == ST_NEEDS_RESET) return fail(e, DS3_E_NEEDS_RESET, "a previous step failed; reset_state first");
+  const ds3_config& c = e->cfg;
+  const int T = c.prefill_rows;
+  if (T < 1) return fail(e, DS3_E_UNSUPPORTED, "the engine was created with prefill_rows = 0");
+  if (!tokens) return fail(e, DS3_E_INVALID, "tokens is NULL");
+  if (row < 0 || row >= c.rows) return fail(e, DS3_E_INVALID, "row out of range");
+  if (n < 1 || n > kMaxPrefill) return fail(e, DS3_E_INVALID, "n must be in 1.." + std::to_string(kMaxPrefill));
+  if (pos0 < 0 || (int64_t)pos0 + n > c.cap) return fail(e, DS3_E_INVALID, "pos0 .. pos0 + n - 1 must lie in the capacity");
+  const bool paged = c.kv_layout == DS3_KV_PAGED;
+  if (paged && !e->slot_map_set) return fail(e, DS3_E_INVALID, "paged prefill needs a slot map");
+  for (int i = 0; i < n; ++i)
+    if (tokens[i] < 0 || tokens[i] >= c.vocab) return fail(e, DS3_E_INVALID, "token out of range at " + std::to_string(i));
+  const SlotLayout sl{T};
+  const int words = sl.words() + T;   // slot words, then the K/V row of each activation row
+  const int chunks = (n + T - 1) / T;
+  // chunk k holds tokens kT .. kT + T - 1 at positions pos0 + kT + t; the rows past the last token repeat the last
+  // token at its position (they write the same K/V again and their logits are not used)
+  for (int k = 0; k < chunks; ++k) {
+    int32_t* w = e->h_pre + (size_t)k * words;
+    for (int t = 0; t < T; ++t) {
+      const int i = std::min(k * T + t, n - 1);
+      const int p = pos0 + i;
+      w[sl.token() + t] = tokens[i];
+      w[sl.pos() + t] = p;
+      int32_t wm = 0;
+      if (paged) {
+        const int ppr = c.cap / c.page_size;
+        wm = e->h_slot_map[(size_t)row * ppr + p / c.page_size] * c.page_size + p % c.page_size;
+      }
+      w[sl.write_map() + t] = wm;
+      w[sl.words() + t] = row;
+    }
+    w[sl.inject()] = 0;
+    w[sl.spin()] = 0;
+    w[sl.chain()] = 0;
+    w[sl.sweep()] = e->kv_sweep;
+  }
+  const auto t_start = std::chrono::steady_clock::now();
+  e->h_status->err = 0;
+  e->h_status->nonfinite = 0;
+  HIP_OR_POISON(e, hipMemcpyAsync(e->status, e->h_status, sizeof(StatusWords), hipMemcpyHostToDevice, e->stream));
+  e->cur = e->pre;
+  hipError_t h = hipSuccess;
+  if (c.exec_mode == DS3_GRAPH && !e->pre_captured) {
+    h = hipStreamBeginCapture(e->stream, hipStreamCaptureModeThreadLocal);
+    if (h == hipSuccess) {
+      hipError_t h1 = hipSuccess;
+      for (const Launch& l : e->pre_sequence)
+        if (h1 == hipSuccess) h1 = enqueue_kernel(e, l);
+      hipGraph_t g = nullptr;
+      h = hipStreamEndCapture(e->stream, &g);
+      if (h == hipSuccess) h = h1;
+      if (h == hipSuccess) {
+        e->pre_graph = g;
+        h = hipGraphInstantiate(&e->pre_exec, g, nullptr, nullptr, 0);
+        if (h == hipSuccess) {
+          e->pre_captured = true;
+          e->stats.captures++;
+        }
+      } else if (g) {
+        (void)hipGraphDestroy(g);
+      }
+    }
+  }
+  if (h == hipSuccess) h = hipEventRecord(e->ev0, e->stream);
+  for (int k = 0; k < chunks && h == hipSuccess; ++k) {
+    h = hipMemcpyAsync(e->pre.slots, e->h_pre + (size_t)k * words, (size_t)words * 4, hipMemcpyHostToDevice, e->stream);
+    if (h != hipSuccess) break;
+    if (c.exec_mode == DS3_GRAPH) {
+      h = hipGraphLaunch(e->pre_exec, e->stream);
+    } else {
+      for (const Launch& l : e->pre_sequence)
+        if (h == hipSuccess) h = enqueue_kernel(e, l);
+    }
+  }
+  e->cur = e->dec;
+  HIP_OR_POISON(e, h);
+  HIP_OR_POISON(e, hipEventRecord(e->ev1, e->stream));
+  HIP_OR_POISON(e, hipMemcpyAsync(e->h_status, e->status, sizeof(StatusWords), hipMemcpyDeviceToHost, e->stream));
+  if (logits_host)
+    HIP_OR_POISON(e, hipMemcpyAsync(logits_host, e->pre.logits + (size_t)((n - 1) % T) * c.vocab, (size_t)c.vocab * 4,
+                                    hipMemcpyDeviceToHost, e->stream));
+  HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
+  e->pending = true;
+  if (ds3_status st = wait_done(e, e->ev_done, e->cfg.timeout_ms)) return st;
+  float gpu_ms = 0.f;
+  HIP_OR_POISON(e, hipEventElapsedTime(&gpu_ms, e->ev0, e->ev1));
+  e->stats.last_prefill_gpu_us = gpu_ms * 1e3;
+  e->stats.last_host_us =
+      std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t_start).count();
+  if (flags) *flags = e->h_status->nonfinite ? 1u : 0u;
+  if (e->h_status->err) {
+    e->state = ST_NEEDS_RESET;
+    e->stats.state = e->state;
+    return fail(e, DS3_E_KERNEL_CHECK, "in-kernel check failed during the prefill");
+  }
+  e->stats.prefill_tokens += n;
+  return DS3_OK;
+}
+
 ds3_status ds3_set_kv_sweep(ds3_engine* e, int32_t mode) {
   if (ds3_status st = refuse_if_unusable(e)) return st;
   if (mode != DS3_SWEEP_FULL && mode != DS3_SWEEP_VISIBLE)
@@ -1262,6 +1413,9 @@ void ds3_destroy(ds3_engine* e) {
   }
   if (e->exec) (void)hipGraphExecDestroy(e->exec);
   if (e->graph) (void)hipGraphDestroy(e->graph);
+  if (e->pre_exec) (void)hipGraphExecDestroy(e->pre_exec);
+  if (e->pre_graph) (void)hipGraphDestroy(e->pre_graph);
+  if (e->h_pre) (void)hipHostFree(e->h_pre);
   for (hipEvent_t ev : {e->ev0, e->ev1, e->ev_done})
     if (ev) (void)hipEventDestroy(ev);
   if (e->h_slots) (void)hipHostFree(e->h_slots);

@@ -48,6 +48,8 @@ struct KvView {
   int page_size;
   int pool_pages;
   const int* slot_map;   // paged: [rows][cap/page_size]
+  const int* row_map;    // null: activation row r uses K/V row r; else row_map[r] (a prefill: every token of the
+                         // chunk is an activation row of the same K/V row)
 };
 
 enum GemvMode : int {

@@ -678,6 +678,7 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
   // visible-sweep slot set: chunks wholly after pos (a suffix of this split's chunks) are not loaded
   const bool vis_only = p.slots[sl.sweep()] != 0;
   auto live = [&](int c0) { return !vis_only || chunk_base(c0) <= pos; };
+  const int kr = kv_row(p.kv, r);   // this row's K/V row
   const KT* Kb = reinterpret_cast<const KT*>(p.kv.k) + (size_t)p.layer * p.kv.layer_stride;
   const KT* Vb = reinterpret_cast<const KT*>(p.kv.v) + (size_t)p.layer * p.kv.layer_stride;
   const float scale2 = p.scale * 1.4426950408889634f;   // 1/sqrt(hd) * log2(e)
@@ -700,7 +701,7 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
     const int n = ((T + TC - 1) / TC) * ppc;
     for (int i = tid; i < n; i += kBlock) {
       const int lp = min(chunk_base((i / ppc) * TC) / ps + i % ppc, ppr - 1);
-      int page = p.kv.slot_map[r * ppr + lp];
+      int page = p.kv.slot_map[kr * ppr + lp];
       if (page < 0 || page >= p.kv.pool_pages) {
         raise_error(p.status, ERR_PAGE);
         page = 0;
@@ -728,7 +729,7 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
         const int page = ptab[(c0 / TC) * ppc + q];
         off = (uint32_t)(((page * p.nkv + g) * ps + (jc % ps)) * HD);
       } else {
-        off = (uint32_t)(((r * p.nkv + g) * cap + jc) * HD);
+        off = (uint32_t)(((kr * p.nkv + g) * cap + jc) * HD);
       }
       const int el = (byte % PB) / (int)sizeof(KT);
       __builtin_amdgcn_global_load_lds((global_cptr)(Kb + off + el), (lds_ptr)(kdst + (size_t)k * 1024), 16, 0, 0);
@@ -897,6 +898,7 @@ __global__ void __launch_bounds__(kBlock) attn_mfma_kernel(AttnParams p) {
   // split's chunks) are neither loaded nor computed
   const bool vis_only = p.slots[sl.sweep()] != 0;
   auto live = [&](int c0) { return !vis_only || chunk_base(c0) <= pos; };
+  const int kr = kv_row(p.kv, r);   // this row's K/V row
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(p.kv.k) + (size_t)p.layer * p.kv.layer_stride;
   const uint16_t* Vb = reinterpret_cast<const uint16_t*>(p.kv.v) + (size_t)p.layer * p.kv.layer_stride;
   const float scale2 = p.scale * 1.4426950408889634f;   // 1/sqrt(hd) * log2(e): scores in the log2 domain
@@ -921,7 +923,7 @@ __global__ void __launch_bounds__(kBlock) attn_mfma_kernel(AttnParams p) {
     const int nt = ((T + TC - 1) / TC) * ppc;
     for (int i = tid; i < nt; i += kBlock) {
       const int lp = min(chunk_base((i / ppc) * TC) / ps + i % ppc, ppr - 1);
-      int page = p.kv.slot_map[r * ppr + lp];
+      int page = p.kv.slot_map[kr * ppr + lp];
       if (page < 0 || page >= p.kv.pool_pages) {
         raise_error(p.status, ERR_PAGE);
         page = 0;
@@ -955,8 +957,8 @@ __global__ void __launch_bounds__(kBlock) attn_mfma_kernel(AttnParams p) {
         koff = (uint32_t)(((pk * nkv + g) * ps + jk % ps) * HD + 8 * c);
         voff = (uint32_t)(((pv * nkv + g) * HD + d) * ps + jv % ps);
       } else {
-        koff = (uint32_t)(((r * nkv + g) * cap + jk) * HD + 8 * c);
-        voff = (uint32_t)(((r * nkv + g) * HD + d) * cap + jv);
+        koff = (uint32_t)(((kr * nkv + g) * cap + jk) * HD + 8 * c);
+        voff = (uint32_t)(((kr * nkv + g) * HD + d) * cap + jv);
       }
       __builtin_amdgcn_global_load_lds((global_cptr)(Kb + koff), (lds_ptr)(kdst + (size_t)k * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((global_cptr)(Vb + voff), (lds_ptr)(vdst + (size_t)k * 1024), 16, 0, 0);

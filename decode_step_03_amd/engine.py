@@ -15,14 +15,15 @@ from . import _ds3 as C
 
 def make_config(*, n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, rms_eps, rope_theta, rows,
                 cap, kv_layout="contiguous", page_size=0, pool_pages=0, weight_dtype="bf16", kv_dtype="bf16",
-                exec_mode="graph", timeout_ms=0, kernel_plan="auto", trace="off") -> C.ds3_config:
+                exec_mode="graph", timeout_ms=0, kernel_plan="auto", trace="off", prefill_rows=0) -> C.ds3_config:
     dt = {"f32": C.DS3_F32, "bf16": C.DS3_BF16}
     return C.ds3_config(
         C.DS3_ABI_VERSION, n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, rms_eps, rope_theta,
         rows, cap, C.DS3_KV_PAGED if kv_layout == "paged" else C.DS3_KV_CONTIGUOUS, page_size, pool_pages,
         dt[weight_dtype], dt[kv_dtype], C.DS3_EAGER if exec_mode == "eager" else C.DS3_GRAPH, timeout_ms,
         {"auto": C.DS3_PLAN_AUTO, "per_op": C.DS3_PLAN_PER_OP, "fused": C.DS3_PLAN_FUSED}[kernel_plan],
-        {"off": C.DS3_TRACE_OFF, "barriers": C.DS3_TRACE_BARRIERS, "phases": C.DS3_TRACE_PHASES}[trace])
+        {"off": C.DS3_TRACE_OFF, "barriers": C.DS3_TRACE_BARRIERS, "phases": C.DS3_TRACE_PHASES}[trace],
+        prefill_rows)
 
 
 class Engine:
@@ -93,6 +94,14 @@ class Engine:
         C.ds3_step_greedy(self.handle, self._tok.ctypes.data, self._pos.ctypes.data, n_steps, ids.ctypes.data,
                           flags.ctypes.data)
         return ids, flags
+
+    def prefill(self, row: int, tokens, pos0: int):
+        """Prefill: tokens (int32 [n]) of row `row` at positions pos0 .. pos0 + n - 1, prefill_rows per launch.
+        Returns (logits float32 [vocab] of the last token, flags)."""
+        toks = np.ascontiguousarray(np.asarray(tokens, np.int32))
+        out = np.empty(self.cfg.vocab, np.float32)
+        flags = C.ds3_prefill(self.handle, row, toks.ctypes.data, pos0, toks.size, out.ctypes.data)
+        return out, flags
 
     def set_kv_sweep(self, mode: str) -> None:
         """"full" (the method: every position of [cap] is loaded) or "visible" (chunks wholly after pos are skipped;

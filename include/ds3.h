@@ -30,7 +30,7 @@
 extern "C" {
 #endif
 
-#define DS3_ABI_VERSION 4u
+#define DS3_ABI_VERSION 5u
 
 typedef struct ds3_engine ds3_engine;
 
@@ -86,6 +86,7 @@ typedef struct {
   uint32_t timeout_ms;
   int32_t kernel_plan;         /* DS3_PLAN_*; FUSED where it does not apply -> DS3_E_UNSUPPORTED */
   int32_t trace;               /* DS3_TRACE_*: fused plan, what every step records for ds3_phase_trace */
+  int32_t prefill_rows;        /* 0: no prefill step; 1..16: ds3_prefill takes this many tokens per launch */
 } ds3_config;
 
 /* Device buffers the caller allocates for ds3_create, in this id order. */
@@ -144,6 +145,8 @@ typedef struct {
   int32_t kernel_plan;       /* the plan in use: DS3_PLAN_PER_OP or DS3_PLAN_FUSED */
   double last_submit_us;     /* host time of the last ds3_step spent issuing work (slot copy, launch or replay,
                                 readback copies), without the wait for the device */
+  uint64_t prefill_tokens;   /* tokens taken by successful ds3_prefill calls */
+  double last_prefill_gpu_us; /* device time of the last ds3_prefill (every chunk) */
 } ds3_stats;
 
 /* Per-kernel device timing of one step, from HIP events around each launch on the engine's stream. */
@@ -200,6 +203,22 @@ ds3_status ds3_step(ds3_engine* e, const int32_t* tokens, const int32_t* pos, co
 #define DS3_MAX_CHAIN 1024
 ds3_status ds3_step_greedy(ds3_engine* e, const int32_t* tokens, const int32_t* pos, int32_t n_steps,
                            int32_t* ids, uint32_t* flags);
+
+/* Prefill (the step before decode): n tokens of one row at positions pos0 .. pos0 + n - 1, with their K/V written
+ * into that row's state ("Models, Registry and the Driver" page, section "The Model": a prefill is a step that
+ * continues from a position, in chunks). The tokens go prefill_rows at a time through one launch sequence (one
+ * graph replay): chunk k is a step of prefill_rows activation rows that all read and write the same K/V row, token
+ * t of the chunk at position pos0 + k prefill_rows + t, so its attention sees the K/V of the chunk's earlier tokens
+ * (written by the same step before the attention runs) and nothing after its own position -- the causal mask
+ * inside the chunk is the position mask of the decode step. More than 4 rows run the projections on the matrix
+ * cores. The rows after the last token of the last chunk repeat that token at its position. logits_host (float32
+ * [vocab], may be NULL) receives the last token's logits, from which the first decode step's token is picked;
+ * flags (may be NULL) bit 0: some logit of the prefill was NaN or infinite. n in 1..DS3_MAX_PREFILL; pos0 + n must
+ * not pass cap; paged layout: the page table must be set. DS3_E_UNSUPPORTED when the engine was created with
+ * prefill_rows = 0; other errors as ds3_step. */
+#define DS3_MAX_PREFILL 8192
+ds3_status ds3_prefill(ds3_engine* e, int32_t row, const int32_t* tokens, int32_t pos0, int32_t n,
+                       float* logits_host, uint32_t* flags);
 
 /* K/V sweep of the attention, from the next step on (a slot word: no recapture). FULL (the default) loads every
  * position of [cap], as the method does ("Execution" page, section "A constant-shape decode graph": the sweep

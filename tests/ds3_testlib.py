@@ -30,7 +30,7 @@ def logits_tol(w: synth.Workload) -> float:
 
 
 def engine_config(w: synth.Workload, exec_mode="graph", timeout_ms=0, rows=None, cap=None, kernel_plan="auto",
-                  trace="off"):
+                  trace="off", prefill_rows=0):
     from decode_step_03_amd import make_config
     m = w.model
     return make_config(n_layers=m.n_layers, d_model=m.d_model, n_q_heads=m.n_q_heads, n_kv_heads=m.n_kv_heads,
@@ -38,13 +38,14 @@ def engine_config(w: synth.Workload, exec_mode="graph", timeout_ms=0, rows=None,
                        rope_theta=m.rope_theta, rows=rows or w.rows, cap=cap or w.cap, kv_layout=w.kv_layout,
                        page_size=w.page_size, pool_pages=w.pool_pages, weight_dtype=m.weight_dtype,
                        kv_dtype=w.kv_dtype, exec_mode=exec_mode, timeout_ms=timeout_ms, kernel_plan=kernel_plan,
-                       trace=trace)
+                       trace=trace, prefill_rows=prefill_rows)
 
 
 def make_engine(w: synth.Workload, ws: synth.WeightSet, exec_mode="graph", timeout_ms=0, kernel_plan="auto",
-                trace="off"):
+                trace="off", prefill_rows=0):
     from decode_step_03_amd import Engine
-    eng = Engine(engine_config(w, exec_mode, timeout_ms, kernel_plan=kernel_plan, trace=trace))
+    eng = Engine(engine_config(w, exec_mode, timeout_ms, kernel_plan=kernel_plan, trace=trace,
+                               prefill_rows=prefill_rows))
     eng.load_weights(ws.layers, ws.glob)
     return eng
 
