@@ -36,11 +36,18 @@ DS3_TRACE_OFF, DS3_TRACE_BARRIERS, DS3_TRACE_PHASES = 0, 1, 2
 DS3_MAX_CHAIN = 1024
 DS3_SWEEP_FULL, DS3_SWEEP_VISIBLE = 0, 1
 DS3_MAX_PREFILL = 8192
+DS3_MAX_LOGPROBS = 8
 DS3_BUF_WEIGHTS, DS3_BUF_KV, DS3_BUF_WORK, DS3_BUF_LOGITS, DS3_NUM_BUFFERS = 0, 1, 2, 3, 4
 DS3_INJECT_KERNEL_CHECK, DS3_INJECT_TIMEOUT_NEXT, DS3_INJECT_BARRIER_TIMEOUT = 1, 2, 3
 
 ROLES = {"embed": 0, "attn_norm": 1, "wq": 2, "wk": 3, "wv": 4, "wo": 5, "ffn_norm": 6, "w_gate": 7, "w_up": 8,
          "w_down": 9, "final_norm": 10, "lm_head": 11}
+
+
+class ds3_sampling(ctypes.Structure):
+    _fields_ = [("temperature", c_float), ("top_p", c_float), ("min_p", c_float), ("repetition_penalty", c_float),
+                ("presence_penalty", c_float), ("frequency_penalty", c_float), ("top_k", c_int32),
+                ("n_logprobs", c_int32), ("seed", c_uint64)]
 
 
 class ds3_config(ctypes.Structure):
@@ -82,6 +89,9 @@ SIGNATURES = [
     ("ds3_step_greedy", c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
     ("ds3_set_kv_sweep", c_int32, [c_void_p, c_int32]),
     ("ds3_prefill", c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, POINTER(c_uint32)]),
+    ("ds3_set_sampling", c_int32, [c_void_p, c_int32, c_void_p]),
+    ("ds3_set_history", c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_void_p]),
+    ("ds3_step_sample", c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     ("ds3_reset_state", c_int32, [c_void_p]),
     ("ds3_write_kv", c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     ("ds3_read_kv", c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
@@ -169,6 +179,19 @@ def ds3_prefill(h: int, row: int, tokens_ptr: int, pos0: int, n: int, logits_ptr
     flags = c_uint32(0)
     _check(load_library().ds3_prefill(h, row, tokens_ptr, pos0, n, logits_ptr, ctypes.byref(flags)), h)
     return flags.value
+
+
+def ds3_set_sampling(h: int, row: int, params: "ds3_sampling") -> None:
+    _check(load_library().ds3_set_sampling(h, row, ctypes.byref(params)), h)
+
+
+def ds3_set_history(h: int, row: int, tokens_ptr: int | None, n: int, bias_ptr: int | None) -> None:
+    _check(load_library().ds3_set_history(h, row, tokens_ptr, n, bias_ptr), h)
+
+
+def ds3_step_sample(h: int, tokens_ptr: int, pos_ptr: int, n_steps: int, ids_ptr: int, flags_ptr: int | None,
+                    lp_ptr: int | None, lp_ids_ptr: int | None) -> None:
+    _check(load_library().ds3_step_sample(h, tokens_ptr, pos_ptr, n_steps, ids_ptr, flags_ptr, lp_ptr, lp_ids_ptr), h)
 
 
 def ds3_set_kv_sweep(h: int, mode: int) -> None:

@@ -31,16 +31,18 @@ size_t dtype_bytes(int dt) { return dt == DS3_BF16 ? 2 : 4; }
 
 struct WorkPlan {
   size_t slots, status, x, q, attn, act, part, pre_slots, pre_logits, kvnew, sync, clocks, trace, pick_val, pick_idx,
-      pick_done, ids, chain_flags, rope, slot_map, frag_hi, frag_lo, total;
+      pick_done, ids, chain_flags, samp_rows, counts, bias, draws, zbuf, lp, lp_ids, rope, slot_map, frag_hi, frag_lo,
+      total;
 };
 
 struct KernelKind {
   const char* name;
 };
-enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN, K_HEAD, K_SPLIT, K_COMBINE, K_FUSED, K_PICK, K_NUM };
+enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN, K_HEAD, K_SPLIT, K_COMBINE, K_FUSED, K_PICK, K_SAMPLE,
+            K_NUM };
 const char* kKindNames[K_NUM] = {"embed", "qkv_rope_kvwrite", "attention_splitk", "o_proj_residual",
                                  "gateup_swiglu", "down_proj_residual", "lm_head", "act_split_mfma",
-                                 "attention_combine", "decode_step_fused", "greedy_pick"};
+                                 "attention_combine", "decode_step_fused", "greedy_pick", "sampler"};
 constexpr int kMaxChain = DS3_MAX_CHAIN;   // steps of one ds3_step_greedy call
 constexpr int kMaxPrefill = DS3_MAX_PREFILL;   // tokens of one ds3_prefill call
 // fused plan: the operation kind of phase k of a layer (the grid barrier after it closes the phase)
@@ -84,6 +86,20 @@ struct ds3_engine {
   unsigned* pick_done = nullptr;
   int32_t* ids = nullptr;                            // [kMaxChain][rows] picks of a chain of steps
   uint32_t* chain_flags = nullptr;                   // [kMaxChain] non-finite flag of each step
+  SampleRow* samp_rows = nullptr;                    // sampling suffix: per-row parameters (uploaded per call)
+  int32_t* counts = nullptr;                         // [rows][vocab] token history
+  float* bias = nullptr;                             // [rows][vocab] logit bias
+  uint32_t* draws = nullptr;                         // [rows] draws so far (the generator's counter)
+  float* zbuf = nullptr;                             // [rows][vocab] adjusted logits (scratch)
+  float* lp = nullptr;                               // [kMaxChain][rows][1 + kMaxLogprobs] logprobs
+  int32_t* lp_ids = nullptr;                         // [kMaxChain][rows][kMaxLogprobs]
+  std::vector<SampleRow> h_samp;                     // host copy of the per-row parameters
+  std::vector<Launch> samp_sequence;                 // the step with the sampler as its pick
+  hipGraph_t samp_graph = nullptr;
+  hipGraphExec_t samp_exec = nullptr;
+  bool samp_captured = false;
+  SampleRow* h_samp_pinned = nullptr;                // pinned staging of h_samp
+  float* h_lp = nullptr;                             // pinned: logprobs and their ids of the last call
   size_t sync_words = 0;
   size_t weight_lstride = 0;                         // bytes between consecutive layers' weights
   size_t work_bytes = 0;
@@ -304,6 +320,13 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
   w.pick_done = take(4);
   w.ids = take((size_t)kMaxChain * c.rows * 4);
   w.chain_flags = take((size_t)kMaxChain * 4);
+  w.samp_rows = take((size_t)c.rows * sizeof(SampleRow));
+  w.counts = take((size_t)c.rows * c.vocab * 4);
+  w.bias = take((size_t)c.rows * c.vocab * 4);
+  w.draws = take((size_t)c.rows * 4);
+  w.zbuf = take((size_t)c.rows * c.vocab * 4);
+  w.lp = take((size_t)kMaxChain * c.rows * (1 + kMaxLogprobs) * 4);
+  w.lp_ids = take((size_t)kMaxChain * c.rows * kMaxLogprobs * 4);
   w.rope = take((size_t)c.cap * (c.head_dim / 2) * 2 * 4);
   w.slot_map = take(c.kv_layout == DS3_KV_PAGED ? (size_t)c.rows * (c.cap / c.page_size) * 4 : 4);
   const size_t kmax = (size_t)std::max(std::max(c.d_model, c.ffn_dim), c.n_q_heads * c.head_dim);
@@ -371,6 +394,7 @@ double kind_bytes(const ds3_config& c, int kind) {
     case K_DOWN: return Lc * d * F * wb;
     case K_HEAD: return (double)c.vocab * d * wb + d * wb;
     case K_PICK: return R * (double)c.vocab * 4;   // the logits, read once
+    case K_SAMPLE: return R * (double)c.vocab * 12;   // logits, history and bias, read once
     case K_FUSED: {
       double t = 0;
       for (int k : {K_EMBED, K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN, K_HEAD}) t += kind_bytes(c, k);
@@ -499,6 +523,28 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
         default: sp.in = e->act; sp.K = c.ffn_dim; norm = false; break;
       }
       return launch_split(sp, norm, e->stream);
+    }
+    case K_SAMPLE: {
+      SampleParams p{};
+      p.logits = e->logits;
+      p.vocab = c.vocab;
+      p.rows = R;
+      p.slots = e->slots;
+      p.page_table = c.kv_layout == DS3_KV_PAGED ? e->slot_map : nullptr;
+      p.page_size = c.page_size;
+      p.cap = c.cap;
+      p.rowp = e->samp_rows;
+      p.counts = e->counts;
+      p.bias = e->bias;
+      p.draws = e->draws;
+      p.z = e->zbuf;
+      p.ids = e->ids;
+      p.flags = e->chain_flags;
+      p.lp = e->lp;
+      p.lp_ids = e->lp_ids;
+      p.max_chain = kMaxChain;
+      p.status = e->status;
+      return launch_sample(p, e->stream);
     }
     case K_PICK: {
       PickParams p{};
@@ -708,6 +754,13 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   e->pick_done = reinterpret_cast<unsigned*>(work + wp.pick_done);
   e->ids = reinterpret_cast<int32_t*>(work + wp.ids);
   e->chain_flags = reinterpret_cast<uint32_t*>(work + wp.chain_flags);
+  e->samp_rows = reinterpret_cast<SampleRow*>(work + wp.samp_rows);
+  e->counts = reinterpret_cast<int32_t*>(work + wp.counts);
+  e->bias = reinterpret_cast<float*>(work + wp.bias);
+  e->draws = reinterpret_cast<uint32_t*>(work + wp.draws);
+  e->zbuf = reinterpret_cast<float*>(work + wp.zbuf);
+  e->lp = reinterpret_cast<float*>(work + wp.lp);
+  e->lp_ids = reinterpret_cast<int32_t*>(work + wp.lp_ids);
   e->sync_words = fused_sync_words(c.n_layers, c.n_kv_heads);
   e->frag_hi = reinterpret_cast<uint16_t*>(work + wp.frag_hi);
   e->frag_lo = reinterpret_cast<uint16_t*>(work + wp.frag_lo);
@@ -784,6 +837,15 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   };
   if (e->fused) e->sequence.push_back({K_FUSED, -1, 0});   // (the fused kernel picks in its own last phase)
   else per_op(e->sequence, e->mfma, true);
+  e->samp_sequence = e->sequence;   // the same step, the sampler as its pick
+  if (e->fused) e->samp_sequence.push_back({K_SAMPLE, -1, 0});
+  else e->samp_sequence.back() = {K_SAMPLE, -1, 0};
+  e->h_samp.assign((size_t)c.rows, SampleRow{0.f, 1.f, 0.f, 1.f, 0.f, 0.f, 0, 0, 0u, 0u});
+  h = hipHostMalloc(reinterpret_cast<void**>(&e->h_samp_pinned), (size_t)c.rows * sizeof(SampleRow), hipHostMallocDefault);
+  if (h == hipSuccess)
+    h = hipHostMalloc(reinterpret_cast<void**>(&e->h_lp), (size_t)kMaxChain * c.rows * (1 + 2 * kMaxLogprobs) * 4,
+                      hipHostMallocDefault);
+  if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("hipHostMalloc: ") + hipGetErrorString(h));
   e->dec.rows = c.rows;
   e->dec.slots = e->slots;
   e->dec.logits = e->logits;
@@ -970,8 +1032,30 @@ ds3_status ds3_set_slot_map(ds3_engine* e, const int32_t* slot_map) {
 
 // n_steps steps from the given slots: the first from the host's words, each later one from the slots the
 // previous step's greedy pick advanced on the device (token = the pick, pos + 1). One host wait for all of them.
+// Capture `seq` into a graph of its own (the sampling variant of the step).
+static ds3_status capture_seq(ds3_engine* e, const std::vector<Launch>& seq, hipGraph_t* graph, hipGraphExec_t* exec,
+                              bool* captured) {
+  if (*captured) return DS3_OK;
+  HIP_OR_POISON(e, hipStreamBeginCapture(e->stream, hipStreamCaptureModeThreadLocal));
+  hipError_t h = hipSuccess;
+  for (const Launch& l : seq)
+    if (h == hipSuccess) h = enqueue_kernel(e, l);
+  hipGraph_t g = nullptr;
+  const hipError_t h2 = hipStreamEndCapture(e->stream, &g);
+  if (h != hipSuccess || h2 != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    return poison(e, DS3_E_DEVICE_LOST, std::string("graph capture: ") + hipGetErrorString(h != hipSuccess ? h : h2));
+  }
+  *graph = g;
+  HIP_OR_POISON(e, hipGraphInstantiate(exec, g, nullptr, nullptr, 0));
+  *captured = true;
+  e->stats.captures++;
+  return DS3_OK;
+}
+
 static ds3_status run_steps(ds3_engine* e, const int32_t* tokens, const int32_t* pos, const int32_t* write_map,
-                            int32_t n_steps, float* logits_host, int32_t* ids_out, uint32_t* flags_out) {
+                            int32_t n_steps, float* logits_host, int32_t* ids_out, uint32_t* flags_out,
+                            bool sample = false, float* lp_out = nullptr, int32_t* lp_ids_out = nullptr) {
   const auto t_start = std::chrono::steady_clock::now();
   if (ds3_status st = refuse_if_unusable(e)) return st;
   if (e->state == ST_NOT_LOADED) return fail(e, DS3_E_NOT_LOADED, "weights are not loaded");
@@ -1009,6 +1093,7 @@ static ds3_status run_steps(ds3_engine* e, const int32_t* tokens, const int32_t*
   e->h_slots[sl.spin()] = e->inject_barrier ? 1 : 0;   // fused kernel: 1 tick forces every barrier wait to time out
   e->h_slots[sl.chain()] = 0;
   e->h_slots[sl.sweep()] = e->kv_sweep;
+  e->h_slots[sl.sample()] = sample ? 1 : 0;
   e->inject_check = false;
   e->inject_barrier = false;
   const uint32_t timeout = e->inject_timeout ? 0u : e->cfg.timeout_ms;
@@ -1018,15 +1103,26 @@ static ds3_status run_steps(ds3_engine* e, const int32_t* tokens, const int32_t*
   e->h_status->err = 0;
   e->h_status->nonfinite = 0;
   HIP_OR_POISON(e, hipMemcpyAsync(e->status, e->h_status, sizeof(StatusWords), hipMemcpyHostToDevice, e->stream));
+  if (sample) {
+    std::memcpy(e->h_samp_pinned, e->h_samp.data(), (size_t)c.rows * sizeof(SampleRow));
+    HIP_OR_POISON(e, hipMemcpyAsync(e->samp_rows, e->h_samp_pinned, (size_t)c.rows * sizeof(SampleRow),
+                                    hipMemcpyHostToDevice, e->stream));
+  }
   if (c.exec_mode == DS3_GRAPH) {
-    if (ds3_status st = ensure_captured(e)) return st;
+    if (sample) {
+      if (ds3_status st = capture_seq(e, e->samp_sequence, &e->samp_graph, &e->samp_exec, &e->samp_captured)) return st;
+    } else if (ds3_status st = ensure_captured(e)) {
+      return st;
+    }
+    hipGraphExec_t x = sample ? e->samp_exec : e->exec;
     HIP_OR_POISON(e, hipEventRecord(e->ev0, e->stream));
-    for (int i = 0; i < n_steps; ++i) HIP_OR_POISON(e, hipGraphLaunch(e->exec, e->stream));
+    for (int i = 0; i < n_steps; ++i) HIP_OR_POISON(e, hipGraphLaunch(x, e->stream));
     HIP_OR_POISON(e, hipEventRecord(e->ev1, e->stream));
     e->stats.replays += n_steps;
   } else {
     HIP_OR_POISON(e, hipEventRecord(e->ev0, e->stream));
-    for (int i = 0; i < n_steps; ++i) HIP_OR_POISON(e, enqueue_step(e));
+    for (int i = 0; i < n_steps; ++i)
+      for (const Launch& l : sample ? e->samp_sequence : e->sequence) HIP_OR_POISON(e, enqueue_kernel(e, l));
     HIP_OR_POISON(e, hipEventRecord(e->ev1, e->stream));
   }
   HIP_OR_POISON(e, hipMemcpyAsync(e->h_status, e->status, sizeof(StatusWords), hipMemcpyDeviceToHost, e->stream));
@@ -1035,6 +1131,11 @@ static ds3_status run_steps(ds3_engine* e, const int32_t* tokens, const int32_t*
   if (ids_out)
     HIP_OR_POISON(e, hipMemcpyAsync(h_ids, e->ids, (size_t)n_steps * c.rows * 4, hipMemcpyDeviceToHost, e->stream));
   HIP_OR_POISON(e, hipMemcpyAsync(h_flags, e->chain_flags, (size_t)n_steps * 4, hipMemcpyDeviceToHost, e->stream));
+  const size_t nlp = (size_t)n_steps * c.rows * (1 + kMaxLogprobs), nlpi = (size_t)n_steps * c.rows * kMaxLogprobs;
+  if (sample && lp_out)
+    HIP_OR_POISON(e, hipMemcpyAsync(e->h_lp, e->lp, nlp * 4, hipMemcpyDeviceToHost, e->stream));
+  if (sample && lp_ids_out)
+    HIP_OR_POISON(e, hipMemcpyAsync(e->h_lp + nlp, e->lp_ids, nlpi * 4, hipMemcpyDeviceToHost, e->stream));
   if (logits_host)
     HIP_OR_POISON(e, hipMemcpyAsync(logits_host, e->logits, (size_t)c.rows * c.vocab * 4, hipMemcpyDeviceToHost,
                                     e->stream));
@@ -1050,6 +1151,8 @@ static ds3_status run_steps(ds3_engine* e, const int32_t* tokens, const int32_t*
   const uint32_t errbits = e->h_status->err;
   if (ids_out) std::memcpy(ids_out, h_ids, (size_t)n_steps * c.rows * 4);
   if (flags_out) std::memcpy(flags_out, h_flags, (size_t)n_steps * 4);
+  if (sample && lp_out) std::memcpy(lp_out, e->h_lp, nlp * 4);
+  if (sample && lp_ids_out) std::memcpy(lp_ids_out, e->h_lp + nlp, nlpi * 4);
   e->stats.last_host_us =
       std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t_start).count();
   if (errbits) {
@@ -1177,6 +1280,53 @@ ds3_status ds3_prefill(ds3_engine* e, int32_t row, const int32_t* tokens, int32_
     return fail(e, DS3_E_KERNEL_CHECK, "in-kernel check failed during the prefill");
   }
   e->stats.prefill_tokens += n;
+  return DS3_OK;
+}
+
+ds3_status ds3_step_sample(ds3_engine* e, const int32_t* tokens, const int32_t* pos, int32_t n_steps, int32_t* ids,
+                           uint32_t* flags, float* logprobs, int32_t* logprob_ids) {
+  if (!ids) return fail(e, DS3_E_INVALID, "ids is NULL");
+  return run_steps(e, tokens, pos, nullptr, n_steps, nullptr, ids, flags, true, logprobs, logprob_ids);
+}
+
+ds3_status ds3_set_sampling(ds3_engine* e, int32_t row, const ds3_sampling* s) {
+  if (ds3_status st = refuse_if_unusable(e)) return st;
+  if (!s) return fail(e, DS3_E_INVALID, "sampling parameters are NULL");
+  if (row < 0 || row >= e->cfg.rows) return fail(e, DS3_E_INVALID, "row out of range");
+  if (!(s->temperature >= 0.f) || !(s->top_p > 0.f && s->top_p <= 1.f) || !(s->min_p >= 0.f && s->min_p < 1.f) ||
+      !(s->repetition_penalty > 0.f) || !std::isfinite(s->presence_penalty) || !std::isfinite(s->frequency_penalty) ||
+      s->top_k < 0 || s->n_logprobs < 0 || s->n_logprobs > DS3_MAX_LOGPROBS)
+    return fail(e, DS3_E_INVALID, "sampling parameter out of range");
+  e->h_samp[(size_t)row] = SampleRow{s->temperature, s->top_p, s->min_p, s->repetition_penalty, s->presence_penalty,
+                                     s->frequency_penalty, s->top_k, s->n_logprobs, (uint32_t)(s->seed & 0xffffffffu),
+                                     (uint32_t)(s->seed >> 32)};
+  // a new seed starts the row's generator over
+  HIP_OR_POISON(e, launch_fill_u32(e->draws + row, 0u, 1, e->stream));
+  HIP_OR_POISON(e, hipStreamSynchronize(e->stream));
+  return DS3_OK;
+}
+
+ds3_status ds3_set_history(ds3_engine* e, int32_t row, const int32_t* tokens, int32_t n, const float* bias) {
+  if (ds3_status st = refuse_if_unusable(e)) return st;
+  const ds3_config& c = e->cfg;
+  if (row < 0 || row >= c.rows) return fail(e, DS3_E_INVALID, "row out of range");
+  if (n < 0 || (n > 0 && !tokens)) return fail(e, DS3_E_INVALID, "tokens is NULL");
+  std::vector<int32_t> cnt((size_t)c.vocab, 0);
+  for (int i = 0; i < n; ++i) {
+    if (tokens[i] < 0 || tokens[i] >= c.vocab) return fail(e, DS3_E_INVALID, "token out of range at " + std::to_string(i));
+    cnt[(size_t)tokens[i]] += 1;
+  }
+  std::vector<float> b((size_t)c.vocab, 0.f);
+  if (bias)
+    for (int v = 0; v < c.vocab; ++v) {
+      if (!std::isfinite(bias[v])) return fail(e, DS3_E_INVALID, "bias must be finite");
+      b[(size_t)v] = bias[v];
+    }
+  HIP_OR_POISON(e, hipMemcpyAsync(e->counts + (size_t)row * c.vocab, cnt.data(), (size_t)c.vocab * 4,
+                                  hipMemcpyHostToDevice, e->stream));
+  HIP_OR_POISON(e, hipMemcpyAsync(e->bias + (size_t)row * c.vocab, b.data(), (size_t)c.vocab * 4,
+                                  hipMemcpyHostToDevice, e->stream));
+  HIP_OR_POISON(e, hipStreamSynchronize(e->stream));
   return DS3_OK;
 }
 
@@ -1413,6 +1563,10 @@ void ds3_destroy(ds3_engine* e) {
   }
   if (e->exec) (void)hipGraphExecDestroy(e->exec);
   if (e->graph) (void)hipGraphDestroy(e->graph);
+  if (e->samp_exec) (void)hipGraphExecDestroy(e->samp_exec);
+  if (e->samp_graph) (void)hipGraphDestroy(e->samp_graph);
+  if (e->h_samp_pinned) (void)hipHostFree(e->h_samp_pinned);
+  if (e->h_lp) (void)hipHostFree(e->h_lp);
   if (e->pre_exec) (void)hipGraphExecDestroy(e->pre_exec);
   if (e->pre_graph) (void)hipGraphDestroy(e->pre_graph);
   if (e->h_pre) (void)hipHostFree(e->h_pre);

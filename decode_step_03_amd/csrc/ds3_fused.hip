@@ -676,7 +676,7 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
         st_dev(opaque_p(p.part) + blockIdx.x, bv);
         st_dev(reinterpret_cast<unsigned*>(opaque_p(p.part)) + kFusedBlocks + blockIdx.x, (unsigned)bi);
       }
-      final_pick(p, gen0, lane, sm.flags);
+      if (p.slots[SlotLayout{1}.sample()] == 0) final_pick(p, gen0, lane, sm.flags);   // (else the sampler picks)
     }
     if constexpr (PH != PH_HEAD) {
       arrive_and_wait(p, gen0, kFusedPhases * layer + (PH == PH_QKV ? 0 : PH == PH_O ? 2 : PH == PH_GU ? 3 : 4), lane,

@@ -27,7 +27,8 @@ struct SlotLayout {
   __host__ __device__ int spin() const { return 3 * rows + 1; }   // fused kernel: barrier wait limit, 0 = default
   __host__ __device__ int chain() const { return 3 * rows + 2; }  // greedy pick: steps since the host wrote slots
   __host__ __device__ int sweep() const { return 3 * rows + 3; }  // 1: K/V chunks wholly after pos are not loaded
-  __host__ __device__ int words() const { return 3 * rows + 4; }
+  __host__ __device__ int sample() const { return 3 * rows + 4; } // 1: the sampler kernel picks (fused: no pick)
+  __host__ __device__ int words() const { return 3 * rows + 5; }
 };
 
 // Status words written by kernels and read back after every step.
@@ -114,6 +115,33 @@ struct PickParams {
   unsigned* done;          // finished-block counter (back to 0 after every launch)
   int32_t* ids;            // [max_chain][rows]
   uint32_t* flags;         // [max_chain]
+  int max_chain;
+  StatusWords* status;
+};
+
+// Sampling suffix (the sampler kernel; one block per row). Per-row parameters: temperature 0 is greedy; top_k 0,
+// top_p 1 and min_p 0 are off; penalties 1 / 0 / 0 are off.
+constexpr int kMaxLogprobs = 8;
+struct SampleRow {
+  float temperature, top_p, min_p, rep, presence, frequency;
+  int32_t top_k, n_logprobs;
+  uint32_t seed_lo, seed_hi;
+};
+struct SampleParams {
+  const float* logits;      // [rows][vocab]
+  int vocab, rows;
+  int32_t* slots;           // SlotLayout{rows}
+  const int* page_table;    // paged: [rows][cap / page_size]; else null
+  int page_size, cap;
+  const SampleRow* rowp;    // [rows]
+  int32_t* counts;          // [rows][vocab] token history (the draws add to it)
+  const float* bias;        // [rows][vocab] logit bias
+  uint32_t* draws;          // [rows] temperature draws so far (the generator's counter)
+  float* z;                 // [rows][vocab] scratch: adjusted logits
+  int32_t* ids;             // [max_chain][rows]
+  uint32_t* flags;          // [max_chain]
+  float* lp;                // [max_chain][rows][1 + kMaxLogprobs]: the drawn token's logprob, then the top-n
+  int32_t* lp_ids;          // [max_chain][rows][kMaxLogprobs]
   int max_chain;
   StatusWords* status;
 };
@@ -207,6 +235,7 @@ hipError_t launch_kv_copy(const KvView& kv, int kv_dtype, int layer, int row, in
                           void* staging, int to_state, StatusWords* status, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t s);
 hipError_t launch_pick(const PickParams& p, hipStream_t s);
+hipError_t launch_sample(const SampleParams& p, hipStream_t s);
 // Fused step kernel (ds3_fused.hip). fused_shape_supported: the model shape has a compiled instantiation.
 bool fused_shape_supported(int d, int ffn, int hd, int nq, int nkv);
 hipError_t launch_fused(const FusedParams& p, int d, int ffn, int hd, int nq, int nkv, bool trace, hipStream_t s);

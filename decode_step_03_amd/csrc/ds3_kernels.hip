@@ -1185,6 +1185,290 @@ __global__ void __launch_bounds__(kPickThreads) pick_kernel(PickParams p) {
 }
 
 // ----------------------------------------------------------------------------------------------------------
+// sampling suffix: one block of kSampleThreads per row, several passes over the row's adjusted logits (L2-resident)
+
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleWaves = kSampleThreads / 64;
+
+// float -> uint32 key in the same order (NaN never reaches here)
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// SplitMix64 output d from state `seed` (Steele, Lea and Flood 2014): the state advances by the golden gamma before
+// each output; an output is the state through two xor-shift-multiply rounds and a final xor-shift
+__device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t d) {
+  uint64_t z = seed + (d + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+struct SampleShared {
+  unsigned long long hist[256];
+  unsigned long long wsum[kSampleThreads];
+  float fv[kSampleWaves];
+  int fi[kSampleWaves];
+  unsigned long long bcast[2];
+};
+
+// block sum of one u64 per thread, fixed order (every thread gets it)
+__device__ __forceinline__ unsigned long long block_sum_u64(SampleShared& sh, unsigned long long x) {
+  sh.wsum[threadIdx.x] = x;
+  __syncthreads();
+  for (int m = kSampleThreads / 2; m >= 1; m >>= 1) {
+    if ((int)threadIdx.x < m) sh.wsum[threadIdx.x] += sh.wsum[threadIdx.x + m];
+    __syncthreads();
+  }
+  const unsigned long long t = sh.wsum[0];
+  __syncthreads();
+  return t;
+}
+
+// block (value, index) maximum in rank order (value descending, index ascending); every thread gets it
+__device__ __forceinline__ void block_best(SampleShared& sh, float& bv, int& bi) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float ov = __shfl_xor(bv, m, 64);
+    const int oi = __shfl_xor(bi, m, 64);
+    if (pick_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  if ((threadIdx.x & 63) == 0) { sh.fv[threadIdx.x >> 6] = bv; sh.fi[threadIdx.x >> 6] = bi; }
+  __syncthreads();
+  bv = sh.fv[0];
+  bi = sh.fi[0];
+  for (int w = 1; w < kSampleWaves; ++w)
+    if (pick_better(sh.fv[w], sh.fi[w], bv, bi)) { bv = sh.fv[w]; bi = sh.fi[w]; }
+  __syncthreads();
+}
+
+// Radix selection over the keys of the tokens `in(v)`, weight `wt(v)` each: the largest key K such that the total
+// weight of keys >= K reaches `target`. Returns K and the weight of keys > K (integer sums: the same on every run).
+template <class IN, class KEY, class WT>
+__device__ __forceinline__ void radix_select(SampleShared& sh, int V, IN&& in, KEY&& key, WT&& wt,
+                                             unsigned long long target, uint32_t& K, unsigned long long& above) {
+  uint32_t prefix = 0, pmask = 0;
+  unsigned long long ab = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int b = threadIdx.x; b < 256; b += kSampleThreads) sh.hist[b] = 0;
+    __syncthreads();
+    for (int v = threadIdx.x; v < V; v += kSampleThreads) {
+      if (!in(v)) continue;
+      const uint32_t k = key(v);
+      if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], wt(v));
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int b = 255;
+      for (; b > 0; --b) {
+        if (ab + sh.hist[b] >= target) break;
+        ab += sh.hist[b];
+      }
+      sh.bcast[0] = (unsigned long long)b;
+      sh.bcast[1] = ab;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sh.bcast[0] << shift;
+    pmask |= 255u << shift;
+    ab = sh.bcast[1];
+    __syncthreads();
+  }
+  K = prefix;
+  above = ab;
+}
+
+// In index order over the tokens `in(v)`: the first v whose running weight reaches `target` (>= 1). Each thread
+// sums a contiguous segment, the segment sums are scanned in order, and one thread walks its segment.
+template <class IN, class WT>
+__device__ __forceinline__ int index_scan(SampleShared& sh, int V, IN&& in, WT&& wt, unsigned long long target) {
+  const int seg = (V + kSampleThreads - 1) / kSampleThreads;
+  const int v0 = threadIdx.x * seg, v1 = min(V, v0 + seg);
+  unsigned long long t = 0;
+  for (int v = v0; v < v1; ++v)
+    if (in(v)) t += wt(v);
+  sh.wsum[threadIdx.x] = t;
+  if (threadIdx.x == 0) sh.bcast[0] = (unsigned long long)(V - 1);   // (past the total: the last token)
+  __syncthreads();
+  if (threadIdx.x == 0) {   // inclusive scan, in thread order
+    unsigned long long run = 0;
+    for (int i = 0; i < kSampleThreads; ++i) {
+      run += sh.wsum[i];
+      sh.wsum[i] = run;
+    }
+  }
+  __syncthreads();
+  const unsigned long long before = threadIdx.x ? sh.wsum[threadIdx.x - 1] : 0ull;
+  if (before < target && sh.wsum[threadIdx.x] >= target) {
+    unsigned long long run = before;
+    for (int v = v0; v < v1; ++v) {
+      if (!in(v)) continue;
+      run += wt(v);
+      if (run >= target) {
+        sh.bcast[0] = (unsigned long long)v;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  const int r = (int)sh.bcast[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) {
+  __shared__ SampleShared sh;
+  const int r = blockIdx.x, V = p.vocab, tid = threadIdx.x;
+  const SampleRow prm = p.rowp[r];
+  const float* lg = p.logits + (size_t)r * V;
+  int32_t* cnt = p.counts + (size_t)r * V;
+  const float* bias = p.bias + (size_t)r * V;
+  float* z = p.z + (size_t)r * V;
+
+  // ---- adjusted logits: repetition penalty on seen tokens (toward zero), presence and frequency, bias; NaN -> -inf
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int v = tid; v < V; v += kSampleThreads) {
+    float x = lg[v];
+    if (x != x) x = -INFINITY;
+    const int c = cnt[v];
+    if (c > 0) x = (x > 0.f ? x / prm.rep : x * prm.rep) - prm.presence - prm.frequency * (float)c;
+    x += bias[v];
+    if (x != x) x = -INFINITY;
+    z[v] = x;
+    if (pick_better(x, v, bv, bi)) { bv = x; bi = v; }
+  }
+  block_best(sh, bv, bi);
+  const float zmax = bv;
+  int token = bi < V ? bi : 0;
+  const float T = prm.temperature;
+  const float inv_t = T > 0.f ? 1.f / T : 1.f;
+
+  if (T > 0.f && zmax > -INFINITY) {
+    auto key = [&](int v) { return order_key(z[v] * inv_t); };
+    const float smax = zmax * inv_t;
+    // weight of a token: exp(s - s_max) in fixed point (2^40 = the top token)
+    auto wt = [&](int v) -> unsigned long long {
+      const float w = __expf(z[v] * inv_t - smax);
+      return (unsigned long long)(w * 1099511627776.f);
+    };
+    auto one = [&](int) -> unsigned long long { return 1ull; };
+    auto all = [&](int) { return true; };
+    // top-k: the k best ranked (ties at the threshold key by lower index)
+    uint32_t kk = 0u;
+    int ki = V;
+    if (prm.top_k > 0 && prm.top_k < V) {
+      unsigned long long above = 0;
+      radix_select(sh, V, all, key, one, (unsigned long long)prm.top_k, kk, above);
+      const uint32_t K = kk;
+      ki = index_scan(sh, V, [&](int v) { return key(v) == K; }, one, (unsigned long long)prm.top_k - above);
+    }
+    const uint32_t K1 = kk;
+    const int I1 = ki;
+    auto in_k = [&](int v) { const uint32_t k = key(v); return k > K1 || (k == K1 && v <= I1); };
+    // top-p: the shortest ranked prefix of the top-k set whose weight reaches p of its total
+    uint32_t kp = 0u;
+    int ip = V;
+    if (prm.top_p < 1.f) {
+      unsigned long long tw = 0;
+      for (int v = tid; v < V; v += kSampleThreads)
+        if (in_k(v)) tw += wt(v);
+      tw = block_sum_u64(sh, tw);
+      unsigned long long target = (unsigned long long)((double)prm.top_p * (double)tw);
+      if (target < 1) target = 1;
+      unsigned long long above = 0;
+      radix_select(sh, V, in_k, key, wt, target, kp, above);
+      const uint32_t K = kp;
+      ip = index_scan(sh, V, [&](int v) { return in_k(v) && key(v) == K; }, wt, target - above);
+    }
+    const uint32_t K2 = kp;
+    const int I2 = ip;
+    // min-p: weight at least min_p of the top token's
+    const float lmin = prm.min_p > 0.f ? __logf(prm.min_p) : -INFINITY;
+    auto kept = [&](int v) {
+      if (!in_k(v)) return false;
+      const uint32_t k = key(v);
+      if (!(k > K2 || (k == K2 && v <= I2))) return false;
+      return z[v] * inv_t - smax >= lmin;
+    };
+    // the draw: inverse CDF in index order over the kept weights
+    unsigned long long tw = 0;
+    for (int v = tid; v < V; v += kSampleThreads)
+      if (kept(v)) tw += wt(v);
+    tw = block_sum_u64(sh, tw);
+    const uint64_t seed = ((uint64_t)prm.seed_hi << 32) | prm.seed_lo;
+    const uint32_t d = p.draws[r];
+    const double u = (double)(splitmix64(seed, d) >> 40) * (1.0 / 16777216.0);
+    unsigned long long target = (unsigned long long)(u * (double)tw) + 1ull;
+    if (target > tw) target = tw;
+    if (tw > 0) token = index_scan(sh, V, kept, wt, target);
+    if (tid == 0) p.draws[r] = d + 1u;
+  }
+
+  // ---- logprobs of the adjusted distribution (temperature 1 for greedy): the drawn token's and the top n by rank
+  const SlotLayout sl{p.rows};
+  const int step = p.slots[sl.chain()];
+  const int slot = step % p.max_chain;
+  float* lpo = p.lp + ((size_t)slot * p.rows + r) * (1 + kMaxLogprobs);
+  int32_t* lpi = p.lp_ids + ((size_t)slot * p.rows + r) * kMaxLogprobs;
+  const int nl = min(max(prm.n_logprobs, 0), kMaxLogprobs);
+  if (nl > 0) {
+    const float smax = zmax * inv_t;
+    float t = 0.f;
+    for (int v = tid; v < V; v += kSampleThreads) t += __expf(z[v] * inv_t - smax);
+    for (int m = 32; m >= 1; m >>= 1) t += __shfl_xor(t, m, 64);
+    if ((tid & 63) == 0) sh.fv[tid >> 6] = t;
+    __syncthreads();
+    float tot = 0.f;
+    for (int w = 0; w < kSampleWaves; ++w) tot += sh.fv[w];
+    __syncthreads();
+    const float lse = smax + __logf(tot);
+    // top n by rank: n rounds, each the best token ranked below the previous round's
+    float pv = INFINITY;
+    int pi = -1;
+    for (int j = 0; j < nl; ++j) {
+      float cv = -INFINITY;
+      int ci = 0x7fffffff;
+      for (int v = tid; v < V; v += kSampleThreads) {
+        const float x = z[v] * inv_t;
+        const bool below = x < pv || (x == pv && v > pi);
+        if (below && pick_better(x, v, cv, ci)) { cv = x; ci = v; }
+      }
+      block_best(sh, cv, ci);
+      if (tid == 0) {
+        lpi[j] = ci < V ? ci : -1;
+        lpo[1 + j] = cv - lse;
+      }
+      pv = cv;
+      pi = ci;
+    }
+    if (tid == 0) lpo[0] = z[token] * inv_t - lse;
+  }
+
+  // ---- the draw into the history and the slots; the chain record
+  if (tid == 0) {
+    cnt[token] += 1;
+    p.ids[(size_t)slot * p.rows + r] = token;
+    const int np = p.slots[sl.pos() + r] + 1;
+    p.slots[sl.token() + r] = token;
+    p.slots[sl.pos() + r] = np;
+    if (p.page_table && np >= 0 && np < p.cap) {
+      const int ppr = p.cap / p.page_size;
+      p.slots[sl.write_map() + r] = p.page_table[(size_t)r * ppr + np / p.page_size] * p.page_size + np % p.page_size;
+    }
+  }
+}
+
+// after every row's sampler: the step's non-finite flag and the chain counter (one thread)
+__global__ void sample_close_kernel(SampleParams p) {
+  const SlotLayout sl{p.rows};
+  const int step = p.slots[sl.chain()];
+  p.flags[step % p.max_chain] = p.status->nonfinite ? 1u : 0u;
+  p.status->nonfinite = 0;
+  p.slots[sl.chain()] = step + 1;
+}
+
+// ----------------------------------------------------------------------------------------------------------
 // host launchers
 
 size_t gemv_lds_bytes(int rows, int K, bool norm) { (void)norm; return (size_t)rows * K * sizeof(float); }
@@ -1400,6 +1684,15 @@ hipError_t launch_kv_copy(const KvView& kv, int kv_dtype, int layer, int row, in
 hipError_t launch_pick(const PickParams& p, hipStream_t s) {
   if (p.rows < 1 || p.rows > kPickThreads || p.vocab < 1 || p.max_chain < 1) return hipErrorInvalidValue;
   pick_kernel<<<p.rows * kPickSplit, kPickThreads, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample(const SampleParams& p, hipStream_t s) {
+  if (p.rows < 1 || p.vocab < 1 || p.max_chain < 1) return hipErrorInvalidValue;
+  sample_kernel<<<p.rows, kSampleThreads, 0, s>>>(p);
+  hipError_t h = hipGetLastError();
+  if (h != hipSuccess) return h;
+  sample_close_kernel<<<1, 1, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -103,6 +103,32 @@ class Engine:
         flags = C.ds3_prefill(self.handle, row, toks.ctypes.data, pos0, toks.size, out.ctypes.data)
         return out, flags
 
+    def set_sampling(self, row: int, *, temperature=0.0, top_k=0, top_p=1.0, min_p=0.0, repetition_penalty=1.0,
+                     presence_penalty=0.0, frequency_penalty=0.0, n_logprobs=0, seed=0) -> None:
+        C.ds3_set_sampling(self.handle, row, C.ds3_sampling(temperature, top_p, min_p, repetition_penalty,
+                                                            presence_penalty, frequency_penalty, top_k, n_logprobs,
+                                                            seed))
+
+    def set_history(self, row: int, tokens=(), bias=None) -> None:
+        toks = np.ascontiguousarray(np.asarray(tokens, np.int32))
+        b = None if bias is None else np.ascontiguousarray(np.asarray(bias, np.float32))
+        C.ds3_set_history(self.handle, row, toks.ctypes.data if toks.size else None, toks.size,
+                          None if b is None else b.ctypes.data)
+
+    def step_sample(self, tokens, pos, n_steps: int):
+        """n_steps chained steps, each row's token drawn by the sampling suffix. Returns (ids [n, rows], flags [n],
+        logprobs [n, rows, 1 + 8] (drawn token's, then top n), logprob ids [n, rows, 8])."""
+        self._tok[:] = tokens
+        self._pos[:] = pos
+        R = self.cfg.rows
+        ids = np.empty((n_steps, R), np.int32)
+        flags = np.empty(n_steps, np.uint32)
+        lp = np.empty((n_steps, R, 1 + C.DS3_MAX_LOGPROBS), np.float32)
+        lpi = np.empty((n_steps, R, C.DS3_MAX_LOGPROBS), np.int32)
+        C.ds3_step_sample(self.handle, self._tok.ctypes.data, self._pos.ctypes.data, n_steps, ids.ctypes.data,
+                          flags.ctypes.data, lp.ctypes.data, lpi.ctypes.data)
+        return ids, flags, lp, lpi
+
     def set_kv_sweep(self, mode: str) -> None:
         """"full" (the method: every position of [cap] is loaded) or "visible" (chunks wholly after pos are skipped;
         outputs bit-identical)."""

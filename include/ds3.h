@@ -204,6 +204,49 @@ ds3_status ds3_step(ds3_engine* e, const int32_t* tokens, const int32_t* pos, co
 ds3_status ds3_step_greedy(ds3_engine* e, const int32_t* tokens, const int32_t* pos, int32_t n_steps,
                            int32_t* ids, uint32_t* flags);
 
+/* Sampling suffix ("Models, Registry and the Driver" page, section "The Driver", item "The sampling suffix": every
+ * sampling rule runs on the device, appended to the decode graph, with penalties and a logit bias read from a
+ * per-sequence token history the device keeps and updates with every token it draws; the host reads back the
+ * token id, a non-finite flag and, when asked, the top-n logprobs). The pages give no formulas; the readings:
+ *   adjusted logits z_v = r(l_v) - presence * [c_v > 0] - frequency * c_v + bias_v, with c_v the row's history count
+ *   of token v and r(x) = x / repetition_penalty if x > 0 else x * repetition_penalty when c_v > 0, r(x) = x
+ *   otherwise (a NaN logit counts as -inf);
+ *   temperature 0: greedy (first index of the largest z). Temperature T > 0: s = z / T, tokens ranked by (s
+ *   descending, index ascending); top_k keeps the k best ranked (0: all); top_p keeps the shortest ranked prefix of
+ *   those whose softmax(s) mass reaches top_p (1: all); min_p keeps the tokens whose probability is at least min_p
+ *   times the top token's (0: all); the token is drawn by inverse CDF in index order over the kept weights, with
+ *   u = the top 24 bits of output d of SplitMix64 seeded with `seed` (d = the row's draw count, reset to 0 by
+ *   ds3_set_sampling) times 2^-24. Weights are exp(s - s_max) in 2^-40 fixed point, so the cuts are exact integer
+ *   decisions on the device;
+ *   logprobs: log-softmax of s (T = 1 for greedy) over every token: the drawn token's, then the top n by rank. */
+#define DS3_MAX_LOGPROBS 8
+typedef struct {
+  float temperature;         /* >= 0; 0 = greedy */
+  float top_p;               /* (0, 1]; 1 = off */
+  float min_p;               /* [0, 1); 0 = off */
+  float repetition_penalty;  /* > 0; 1 = off */
+  float presence_penalty;    /* 0 = off */
+  float frequency_penalty;   /* 0 = off */
+  int32_t top_k;             /* >= 0; 0 = off */
+  int32_t n_logprobs;        /* 0 .. DS3_MAX_LOGPROBS */
+  uint64_t seed;
+} ds3_sampling;
+
+/* Row `row`'s sampling parameters for the following ds3_step_sample calls (default: greedy, no penalties); resets
+ * the row's draw count. DS3_E_INVALID for a parameter out of range. */
+ds3_status ds3_set_sampling(ds3_engine* e, int32_t row, const ds3_sampling* params);
+
+/* Seed row `row`'s history: the counts of `tokens` (host int32 [n], e.g. the prompt) and the logit bias (host
+ * float32 [vocab], NULL = none). The sampler adds each token it draws to the counts. */
+ds3_status ds3_set_history(ds3_engine* e, int32_t row, const int32_t* tokens, int32_t n, const float* bias);
+
+/* As ds3_step_greedy (n_steps chained steps, one host wait), with each row's token drawn by the sampling suffix.
+ * logprobs (host float32 [n_steps][rows][1 + DS3_MAX_LOGPROBS], may be NULL): the drawn token's logprob, then the
+ * top n_logprobs; logprob_ids (host int32 [n_steps][rows][DS3_MAX_LOGPROBS], may be NULL): their token ids. Slots
+ * beyond a row's n_logprobs are unspecified. */
+ds3_status ds3_step_sample(ds3_engine* e, const int32_t* tokens, const int32_t* pos, int32_t n_steps, int32_t* ids,
+                           uint32_t* flags, float* logprobs, int32_t* logprob_ids);
+
 /* Prefill (the step before decode): n tokens of one row at positions pos0 .. pos0 + n - 1, with their K/V written
  * into that row's state ("Models, Registry and the Driver" page, section "The Model": a prefill is a step that
  * continues from a position, in chunks). The tokens go prefill_rows at a time through one launch sequence (one
