@@ -32,24 +32,26 @@ size_t dtype_bytes(int dt) { return dt == DS3_BF16 ? 2 : 4; }
 struct WorkPlan {
   size_t slots, status, x, q, attn, act, part, pre_slots, pre_logits, kvnew, sync, clocks, trace, pick_val, pick_idx,
       pick_done, ids, chain_flags, samp_rows, counts, bias, draws, zbuf, lp, lp_ids, rope, slot_map, frag_hi, frag_lo,
-      total;
+      skpart, skss, total;
 };
 
 struct KernelKind {
   const char* name;
 };
 enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN, K_HEAD, K_SPLIT, K_COMBINE, K_FUSED, K_PICK, K_SAMPLE,
-            K_NUM };
+            K_QKVFIN, K_SWIGLU, K_NUM };
 const char* kKindNames[K_NUM] = {"embed", "qkv_rope_kvwrite", "attention_splitk", "o_proj_residual",
-                                 "gateup_swiglu", "down_proj_residual", "lm_head", "act_split_mfma",
-                                 "attention_combine", "decode_step_fused", "greedy_pick", "sampler"};
+                                 "gateup_swiglu", "down_proj_residual", "lm_head", "norm_prep_mfma",
+                                 "attention_combine", "decode_step_fused", "greedy_pick", "sampler",
+                                 "qkv_epilogue_mfma", "swiglu_split_mfma"};
 constexpr int kMaxChain = DS3_MAX_CHAIN;   // steps of one ds3_step_greedy call
 constexpr int kMaxPrefill = DS3_MAX_PREFILL;   // tokens of one ds3_prefill call
 // fused plan: the operation kind of phase k of a layer (the grid barrier after it closes the phase)
 const int kPhaseKind[kFusedPhases] = {K_QKV, K_ATTN, K_OPROJ, K_GATEUP, K_DOWN};
 
-// activation sites the MFMA path splits into bf16 hi/lo operands
-enum Site { S_ATTN_NORM = 0, S_ATTN_OUT, S_FFN_NORM, S_ACT, S_FINAL_NORM };
+// RMSNorm sites of the MFMA path: a prep kernel adds the producing projection's partial products into x, writes
+// the per-block sums of squares and the fragments of gain * x
+enum Site { S_ATTN_NORM = 0, S_FFN_NORM, S_FINAL_NORM };
 
 struct Launch {
   int kind;
@@ -73,6 +75,7 @@ struct ds3_engine {
   int* slot_map = nullptr;
   float* logits = nullptr;
   uint16_t *frag_hi = nullptr, *frag_lo = nullptr;   // MFMA path: activation operands
+  float *skpart = nullptr, *skss = nullptr;          // MFMA path: partial products, per-block sums of squares
   bool mfma = false;                                 // rows > 4: projections on the matrix cores
   bool fused = false;                                // the whole step as one persistent kernel
   float* kvnew = nullptr;                            // fused: this step's k and v [nkv][2][hd]
@@ -263,8 +266,14 @@ std::string check_config(const ds3_config* c) {
     } else {
       // matrix-core path: bf16 weights in whole 16-row tiles and 32-input steps
       if (c->weight_dtype != DS3_BF16) return std::string(what) + ": more than 4 rows needs bf16 weights (matrix-core path)";
-      if (c->d_model % 32 || c->ffn_dim % 32 || c->head_dim % 32 || c->vocab % 32)
-        return "d_model, ffn_dim, head_dim and vocab must be multiples of 32 for more than 4 rows";
+      if (c->d_model % kSkChunk || c->ffn_dim % kSkChunk || (c->n_q_heads * c->head_dim) % kSkChunk)
+        return "d_model, ffn_dim and n_q_heads x head_dim must be multiples of 128 for more than 4 rows";
+      if (c->head_dim % 32 || c->vocab % 32) return "head_dim and vocab must be multiples of 32 for more than 4 rows";
+      const int qkv = (c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim, qw = c->n_q_heads * c->head_dim;
+      if (!sk_plan(qkv, c->d_model, false).groups || !sk_plan(c->d_model, qw, false).groups ||
+          !sk_plan(2 * c->ffn_dim, c->d_model, false).groups || !sk_plan(c->d_model, c->ffn_dim, false).groups ||
+          !sk_plan(c->vocab, c->d_model, true).groups)
+        return "the projection shapes are outside what the matrix-core kernels take for more than 4 rows";
     }
   }
   return "";
@@ -333,6 +342,15 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
   const size_t frag = RA > (size_t)kMaxGemvRows ? kmax * kMfmaRows * 2 : 16;
   w.frag_hi = take(frag);
   w.frag_lo = take(frag);
+  size_t skp = 4;
+  if (RA > (size_t)kMaxGemvRows) {
+    const int qkv = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim, qw = c.n_q_heads * c.head_dim;
+    for (const SkPlan& sp : {sk_plan(qkv, c.d_model, false), sk_plan(c.d_model, qw, false),
+                             sk_plan(2 * c.ffn_dim, c.d_model, false), sk_plan(c.d_model, c.ffn_dim, false)})
+      skp = std::max(skp, sk_partial_floats(sp) * 4);
+  }
+  w.skpart = take(skp);
+  w.skss = take((size_t)((c.d_model + kPrepSpan - 1) / kPrepSpan) * kMfmaRows * 4);
   w.total = off;
   return w;
 }
@@ -430,20 +448,38 @@ ds3_status wait_done(ds3_engine* e, hipEvent_t ev, uint32_t timeout_ms) {
   }
 }
 
-// One projection: the paired-row GEMV for up to 4 rows, the MFMA tile GEMM (on the split activations) beyond.
+// One projection: the paired-row GEMV for up to 4 rows; beyond, the matrix-core GEMM on the activation fragments,
+// which leaves partial products for the next kernel (the LM head writes the logits itself).
 hipError_t run_projection(ds3_engine* e, const GemvParams& p, int mode, int kind) {
   const ds3_config& c = e->cfg;
   if (!e->cur.mfma) return launch_gemv(p, mode, c.weight_dtype, c.kv_dtype, e->blocks[kind], e->stream);
-  MfmaParams mp{};
-  mp.g = p;
-  mp.hi = e->frag_hi;
-  mp.lo = e->frag_lo;
-  switch (mode) {
-    case GEMV_QKV: mp.n_units = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim / 32; break;
-    case GEMV_GATEUP: mp.n_units = c.ffn_dim / 16; break;
-    default: mp.n_units = 2 * p.n_pairs / 32; break;
+  const bool head = mode == GEMV_HEAD;
+  SkGemmParams g{};
+  g.w = reinterpret_cast<const uint16_t*>(p.w);
+  g.hi = e->frag_hi;
+  g.lo = e->frag_lo;
+  g.K = p.K;
+  g.plan = sk_plan(2 * p.n_pairs, p.K, head);
+  g.part = e->skpart;
+  g.out = p.out;
+  g.rows = p.rows;
+  g.n_out = 2 * p.n_pairs;
+  g.ss = e->skss;
+  g.ss_blocks = (c.d_model + kPrepSpan - 1) / kPrepSpan;
+  g.norm_dim = c.d_model;
+  g.eps = c.rms_eps;
+  g.status = e->status;
+  return launch_sk_gemm(g, head, e->stream);
+}
+
+// the plans of the matrix-core projections whose partial products a consumer kernel sums
+SkPlan plan_of(const ds3_config& c, int kind) {
+  switch (kind) {
+    case K_QKV: return sk_plan((c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim, c.d_model, false);
+    case K_OPROJ: return sk_plan(c.d_model, c.n_q_heads * c.head_dim, false);
+    case K_GATEUP: return sk_plan(2 * c.ffn_dim, c.d_model, false);
+    default: return sk_plan(c.d_model, c.ffn_dim, false);   // K_DOWN
   }
-  return launch_gemm_mfma(mp, mode, c.kv_dtype, e->stream);
 }
 
 hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
@@ -509,20 +545,53 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       return launch_fused(p, c.d_model, c.ffn_dim, c.head_dim, c.n_q_heads, c.n_kv_heads, trace, e->stream);
     }
     case K_SPLIT: {
-      SplitParams sp{};
-      sp.hi = e->frag_hi;
-      sp.lo = e->frag_lo;
-      sp.rows = R;
-      sp.eps = c.rms_eps;
-      bool norm = true;
-      switch (l.site) {
-        case S_ATTN_NORM: sp.in = e->x; sp.gain = e->L[l.layer].attn_norm; sp.K = c.d_model; break;
-        case S_FFN_NORM: sp.in = e->x; sp.gain = e->L[l.layer].ffn_norm; sp.K = c.d_model; break;
-        case S_FINAL_NORM: sp.in = e->x; sp.gain = e->final_norm; sp.K = c.d_model; break;
-        case S_ATTN_OUT: sp.in = e->attn; sp.K = c.n_q_heads * c.head_dim; norm = false; break;
-        default: sp.in = e->act; sp.K = c.ffn_dim; norm = false; break;
-      }
-      return launch_split(sp, norm, e->stream);
+      // x (+)= the o-proj (before the FFN norm) or down (before the next layer or the final norm) partials
+      SkPrepParams pp{};
+      pp.x = e->x;
+      pp.part = (l.site == S_ATTN_NORM && l.layer == 0) ? nullptr : e->skpart;
+      pp.plan = plan_of(c, l.site == S_FFN_NORM ? K_OPROJ : K_DOWN);
+      pp.gain = l.site == S_ATTN_NORM ? e->L[l.layer].attn_norm
+                                      : (l.site == S_FFN_NORM ? e->L[l.layer].ffn_norm : e->final_norm);
+      pp.hi = e->frag_hi;
+      pp.lo = e->frag_lo;
+      pp.ss = e->skss;
+      pp.D = c.d_model;
+      pp.rows = R;
+      return launch_sk_prep(pp, e->stream);
+    }
+    case K_QKVFIN: {
+      SkQkvParams qp{};
+      qp.part = e->skpart;
+      qp.plan = plan_of(c, K_QKV);
+      qp.ss = e->skss;
+      qp.ss_blocks = (c.d_model + kPrepSpan - 1) / kPrepSpan;
+      qp.D = c.d_model;
+      qp.eps = c.rms_eps;
+      qp.q = e->q;
+      qp.nq = c.n_q_heads;
+      qp.nkv = c.n_kv_heads;
+      qp.hd = c.head_dim;
+      qp.rope = e->rope;
+      qp.kv = kv;
+      qp.layer = l.layer;
+      qp.slots = e->cur.slots;
+      qp.status = e->status;
+      qp.rows = R;
+      return launch_sk_qkv(qp, c.kv_dtype, e->stream);
+    }
+    case K_SWIGLU: {
+      SkActParams ap{};
+      ap.part = e->skpart;
+      ap.plan = plan_of(c, K_GATEUP);
+      ap.ss = e->skss;
+      ap.ss_blocks = (c.d_model + kPrepSpan - 1) / kPrepSpan;
+      ap.D = c.d_model;
+      ap.eps = c.rms_eps;
+      ap.F = c.ffn_dim;
+      ap.rows = R;
+      ap.hi = e->frag_hi;
+      ap.lo = e->frag_lo;
+      return launch_sk_swiglu(ap, e->stream);
     }
     case K_SAMPLE: {
       SampleParams p{};
@@ -596,6 +665,10 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.scale = (float)(1.0 / std::sqrt((double)c.head_dim));
       p.slots = e->cur.slots;
       p.status = e->status;
+      if (e->cur.mfma) {   // the combine also writes the o-projection's fragments
+        p.frag_hi = e->frag_hi;
+        p.frag_lo = e->frag_lo;
+      }
       return l.kind == K_ATTN ? launch_attention(p, c.kv_dtype, R, e->stream)
                               : launch_attention_combine(p, R, e->stream);
     }
@@ -764,6 +837,8 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   e->sync_words = fused_sync_words(c.n_layers, c.n_kv_heads);
   e->frag_hi = reinterpret_cast<uint16_t*>(work + wp.frag_hi);
   e->frag_lo = reinterpret_cast<uint16_t*>(work + wp.frag_lo);
+  e->skpart = reinterpret_cast<float*>(work + wp.skpart);
+  e->skss = reinterpret_cast<float*>(work + wp.skss);
   e->mfma = c.rows > kMaxGemvRows;
   e->work_bytes = wp.total;
   e->logits = reinterpret_cast<float*>(e->buf[DS3_BUF_LOGITS]);
@@ -822,13 +897,13 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
     for (int l = 0; l < c.n_layers; ++l) {
       if (mfma) seq.push_back({K_SPLIT, l, S_ATTN_NORM});
       seq.push_back({K_QKV, l, 0});
+      if (mfma) seq.push_back({K_QKVFIN, l, 0});
       seq.push_back({K_ATTN, l, 0});
       seq.push_back({K_COMBINE, l, 0});
-      if (mfma) seq.push_back({K_SPLIT, l, S_ATTN_OUT});
       seq.push_back({K_OPROJ, l, 0});
       if (mfma) seq.push_back({K_SPLIT, l, S_FFN_NORM});
       seq.push_back({K_GATEUP, l, 0});
-      if (mfma) seq.push_back({K_SPLIT, l, S_ACT});
+      if (mfma) seq.push_back({K_SWIGLU, l, 0});
       seq.push_back({K_DOWN, l, 0});
     }
     if (mfma) seq.push_back({K_SPLIT, -1, S_FINAL_NORM});

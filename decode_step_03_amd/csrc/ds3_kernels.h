@@ -94,6 +94,8 @@ struct AttnParams {
   float scale;           // 1/sqrt(hd)
   const int* slots;
   StatusWords* status;
+  uint16_t* frag_hi;     // combine, matrix-core path: also the o-projection's activation fragments (else null)
+  uint16_t* frag_lo;
 };
 
 // Greedy pick after the LM head ("Execution" page, section "A constant-shape decode graph": the step's output
@@ -156,28 +158,97 @@ struct EmbedParams {
 
 // MFMA path (5..16 rows): activations are handed to the matrix cores as two bf16 parts, hi = bf16(a) and
 // lo = bf16(a - hi), stored in the operand order of v_mfma_f32_16x16x32_bf16 (step t of 32 inputs, lane l holds
-// inputs 32t + 8(l/16) .. +8 of activation row l % 16).
-struct SplitParams {
-  const float* in;       // [rows][K] fp32
-  const float* gain;     // RMSNorm gain [K] (norm only)
-  uint16_t* hi;          // [K/32][64][8] bf16
-  uint16_t* lo;
-  int K;
-  int rows;
-  float eps;
-};
+// inputs 32t + 8(l/16) .. +8 of activation row l % 16), the "fragments" [K/32][64][8]. Rows past the step's rows
+// are zero. The kernel that produces an activation writes its fragments.
 
 constexpr int kMaxGemvRows = 4;
 constexpr int kMaxRows = 16;
 constexpr int kMfmaRows = 16;   // activation rows of one MFMA tile (rows are zero-padded to it)
 
-// The same GEMM contract as GemvParams, for the MFMA path: `hi`/`lo` replace `in`/`gain` (the RMSNorm scale and
-// gain are already applied by the split kernel).
-struct MfmaParams {
-  GemvParams g;
-  const uint16_t* hi;
+// Matrix-core projection plan (stream-K). The weight matrix [N][K] is cut into items (group of kSkRows rows, chunk
+// of kSkChunk inputs), numbered group-major; wave w of the launch streams items [first(w), first(w + 1)), an equal
+// share whatever N and K. A block sums its waves' products per group (wave order) and stores one partial product
+// per group it touched: part[group][k][tile 0/1][lane 64][4] fp32, k = block - block_of(first item of the group)
+// (the MFMA output layout: lane l, element e is weight row 16 tile + 4 (l / 16) + e of the group and activation
+// row l % 16). The kernel that consumes the projection sums a group's k = 0, 1, ... in order, which is input order.
+constexpr int kSkRows = 32;        // weight rows per group (two 16-row tiles)
+constexpr int kSkChunk = 128;      // inputs per chunk
+constexpr int kSkWaves = 4;        // waves per block (one block per CU: its LDS takes 120 KB)
+constexpr int kSkMaxBlocks = 256;
+constexpr int kSkWaveSlots = 3;    // most groups one wave's run may touch
+constexpr int kPrepSpan = 512;     // consumer kernels: inputs per block (one wave, 8 per lane)
+struct SkPlan {
+  int groups;   // N / kSkRows
+  int nck;      // K / kSkChunk
+  int nw;       // waves with work (every one has at least one item, or one group with whole groups)
+  int cmax;     // most blocks that contribute to one group
+  __host__ __device__ unsigned total() const { return (unsigned)groups * (unsigned)nck; }
+  __host__ __device__ int first(int w) const { return (int)(total() * (unsigned)w / (unsigned)nw); }
+  // the wave, and the block, whose run holds item i (total x nw < 2^32: sk_plan checks it)
+  __host__ __device__ int wave_of(int i) const { return (int)(((unsigned)(i + 1) * (unsigned)nw - 1) / total()); }
+  __host__ __device__ int block_of(int i) const { return wave_of(i) / kSkWaves; }
+};
+// whole_groups: each wave takes whole groups (the LM head, whose epilogue writes the logits itself).
+// Returns a plan with groups == 0 if the shape is outside what the kernels take.
+SkPlan sk_plan(int n_rows, int K, bool whole_groups);
+inline size_t sk_partial_floats(const SkPlan& p) { return (size_t)p.groups * p.cmax * 512; }
+
+struct SkGemmParams {
+  const uint16_t* w;     // [N][K] bf16
+  const uint16_t* hi;    // activation fragments [K/32][64][8]
   const uint16_t* lo;
-  int n_units;           // pairs of 16-row weight tiles
+  int K;
+  SkPlan plan;
+  float* part;           // partial products (see SkPlan)
+  // LM head (whole groups): logits[r][n] = scale_r * sum, scale_r from the final norm's sums of squares
+  float* out;
+  int rows, n_out;
+  const float* ss;       // [ss_blocks][16] per-block sums of squares of x
+  int ss_blocks, norm_dim;
+  float eps;
+  StatusWords* status;
+};
+
+// x (+)= the partial products of the projection that produced it (part null: x as it is); per block and row the
+// sum of squares of x into ss; the fragments of gain * x. The RMSNorm's row scale is applied by the consumer.
+struct SkPrepParams {
+  float* x;              // [rows][D]
+  const float* part;
+  SkPlan plan;
+  const float* gain;     // [D]
+  uint16_t* hi;
+  uint16_t* lo;
+  float* ss;             // [ceil(D / kPrepSpan)][16]
+  int D, rows;
+};
+
+// QKV epilogue on the partial products: scale, rotary on q and k, q out, k and v stored at Slot::Pos / WriteMap.
+struct SkQkvParams {
+  const float* part;
+  SkPlan plan;
+  const float* ss;
+  int ss_blocks, D;
+  float eps;
+  float* q;              // [rows][nq][hd]
+  int nq, nkv, hd;
+  const float* rope;     // [cap][hd/2][2]
+  KvView kv;
+  int layer;
+  const int* slots;
+  StatusWords* status;
+  int rows;
+};
+
+// SwiGLU on the partial products (gate rows 0..F-1, up rows F..2F-1): fragments of silu(gate) * up.
+struct SkActParams {
+  const float* part;
+  SkPlan plan;
+  const float* ss;
+  int ss_blocks, D;
+  float eps;
+  int F, rows;
+  uint16_t* hi;
+  uint16_t* lo;
 };
 
 // Fused step kernel (batch 1): the whole step as one persistent launch of kFusedBlocks blocks (one per CU),
@@ -225,8 +296,10 @@ constexpr int kSyncArrive = 256, kSyncRelease = 512, kSyncSplit = 1024;
 inline size_t fused_sync_words(int n_layers, int nkv) { (void)n_layers; return (size_t)kSyncSplit + 32 * (size_t)nkv; }
 
 // Host launchers (defined in ds3_kernels.hip). Each returns the launch error, if any.
-hipError_t launch_split(const SplitParams& p, bool norm, hipStream_t s);
-hipError_t launch_gemm_mfma(const MfmaParams& p, int mode, int kv_dtype, hipStream_t s);
+hipError_t launch_sk_gemm(const SkGemmParams& p, bool head, hipStream_t s);
+hipError_t launch_sk_prep(const SkPrepParams& p, hipStream_t s);
+hipError_t launch_sk_qkv(const SkQkvParams& p, int kv_dtype, hipStream_t s);
+hipError_t launch_sk_swiglu(const SkActParams& p, hipStream_t s);
 hipError_t launch_embed(const EmbedParams& p, int weight_dtype, hipStream_t s);
 hipError_t launch_gemv(const GemvParams& p, int mode, int weight_dtype, int kv_dtype, int blocks, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, int kv_dtype, int rows, hipStream_t s);

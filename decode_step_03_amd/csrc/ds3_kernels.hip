@@ -30,6 +30,16 @@ constexpr int kMaxSplits = 32;          // attention: splits per (row, kv head),
 constexpr int kAttnChunk = 128;         // attention: positions staged in LDS per chunk, at most ...
 constexpr int kAttnChunkBytes = 32768;  // ... and at most this many bytes of K (and of V)
 
+// 8 values of activation row r from input k0 -> hi/lo fragment words
+__device__ __forceinline__ void store_frag8(uint16_t* hi, uint16_t* lo, int r, int k0, const float (&v)[8]) {
+  bf16x8 h, l;
+  split_hi_lo8(v, h, l);
+  const size_t idx = ((size_t)(k0 >> 5) * 64 + ((k0 >> 3) & 3) * 16 + r) * 8;
+  *reinterpret_cast<bf16x8*>(hi + idx) = h;
+  *reinterpret_cast<bf16x8*>(lo + idx) = l;
+}
+
+
 // ----------------------------------------------------------------------------------------------------------
 // embedding
 
@@ -369,177 +379,248 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
 }
 
 // ----------------------------------------------------------------------------------------------------------
-// MFMA path for 5..16 rows (batched decode). Each weight element now feeds up to 16 products, which is matrix
-// work: v_mfma_f32_16x16x32_bf16 multiplies a 16x32 bf16 weight tile by a 32x16 bf16 activation tile into fp32.
-// The activations are fp32, so they enter as two bf16 parts (hi and the remainder lo, about 16 significant bits
-// together): D = W.hi + W.lo. Weights are still read once per step.
+// Matrix-core path for 5..16 rows (batched decode, prefill chunks). Each weight element now feeds up to 16
+// products, which is matrix work: v_mfma_f32_16x16x32_bf16 multiplies a 16x32 bf16 weight tile by a 32x16 bf16
+// activation tile into fp32. The activations are fp32, so they enter as two bf16 parts (hi and the remainder lo,
+// about 16 significant bits together): D = W.hi + W.lo. Weights are still read once per step.
+//
+// The GEMM gives every wave of the launch an equal run of (32-row group, 128-input chunk) items, so a projection
+// with few output rows (o-proj, down) keeps every CU streaming as well as one with many. Weight tiles reach LDS
+// through direct global->LDS loads in which each instruction covers four whole 256-byte row segments (the 16
+// lanes of a row read its 16-byte pieces in a swizzled order), then move to the matrix cores with ds_read in the
+// operand layout. Loading them straight into registers in the operand layout touches sixteen half cache lines
+// per instruction instead of eight whole ones, and streamed at half the rate. A wave keeps three chunks in flight.
+// The two tiles of a group share the activation loads.
+//
+// RMSNorm on this path: the fragments carry gain * x, and the row's scale 1/sqrt(mean(x^2) + eps), one factor
+// of the whole product, multiplies the sums in the consumer. The sums of squares come from the kernel that wrote
+// x, one partial per block and row, added in block order.
 
+constexpr int kSkBufs = 3;                       // chunks in flight per wave
+constexpr int kSkTileBytes = 16 * kSkChunk * 2;  // one 16-row tile of one chunk: 4 KB
+constexpr int kSkNt = 2;                         // cache policy of the weight loads: streamed once
+constexpr size_t kSkRingBytes = (size_t)kSkWaves * kSkBufs * 2 * kSkTileBytes;               // 96 KB
+constexpr size_t kSkLds = kSkRingBytes + (size_t)kSkWaves * kSkWaveSlots * 2 * 64 * 16;   // + 24 KB
 
-// grid = (K / (8 * kBlock) rounded up, 16 rows): each thread turns 8 consecutive inputs of one row into one 16-byte
-// hi store and one 16-byte lo store in fragment order. With the RMSNorm, every block of a row first reduces that
-// row's sum of squares itself (the same order in every block, so the scale is identical across the row's blocks).
-template <bool NORM>
-__global__ void __launch_bounds__(kBlock) split_kernel(SplitParams p) {
-  const int r = blockIdx.y;   // activation row of the tile (rows >= p.rows are zero padding)
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const bool live = r < p.rows;
-  const float* x = p.in + (size_t)(live ? r : 0) * p.K;
-  const int k0 = (blockIdx.x * kBlock + tid) * 8;
-  float scale = 1.f;
-  if constexpr (NORM) {
-    __shared__ float red[kBlock / 64];
-    float ss = 0.f;
-    for (int k = tid * 4; k < p.K; k += kBlock * 4) {
-      const float4 v = *reinterpret_cast<const float4*>(x + k);
-      ss += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) red[wid] = ss;
-    __syncthreads();
-    scale = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)p.K + p.eps);
-  }
-  if (k0 >= p.K) return;
-  float v[8];
-  {
-    const float4 a = *reinterpret_cast<const float4*>(x + k0);
-    const float4 b = *reinterpret_cast<const float4*>(x + k0 + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-  if constexpr (NORM) {
-    const float4 a = *reinterpret_cast<const float4*>(p.gain + k0);
-    const float4 b = *reinterpret_cast<const float4*>(p.gain + k0 + 4);
-    const float gn[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+// sum of the partial products of weight rows n .. n + 3 (n % 4 == 0) for activation row r, in block order; the
+// loads of four contributors are issued before their adds
+__device__ __forceinline__ f32x4 sk_sum4(const float* part, const SkPlan& pl, int n, int r) {
+  const int g = n / kSkRows, t = (n >> 4) & 1, lane = 16 * ((n & 15) >> 2) + r;
+  const int a = g * pl.nck;
+  const int nb = pl.block_of(a + pl.nck - 1) - pl.block_of(a) + 1;
+  const float* base = part + ((size_t)g * pl.cmax * 128 + t * 64 + lane) * 4;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int kb = 0; kb < nb; kb += 4) {
+    f32x4 v[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = v[e] * scale * gn[e];
-  }
-  uint32_t hw[4], lw[4];
+    for (int c = 0; c < 4; ++c) v[c] = *reinterpret_cast<const f32x4*>(base + (size_t)min(kb + c, nb - 1) * 512);
 #pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    const float v0 = live ? v[e] : 0.f, v1 = live ? v[e + 1] : 0.f;
-    const uint16_t h0 = to_bf16(v0), h1 = to_bf16(v1);
-    const uint16_t l0 = to_bf16(v0 - widen1(h0)), l1 = to_bf16(v1 - widen1(h1));
-    hw[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    lw[e / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    for (int c = 0; c < 4; ++c)
+      if (kb + c < nb) s += v[c];
   }
-  const size_t idx = ((size_t)(k0 >> 5) * 64 + ((k0 >> 3) & 3) * 16 + r) * 8;
-  *reinterpret_cast<u32x4*>(p.hi + idx) = u32x4{hw[0], hw[1], hw[2], hw[3]};
-  *reinterpret_cast<u32x4*>(p.lo + idx) = u32x4{lw[0], lw[1], lw[2], lw[3]};
+  return s;
 }
 
-// A unit is a pair of 16-row weight tiles, chosen so the epilogue has what it needs (as PairMap for the GEMV):
-// rotary partners (rows i and i + hd/2 of a q or k head), a gate tile and its up tile, or two adjacent tiles.
-template <int MODE>
-struct TileMap {
-  int row0, row1;
-  int seg, head, idx0;   // QKV: segment 0 q / 1 k / 2 v, head, first element (within the head) of tile 0
-  __device__ __forceinline__ TileMap(const GemvParams& p, int unit) : seg(0), head(0), idx0(0) {
-    if constexpr (MODE == GEMV_QKV) {
-      const int per_head = p.hd / 32;              // units per q or k head
-      const int nqk = (p.nq + p.nkv) * per_head;
-      if (unit < nqk) {
-        head = unit / per_head;
-        idx0 = 16 * (unit % per_head);
-        seg = head < p.nq ? 0 : 1;
-        if (seg == 1) head -= p.nq;
-        row0 = (seg == 0 ? head : p.nq + head) * p.hd + idx0;
-        row1 = row0 + p.hd / 2;
-      } else {
-        const int v = 32 * (unit - nqk);            // first value row of the unit
-        seg = 2; head = v / p.hd; idx0 = v % p.hd;
-        row0 = (p.nq + p.nkv) * p.hd + v; row1 = row0 + 16;
-      }
-    } else if constexpr (MODE == GEMV_GATEUP) {
-      row0 = 16 * unit; row1 = p.up_offset + 16 * unit;
+// RMSNorm row scale from the per-block sums of squares, added in block order
+__device__ __forceinline__ float sk_row_scale(const float* ss, int nblk, int r, int D, float eps) {
+  float t = 0.f;
+#pragma unroll 8
+  for (int b = 0; b < nblk; ++b) t += ss[b * kMfmaRows + r];
+  return 1.0f / sqrtf(t / (float)D + eps);
+}
+
+// One block per CU, kSkWaves waves, each with its own ring of kSkBufs chunk buffers in LDS (no barrier while they
+// stream). HEAD: whole groups per wave, logits out. Else the waves leave their group products in LDS and the block
+// adds them per group in wave order into its partial products.
+template <bool HEAD>
+__global__ void __launch_bounds__(64 * kSkWaves) sk_gemm_kernel(SkGemmParams p) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char sk_lds[];
+  constexpr int OPC = 16;   // vector-memory operations per chunk: 8 weight (2 tiles x 4 rows of 4), 8 activation
+  const int lane = threadIdx.x & 63, r16 = lane & 15, hq = lane >> 4;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const SkPlan pl = p.plan;
+  const int gw = blockIdx.x * kSkWaves + wid;
+  int i0 = 0, i1 = 0;
+  if (gw < pl.nw) {
+    if constexpr (HEAD) {
+      i0 = (int)((unsigned)pl.groups * (unsigned)gw / (unsigned)pl.nw) * pl.nck;
+      i1 = (int)((unsigned)pl.groups * (unsigned)(gw + 1) / (unsigned)pl.nw) * pl.nck;
     } else {
-      row0 = 32 * unit; row1 = row0 + 16;
+      i0 = pl.first(gw);
+      i1 = pl.first(gw + 1);
     }
   }
-};
+  if constexpr (HEAD)
+    if (i0 >= i1) return;
+  unsigned char* mine = sk_lds + (size_t)wid * kSkBufs * 2 * kSkTileBytes;
+  f32x4* wpart = reinterpret_cast<f32x4*>(sk_lds + kSkRingBytes);   // [wave][slot][tile][lane]
+  const int K = p.K, nck = pl.nck;
+  u32x4 bh[kSkBufs][4], bl[kSkBufs][4];
 
-// One block per unit; its NW waves split the inputs (split-K) and are summed in wave order. NW grows as the units
-// get fewer, so that a projection with few outputs (o-proj, down) still has enough waves per CU in flight.
-template <typename KT, int MODE, int NW>
-__global__ void __launch_bounds__(64 * NW) gemm_mfma_kernel(MfmaParams mp) {
-  const GemvParams& p = mp.g;
-  constexpr int U = 8;                       // k-steps of 32 inputs in flight per wave
-  __shared__ f32x4 red[NW][2][64];           // split-K partials of the two tiles
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int K = p.K;
-  const int NS = K / 32;                     // k-steps
-  const int per = (NS + NW - 1) / NW;        // k-steps per wave
-  const int t0 = wid * per, t1 = min(NS, t0 + per);
-  const TileMap<MODE> tm(p, blockIdx.x);
-  const uint16_t* W = reinterpret_cast<const uint16_t*>(p.w);
-  const uint16_t* a0p = W + (size_t)(tm.row0 + lane % 16) * K + 8 * (lane / 16);
-  const uint16_t* a1p = W + (size_t)(tm.row1 + lane % 16) * K + 8 * (lane / 16);
-  const uint16_t* hp = mp.hi + (size_t)lane * 8;
-  const uint16_t* lp = mp.lo + (size_t)lane * 8;
-  f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-  for (int t = t0; t < t1; t += U) {
-    u32x4 a0[U], a1[U], bh[U], bl[U];
+  // chunk i into buffer b: tile t's row r (16 per tile) lands at byte 256 r of the tile buffer, its 16-byte piece
+  // c at position c ^ r (instruction j covers rows 4j .. 4j + 3, lane = 16 (r - 4j) + position)
+  auto issue = [&](int i, int b) {
+    const int g = i / nck, ck = i - g * nck;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {   // steps past t1 are clamped (in bounds) and skipped below
-      const int tt = min(t + u, t1 - 1);
-      a0[u] = load_stream(a0p + 32 * tt);
-      a1[u] = load_stream(a1p + 32 * tt);
-      bh[u] = *reinterpret_cast<const u32x4*>(hp + (size_t)tt * 512);
-      bl[u] = *reinterpret_cast<const u32x4*>(lp + (size_t)tt * 512);
-    }
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t* tile = p.w + (size_t)(kSkRows * g + 16 * t) * K + ck * kSkChunk;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (t + u < t1) {
-        const bf16x8 A0 = __builtin_bit_cast(bf16x8, a0[u]);
-        const bf16x8 A1 = __builtin_bit_cast(bf16x8, a1[u]);
-        const bf16x8 BH = __builtin_bit_cast(bf16x8, bh[u]);
-        const bf16x8 BL = __builtin_bit_cast(bf16x8, bl[u]);
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BH, c0, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BL, c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BH, c1, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BL, c1, 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * j + hq;
+        __builtin_amdgcn_global_load_lds((global_cptr)(tile + (size_t)r * K + 8 * (r16 ^ r)),
+                                         (lds_ptr)(mine + (b * 2 + t) * kSkTileBytes + 1024 * j), 16, 0, kSkNt);
       }
     }
-  }
-  red[wid][0][lane] = c0;
-  red[wid][1][lane] = c1;
-  __syncthreads();
-  if (tid >= 256) return;
-
-  // thread (l, i) of the first 256: lane l's element i of both tiles, summed over the waves in wave order.
-  // Tile element (l, i) is weight row tile_base + 4(l/16) + i and activation row l % 16.
-  const int l = tid >> 2, i = tid & 3;
-  float a = 0.f, b = 0.f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    a += red[w][0][l][i];
-    b += red[w][1][l][i];
+    for (int s = 0; s < 4; ++s) {
+      const size_t at = ((size_t)(ck * 4 + s) * 64 + lane) * 8;
+      bh[b][s] = *reinterpret_cast<const u32x4*>(p.hi + at);
+      bl[b][s] = *reinterpret_cast<const u32x4*>(p.lo + at);
+    }
+  };
+
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const int g_first = i0 / nck;
+  int cur = g_first;
+  float scale = 1.f;
+  if constexpr (HEAD) scale = sk_row_scale(p.ss, p.ss_blocks, r16, p.norm_dim, p.eps);
+  auto flush = [&](int g) {
+    if constexpr (HEAD) {
+      if (r16 < p.rows) {
+        const f32x4 a = acc0 * scale, b = acc1 * scale;
+        float* o = p.out + (size_t)r16 * p.n_out + kSkRows * g + 4 * hq;
+        *reinterpret_cast<f32x4*>(o) = a;
+        *reinterpret_cast<f32x4*>(o + 16) = b;
+        bool fin = true;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fin = fin && isfinite(a[e]) && isfinite(b[e]);
+        if (!fin) atomicOr(&p.status->nonfinite, 1u);
+      }
+    } else {
+      f32x4* o = wpart + ((wid * kSkWaveSlots + (g - g_first)) * 2) * 64 + lane;
+      o[0] = acc0;
+      o[64] = acc1;
+    }
+    acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  if (i0 < i1) {
+#pragma unroll
+    for (int q = 0; q < kSkBufs - 1; ++q)
+      if (i0 + q < i1) issue(i0 + q, q);
+    for (int base = i0; base < i1; base += kSkBufs) {
+#pragma unroll
+      for (int q = 0; q < kSkBufs; ++q) {
+        const int i = base + q;
+        if (i < i1) {
+          // chunk i sits in buffer q; refill the buffer read in the previous step with chunk i + kSkBufs - 1, then
+          // wait until only the chunks after i are outstanding (loads complete in order; a store issued in
+          // between only makes the wait stricter)
+          if (i + kSkBufs - 1 < i1) {
+            issue(i + kSkBufs - 1, (q + kSkBufs - 1) % kSkBufs);
+            __builtin_amdgcn_s_waitcnt(kVmcntChunk<OPC * (kSkBufs - 1)>());
+          } else {
+            __builtin_amdgcn_s_waitcnt(kVmcntChunk<0>());
+          }
+          const int g = i / nck;
+          if (g != cur) {
+            flush(cur);
+            cur = g;
+          }
+          const unsigned char* t0 = mine + (q * 2) * kSkTileBytes + r16 * 256;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const int at = 16 * ((4 * s + hq) ^ r16);
+            const bf16x8 A0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(t0 + at));
+            const bf16x8 A1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(t0 + kSkTileBytes + at));
+            const bf16x8 BH = __builtin_bit_cast(bf16x8, bh[q][s]);
+            const bf16x8 BL = __builtin_bit_cast(bf16x8, bl[q][s]);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BH, acc0, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BL, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BH, acc1, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BL, acc1, 0, 0, 0);
+          }
+        }
+      }
+    }
+    flush(cur);
   }
-  const int r = l % 16;
-  if (r >= p.rows) return;
-  const int e = 4 * (l / 16) + i;           // row within the tile
+  if constexpr (!HEAD) {
+    __syncthreads();
+    // the block's groups: 128 threads per group, thread e = tile 64 + lane of it
+    const int wb0 = blockIdx.x * kSkWaves, wb1 = min(wb0 + kSkWaves, pl.nw);
+    const int g0 = pl.first(wb0) / nck, g1 = (pl.first(wb1) - 1) / nck;
+    const int e = threadIdx.x & 127;
+    for (int g = g0 + (int)(threadIdx.x >> 7); g <= g1; g += 64 * kSkWaves / 128) {
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+      for (int w = wb0; w < wb1; ++w) {
+        const int a = pl.first(w), b = pl.first(w + 1);
+        if (b <= g * nck || a >= (g + 1) * nck) continue;   // wave w's run misses group g
+        sum += wpart[((w - wb0) * kSkWaveSlots + (g - a / nck)) * 128 + e];
+      }
+      const int k = blockIdx.x - pl.block_of(g * nck);
+      *reinterpret_cast<f32x4*>(p.part + (((size_t)g * pl.cmax + k) * 128 + e) * 4) = sum;
+    }
+  }
+}
+
+// grid = (ceil(D / kPrepSpan), 16 rows), one wave per block, 8 inputs per lane.
+__global__ void __launch_bounds__(64) sk_prep_kernel(SkPrepParams p) {
+  const int r = blockIdx.y, lane = threadIdx.x;
+  const int k0 = blockIdx.x * kPrepSpan + 8 * lane;
+  const bool in = k0 < p.D, live = in && r < p.rows;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    float* x = p.x + (size_t)r * p.D + k0;
+    float4 a = *reinterpret_cast<const float4*>(x);
+    float4 b = *reinterpret_cast<const float4*>(x + 4);
+    if (p.part) {
+      const f32x4 pa = sk_sum4(p.part, p.plan, k0, r), pb = sk_sum4(p.part, p.plan, k0 + 4, r);
+      a.x += pa[0]; a.y += pa[1]; a.z += pa[2]; a.w += pa[3];
+      b.x += pb[0]; b.y += pb[1]; b.z += pb[2]; b.w += pb[3];
+      *reinterpret_cast<float4*>(x) = a;
+      *reinterpret_cast<float4*>(x + 4) = b;
+    }
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) ss += v[e] * v[e] + v[e + 1] * v[e + 1];
+  ss = wave_total(ss);
+  if (lane == 0) p.ss[blockIdx.x * kMfmaRows + r] = ss;
+  if (!in) return;
+  if (live) {
+    const float4 ga = *reinterpret_cast<const float4*>(p.gain + k0);
+    const float4 gb = *reinterpret_cast<const float4*>(p.gain + k0 + 4);
+    v[0] *= ga.x; v[1] *= ga.y; v[2] *= ga.z; v[3] *= ga.w; v[4] *= gb.x; v[5] *= gb.y; v[6] *= gb.z; v[7] *= gb.w;
+  }
+  store_frag8(p.hi, p.lo, r, k0, v);
+}
+
+// grid = (ceil(N / 4 / kBlock), rows): a thread takes output rows n .. n + 3 (n = 4 x index) of activation row r;
+// the first rotary half of a q or k head also takes its partners n + hd/2 .. + 3.
+template <typename KT>
+__global__ void __launch_bounds__(kBlock) sk_qkv_kernel(SkQkvParams p) {
+  const int r = blockIdx.y;
+  const int n = 4 * (blockIdx.x * kBlock + threadIdx.x);
+  const int hd = p.hd, half = hd / 2;
+  if (n >= (p.nq + 2 * p.nkv) * hd) return;
+  const int hh = n / hd, idx = n % hd;
+  const int seg = hh < p.nq ? 0 : (hh < p.nq + p.nkv ? 1 : 2);   // q, k, v
+  if (seg != 2 && idx >= half) return;
   const SlotLayout sl{p.rows};
-  if constexpr (MODE == GEMV_QKV) {
-    int pos = p.slots[sl.pos() + r];
-    const bool ok = pos >= 0 && pos < p.kv.cap;
-    if (!ok) {
-      raise_error(p.status, ERR_POS);
-      pos = 0;
-    }
-    const int half = p.hd / 2;
-    const int idx = tm.idx0 + e;
-    float va = a, vb = b;
-    if (tm.seg != 2) {
-      const float2 cs = reinterpret_cast<const float2*>(p.rope)[(size_t)pos * half + idx];
-      va = a * cs.x - b * cs.y;
-      vb = a * cs.y + b * cs.x;
-    }
-    if (tm.seg == 0) {
-      float* q = p.out + ((size_t)r * p.nq + tm.head) * p.hd;
-      q[idx] = va;
-      q[idx + half] = vb;
-      return;
-    }
+  int pos = p.slots[sl.pos() + r];
+  const bool ok = pos >= 0 && pos < p.kv.cap;
+  if (!ok) {
+    raise_error(p.status, ERR_POS);
+    pos = 0;
+  }
+  const float sc = sk_row_scale(p.ss, p.ss_blocks, r, p.D, p.eps);
+  const f32x4 a = sk_sum4(p.part, p.plan, n, r) * sc;
+  int loc = pos;
+  if (seg != 0) {
     if (!ok) return;
-    int loc = pos;
     if (p.kv.paged) {
       loc = p.slots[sl.write_map() + r];
       if (loc < 0 || loc >= p.kv.pool_pages * p.kv.page_size) {
@@ -547,24 +628,57 @@ __global__ void __launch_bounds__(64 * NW) gemm_mfma_kernel(MfmaParams mp) {
         return;
       }
     }
-    // k: rotary partners (element idx and idx + hd/2); v: elements idx and idx + 16 of the head
-    KT* base = reinterpret_cast<KT*>(tm.seg == 1 ? p.kv.k : p.kv.v) + (size_t)p.layer * p.kv.layer_stride;
-    const bool isv = tm.seg == 2;
-    store_kv(base + kv_at(p.kv, isv, r, p.nkv, tm.head, p.hd, loc, idx), va);
-    store_kv(base + kv_at(p.kv, isv, r, p.nkv, tm.head, p.hd, loc, idx + (isv ? 16 : half)), vb);
-  } else if constexpr (MODE == GEMV_GATEUP) {
-    const float silu = a / (1.0f + expf(-a));
-    p.out[(size_t)r * p.n_pairs + tm.row0 + e] = silu * b;
-  } else if constexpr (MODE == GEMV_RESID) {
-    float* x = p.out + (size_t)r * 2 * p.n_pairs;
-    x[tm.row0 + e] += a;
-    x[tm.row1 + e] += b;
-  } else {  // GEMV_HEAD
-    float* lg = p.out + (size_t)r * 2 * p.n_pairs;
-    lg[tm.row0 + e] = a;
-    lg[tm.row1 + e] = b;
-    if (!isfinite(a) || !isfinite(b)) atomicOr(&p.status->nonfinite, 1u);
   }
+  if (seg == 2) {
+    const int head = hh - p.nq - p.nkv;
+    KT* base = reinterpret_cast<KT*>(p.kv.v) + (size_t)p.layer * p.kv.layer_stride;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_kv(base + kv_at(p.kv, true, r, p.nkv, head, hd, loc, idx + e), a[e]);
+    return;
+  }
+  const f32x4 b = sk_sum4(p.part, p.plan, n + half, r) * sc;
+  float va[4], vb[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float2 cs = reinterpret_cast<const float2*>(p.rope)[(size_t)pos * half + idx + e];
+    va[e] = a[e] * cs.x - b[e] * cs.y;
+    vb[e] = a[e] * cs.y + b[e] * cs.x;
+  }
+  if (seg == 0) {
+    float* q = p.q + ((size_t)r * p.nq + hh) * hd + idx;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      q[e] = va[e];
+      q[e + half] = vb[e];
+    }
+    return;
+  }
+  const int head = hh - p.nq;
+  KT* base = reinterpret_cast<KT*>(p.kv.k) + (size_t)p.layer * p.kv.layer_stride;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    store_kv(base + kv_at(p.kv, false, r, p.nkv, head, hd, loc, idx + e), va[e]);
+    store_kv(base + kv_at(p.kv, false, r, p.nkv, head, hd, loc, idx + e + half), vb[e]);
+  }
+}
+
+// grid = (ceil(F / kPrepSpan), 16 rows), one wave per block: silu(gate) * up of 8 consecutive j -> fragments.
+__global__ void __launch_bounds__(64) sk_swiglu_kernel(SkActParams p) {
+  const int r = blockIdx.y;
+  const int j0 = blockIdx.x * kPrepSpan + 8 * threadIdx.x;
+  if (j0 >= p.F) return;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (r < p.rows) {
+    const float sc = sk_row_scale(p.ss, p.ss_blocks, r, p.D, p.eps);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 g = sk_sum4(p.part, p.plan, j0 + 4 * h, r) * sc;
+      const f32x4 u = sk_sum4(p.part, p.plan, p.F + j0 + 4 * h, r) * sc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * h + e] = g[e] / (1.0f + expf(-g[e])) * u[e];
+    }
+  }
+  store_frag8(p.hi, p.lo, r, j0, v);
 }
 
 // ----------------------------------------------------------------------------------------------------------
@@ -638,7 +752,15 @@ __global__ void __launch_bounds__(128) attn_combine_kernel(AttnParams p) {
     const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));   // 0 for k >= S
     acc = fmaf(wk, k < S ? ov[k] : 0.f, acc);   // a padded split adds an exact zero, never 0 * garbage
   }
-  p.out[((size_t)r * p.nq + h) * HD + d] = acc / L;
+  const float o = acc / L;
+  p.out[((size_t)r * p.nq + h) * HD + d] = o;
+  if (p.frag_hi) {   // lanes d .. d + 7 (one wave) -> lane d's 8 values -> the fragment words
+    float v[8];
+    v[0] = o;
+#pragma unroll
+    for (int k = 1; k < 8; ++k) v[k] = __shfl_down(o, k, 64);
+    if ((d & 7) == 0) store_frag8(p.frag_hi, p.frag_lo, r, h * HD + d, v);
+  }
 }
 
 template <typename KT, int HD, int G, bool PAGED>
@@ -1627,43 +1749,61 @@ hipError_t launch_attention(const AttnParams& p, int kv_dtype, int rows, hipStre
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_split(const SplitParams& p, bool norm, hipStream_t s) {
-  if (p.K % 32) return hipErrorInvalidValue;
-  const dim3 grid((p.K + 8 * kBlock - 1) / (8 * kBlock), kMfmaRows);
-  if (norm) split_kernel<true><<<grid, kBlock, 0, s>>>(p);
-  else split_kernel<false><<<grid, kBlock, 0, s>>>(p);
+SkPlan sk_plan(int n_rows, int K, bool whole_groups) {
+  SkPlan p{};
+  const int groups = n_rows / kSkRows, nck = K / kSkChunk;
+  const long long total = (long long)groups * nck;
+  if (groups < 1 || nck < 1 || n_rows % kSkRows || K % kSkChunk) return p;
+  const long long most = (long long)kSkWaves * kSkMaxBlocks;
+  const long long nw = std::max(1LL, std::min(most, whole_groups ? (long long)groups : total));
+  if (total * nw >= (1LL << 32)) return p;
+  p.groups = groups;
+  p.nck = nck;
+  p.nw = (int)nw;
+  if (!whole_groups) {
+    // a wave's run covers at most kSkWaveSlots groups
+    const long long per = (total + nw - 1) / nw;
+    if ((per + nck - 1) / nck + 1 > kSkWaveSlots) return SkPlan{};
+    for (int g = 0; g < groups; ++g)
+      p.cmax = std::max(p.cmax, p.block_of((g + 1) * nck - 1) - p.block_of(g * nck) + 1);
+  }
+  return p;
+}
+
+hipError_t launch_sk_gemm(const SkGemmParams& p, bool head, hipStream_t s) {
+  const SkPlan& pl = p.plan;
+  if (p.K % kSkChunk || pl.nck != p.K / kSkChunk || pl.groups < 1 || pl.nck < 1 || pl.nw < 1) return hipErrorInvalidValue;
+  if (!head && pl.cmax < 1) return hipErrorInvalidValue;
+  if (head && (p.rows < 1 || p.rows > kMfmaRows || p.n_out != pl.groups * kSkRows || p.n_out % 4)) return hipErrorInvalidValue;
+  if (!head && !p.part) return hipErrorInvalidValue;
+  auto* f = head ? sk_gemm_kernel<true> : sk_gemm_kernel<false>;
+  hipError_t e = set_lds(f, kSkLds);
+  if (e != hipSuccess) return e;
+  f<<<(pl.nw + kSkWaves - 1) / kSkWaves, 64 * kSkWaves, kSkLds, s>>>(p);
   return hipGetLastError();
 }
 
-int mfma_waves_per_unit(int n_units) {
-  // aim for about 8 waves per CU over the 256 CUs
-  return n_units >= 512 ? 4 : (n_units >= 256 ? 8 : 16);
-}
-
-template <typename KT, int NW>
-static hipError_t gemm_nw(const MfmaParams& p, int mode, hipStream_t s) {
-  switch (mode) {
-    case GEMV_QKV: gemm_mfma_kernel<KT, GEMV_QKV, NW><<<p.n_units, 64 * NW, 0, s>>>(p); break;
-    case GEMV_GATEUP: gemm_mfma_kernel<KT, GEMV_GATEUP, NW><<<p.n_units, 64 * NW, 0, s>>>(p); break;
-    case GEMV_RESID: gemm_mfma_kernel<KT, GEMV_RESID, NW><<<p.n_units, 64 * NW, 0, s>>>(p); break;
-    case GEMV_HEAD: gemm_mfma_kernel<KT, GEMV_HEAD, NW><<<p.n_units, 64 * NW, 0, s>>>(p); break;
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_sk_prep(const SkPrepParams& p, hipStream_t s) {
+  if (p.D % 8 || p.rows < 1 || p.rows > kMfmaRows) return hipErrorInvalidValue;
+  const dim3 grid((p.D + kPrepSpan - 1) / kPrepSpan, kMfmaRows);
+  sk_prep_kernel<<<grid, 64, 0, s>>>(p);
   return hipGetLastError();
 }
 
-template <typename KT>
-static hipError_t gemm_go(const MfmaParams& p, int mode, hipStream_t s) {
-  switch (mfma_waves_per_unit(p.n_units)) {
-    case 4: return gemm_nw<KT, 4>(p, mode, s);
-    case 8: return gemm_nw<KT, 8>(p, mode, s);
-    default: return gemm_nw<KT, 16>(p, mode, s);
-  }
+hipError_t launch_sk_qkv(const SkQkvParams& p, int kv_dtype, hipStream_t s) {
+  const int n4 = (p.nq + 2 * p.nkv) * p.hd / 4;
+  if (p.hd % 8 || p.rows < 1 || p.rows > kMfmaRows) return hipErrorInvalidValue;
+  const dim3 grid((n4 + kBlock - 1) / kBlock, p.rows);
+  if (kv_dtype == 1) sk_qkv_kernel<uint16_t><<<grid, kBlock, 0, s>>>(p);
+  else sk_qkv_kernel<float><<<grid, kBlock, 0, s>>>(p);
+  return hipGetLastError();
 }
 
-hipError_t launch_gemm_mfma(const MfmaParams& p, int mode, int kv_dtype, hipStream_t s) {
-  if (mode == GEMV_QKV && kv_dtype != 1) return gemm_go<float>(p, mode, s);
-  return gemm_go<uint16_t>(p, mode, s);
+hipError_t launch_sk_swiglu(const SkActParams& p, hipStream_t s) {
+  if (p.F % 8 || p.rows < 1 || p.rows > kMfmaRows) return hipErrorInvalidValue;
+  const dim3 grid((p.F + kPrepSpan - 1) / kPrepSpan, kMfmaRows);
+  sk_swiglu_kernel<<<grid, 64, 0, s>>>(p);
+  return hipGetLastError();
 }
 
 hipError_t launch_kv_copy(const KvView& kv, int kv_dtype, int layer, int row, int pos0, int n, int nkv, int hd,

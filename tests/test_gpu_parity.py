@@ -197,8 +197,10 @@ def test_profile_kernels_times_every_kind_and_restores_state():
         for k in kinds:
             if k["launches"]:
                 assert k["us_per_step"] > 0, k
-                # the combine and split kernels move only work-buffer bytes, which the algorithmic count omits
-                assert k["bytes_per_step"] > 0 or k["name"] in ("attention_combine", "act_split_mfma"), k
+                # the combine and the matrix-core consumer kernels move only work-buffer bytes, which the algorithmic
+                # count omits
+                assert k["bytes_per_step"] > 0 or k["name"] in ("attention_combine", "norm_prep_mfma", "qkv_epilogue_mfma",
+                                                                   "swiglu_split_mfma"), k
         for li in range(w.model.n_layers):
             ls.check_kv(li, 0, 0, 6)
         tokens = np.array([11], np.int32)
