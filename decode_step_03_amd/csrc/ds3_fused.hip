@@ -360,8 +360,8 @@ __device__ __forceinline__ void stage_chunk(const FusedParams& p, int layer, int
     const int jv = min(jb + 8 * cv, cap - 8);
     const uint16_t* ks = Kb + ((size_t)g * cap + jk) * HD + 8 * c;
     const uint16_t* vs = Vb + ((size_t)g * HD + d) * cap + jv;
-    __builtin_amdgcn_global_load_lds((global_cptr)ks, (lds_ptr)(stage + (size_t)k * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((global_cptr)vs, (lds_ptr)(stage + SH::KB + (size_t)k * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((global_cptr)ks, (lds_ptr)(stage + (size_t)k * 1024), 16, 0, kNt);
+    __builtin_amdgcn_global_load_lds((global_cptr)vs, (lds_ptr)(stage + SH::KB + (size_t)k * 1024), 16, 0, kNt);
   }
 }
 

@@ -854,8 +854,8 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
         off = (uint32_t)(((kr * p.nkv + g) * cap + jc) * HD);
       }
       const int el = (byte % PB) / (int)sizeof(KT);
-      __builtin_amdgcn_global_load_lds((global_cptr)(Kb + off + el), (lds_ptr)(kdst + (size_t)k * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((global_cptr)(Vb + off + el), (lds_ptr)(vdst + (size_t)k * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_cptr)(Kb + off + el), (lds_ptr)(kdst + (size_t)k * 1024), 16, 0, 2);
+      __builtin_amdgcn_global_load_lds((global_cptr)(Vb + off + el), (lds_ptr)(vdst + (size_t)k * 1024), 16, 0, 2);
     }
   };
   // Both buffers are filled up front; afterwards a buffer is refilled as soon as its chunk has been consumed.
@@ -1082,8 +1082,8 @@ __global__ void __launch_bounds__(kBlock) attn_mfma_kernel(AttnParams p) {
         koff = (uint32_t)(((kr * nkv + g) * cap + jk) * HD + 8 * c);
         voff = (uint32_t)(((kr * nkv + g) * HD + d) * cap + jv);
       }
-      __builtin_amdgcn_global_load_lds((global_cptr)(Kb + koff), (lds_ptr)(kdst + (size_t)k * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((global_cptr)(Vb + voff), (lds_ptr)(vdst + (size_t)k * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_cptr)(Kb + koff), (lds_ptr)(kdst + (size_t)k * 1024), 16, 0, 2);
+      __builtin_amdgcn_global_load_lds((global_cptr)(Vb + voff), (lds_ptr)(vdst + (size_t)k * 1024), 16, 0, 2);
     }
   };
   if (live(0)) stage(0, 0);
