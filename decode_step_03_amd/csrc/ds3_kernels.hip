@@ -817,6 +817,7 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
   // q-th logical page the chunk covers, clamped to the row's last page; an id outside the pool raises the error
   // word and reads page 0 instead.
   const int ps = PAGED ? p.kv.page_size : 1;
+  const int psl = __builtin_ctz((unsigned)ps);            // page sizes are powers of two
   const int ppc = PAGED ? (ps <= TC ? TC / ps : 1) : 1;   // pages per chunk
   if constexpr (PAGED) {
     const int ppr = cap / ps;
@@ -847,9 +848,9 @@ __global__ void __launch_bounds__(kBlock) attn_kernel(AttnParams p) {
       uint32_t off;
       if constexpr (PAGED) {
         const int jb = chunk_base(c0);
-        const int q = min(max(jc / ps - jb / ps, 0), ppc - 1);
+        const int q = min(max((jc >> psl) - (jb >> psl), 0), ppc - 1);
         const int page = ptab[(c0 / TC) * ppc + q];
-        off = (uint32_t)(((page * p.nkv + g) * ps + (jc % ps)) * HD);
+        off = (uint32_t)(((page * p.nkv + g) * ps + (jc & (ps - 1))) * HD);
       } else {
         off = (uint32_t)(((kr * p.nkv + g) * cap + jc) * HD);
       }
@@ -1039,6 +1040,7 @@ __global__ void __launch_bounds__(kBlock) attn_mfma_kernel(AttnParams p) {
 
   // ---- paged: the pool pages of every chunk of this split go to LDS first (as in attn_kernel)
   const int ps = PAGED ? p.kv.page_size : 1;
+  const int psl = __builtin_ctz((unsigned)ps);            // page sizes are powers of two
   const int ppc = PAGED ? (ps <= TC ? TC / ps : 1) : 1;
   if constexpr (PAGED) {
     const int ppr = cap / ps;
@@ -1074,10 +1076,10 @@ __global__ void __launch_bounds__(kBlock) attn_mfma_kernel(AttnParams p) {
       uint32_t koff, voff;
       if constexpr (PAGED) {
         const int q0 = (c0 / TC) * ppc;
-        const int pk = ptab[q0 + min(max(jk / ps - jb / ps, 0), ppc - 1)];
-        const int pv = ptab[q0 + min(max(jv / ps - jb / ps, 0), ppc - 1)];
-        koff = (uint32_t)(((pk * nkv + g) * ps + jk % ps) * HD + 8 * c);
-        voff = (uint32_t)(((pv * nkv + g) * HD + d) * ps + jv % ps);
+        const int pk = ptab[q0 + min(max((jk >> psl) - (jb >> psl), 0), ppc - 1)];
+        const int pv = ptab[q0 + min(max((jv >> psl) - (jb >> psl), 0), ppc - 1)];
+        koff = (uint32_t)(((pk * nkv + g) * ps + (jk & (ps - 1))) * HD + 8 * c);
+        voff = (uint32_t)(((pv * nkv + g) * HD + d) * ps + (jv & (ps - 1)));
       } else {
         koff = (uint32_t)(((kr * nkv + g) * cap + jk) * HD + 8 * c);
         voff = (uint32_t)(((kr * nkv + g) * HD + d) * cap + jv);
