@@ -891,7 +891,8 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
                                          " compute units with one block each (device has " + std::to_string(cus) +
                                          ", " + std::to_string(per_cu) + " block(s) per unit)");
   }
-  // the per-operation sequence of R rows (with the matrix-core split kernels above 4 rows)
+  // the per-operation sequence of R rows (above 4 rows: the matrix-core GEMMs and the kernels that consume their
+  // partial products)
   auto per_op = [&](std::vector<Launch>& seq, bool mfma, bool pick) {
     seq.push_back({K_EMBED, -1, 0});
     for (int l = 0; l < c.n_layers; ++l) {

@@ -7,14 +7,22 @@
 //
 // Kernel set (one launch each, per layer where noted):
 //   embed_kernel      x[r] = E[token[r]]                                      (reads Slot::Token)
+//   1-4 rows (vector ALU):
 //   gemv_kernel<QKV>  RMSNorm(x) -> q, k, v rows; rotary epilogue on q and k; k and v stored at Slot::Pos
 //                     (contiguous) or at Slot::WriteMap (paged)             per layer
-//   attn_kernel       split sweep of all [cap] positions, mask from Slot::Pos against the position index,
-//                     per-split softmax partials, last-arriving block merges the splits in fixed order  per layer
-//   gemv_kernel<RESID> x += W_o . o                                         per layer
+//   gemv_kernel<RESID> x += W_o . o, x += W_down . act                      per layer (two launches)
 //   gemv_kernel<GATEUP> RMSNorm(x) -> gate/up rows, SwiGLU epilogue -> act  per layer
-//   gemv_kernel<RESID> x += W_down . act                                    per layer
 //   gemv_kernel<HEAD> RMSNorm(x) -> logits, non-finite flag
+//   5-16 rows (matrix cores):
+//   sk_prep_kernel    x += partial products of the previous projection; RMSNorm sums; fragments of gain * x
+//   sk_gemm_kernel    stream-K projection on the fragments -> partial products (LM head: logits)
+//   sk_qkv_kernel     q, k, v from the QKV partials; rotary; k and v stored as above      per layer
+//   sk_swiglu_kernel  SwiGLU on the gate/up partials -> the down projection's fragments  per layer
+//   both:
+//   attn_mfma_kernel / attn_kernel  split sweep of all [cap] positions (bf16 K/V on the matrix cores, fp32 on
+//                     the vector ALU), mask from Slot::Pos against the position index, per-split softmax partials
+//   attn_combine_kernel  the splits merged in fixed order (and, 5-16 rows, the o-projection's fragments)
+//   pick_kernel / sample_kernel  the next token into the slots (greedy, or the sampling suffix)
 //
 // No kernel takes a token, a position or a map entry by value: they are read from the slot buffer, so one
 // recorded graph serves every step ("Execution" page, section "Slot buffers").
