@@ -273,7 +273,8 @@ std::string check_config(const ds3_config* c) {
       if (!sk_plan(qkv, c->d_model, false).groups || !sk_plan(c->d_model, qw, false).groups ||
           !sk_plan(2 * c->ffn_dim, c->d_model, false).groups || !sk_plan(c->d_model, c->ffn_dim, false).groups ||
           !sk_plan(c->vocab, c->d_model, true).groups)
-        return "the projection shapes are outside what the matrix-core kernels take for more than 4 rows";
+        return "more than 4 rows: vocab, d_model, 2 x ffn_dim and (n_q_heads + 2 n_kv_heads) x head_dim must be "
+               "multiples of 128";
     }
   }
   return "";

@@ -165,32 +165,34 @@ constexpr int kMaxGemvRows = 4;
 constexpr int kMaxRows = 16;
 constexpr int kMfmaRows = 16;   // activation rows of one MFMA tile (rows are zero-padded to it)
 
-// Matrix-core projection plan (stream-K). The weight matrix [N][K] is cut into items (group of kSkRows rows, chunk
-// of kSkChunk inputs), numbered group-major; wave w of the launch streams items [first(w), first(w + 1)), an equal
-// share whatever N and K. A block sums its waves' products per group (wave order) and stores one partial product
-// per group it touched: part[group][k][tile 0/1][lane 64][4] fp32, k = block - block_of(first item of the group)
-// (the MFMA output layout: lane l, element e is weight row 16 tile + 4 (l / 16) + e of the group and activation
-// row l % 16). The kernel that consumes the projection sums a group's k = 0, 1, ... in order, which is input order.
+// Matrix-core projection plan (stream-K). The weight matrix [N][K] is cut into groups of kSkRows rows (two 16-row
+// tiles), four neighbouring groups form a quad, and the items (quad, chunk of kSkChunk inputs), numbered
+// quad-major, are split into equal contiguous runs, one per block: block b streams items [first(b), first(b + 1))
+// whatever N and K, its wave w taking group w of each quad (the four waves share the chunk's activations). A wave
+// stores one partial product per group it touched: part[group][k][tile 0/1][lane 64][4] fp32, k = block -
+// block_of(first item of the group's quad) (the MFMA output layout: lane l, element e is weight row
+// 16 tile + 4 (l / 16) + e of the group and activation row l % 16). The kernel that consumes the projection sums
+// a group's k = 0, 1, ... in order, which is input order.
 constexpr int kSkRows = 32;        // weight rows per group (two 16-row tiles)
+constexpr int kSkQuad = 4;         // groups per quad = waves per block
 constexpr int kSkChunk = 128;      // inputs per chunk
-constexpr int kSkWaves = 4;        // waves per block (one block per CU: its LDS takes 120 KB)
+constexpr int kSkWaves = kSkQuad;  // waves per block (one block per CU: its LDS takes 120 KB)
 constexpr int kSkMaxBlocks = 256;
-constexpr int kSkWaveSlots = 3;    // most groups one wave's run may touch
 constexpr int kPrepSpan = 512;     // consumer kernels: inputs per block (one wave, 8 per lane)
 struct SkPlan {
   int groups;   // N / kSkRows
   int nck;      // K / kSkChunk
-  int nw;       // waves with work (every one has at least one item, or one group with whole groups)
+  int nb;       // blocks with work (every one has at least one item, or one quad with whole quads)
   int cmax;     // most blocks that contribute to one group
-  __host__ __device__ unsigned total() const { return (unsigned)groups * (unsigned)nck; }
-  __host__ __device__ int first(int w) const { return (int)(total() * (unsigned)w / (unsigned)nw); }
-  // the wave, and the block, whose run holds item i (total x nw < 2^32: sk_plan checks it)
-  __host__ __device__ int wave_of(int i) const { return (int)(((unsigned)(i + 1) * (unsigned)nw - 1) / total()); }
-  __host__ __device__ int block_of(int i) const { return wave_of(i) / kSkWaves; }
+  __host__ __device__ int quads() const { return groups / kSkQuad; }
+  __host__ __device__ unsigned total() const { return (unsigned)quads() * (unsigned)nck; }
+  __host__ __device__ int first(int b) const { return (int)(total() * (unsigned)b / (unsigned)nb); }
+  // the block whose run holds item i (total x nb < 2^32: sk_plan checks it)
+  __host__ __device__ int block_of(int i) const { return (int)(((unsigned)(i + 1) * (unsigned)nb - 1) / total()); }
 };
-// whole_groups: each wave takes whole groups (the LM head, whose epilogue writes the logits itself).
+// whole_quads: each block takes whole quads (the LM head, whose epilogue writes the logits itself).
 // Returns a plan with groups == 0 if the shape is outside what the kernels take.
-SkPlan sk_plan(int n_rows, int K, bool whole_groups);
+SkPlan sk_plan(int n_rows, int K, bool whole_quads);
 inline size_t sk_partial_floats(const SkPlan& p) { return (size_t)p.groups * p.cmax * 512; }
 
 struct SkGemmParams {

@@ -392,38 +392,42 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
 // activation tile into fp32. The activations are fp32, so they enter as two bf16 parts (hi and the remainder lo,
 // about 16 significant bits together): D = W.hi + W.lo. Weights are still read once per step.
 //
-// The GEMM gives every wave of the launch an equal run of (32-row group, 128-input chunk) items, so a projection
-// with few output rows (o-proj, down) keeps every CU streaming as well as one with many. Weight tiles reach LDS
-// through direct global->LDS loads in which each instruction covers four whole 256-byte row segments (the 16
-// lanes of a row read its 16-byte pieces in a swizzled order), then move to the matrix cores with ds_read in the
-// operand layout. Loading them straight into registers in the operand layout touches sixteen half cache lines
-// per instruction instead of eight whole ones, and streamed at half the rate. A wave keeps three chunks in flight.
-// The two tiles of a group share the activation loads.
+// The GEMM gives every block (one per CU) an equal run of (quad of four 32-row groups, 128-input chunk) items, so
+// a projection with few output rows (o-proj, down) keeps every CU streaming as well as one with many. Wave w takes
+// group w of the quad; the four waves walk the chunks in step and share the chunk's activation fragments, which
+// they load a quarter each into LDS (as many bytes as the weights when every wave loaded its own: a probe streamed
+// 10-17% faster without them). Weight tiles reach LDS through direct global->LDS loads in which each instruction
+// covers four whole 256-byte row segments (the 16 lanes of a row read its 16-byte pieces in a swizzled order),
+// then move to the matrix cores with ds_read in the operand layout. Loading them straight into registers in the
+// operand layout touches sixteen half cache lines per instruction instead of eight whole ones, and streamed at
+// half the rate. Three chunks are in flight.
 //
 // RMSNorm on this path: the fragments carry gain * x, and the row's scale 1/sqrt(mean(x^2) + eps), one factor
 // of the whole product, multiplies the sums in the consumer. The sums of squares come from the kernel that wrote
 // x, one partial per block and row, added in block order.
 
-constexpr int kSkBufs = 3;                       // chunks in flight per wave
+constexpr int kSkBufs = 3;                       // chunk buffers (two load while one is consumed)
 constexpr int kSkTileBytes = 16 * kSkChunk * 2;  // one 16-row tile of one chunk: 4 KB
+constexpr int kSkActBytes = kSkChunk / 32 * 2 * 1024;   // a chunk's activation fragments, hi and lo: 8 KB
 constexpr int kSkNt = 2;                         // cache policy of the weight loads: streamed once
-constexpr size_t kSkRingBytes = (size_t)kSkWaves * kSkBufs * 2 * kSkTileBytes;               // 96 KB
-constexpr size_t kSkLds = kSkRingBytes + (size_t)kSkWaves * kSkWaveSlots * 2 * 64 * 16;   // + 24 KB
+constexpr size_t kSkRingBytes = (size_t)kSkWaves * kSkBufs * 2 * kSkTileBytes;   // weights: 96 KB
+constexpr size_t kSkLds = kSkRingBytes + (size_t)kSkBufs * kSkActBytes;          // + activations: 24 KB
 
 // sum of the partial products of weight rows n .. n + 3 (n % 4 == 0) for activation row r, in block order; the
-// loads of four contributors are issued before their adds
+// loads of up to eight contributors are issued before their adds
 __device__ __forceinline__ f32x4 sk_sum4(const float* part, const SkPlan& pl, int n, int r) {
   const int g = n / kSkRows, t = (n >> 4) & 1, lane = 16 * ((n & 15) >> 2) + r;
-  const int a = g * pl.nck;
+  const int a = g / kSkQuad * pl.nck;
   const int nb = pl.block_of(a + pl.nck - 1) - pl.block_of(a) + 1;
   const float* base = part + ((size_t)g * pl.cmax * 128 + t * 64 + lane) * 4;
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  for (int kb = 0; kb < nb; kb += 4) {
-    f32x4 v[4];
+  for (int kb = 0; kb < nb; kb += 8) {
+    f32x4 v[8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) v[c] = *reinterpret_cast<const f32x4*>(base + (size_t)min(kb + c, nb - 1) * 512);
+    for (int c = 0; c < 8; ++c)
+      v[c] = kb + c < nb ? *reinterpret_cast<const f32x4*>(base + (size_t)(kb + c) * 512) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < 8; ++c)
       if (kb + c < nb) s += v[c];
   }
   return s;
@@ -437,38 +441,45 @@ __device__ __forceinline__ float sk_row_scale(const float* ss, int nblk, int r, 
   return 1.0f / sqrtf(t / (float)D + eps);
 }
 
-// One block per CU, kSkWaves waves, each with its own ring of kSkBufs chunk buffers in LDS (no barrier while they
-// stream). HEAD: whole groups per wave, logits out. Else the waves leave their group products in LDS and the block
-// adds them per group in wave order into its partial products.
+// Block barrier that orders LDS only. __syncthreads() is a workgroup fence as well, which waits for every
+// outstanding global load and store of the wave (vmcnt 0) when stores precede it, and would drain the chunks in
+// flight; here each wave has waited for the loads it needs, and its LDS reads have been consumed.
+__device__ __forceinline__ void barrier_lds() {
+  constexpr int kLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);   // s_waitcnt lgkmcnt(0) only (gfx9 encoding)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kLgkm0);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One block per CU, wave w on group w of each quad of the block's run; the waves meet at a barrier per chunk
+// (the chunk's activations come from all four). HEAD: whole quads per block, logits out; else partial products.
 template <bool HEAD>
 __global__ void __launch_bounds__(64 * kSkWaves) sk_gemm_kernel(SkGemmParams p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char sk_lds[];
-  constexpr int OPC = 16;   // vector-memory operations per chunk: 8 weight (2 tiles x 4 rows of 4), 8 activation
+  constexpr int OPC = 10;   // vector-memory operations per chunk and wave: 8 weight (2 tiles x 4), 2 activation
   const int lane = threadIdx.x & 63, r16 = lane & 15, hq = lane >> 4;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const SkPlan pl = p.plan;
-  const int gw = blockIdx.x * kSkWaves + wid;
-  int i0 = 0, i1 = 0;
-  if (gw < pl.nw) {
-    if constexpr (HEAD) {
-      i0 = (int)((unsigned)pl.groups * (unsigned)gw / (unsigned)pl.nw) * pl.nck;
-      i1 = (int)((unsigned)pl.groups * (unsigned)(gw + 1) / (unsigned)pl.nw) * pl.nck;
-    } else {
-      i0 = pl.first(gw);
-      i1 = pl.first(gw + 1);
-    }
+  const int b = blockIdx.x;
+  int i0, i1;
+  if constexpr (HEAD) {
+    i0 = (int)((unsigned)pl.quads() * (unsigned)b / (unsigned)pl.nb) * pl.nck;
+    i1 = (int)((unsigned)pl.quads() * (unsigned)(b + 1) / (unsigned)pl.nb) * pl.nck;
+  } else {
+    i0 = pl.first(b);
+    i1 = pl.first(b + 1);
   }
-  if constexpr (HEAD)
-    if (i0 >= i1) return;
+  if (i0 >= i1) return;   // (block-uniform)
   unsigned char* mine = sk_lds + (size_t)wid * kSkBufs * 2 * kSkTileBytes;
-  f32x4* wpart = reinterpret_cast<f32x4*>(sk_lds + kSkRingBytes);   // [wave][slot][tile][lane]
+  unsigned char* act = sk_lds + kSkRingBytes;   // [buffer][hi k-steps 0..3, lo k-steps 0..3][64 lanes][16 B]
   const int K = p.K, nck = pl.nck;
-  u32x4 bh[kSkBufs][4], bl[kSkBufs][4];
 
-  // chunk i into buffer b: tile t's row r (16 per tile) lands at byte 256 r of the tile buffer, its 16-byte piece
-  // c at position c ^ r (instruction j covers rows 4j .. 4j + 3, lane = 16 (r - 4j) + position)
-  auto issue = [&](int i, int b) {
-    const int g = i / nck, ck = i - g * nck;
+  // chunk i into buffer bf: the wave's own two tiles (tile t's row r lands at byte 256 r, its 16-byte piece c at
+  // position c ^ r; instruction j covers rows 4j .. 4j + 3) and a quarter of the activation fragments
+  auto issue = [&](int i, int bf) {
+    const int q = i / nck, ck = i - q * nck;
+    const int g = kSkQuad * q + wid;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const uint16_t* tile = p.w + (size_t)(kSkRows * g + 16 * t) * K + ck * kSkChunk;
@@ -476,101 +487,81 @@ __global__ void __launch_bounds__(64 * kSkWaves) sk_gemm_kernel(SkGemmParams p) 
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * j + hq;
         __builtin_amdgcn_global_load_lds((global_cptr)(tile + (size_t)r * K + 8 * (r16 ^ r)),
-                                         (lds_ptr)(mine + (b * 2 + t) * kSkTileBytes + 1024 * j), 16, 0, kSkNt);
+                                         (lds_ptr)(mine + (bf * 2 + t) * kSkTileBytes + 1024 * j), 16, 0, kSkNt);
       }
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const size_t at = ((size_t)(ck * 4 + s) * 64 + lane) * 8;
-      bh[b][s] = *reinterpret_cast<const u32x4*>(p.hi + at);
-      bl[b][s] = *reinterpret_cast<const u32x4*>(p.lo + at);
+    for (int m = 2 * wid; m < 2 * wid + 2; ++m) {   // 1 KB each: (hi, lo) x 4 k-steps
+      const uint16_t* src = (m < 4 ? p.hi : p.lo) + ((size_t)(ck * 4 + (m & 3)) * 64 + lane) * 8;
+      __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(act + bf * kSkActBytes + 1024 * m), 16, 0, 0);
     }
   };
 
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  const int g_first = i0 / nck;
-  int cur = g_first;
+  int cur = i0 / nck;
   float scale = 1.f;
   if constexpr (HEAD) scale = sk_row_scale(p.ss, p.ss_blocks, r16, p.norm_dim, p.eps);
-  auto flush = [&](int g) {
+  auto flush = [&](int q) {
+    const int g = kSkQuad * q + wid;
     if constexpr (HEAD) {
       if (r16 < p.rows) {
-        const f32x4 a = acc0 * scale, b = acc1 * scale;
+        const f32x4 a = acc0 * scale, c = acc1 * scale;
         float* o = p.out + (size_t)r16 * p.n_out + kSkRows * g + 4 * hq;
         *reinterpret_cast<f32x4*>(o) = a;
-        *reinterpret_cast<f32x4*>(o + 16) = b;
+        *reinterpret_cast<f32x4*>(o + 16) = c;
         bool fin = true;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) fin = fin && isfinite(a[e]) && isfinite(b[e]);
+        for (int e = 0; e < 4; ++e) fin = fin && isfinite(a[e]) && isfinite(c[e]);
         if (!fin) atomicOr(&p.status->nonfinite, 1u);
       }
     } else {
-      f32x4* o = wpart + ((wid * kSkWaveSlots + (g - g_first)) * 2) * 64 + lane;
-      o[0] = acc0;
-      o[64] = acc1;
+      const int k = b - pl.block_of(q * nck);
+      float* o = p.part + (((size_t)g * pl.cmax + k) * 2 * 64 + lane) * 4;
+      *reinterpret_cast<f32x4*>(o) = acc0;
+      *reinterpret_cast<f32x4*>(o + 256) = acc1;
     }
     acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
     acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
   };
 
-  if (i0 < i1) {
 #pragma unroll
-    for (int q = 0; q < kSkBufs - 1; ++q)
-      if (i0 + q < i1) issue(i0 + q, q);
-    for (int base = i0; base < i1; base += kSkBufs) {
+  for (int q = 0; q < kSkBufs - 1; ++q)
+    if (i0 + q < i1) issue(i0 + q, q);
+  for (int base = i0; base < i1; base += kSkBufs) {
 #pragma unroll
-      for (int q = 0; q < kSkBufs; ++q) {
-        const int i = base + q;
-        if (i < i1) {
-          // chunk i sits in buffer q; refill the buffer read in the previous step with chunk i + kSkBufs - 1, then
-          // wait until only the chunks after i are outstanding (loads complete in order; a store issued in
-          // between only makes the wait stricter)
-          if (i + kSkBufs - 1 < i1) {
-            issue(i + kSkBufs - 1, (q + kSkBufs - 1) % kSkBufs);
-            __builtin_amdgcn_s_waitcnt(kVmcntChunk<OPC * (kSkBufs - 1)>());
-          } else {
-            __builtin_amdgcn_s_waitcnt(kVmcntChunk<0>());
-          }
-          const int g = i / nck;
-          if (g != cur) {
-            flush(cur);
-            cur = g;
-          }
-          const unsigned char* t0 = mine + (q * 2) * kSkTileBytes + r16 * 256;
+    for (int q = 0; q < kSkBufs; ++q) {
+      const int i = base + q;
+      if (i < i1) {
+        // chunk i (buffer q) has landed once only the chunk after it is outstanding (loads complete in order; a
+        // store issued in between only makes the wait stricter); the barrier makes every wave's quarter of the
+        // activations visible and frees the buffer read in the previous step, which then takes chunk i + 2
+        if (i + 1 < i1) __builtin_amdgcn_s_waitcnt(kVmcntChunk<OPC>());
+        else __builtin_amdgcn_s_waitcnt(kVmcntChunk<0>());
+        barrier_lds();
+        if (i + kSkBufs - 1 < i1) issue(i + kSkBufs - 1, (q + kSkBufs - 1) % kSkBufs);
+        const int qd = i / nck;
+        if (qd != cur) {
+          flush(cur);
+          cur = qd;
+        }
+        const unsigned char* t0 = mine + (q * 2) * kSkTileBytes + r16 * 256;
+        const unsigned char* av = act + q * kSkActBytes + lane * 16;
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const int at = 16 * ((4 * s + hq) ^ r16);
-            const bf16x8 A0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(t0 + at));
-            const bf16x8 A1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(t0 + kSkTileBytes + at));
-            const bf16x8 BH = __builtin_bit_cast(bf16x8, bh[q][s]);
-            const bf16x8 BL = __builtin_bit_cast(bf16x8, bl[q][s]);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BH, acc0, 0, 0, 0);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BL, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BH, acc1, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BL, acc1, 0, 0, 0);
-          }
+        for (int s = 0; s < 4; ++s) {
+          const int at = 16 * ((4 * s + hq) ^ r16);
+          const bf16x8 A0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(t0 + at));
+          const bf16x8 A1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(t0 + kSkTileBytes + at));
+          const bf16x8 BH = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(av + 1024 * s));
+          const bf16x8 BL = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(av + 1024 * (4 + s)));
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BH, acc0, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BL, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BH, acc1, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BL, acc1, 0, 0, 0);
         }
       }
     }
-    flush(cur);
   }
-  if constexpr (!HEAD) {
-    __syncthreads();
-    // the block's groups: 128 threads per group, thread e = tile 64 + lane of it
-    const int wb0 = blockIdx.x * kSkWaves, wb1 = min(wb0 + kSkWaves, pl.nw);
-    const int g0 = pl.first(wb0) / nck, g1 = (pl.first(wb1) - 1) / nck;
-    const int e = threadIdx.x & 127;
-    for (int g = g0 + (int)(threadIdx.x >> 7); g <= g1; g += 64 * kSkWaves / 128) {
-      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-      for (int w = wb0; w < wb1; ++w) {
-        const int a = pl.first(w), b = pl.first(w + 1);
-        if (b <= g * nck || a >= (g + 1) * nck) continue;   // wave w's run misses group g
-        sum += wpart[((w - wb0) * kSkWaveSlots + (g - a / nck)) * 128 + e];
-      }
-      const int k = blockIdx.x - pl.block_of(g * nck);
-      *reinterpret_cast<f32x4*>(p.part + (((size_t)g * pl.cmax + k) * 128 + e) * 4) = sum;
-    }
-  }
+  flush(cur);
 }
 
 // grid = (ceil(D / kPrepSpan), 16 rows), one wave per block, 8 inputs per lane.
@@ -1759,37 +1750,32 @@ hipError_t launch_attention(const AttnParams& p, int kv_dtype, int rows, hipStre
   return hipErrorInvalidValue;
 }
 
-SkPlan sk_plan(int n_rows, int K, bool whole_groups) {
+SkPlan sk_plan(int n_rows, int K, bool whole_quads) {
   SkPlan p{};
-  const int groups = n_rows / kSkRows, nck = K / kSkChunk;
-  const long long total = (long long)groups * nck;
-  if (groups < 1 || nck < 1 || n_rows % kSkRows || K % kSkChunk) return p;
-  const long long most = (long long)kSkWaves * kSkMaxBlocks;
-  const long long nw = std::max(1LL, std::min(most, whole_groups ? (long long)groups : total));
-  if (total * nw >= (1LL << 32)) return p;
-  p.groups = groups;
-  p.nck = nck;
-  p.nw = (int)nw;
-  if (!whole_groups) {
-    // a wave's run covers at most kSkWaveSlots groups
-    const long long per = (total + nw - 1) / nw;
-    if ((per + nck - 1) / nck + 1 > kSkWaveSlots) return SkPlan{};
-    for (int g = 0; g < groups; ++g)
-      p.cmax = std::max(p.cmax, p.block_of((g + 1) * nck - 1) - p.block_of(g * nck) + 1);
-  }
+  if (n_rows % (kSkRows * kSkQuad) || K % kSkChunk || n_rows < 1 || K < 1) return p;
+  p.groups = n_rows / kSkRows;
+  p.nck = K / kSkChunk;
+  const long long total = (long long)p.quads() * p.nck;
+  const long long nb = std::max(1LL, std::min((long long)kSkMaxBlocks, whole_quads ? (long long)p.quads() : total));
+  if (total * nb >= (1LL << 32)) return SkPlan{};
+  p.nb = (int)nb;
+  if (!whole_quads)
+    for (int q = 0; q < p.quads(); ++q)
+      p.cmax = std::max(p.cmax, p.block_of((q + 1) * p.nck - 1) - p.block_of(q * p.nck) + 1);
   return p;
 }
 
 hipError_t launch_sk_gemm(const SkGemmParams& p, bool head, hipStream_t s) {
   const SkPlan& pl = p.plan;
-  if (p.K % kSkChunk || pl.nck != p.K / kSkChunk || pl.groups < 1 || pl.nck < 1 || pl.nw < 1) return hipErrorInvalidValue;
+  if (p.K % kSkChunk || pl.nck != p.K / kSkChunk || pl.groups < kSkQuad || pl.groups % kSkQuad || pl.nck < 1 || pl.nb < 1)
+    return hipErrorInvalidValue;
   if (!head && pl.cmax < 1) return hipErrorInvalidValue;
   if (head && (p.rows < 1 || p.rows > kMfmaRows || p.n_out != pl.groups * kSkRows || p.n_out % 4)) return hipErrorInvalidValue;
   if (!head && !p.part) return hipErrorInvalidValue;
   auto* f = head ? sk_gemm_kernel<true> : sk_gemm_kernel<false>;
   hipError_t e = set_lds(f, kSkLds);
   if (e != hipSuccess) return e;
-  f<<<(pl.nw + kSkWaves - 1) / kSkWaves, 64 * kSkWaves, kSkLds, s>>>(p);
+  f<<<pl.nb, 64 * kSkWaves, kSkLds, s>>>(p);
   return hipGetLastError();
 }
 

@@ -98,11 +98,11 @@ def test_paged_single_row_gemv_path():
 
 
 def test_narrow_shapes_ragged_stream_k():
-    """A narrow bf16 model (d_model 384, q width 256, ffn 640, vocab 1056, 6 rows) puts every matrix-core kernel on
-    its uneven paths: fewer waves than one per item group of the chip (48, 24, 120, 60 and 33 waves, blocks with
-    fewer than 4 waves), groups whose inputs span several blocks, d_model not a multiple of the prep kernels' 512
-    inputs, d_model != q width, and G = 2 heads per kv head."""
-    m = synth.ModelShape("narrow", 2, 384, 4, 2, 64, 640, 1056, 1e-5, 1e4, "bf16")
+    """A narrow bf16 model (d_model 384, q width 256, ffn 640, vocab 1152, 6 rows) puts every matrix-core kernel on
+    its uneven paths: fewer blocks than CUs (12, 6, 30 and 15 blocks for the projections, 9 for the head), quads
+    whose inputs span up to 5 blocks, d_model not a multiple of the prep kernels' 512 inputs, d_model != q width,
+    and G = 2 heads per kv head."""
+    m = synth.ModelShape("narrow", 2, 384, 4, 2, 64, 640, 1152, 1e-5, 1e4, "bf16")
     w = synth.Workload("narrow-bf16-r6", m, 6, 256, "contiguous", "bf16", 3, "random_kv")
     ws = synth.make_weights(w.model, gains="random")
     _run(w, ws, [0, 5, 64, 127, 200, 255 - 3], steps=3)
