@@ -151,6 +151,18 @@ constexpr int kVmcntChunk() {
   return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 }
 
+// Block barrier that orders LDS only. __syncthreads() is a workgroup fence as well, which compiles to
+// s_waitcnt vmcnt(0) -- every outstanding global load and store of the wave -- wherever a store may precede it, and
+// so drains loads issued ahead (the next chunk's or the next phase's). Callers wait explicitly for the loads whose
+// data the other waves read (s_waitcnt vmcnt(N)); the wave's own LDS reads and writes complete first.
+__device__ __forceinline__ void barrier_lds() {
+  constexpr int kLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);   // s_waitcnt lgkmcnt(0) only (gfx9 encoding)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kLgkm0);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 typedef __attribute__((address_space(1))) const void* global_cptr;
 typedef __attribute__((address_space(3))) void* lds_ptr;
 

@@ -687,7 +687,8 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
     }
   }
   if constexpr (PH != PH_HEAD) {
-    __syncthreads();
+    // (waves 1-7 hold the next phase's first batches in flight: no vmcnt(0) here)
+    barrier_lds();
     after_barrier(p, kFusedPhases * layer + (PH == PH_QKV ? 0 : PH == PH_O ? 2 : PH == PH_GU ? 3 : 4));
   }
 }
@@ -931,7 +932,7 @@ __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, con
       nx.issue(1, B);
     });
   }
-  __syncthreads();
+  barrier_lds();   // (the next phase's first batches and the gate/up LDS batches stay in flight)
   after_barrier(p, kFusedPhases * layer + 1);
 }
 

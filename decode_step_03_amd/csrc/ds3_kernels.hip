@@ -441,17 +441,6 @@ __device__ __forceinline__ float sk_row_scale(const float* ss, int nblk, int r, 
   return 1.0f / sqrtf(t / (float)D + eps);
 }
 
-// Block barrier that orders LDS only. __syncthreads() is a workgroup fence as well, which waits for every
-// outstanding global load and store of the wave (vmcnt 0) when stores precede it, and would drain the chunks in
-// flight; here each wave has waited for the loads it needs, and its LDS reads have been consumed.
-__device__ __forceinline__ void barrier_lds() {
-  constexpr int kLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);   // s_waitcnt lgkmcnt(0) only (gfx9 encoding)
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(kLgkm0);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // One block per CU, wave w on group w of each quad of the block's run; the waves meet at a barrier per chunk
 // (the chunk's activations come from all four). HEAD: whole quads per block, logits out; else partial products.
 template <bool HEAD>
