@@ -126,7 +126,7 @@ def cpu_baseline(w, ws, start_pos, start_tok, budget_s: float) -> dict:
     return {"value": steps / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": f"{steps} greedy decode step(s) of row 0 from position {int(start_pos[0])}, all "
                       f"{w.model.n_layers} layers and the head, float64, weights widened per 256-row block",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), "host": host_info()}
 
 
 CSRC = os.path.join(ROOT, "decode_step_03_amd", "csrc")
@@ -167,6 +167,64 @@ def pmc_traffic(kind: str, workload: str):
                 + float(vals["write_kib_per_launch"]) * float(vals["write_scale"])) * 1024.0
     except (KeyError, ValueError, OSError):
         return None
+
+
+def host_info() -> dict:
+    """What the oracle's time is measured on: CPU model, logical cores, host RAM, the BLAS behind NumPy and its
+    threads."""
+    info = {"cpu_model": None, "logical_cpus": os.cpu_count(), "host_ram_gb": None, "blas": None}
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal"):
+                info["host_ram_gb"] = round(int(line.split()[1]) / 2**20, 1)
+                break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        info["blas"] = [{"api": d.get("internal_api"), "threads": d.get("num_threads")} for d in threadpool_info()
+                        if d.get("user_api") == "blas"]
+    except Exception:   # (threadpoolctl absent or failing: leave it unrecorded)
+        pass
+    return info
+
+
+def achievable_bandwidth(torch) -> dict:
+    """What plain streaming reaches on this GPU, beside the roofline's 8 TB/s: the library's streaming-read probe
+    (the weight streams' access pattern: 16-byte non-temporal loads, 1 KB per wave instruction) over 4 GiB, and a
+    device-to-device copy of 1 GiB (bytes read + written); both are larger than the 256 MB infinity cache. HIP
+    events on torch's stream, best of 3 after a warm-up."""
+    from decode_step_03_amd import _ds3
+
+    def best(fn, reps=3):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        return min(ts)
+    n_read = 4 << 30
+    a = torch.ones(n_read // 4, dtype=torch.int32, device="cuda:0")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    us_read = best(lambda: _ds3.ds3_probe_read(a.data_ptr(), n_read, sink.data_ptr(), stream))
+    del a, sink
+    src = torch.ones((1 << 30) // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    us_copy = best(lambda: dst.copy_(src))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"read_gbs": round(n_read / us_read / 1e3, 1), "copy_gbs": round(2 * (1 << 30) / us_copy / 1e3, 1),
+            "probe": "ds3_probe_read over 4 GiB (read only); copy of 1 GiB (read + write)"}
 
 
 def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 5) -> int:
@@ -295,10 +353,12 @@ def main() -> int:
     per_launch_us = dom["us_per_step"] / dom["launches"]
     achieved = per_launch_bytes / per_launch_us / 1e3
     traffic = pmc_traffic(dom["name"], w.name)
+    reach = achievable_bandwidth(torch)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": round(traffic) if traffic is not None else None, "kernel": dom["name"],
-                "bytes_per_launch": per_launch_bytes, "us_per_launch": round(per_launch_us, 3)}
+                "bytes_per_launch": per_launch_bytes, "us_per_launch": round(per_launch_us, 3),
+                "achievable": reach, "frac_of_achievable_read": round(achieved / reach["read_gbs"], 4)}
 
     # beyond the method: the visible K/V sweep (chunks wholly after pos not loaded; outputs bit-identical), timed
     # on the same engine and capture from where the timed steps ended; fewer bytes than the formula's count

@@ -99,6 +99,7 @@ SIGNATURES = [
     ("ds3_profile_kernels", c_int32, [c_void_p, c_int32, POINTER(ds3_kernel_time), POINTER(c_int32)]),
     ("ds3_phase_trace", c_int32, [c_void_p, POINTER(c_uint64), POINTER(c_int32)]),
     ("ds3_debug_inject", c_int32, [c_void_p, c_int32]),
+    ("ds3_probe_read", c_int32, [c_void_p, ctypes.c_uint64, c_void_p, c_void_p]),
     ("ds3_last_error", ctypes.c_char_p, [c_void_p]),
     ("ds3_destroy", None, [c_void_p]),
 ]
@@ -228,6 +229,11 @@ def ds3_phase_trace(h: int, n: int):
     k = c_int32(n)
     _check(load_library().ds3_phase_trace(h, out, ctypes.byref(k)), h)
     return list(out)[: k.value]
+
+
+def ds3_probe_read(buf_ptr: int, nbytes: int, sink_ptr: int, stream_ptr: int) -> None:
+    """One streaming read of `nbytes` of device memory (measurement only; see include/ds3.h)."""
+    _check(load_library().ds3_probe_read(buf_ptr, nbytes, sink_ptr, stream_ptr), None)
 
 
 def ds3_debug_inject(h: int, kind: int) -> None:

@@ -1625,6 +1625,14 @@ ds3_status ds3_debug_inject(ds3_engine* e, int32_t kind) {
   return DS3_OK;
 }
 
+ds3_status ds3_probe_read(const void* buf, uint64_t bytes, void* sink, void* hip_stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16) return fail(nullptr, DS3_E_INVALID, "probe: buf, sink and bytes (a multiple of 16)");
+  const hipError_t h = launch_stream_read(buf, (size_t)bytes, reinterpret_cast<uint32_t*>(sink),
+                                          reinterpret_cast<hipStream_t>(hip_stream));
+  if (h != hipSuccess) return fail(nullptr, DS3_E_DEVICE_LOST, std::string("probe: ") + hipGetErrorString(h));
+  return DS3_OK;
+}
+
 const char* ds3_last_error(const ds3_engine* e) { return e ? e->err.c_str() : g_last_error.c_str(); }
 
 void ds3_destroy(ds3_engine* e) {

@@ -309,6 +309,8 @@ hipError_t launch_attention_combine(const AttnParams& p, int rows, hipStream_t s
 hipError_t launch_kv_copy(const KvView& kv, int kv_dtype, int layer, int row, int pos0, int n, int nkv, int hd,
                           void* staging, int to_state, StatusWords* status, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t s);
+// Streaming-read probe (measurement): reads `bytes` (a multiple of 16) once; `sink` holds at least 1024 words.
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_pick(const PickParams& p, hipStream_t s);
 hipError_t launch_sample(const SampleParams& p, hipStream_t s);
 // Fused step kernel (ds3_fused.hip). fused_shape_supported: the model shape has a compiled instantiation.

@@ -1197,6 +1197,29 @@ __global__ void __launch_bounds__(kBlock) attn_mfma_kernel(AttnParams p) {
 }
 
 // ----------------------------------------------------------------------------------------------------------
+// Streaming-read probe (measurement only, not part of a step): what plain reading reaches on this GPU, beside the
+// roofline's 8 TB/s. Every wave reads 8 KB per step (eight 1 KB contiguous instructions, non-temporal) over a
+// wave-strided sweep of the buffer.
+constexpr int kProbeBlocks = 1024;
+__global__ void __launch_bounds__(512) stream_read_kernel(const u32x4* __restrict__ buf, size_t n16, uint32_t* sink) {
+  const size_t lane = threadIdx.x & 63;
+  const size_t gw = (size_t)blockIdx.x * 8 + (threadIdx.x >> 6), nw = (size_t)gridDim.x * 8;
+  uint32_t acc = 0;
+  for (size_t base = gw * 512; base < n16; base += nw * 512) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t i = base + (size_t)u * 64 + lane;
+      v[u] = i < n16 ? load_stream(buf + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  // a store the compiler cannot drop keeps every load (the data practically never hashes to this value)
+  if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
+}
+
+// ----------------------------------------------------------------------------------------------------------
 // K/V state copies for write_kv / read_kv: staging <-> state (contiguous or paged). The staging holds K as
 // [nkv][n][hd] and V as [nkv][n][hd], or as [nkv][hd][n] when V is stored transposed, so that consecutive
 // threads touch consecutive elements of the state in either layout.
@@ -1818,6 +1841,12 @@ hipError_t launch_sample(const SampleParams& p, hipStream_t s) {
   hipError_t h = hipGetLastError();
   if (h != hipSuccess) return h;
   sample_close_kernel<<<1, 1, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s) {
+  if (!buf || !sink || bytes < 16 || bytes % 16) return hipErrorInvalidValue;
+  stream_read_kernel<<<kProbeBlocks, 512, 0, s>>>(reinterpret_cast<const u32x4*>(buf), bytes / 16, sink);
   return hipGetLastError();
 }
 

@@ -311,6 +311,13 @@ ds3_status ds3_phase_trace(ds3_engine* e, uint64_t* out, int32_t* n_inout);
 enum { DS3_INJECT_KERNEL_CHECK = 1, DS3_INJECT_TIMEOUT_NEXT = 2, DS3_INJECT_BARRIER_TIMEOUT = 3 };
 ds3_status ds3_debug_inject(ds3_engine* e, int32_t kind);
 
+/* Measurement only, outside the step: enqueue one streaming read of `bytes` (a multiple of 16) of device memory
+ * `buf` on HIP stream `hip_stream` (a hipStream_t; NULL = the null stream), with the access pattern the weight
+ * streams use (16-byte non-temporal loads, 1 KB contiguous per wave instruction). `sink` is device memory of at
+ * least 4096 bytes that the kernel may write (its contents carry no meaning). Returns after the launch (time it
+ * with events on the stream). DS3_E_INVALID for a bad argument, DS3_E_DEVICE_LOST if the launch fails. */
+ds3_status ds3_probe_read(const void* buf, uint64_t bytes, void* sink, void* hip_stream);
+
 /* Message of the engine's last failure ("" if none); engine-owned, valid until the next call. With e == NULL,
  * the last failure of ds3_query_buffers/ds3_create on this thread. */
 const char* ds3_last_error(const ds3_engine* e);

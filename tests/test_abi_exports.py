@@ -95,3 +95,12 @@ def test_create_rejects_bad_buffers_without_touching_a_device():
     with pytest.raises(ds3.DS3Error) as ei:
         C.ds3_create(_cfg(), [0, 0, 0, 0], None)
     assert ei.value.status == C.DS3_E_INVALID
+
+
+def test_probe_read_rejects_bad_arguments_without_touching_a_device():
+    """The streaming-read probe validates before any HIP call: null pointers and sizes that are not a positive
+    multiple of 16 bytes are DS3_E_INVALID."""
+    for buf, n, sink in [(0, 4096, 4096), (4096, 4096, 0), (4096, 17, 4096), (4096, 0, 4096)]:
+        with pytest.raises(ds3.DS3Error) as ei:
+            C.ds3_probe_read(buf, n, sink, None)
+        assert ei.value.status == C.DS3_E_INVALID and "probe" in ei.value.message

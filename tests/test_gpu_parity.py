@@ -209,3 +209,17 @@ def test_profile_kernels_times_every_kind_and_restores_state():
             tokens = np.array([int(np.argmax(ref[0]))], np.int32)
     finally:
         eng.close()
+
+
+def test_streaming_read_probe_runs():
+    """The measurement probe (outside the step) reads a buffer on torch's stream and leaves the engine-free state
+    alone: it completes, and a second launch on the same stream completes too."""
+    import torch
+    from decode_step_03_amd import _ds3
+    a = torch.ones(1 << 22, dtype=torch.int32, device="cuda:0")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        _ds3.ds3_probe_read(a.data_ptr(), 4 * a.numel(), sink.data_ptr(), stream)
+    torch.cuda.synchronize()
+    assert int(a.sum()) == a.numel()
