@@ -262,6 +262,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--visible-steps", type=int, default=64,
                     help="also time this many steps with the visible K/V sweep (0: skip)")
+    ap.add_argument("--sample-steps", type=int, default=64,
+                    help="also time this many steps with the sampling suffix in place of the greedy pick (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of known size (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -382,6 +384,30 @@ def main() -> int:
         visible = {"tok_s": round(w.rows * n_vis / ev, 2), "gpu_ms": round(float(np.median(gv)) / 1e3, 4),
                    "steps": n_vis, "note": "K/V chunks wholly after pos skipped; not the method's full sweep"}
         log(f"visible sweep: {visible['tok_s']} tok/s, GPU {visible['gpu_ms']} ms/step")
+
+    # the sampling suffix in place of the greedy pick (temperature, top-k, top-p, min-p, repetition penalty, the
+    # drawn token's log-probability and the top 5), on the same engine from where the steps above ended
+    sampled = None
+    n_smp = min(args.sample_steps, w.cap - int(pos.max()))
+    if args.sample_steps > 0 and n_smp >= 8:
+        params = dict(temperature=0.8, top_k=40, top_p=0.95, min_p=0.02, repetition_penalty=1.1, n_logprobs=5)
+        for r in range(w.rows):
+            eng.set_sampling(r, seed=1234 + r, **params)
+            eng.set_history(r, [int(tok[r])])
+        torch.cuda.synchronize()
+        ts0 = time.perf_counter()
+        gs = []
+        done = 0
+        while done < n_smp:
+            n = min(32, n_smp - done)
+            ids, _, _, _ = eng.step_sample(tok, pos, n)
+            tok, pos, done = ids[-1].copy(), pos + n, done + n
+            gs.append(eng.stats()["last_gpu_us"])
+        torch.cuda.synchronize()
+        es = time.perf_counter() - ts0
+        sampled = {"tok_s": round(w.rows * n_smp / es, 2), "gpu_ms": round(float(np.median(gs)) / 1e3, 4),
+                   "steps": n_smp, "params": params}
+        log(f"sampling suffix: {sampled['tok_s']} tok/s, GPU {sampled['gpu_ms']} ms/step")
     eng.close()
     del eng
     torch.cuda.empty_cache()
@@ -447,7 +473,7 @@ def main() -> int:
                  "token_pick": "device (greedy, chained)" if args.chain > 0 else "host argmax of copied logits",
                  "host_submit_us_graph": round(float(np.median(submit_us)), 1),
                  "per_op_graph": per_op.get("graph", {}), "eager": per_op.get("eager", {}),
-                 "attn_splits": stats["attn_splits"], "visible_sweep": visible, "prompt_prefill": prefill.last},
+                 "attn_splits": stats["attn_splits"], "visible_sweep": visible, "sampled": sampled, "prompt_prefill": prefill.last},
         "kernels": [{"name": k["name"], "launches": k["launches"], "us_per_step": round(k["us_per_step"], 2),
                      "gbs": round(k["bytes_per_step"] / k["us_per_step"] / 1e3, 1) if k["us_per_step"] else None}
                     for k in kernels],

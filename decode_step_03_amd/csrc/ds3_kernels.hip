@@ -1343,21 +1343,44 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t d) {
 
 struct SampleShared {
   unsigned long long hist[256];
-  unsigned long long wsum[kSampleThreads];
+  unsigned long long wsum[kSampleWaves];
   float fv[kSampleWaves];
   int fi[kSampleWaves];
   unsigned long long bcast[2];
 };
 
-// block sum of one u64 per thread, fixed order (every thread gets it)
-__device__ __forceinline__ unsigned long long block_sum_u64(SampleShared& sh, unsigned long long x) {
-  sh.wsum[threadIdx.x] = x;
-  __syncthreads();
-  for (int m = kSampleThreads / 2; m >= 1; m >>= 1) {
-    if ((int)threadIdx.x < m) sh.wsum[threadIdx.x] += sh.wsum[threadIdx.x + m];
-    __syncthreads();
+// 64-bit lane exchanges as two 32-bit ones
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long x, int m) {
+  const unsigned lo = __shfl_xor((unsigned)x, m, 64), hi = __shfl_xor((unsigned)(x >> 32), m, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long shfl_up_u64(unsigned long long x, int d) {
+  const unsigned lo = __shfl_up((unsigned)x, d, 64), hi = __shfl_up((unsigned)(x >> 32), d, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += shfl_xor_u64(x, m);
+  return x;
+}
+// inclusive prefix sum over the lanes of a wave, in lane order
+__device__ __forceinline__ unsigned long long wave_scan_u64(unsigned long long x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const unsigned long long y = shfl_up_u64(x, d);
+    if (lane >= d) x += y;
   }
-  const unsigned long long t = sh.wsum[0];
+  return x;
+}
+
+// block sum of one u64 per thread (integer: the same in any order; every thread gets it)
+__device__ __forceinline__ unsigned long long block_sum_u64(SampleShared& sh, unsigned long long x) {
+  x = wave_sum_u64(x);
+  if ((threadIdx.x & 63) == 0) sh.wsum[threadIdx.x >> 6] = x;
+  __syncthreads();
+  unsigned long long t = 0;
+  for (int w = 0; w < kSampleWaves; ++w) t += sh.wsum[w];
   __syncthreads();
   return t;
 }
@@ -1379,21 +1402,37 @@ __device__ __forceinline__ void block_best(SampleShared& sh, float& bv, int& bi)
   __syncthreads();
 }
 
-// Radix selection over the keys of the tokens `in(v)`, weight `wt(v)` each: the largest key K such that the total
-// weight of keys >= K reaches `target`. Returns K and the weight of keys > K (integer sums: the same on every run).
+// Tokens v0, v0 + stride, ... below v1 in groups of U: the U loads of a group are issued before any is used
+// (addresses clamped into the range, so every load is in bounds), then f(v, z[v]) for the tokens of the group.
+template <int U, class F>
+__device__ __forceinline__ void sweep(const float* z, int v0, int v1, int stride, F&& f) {
+  for (int base = v0; base < v1; base += stride * U) {
+    float x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = z[min(base + u * stride, v1 - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (base + u * stride < v1) f(base + u * stride, x[u]);
+  }
+}
+constexpr int kSweepU = 8;
+
+// Radix selection over the keys of the tokens `in(v, x)` (x = z[v]), weight `wt(x)` each: the largest key K such
+// that the total weight of keys >= K reaches `target`. Returns K and the weight of keys > K (integer sums: the
+// same on every run).
 template <class IN, class KEY, class WT>
-__device__ __forceinline__ void radix_select(SampleShared& sh, int V, IN&& in, KEY&& key, WT&& wt,
+__device__ __forceinline__ void radix_select(SampleShared& sh, const float* z, int V, IN&& in, KEY&& key, WT&& wt,
                                              unsigned long long target, uint32_t& K, unsigned long long& above) {
   uint32_t prefix = 0, pmask = 0;
   unsigned long long ab = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int b = threadIdx.x; b < 256; b += kSampleThreads) sh.hist[b] = 0;
     __syncthreads();
-    for (int v = threadIdx.x; v < V; v += kSampleThreads) {
-      if (!in(v)) continue;
-      const uint32_t k = key(v);
-      if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], wt(v));
-    }
+    sweep<kSweepU>(z, threadIdx.x, V, kSampleThreads, [&](int v, float x) __attribute__((always_inline)) {
+      if (!in(v, x)) return;
+      const uint32_t k = key(x);
+      if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], wt(x));
+    });
     __syncthreads();
     if (threadIdx.x == 0) {
       int b = 255;
@@ -1414,35 +1453,61 @@ __device__ __forceinline__ void radix_select(SampleShared& sh, int V, IN&& in, K
   above = ab;
 }
 
-// In index order over the tokens `in(v)`: the first v whose running weight reaches `target` (>= 1). Each thread
-// sums a contiguous segment, the segment sums are scanned in order, and one thread walks its segment.
+// In index order over the tokens `in(v, x)`: the first v whose running weight reaches `target` (>= 1); the last
+// token if the total stays below it. Integer weights, so the sums are exact in any grouping. Two levels, every load
+// coalesced or contiguous: wave w sums the w-th of kSampleWaves contiguous segments (lanes on consecutive tokens);
+// the segment where the running sum reaches the target is cut into runs of E consecutive tokens, one per thread; a
+// block scan of the run sums in index order finds the run, and its thread walks at most E tokens.
 template <class IN, class WT>
-__device__ __forceinline__ int index_scan(SampleShared& sh, int V, IN&& in, WT&& wt, unsigned long long target) {
-  const int seg = (V + kSampleThreads - 1) / kSampleThreads;
-  const int v0 = threadIdx.x * seg, v1 = min(V, v0 + seg);
-  unsigned long long t = 0;
-  for (int v = v0; v < v1; ++v)
-    if (in(v)) t += wt(v);
-  sh.wsum[threadIdx.x] = t;
-  if (threadIdx.x == 0) sh.bcast[0] = (unsigned long long)(V - 1);   // (past the total: the last token)
-  __syncthreads();
-  if (threadIdx.x == 0) {   // inclusive scan, in thread order
-    unsigned long long run = 0;
-    for (int i = 0; i < kSampleThreads; ++i) {
-      run += sh.wsum[i];
-      sh.wsum[i] = run;
-    }
+__device__ __forceinline__ int index_scan(SampleShared& sh, const float* z, int V, IN&& in, WT&& wt,
+                                          unsigned long long target) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int S1 = (V + kSampleWaves - 1) / kSampleWaves;   // tokens per wave segment
+  {
+    const int a0 = wv * S1, a1 = min(V, a0 + S1);
+    unsigned long long t = 0;
+    sweep<kSweepU>(z, a0 + lane, a1, 64, [&](int v, float x) __attribute__((always_inline)) {
+      if (in(v, x)) t += wt(x);
+    });
+    t = wave_sum_u64(t);
+    if (lane == 0) sh.wsum[wv] = t;
   }
+  if (tid == 0) sh.bcast[0] = (unsigned long long)(V - 1);   // (past the total: the last token)
   __syncthreads();
-  const unsigned long long before = threadIdx.x ? sh.wsum[threadIdx.x - 1] : 0ull;
-  if (before < target && sh.wsum[threadIdx.x] >= target) {
-    unsigned long long run = before;
-    for (int v = v0; v < v1; ++v) {
-      if (!in(v)) continue;
-      run += wt(v);
-      if (run >= target) {
-        sh.bcast[0] = (unsigned long long)v;
-        break;
+  unsigned long long run = 0;   // the weight before the segment that holds the target
+  int seg = kSampleWaves;
+  for (int w = 0; w < kSampleWaves; ++w) {
+    if (run + sh.wsum[w] >= target) {
+      seg = w;
+      break;
+    }
+    run += sh.wsum[w];
+  }
+  __syncthreads();   // (wsum is rewritten below)
+  if (seg < kSampleWaves) {   // (the same for every thread)
+    const int E = (S1 + kSampleThreads - 1) / kSampleThreads;   // tokens per run
+    const int b1 = min(V, (seg + 1) * S1);
+    const int c0 = min(b1, seg * S1 + tid * E), c1 = min(b1, c0 + E);
+    unsigned long long t = 0;
+    sweep<kSweepU>(z, c0, c1, 1, [&](int v, float x) __attribute__((always_inline)) {
+      if (in(v, x)) t += wt(x);
+    });
+    const unsigned long long incl = wave_scan_u64(t);
+    if (lane == 63) sh.wsum[wv] = incl;
+    __syncthreads();
+    unsigned long long off = run;
+    for (int w = 0; w < wv; ++w) off += sh.wsum[w];
+    const unsigned long long before = off + incl - t;
+    if (before < target && before + t >= target) {
+      unsigned long long r2 = before;
+      for (int v = c0; v < c1; ++v) {
+        const float x = z[v];
+        if (!in(v, x)) continue;
+        r2 += wt(x);
+        if (r2 >= target) {
+          sh.bcast[0] = (unsigned long long)v;
+          break;
+        }
       }
     }
   }
@@ -1462,82 +1527,104 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
   float* z = p.z + (size_t)r * V;
 
   // ---- adjusted logits: repetition penalty on seen tokens (toward zero), presence and frequency, bias; NaN -> -inf
+  // (four tokens per thread in flight, three loads each)
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int v = tid; v < V; v += kSampleThreads) {
-    float x = lg[v];
-    if (x != x) x = -INFINITY;
-    const int c = cnt[v];
-    if (c > 0) x = (x > 0.f ? x / prm.rep : x * prm.rep) - prm.presence - prm.frequency * (float)c;
-    x += bias[v];
-    if (x != x) x = -INFINITY;
-    z[v] = x;
-    if (pick_better(x, v, bv, bi)) { bv = x; bi = v; }
+  for (int base = tid; base < V; base += 4 * kSampleThreads) {
+    float xl[4], xb[4];
+    int xc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = min(base + u * kSampleThreads, V - 1);
+      xl[u] = lg[v];
+      xc[u] = cnt[v];
+      xb[u] = bias[v];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = base + u * kSampleThreads;
+      if (v >= V) break;
+      float x = xl[u];
+      if (x != x) x = -INFINITY;
+      const int c = xc[u];
+      if (c > 0) x = (x > 0.f ? x / prm.rep : x * prm.rep) - prm.presence - prm.frequency * (float)c;
+      x += xb[u];
+      if (x != x) x = -INFINITY;
+      z[v] = x;
+      if (pick_better(x, v, bv, bi)) { bv = x; bi = v; }
+    }
   }
-  block_best(sh, bv, bi);
+  block_best(sh, bv, bi);   // (its barriers also order the z stores before the sweeps below)
   const float zmax = bv;
   int token = bi < V ? bi : 0;
   const float T = prm.temperature;
   const float inv_t = T > 0.f ? 1.f / T : 1.f;
 
   if (T > 0.f && zmax > -INFINITY) {
-    auto key = [&](int v) { return order_key(z[v] * inv_t); };
+    auto key = [&](float x) __attribute__((always_inline)) { return order_key(x * inv_t); };
     const float smax = zmax * inv_t;
     // weight of a token: exp(s - s_max) in fixed point (2^40 = the top token)
-    auto wt = [&](int v) -> unsigned long long {
-      const float w = __expf(z[v] * inv_t - smax);
+    auto wt = [&](float x) __attribute__((always_inline)) -> unsigned long long {
+      const float w = __expf(x * inv_t - smax);
       return (unsigned long long)(w * 1099511627776.f);
     };
-    auto one = [&](int) -> unsigned long long { return 1ull; };
-    auto all = [&](int) { return true; };
+    auto one = [&](float) __attribute__((always_inline)) -> unsigned long long { return 1ull; };
+    auto all = [&](int, float) __attribute__((always_inline)) { return true; };
     // top-k: the k best ranked (ties at the threshold key by lower index)
     uint32_t kk = 0u;
     int ki = V;
     if (prm.top_k > 0 && prm.top_k < V) {
       unsigned long long above = 0;
-      radix_select(sh, V, all, key, one, (unsigned long long)prm.top_k, kk, above);
+      radix_select(sh, z, V, all, key, one, (unsigned long long)prm.top_k, kk, above);
       const uint32_t K = kk;
-      ki = index_scan(sh, V, [&](int v) { return key(v) == K; }, one, (unsigned long long)prm.top_k - above);
+      ki = index_scan(sh, z, V, [&](int, float x) __attribute__((always_inline)) { return key(x) == K; }, one,
+                      (unsigned long long)prm.top_k - above);
     }
     const uint32_t K1 = kk;
     const int I1 = ki;
-    auto in_k = [&](int v) { const uint32_t k = key(v); return k > K1 || (k == K1 && v <= I1); };
+    auto in_k = [&](int v, float x) __attribute__((always_inline)) {
+      const uint32_t k = key(x);
+      return k > K1 || (k == K1 && v <= I1);
+    };
     // top-p: the shortest ranked prefix of the top-k set whose weight reaches p of its total
     uint32_t kp = 0u;
     int ip = V;
     if (prm.top_p < 1.f) {
       unsigned long long tw = 0;
-      for (int v = tid; v < V; v += kSampleThreads)
-        if (in_k(v)) tw += wt(v);
+      sweep<kSweepU>(z, tid, V, kSampleThreads, [&](int v, float x) __attribute__((always_inline)) {
+        if (in_k(v, x)) tw += wt(x);
+      });
       tw = block_sum_u64(sh, tw);
       unsigned long long target = (unsigned long long)((double)prm.top_p * (double)tw);
       if (target < 1) target = 1;
       unsigned long long above = 0;
-      radix_select(sh, V, in_k, key, wt, target, kp, above);
+      radix_select(sh, z, V, in_k, key, wt, target, kp, above);
       const uint32_t K = kp;
-      ip = index_scan(sh, V, [&](int v) { return in_k(v) && key(v) == K; }, wt, target - above);
+      ip = index_scan(sh, z, V, [&](int v, float x) __attribute__((always_inline)) { return in_k(v, x) && key(x) == K; },
+                      wt, target - above);
     }
     const uint32_t K2 = kp;
     const int I2 = ip;
     // min-p: weight at least min_p of the top token's
     const float lmin = prm.min_p > 0.f ? __logf(prm.min_p) : -INFINITY;
-    auto kept = [&](int v) {
-      if (!in_k(v)) return false;
-      const uint32_t k = key(v);
+    auto kept = [&](int v, float x) __attribute__((always_inline)) {
+      if (!in_k(v, x)) return false;
+      const uint32_t k = key(x);
       if (!(k > K2 || (k == K2 && v <= I2))) return false;
-      return z[v] * inv_t - smax >= lmin;
+      return x * inv_t - smax >= lmin;
     };
     // the draw: inverse CDF in index order over the kept weights
     unsigned long long tw = 0;
-    for (int v = tid; v < V; v += kSampleThreads)
-      if (kept(v)) tw += wt(v);
+    sweep<kSweepU>(z, tid, V, kSampleThreads, [&](int v, float x) __attribute__((always_inline)) {
+      if (kept(v, x)) tw += wt(x);
+    });
     tw = block_sum_u64(sh, tw);
     const uint64_t seed = ((uint64_t)prm.seed_hi << 32) | prm.seed_lo;
     const uint32_t d = p.draws[r];
     const double u = (double)(splitmix64(seed, d) >> 40) * (1.0 / 16777216.0);
     unsigned long long target = (unsigned long long)(u * (double)tw) + 1ull;
     if (target > tw) target = tw;
-    if (tw > 0) token = index_scan(sh, V, kept, wt, target);
+    if (tw > 0) token = index_scan(sh, z, V, kept, wt, target);
     if (tid == 0) p.draws[r] = d + 1u;
   }
 
@@ -1551,7 +1638,9 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
   if (nl > 0) {
     const float smax = zmax * inv_t;
     float t = 0.f;
-    for (int v = tid; v < V; v += kSampleThreads) t += __expf(z[v] * inv_t - smax);
+    sweep<kSweepU>(z, tid, V, kSampleThreads, [&](int, float x) __attribute__((always_inline)) {
+      t += __expf(x * inv_t - smax);
+    });
     for (int m = 32; m >= 1; m >>= 1) t += __shfl_xor(t, m, 64);
     if ((tid & 63) == 0) sh.fv[tid >> 6] = t;
     __syncthreads();
@@ -1565,11 +1654,11 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
     for (int j = 0; j < nl; ++j) {
       float cv = -INFINITY;
       int ci = 0x7fffffff;
-      for (int v = tid; v < V; v += kSampleThreads) {
-        const float x = z[v] * inv_t;
+      sweep<kSweepU>(z, tid, V, kSampleThreads, [&](int v, float zx) __attribute__((always_inline)) {
+        const float x = zx * inv_t;
         const bool below = x < pv || (x == pv && v > pi);
         if (below && pick_better(x, v, cv, ci)) { cv = x; ci = v; }
-      }
+      });
       block_best(sh, cv, ci);
       if (tid == 0) {
         lpi[j] = ci < V ? ci : -1;
