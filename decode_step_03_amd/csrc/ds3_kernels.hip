@@ -1453,17 +1453,37 @@ __device__ __forceinline__ void radix_select(SampleShared& sh, const float* z, i
   above = ab;
 }
 
+// The weight of the tokens `in(v, x)` in each of the kSampleWaves contiguous segments index_scan uses, into
+// sh.wsum (wave w sums segment w, lanes on consecutive tokens); returns the total (every thread).
+template <class IN, class WT>
+__device__ __forceinline__ unsigned long long segment_sums(SampleShared& sh, const float* z, int V, IN&& in, WT&& wt) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int S1 = (V + kSampleWaves - 1) / kSampleWaves;
+  const int a0 = wv * S1, a1 = min(V, a0 + S1);
+  unsigned long long t = 0;
+  sweep<kSweepU>(z, a0 + lane, a1, 64, [&](int v, float x) __attribute__((always_inline)) {
+    if (in(v, x)) t += wt(x);
+  });
+  t = wave_sum_u64(t);
+  if (lane == 0) sh.wsum[wv] = t;
+  __syncthreads();
+  unsigned long long tot = 0;
+  for (int w = 0; w < kSampleWaves; ++w) tot += sh.wsum[w];
+  return tot;
+}
+
 // In index order over the tokens `in(v, x)`: the first v whose running weight reaches `target` (>= 1); the last
 // token if the total stays below it. Integer weights, so the sums are exact in any grouping. Two levels, every load
 // coalesced or contiguous: wave w sums the w-th of kSampleWaves contiguous segments (lanes on consecutive tokens);
 // the segment where the running sum reaches the target is cut into runs of E consecutive tokens, one per thread; a
 // block scan of the run sums in index order finds the run, and its thread walks at most E tokens.
+// have_seg: sh.wsum already holds the segment sums (segment_sums below, same predicate and weights).
 template <class IN, class WT>
 __device__ __forceinline__ int index_scan(SampleShared& sh, const float* z, int V, IN&& in, WT&& wt,
-                                          unsigned long long target) {
+                                          unsigned long long target, bool have_seg = false) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int S1 = (V + kSampleWaves - 1) / kSampleWaves;   // tokens per wave segment
-  {
+  if (!have_seg) {
     const int a0 = wv * S1, a1 = min(V, a0 + S1);
     unsigned long long t = 0;
     sweep<kSweepU>(z, a0 + lane, a1, 64, [&](int v, float x) __attribute__((always_inline)) {
@@ -1613,18 +1633,15 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
       if (!(k > K2 || (k == K2 && v <= I2))) return false;
       return x * inv_t - smax >= lmin;
     };
-    // the draw: inverse CDF in index order over the kept weights
-    unsigned long long tw = 0;
-    sweep<kSweepU>(z, tid, V, kSampleThreads, [&](int v, float x) __attribute__((always_inline)) {
-      if (kept(v, x)) tw += wt(x);
-    });
-    tw = block_sum_u64(sh, tw);
+    // the draw: inverse CDF in index order over the kept weights (the segment sums of the total are the scan's first
+    // level)
+    const unsigned long long tw = segment_sums(sh, z, V, kept, wt);
     const uint64_t seed = ((uint64_t)prm.seed_hi << 32) | prm.seed_lo;
     const uint32_t d = p.draws[r];
     const double u = (double)(splitmix64(seed, d) >> 40) * (1.0 / 16777216.0);
     unsigned long long target = (unsigned long long)(u * (double)tw) + 1ull;
     if (target > tw) target = tw;
-    if (tw > 0) token = index_scan(sh, z, V, kept, wt, target);
+    if (tw > 0) token = index_scan(sh, z, V, kept, wt, target, true);
     if (tid == 0) p.draws[r] = d + 1u;
   }
 
