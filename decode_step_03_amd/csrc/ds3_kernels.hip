@@ -1341,8 +1341,15 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t d) {
   return z ^ (z >> 31);
 }
 
+constexpr int kSampleList = 1024;   // top-k sets up to this size are gathered into LDS for the rest of the selection
+
 struct SampleShared {
   unsigned long long hist[256];
+  int gv[kSampleList];   // the top-k set as gathered (any order): tokens, adjusted logits
+  float gx[kSampleList];
+  int lv[kSampleList];   // the same in index order
+  float lx[kSampleList];
+  int nlist;
   unsigned long long wsum[kSampleWaves];
   float fv[kSampleWaves];
   int fi[kSampleWaves];
@@ -1606,42 +1613,84 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
       const uint32_t k = key(x);
       return k > K1 || (k == K1 && v <= I1);
     };
-    // top-p: the shortest ranked prefix of the top-k set whose weight reaches p of its total
-    uint32_t kp = 0u;
-    int ip = V;
-    if (prm.top_p < 1.f) {
-      unsigned long long tw = 0;
+    // With top-k on (k <= kSampleList) the rest of the selection runs over the top-k set alone, its tokens and
+    // adjusted logits gathered into LDS in index order: position i of the list stands for token lv[i], and the
+    // order, keys and weights are those of the full sweep, so every selection below comes out the same.
+    const bool listed = prm.top_k > 0 && prm.top_k < V && prm.top_k <= kSampleList;
+    int n = 0;
+    if (listed) {
+      if (tid == 0) sh.nlist = 0;
+      __syncthreads();
       sweep<kSweepU>(z, tid, V, kSampleThreads, [&](int v, float x) __attribute__((always_inline)) {
-        if (in_k(v, x)) tw += wt(x);
+        if (in_k(v, x)) {
+          const int i = atomicAdd(&sh.nlist, 1);
+          if (i < kSampleList) {
+            sh.gv[i] = v;
+            sh.gx[i] = x;
+          }
+        }
       });
-      tw = block_sum_u64(sh, tw);
-      unsigned long long target = (unsigned long long)((double)prm.top_p * (double)tw);
-      if (target < 1) target = 1;
-      unsigned long long above = 0;
-      radix_select(sh, z, V, in_k, key, wt, target, kp, above);
-      const uint32_t K = kp;
-      ip = index_scan(sh, z, V, [&](int v, float x) __attribute__((always_inline)) { return in_k(v, x) && key(x) == K; },
-                      wt, target - above);
+      __syncthreads();
+      n = min(sh.nlist, kSampleList);
+      for (int i = tid; i < n; i += kSampleThreads) {   // index order: a token's rank among the gathered ones
+        const int v = sh.gv[i];
+        int rank = 0;
+        for (int j = 0; j < n; ++j) rank += sh.gv[j] < v;
+        sh.lv[rank] = v;
+        sh.lx[rank] = sh.gx[i];
+      }
+      __syncthreads();
     }
-    const uint32_t K2 = kp;
-    const int I2 = ip;
-    // min-p: weight at least min_p of the top token's
-    const float lmin = prm.min_p > 0.f ? __logf(prm.min_p) : -INFINITY;
-    auto kept = [&](int v, float x) __attribute__((always_inline)) {
-      if (!in_k(v, x)) return false;
-      const uint32_t k = key(x);
-      if (!(k > K2 || (k == K2 && v <= I2))) return false;
-      return x * inv_t - smax >= lmin;
-    };
-    // the draw: inverse CDF in index order over the kept weights (the segment sums of the total are the scan's first
-    // level)
-    const unsigned long long tw = segment_sums(sh, z, V, kept, wt);
     const uint64_t seed = ((uint64_t)prm.seed_hi << 32) | prm.seed_lo;
     const uint32_t d = p.draws[r];
     const double u = (double)(splitmix64(seed, d) >> 40) * (1.0 / 16777216.0);
-    unsigned long long target = (unsigned long long)(u * (double)tw) + 1ull;
-    if (target > tw) target = tw;
-    if (tw > 0) token = index_scan(sh, z, V, kept, wt, target, true);
+    const float lmin = prm.min_p > 0.f ? __logf(prm.min_p) : -INFINITY;
+    // top-p, min-p and the draw over the selection's tokens (zs, Vs; in_s: member of the top-k set), instantiated
+    // once for the whole vocabulary in global memory and once for the list in LDS; the position of the drawn token
+    // among them, or -1 if no weight is kept
+    auto select = [&](const float* zs, int Vs, auto&& in_s) __attribute__((always_inline)) -> int {
+      // top-p: the shortest ranked prefix of the top-k set whose weight reaches p of its total
+      uint32_t kp = 0u;
+      int ip = Vs;
+      if (prm.top_p < 1.f) {
+        unsigned long long tw = 0;
+        sweep<kSweepU>(zs, tid, Vs, kSampleThreads, [&](int v, float x) __attribute__((always_inline)) {
+          if (in_s(v, x)) tw += wt(x);
+        });
+        tw = block_sum_u64(sh, tw);
+        unsigned long long target = (unsigned long long)((double)prm.top_p * (double)tw);
+        if (target < 1) target = 1;
+        unsigned long long above = 0;
+        radix_select(sh, zs, Vs, in_s, key, wt, target, kp, above);
+        const uint32_t K = kp;
+        ip = index_scan(sh, zs, Vs,
+                        [&](int v, float x) __attribute__((always_inline)) { return in_s(v, x) && key(x) == K; }, wt,
+                        target - above);
+      }
+      const uint32_t K2 = kp;
+      const int I2 = ip;
+      // min-p: weight at least min_p of the top token's
+      auto kept = [&](int v, float x) __attribute__((always_inline)) {
+        if (!in_s(v, x)) return false;
+        const uint32_t k = key(x);
+        if (!(k > K2 || (k == K2 && v <= I2))) return false;
+        return x * inv_t - smax >= lmin;
+      };
+      // the draw: inverse CDF in index order over the kept weights (the segment sums of the total are the scan's
+      // first level)
+      const unsigned long long tw = segment_sums(sh, zs, Vs, kept, wt);
+      unsigned long long target = (unsigned long long)(u * (double)tw) + 1ull;
+      if (target > tw) target = tw;
+      return tw > 0 ? index_scan(sh, zs, Vs, kept, wt, target, true) : -1;
+    };
+    if (listed) {
+      const float* lx = sh.lx;
+      const int i = select(lx, n, [](int, float) __attribute__((always_inline)) { return true; });
+      if (i >= 0) token = sh.lv[i];
+    } else {
+      const int i = select(z, V, in_k);
+      if (i >= 0) token = i;
+    }
     if (tid == 0) p.draws[r] = d + 1u;
   }
 

@@ -23,6 +23,8 @@ PARAMS = [   # one row each: (temperature, top_k, top_p, min_p, rep, presence, f
     (0.9, 0, 1.0, 0.0, 1.0, 0.0, 0.0, 8),
     (1.2, 20, 0.9, 0.0, 1.1, 0.0, 0.05, 3),
     (0.7, 0, 0.8, 0.05, 1.0, 0.3, 0.0, 0),
+    (1.0, 50, 1.0, 0.1, 1.0, 0.0, 0.0, 2),      # top-k alone (the set gathered into LDS), with min-p
+    (0.8, 1500, 0.7, 0.0, 1.0, 0.0, 0.0, 0),    # top-k above the gathered-set limit: the whole-vocabulary path
 ]
 
 
@@ -56,7 +58,7 @@ def _set(eng, w, rng, shift=0):
 
 
 @pytest.mark.parametrize("name,shift", [("tiny-fp32", 1), ("tiny-fp32", 2), ("8b-fused", 0), ("8b-fused", 2),
-                                        ("8b-fused", 3), ("8b-r8", 0)])
+                                        ("8b-fused", 3), ("8b-fused", 4), ("8b-fused", 5), ("8b-r8", 0)])
 def test_sampler_follows_oracle(name, shift):
     w = _workload(name)
     ws = synth.make_weights(w.model)
