@@ -1554,31 +1554,65 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
   float* z = p.z + (size_t)r * V;
 
   // ---- adjusted logits: repetition penalty on seen tokens (toward zero), presence and frequency, bias; NaN -> -inf
-  // (four tokens per thread in flight, three loads each)
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int base = tid; base < V; base += 4 * kSampleThreads) {
-    float xl[4], xb[4];
-    int xc[4];
+  auto adjust = [&](float x, int c, float bias_v) __attribute__((always_inline)) {
+    if (x != x) x = -INFINITY;
+    if (c > 0) x = (x > 0.f ? x / prm.rep : x * prm.rep) - prm.presence - prm.frequency * (float)c;
+    x += bias_v;
+    if (x != x) x = -INFINITY;
+    return x;
+  };
+  if ((V & 3) == 0) {
+    // 16-byte loads, four tokens each, four of them per thread in flight (rows start 16-byte aligned)
+    const int V4 = V >> 2;
+    const float4* lg4 = reinterpret_cast<const float4*>(lg);
+    const int4* cnt4 = reinterpret_cast<const int4*>(cnt);
+    const float4* bias4 = reinterpret_cast<const float4*>(bias);
+    float4* z4 = reinterpret_cast<float4*>(z);
+    for (int base = tid; base < V4; base += 4 * kSampleThreads) {
+      float4 xl[4], xb[4];
+      int4 xc[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int v = min(base + u * kSampleThreads, V - 1);
-      xl[u] = lg[v];
-      xc[u] = cnt[v];
-      xb[u] = bias[v];
+      for (int u = 0; u < 4; ++u) {
+        const int i = min(base + u * kSampleThreads, V4 - 1);
+        xl[u] = lg4[i];
+        xc[u] = cnt4[i];
+        xb[u] = bias4[i];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = base + u * kSampleThreads;
+        if (i >= V4) break;
+        const float4 o = make_float4(adjust(xl[u].x, xc[u].x, xb[u].x), adjust(xl[u].y, xc[u].y, xb[u].y),
+                                     adjust(xl[u].z, xc[u].z, xb[u].z), adjust(xl[u].w, xc[u].w, xb[u].w));
+        z4[i] = o;
+        const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (pick_better(ov[e], 4 * i + e, bv, bi)) { bv = ov[e]; bi = 4 * i + e; }
+      }
     }
+  } else {
+    // four tokens per thread in flight, three loads each
+    for (int base = tid; base < V; base += 4 * kSampleThreads) {
+      float xl[4], xb[4];
+      int xc[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int v = base + u * kSampleThreads;
-      if (v >= V) break;
-      float x = xl[u];
-      if (x != x) x = -INFINITY;
-      const int c = xc[u];
-      if (c > 0) x = (x > 0.f ? x / prm.rep : x * prm.rep) - prm.presence - prm.frequency * (float)c;
-      x += xb[u];
-      if (x != x) x = -INFINITY;
-      z[v] = x;
-      if (pick_better(x, v, bv, bi)) { bv = x; bi = v; }
+      for (int u = 0; u < 4; ++u) {
+        const int v = min(base + u * kSampleThreads, V - 1);
+        xl[u] = lg[v];
+        xc[u] = cnt[v];
+        xb[u] = bias[v];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int v = base + u * kSampleThreads;
+        if (v >= V) break;
+        const float x = adjust(xl[u], xc[u], xb[u]);
+        z[v] = x;
+        if (pick_better(x, v, bv, bi)) { bv = x; bi = v; }
+      }
     }
   }
   block_best(sh, bv, bi);   // (its barriers also order the z stores before the sweeps below)
