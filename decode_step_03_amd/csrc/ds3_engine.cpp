@@ -76,7 +76,7 @@ struct ds3_engine {
   float* logits = nullptr;
   uint16_t *frag_hi = nullptr, *frag_lo = nullptr;   // MFMA path: activation operands
   float *skpart = nullptr, *skss = nullptr;          // MFMA path: partial products, per-block sums of squares
-  bool mfma = false;                                 // rows > 4: projections on the matrix cores
+  bool mfma = false;                                 // projections on the matrix cores (rows_on_mfma)
   bool fused = false;                                // the whole step as one persistent kernel
   float* kvnew = nullptr;                            // fused: this step's k and v [nkv][2][hd]
   unsigned* sync = nullptr;                          // fused: barrier and merge counters
@@ -154,7 +154,7 @@ struct ds3_engine {
     int rows = 0;
     int* slots = nullptr;
     float* logits = nullptr;
-    bool mfma = false;            // projections on the matrix cores (more than 4 rows)
+    bool mfma = false;            // projections on the matrix cores (rows_on_mfma)
     const int* row_map = nullptr; // K/V row of each activation row (null: the row itself)
   };
   RunCtx dec, pre, cur;
@@ -198,6 +198,14 @@ std::string fused_refusal(const ds3_config& c) {
   if (c.cap != 128 * S && c.cap != 256 * S) return "cap must be 128 or 256 positions per split";
   if (c.vocab < 16 * kFusedBlocks || c.vocab > 520 * kFusedBlocks) return "vocab out of the LM head's range";
   return "";
+}
+
+// Whether a step of R activation rows runs its projections on the matrix cores: above kMaxGemvRows rows, and for
+// 2..4 rows too when the vector path's activations (R x the widest input, float32, in LDS) do not fit a CU's LDS.
+bool rows_on_mfma(const ds3_config& c, int R) {
+  if (R > kMaxGemvRows) return true;
+  const int kres = std::max(c.ffn_dim, c.n_q_heads * c.head_dim);
+  return gemv_lds_bytes(R, c.d_model, true) > 160 * 1024 || gemv_lds_bytes(R, kres, false) > 160 * 1024;
 }
 
 std::string check_config(const ds3_config* c) {
@@ -259,41 +267,35 @@ std::string check_config(const ds3_config* c) {
   for (const int R : {c->rows, c->prefill_rows}) {
     if (R == 0) continue;
     const char* what = R == c->rows ? "rows" : "prefill_rows";
-    if (R <= kMaxGemvRows) {
-      const int kres = std::max(c->ffn_dim, c->n_q_heads * c->head_dim);
-      if (gemv_lds_bytes(R, c->d_model, true) > 160 * 1024 || gemv_lds_bytes(R, kres, false) > 160 * 1024)
-        return std::string(what) + ": activations of rows x max(d_model, ffn_dim, q width) floats exceed the 160 KB LDS";
-    } else {
-      // matrix-core path: bf16 weights in whole 16-row tiles and 32-input steps
-      if (c->weight_dtype != DS3_BF16) return std::string(what) + ": more than 4 rows needs bf16 weights (matrix-core path)";
-      if (c->d_model % kSkChunk || c->ffn_dim % kSkChunk || (c->n_q_heads * c->head_dim) % kSkChunk)
-        return "d_model, ffn_dim and n_q_heads x head_dim must be multiples of 128 for more than 4 rows";
-      if (c->head_dim % 32 || c->vocab % 32) return "head_dim and vocab must be multiples of 32 for more than 4 rows";
-      const int qkv = (c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim, qw = c->n_q_heads * c->head_dim;
-      if (!sk_plan(qkv, c->d_model, false).groups || !sk_plan(c->d_model, qw, false).groups ||
-          !sk_plan(2 * c->ffn_dim, c->d_model, false).groups || !sk_plan(c->d_model, c->ffn_dim, false).groups ||
-          !sk_plan(c->vocab, c->d_model, true).groups)
-        return "more than 4 rows: vocab, d_model, 2 x ffn_dim and (n_q_heads + 2 n_kv_heads) x head_dim must be "
-               "multiples of 128";
-    }
+    if (!rows_on_mfma(*c, R)) continue;
+    // matrix-core path: bf16 weights in whole 16-row tiles and 32-input steps
+    const std::string why_gemv = R <= kMaxGemvRows ? " (the vector path's activations of rows x max(d_model, "
+                                                     "ffn_dim, q width) floats exceed the 160 KB LDS)" : "";
+    if (c->weight_dtype != DS3_BF16)
+      return std::string(what) + ": the matrix-core path needs bf16 weights" + why_gemv;
+    if (c->d_model % kSkChunk || c->ffn_dim % kSkChunk || (c->n_q_heads * c->head_dim) % kSkChunk)
+      return std::string(what) + ": d_model, ffn_dim and n_q_heads x head_dim must be multiples of 128 on the "
+             "matrix-core path" + why_gemv;
+    if (c->head_dim % 32 || c->vocab % 32)
+      return std::string(what) + ": head_dim and vocab must be multiples of 32 on the matrix-core path" + why_gemv;
+    const int qkv = (c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim, qw = c->n_q_heads * c->head_dim;
+    if (!sk_plan(qkv, c->d_model, false).groups || !sk_plan(c->d_model, qw, false).groups ||
+        !sk_plan(2 * c->ffn_dim, c->d_model, false).groups || !sk_plan(c->d_model, c->ffn_dim, false).groups ||
+        !sk_plan(c->vocab, c->d_model, true).groups)
+      return std::string(what) + ": vocab, d_model, 2 x ffn_dim and (n_q_heads + 2 n_kv_heads) x head_dim must be "
+             "multiples of 128 on the matrix-core path" + why_gemv;
   }
   return "";
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  if (!v || !*v) return dflt;
-  const int x = std::atoi(v);
-  return x > 0 ? x : dflt;
-}
-
-// Attention split plan: about DS3_ATTN_BLOCKS blocks (default 512) over rows x kv heads x splits.
-// A split is a whole number of LDS chunks, and there are no more splits than the in-kernel merge takes.
+// Attention split plan: about kAttnBlocks blocks over rows x kv heads x splits (measured best among 256..1024 on
+// MI355X). A split is a whole number of LDS chunks, and there are no more splits than the in-kernel merge takes.
+// The plan is a function of the configuration alone, so one configuration always reduces in the same order.
+constexpr int kAttnBlocks = 512;
 void plan_splits(const ds3_config& c, int* splits, int* split_len) {
   const int chunk = attn_positions_per_pass(c.head_dim, c.kv_dtype);
   const int units = (c.cap + chunk - 1) / chunk;
-  const int target_blocks = env_int("DS3_ATTN_BLOCKS", 512);
-  int s = std::max(1, target_blocks / (c.rows * c.n_kv_heads));
+  int s = std::max(1, kAttnBlocks / (c.rows * c.n_kv_heads));
   s = std::min(s, units);
   s = std::min(s, attn_max_splits(c.n_q_heads, c.n_kv_heads, c.head_dim));
   const int per = (units + s - 1) / s;
@@ -340,11 +342,12 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
   w.rope = take((size_t)c.cap * (c.head_dim / 2) * 2 * 4);
   w.slot_map = take(c.kv_layout == DS3_KV_PAGED ? (size_t)c.rows * (c.cap / c.page_size) * 4 : 4);
   const size_t kmax = (size_t)std::max(std::max(c.d_model, c.ffn_dim), c.n_q_heads * c.head_dim);
-  const size_t frag = RA > (size_t)kMaxGemvRows ? kmax * kMfmaRows * 2 : 16;
+  const bool any_mfma = rows_on_mfma(c, c.rows) || (c.prefill_rows > 0 && rows_on_mfma(c, c.prefill_rows));
+  const size_t frag = any_mfma ? kmax * kMfmaRows * 2 : 16;
   w.frag_hi = take(frag);
   w.frag_lo = take(frag);
   size_t skp = 4;
-  if (RA > (size_t)kMaxGemvRows) {
+  if (any_mfma) {
     const int qkv = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim, qw = c.n_q_heads * c.head_dim;
     for (const SkPlan& sp : {sk_plan(qkv, c.d_model, false), sk_plan(c.d_model, qw, false),
                              sk_plan(2 * c.ffn_dim, c.d_model, false), sk_plan(c.d_model, c.ffn_dim, false)})
@@ -424,12 +427,8 @@ double kind_bytes(const ds3_config& c, int kind) {
 }
 
 // GEMV launch: one resident round of waves (2 per SIMD at these kernels' register use: 8 per CU, 2048 on 256
-// CUs, i.e. 2 blocks of 4 waves per CU); measured best among 256..4096 blocks. DS3_GEMV_BLOCKS overrides it.
-int gemv_blocks(int n_pairs, int cus) {
-  const int forced = env_int("DS3_GEMV_BLOCKS", 0);
-  const int target = forced > 0 ? forced : 2 * cus;
-  return std::max(1, std::min(target, (n_pairs + 3) / 4));
-}
+// CUs, i.e. 2 blocks of 4 waves per CU); measured best among 256..4096 blocks.
+int gemv_blocks(int n_pairs, int cus) { return std::max(1, std::min(2 * cus, (n_pairs + 3) / 4)); }
 
 ds3_status wait_done(ds3_engine* e, hipEvent_t ev, uint32_t timeout_ms) {
   const auto t0 = std::chrono::steady_clock::now();
@@ -499,7 +498,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
     p.layer = l.layer;
     p.slots = e->cur.slots;
     p.status = e->status;
-    p.ping_pong = env_int("DS3_GEMV_PP", 1) == 1;
+    p.ping_pong = true;
   };
   switch (l.kind) {
     case K_FUSED: {
@@ -840,7 +839,7 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   e->frag_lo = reinterpret_cast<uint16_t*>(work + wp.frag_lo);
   e->skpart = reinterpret_cast<float*>(work + wp.skpart);
   e->skss = reinterpret_cast<float*>(work + wp.skss);
-  e->mfma = c.rows > kMaxGemvRows;
+  e->mfma = rows_on_mfma(c, c.rows);
   e->work_bytes = wp.total;
   e->logits = reinterpret_cast<float*>(e->buf[DS3_BUF_LOGITS]);
 
@@ -933,7 +932,7 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
     e->pre.rows = T;
     e->pre.slots = reinterpret_cast<int*>(work + wp.pre_slots);
     e->pre.logits = reinterpret_cast<float*>(work + wp.pre_logits);
-    e->pre.mfma = T > kMaxGemvRows;
+    e->pre.mfma = rows_on_mfma(c, T);
     e->pre.row_map = e->pre.slots + SlotLayout{T}.words();
     per_op(e->pre_sequence, e->pre.mfma, false);
     h = hipHostMalloc(reinterpret_cast<void**>(&e->h_pre),
@@ -1143,16 +1142,21 @@ static ds3_status run_steps(ds3_engine* e, const int32_t* tokens, const int32_t*
     return fail(e, DS3_E_INVALID, "n_steps must be in 1.." + std::to_string(kMaxChain));
   const SlotLayout sl{c.rows};
   const bool paged = c.kv_layout == DS3_KV_PAGED;
-  if (paged && !write_map && !e->slot_map_set) return fail(e, DS3_E_INVALID, "paged step needs a slot map");
-  if (paged && n_steps > 1 && !e->slot_map_set) return fail(e, DS3_E_INVALID, "chained paged steps need a slot map");
+  // attention reads every position through the page table, so no paged step runs before one was set
+  if (paged && !e->slot_map_set) return fail(e, DS3_E_INVALID, "paged step needs a slot map (ds3_set_slot_map)");
   for (int r = 0; r < c.rows; ++r) {
     if (tokens[r] < 0 || tokens[r] >= c.vocab) return fail(e, DS3_E_INVALID, "token out of range in row " + std::to_string(r));
     if (pos[r] < 0 || pos[r] >= c.cap) return fail(e, DS3_E_INVALID, "pos out of range in row " + std::to_string(r));
     if ((int64_t)pos[r] + n_steps > c.cap)
       return fail(e, DS3_E_INVALID, "pos + n_steps passes the capacity in row " + std::to_string(r));
-    if (paged && write_map &&
-        (write_map[r] < 0 || (int64_t)write_map[r] >= (int64_t)c.pool_pages * c.page_size))
-      return fail(e, DS3_E_INVALID, "write_map out of range in row " + std::to_string(r));
+    if (paged && write_map) {
+      // the K/V write must land where the sweep reads position pos[r]: its page-table slot
+      const int ppr = c.cap / c.page_size;
+      const int64_t want =
+          (int64_t)e->h_slot_map[(size_t)r * ppr + pos[r] / c.page_size] * c.page_size + pos[r] % c.page_size;
+      if (write_map[r] != want)
+        return fail(e, DS3_E_INVALID, "write_map of row " + std::to_string(r) + " is not the page-table slot of pos");
+    }
   }
   // slot words, then the status words (cleared every call by the same copy)
   for (int r = 0; r < c.rows; ++r) {

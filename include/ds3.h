@@ -71,7 +71,11 @@ enum { DS3_TRACE_OFF = 0, DS3_TRACE_BARRIERS = 1, DS3_TRACE_PHASES = 2 };
  * and the LM head ("Models, Registry and the Driver" page, section "Shared components": embed, one layer scope
  * per layer with x += mixer(norm(x)); x += ffn(norm(x)), final norm, head).
  *
- * rows: sequences per step (1..16). cap: KV capacity per row (positions 0..cap-1). kv_layout CONTIGUOUS keeps
+ * rows: sequences per step (1..16). Up to 4 rows run the projections as vector GEMVs, more on the matrix cores
+ * (bf16 weights, widths multiples of 128); 2..4 rows also go to the matrix cores when their activations (rows x
+ * max(d_model, ffn_dim, q width) floats) do not fit a compute unit's 160 KB LDS, e.g. 3 or 4 rows of the 8B shape
+ * ("Models, Registry and the Driver" page, section "The Model": a step shape of any number of sequences).
+ * cap: KV capacity per row (positions 0..cap-1). kv_layout CONTIGUOUS keeps
  * K and V as [layer][row][kv_head][cap][head_dim]; PAGED keeps a pool [layer][page][kv_head][page_size][head_dim]
  * of pool_pages pages addressed through a per-row page table (see ds3_set_slot_map). timeout_ms = 0 selects the
  * default of 600000 ms ("Execution" page, section "Failure handling": every device wait is bounded).
@@ -183,7 +187,10 @@ ds3_status ds3_set_slot_map(ds3_engine* e, const int32_t* slot_map);
  * so positions need not be consecutive and a prefill is a sequence of steps). K/V of positions below pos[r] must
  * already be in the state (earlier steps or ds3_write_kv). The first step in graph mode captures the kernel
  * sequence into a HIP graph; every step replays it. If logits_host is not NULL the logits are also copied there.
- * flags (may be NULL) receives bit 0 = some logit is NaN or infinite (not an error by itself). */
+ * flags (may be NULL) receives bit 0 = some logit is NaN or infinite (not an error by itself).
+ * Paged layout: every step needs the page table (ds3_set_slot_map first, else DS3_E_INVALID), because the sweep
+ * reads every position through it; an explicit write_map[r] must equal the page-table slot of pos[r] given above
+ * (else DS3_E_INVALID: a K/V row written elsewhere would never be read at pos[r]). */
 ds3_status ds3_step(ds3_engine* e, const int32_t* tokens, const int32_t* pos, const int32_t* write_map,
                     float* logits_host, uint32_t* flags);
 
@@ -253,8 +260,8 @@ ds3_status ds3_step_sample(ds3_engine* e, const int32_t* tokens, const int32_t* 
  * graph replay): chunk k is a step of prefill_rows activation rows that all read and write the same K/V row, token
  * t of the chunk at position pos0 + k prefill_rows + t, so its attention sees the K/V of the chunk's earlier tokens
  * (written by the same step before the attention runs) and nothing after its own position -- the causal mask
- * inside the chunk is the position mask of the decode step. More than 4 rows run the projections on the matrix
- * cores. The rows after the last token of the last chunk repeat that token at its position. logits_host (float32
+ * inside the chunk is the position mask of the decode step. Chunks run their projections on the matrix cores
+ * under the same rule as decode rows (see the rows field of ds3_config). The rows after the last token of the last chunk repeat that token at its position. logits_host (float32
  * [vocab], may be NULL) receives the last token's logits, from which the first decode step's token is picked;
  * flags (may be NULL) bit 0: some logit of the prefill was NaN or infinite. n in 1..DS3_MAX_PREFILL; pos0 + n must
  * not pass cap; paged layout: the page table must be set. DS3_E_UNSUPPORTED when the engine was created with

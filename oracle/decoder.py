@@ -37,7 +37,7 @@ import numpy as np
 __all__ = [
     "widen", "round_to_bf16", "round_to_kv", "rmsnorm", "rope_inv_freq", "apply_rope", "softmax",
     "attend_prefix", "masked_cap_attend", "silu", "matvec", "OracleModel", "RowCache", "decode_step",
-    "causal_forward", "greedy",
+    "decode_rows", "causal_forward", "greedy",
 ]
 
 _MATVEC_ROWS = 256          # weight rows widened at a time (keeps the float64 copy cache-sized)
@@ -134,18 +134,18 @@ def attend_prefix(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
 
     q: [nq, hd]; K, V: [nkv, n, hd] holding exactly the visible positions 0..p (n = p + 1).
     Query head h reads kv head h // (nq / nkv) (contiguous groups). Scores are q.k / sqrt(hd).
-    Returns [nq, hd].
+    Returns [nq, hd]. (Each kv head is widened to float64 once and serves its group of query heads.)
     """
     nq, hd = q.shape
     nkv = K.shape[0]
     rep = nq // nkv
     out = np.empty((nq, hd), dtype=np.float64)
-    for h in range(nq):
-        g = h // rep
+    for g in range(nkv):
         Kg = np.asarray(K[g], dtype=np.float64)
         Vg = np.asarray(V[g], dtype=np.float64)
-        w = softmax(Kg @ q[h] / math.sqrt(hd))
-        out[h] = w @ Vg
+        for h in range(g * rep, (g + 1) * rep):
+            w = softmax(Kg @ q[h] / math.sqrt(hd))
+            out[h] = w @ Vg
     return out
 
 
@@ -179,7 +179,11 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 
 def matvec(W: np.ndarray, h: np.ndarray) -> np.ndarray:
-    """W @ h in float64 for a stored [out, in] matrix; rows are widened a block at a time."""
+    """W @ h in float64 for a stored [out, in] matrix; rows are widened a block at a time.
+
+    h is one input vector [in] or several independent ones as the columns of [in, R] (result [out, R]): the same
+    products, one weight pass for all of them.
+    """
     global _pool
     h = np.asarray(h, dtype=np.float64)
     n = W.shape[0]
@@ -262,11 +266,42 @@ def decode_step(model: OracleModel, cache: RowCache, token: int, p: int, *, trac
     return matvec(model.glob["lm_head"], rmsnorm(x, model.glob["final_norm"], eps))
 
 
-def causal_forward(model: OracleModel, tokens, kv_dtype: str) -> np.ndarray:
+def decode_rows(model: OracleModel, caches, tokens, positions) -> np.ndarray:
+    """One decode step of several independent rows: row r takes tokens[r] at absolute position positions[r] with
+    its own cache caches[r]. Returns logits [rows, vocab] (float64).
+
+    Each row computes exactly what `decode_step` computes for it alone; the only difference is that every weight
+    matrix is multiplied with the rows' activations as the columns of one matrix (one weight pass per step).
+    """
+    nq, nkv, hd = model.n_q_heads, model.n_kv_heads, model.head_dim
+    eps = model.rms_eps
+    R = len(tokens)
+    X = np.stack([widen(model.glob["embed"][int(t)]) for t in tokens])                # [R, d]
+    for li, L in enumerate(model.layers):
+        H = rmsnorm(X, L["attn_norm"], eps)
+        Qa, Ka, Va = matvec(L["wq"], H.T).T, matvec(L["wk"], H.T).T, matvec(L["wv"], H.T).T
+        O = np.empty((R, nq * hd))
+        for r in range(R):
+            p = int(positions[r])
+            q = apply_rope(Qa[r].reshape(nq, hd), p, model.rope_theta)
+            k = apply_rope(Ka[r].reshape(nkv, hd), p, model.rope_theta)
+            c = caches[r]
+            c.K[li][:, p] = round_to_kv(k, c.kv_dtype)
+            c.V[li][:, p] = round_to_kv(Va[r].reshape(nkv, hd), c.kv_dtype)
+            O[r] = attend_prefix(q, c.K[li][:, :p + 1], c.V[li][:, :p + 1]).reshape(-1)
+        X = X + matvec(L["wo"], O.T).T
+        H2 = rmsnorm(X, L["ffn_norm"], eps)
+        A = silu(matvec(L["w_gate"], H2.T)) * matvec(L["w_up"], H2.T)
+        X = X + matvec(L["w_down"], A).T
+    return matvec(model.glob["lm_head"], rmsnorm(X, model.glob["final_norm"], eps).T).T
+
+
+def causal_forward(model: OracleModel, tokens, kv_dtype: str, cache: "RowCache | None" = None) -> np.ndarray:
     """All positions of a prefix at once: logits [T, vocab] for tokens at positions 0..T-1.
 
-    No cache: each layer forms K and V for the whole prefix (rounded to the KV dtype, as the cache would hold
-    them) and applies a full [T, T] causal mask (key j visible to query i iff j <= i).
+    No cache is read: each layer forms K and V for the whole prefix (rounded to the KV dtype, as the cache would
+    hold them) and applies a full [T, T] causal mask (key j visible to query i iff j <= i). When `cache` is given
+    it receives those K and V at positions 0..T-1 of every layer (what T decode steps would have written).
     """
     tokens = np.asarray(tokens)
     T = len(tokens)
@@ -275,13 +310,16 @@ def causal_forward(model: OracleModel, tokens, kv_dtype: str) -> np.ndarray:
     eps = model.rms_eps
     X = np.stack([widen(model.glob["embed"][t]) for t in tokens])                  # [T, d]
     causal = np.tril(np.ones((T, T), dtype=bool))
-    for L in model.layers:
+    for li, L in enumerate(model.layers):
         H = rmsnorm(X, L["attn_norm"], eps)
-        Wq, Wk = widen(L["wq"]), widen(L["wk"])
-        Q = np.stack([apply_rope((Wq @ H[i]).reshape(nq, hd), i, model.rope_theta) for i in range(T)])
-        Kx = np.stack([apply_rope((Wk @ H[i]).reshape(nkv, hd), i, model.rope_theta) for i in range(T)])
+        QH, KH = H @ widen(L["wq"]).T, H @ widen(L["wk"]).T                        # [T, nq hd], [T, nkv hd]
+        Q = np.stack([apply_rope(QH[i].reshape(nq, hd), i, model.rope_theta) for i in range(T)])
+        Kx = np.stack([apply_rope(KH[i].reshape(nkv, hd), i, model.rope_theta) for i in range(T)])
         Vx = (H @ widen(L["wv"]).T).reshape(T, nkv, hd)
         Kx, Vx = round_to_kv(Kx, kv_dtype), round_to_kv(Vx, kv_dtype)
+        if cache is not None:
+            cache.K[li][:, :T] = Kx.transpose(1, 0, 2)
+            cache.V[li][:, :T] = Vx.transpose(1, 0, 2)
         O = np.empty((T, nq, hd))
         for hh in range(nq):
             g = hh // rep

@@ -5,8 +5,11 @@ arithmetic.
 """
 from __future__ import annotations
 
+import functools
+import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -23,6 +26,15 @@ GREEDY_MARGIN = 5e-2
 def log(*a):
     print("[ds3-test]", *a, flush=True)
     sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=2)
+def weights(model: synth.ModelShape, gains: str = "ones") -> synth.WeightSet:
+    """The seeded weights of `model`, drawn once per test session (the 8B shape's 16 GB serve every test of it)."""
+    t0 = time.time()
+    ws = synth.make_weights(model, gains=gains)
+    log(f"weights of {model.name} ({model.n_layers} layers) drawn in {time.time() - t0:.1f}s")
+    return ws
 
 
 def logits_tol(w: synth.Workload) -> float:
@@ -66,32 +78,42 @@ def kv_to_f64(a: np.ndarray) -> np.ndarray:
 class Lockstep:
     """Runs the engine and the oracle side by side, teacher-forced by the oracle's greedy token."""
 
-    def __init__(self, w: synth.Workload, ws: synth.WeightSet, engine, n_alloc: int | None = None):
+    def __init__(self, w: synth.Workload, ws: synth.WeightSet, engine, n_alloc=None):
+        """n_alloc: positions the oracle's cache holds per row (an int for every row, or one per row); the
+        capacity when None."""
         self.w, self.ws, self.engine = w, ws, engine
         self.model = oracle.OracleModel.from_weightset(ws)
-        self.caches = [oracle.RowCache(self.model, n_alloc or w.cap, w.kv_dtype) for _ in range(w.rows)]
+        per_row = [n_alloc or w.cap] * w.rows if not hasattr(n_alloc, "__len__") else list(n_alloc)
+        self.caches = [oracle.RowCache(self.model, int(n), w.kv_dtype) for n in per_row]
         self.max_err = 0.0
         self.greedy_checked = 0
         self.greedy_flips_inside_margin = 0
 
     def prefill_random_kv(self, n_pos_per_row, seed=0):
-        """K/V contents ~ N(0,1) (stored in the KV dtype) at positions [0, n) of every row and layer, both sides."""
-        for r, n in enumerate(n_pos_per_row):
-            if n == 0:
-                continue
-            for li in range(self.w.model.n_layers):
-                K = synth.kv_prefill(self.w, li, r, "k", n, seed)
-                V = synth.kv_prefill(self.w, li, r, "v", n, seed)
-                self.engine.write_kv(li, r, 0, K, V)
-                self.caches[r].set(li, 0, K, V)
+        """K/V contents ~ N(0,1) (stored in the KV dtype) at positions [0, n) of every row and layer, both sides.
+        The draws run on a thread pool (a window of jobs at a time); the engine and the oracle take them in order."""
+        jobs = [(li, r, int(n)) for r, n in enumerate(n_pos_per_row) if n > 0 for li in range(self.w.model.n_layers)]
+
+        def gen(job):
+            li, r, n = job
+            return li, r, synth.kv_prefill(self.w, li, r, "k", n, seed), synth.kv_prefill(self.w, li, r, "v", n, seed)
+
+        t0 = time.time()
+        window = 32
+        with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+            for lo in range(0, len(jobs), window):
+                for li, r, K, V in ex.map(gen, jobs[lo:lo + window]):
+                    self.engine.write_kv(li, r, 0, K, V)
+                    self.caches[r].set(li, 0, K, V)
+        if len(jobs) > 64:
+            log(f"K/V pre-filled for {len(jobs)} (layer, row) pairs in {time.time() - t0:.1f}s")
 
     def step(self, tokens, pos, write_map=None, check=True):
         t0 = time.time()
         got, flags = self.engine.step(tokens, pos, write_map)
         got = got.copy()
         t1 = time.time()
-        ref = np.stack([oracle.decode_step(self.model, self.caches[r], int(tokens[r]), int(pos[r]))
-                        for r in range(self.w.rows)])
+        ref = oracle.decode_rows(self.model, self.caches, [int(t) for t in tokens], [int(p) for p in pos])
         t2 = time.time()
         if check:
             self.check_logits(got, ref, flags)

@@ -58,6 +58,15 @@ def test_five_rows_padded_tile():
     _run(w, ws, [0, 7, 300, 513, 1000], steps=3)
 
 
+@pytest.mark.parametrize("rows", [3, 4])
+def test_three_and_four_rows_of_the_8b_shape(rows):
+    """3 and 4 rows of the 8B-shaped layers: the vector path's activations (rows x 14336 floats) do not fit the LDS,
+    so these steps run their projections on the matrix cores (padded tile), and must match the oracle."""
+    w = replace(_layers2("llama8b-bf16-r8-cap32768", cap=2048), rows=rows, name=f"llama8b-2l-r{rows}")
+    ws = synth.make_weights(w.model, gains="random")
+    _run(w, ws, [0, 1000, 2040, 513][:rows], steps=3)
+
+
 def test_sixteen_rows_paged_and_page_table_invariance():
     """16 rows over a paged pool (16-token pages): parity with the oracle, and bit-identical logits for two
     different page tables (identity and a random permutation of the pool)."""

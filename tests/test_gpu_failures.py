@@ -100,3 +100,29 @@ def test_unsupported_config_is_refused_with_field():
     with pytest.raises(DS3Error) as ei:
         C.ds3_query_buffers(cfg)
     assert ei.value.status == C.DS3_E_UNSUPPORTED and "head_dim" in ei.value.message
+
+
+def test_paged_step_needs_the_page_table_and_a_consistent_write_map():
+    """A paged step reads every position through the page table: without one, every step is refused, also with an
+    explicit write map; an explicit write map must be the page-table slot of pos. Nothing runs on the device."""
+    base = synth.workload("llama8b-bf16-r16-paged")
+    w = replace(synth.small_variant(base, n_layers=1, vocab=1024, cap=256, pool_pages=40), rows=2, name="paged-guard")
+    ws = synth.make_weights(w.model)
+    eng = make_engine(w, ws)
+    try:
+        tok, pos = np.array([1, 2], np.int32), np.array([5, 17], np.int32)
+        for wm in (None, np.array([5, 17], np.int32)):
+            with pytest.raises(DS3Error) as ei:
+                eng.step(tok, pos, wm)
+            assert ei.value.status == C.DS3_E_INVALID and "slot map" in ei.value.message
+        table = np.arange(32, dtype=np.int32)[::-1].copy().reshape(2, 16)
+        eng.set_slot_map(table)
+        good = np.array([table[0, 0] * 16 + 5, table[1, 1] * 16 + 1], np.int32)
+        with pytest.raises(DS3Error) as ei:
+            eng.step(tok, pos, good + 1)
+        assert ei.value.status == C.DS3_E_INVALID and "write_map" in ei.value.message
+        eng.step(tok, pos, good)
+        eng.step(tok, pos + 1)
+        assert eng.stats()["state"] == 0
+    finally:
+        eng.close()

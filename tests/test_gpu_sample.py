@@ -14,7 +14,7 @@ import bench
 import synth
 from decode_step_03_amd import DS3Error, _ds3 as C
 from oracle import sampler as S
-from tests.ds3_testlib import log, make_engine
+from tests.ds3_testlib import log, make_engine, weights
 
 pytestmark = pytest.mark.gpu
 
@@ -25,6 +25,8 @@ PARAMS = [   # one row each: (temperature, top_k, top_p, min_p, rep, presence, f
     (0.7, 0, 0.8, 0.05, 1.0, 0.3, 0.0, 0),
     (1.0, 50, 1.0, 0.1, 1.0, 0.0, 0.0, 2),      # top-k alone (the set gathered into LDS), with min-p
     (0.8, 1500, 0.7, 0.0, 1.0, 0.0, 0.0, 0),    # top-k above the gathered-set limit: the whole-vocabulary path
+    (0.8, 40, 0.95, 0.02, 1.1, 0.0, 0.0, 5),    # the parameters bench.py times
+    (1.0, 5000, 0.98, 0.0, 1.0, 0.1, 0.0, 1),   # a large top-k with top-p
 ]
 
 
@@ -34,6 +36,9 @@ def _workload(name):
     if name == "8b-fused":
         base = synth.workload("llama8b-bf16-cap8192")
         return replace(synth.small_variant(base, n_layers=1, vocab=4096), name="llama8b-1l-sample")
+    if name == "8b-fullvocab":   # the full 128,256-token vocabulary the benchmark samples from
+        base = synth.workload("llama8b-bf16-cap8192")
+        return replace(synth.small_variant(base, n_layers=1), name="llama8b-1l-sample-v128256")
     if name == "8b-r8":
         base = synth.workload("llama8b-bf16-r8-cap32768")
         return replace(synth.small_variant(base, n_layers=1, vocab=4096, cap=4096), name="llama8b-r8-sample")
@@ -58,10 +63,11 @@ def _set(eng, w, rng, shift=0):
 
 
 @pytest.mark.parametrize("name,shift", [("tiny-fp32", 1), ("tiny-fp32", 2), ("8b-fused", 0), ("8b-fused", 2),
-                                        ("8b-fused", 3), ("8b-fused", 4), ("8b-fused", 5), ("8b-r8", 0)])
+                                        ("8b-fused", 3), ("8b-fused", 4), ("8b-fused", 5), ("8b-r8", 0),
+                                        ("8b-fullvocab", 6), ("8b-fullvocab", 7), ("8b-fullvocab", 5)])
 def test_sampler_follows_oracle(name, shift):
     w = _workload(name)
-    ws = synth.make_weights(w.model)
+    ws = weights(w.model)
     a = make_engine(w, ws)
     b = make_engine(w, ws)
     try:
@@ -95,11 +101,19 @@ def test_sampler_follows_oracle(name, shift):
                         j = int(np.nonzero(kept == got)[0][0])
                         assert run[j] - 1e-4 <= u <= run[j + 1] + 1e-4, f"step {i} row {r}: u {u} outside [{run[j]}, {run[j + 1]}]"
                         checked += 1
-                    else:   # only a token on a cut boundary may differ from the oracle's kept set
+                    else:
+                        # only a token on a cut boundary may differ from the oracle's kept set (the device cuts on
+                        # fixed-point weights): its score is within 1e-4 of the last kept one, and u falls in its
+                        # inverse-CDF interval once it is added to the kept set
                         s = z / T
                         order = np.lexsort((np.arange(s.size), -s))
                         rank = int(np.nonzero(order == got)[0][0])
                         assert abs(s[got] - s[order[min(rank, len(kept)) - 1]]) < 1e-4, f"step {i} row {r}: {got} not kept"
+                        k2 = np.sort(np.append(kept, got))
+                        w2 = np.exp(s[k2] - np.max(s[k2]))
+                        run2 = np.concatenate([[0.0], np.cumsum(w2)]) / np.sum(w2)
+                        j = int(np.nonzero(k2 == got)[0][0])
+                        assert run2[j] - 1e-4 <= u <= run2[j + 1] + 1e-4, f"step {i} row {r}: u {u} outside the cut token's interval"
                     drawn += 1
                 if nl > 0:
                     top, lps, lt = S.logprobs(z, T, nl, got)

@@ -5,6 +5,8 @@
 * A one-layer toy decoder evaluated with plain Python loops (no numpy) must give the same logits: this pins the
   order of the pre-norm residual pair, which weight feeds which product, and the head.
 * The cache holds exactly the rounded k and v of each position.
+* Rows of a step are independent: the several-row step equals the one-row step of each row, and the K/V a causal
+  forward forms for a prefix equal what the step-by-step decode writes into the cache.
 """
 import math
 
@@ -31,6 +33,52 @@ def test_step_by_step_equals_causal_forward(kv_dtype, wdtype, kvh):
     for p, t in enumerate(tokens):
         got = oracle.decode_step(model, cache, int(t), p)
         np.testing.assert_allclose(got, ref[p], rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("kv_dtype,wdtype", [("f32", "f32"), ("bf16", "bf16")])
+def test_rows_step_equals_each_row_alone(kv_dtype, wdtype):
+    """Three rows at different positions with different histories: decode_rows gives each row the logits and the
+    cache entries that decode_step gives it alone (the rows only share the weight passes)."""
+    model = _tiny_model(kv_heads=2, dtype=wdtype)
+    rng = np.random.default_rng(4)
+    positions = [0, 5, 13]
+    tokens = rng.integers(0, model.vocab, size=3)
+    a = [oracle.RowCache(model, 16, kv_dtype) for _ in positions]
+    b = [oracle.RowCache(model, 16, kv_dtype) for _ in positions]
+    for r, p in enumerate(positions):
+        for li in range(model.n_layers):
+            K = oracle.round_to_kv(rng.standard_normal((2, p, 8)), kv_dtype).astype(np.float32)
+            V = oracle.round_to_kv(rng.standard_normal((2, p, 8)), kv_dtype).astype(np.float32)
+            a[r].set(li, 0, K, V)
+            b[r].set(li, 0, K, V)
+    got = oracle.decode_rows(model, a, tokens, positions)
+    for r, p in enumerate(positions):
+        ref = oracle.decode_step(model, b[r], int(tokens[r]), p)
+        np.testing.assert_allclose(got[r], ref, rtol=1e-11, atol=1e-12)
+        for li in range(model.n_layers):
+            np.testing.assert_array_equal(a[r].K[li], b[r].K[li])
+            np.testing.assert_array_equal(a[r].V[li], b[r].V[li])
+
+
+@pytest.mark.parametrize("kv_dtype,wdtype", [("f32", "f32"), ("bf16", "bf16")])
+def test_causal_forward_cache_equals_step_by_step_cache(kv_dtype, wdtype):
+    """The K/V a causal forward returns for a prefix are the ones T decode steps write, up to one unit in the last
+    place of the KV dtype (the two evaluate the same float64 products in a different order before rounding)."""
+    model = _tiny_model(kv_heads=2, dtype=wdtype)
+    tokens = np.random.default_rng(6).integers(0, model.vocab, size=11)
+    c1 = oracle.RowCache(model, 16, kv_dtype)
+    c2 = oracle.RowCache(model, 16, kv_dtype)
+    oracle.causal_forward(model, tokens, kv_dtype, cache=c1)
+    for p, t in enumerate(tokens):
+        oracle.decode_step(model, c2, int(t), p)
+    ulp_bits = 8 if kv_dtype == "bf16" else 24
+    for li in range(model.n_layers):
+        for A, B in ((c1.K[li], c2.K[li]), (c1.V[li], c2.V[li])):
+            a, b = A.astype(np.float64), B.astype(np.float64)
+            assert np.any(a[:, :11] != 0)
+            np.testing.assert_array_equal(a[:, 11:], 0.0)
+            ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(b), 1e-30))[1] - ulp_bits)
+            assert np.all(np.abs(a - b) <= ulp)
 
 
 def test_cache_holds_rounded_k_and_v():
