@@ -37,6 +37,7 @@ DS3_MAX_CHAIN = 1024
 DS3_SWEEP_FULL, DS3_SWEEP_VISIBLE = 0, 1
 DS3_MAX_PREFILL = 8192
 DS3_MAX_LOGPROBS = 8
+DS3_NOALLOC_MAX_BYTES = 8 << 20   # the fixed device array of ds3_write_kv_noalloc
 DS3_BUF_WEIGHTS, DS3_BUF_KV, DS3_BUF_WORK, DS3_BUF_LOGITS, DS3_NUM_BUFFERS = 0, 1, 2, 3, 4
 DS3_INJECT_KERNEL_CHECK, DS3_INJECT_TIMEOUT_NEXT, DS3_INJECT_BARRIER_TIMEOUT = 1, 2, 3
 
@@ -95,6 +96,7 @@ SIGNATURES = [
     ("ds3_reset_state", c_int32, [c_void_p]),
     ("ds3_write_kv", c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     ("ds3_read_kv", c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
+    ("ds3_write_kv_noalloc", c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     ("ds3_stats_get", c_int32, [c_void_p, POINTER(ds3_stats)]),
     ("ds3_profile_kernels", c_int32, [c_void_p, c_int32, POINTER(ds3_kernel_time), POINTER(c_int32)]),
     ("ds3_phase_trace", c_int32, [c_void_p, POINTER(c_uint64), POINTER(c_int32)]),
@@ -209,6 +211,10 @@ def ds3_write_kv(h: int, layer: int, row: int, pos0: int, n: int, k_ptr: int, v_
 
 def ds3_read_kv(h: int, layer: int, row: int, pos0: int, n: int, k_ptr: int, v_ptr: int) -> None:
     _check(load_library().ds3_read_kv(h, layer, row, pos0, n, k_ptr, v_ptr), h)
+
+
+def ds3_write_kv_noalloc(h: int, layer: int, row: int, pos0: int, n: int, k_ptr: int, v_ptr: int) -> None:
+    _check(load_library().ds3_write_kv_noalloc(h, layer, row, pos0, n, k_ptr, v_ptr), h)
 
 
 def ds3_stats_get(h: int) -> ds3_stats:

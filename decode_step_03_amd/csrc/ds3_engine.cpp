@@ -18,6 +18,8 @@
 
 using namespace ds3;
 
+static_assert(kScratchBytes == DS3_NOALLOC_MAX_BYTES, "the scratch array is the size the header states");
+
 namespace {
 
 enum EngineState { ST_READY = 0, ST_NOT_LOADED = 1, ST_NEEDS_RESET = 2, ST_POISONED = 3 };
@@ -146,6 +148,7 @@ struct ds3_engine {
   std::string err;
   void* kv_staging = nullptr;
   size_t kv_staging_bytes = 0;
+  void* scratch = nullptr;   // this device's allocation-free staging array (ds3_write_kv_noalloc)
   std::vector<Launch> sequence;
 
   // what enqueue_kernel launches for: the decode step (cfg.rows rows) or the prefill step (prefill_rows tokens
@@ -806,6 +809,9 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
     if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("hipStreamCreate: ") + hipGetErrorString(h));
     e->own_stream = true;
   }
+  // the allocation-free staging array of this device, looked up once per device while it is current
+  h = scratch_device_ptr(e->device, &e->scratch);
+  if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("scratch array: ") + hipGetErrorString(h));
   plan_splits(c, &e->splits, &e->split_len);
   const WorkPlan wp = plan_work(c, e->splits);
   char* work = reinterpret_cast<char*>(e->buf[DS3_BUF_WORK]);
@@ -1476,9 +1482,9 @@ static ds3_status kv_transfer(ds3_engine* e, int32_t layer, int32_t row, int32_t
     if (vt) transpose(reinterpret_cast<const char*>(v), vtmp.data(), true);
     HIP_OR_POISON(e, hipMemcpyAsync(stg, k, half, hipMemcpyHostToDevice, e->stream));
     HIP_OR_POISON(e, hipMemcpyAsync(stg + half, vt ? vtmp.data() : v, half, hipMemcpyHostToDevice, e->stream));
-    HIP_OR_POISON(e, launch_kv_copy(e->kv, c.kv_dtype, layer, row, pos0, n, nkv, hd, stg, 1, e->status, e->stream));
+    HIP_OR_POISON(e, launch_kv_copy(e->kv, c.kv_dtype, layer, row, pos0, n, nkv, hd, stg, 1, vt, e->status, e->stream));
   } else {
-    HIP_OR_POISON(e, launch_kv_copy(e->kv, c.kv_dtype, layer, row, pos0, n, nkv, hd, stg, 0, e->status, e->stream));
+    HIP_OR_POISON(e, launch_kv_copy(e->kv, c.kv_dtype, layer, row, pos0, n, nkv, hd, stg, 0, vt, e->status, e->stream));
     HIP_OR_POISON(e, hipMemcpyAsync(k, stg, half, hipMemcpyDeviceToHost, e->stream));
     HIP_OR_POISON(e, hipMemcpyAsync(vt ? vtmp.data() : v, stg + half, half, hipMemcpyDeviceToHost, e->stream));
   }
@@ -1496,6 +1502,31 @@ ds3_status ds3_write_kv(ds3_engine* e, int32_t layer, int32_t row, int32_t pos0,
 
 ds3_status ds3_read_kv(ds3_engine* e, int32_t layer, int32_t row, int32_t pos0, int32_t n, void* k, void* v) {
   return kv_transfer(e, layer, row, pos0, n, k, v, false);
+}
+
+// As ds3_write_kv, staged through the device's file-scope scratch array instead of a buffer the library allocates:
+// the host arrays are copied into it as they are and the copy kernel transposes V on the device.
+ds3_status ds3_write_kv_noalloc(ds3_engine* e, int32_t layer, int32_t row, int32_t pos0, int32_t n, const void* k,
+                                const void* v) {
+  if (ds3_status st = refuse_if_unusable(e)) return st;
+  const ds3_config& c = e->cfg;
+  if (!k || !v) return fail(e, DS3_E_INVALID, "k or v is NULL");
+  if (layer < 0 || layer >= c.n_layers || row < 0 || row >= c.rows || pos0 < 0 || n < 0 || (int64_t)pos0 + n > c.cap)
+    return fail(e, DS3_E_INVALID, "layer/row/position range out of bounds");
+  if (c.kv_layout == DS3_KV_PAGED && !e->slot_map_set) return fail(e, DS3_E_INVALID, "paged KV needs a slot map");
+  const size_t half = (size_t)c.n_kv_heads * n * c.head_dim * dtype_bytes(c.kv_dtype);
+  if (2 * half > kScratchBytes)
+    return fail(e, DS3_E_INVALID, "K and V of " + std::to_string(n) + " positions take " + std::to_string(2 * half) +
+                                      " bytes, more than the " + std::to_string(kScratchBytes) + "-byte scratch array");
+  if (n == 0) return DS3_OK;
+  char* stg = reinterpret_cast<char*>(e->scratch);
+  HIP_OR_POISON(e, hipMemcpyAsync(stg, k, half, hipMemcpyDefault, e->stream));
+  HIP_OR_POISON(e, hipMemcpyAsync(stg + half, v, half, hipMemcpyDefault, e->stream));
+  HIP_OR_POISON(e, launch_kv_copy(e->kv, c.kv_dtype, layer, row, pos0, n, c.n_kv_heads, c.head_dim, stg, 1, 0,
+                                  e->status, e->stream));
+  HIP_OR_POISON(e, hipEventRecord(e->ev_done, e->stream));
+  e->pending = true;
+  return wait_done(e, e->ev_done, e->cfg.timeout_ms);
 }
 
 ds3_status ds3_stats_get(const ds3_engine* e, ds3_stats* out) {

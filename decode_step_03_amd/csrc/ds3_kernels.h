@@ -306,8 +306,14 @@ hipError_t launch_embed(const EmbedParams& p, int weight_dtype, hipStream_t s);
 hipError_t launch_gemv(const GemvParams& p, int mode, int weight_dtype, int kv_dtype, int blocks, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, int kv_dtype, int rows, hipStream_t s);
 hipError_t launch_attention_combine(const AttnParams& p, int rows, hipStream_t s);
+// staging: K [nkv][n][hd], then V as [nkv][hd][n] when stage_vt, else [nkv][n][hd] (the state's own V order,
+// transposed or not, is the KvView's)
 hipError_t launch_kv_copy(const KvView& kv, int kv_dtype, int layer, int row, int pos0, int n, int nkv, int hd,
-                          void* staging, int to_state, StatusWords* status, hipStream_t s);
+                          void* staging, int to_state, int stage_vt, StatusWords* status, hipStream_t s);
+// Allocation-free staging: a file-scope device array of kScratchBytes per GPU (its address for `device`, looked
+// up once per device)
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+hipError_t scratch_device_ptr(int device, void** out);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t s);
 // Streaming-read probe (measurement): reads `bytes` (a multiple of 16) once; `sink` holds at least 1024 words.
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);

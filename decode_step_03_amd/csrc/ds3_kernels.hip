@@ -26,6 +26,8 @@
 //
 // No kernel takes a token, a position or a map entry by value: they are read from the slot buffer, so one
 // recorded graph serves every step ("Execution" page, section "Slot buffers").
+#include <mutex>
+
 #include "ds3_device.h"
 
 namespace ds3 {
@@ -1227,14 +1229,15 @@ __global__ void __launch_bounds__(512) stream_read_kernel(const u32x4* __restric
 
 template <typename KT>
 __global__ void __launch_bounds__(kBlock) kv_copy_kernel(KvView kv, int layer, int row, int pos0, int n, int nkv,
-                                                          int hd, KT* staging, int to_state, StatusWords* st) {
+                                                          int hd, KT* staging, int to_state, int stage_vt,
+                                                          StatusWords* st) {
   const size_t per = (size_t)n * hd;
   const size_t total = 2 * (size_t)nkv * per;   // K then V
   for (size_t i = blockIdx.x * (size_t)kBlock + threadIdx.x; i < total; i += (size_t)gridDim.x * kBlock) {
     const int which = (int)(i / (nkv * per));
     const size_t rem = i % (nkv * per);
     const int g = (int)(rem / per);
-    const bool t = which == 1 && kv.v_t;
+    const bool t = which == 1 && stage_vt;   // staged V order: [nkv][hd][n] when set, else [nkv][n][hd]
     const int pos = t ? (int)(rem % n) : (int)((rem / hd) % n);
     const int e = t ? (int)((rem / n) % hd) : (int)(rem % hd);
     KT* base = reinterpret_cast<KT*>(which ? kv.v : kv.k) + (size_t)layer * kv.layer_stride;
@@ -2005,17 +2008,18 @@ hipError_t launch_sk_swiglu(const SkActParams& p, hipStream_t s) {
 }
 
 hipError_t launch_kv_copy(const KvView& kv, int kv_dtype, int layer, int row, int pos0, int n, int nkv, int hd,
-                          void* staging, int to_state, StatusWords* status, hipStream_t s) {
+                          void* staging, int to_state, int stage_vt, StatusWords* status, hipStream_t s) {
   const size_t total = 2 * (size_t)nkv * n * hd;
   int blocks = (int)((total + kBlock - 1) / kBlock);
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   if (kv_dtype == 1)
     kv_copy_kernel<uint16_t><<<blocks, kBlock, 0, s>>>(kv, layer, row, pos0, n, nkv, hd,
-                                                       reinterpret_cast<uint16_t*>(staging), to_state, status);
+                                                       reinterpret_cast<uint16_t*>(staging), to_state, stage_vt,
+                                                       status);
   else
     kv_copy_kernel<float><<<blocks, kBlock, 0, s>>>(kv, layer, row, pos0, n, nkv, hd,
-                                                    reinterpret_cast<float*>(staging), to_state, status);
+                                                    reinterpret_cast<float*>(staging), to_state, stage_vt, status);
   return hipGetLastError();
 }
 
@@ -2046,6 +2050,40 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t s)
   if (blocks < 1) blocks = 1;
   fill_u32_kernel<<<blocks, kBlock, 0, s>>>(p, value, n);
   return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------------------------------------
+// Allocation-free staging (ds3_write_kv_noalloc). One array per GPU the library runs on, held until the process
+// ends. In host code `scratch` is a host-side stand-in, not a device address: every host use goes through the
+// address hipGetSymbolAddress returns for the device, looked up once per device with that device current.
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+hipError_t scratch_device_ptr(int device, void** out) {
+  *out = nullptr;
+  if (device < 0 || device >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    int cur = 0;
+    hipError_t h = hipGetDevice(&cur);
+    if (h != hipSuccess) return h;
+    if (cur != device && (h = hipSetDevice(device)) != hipSuccess) return h;
+    void* ptr = nullptr;
+    h = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    const hipError_t h2 = cur != device ? hipSetDevice(cur) : hipSuccess;
+    if (h != hipSuccess) return h;
+    if (h2 != hipSuccess) return h2;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
 }
 
 }  // namespace ds3

@@ -142,6 +142,12 @@ class Engine:
         v = np.ascontiguousarray(v)
         C.ds3_write_kv(self.handle, layer, row, pos0, k.shape[1], k.ctypes.data, v.ctypes.data)
 
+    def write_kv_noalloc(self, layer: int, row: int, pos0: int, k: np.ndarray, v: np.ndarray) -> None:
+        """As write_kv, staged through the library's fixed device array (no allocation; see include/ds3.h)."""
+        k = np.ascontiguousarray(k)
+        v = np.ascontiguousarray(v)
+        C.ds3_write_kv_noalloc(self.handle, layer, row, pos0, k.shape[1], k.ctypes.data, v.ctypes.data)
+
     def read_kv(self, layer: int, row: int, pos0: int, n: int):
         dt = np.uint16 if self.cfg.kv_dtype == C.DS3_BF16 else np.float32
         shape = (self.cfg.n_kv_heads, n, self.cfg.head_dim)

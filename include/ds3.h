@@ -290,6 +290,19 @@ ds3_status ds3_write_kv(ds3_engine* e, int32_t layer, int32_t row, int32_t pos0,
                         const void* v);
 ds3_status ds3_read_kv(ds3_engine* e, int32_t layer, int32_t row, int32_t pos0, int32_t n, void* k, void* v);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): ds3_write_kv without any allocation. ds3_write_kv stages K and V through a device
+ * buffer the library allocates on first use; this call stages them through a fixed device array of
+ * DS3_NOALLOC_MAX_BYTES that the library holds on every GPU it runs on until the process ends, and transposes V on
+ * the device. Same arguments, layout and result as ds3_write_kv (k, v: [n_kv_heads][n][head_dim] in the KV dtype,
+ * host or device memory). 2 * n_kv_heads * n * head_dim * (2 or 4 bytes) must not exceed DS3_NOALLOC_MAX_BYTES
+ * (else DS3_E_INVALID, nothing written). It calls no hipMalloc, hipFree or other allocating routine. Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (several threads, or engines on different streams
+ * at once) race and must be serialized by the caller; one call has finished with the array when it returns. */
+#define DS3_NOALLOC_MAX_BYTES (8u << 20)
+ds3_status ds3_write_kv_noalloc(ds3_engine* e, int32_t layer, int32_t row, int32_t pos0, int32_t n, const void* k,
+                                const void* v);
+
 ds3_status ds3_stats_get(const ds3_engine* e, ds3_stats* out);
 
 /* Per kernel kind, the device time of one step's launches of that kind: they are captured as a graph of their
