@@ -56,7 +56,9 @@ struct Shape {
   static constexpr int KB = TC * HD * 2;             // bytes of one staged K chunk (and of its V^T chunk)
   static constexpr int WST = kFW * G * (HD + 2);     // attention wave states
   static constexpr int UNI = WST > kFW * 520 ? WST : kFW * 520;
+  static constexpr int QU = (G + 2) * HD / 2;        // QKV units (rotary / v row pairs) of one kv-head group
   static_assert(kFusedBlocks % NKV == 0 && S <= 64, "splits per kv head");
+  static_assert(QU % S == 0, "a group's QKV units split evenly over its blocks");
   static_assert(TC % 32 == 0 && TC / 32 <= kFW && TC >= 128, "a chunk is 32 positions per wave");
   static_assert(KB % (1024 * kFW) == 0, "a chunk's 1 KB staging instructions split evenly over the waves");
   static_assert(G >= 1 && G <= 16 && (HD == 64 || HD == 128), "group and head width");
@@ -193,6 +195,14 @@ __device__ __forceinline__ float norm_scale(const float* ssq, int K, float eps) 
 template <class SH>
 struct QkvUnit {
   int seg, head, idx, row0, row1;
+  // unit lu (0 .. QU - 1) of kv-head group g: the rotary pairs of its G q heads, then of its k head, then the row
+  // pairs of its v head. The S blocks of group g produce exactly the q, k and v its attention reads.
+  __device__ __forceinline__ static int of_group(int g, int lu) {
+    constexpr int half = SH::HD / 2, nqg = SH::G * half;
+    if (lu < nqg) return g * nqg + lu;
+    if (lu < nqg + half) return SH::NQ * half + g * half + (lu - nqg);
+    return (SH::NQ + SH::NKV) * half + g * half + (lu - nqg - half);
+  }
   __device__ __forceinline__ explicit QkvUnit(int u) {
     constexpr int half = SH::HD / 2, nqp = SH::NQ * half, nkp = SH::NKV * half;
     if (u < nqp) {
@@ -219,7 +229,8 @@ template <class SH, int PH>
 struct GemvPhase {
   using GE = Geo<SH, PH>;
   const uint16_t* w;
-  int u0, nunits, rb;   // block: first unit, units, rows (2 per pair unit)
+  int u0, nunits, rb;   // block: first unit (QKV: within its group), units, rows (2 per pair unit)
+  int grp;              // QKV: the block's kv-head group
   int r0, r1, ks;       // wave: rows [r0, r1) of the block, input slice
   int nb;               // batches (even)
   int lane;
@@ -231,8 +242,15 @@ struct GemvPhase {
     rtab = rtab_;
     lane = lane_;
     const int units = PH == PH_HEAD ? units_total : GE::UNITS;
-    u0 = (int)(((long long)b * units) / kFusedBlocks);
-    nunits = (int)(((long long)(b + 1) * units) / kFusedBlocks) - u0;
+    if constexpr (PH == PH_QKV) {   // block (g, s) of group g = b / S: units [s QU / S, (s + 1) QU / S) of g
+      grp = b / SH::S;
+      nunits = SH::QU / SH::S;
+      u0 = (b % SH::S) * nunits;
+    } else {
+      grp = 0;
+      u0 = (int)(((long long)b * units) / kFusedBlocks);
+      nunits = (int)(((long long)(b + 1) * units) / kFusedBlocks) - u0;
+    }
     rb = nunits * (GE::PAIRS ? 2 : 1);
     const int rg = wid / GE::KS;
     ks = wid % GE::KS;
@@ -244,7 +262,7 @@ struct GemvPhase {
   // weight row of block row br
   __device__ __forceinline__ int row_of(int br) const {
     if constexpr (PH == PH_QKV) {
-      const QkvUnit<SH> q(u0 + (br >> 1));
+      const QkvUnit<SH> q(QkvUnit<SH>::of_group(grp, u0 + (br >> 1)));
       return (br & 1) ? q.row1 : q.row0;
     } else if constexpr (PH == PH_GU) {
       const int j = u0 + (br >> 1);
@@ -429,6 +447,30 @@ __device__ __forceinline__ void arrive_and_wait(const FusedParams& p, unsigned g
   if (!early) prefetch();
 }
 
+// End of the QKV phase, wave 0 only (after its epilogue stores): wait for them and raise this block's arrival flag
+// to the phase's generation gen0 + bar + 1. No grid barrier follows: each kv-head group's attention needs only the
+// q, k and v its own S blocks produce, so it waits for those S flags alone (group_wait).
+__device__ __forceinline__ void group_arrive(const FusedParams& p, unsigned gen0, int bar, int lane, const int* flags) {
+  wait_all();
+  if (!flags[0] && lane == 0) st_dev(&p.sync[kSyncArrive + blockIdx.x], gen0 + (unsigned)bar + 1u);
+  if (lane == 0 && p.trace) p.trace[((size_t)bar * kFusedBlocks + blockIdx.x) * 2] = (unsigned long long)wall_clock64();
+}
+
+// Wave 0: wait until the S blocks of kv-head group g have raised their arrival flags to generation gen0 + bar + 1
+// or later (a block of the group may already have moved on to the next barrier's generation).
+template <int S>
+__device__ __forceinline__ void group_wait(const FusedParams& p, unsigned gen0, int bar, int g, int lane, int* flags) {
+  const unsigned gen = gen0 + (unsigned)bar + 1u;
+  if (!flags[0]) {
+    const unsigned* f = p.sync + kSyncArrive + g * S;
+    spin_until(p, flags, [&]() __attribute__((always_inline)) {
+      return __all(lane >= S || (int)(ld_dev(f + min(lane, S - 1)) - gen) >= 0) != 0;
+    });
+  }
+  if (lane == 0 && p.trace)
+    p.trace[((size_t)bar * kFusedBlocks + blockIdx.x) * 2 + 1] = (unsigned long long)wall_clock64();
+}
+
 // Greedy candidate of the wave: the (value, index) maximum over its lanes, in every lane.
 __device__ __forceinline__ void pick_reduce(float& bv, int& bi) {
 #pragma unroll
@@ -548,7 +590,7 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
   float eo_a = 0.f, eo_b = 0.f;
   if constexpr (PH == PH_QKV) {
     if (wid == 0 && lane < ph.nunits) {
-      const QkvUnit<SH> q(ph.u0 + lane);
+      const QkvUnit<SH> q(QkvUnit<SH>::of_group(ph.grp, ph.u0 + lane));
       if (q.seg != 2) {
         const float2 cs = reinterpret_cast<const float2*>(opaque_p(p.rope))[(size_t)pos * half + q.idx];
         eo_a = cs.x;
@@ -622,7 +664,7 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
     };
     if constexpr (PH == PH_QKV) {
       if (lane < ph.nunits) {
-        const QkvUnit<SH> q(ph.u0 + lane);
+        const QkvUnit<SH> q(QkvUnit<SH>::of_group(ph.grp, ph.u0 + lane));
         const float a = total(2 * lane) * scale, b = total(2 * lane + 1) * scale;
         float va = a, vb = b;
         if (q.seg != 2) {   // rotate the pair (element idx, element idx + hd/2) by the angles of pos
@@ -678,9 +720,11 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
       }
       if (p.slots[SlotLayout{1}.sample()] == 0) final_pick(p, gen0, lane, sm.flags);   // (else the sampler picks)
     }
-    if constexpr (PH != PH_HEAD) {
-      arrive_and_wait(p, gen0, kFusedPhases * layer + (PH == PH_QKV ? 0 : PH == PH_O ? 2 : PH == PH_GU ? 3 : 4), lane,
-                      sm.flags, [&]() __attribute__((always_inline)) {
+    if constexpr (PH == PH_QKV) {
+      group_arrive(p, gen0, kFusedPhases * layer, lane, sm.flags);
+    } else if constexpr (PH != PH_HEAD) {
+      arrive_and_wait(p, gen0, kFusedPhases * layer + (PH == PH_O ? 2 : PH == PH_GU ? 3 : 4), lane, sm.flags,
+                      [&]() __attribute__((always_inline)) {
                         nx.issue(0, A);
                         nx.issue(1, B);
                       });
@@ -689,7 +733,8 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
   if constexpr (PH != PH_HEAD) {
     // (waves 1-7 hold the next phase's first batches in flight: no vmcnt(0) here)
     barrier_lds();
-    after_barrier(p, kFusedPhases * layer + (PH == PH_QKV ? 0 : PH == PH_O ? 2 : PH == PH_GU ? 3 : 4));
+    if constexpr (PH != PH_QKV)   // (the QKV phase closes with its group's wait, at the start of the attention)
+      after_barrier(p, kFusedPhases * layer + (PH == PH_O ? 2 : PH == PH_GU ? 3 : 4));
   }
 }
 
@@ -716,6 +761,7 @@ __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, con
   // kv head reads the same device-scope lines, so one read per block, not one per wave)
   float* qs = sm.uni;                  // [G][HD] q, then [2][HD] this step's k and v
   if (wid == 0) {
+    group_wait<S>(p, gen0, kFusedPhases * layer, g, lane, sm.flags);   // the group's q, k and v are stored
     const auto rq = make_rsrc(opaque_p(p.q) + g * G * HD);
     const auto rk = make_rsrc(opaque_p(p.kvnew) + g * 2 * HD);
     for (int i = lane; i < G * HD / 4; i += 64)
@@ -725,6 +771,7 @@ __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, con
   }
   wait_all();   // (every wave: also its share of the chunk staged during the previous phases)
   __syncthreads();
+  after_barrier(p, kFusedPhases * layer);
   if (st) st[1] = (unsigned long long)wall_clock64();
 
   // ---- q^T as the B operand (lane (n, Lg): head g G + n, elements 32 k + 8 Lg + 0..7, times 1/sqrt(hd) log2(e);

@@ -145,8 +145,9 @@ def test_fused_profile_reports_phases_and_restores_state():
 
 def test_fused_phase_trace_records_barriers_and_leaves_results_alone():
     """A traced engine (the separately compiled, traced step kernel) gives the untraced engine's logits bit for
-    bit; its grid-barrier trace has, for every block and barrier, arrival <= release, releases in barrier order,
-    and every block released only after the last block arrived; its GEMV sub-phase clocks are in order. An
+    bit; its barrier trace has, for every block and barrier, arrival <= release, releases in barrier order, every
+    block released only after the last block arrived (after the QKV phase: the last block of its kv-head group);
+    its GEMV sub-phase clocks are in order. An
     untraced engine refuses the trace."""
     w, ws = _case(n_layers=2)
     plain = make_engine(w, ws, kernel_plan="fused")
@@ -167,7 +168,11 @@ def test_fused_phase_trace_records_barriers_and_leaves_results_alone():
         arr, rel = bar[..., 0].astype(np.int64), bar[..., 1].astype(np.int64)
         assert (arr > 0).all() and (arr <= rel).all()
         assert (np.diff(rel, axis=0) >= 0).all(), "releases out of barrier order"
-        assert (rel.min(axis=1) >= arr.max(axis=1)).all(), "a block was released before every block arrived"
+        grid = [i for i in range(nb) if i % 5 != 0]   # the QKV phase closes with a wait of each kv-head group
+        assert (rel[grid].min(axis=1) >= arr[grid].max(axis=1)).all(), "a block was released before every block arrived"
+        qa = arr[0::5].reshape(w.model.n_layers, 8, 32)
+        qr = rel[0::5].reshape(w.model.n_layers, 8, 32)
+        assert (qr.min(axis=2) >= qa.max(axis=2)).all(), "a group's attention began before its QKV blocks arrived"
         for ph in (0, 2, 3, 4):   # GEMV phases: start, first batch consumed, batches done, block done
             st = sub[ph::5, :, :4].astype(np.int64)
             assert (st > 0).all() and (np.diff(st, axis=2) >= 0).all()
