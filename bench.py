@@ -6,8 +6,11 @@ vocab 128256, RoPE theta 5e5), batch 1, contiguous KV of capacity 8192 pre-fille
 position 2048; greedy decode from position 2048 (warm-up steps first, then the timed steps, 512 in total by
 default). Weights are seeded N(0, 0.02) draws rounded to bf16; nothing is trained or downloaded.
 
-One step = write the slot buffers, one HIP-graph replay of every kernel of the step, copy the logits back, pick
-the greedy token on the host. `value` is decode tokens/s over the timed steps (rows x steps / wall time).
+One step = one HIP-graph replay of every kernel of the step (the slot buffers hold token and position). By default
+the greedy token is picked on the device and fed to the next step, and the host waits once per --chain steps
+(reading back the ids); `value` is decode tokens/s over the timed steps (rows x steps / wall time). Beside it,
+`step.per_token_readback` times the same engine with one host wait per step, the logits copied back and the greedy
+token picked on the host (--chain 0 makes that the headline).
 
 Printed as one JSON line, with:
   roofline      the dominant kernel's achieved HBM bandwidth against MI355X's 8 TB/s: algorithmic bytes per
@@ -17,7 +20,12 @@ Printed as one JSON line, with:
                 changed since);
   step          whole-step device time (HIP events around the replay) and bytes, kernels per step, host submit
                 time for the graph replay and for one-launch-per-kernel;
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload on this host.
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload on this host (all cores; one core
+                too for the tiny and 1B-shaped workloads), with its seconds per step and the algorithmic bytes per
+                second of oracle time;
+  parity        the timed engine against that oracle run, from the same initial state: teacher-forced (the oracle's
+                tokens) max-abs logits error and greedy agreement where the oracle's top-2 margin exceeds 5e-2, and
+                the free-running agreement length of the device's own greedy chain.
 """
 from __future__ import annotations
 
@@ -69,7 +77,8 @@ def engine_for(w, ws, exec_mode, kernel_plan="auto", trace="off", prefill_rows=N
 
 def prefill(eng, w, start_pos):
     """Initial state: the page table (paged layout) and N(0,1) K/V for positions [0, start) of every row; or, for
-    a workload that starts from a prompt, the prompt tokens fed as one-token steps (positions 0..len-1)."""
+    a workload that starts from a prompt, the prompt (ds3_prefill in chunks, or one-token steps), and then the
+    first decode token of each row (the greedy pick of the prompt's last logits) is returned. None otherwise."""
     from concurrent.futures import ThreadPoolExecutor
 
     import synth
@@ -77,18 +86,20 @@ def prefill(eng, w, start_pos):
         eng.set_slot_map(synth.page_table(w))
     if w.start == "prefill_tokens":
         toks = synth.prefill_tokens(w)
+        first = np.zeros(w.rows, np.int32)
         if eng.cfg.prefill_rows > 0:   # the prompt in chunks of prefill_rows tokens per launch sequence
             t0 = time.perf_counter()
             for r in range(w.rows):
-                eng.prefill(r, toks[r], 0)
+                lg, _ = eng.prefill(r, toks[r], 0)
+                first[r] = int(np.argmax(lg))
             dt = time.perf_counter() - t0
             prefill.last = {"tokens": int(w.rows * w.prefill_len), "chunk": int(eng.cfg.prefill_rows),
                             "ms": round(1e3 * dt, 3), "tok_s": round(w.rows * w.prefill_len / dt, 1),
                             "gpu_ms": round(eng.stats()["last_prefill_gpu_us"] / 1e3, 3)}
-            return
+            return first
         for p in range(w.prefill_len):
-            eng.step(toks[:, p], np.full(w.rows, p, np.int32), copy_logits=False)
-        return
+            lg, _ = eng.step(toks[:, p], np.full(w.rows, p, np.int32))
+        return lg.argmax(axis=1).astype(np.int32)   # the first decode token: the prompt's last logits' pick
     jobs = [(li, r, int(start_pos[r])) for r in range(w.rows) for li in range(w.model.n_layers) if start_pos[r] > 0]
 
     def gen(job):
@@ -106,27 +117,109 @@ def prefill(eng, w, start_pos):
 prefill.last = None
 
 
-def cpu_baseline(w, ws, start_pos, start_tok, budget_s: float) -> dict:
-    """The oracle as it is, on this host's cores, over a bounded sample of the workload (whole decode steps)."""
+def oracle_start(w, model, start_pos, start_tok, n_extra: int = 64):
+    """The oracle's state of row 0 where the workload's decode steps begin, and its first token: N(0,1) K/V up to
+    the start position (the same seeded draws the engine gets), or the prompt through a causal forward (its K/V, and
+    the first token picked from its last logits); the tiny workload starts empty at position 0."""
     import oracle
     import synth
-    model = oracle.OracleModel.from_weightset(ws)
-    cache = oracle.RowCache(model, int(start_pos[0]) + 64, w.kv_dtype)
-    for li in range(w.model.n_layers):
+    cache = oracle.RowCache(model, int(start_pos[0]) + n_extra, w.kv_dtype)
+    tok = int(start_tok[0])
+    if w.start == "prefill_tokens":
+        lg = oracle.causal_forward(model, synth.prefill_tokens(w)[0], w.kv_dtype, cache=cache)
+        tok = int(np.argmax(lg[-1]))
+    else:
         n = int(start_pos[0])
-        cache.set(li, 0, synth.kv_prefill(w, li, 0, "k", n), synth.kv_prefill(w, li, 0, "v", n))
-    tok, p = int(start_tok[0]), int(start_pos[0])
-    steps, t0 = 0, time.time()
-    while True:
-        logits = oracle.decode_step(model, cache, tok, p)
-        tok, p, steps = int(np.argmax(logits)), p + 1, steps + 1
-        if time.time() - t0 >= budget_s or steps >= 32:
+        for li in range(w.model.n_layers if n > 0 else 0):
+            cache.set(li, 0, synth.kv_prefill(w, li, 0, "k", n), synth.kv_prefill(w, li, 0, "v", n))
+    return cache, tok
+
+
+def cpu_baseline(w, ws, start_pos, start_tok, budget_s: float, single_core_s: float = 0.0) -> tuple:
+    """The oracle as it is, on this host's cores, over a bounded sample of the workload: whole greedy decode steps
+    of row 0 from its start. Returns (the baseline record, the steps' tokens and logits for the parity check).
+    With single_core_s > 0 the oracle is timed again on one core (one thread, one BLAS thread)."""
+    import oracle
+    model = oracle.OracleModel.from_weightset(ws)
+
+    def run(budget, max_steps):
+        cache, tok = oracle_start(w, model, start_pos, start_tok)
+        p = int(start_pos[0])
+        toks, logits = [], []
+        t0 = time.time()
+        while True:
+            lg = oracle.decode_step(model, cache, tok, p)
+            toks.append(tok)
+            logits.append(lg.astype(np.float32))
+            tok, p = int(np.argmax(lg)), p + 1
+            if time.time() - t0 >= budget or len(toks) >= max_steps:
+                break
+        return time.time() - t0, toks, logits
+
+    dt, toks, logits = run(budget_s, 32)
+    steps = len(toks)
+    nbytes = algorithmic_bytes(w) / w.rows   # one row's share of the step's bytes (the oracle runs one row)
+    out = {"value": steps / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+           "sample": f"{steps} greedy decode step(s) of row 0 from position {int(start_pos[0])}, all "
+                     f"{w.model.n_layers} layers and the head, float64, weights widened per 256-row block",
+           "seconds": round(dt, 2), "s_per_step": round(dt / steps, 4),
+           "gbs_of_algorithmic_bytes": round(nbytes * steps / dt / 1e9, 3), "host": host_info()}
+    if single_core_s > 0:
+        from threadpoolctl import threadpool_limits
+        n_threads = oracle.threads()
+        oracle.set_threads(1)
+        try:
+            with threadpool_limits(1):
+                dt1, t1, _ = run(single_core_s, 8)
+        finally:
+            oracle.set_threads(n_threads)
+        out["single_core"] = {"value": len(t1) / dt1, "unit": "tokens/s", "cores": 1, "steps": len(t1),
+                              "seconds": round(dt1, 2), "s_per_step": round(dt1 / len(t1), 4),
+                              "gbs_of_algorithmic_bytes": round(nbytes * len(t1) / dt1 / 1e9, 4)}
+    return out, {"tokens": toks, "logits": logits}
+
+
+def parity_leg(eng, w, start_pos, start_tok, ref) -> dict:
+    """The engine against the oracle's run of row 0, from the same initial state (reset, then the workload's
+    prefill): teacher-forced by the oracle's tokens, the max-abs logits error and the greedy ids wherever the
+    oracle's top-2 margin exceeds 5e-2; then the device's own greedy chain from the same start, and for how many
+    steps its picks agree with the oracle's."""
+    tol = 1e-4 if w.model.weight_dtype == "f32" else 2e-2
+    toks, refl = ref["tokens"], ref["logits"]
+    n = len(toks)
+
+    def restart():
+        eng.reset_state()
+        first = prefill(eng, w, start_pos)
+        t = (first if first is not None else start_tok).copy()
+        t[0] = toks[0]
+        return t
+
+    tok, pos = restart(), start_pos.copy()
+    err, checked, agree, inside = 0.0, 0, 0, 0
+    for i in range(n):
+        lg, flags = eng.step(tok, pos)
+        err = max(err, float(np.max(np.abs(lg[0].astype(np.float64) - refl[i]))))
+        top2 = np.partition(refl[i], -2)[-2:]
+        if top2[1] - top2[0] > 5e-2:
+            checked += 1
+            agree += int(int(np.argmax(lg[0])) == int(np.argmax(refl[i])))
+        else:
+            inside += 1
+        tok = lg.argmax(axis=1).astype(np.int32)
+        if i + 1 < n:
+            tok[0] = toks[i + 1]
+        pos = pos + 1
+    tok, pos = restart(), start_pos.copy()
+    ids, _ = eng.step_greedy(tok, pos, n)
+    run = 0
+    for i in range(n - 1):
+        if int(ids[i, 0]) != int(toks[i + 1]):
             break
-    dt = time.time() - t0
-    return {"value": steps / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"{steps} greedy decode step(s) of row 0 from position {int(start_pos[0])}, all "
-                      f"{w.model.n_layers} layers and the head, float64, weights widened per 256-row block",
-            "seconds": round(dt, 2), "host": host_info()}
+        run += 1
+    return {"rows_checked": 1, "steps": n, "logits_max_abs_err": float(f"{err:.3e}"), "tolerance": tol,
+            "within_tolerance": bool(err <= tol), "greedy_checked": checked, "greedy_equal": agree,
+            "greedy_inside_margin": inside, "free_running_agreement": run, "free_running_of": n - 1}
 
 
 CSRC = os.path.join(ROOT, "decode_step_03_amd", "csrc")
@@ -290,7 +383,9 @@ def main() -> int:
 
     t0 = time.time()
     eng = engine_for(w, ws, "graph", args.kernel_plan)
-    prefill(eng, w, start_pos)
+    first = prefill(eng, w, start_pos)
+    if first is not None:   # a prompt workload: decoding starts from the prompt's greedy pick
+        start_tok = first
     log(f"engine loaded and K/V pre-filled in {time.time() - t0:.1f}s")
 
     pos = start_pos.copy()
@@ -408,6 +503,38 @@ def main() -> int:
         sampled = {"tok_s": round(w.rows * n_smp / es, 2), "gpu_ms": round(float(np.median(gs)) / 1e3, 4),
                    "steps": n_smp, "params": params}
         log(f"sampling suffix: {sampled['tok_s']} tok/s, GPU {sampled['gpu_ms']} ms/step")
+    # the step as the pages count it per token: one host wait per step, the logits copied back, the greedy token
+    # picked on the host (same engine, from where the steps above ended)
+    readback = None
+    n_rb = min(32, w.cap - int(pos.max()))
+    if n_rb >= 4:
+        wr, gr = [], []
+        torch.cuda.synchronize()
+        tr = time.perf_counter()
+        for _ in range(n_rb):
+            ts = time.perf_counter()
+            lg, _ = eng.step(tok, pos)
+            tok = lg.argmax(axis=1).astype(np.int32)
+            pos = pos + 1
+            wr.append(time.perf_counter() - ts)
+            gr.append(eng.stats()["last_gpu_us"])
+        er = time.perf_counter() - tr
+        readback = {"tok_s": round(w.rows * n_rb / er, 2), "steps": n_rb,
+                    "wall_ms_p10_p50_p90": [round(1e3 * float(np.percentile(wr, q)), 4) for q in (10, 50, 90)],
+                    "gpu_ms": round(float(np.median(gr)) / 1e3, 4),
+                    "token_pick": "host argmax of the copied logits, one host wait per step"}
+        log(f"per-token readback: {readback['tok_s']} tok/s")
+
+    # the oracle on this host's cores (a bounded sample of the same workload), and the engine against it
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        single = 10.0 if w.name in ("tiny-fp32", "llama1b-bf16") else 0.0
+        cpu, ref = cpu_baseline(w, ws, start_pos, start_tok, args.cpu_baseline_seconds, single)
+        log(f"cpu oracle {cpu['value']:.4f} tok/s on {cpu['cores']} threads")
+        parity = parity_leg(eng, w, start_pos, start_tok, ref)
+        log(f"parity: max-abs logits error {parity['logits_max_abs_err']}, greedy {parity['greedy_equal']}/"
+            f"{parity['greedy_checked']}, free-running agreement {parity['free_running_agreement']}/"
+            f"{parity['free_running_of']}")
     eng.close()
     del eng
     torch.cuda.empty_cache()
@@ -417,7 +544,7 @@ def main() -> int:
     if args.eager_steps > 0:
         for mode in ("graph", "eager"):
             e2 = engine_for(w, ws, mode, "per_op")
-            prefill(e2, w, start_pos)
+            prefill(e2, w, start_pos)   # (start_tok already holds a prompt workload's first token)
             sub, wl, gu = [], [], []
             p2, t2 = start_pos.copy(), start_tok.copy()
             for i in range(args.eager_steps + 2):
@@ -438,10 +565,6 @@ def main() -> int:
             del e2
             torch.cuda.empty_cache()
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, ws, start_pos, start_tok, args.cpu_baseline_seconds)
-        log(f"cpu oracle {cpu['value']:.4f} tok/s on {cpu['cores']} threads")
 
     metric = METRIC if w.name == "llama8b-bf16-cap8192" else f"decode tokens/s + % HBM roofline, {w.name}"
     out = {
@@ -463,10 +586,12 @@ def main() -> int:
                    "start_pos": int(start_pos[0])},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
         "step": {"bytes": step_bytes, "gpu_ms": round(gpu_ms, 4),
                  "hbm_gbs": round(step_bytes / gpu_ms / 1e6, 1),
                  "hbm_frac": round(step_bytes / gpu_ms / 1e6 / HBM_PEAK_GBS, 4),
                  "wall_ms_p10_p50_p90": [round(1e3 * float(np.percentile(wall, q)), 4) for q in (10, 50, 90)],
+                 "wall_samples": len(wall), "per_token_readback": readback,
                  "kernel_plan": stats["kernel_plan"],
                  "kernels_per_step": stats["kernels_per_step"], "graph_replays_per_step": 1,
                  "steps_per_host_wait": args.chain if args.chain > 0 else 1,
