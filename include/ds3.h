@@ -162,7 +162,10 @@ typedef struct {
 } ds3_kernel_time;
 
 /* Sizes of the device buffers for `cfg`. `out` has room for *n_inout entries; on return *n_inout is
- * DS3_NUM_BUFFERS. Validates the configuration (DS3_E_UNSUPPORTED names the failing field). */
+ * DS3_NUM_BUFFERS. Validates the configuration (DS3_E_UNSUPPORTED names the failing field). Every size follows from
+ * the configuration alone ("Models, Registry and the Driver" page, section "The Driver": capacity sizes the buffers
+ * and is part of the step's shape, while tokens, positions and sampler parameters are bound inputs), so the caller can
+ * allocate them once and the addresses never change ("Execution" page, section "Slot buffers"). */
 ds3_status ds3_query_buffers(const ds3_config* cfg, ds3_buffer_req* out, int32_t* n_inout);
 
 /* Create an engine over caller-allocated device buffers (`dev_ptrs[i]` for buffer id i, n = DS3_NUM_BUFFERS),
@@ -176,7 +179,10 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
 ds3_status ds3_load_weights(ds3_engine* e, const ds3_weight_src* w, int32_t n);
 
 /* Paged layout only: the per-row page table, int32 [rows][cap/page_size] of physical page ids in
- * [0, pool_pages). Rows must not share pages. Copied to its slot buffer; it stays until the next call. */
+ * [0, pool_pages). Rows must not share pages. Copied to its slot buffer; it stays until the next call. This is the
+ * per-step SlotMap input of the "Execution" page, section "Slot buffers" (a device buffer at a stable address whose
+ * contents the host rewrites), through which the sweep reads and from which the K/V write target is derived
+ * (section "A constant-shape decode graph": the ScatterUpdate through the WriteMap for paged K/V). */
 ds3_status ds3_set_slot_map(ds3_engine* e, const int32_t* slot_map);
 
 /* One decode step for every row r: take token tokens[r] at absolute position pos[r] (0 <= pos < cap), write its
@@ -255,9 +261,9 @@ ds3_status ds3_step_sample(ds3_engine* e, const int32_t* tokens, const int32_t* 
                            uint32_t* flags, float* logprobs, int32_t* logprob_ids);
 
 /* Prefill (the step before decode): n tokens of one row at positions pos0 .. pos0 + n - 1, with their K/V written
- * into that row's state ("Models, Registry and the Driver" page, section "The Model": a prefill is a step that
- * continues from a position, in chunks). The tokens go prefill_rows at a time through one launch sequence (one
- * graph replay): chunk k is a step of prefill_rows activation rows that all read and write the same K/V row, token
+ * into that row's state ("Models, Registry and the Driver" page, section "The Model": positions are absolute, and
+ * a prefill is the same step taken from a given position, in chunks). The tokens go prefill_rows at a time through
+ * one launch sequence (one graph replay): chunk k is a step of prefill_rows activation rows that all read and write the same K/V row, token
  * t of the chunk at position pos0 + k prefill_rows + t, so its attention sees the K/V of the chunk's earlier tokens
  * (written by the same step before the attention runs) and nothing after its own position -- the causal mask
  * inside the chunk is the position mask of the decode step. Chunks run their projections on the matrix cores
@@ -285,7 +291,10 @@ ds3_status ds3_reset_state(ds3_engine* e);
 
 /* Write / read K and V of `n` logical positions pos0..pos0+n-1 of one row and layer. `k` and `v` are host arrays
  * [n_kv_heads][n][head_dim] in the KV dtype (float32 or bf16 words). Paged layout maps positions through the
- * row's page table. */
+ * row's page table. The K/V cache is the state the step program carries ("Models, Registry and the Driver" page,
+ * section "The Model": the states of a program, the KV cache among them); writing it sets a sequence's state at a
+ * position (e.g. a pre-filled context), and reading it lets a check compare every element of the carried state
+ * with the oracle ("Execution" page, section "Verification", the stated-tolerance tier). */
 ds3_status ds3_write_kv(ds3_engine* e, int32_t layer, int32_t row, int32_t pos0, int32_t n, const void* k,
                         const void* v);
 ds3_status ds3_read_kv(ds3_engine* e, int32_t layer, int32_t row, int32_t pos0, int32_t n, void* k, void* v);

@@ -16,8 +16,8 @@ What it computes, and where that comes from (pages of the poot documentation):
   x += mixer(norm(x)); x += ffn(norm(x)) per layer, then applies the final norm and the head. The components it
   names (norms, rotary embeddings, linear projections, attention, gated feed-forward) are given no formulas on the
   pages; the readings taken for them are the standard Llama-style ones, listed per function below.
-* "Models, Registry and the Driver", section "The Model": positions are absolute, so a prefill is a step that
-  continues from a position; `causal_forward` evaluates a whole prefix at once to pin that equivalence.
+* "Models, Registry and the Driver", section "The Model": positions are absolute, and a prefill of n tokens is n
+  steps at consecutive positions; `causal_forward` evaluates a whole prefix at once to pin that equivalence.
 
 Precision: everything is evaluated in float64. Stored inputs are widened exactly (bf16 words or float32). The one
 rounding that belongs to the method's state is kept: the K/V cache holds values in the workload's KV dtype

@@ -3,12 +3,11 @@
 TEST INFRASTRUCTURE ONLY, like the rest of this package: only the tests and the smoke check may use it; it shares
 nothing with the HIP path.
 
-The pages ("Models, Registry and the Driver" page, section "The Driver", item "The sampling suffix"; "Backends"
-page, section "ROCm (AMD)") say that every sampling rule runs on the device as a suffix of the decode graph: greedy and
-temperature draws with top-k, top-p and min-p; repetition, presence and frequency penalties and a logit bias read
-from a per-sequence history of token counts and bias that the device keeps and updates with every token it draws;
-and the top-n logprobs of the adjusted distribution. They give no formulas, so each rule below is the plainest
-reading of its name, and the kernel follows the same readings:
+Source: "Models, Registry and the Driver" page, section "The Driver", item "The sampling suffix", and the
+"Backends" page, section "ROCm (AMD)". The rules named there -- greedy and temperature draws with top-k, top-p and
+min-p cuts, the repetition, presence and frequency penalties with a logit bias taken from each sequence's token
+history (kept on the device and grown by each drawn token), and the top-n logprobs -- come without formulas, so
+each rule below is the plainest reading of its name, and the kernel follows the same readings:
 
 * adjusted logits, per token v with history count c_v and bias b_v:
   z_v = r(l_v) - presence * [c_v > 0] - frequency * c_v + b_v, where r(x) = x / rep if x > 0 else x * rep when

@@ -1,6 +1,6 @@
 """Multi-token prefill (ds3_prefill): a prompt of one row goes prefill_rows tokens per launch sequence, every token
 of a chunk an activation row of the same K/V row. Against the oracle fed the same tokens one decode step at a
-time (the pages' reading of a prefill: a step that continues from a position): the last token's logits within
+time (a prefill is steps at consecutive absolute positions): the last token's logits within
 the stated tolerance and its greedy id outside the margin, the K/V of every prompt position, and decoding after
 the prefill staying in parity. Chunks of 16 tokens run the projections on the matrix cores, chunks of up to 4 on
 the GEMV kernels; the last chunk may be partial.

@@ -1,7 +1,8 @@
 """Pins of the oracle's whole step.
 
-* A prefill is a step that continues from a position, so step-by-step decode must equal a causal forward over the
-  whole prefix, evaluated by an independent entry point with a full [T, T] mask and no cache.
+* Positions are absolute and a prefill is just steps at consecutive positions, so step-by-step decode must equal a
+  causal forward over the whole prefix, evaluated by an independent entry point with a full [T, T] mask and no
+  cache.
 * A one-layer toy decoder evaluated with plain Python loops (no numpy) must give the same logits: this pins the
   order of the pre-norm residual pair, which weight feeds which product, and the head.
 * The cache holds exactly the rounded k and v of each position.
