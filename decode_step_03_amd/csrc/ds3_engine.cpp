@@ -33,7 +33,7 @@ size_t dtype_bytes(int dt) { return dt == DS3_BF16 ? 2 : 4; }
 
 struct WorkPlan {
   size_t slots, status, x, q, attn, act, part, pre_slots, pre_logits, kvnew, sync, clocks, trace, pick_val, pick_idx,
-      pick_done, ids, chain_flags, samp_rows, counts, bias, draws, zbuf, lp, lp_ids, rope, slot_map, frag_hi, frag_lo,
+      pick_done, ids, chain_flags, samp_rows, counts, bias, draws, zbuf, samp_part, lp, lp_ids, rope, slot_map, frag_hi, frag_lo,
       skpart, skss, total;
 };
 
@@ -96,6 +96,7 @@ struct ds3_engine {
   float* bias = nullptr;                             // [rows][vocab] logit bias
   uint32_t* draws = nullptr;                         // [rows] draws so far (the generator's counter)
   float* zbuf = nullptr;                             // [rows][vocab] adjusted logits (scratch)
+  SampPart* samp_part = nullptr;                     // [rows][segments] the sampler's segment records (scratch)
   float* lp = nullptr;                               // [kMaxChain][rows][1 + kMaxLogprobs] logprobs
   int32_t* lp_ids = nullptr;                         // [kMaxChain][rows][kMaxLogprobs]
   std::vector<SampleRow> h_samp;                     // host copy of the per-row parameters
@@ -340,6 +341,7 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
   w.bias = take((size_t)c.rows * c.vocab * 4);
   w.draws = take((size_t)c.rows * 4);
   w.zbuf = take((size_t)c.rows * c.vocab * 4);
+  w.samp_part = take((size_t)c.rows * samp_segments(c.vocab) * sizeof(SampPart));
   w.lp = take((size_t)kMaxChain * c.rows * (1 + kMaxLogprobs) * 4);
   w.lp_ids = take((size_t)kMaxChain * c.rows * kMaxLogprobs * 4);
   w.rope = take((size_t)c.cap * (c.head_dim / 2) * 2 * 4);
@@ -610,6 +612,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.bias = e->bias;
       p.draws = e->draws;
       p.z = e->zbuf;
+      p.part = e->samp_part;
       p.ids = e->ids;
       p.flags = e->chain_flags;
       p.lp = e->lp;
@@ -838,6 +841,7 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   e->bias = reinterpret_cast<float*>(work + wp.bias);
   e->draws = reinterpret_cast<uint32_t*>(work + wp.draws);
   e->zbuf = reinterpret_cast<float*>(work + wp.zbuf);
+  e->samp_part = reinterpret_cast<SampPart*>(work + wp.samp_part);
   e->lp = reinterpret_cast<float*>(work + wp.lp);
   e->lp_ids = reinterpret_cast<int32_t*>(work + wp.lp_ids);
   e->sync_words = fused_sync_words(c.n_layers, c.n_kv_heads);

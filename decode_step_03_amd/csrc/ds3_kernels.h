@@ -129,6 +129,28 @@ struct SampleRow {
   int32_t top_k, n_logprobs;
   uint32_t seed_lo, seed_hi;
 };
+// The sampler's first kernel splits each row's vocabulary into segments of kSampSeg tokens, one block each, and
+// leaves one record per (row, segment): the segment's best (value, index) of the adjusted logits, its log-sum-exp
+// partial (max and sum of exp(s - max), s = z / T), its top kMaxLogprobs tokens by rank, and -- when the row's top-k
+// is small enough for the candidate path -- its own top-k tokens in index order. The global top-k lies in the union
+// of the segments' top-k sets, so the per-row kernel selects from at most kSampCand candidates instead of the
+// vocabulary.
+constexpr int kSampSeg = 2048;    // tokens per segment block
+constexpr int kSampFastK = 128;   // largest top-k the candidate path takes
+constexpr int kSampCand = 8192;   // most candidates of one row (segments x top-k)
+struct SampPart {
+  float best_v;
+  int best_i;
+  float m, l;                     // log-sum-exp partial: max of s and sum of exp(s - m) over the segment
+  float top_v[kMaxLogprobs];      // top by rank (s descending, index ascending): s and token
+  int top_i[kMaxLogprobs];
+  int n_cand;
+  int pad[3];
+  int cand_v[kSampFastK];         // the segment's top-k tokens in index order, and their adjusted logits
+  float cand_x[kSampFastK];
+};
+__host__ __device__ inline int samp_segments(int vocab) { return (vocab + kSampSeg - 1) / kSampSeg; }
+
 struct SampleParams {
   const float* logits;      // [rows][vocab]
   int vocab, rows;
@@ -140,6 +162,7 @@ struct SampleParams {
   const float* bias;        // [rows][vocab] logit bias
   uint32_t* draws;          // [rows] temperature draws so far (the generator's counter)
   float* z;                 // [rows][vocab] scratch: adjusted logits
+  SampPart* part;           // [rows][samp_segments(vocab)] scratch: the segment records
   int32_t* ids;             // [max_chain][rows]
   uint32_t* flags;          // [max_chain]
   float* lp;                // [max_chain][rows][1 + kMaxLogprobs]: the drawn token's logprob, then the top-n

@@ -22,7 +22,7 @@
 //   attn_mfma_kernel / attn_kernel  split sweep of all [cap] positions (bf16 K/V on the matrix cores, fp32 on
 //                     the vector ALU), mask from Slot::Pos against the position index, per-split softmax partials
 //   attn_combine_kernel  the splits merged in fixed order (and, 5-16 rows, the o-projection's fragments)
-//   pick_kernel / sample_kernel  the next token into the slots (greedy, or the sampling suffix)
+//   pick_kernel / sample_part_kernel + sample_kernel  the next token into the slots (greedy, or the sampling suffix)
 //
 // No kernel takes a token, a position or a map entry by value: they are read from the slot buffer, so one
 // recorded graph serves every step ("Execution" page, section "Slot buffers").
@@ -1324,7 +1324,10 @@ __global__ void __launch_bounds__(kPickThreads) pick_kernel(PickParams p) {
 }
 
 // ----------------------------------------------------------------------------------------------------------
-// sampling suffix: one block of kSampleThreads per row, several passes over the row's adjusted logits (L2-resident)
+// sampling suffix: the segment kernel (sample_part_kernel, one block per 2048-token segment of a row) forms the
+// adjusted logits and the segment records; then one block of kSampleThreads per row selects: from the candidates
+// (the segments' top-k sets) when top-k is small, else by several passes over the row's adjusted logits
+// (L2-resident)
 
 constexpr int kSampleThreads = 1024;
 constexpr int kSampleWaves = kSampleThreads / 64;
@@ -1346,8 +1349,14 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t d) {
 
 constexpr int kSampleList = 1024;   // top-k sets up to this size are gathered into LDS for the rest of the selection
 
+constexpr int kSampLpSeg = 128;   // segment records staged in LDS for the logprob merge (vocabularies <= 262144)
+
 struct SampleShared {
   unsigned long long hist[256];
+  float seg_m[kSampLpSeg], seg_l[kSampLpSeg];            // the segments' log-sum-exp partials
+  float seg_tv[kSampLpSeg * kMaxLogprobs];               // and their top-n lists
+  int seg_ti[kSampLpSeg * kMaxLogprobs];
+  int seg_n[kSampLpSeg], seg_off[kSampLpSeg];            // the candidate path: candidates per segment, offsets
   int gv[kSampleList];   // the top-k set as gathered (any order): tokens, adjusted logits
   float gx[kSampleList];
   int lv[kSampleList];   // the same in index order
@@ -1444,14 +1453,29 @@ __device__ __forceinline__ void radix_select(SampleShared& sh, const float* z, i
       if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], wt(x));
     });
     __syncthreads();
-    if (threadIdx.x == 0) {
-      int b = 255;
-      for (; b > 0; --b) {
-        if (ab + sh.hist[b] >= target) break;
-        ab += sh.hist[b];
-      }
-      sh.bcast[0] = (unsigned long long)b;
+    // the bin where the weight counted from the top reaches the target: threads 0..255 hold bins 255..0 and form
+    // an inclusive scan in that order (integer sums: exact); the one thread whose range crosses the target writes
+    // its bin, and bin 0 takes the rest when bins 255..1 stay below it (as a walk down from bin 255 would)
+    unsigned long long c = 0, incl = 0;
+    if (threadIdx.x == 0) {   // (overwritten below by the thread whose range crosses the target)
+      sh.bcast[0] = 0ull;
       sh.bcast[1] = ab;
+    }
+    if (threadIdx.x < 256) {
+      c = sh.hist[255 - threadIdx.x];
+      incl = wave_scan_u64(c);
+      if ((threadIdx.x & 63) == 63) sh.wsum[threadIdx.x >> 6] = incl;
+    }
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      unsigned long long off = ab;
+      for (int w = 0; w < (int)(threadIdx.x >> 6); ++w) off += sh.wsum[w];
+      incl += off;
+      const unsigned long long before = incl - c;
+      if (before < target && (incl >= target || threadIdx.x == 255)) {
+        sh.bcast[0] = (unsigned long long)(255 - threadIdx.x);
+        sh.bcast[1] = before;
+      }
     }
     __syncthreads();
     prefix |= (uint32_t)sh.bcast[0] << shift;
@@ -1547,78 +1571,304 @@ __device__ __forceinline__ int index_scan(SampleShared& sh, const float* z, int 
   return r;
 }
 
-__global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) {
-  __shared__ SampleShared sh;
-  const int r = blockIdx.x, V = p.vocab, tid = threadIdx.x;
-  const SampleRow prm = p.rowp[r];
-  const float* lg = p.logits + (size_t)r * V;
-  int32_t* cnt = p.counts + (size_t)r * V;
-  const float* bias = p.bias + (size_t)r * V;
-  float* z = p.z + (size_t)r * V;
+// Adjusted logit of one token: the repetition penalty on a seen token (toward zero), presence and frequency
+// penalties, then the bias; a NaN logit (or result) counts as -inf.
+__device__ __forceinline__ float adjust_logit(float x, int c, float bias_v, const SampleRow& prm) {
+  if (x != x) x = -INFINITY;
+  if (c > 0) x = (x > 0.f ? x / prm.rep : x * prm.rep) - prm.presence - prm.frequency * (float)c;
+  x += bias_v;
+  if (x != x) x = -INFINITY;
+  return x;
+}
 
-  // ---- adjusted logits: repetition penalty on seen tokens (toward zero), presence and frequency, bias; NaN -> -inf
+// Whether a row's draw takes the candidate path: a temperature draw whose top-k (below the vocabulary) is at most
+// kSampFastK, with at most kSampCand candidates over at most kSampLpSeg segments.
+__host__ __device__ __forceinline__ bool samp_fast(const SampleRow& prm, int V) {
+  return prm.temperature > 0.f && prm.top_k >= 1 && prm.top_k <= kSampFastK && prm.top_k < V &&
+         samp_segments(V) * prm.top_k <= kSampCand && samp_segments(V) <= kSampLpSeg;
+}
+
+constexpr int kPartThreads = 256;
+constexpr int kPartWaves = kPartThreads / 64;
+
+// exclusive prefix sum over the block's threads in thread order (every value is an integer count)
+__device__ __forceinline__ int part_scan(int* wtot, int x, int& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) wtot[wv] = incl;
+  __syncthreads();
+  int off = 0;
+  total = 0;
+  for (int w = 0; w < kPartWaves; ++w) {
+    if (w < wv) off += wtot[w];
+    total += wtot[w];
+  }
+  __syncthreads();
+  return off + incl - x;
+}
+
+// (value, index) best of the block in rank order, in every thread
+__device__ __forceinline__ void part_best(float* fv, int* fi, float& bv, int& bi) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float ov = __shfl_xor(bv, m, 64);
+    const int oi = __shfl_xor(bi, m, 64);
+    if (pick_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  if ((threadIdx.x & 63) == 0) { fv[threadIdx.x >> 6] = bv; fi[threadIdx.x >> 6] = bi; }
+  __syncthreads();
+  bv = fv[0];
+  bi = fi[0];
+  for (int w = 1; w < kPartWaves; ++w)
+    if (pick_better(fv[w], fi[w], bv, bi)) { bv = fv[w]; bi = fi[w]; }
+  __syncthreads();
+}
+
+// Lane exchanges for the (value, index) best of a wave without LDS traffic: quad permutations and the half-row and
+// row mirrors (DPP) within each 16 lanes, then the permlane swaps between rows (16) and halves (32). Every step
+// pairs each lane with one partner and both keep the better of the two, so every lane ends with the wave's best.
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov_i(int x) { return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false); }
+template <int CTRL>
+__device__ __forceinline__ void best_step_dpp(float& v, int& i) {
+  const float ov = __int_as_float(dpp_mov_i<CTRL>(__float_as_int(v)));
+  const int oi = dpp_mov_i<CTRL>(i);
+  if (pick_better(ov, oi, v, i)) { v = ov; i = oi; }
+}
+__device__ __forceinline__ void best_step_swap(float& v, int& i, bool rows32) {
+  const auto a = rows32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)
+                        : __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const auto b = rows32 ? __builtin_amdgcn_permlane32_swap((unsigned)i, (unsigned)i, false, false)
+                        : __builtin_amdgcn_permlane16_swap((unsigned)i, (unsigned)i, false, false);
+  // (the pair holds this lane's and its partner's value, in either order)
+  const float v0 = __uint_as_float(a[0]), v1 = __uint_as_float(a[1]);
+  const int i0 = (int)b[0], i1 = (int)b[1];
+  float bv = v0;
+  int bi = i0;
+  if (pick_better(v1, i1, bv, bi)) { bv = v1; bi = i1; }
+  v = bv;
+  i = bi;
+}
+__device__ __forceinline__ void wave_best_dpp(float& v, int& i) {
+  best_step_dpp<0xB1>(v, i);    // quad_perm [1,0,3,2]
+  best_step_dpp<0x4E>(v, i);    // quad_perm [2,3,0,1]
+  best_step_dpp<0x141>(v, i);   // row_half_mirror
+  best_step_dpp<0x140>(v, i);   // row_mirror
+  best_step_swap(v, i, false);  // rows 0 <-> 1, 2 <-> 3
+  best_step_swap(v, i, true);   // halves
+}
+
+// The top n (n <= kMaxLogprobs) by rank (value descending, index ascending) among the entries a wave's lanes hold
+// (E each; an unused entry has value -inf and index INT_MAX): n rounds, each the wave's best entry ranked below the
+// previous round's, by shuffles alone. Every lane gets the results.
+template <int E>
+__device__ __forceinline__ void wave_topn(const float (&x)[E], const int (&v)[E], int n, float (&ov)[kMaxLogprobs],
+                                          int (&oi)[kMaxLogprobs]) {
+  float pv = INFINITY;
+  int pi = -1;
+  for (int j = 0; j < kMaxLogprobs; ++j) {
+    float cv = -INFINITY;
+    int ci = 0x7fffffff;
+    if (j < n) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool below = x[e] < pv || (x[e] == pv && v[e] > pi);
+        if (below && pick_better(x[e], v[e], cv, ci)) { cv = x[e]; ci = v[e]; }
+      }
+      wave_best_dpp(cv, ci);
+    }
+    ov[j] = cv;
+    oi[j] = ci;
+    pv = cv;
+    pi = ci;
+  }
+}
+
+// The sampler's first kernel: block (segment b, row r) takes tokens [b kSampSeg, b kSampSeg + n) of row r. It forms
+// their adjusted logits (into z, and into LDS for the passes below) and the segment record (SampPart): the best
+// (value, index); with logprobs asked for, the log-sum-exp partial of s = z / T (T = 1 for greedy) and the top n
+// tokens by rank; on the candidate path, the segment's own top-k by (s descending, index ascending) -- a radix
+// selection of the k-th largest key, then the tokens above it and the lowest-index ones at it, in index order.
+__global__ void __launch_bounds__(kPartThreads) sample_part_kernel(SampleParams p) {
+  __shared__ float zs[kSampSeg];
+  __shared__ unsigned hist[256];
+  __shared__ float fv[kPartWaves];
+  __shared__ int fi[kPartWaves];
+  __shared__ int wtot[kPartWaves];
+  __shared__ int bc[2];
+  __shared__ float wtop_v[kPartWaves * kMaxLogprobs];
+  __shared__ int wtop_i[kPartWaves * kMaxLogprobs];
+  const int r = blockIdx.y, b = blockIdx.x, V = p.vocab, tid = threadIdx.x;
+  const int v0 = b * kSampSeg, n = min(kSampSeg, V - v0);
+  const SampleRow prm = p.rowp[r];
+  const float* lg = p.logits + (size_t)r * V + v0;
+  const int32_t* cnt = p.counts + (size_t)r * V + v0;
+  const float* bias = p.bias + (size_t)r * V + v0;
+  float* z = p.z + (size_t)r * V + v0;
+  SampPart& out = p.part[(size_t)r * gridDim.x + b];
+
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  auto adjust = [&](float x, int c, float bias_v) __attribute__((always_inline)) {
-    if (x != x) x = -INFINITY;
-    if (c > 0) x = (x > 0.f ? x / prm.rep : x * prm.rep) - prm.presence - prm.frequency * (float)c;
-    x += bias_v;
-    if (x != x) x = -INFINITY;
-    return x;
-  };
-  if ((V & 3) == 0) {
-    // 16-byte loads, four tokens each, four of them per thread in flight (rows start 16-byte aligned)
-    const int V4 = V >> 2;
-    const float4* lg4 = reinterpret_cast<const float4*>(lg);
-    const int4* cnt4 = reinterpret_cast<const int4*>(cnt);
-    const float4* bias4 = reinterpret_cast<const float4*>(bias);
-    float4* z4 = reinterpret_cast<float4*>(z);
-    for (int base = tid; base < V4; base += 4 * kSampleThreads) {
-      float4 xl[4], xb[4];
-      int4 xc[4];
+  constexpr int PT = kSampSeg / kPartThreads;   // tokens per thread, all loads issued first
+  {
+    float xl[PT], xb[PT];
+    int xc[PT];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = min(base + u * kSampleThreads, V4 - 1);
-        xl[u] = lg4[i];
-        xc[u] = cnt4[i];
-        xb[u] = bias4[i];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = base + u * kSampleThreads;
-        if (i >= V4) break;
-        const float4 o = make_float4(adjust(xl[u].x, xc[u].x, xb[u].x), adjust(xl[u].y, xc[u].y, xb[u].y),
-                                     adjust(xl[u].z, xc[u].z, xb[u].z), adjust(xl[u].w, xc[u].w, xb[u].w));
-        z4[i] = o;
-        const float ov[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (pick_better(ov[e], 4 * i + e, bv, bi)) { bv = ov[e]; bi = 4 * i + e; }
-      }
+    for (int u = 0; u < PT; ++u) {
+      const int i = min(tid + u * kPartThreads, n - 1);
+      xl[u] = lg[i];
+      xc[u] = cnt[i];
+      xb[u] = bias[i];
     }
-  } else {
-    // four tokens per thread in flight, three loads each
-    for (int base = tid; base < V; base += 4 * kSampleThreads) {
-      float xl[4], xb[4];
-      int xc[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int v = min(base + u * kSampleThreads, V - 1);
-        xl[u] = lg[v];
-        xc[u] = cnt[v];
-        xb[u] = bias[v];
+    for (int u = 0; u < PT; ++u) {
+      const int i = tid + u * kPartThreads;
+      if (i >= n) break;
+      const float x = adjust_logit(xl[u], xc[u], xb[u], prm);
+      zs[i] = x;
+      z[i] = x;
+      if (pick_better(x, v0 + i, bv, bi)) { bv = x; bi = v0 + i; }
+    }
+  }
+  part_best(fv, fi, bv, bi);   // (its barriers also publish zs)
+  if (tid == 0) {
+    out.best_v = bv;
+    out.best_i = bi;
+  }
+  const float T = prm.temperature;
+  const float inv_t = T > 0.f ? 1.f / T : 1.f;
+  const int nl = min(max(prm.n_logprobs, 0), kMaxLogprobs);
+  if (nl > 0) {
+    // log-sum-exp partial over the segment: m = its largest s, l = sum of exp(s - m) (in a fixed order)
+    const float m = bv * inv_t;
+    float t = 0.f;
+    if (m > -INFINITY)
+      for (int i = tid; i < n; i += kPartThreads) t += __expf(zs[i] * inv_t - m);
+    t = wave_total(t);
+    if ((tid & 63) == 0) fv[tid >> 6] = t;
+    __syncthreads();
+    float l = 0.f;
+    for (int w = 0; w < kPartWaves; ++w) l += fv[w];
+    __syncthreads();
+    if (tid == 0) {
+      out.m = m;
+      out.l = l;
+    }
+    // the top nl by rank: each wave's own (its lanes' PT tokens each), then wave 0 over the waves' lists
+    {
+      float x[PT];
+      int v[PT];
+#pragma unroll
+      for (int u = 0; u < PT; ++u) {
+        const int i = tid + u * kPartThreads;
+        x[u] = i < n ? zs[i] * inv_t : -INFINITY;
+        v[u] = i < n ? v0 + i : 0x7fffffff;
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int v = base + u * kSampleThreads;
-        if (v >= V) break;
-        const float x = adjust(xl[u], xc[u], xb[u]);
-        z[v] = x;
-        if (pick_better(x, v, bv, bi)) { bv = x; bi = v; }
+      float tv[kMaxLogprobs];
+      int ti[kMaxLogprobs];
+      wave_topn<PT>(x, v, nl, tv, ti);
+      if ((tid & 63) == 0)
+        for (int j = 0; j < kMaxLogprobs; ++j) {
+          wtop_v[(tid >> 6) * kMaxLogprobs + j] = tv[j];
+          wtop_i[(tid >> 6) * kMaxLogprobs + j] = ti[j];
+        }
+      __syncthreads();
+      if (tid < 64) {
+        float x1[1] = {tid < kPartWaves * kMaxLogprobs ? wtop_v[tid] : -INFINITY};
+        int v1[1] = {tid < kPartWaves * kMaxLogprobs ? wtop_i[tid] : 0x7fffffff};
+        wave_topn<1>(x1, v1, nl, tv, ti);
+        if (tid == 0)
+          for (int j = 0; j < nl; ++j) {
+            out.top_v[j] = tv[j];
+            out.top_i[j] = ti[j];
+          }
       }
     }
   }
-  block_best(sh, bv, bi);   // (its barriers also order the z stores before the sweeps below)
+  if (!samp_fast(prm, V)) return;
+
+  // ---- the segment's top-k by (s descending, index ascending)
+  const int kl = min(prm.top_k, n);
+  uint32_t prefix = 0u, pmask = 0u;
+  int above = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0u;   // (256 threads, 256 bins)
+    __syncthreads();
+    for (int i = tid; i < n; i += kPartThreads) {
+      const uint32_t k = order_key(zs[i] * inv_t);
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    // bins in descending order: thread t holds bin 255 - t; the bin where the count from the top reaches kl
+    const int c = (int)hist[255 - tid];
+    int tot = 0;
+    const int before = above + part_scan(wtot, c, tot);
+    if (before < kl && before + c >= kl) {
+      bc[0] = 255 - tid;
+      bc[1] = before;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)bc[0] << shift;
+    pmask |= 255u << shift;
+    above = bc[1];
+    __syncthreads();
+  }
+  const uint32_t K = prefix;
+  const int need_eq = kl - above;   // tokens at key K to take, lowest index first
+  // emit in index order: thread t takes the run [t E, t E + E)
+  constexpr int E = kSampSeg / kPartThreads;
+  const int c0 = min(n, tid * E), c1 = min(n, c0 + E);
+  int n_eq = 0;
+  for (int i = c0; i < c1; ++i) n_eq += order_key(zs[i] * inv_t) == K;
+  int tot = 0;
+  int eq_before = part_scan(wtot, n_eq, tot);
+  bool keep[E];
+  int n_keep = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = c0 + e;
+    bool k = false;
+    if (i < c1) {
+      const uint32_t key = order_key(zs[i] * inv_t);
+      if (key > K) k = true;
+      else if (key == K) k = eq_before++ < need_eq;
+    }
+    keep[e] = k;
+    n_keep += k;
+  }
+  int pos = part_scan(wtot, n_keep, tot);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (keep[e]) {
+      out.cand_v[pos] = v0 + c0 + e;
+      out.cand_x[pos] = zs[c0 + e];
+      ++pos;
+    }
+  if (tid == 0) out.n_cand = tot;
+}
+
+__global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) {
+  __shared__ SampleShared sh;
+  __shared__ int s_cv[kSampCand];     // the candidate path: every segment's top-k, concatenated (index order)
+  __shared__ float s_cx[kSampCand];
+  const int r = blockIdx.x, V = p.vocab, tid = threadIdx.x;
+  const SampleRow prm = p.rowp[r];
+  int32_t* cnt = p.counts + (size_t)r * V;
+  const float* z = p.z + (size_t)r * V;   // adjusted logits (the segment kernel)
+  const int NB = samp_segments(V);
+  const SampPart* pr = p.part + (size_t)r * NB;
+
+  // ---- the largest adjusted logit: the best of the segments' bests
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int b = tid; b < NB; b += kSampleThreads)
+    if (pick_better(pr[b].best_v, pr[b].best_i, bv, bi)) { bv = pr[b].best_v; bi = pr[b].best_i; }
+  block_best(sh, bv, bi);
   const float zmax = bv;
   int token = bi < V ? bi : 0;
   const float T = prm.temperature;
@@ -1634,14 +1884,45 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
     };
     auto one = [&](float) __attribute__((always_inline)) -> unsigned long long { return 1ull; };
     auto all = [&](int, float) __attribute__((always_inline)) { return true; };
+    // The top-k set is chosen from the candidates (every segment's top-k, in index order) on the candidate path,
+    // else from the whole vocabulary: (zk, Vk) and the token a position of it stands for.
+    const bool fast = samp_fast(prm, V);
+    int n_c = V;
+    if (fast) {
+      // the segments' candidate counts (loaded in parallel), their offsets in segment order, then every entry
+      // copied in parallel to its place: the concatenation is in index order
+      for (int b = tid; b < NB; b += kSampleThreads) sh.seg_n[b] = pr[b].n_cand;
+      __syncthreads();
+      if (tid == 0) {
+        int off = 0;
+        for (int b = 0; b < NB; ++b) {
+          sh.seg_off[b] = off;
+          off += sh.seg_n[b];
+        }
+        sh.nlist = off;
+      }
+      __syncthreads();
+      n_c = sh.nlist;
+      for (int i = tid; i < NB * kSampFastK; i += kSampleThreads) {
+        const int b = i / kSampFastK, j = i % kSampFastK;
+        if (j < sh.seg_n[b]) {
+          s_cv[sh.seg_off[b] + j] = pr[b].cand_v[j];
+          s_cx[sh.seg_off[b] + j] = pr[b].cand_x[j];
+        }
+      }
+      __syncthreads();
+    }
+    const float* zk = fast ? s_cx : z;
+    const int Vk = n_c;
+    auto tok_of = [&](int v) __attribute__((always_inline)) { return fast ? s_cv[v] : v; };
     // top-k: the k best ranked (ties at the threshold key by lower index)
     uint32_t kk = 0u;
-    int ki = V;
-    if (prm.top_k > 0 && prm.top_k < V) {
+    int ki = Vk;
+    if (prm.top_k > 0 && prm.top_k < Vk) {
       unsigned long long above = 0;
-      radix_select(sh, z, V, all, key, one, (unsigned long long)prm.top_k, kk, above);
+      radix_select(sh, zk, Vk, all, key, one, (unsigned long long)prm.top_k, kk, above);
       const uint32_t K = kk;
-      ki = index_scan(sh, z, V, [&](int, float x) __attribute__((always_inline)) { return key(x) == K; }, one,
+      ki = index_scan(sh, zk, Vk, [&](int, float x) __attribute__((always_inline)) { return key(x) == K; }, one,
                       (unsigned long long)prm.top_k - above);
     }
     const uint32_t K1 = kk;
@@ -1658,11 +1939,11 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
     if (listed) {
       if (tid == 0) sh.nlist = 0;
       __syncthreads();
-      sweep<kSweepU>(z, tid, V, kSampleThreads, [&](int v, float x) __attribute__((always_inline)) {
+      sweep<kSweepU>(zk, tid, Vk, kSampleThreads, [&](int v, float x) __attribute__((always_inline)) {
         if (in_k(v, x)) {
           const int i = atomicAdd(&sh.nlist, 1);
           if (i < kSampleList) {
-            sh.gv[i] = v;
+            sh.gv[i] = tok_of(v);
             sh.gx[i] = x;
           }
         }
@@ -1731,7 +2012,8 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
     if (tid == 0) p.draws[r] = d + 1u;
   }
 
-  // ---- logprobs of the adjusted distribution (temperature 1 for greedy): the drawn token's and the top n by rank
+  // ---- logprobs of the adjusted distribution (temperature 1 for greedy): the drawn token's and the top n by rank,
+  // from the segments' log-sum-exp partials (merged in segment order) and their top-n lists
   const SlotLayout sl{p.rows};
   const int step = p.slots[sl.chain()];
   const int slot = step % p.max_chain;
@@ -1739,36 +2021,78 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
   int32_t* lpi = p.lp_ids + ((size_t)slot * p.rows + r) * kMaxLogprobs;
   const int nl = min(max(prm.n_logprobs, 0), kMaxLogprobs);
   if (nl > 0) {
-    const float smax = zmax * inv_t;
-    float t = 0.f;
-    sweep<kSweepU>(z, tid, V, kSampleThreads, [&](int, float x) __attribute__((always_inline)) {
-      t += __expf(x * inv_t - smax);
-    });
-    for (int m = 32; m >= 1; m >>= 1) t += __shfl_xor(t, m, 64);
-    if ((tid & 63) == 0) sh.fv[tid >> 6] = t;
-    __syncthreads();
-    float tot = 0.f;
-    for (int w = 0; w < kSampleWaves; ++w) tot += sh.fv[w];
-    __syncthreads();
-    const float lse = smax + __logf(tot);
-    // top n by rank: n rounds, each the best token ranked below the previous round's
-    float pv = INFINITY;
-    int pi = -1;
-    for (int j = 0; j < nl; ++j) {
-      float cv = -INFINITY;
-      int ci = 0x7fffffff;
-      sweep<kSweepU>(z, tid, V, kSampleThreads, [&](int v, float zx) __attribute__((always_inline)) {
-        const float x = zx * inv_t;
-        const bool below = x < pv || (x == pv && v > pi);
-        if (below && pick_better(x, v, cv, ci)) { cv = x; ci = v; }
-      });
-      block_best(sh, cv, ci);
-      if (tid == 0) {
-        lpi[j] = ci < V ? ci : -1;
-        lpo[1 + j] = cv - lse;
+    // the segment records, staged in LDS by all threads (read from global memory past kSampLpSeg segments)
+    const bool staged = NB <= kSampLpSeg;
+    if (staged) {
+      for (int b = tid; b < NB; b += kSampleThreads) {
+        sh.seg_m[b] = pr[b].m;
+        sh.seg_l[b] = pr[b].l;
       }
-      pv = cv;
-      pi = ci;
+      for (int i = tid; i < NB * kMaxLogprobs; i += kSampleThreads) {   // (stride kMaxLogprobs per segment)
+        const int b = i / kMaxLogprobs, q = i % kMaxLogprobs;
+        sh.seg_tv[i] = q < nl ? pr[b].top_v[q] : -INFINITY;
+        sh.seg_ti[i] = q < nl ? pr[b].top_i[q] : 0x7fffffff;
+      }
+    }
+    __syncthreads();
+    // log-sum-exp of the segments' partials, by wave 0 (lanes over segments; sums in a fixed order)
+    float lse = 0.f;
+    if (tid < 64) {
+      float M = -INFINITY;
+      for (int b = tid; b < NB; b += 64) M = fmaxf(M, staged ? sh.seg_m[b] : pr[b].m);
+      M = wave_max(M);
+      float L = 0.f;
+      for (int b = tid; b < NB; b += 64) {
+        const float m = staged ? sh.seg_m[b] : pr[b].m;
+        if (m > -INFINITY) L += (staged ? sh.seg_l[b] : pr[b].l) * __expf(m - M);
+      }
+      lse = M + __logf(wave_total(L));
+    }
+    // the top n by rank over the segments' top-n lists, by wave 0: chunks of 64 EL entries, each merged with the
+    // running top n (lane j < n offers running entry j)
+    if (tid < 64) {
+      constexpr int EL = kSampLpSeg * kMaxLogprobs / 64;
+      float tv[kMaxLogprobs];
+      int ti[kMaxLogprobs];
+      for (int j = 0; j < kMaxLogprobs; ++j) {
+        tv[j] = -INFINITY;
+        ti[j] = 0x7fffffff;
+      }
+      for (int base = 0; base < NB * kMaxLogprobs; base += 64 * EL) {
+        float x[EL + 1];
+        int v[EL + 1];
+        if (staged) {
+#pragma unroll
+          for (int e = 0; e < EL; ++e) {
+            const int i = base + tid + 64 * e;
+            x[e] = i < NB * kMaxLogprobs ? sh.seg_tv[i] : -INFINITY;
+            v[e] = i < NB * kMaxLogprobs ? sh.seg_ti[i] : 0x7fffffff;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < EL; ++e) {
+            const int i = base + tid + 64 * e;
+            const int b = i / kMaxLogprobs, q = i % kMaxLogprobs;
+            const bool ok = i < NB * kMaxLogprobs && q < nl;
+            x[e] = ok ? pr[b].top_v[q] : -INFINITY;
+            v[e] = ok ? pr[b].top_i[q] : 0x7fffffff;
+          }
+        }
+        x[EL] = -INFINITY;
+        v[EL] = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < kMaxLogprobs; ++j)
+          if (tid == j) {
+            x[EL] = tv[j];
+            v[EL] = ti[j];
+          }
+        wave_topn<EL + 1>(x, v, nl, tv, ti);
+      }
+      if (tid == 0)
+        for (int j = 0; j < nl; ++j) {
+          lpi[j] = ti[j] < V ? ti[j] : -1;
+          lpo[1 + j] = tv[j] - lse;
+        }
     }
     if (tid == 0) lpo[0] = z[token] * inv_t - lse;
   }
@@ -2030,7 +2354,10 @@ hipError_t launch_pick(const PickParams& p, hipStream_t s) {
 }
 
 hipError_t launch_sample(const SampleParams& p, hipStream_t s) {
-  if (p.rows < 1 || p.vocab < 1 || p.max_chain < 1) return hipErrorInvalidValue;
+  if (p.rows < 1 || p.vocab < 1 || p.max_chain < 1 || !p.part) return hipErrorInvalidValue;
+  sample_part_kernel<<<dim3(samp_segments(p.vocab), p.rows), kPartThreads, 0, s>>>(p);
+  hipError_t h0 = hipGetLastError();
+  if (h0 != hipSuccess) return h0;
   sample_kernel<<<p.rows, kSampleThreads, 0, s>>>(p);
   hipError_t h = hipGetLastError();
   if (h != hipSuccess) return h;
