@@ -344,6 +344,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=504)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="llama8b-bf16-cap8192")
+    ap.add_argument("--cap", type=int, default=0,
+                    help="run the workload at this K/V capacity instead of its own (reported beside it, not as the "
+                         "headline)")
     ap.add_argument("--profile-iters", type=int, default=10)
     ap.add_argument("--eager-steps", type=int, default=16,
                     help="steps of the per-operation kernels, as a graph replay and launched one by one")
@@ -374,6 +377,9 @@ def main() -> int:
 
     import synth
     w = synth.workload(args.workload)
+    if args.cap:
+        from dataclasses import replace
+        w = replace(w, cap=args.cap, name=f"{w.name}@cap{args.cap}")
     m = w.model
     t0 = time.time()
     ws = synth.make_weights(m)

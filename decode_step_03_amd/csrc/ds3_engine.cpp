@@ -199,7 +199,7 @@ std::string fused_refusal(const ds3_config& c) {
   if (!fused_shape_supported(c.d_model, c.ffn_dim, c.head_dim, c.n_q_heads, c.n_kv_heads))
     return "no compiled instantiation for this model shape";
   const int S = kFusedBlocks / c.n_kv_heads;
-  if (c.cap != 128 * S && c.cap != 256 * S) return "cap must be 128 or 256 positions per split";
+  if (c.cap % (128 * S) != 0) return "cap must be a multiple of 128 positions per split";
   if (c.vocab < 16 * kFusedBlocks || c.vocab > 520 * kFusedBlocks) return "vocab out of the LM head's range";
   return "";
 }

@@ -48,9 +48,12 @@ constexpr int kRsrcWord3 = 0x00020000; // buffer resource word 3: raw 32-bit dat
 
 enum { PH_QKV = 0, PH_ATTN, PH_O, PH_GU, PH_DOWN, PH_HEAD };
 
-template <int D_, int F_, int HD_, int NQ_, int NKV_, int TC_>
+// MC_: a split sweeps several staged chunks (cap above S TC); a separate instantiation, so the one-chunk kernel
+// carries no chunk loop
+template <int D_, int F_, int HD_, int NQ_, int NKV_, int TC_, bool MC_ = false>
 struct Shape {
   static constexpr int D = D_, F = F_, HD = HD_, NQ = NQ_, NKV = NKV_, G = NQ_ / NKV_, TC = TC_;
+  static constexpr bool MC = MC_;
   static constexpr int QW = NQ * HD;                 // q width, the o-projection's input
   static constexpr int S = kFusedBlocks / NKV;       // attention splits per kv head: one (kv head, split) per block
   static constexpr int KB = TC * HD * 2;             // bytes of one staged K chunk (and of its V^T chunk)
@@ -796,9 +799,19 @@ __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, con
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  {
-    // one chunk per split (split_len == TC): staged during the previous layer's gate/up phase
-    const int jb = s * TC;   // (the chunk is in LDS: every wave waited for its part, then the barrier above)
+  // The split's chunks of TC positions, interleaved over the splits (chunk c of split s starts at (c S + s) TC, so
+  // the visible prefix spreads over every split). Chunk 0 was staged during the previous layer's gate/up phase; each
+  // later one is loaded here once every wave has swept the one before (the stage area holds one chunk).
+  const int nch = SH::MC ? p.split_len / TC : 1;
+  for (int ch = 0; ch < nch; ++ch) {
+    const int jb = (ch * S + s) * TC;
+    if (ch > 0) {
+      __syncthreads();   // (every wave is done with chunk c - 1 in LDS)
+      if (p.slots[SlotLayout{1}.sweep()] == 0 || jb <= pos)
+        stage_chunk<SH>(p, layer, g, jb, sm.stage, wid, lane, 0, SH::KB / 1024 / kFW);
+      wait_all();
+      __syncthreads();
+    }
     // the row at pos: this step's k and v (the staged copy may predate their store)
     if (pos_ok && pos >= jb && pos < jb + TC && tid < HD) {
       const int pj = pos - jb;
@@ -1107,30 +1120,40 @@ bool fused_shape_supported(int d, int ffn, int hd, int nq, int nkv) {
          (d == 2048 && ffn == 8192 && hd == 64 && nq == 32 && nkv == 8);
 }
 
+// Positions per staged chunk for a split of split_len positions: 256 where they divide it, else 128 (0: neither).
+int fused_chunk(int split_len) { return split_len % 256 == 0 ? 256 : (split_len % 128 == 0 ? 128 : 0); }
+
+template <int D, int F, int HD, int NQ, int NKV>
+hipError_t fused_occ_any(int tc, bool mc, int* out) {
+  if (tc == 256) return mc ? fused_occ<Shape<D, F, HD, NQ, NKV, 256, true>>(out) : fused_occ<Shape<D, F, HD, NQ, NKV, 256>>(out);
+  return mc ? fused_occ<Shape<D, F, HD, NQ, NKV, 128, true>>(out) : fused_occ<Shape<D, F, HD, NQ, NKV, 128>>(out);
+}
+template <int D, int F, int HD, int NQ, int NKV>
+hipError_t fused_go_any(const FusedParams& p, int tc, bool mc, bool trace, hipStream_t s) {
+  if (tc == 256) return mc ? fused_go<Shape<D, F, HD, NQ, NKV, 256, true>>(p, trace, s) : fused_go<Shape<D, F, HD, NQ, NKV, 256>>(p, trace, s);
+  return mc ? fused_go<Shape<D, F, HD, NQ, NKV, 128, true>>(p, trace, s) : fused_go<Shape<D, F, HD, NQ, NKV, 128>>(p, trace, s);
+}
+
 hipError_t fused_blocks_per_cu(int d, int ffn, int hd, int nq, int nkv, int split_len, int* out) {
   *out = 0;
-  if (d == 4096 && ffn == 14336 && hd == 128 && nq == 32 && nkv == 8) {
-    return split_len == 256 ? fused_occ<Shape<4096, 14336, 128, 32, 8, 256>>(out)
-                            : fused_occ<Shape<4096, 14336, 128, 32, 8, 128>>(out);
-  }
-  if (d == 2048 && ffn == 8192 && hd == 64 && nq == 32 && nkv == 8) {
-    return split_len == 256 ? fused_occ<Shape<2048, 8192, 64, 32, 8, 256>>(out)
-                            : fused_occ<Shape<2048, 8192, 64, 32, 8, 128>>(out);
-  }
+  const int tc = fused_chunk(split_len);
+  if (tc == 0) return hipErrorInvalidValue;
+  const bool mc = split_len > tc;
+  if (d == 4096 && ffn == 14336 && hd == 128 && nq == 32 && nkv == 8)
+    return fused_occ_any<4096, 14336, 128, 32, 8>(tc, mc, out);
+  if (d == 2048 && ffn == 8192 && hd == 64 && nq == 32 && nkv == 8)
+    return fused_occ_any<2048, 8192, 64, 32, 8>(tc, mc, out);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_fused(const FusedParams& p, int d, int ffn, int hd, int nq, int nkv, bool trace, hipStream_t s) {
-  const int tc = p.split_len;   // one staged chunk per split
-  if ((tc != 256 && tc != 128) || p.cap != tc * (kFusedBlocks / nkv)) return hipErrorInvalidValue;
-  if (d == 4096 && ffn == 14336 && hd == 128 && nq == 32 && nkv == 8) {
-    return tc == 256 ? fused_go<Shape<4096, 14336, 128, 32, 8, 256>>(p, trace, s)
-                     : fused_go<Shape<4096, 14336, 128, 32, 8, 128>>(p, trace, s);
-  }
-  if (d == 2048 && ffn == 8192 && hd == 64 && nq == 32 && nkv == 8) {
-    return tc == 256 ? fused_go<Shape<2048, 8192, 64, 32, 8, 256>>(p, trace, s)
-                     : fused_go<Shape<2048, 8192, 64, 32, 8, 128>>(p, trace, s);
-  }
+  const int tc = fused_chunk(p.split_len);   // split_len / tc staged chunks per split
+  if (tc == 0 || p.cap != p.split_len * (kFusedBlocks / nkv)) return hipErrorInvalidValue;
+  const bool mc = p.split_len > tc;
+  if (d == 4096 && ffn == 14336 && hd == 128 && nq == 32 && nkv == 8)
+    return fused_go_any<4096, 14336, 128, 32, 8>(p, tc, mc, trace, s);
+  if (d == 2048 && ffn == 8192 && hd == 64 && nq == 32 && nkv == 8)
+    return fused_go_any<2048, 8192, 64, 32, 8>(p, tc, mc, trace, s);
   return hipErrorInvalidValue;
 }
 

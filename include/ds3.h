@@ -53,7 +53,7 @@ enum { DS3_GRAPH = 0, DS3_EAGER = 1 };               /* replay one captured grap
 /* Kernel plan. PER_OP: one kernel per operation (embed, then per layer QKV, attention, split combine, o-proj,
  * gate/up, down; then the LM head). FUSED: the whole step as one persistent kernel whose phases are those
  * operations, separated by grid barriers (one block per compute unit; one row, bf16 weights and K/V, contiguous
- * layout, the 1B and 8B model shapes, cap = 32 x 128 or 32 x 256 positions per 8 kv heads, a 256-CU device).
+ * layout, the 1B and 8B model shapes, cap a multiple of 32 x 128 positions per 8 kv heads, a 256-CU device).
  * AUTO picks FUSED where it applies (the faster of the two on MI355X) and PER_OP elsewhere. Both compute the same
  * step; the graph records whichever runs. FUSED needs all of its 256 blocks resident at once: work running
  * concurrently on the device that keeps compute units busy makes its grid barriers wait, and a wait past the

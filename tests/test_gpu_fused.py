@@ -22,10 +22,12 @@ def _case(n_layers=1, cap=8192, vocab=4096, gains="random"):
     return w, ws
 
 
-@pytest.mark.parametrize("cap", [8192, 4096])
+@pytest.mark.parametrize("cap", [8192, 4096, 16384, 12288])
 def test_fused_matches_oracle_and_per_op(cap):
-    """8B-shaped layers (2 of them), one row: the fused kernel (one 256- or 128-position chunk per split) and the
-    per-operation kernels both within 2e-2 of the oracle on every logit, positions spread over the capacity."""
+    """8B-shaped layers (2 of them), one row: the fused kernel (one 256- or 128-position chunk per split at caps 8192
+    and 4096; two 256-position and three 128-position chunks per split at 16384 and 12288, the later ones loaded in
+    the attention phase) and the per-operation kernels both within 2e-2 of the oracle on every logit, positions
+    spread over the capacity and across the chunk boundaries."""
     w, ws = _case(n_layers=2, cap=cap)
     f = make_engine(w, ws, kernel_plan="fused")
     o = make_engine(w, ws, kernel_plan="per_op")
@@ -36,7 +38,7 @@ def test_fused_matches_oracle_and_per_op(cap):
         for ls in (lf, lo):
             ls.prefill_random_kv([pre])
         tok = np.array([123], np.int32)
-        for p in (pre, pre + 1, pre + 2, cap - 1, 0, 255, 256):
+        for p in (pre, pre + 1, pre + 2, cap - 1, 0, 255, 256, cap // 2 - 1, cap // 2, 8192 % cap + 1):
             a, ref, _ = lf.step(tok, np.array([p], np.int32))
             b, _, _ = lo.step(tok, np.array([p], np.int32))
             d = float(np.max(np.abs(a.astype(np.float64) - b)))
@@ -70,14 +72,16 @@ def test_fused_replay_equals_eager_and_serves_every_position():
         e.close()
 
 
-def test_fused_garbage_after_position_does_not_leak():
-    """K/V after pos (huge values, NaN, +-inf) leave the fused kernel's logits bit-identical."""
-    w, ws = _case(n_layers=1)
+@pytest.mark.parametrize("cap,pos", [(8192, 300), (16384, 300), (16384, 9000)])
+def test_fused_garbage_after_position_does_not_leak(cap, pos):
+    """K/V after pos (huge values, NaN, +-inf) leave the fused kernel's logits bit-identical, whether the garbage
+    sits in the chunks staged during the gate/up phase or in those loaded during the attention phase."""
+    w, ws = _case(n_layers=1, cap=cap)
     eng = make_engine(w, ws, kernel_plan="fused")
     try:
         ls = Lockstep(w, ws, eng)
-        ls.prefill_random_kv([300])
-        clean, _ = eng.step([7], [300])
+        ls.prefill_random_kv([pos])
+        clean, _ = eng.step([7], [pos])
         clean = clean.copy()
         rng = np.random.default_rng(1)
         n = 2000
@@ -86,10 +90,10 @@ def test_fused_garbage_after_position_does_not_leak():
         specials = np.array([0x7fc0, 0x7f80, 0xff80], np.uint16)      # NaN, +inf, -inf
         weird = rng.choice(specials, (nkv, n, hd))
         for garbage in (huge, weird):
-            eng.write_kv(0, 0, 301, garbage, garbage)
+            eng.write_kv(0, 0, pos + 1, garbage, garbage)
             eng.write_kv(0, 0, w.cap - n, garbage, garbage)
-            ls.prefill_random_kv([300])
-            got, flags = eng.step([7], [300])
+            ls.prefill_random_kv([pos])
+            got, flags = eng.step([7], [pos])
             assert flags == 0
             assert np.array_equal(got.view(np.uint32), clean.view(np.uint32))
     finally:

@@ -22,6 +22,9 @@ def _workload(name):
     if name == "8b-fused":
         base = synth.workload("llama8b-bf16-cap8192")
         return replace(synth.small_variant(base, n_layers=2, vocab=4096), name="llama8b-2l-sweep")
+    if name == "8b-fused-cap16384":   # two chunks per split, the second loaded in the attention phase
+        base = synth.workload("llama8b-bf16-cap8192")
+        return replace(synth.small_variant(base, n_layers=2, vocab=4096, cap=16384), name="llama8b-2l-sweep-16k")
     if name == "8b-r8":
         base = synth.workload("llama8b-bf16-r8-cap32768")
         return replace(synth.small_variant(base, n_layers=1, vocab=4096, cap=8192), name="llama8b-r8-sweep")
@@ -31,7 +34,7 @@ def _workload(name):
     raise KeyError(name)
 
 
-@pytest.mark.parametrize("name", ["tiny-fp32", "8b-fused", "8b-r8", "8b-r16-paged"])
+@pytest.mark.parametrize("name", ["tiny-fp32", "8b-fused", "8b-fused-cap16384", "8b-r8", "8b-r16-paged"])
 def test_visible_sweep_is_bit_identical(name):
     w = _workload(name)
     ws = synth.make_weights(w.model)
