@@ -100,6 +100,12 @@ struct Geo {
   static_assert(PH != PH_GU || UNITS / kFusedBlocks <= 64, "one epilogue lane per gate/up pair");
 };
 
+// The o-projection's first two batches are issued by waves 1-7 as the attention sweep starts when they are small
+// (at most 32 KB per block: they land within the sweep); larger ones would hold the block barriers that follow the
+// sweep (each waits for every outstanding load of its wave), so they go out after the split's partial is stored.
+template <class SH>
+constexpr bool kEarlyO = 2 * Geo<SH, PH_O>::NL * 1024 * (kFW - 1) <= 32 * 1024;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, kRsrcWord3);
 }
@@ -392,7 +398,8 @@ struct Smem {
   unsigned char* stage;   // [K chunk | V^T chunk]
   float* uni;             // GEMV row partials [KS][rows] / attention wave states [8][G][HD + 2]
   float* ssq;             // [KS] RMSNorm sums of squares
-  int* flags;             // [0] abort seen, [1] generation of the last attention merge done by wave 0
+  int* flags;             // [0] abort seen, [1] generation of the last attention merge done by wave 0,
+                          // [2] generation of the last GEMV epilogue whose stores wave 0 has issued
 };
 
 // Bounded wait of wave 0 for `done()` (evaluated by every lane; the result must agree across the wave): false
@@ -648,10 +655,16 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
   __syncthreads();
   if (st) st[3] = (unsigned long long)wall_clock64();
 
-  // ---- 4. wave 0: slice sums in slice order, epilogue, barrier. Waves 1-7 meanwhile issue the next phase's
-  // first two batches (at a saturated memory system an issue can stall for microseconds, so they must not sit
-  // between wave 0 and its barrier arrival).
+  // ---- 4. wave 0: slice sums in slice order, epilogue, barrier. Waves 1-7 issue the next phase's first two
+  // batches once wave 0 has issued its epilogue stores (at a saturated memory system an issue can stall for
+  // microseconds, so they must not sit between wave 0 and its barrier arrival; and a CU serves its memory requests
+  // roughly in issue order, so stores issued after ~100 KB of loads complete only once those loads have landed).
+  constexpr bool ORDERED = PH == PH_O || PH == PH_GU || PH == PH_DOWN;
+  const int epi_tok = (int)(gen0 + (unsigned)(kFusedPhases * layer + BAR) + 1u);
   if (wid != 0) {
+    if constexpr (ORDERED)   // (wave 0 has issued its epilogue stores: they do not queue behind these batches)
+      while (__hip_atomic_load(&sm.flags[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != epi_tok)
+        __builtin_amdgcn_s_sleep(1);
     nx.issue(0, A);
     nx.issue(1, B);
     if constexpr (PH == PH_O && Geo<SH, PH_GU>::NLB > 0)   // the gate/up LDS batches (loaded during attention) have
@@ -723,6 +736,8 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
       }
       if (p.slots[SlotLayout{1}.sample()] == 0) final_pick(p, gen0, lane, sm.flags);   // (else the sampler picks)
     }
+    if constexpr (ORDERED)
+      if (lane == 0) __hip_atomic_store(&sm.flags[2], epi_tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     if constexpr (PH == PH_QKV) {
       group_arrive(p, gen0, kFusedPhases * layer, lane, sm.flags);
     } else if constexpr (PH != PH_HEAD) {
@@ -819,6 +834,12 @@ __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, con
       vl[(tid * (TC / 8) + ((pj >> 3) ^ (tid & 15))) * 8 + (pj & 7)] = to_bf16(vn);
     }
     __syncthreads();
+    if constexpr (kEarlyO<SH>) {   // a small o-projection prefetch streams during the last chunk's sweep
+      if (ch == nch - 1 && wid != 0) {
+        nx.issue(0, A);
+        nx.issue(1, B);
+      }
+    }
     const int jw = jb + 32 * wid;   // first position of this wave's block of 32
     if (32 * wid < TC && jw <= pos) {
       f32x4 sc[2];
@@ -940,11 +961,13 @@ __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, con
   if (st) st[3] = (unsigned long long)wall_clock64();
 
   if (wid != 0) {
-    // waves 1-7: the next phase's first weights, concurrent with wave 0's merge and barrier; then, once wave 0 has
-    // its merge inputs (bulk loads issued earlier would queue ahead of them), the gate/up batches that go through
-    // LDS (the K/V chunk is no longer needed)
-    nx.issue(0, A);
-    nx.issue(1, B);
+    // waves 1-7: the next phase's first weights (unless issued at the sweep), concurrent with wave 0's merge and
+    // barrier; then, once wave 0 has its merge inputs (bulk loads issued earlier would queue ahead of them), the
+    // gate/up batches that go through LDS (the K/V chunk is no longer needed)
+    if constexpr (!kEarlyO<SH>) {
+      nx.issue(0, A);
+      nx.issue(1, B);
+    }
     if constexpr (Geo<SH, PH_GU>::NLB > 0) {
       while (__hip_atomic_load(&sm.flags[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != (int)gen)
         __builtin_amdgcn_s_sleep(2);
@@ -1010,7 +1033,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedParams p_in) {
   __shared__ __attribute__((aligned(16))) unsigned char s_stage[2 * SH::KB];
   __shared__ __attribute__((aligned(16))) float s_uni[SH::UNI];
   __shared__ float s_ssq[kFW];
-  __shared__ int s_flags[2];
+  __shared__ int s_flags[3];
   __shared__ int s_qrow[Geo<SH, PH_QKV>::RPB];
   const Smem<SH> sm{s_stage, s_uni, s_ssq, s_flags};
   const int tid = threadIdx.x, lane0 = tid & 63, wid0 = __builtin_amdgcn_readfirstlane(tid >> 6), b0 = blockIdx.x;
@@ -1028,6 +1051,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedParams p_in) {
   if (tid == 0) {
     s_flags[0] = 0;
     s_flags[1] = 0;
+    s_flags[2] = 0;
     if (b0 == 0) {
       if (!tok_ok) raise_error(p.status, ERR_TOKEN);
       if (!pos_ok) raise_error(p.status, ERR_POS);
