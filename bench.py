@@ -69,7 +69,7 @@ def engine_for(w, ws, exec_mode, kernel_plan="auto", trace="off", prefill_rows=N
                       rope_theta=m.rope_theta, rows=w.rows, cap=w.cap, kv_layout=w.kv_layout,
                       page_size=w.page_size, pool_pages=w.pool_pages, weight_dtype=m.weight_dtype,
                       kv_dtype=w.kv_dtype, exec_mode=exec_mode, kernel_plan=kernel_plan, trace=trace,
-                      prefill_rows=(16 if w.start == "prefill_tokens" else 0) if prefill_rows is None else prefill_rows)
+                      prefill_rows=(64 if w.start == "prefill_tokens" else 0) if prefill_rows is None else prefill_rows)
     eng = Engine(cfg, "cuda:0")
     eng.load_weights(ws.layers, ws.glob)
     return eng
@@ -88,13 +88,17 @@ def prefill(eng, w, start_pos):
         toks = synth.prefill_tokens(w)
         first = np.zeros(w.rows, np.int32)
         if eng.cfg.prefill_rows > 0:   # the prompt in chunks of prefill_rows tokens per launch sequence
+            # (a chunk sweeps only the positions up to its own: bit-identical to the full sweep, and a 64-token chunk
+            # would otherwise read every row's whole capacity; decode steps sweep the full capacity again)
+            eng.set_kv_sweep("visible")
             t0 = time.perf_counter()
             for r in range(w.rows):
                 lg, _ = eng.prefill(r, toks[r], 0)
                 first[r] = int(np.argmax(lg))
             dt = time.perf_counter() - t0
+            eng.set_kv_sweep("full")
             prefill.last = {"tokens": int(w.rows * w.prefill_len), "chunk": int(eng.cfg.prefill_rows),
-                            "ms": round(1e3 * dt, 3), "tok_s": round(w.rows * w.prefill_len / dt, 1),
+                            "sweep": "visible", "ms": round(1e3 * dt, 3), "tok_s": round(w.rows * w.prefill_len / dt, 1),
                             "gpu_ms": round(eng.stats()["last_prefill_gpu_us"] / 1e3, 3)}
             return first
         for p in range(w.prefill_len):

@@ -267,7 +267,7 @@ std::string check_config(const ds3_config* c) {
     const std::string why = fused_refusal(*c);
     if (!why.empty()) return "kernel_plan: the fused step kernel does not apply (" + why + ")";
   }
-  if (c->prefill_rows < 0 || c->prefill_rows > kMaxRows) return "prefill_rows must be in 0..16";
+  if (c->prefill_rows < 0 || c->prefill_rows > kMaxPrefillRows) return "prefill_rows must be in 0..64";
   for (const int R : {c->rows, c->prefill_rows}) {
     if (R == 0) continue;
     const char* what = R == c->rows ? "rows" : "prefill_rows";
@@ -348,7 +348,8 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
   w.slot_map = take(c.kv_layout == DS3_KV_PAGED ? (size_t)c.rows * (c.cap / c.page_size) * 4 : 4);
   const size_t kmax = (size_t)std::max(std::max(c.d_model, c.ffn_dim), c.n_q_heads * c.head_dim);
   const bool any_mfma = rows_on_mfma(c, c.rows) || (c.prefill_rows > 0 && rows_on_mfma(c, c.prefill_rows));
-  const size_t frag = any_mfma ? kmax * kMfmaRows * 2 : 16;
+  const int nt_max = sk_tiles(std::max(c.rows, c.prefill_rows));   // activation tiles of the larger step
+  const size_t frag = any_mfma ? kmax * kMfmaRows * nt_max * 2 : 16;
   w.frag_hi = take(frag);
   w.frag_lo = take(frag);
   size_t skp = 4;
@@ -356,10 +357,10 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
     const int qkv = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim, qw = c.n_q_heads * c.head_dim;
     for (const SkPlan& sp : {sk_plan(qkv, c.d_model, false), sk_plan(c.d_model, qw, false),
                              sk_plan(2 * c.ffn_dim, c.d_model, false), sk_plan(c.d_model, c.ffn_dim, false)})
-      skp = std::max(skp, sk_partial_floats(sp) * 4);
+      skp = std::max(skp, sk_partial_floats(sp, nt_max) * 4);
   }
   w.skpart = take(skp);
-  w.skss = take((size_t)((c.d_model + kPrepSpan - 1) / kPrepSpan) * kMfmaRows * 4);
+  w.skss = take((size_t)((c.d_model + kPrepSpan - 1) / kPrepSpan) * kSsRows * 4);
   w.total = off;
   return w;
 }
@@ -468,6 +469,7 @@ hipError_t run_projection(ds3_engine* e, const GemvParams& p, int mode, int kind
   g.part = e->skpart;
   g.out = p.out;
   g.rows = p.rows;
+  g.nt = sk_tiles(p.rows);
   g.n_out = 2 * p.n_pairs;
   g.ss = e->skss;
   g.ss_blocks = (c.d_model + kPrepSpan - 1) / kPrepSpan;
@@ -562,6 +564,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       pp.ss = e->skss;
       pp.D = c.d_model;
       pp.rows = R;
+      pp.nt = sk_tiles(R);
       return launch_sk_prep(pp, e->stream);
     }
     case K_QKVFIN: {
@@ -582,6 +585,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       qp.slots = e->cur.slots;
       qp.status = e->status;
       qp.rows = R;
+      qp.nt = sk_tiles(R);
       return launch_sk_qkv(qp, c.kv_dtype, e->stream);
     }
     case K_SWIGLU: {
@@ -594,6 +598,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       ap.eps = c.rms_eps;
       ap.F = c.ffn_dim;
       ap.rows = R;
+      ap.nt = sk_tiles(R);
       ap.hi = e->frag_hi;
       ap.lo = e->frag_lo;
       return launch_sk_swiglu(ap, e->stream);
@@ -674,6 +679,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       if (e->cur.mfma) {   // the combine also writes the o-projection's fragments
         p.frag_hi = e->frag_hi;
         p.frag_lo = e->frag_lo;
+        p.nt = sk_tiles(R);
       }
       return l.kind == K_ATTN ? launch_attention(p, c.kv_dtype, R, e->stream)
                               : launch_attention_combine(p, R, e->stream);

@@ -96,6 +96,7 @@ struct AttnParams {
   StatusWords* status;
   uint16_t* frag_hi;     // combine, matrix-core path: also the o-projection's activation fragments (else null)
   uint16_t* frag_lo;
+  int nt;                // their activation tiles (sk_tiles(rows))
 };
 
 // Greedy pick after the LM head ("Execution" page, section "A constant-shape decode graph": the step's output
@@ -179,23 +180,28 @@ struct EmbedParams {
   StatusWords* status;
 };
 
-// MFMA path (5..16 rows): activations are handed to the matrix cores as two bf16 parts, hi = bf16(a) and
-// lo = bf16(a - hi), stored in the operand order of v_mfma_f32_16x16x32_bf16 (step t of 32 inputs, lane l holds
-// inputs 32t + 8(l/16) .. +8 of activation row l % 16), the "fragments" [K/32][64][8]. Rows past the step's rows
-// are zero. The kernel that produces an activation writes its fragments.
+// MFMA path (5..16 rows of a decode step, 5..64 of a prefill step): activations are handed to the matrix cores as
+// two bf16 parts, hi = bf16(a) and lo = bf16(a - hi), stored in the operand order of v_mfma_f32_16x16x32_bf16
+// (step t of 32 inputs, tile c of 16 activation rows, lane l holds inputs 32t + 8(l/16) .. +8 of activation row
+// 16c + l % 16), the "fragments" [K/32][nt][64][8] with nt = 1 (up to 16 rows) or 4 (up to 64). Rows past the
+// step's rows are zero. The kernel that produces an activation writes its fragments.
 
 constexpr int kMaxGemvRows = 4;
-constexpr int kMaxRows = 16;
-constexpr int kMfmaRows = 16;   // activation rows of one MFMA tile (rows are zero-padded to it)
+constexpr int kMaxRows = 16;          // rows of a decode step
+constexpr int kMaxPrefillRows = 64;   // tokens of a prefill step
+constexpr int kMfmaRows = 16;         // activation rows of one MFMA tile (rows are zero-padded to whole tiles)
+constexpr int kSsRows = kMaxPrefillRows;   // row stride of the RMSNorm sums of squares
+// activation tiles of a matrix-core step of `rows` rows
+__host__ __device__ inline int sk_tiles(int rows) { return rows > kMfmaRows ? 4 : 1; }
 
 // Matrix-core projection plan (stream-K). The weight matrix [N][K] is cut into groups of kSkRows rows (two 16-row
 // tiles), four neighbouring groups form a quad, and the items (quad, chunk of kSkChunk inputs), numbered
 // quad-major, are split into equal contiguous runs, one per block: block b streams items [first(b), first(b + 1))
 // whatever N and K, its wave w taking group w of each quad (the four waves share the chunk's activations). A wave
-// stores one partial product per group it touched: part[group][k][tile 0/1][lane 64][4] fp32, k = block -
-// block_of(first item of the group's quad) (the MFMA output layout: lane l, element e is weight row
-// 16 tile + 4 (l / 16) + e of the group and activation row l % 16). The kernel that consumes the projection sums
-// a group's k = 0, 1, ... in order, which is input order.
+// stores one partial product per group it touched: part[group][k][activation tile c][tile 0/1][lane 64][4] fp32,
+// k = block - block_of(first item of the group's quad) (the MFMA output layout: lane l, element e is weight row
+// 16 tile + 4 (l / 16) + e of the group and activation row 16 c + l % 16). The kernel that consumes the projection
+// sums a group's k = 0, 1, ... in order, which is input order.
 constexpr int kSkRows = 32;        // weight rows per group (two 16-row tiles)
 constexpr int kSkQuad = 4;         // groups per quad = waves per block
 constexpr int kSkChunk = 128;      // inputs per chunk
@@ -216,11 +222,11 @@ struct SkPlan {
 // whole_quads: each block takes whole quads (the LM head, whose epilogue writes the logits itself).
 // Returns a plan with groups == 0 if the shape is outside what the kernels take.
 SkPlan sk_plan(int n_rows, int K, bool whole_quads);
-inline size_t sk_partial_floats(const SkPlan& p) { return (size_t)p.groups * p.cmax * 512; }
+inline size_t sk_partial_floats(const SkPlan& p, int nt) { return (size_t)p.groups * p.cmax * nt * 512; }
 
 struct SkGemmParams {
   const uint16_t* w;     // [N][K] bf16
-  const uint16_t* hi;    // activation fragments [K/32][64][8]
+  const uint16_t* hi;    // activation fragments [K/32][nt][64][8]
   const uint16_t* lo;
   int K;
   SkPlan plan;
@@ -228,7 +234,8 @@ struct SkGemmParams {
   // LM head (whole groups): logits[r][n] = scale_r * sum, scale_r from the final norm's sums of squares
   float* out;
   int rows, n_out;
-  const float* ss;       // [ss_blocks][16] per-block sums of squares of x
+  int nt;                // activation tiles (sk_tiles(rows))
+  const float* ss;       // [ss_blocks][kSsRows] per-block sums of squares of x
   int ss_blocks, norm_dim;
   float eps;
   StatusWords* status;
@@ -243,8 +250,8 @@ struct SkPrepParams {
   const float* gain;     // [D]
   uint16_t* hi;
   uint16_t* lo;
-  float* ss;             // [ceil(D / kPrepSpan)][16]
-  int D, rows;
+  float* ss;             // [ceil(D / kPrepSpan)][kSsRows]
+  int D, rows, nt;       // (nt: activation tiles of the partials and the fragments)
 };
 
 // QKV epilogue on the partial products: scale, rotary on q and k, q out, k and v stored at Slot::Pos / WriteMap.
@@ -261,7 +268,7 @@ struct SkQkvParams {
   int layer;
   const int* slots;
   StatusWords* status;
-  int rows;
+  int rows, nt;
 };
 
 // SwiGLU on the partial products (gate rows 0..F-1, up rows F..2F-1): fragments of silu(gate) * up.
@@ -271,7 +278,7 @@ struct SkActParams {
   const float* ss;
   int ss_blocks, D;
   float eps;
-  int F, rows;
+  int F, rows, nt;
   uint16_t* hi;
   uint16_t* lo;
 };

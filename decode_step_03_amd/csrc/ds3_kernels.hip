@@ -40,11 +40,11 @@ constexpr int kMaxSplits = 32;          // attention: splits per (row, kv head),
 constexpr int kAttnChunk = 128;         // attention: positions staged in LDS per chunk, at most ...
 constexpr int kAttnChunkBytes = 32768;  // ... and at most this many bytes of K (and of V)
 
-// 8 values of activation row r from input k0 -> hi/lo fragment words
-__device__ __forceinline__ void store_frag8(uint16_t* hi, uint16_t* lo, int r, int k0, const float (&v)[8]) {
+// 8 values of activation row r from input k0 -> hi/lo fragment words (nt activation tiles)
+__device__ __forceinline__ void store_frag8(uint16_t* hi, uint16_t* lo, int nt, int r, int k0, const float (&v)[8]) {
   bf16x8 h, l;
   split_hi_lo8(v, h, l);
-  const size_t idx = ((size_t)(k0 >> 5) * 64 + ((k0 >> 3) & 3) * 16 + r) * 8;
+  const size_t idx = (((size_t)(k0 >> 5) * nt + (r >> 4)) * 64 + ((k0 >> 3) & 3) * 16 + (r & 15)) * 8;
   *reinterpret_cast<bf16x8*>(hi + idx) = h;
   *reinterpret_cast<bf16x8*>(lo + idx) = l;
 }
@@ -408,26 +408,32 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
 // of the whole product, multiplies the sums in the consumer. The sums of squares come from the kernel that wrote
 // x, one partial per block and row, added in block order.
 
-constexpr int kSkBufs = 3;                       // chunk buffers (two load while one is consumed)
-constexpr int kSkTileBytes = 16 * kSkChunk * 2;  // one 16-row tile of one chunk: 4 KB
-constexpr int kSkActBytes = kSkChunk / 32 * 2 * 1024;   // a chunk's activation fragments, hi and lo: 8 KB
+constexpr int kSkTileBytes = 16 * kSkChunk * 2;  // one 16-row weight tile of one chunk: 4 KB
+constexpr int kSkActTileBytes = kSkChunk / 32 * 2 * 1024;   // a chunk's fragments of one activation tile, hi and lo: 8 KB
 constexpr int kSkNt = 2;                         // cache policy of the weight loads: streamed once
-constexpr size_t kSkRingBytes = (size_t)kSkWaves * kSkBufs * 2 * kSkTileBytes;   // weights: 96 KB
-constexpr size_t kSkLds = kSkRingBytes + (size_t)kSkBufs * kSkActBytes;          // + activations: 24 KB
+// chunk buffers: three (two load while one is consumed) with one activation tile; two with four, whose fragments
+// take four times the LDS (weights 64 KB + activations 64 KB)
+template <int NT>
+constexpr int kSkBufs = NT == 1 ? 3 : 2;
+template <int NT>
+constexpr size_t kSkRingBytes = (size_t)kSkWaves * kSkBufs<NT> * 2 * kSkTileBytes;   // weights: 96 / 64 KB
+template <int NT>
+constexpr size_t kSkLds = kSkRingBytes<NT> + (size_t)kSkBufs<NT> * NT * kSkActTileBytes;   // + 24 / 64 KB
 
 // sum of the partial products of weight rows n .. n + 3 (n % 4 == 0) for activation row r, in block order; the
 // loads of up to eight contributors are issued before their adds
-__device__ __forceinline__ f32x4 sk_sum4(const float* part, const SkPlan& pl, int n, int r) {
-  const int g = n / kSkRows, t = (n >> 4) & 1, lane = 16 * ((n & 15) >> 2) + r;
+__device__ __forceinline__ f32x4 sk_sum4(const float* part, const SkPlan& pl, int nt, int n, int r) {
+  const int g = n / kSkRows, t = (n >> 4) & 1, lane = 16 * ((n & 15) >> 2) + (r & 15);
   const int a = g / kSkQuad * pl.nck;
   const int nb = pl.block_of(a + pl.nck - 1) - pl.block_of(a) + 1;
-  const float* base = part + ((size_t)g * pl.cmax * 128 + t * 64 + lane) * 4;
+  const float* base = part + ((((size_t)g * pl.cmax * nt + (r >> 4)) * 2 + t) * 64 + lane) * 4;
+  const size_t stride = (size_t)nt * 512;   // one contributor
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
   for (int kb = 0; kb < nb; kb += 8) {
     f32x4 v[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c)
-      v[c] = kb + c < nb ? *reinterpret_cast<const f32x4*>(base + (size_t)(kb + c) * 512) : f32x4{0.f, 0.f, 0.f, 0.f};
+      v[c] = kb + c < nb ? *reinterpret_cast<const f32x4*>(base + (size_t)(kb + c) * stride) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 8; ++c)
       if (kb + c < nb) s += v[c];
@@ -439,16 +445,19 @@ __device__ __forceinline__ f32x4 sk_sum4(const float* part, const SkPlan& pl, in
 __device__ __forceinline__ float sk_row_scale(const float* ss, int nblk, int r, int D, float eps) {
   float t = 0.f;
 #pragma unroll 8
-  for (int b = 0; b < nblk; ++b) t += ss[b * kMfmaRows + r];
+  for (int b = 0; b < nblk; ++b) t += ss[b * kSsRows + r];
   return 1.0f / sqrtf(t / (float)D + eps);
 }
 
 // One block per CU, wave w on group w of each quad of the block's run; the waves meet at a barrier per chunk
 // (the chunk's activations come from all four). HEAD: whole quads per block, logits out; else partial products.
-template <bool HEAD>
+// NT activation tiles of 16 rows (1: up to 16 rows, 4: up to 64): every weight tile meets each of them.
+template <bool HEAD, int NT>
 __global__ void __launch_bounds__(64 * kSkWaves) sk_gemm_kernel(SkGemmParams p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char sk_lds[];
-  constexpr int OPC = 10;   // vector-memory operations per chunk and wave: 8 weight (2 tiles x 4), 2 activation
+  constexpr int B = kSkBufs<NT>;
+  constexpr int OPC = 8 + 2 * NT;   // vector-memory operations per chunk and wave: 8 weight (2 tiles x 4), 2 NT activation
+  constexpr int ACT = NT * kSkActTileBytes;   // a chunk's activation fragments
   const int lane = threadIdx.x & 63, r16 = lane & 15, hq = lane >> 4;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const SkPlan pl = p.plan;
@@ -462,12 +471,14 @@ __global__ void __launch_bounds__(64 * kSkWaves) sk_gemm_kernel(SkGemmParams p) 
     i1 = pl.first(b + 1);
   }
   if (i0 >= i1) return;   // (block-uniform)
-  unsigned char* mine = sk_lds + (size_t)wid * kSkBufs * 2 * kSkTileBytes;
-  unsigned char* act = sk_lds + kSkRingBytes;   // [buffer][hi k-steps 0..3, lo k-steps 0..3][64 lanes][16 B]
+  unsigned char* mine = sk_lds + (size_t)wid * B * 2 * kSkTileBytes;
+  // activations: [buffer][hi k-steps 0..3 x tiles, lo k-steps 0..3 x tiles][64 lanes][16 B]
+  unsigned char* act = sk_lds + kSkRingBytes<NT>;
   const int K = p.K, nck = pl.nck;
 
-  // chunk i into buffer bf: the wave's own two tiles (tile t's row r lands at byte 256 r, its 16-byte piece c at
-  // position c ^ r; instruction j covers rows 4j .. 4j + 3) and a quarter of the activation fragments
+  // chunk i into buffer bf: the wave's own two weight tiles (tile t's row r lands at byte 256 r, its 16-byte piece
+  // c at position c ^ r; instruction j covers rows 4j .. 4j + 3) and its share of the activation fragments
+  // (1 KB pieces m = part x 4 NT + k-step x NT + tile, wave w taking pieces 2 NT w .. 2 NT w + 2 NT - 1)
   auto issue = [&](int i, int bf) {
     const int q = i / nck, ck = i - q * nck;
     const int g = kSkQuad * q + wid;
@@ -482,72 +493,90 @@ __global__ void __launch_bounds__(64 * kSkWaves) sk_gemm_kernel(SkGemmParams p) 
       }
     }
 #pragma unroll
-    for (int m = 2 * wid; m < 2 * wid + 2; ++m) {   // 1 KB each: (hi, lo) x 4 k-steps
-      const uint16_t* src = (m < 4 ? p.hi : p.lo) + ((size_t)(ck * 4 + (m & 3)) * 64 + lane) * 8;
-      __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(act + bf * kSkActBytes + 1024 * m), 16, 0, 0);
+    for (int m = 2 * NT * wid; m < 2 * NT * wid + 2 * NT; ++m) {
+      const int part = m / (4 * NT), st = (m / NT) % 4, ct = m % NT;
+      const uint16_t* src = (part == 0 ? p.hi : p.lo) + (((size_t)(ck * 4 + st) * NT + ct) * 64 + lane) * 8;
+      __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(act + bf * ACT + 1024 * m), 16, 0, 0);
     }
   };
 
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc0[NT], acc1[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+    acc0[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc1[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   int cur = i0 / nck;
-  float scale = 1.f;
-  if constexpr (HEAD) scale = sk_row_scale(p.ss, p.ss_blocks, r16, p.norm_dim, p.eps);
+  float scale[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) scale[c] = 1.f;
+  if constexpr (HEAD)
+#pragma unroll
+    for (int c = 0; c < NT; ++c) scale[c] = sk_row_scale(p.ss, p.ss_blocks, 16 * c + r16, p.norm_dim, p.eps);
   auto flush = [&](int q) {
     const int g = kSkQuad * q + wid;
-    if constexpr (HEAD) {
-      if (r16 < p.rows) {
-        const f32x4 a = acc0 * scale, c = acc1 * scale;
-        float* o = p.out + (size_t)r16 * p.n_out + kSkRows * g + 4 * hq;
-        *reinterpret_cast<f32x4*>(o) = a;
-        *reinterpret_cast<f32x4*>(o + 16) = c;
-        bool fin = true;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) fin = fin && isfinite(a[e]) && isfinite(c[e]);
-        if (!fin) atomicOr(&p.status->nonfinite, 1u);
+    for (int c = 0; c < NT; ++c) {
+      if constexpr (HEAD) {
+        const int r = 16 * c + r16;
+        if (r < p.rows) {
+          const f32x4 a = acc0[c] * scale[c], d = acc1[c] * scale[c];
+          float* o = p.out + (size_t)r * p.n_out + kSkRows * g + 4 * hq;
+          *reinterpret_cast<f32x4*>(o) = a;
+          *reinterpret_cast<f32x4*>(o + 16) = d;
+          bool fin = true;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fin = fin && isfinite(a[e]) && isfinite(d[e]);
+          if (!fin) atomicOr(&p.status->nonfinite, 1u);
+        }
+      } else {
+        const int k = b - pl.block_of(q * nck);
+        float* o = p.part + (((((size_t)g * pl.cmax + k) * NT + c) * 2) * 64 + lane) * 4;
+        *reinterpret_cast<f32x4*>(o) = acc0[c];
+        *reinterpret_cast<f32x4*>(o + 256) = acc1[c];
       }
-    } else {
-      const int k = b - pl.block_of(q * nck);
-      float* o = p.part + (((size_t)g * pl.cmax + k) * 2 * 64 + lane) * 4;
-      *reinterpret_cast<f32x4*>(o) = acc0;
-      *reinterpret_cast<f32x4*>(o + 256) = acc1;
+      acc0[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc1[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
   };
 
 #pragma unroll
-  for (int q = 0; q < kSkBufs - 1; ++q)
+  for (int q = 0; q < B - 1; ++q)
     if (i0 + q < i1) issue(i0 + q, q);
-  for (int base = i0; base < i1; base += kSkBufs) {
+  for (int base = i0; base < i1; base += B) {
 #pragma unroll
-    for (int q = 0; q < kSkBufs; ++q) {
+    for (int q = 0; q < B; ++q) {
       const int i = base + q;
       if (i < i1) {
-        // chunk i (buffer q) has landed once only the chunk after it is outstanding (loads complete in order; a
-        // store issued in between only makes the wait stricter); the barrier makes every wave's quarter of the
-        // activations visible and frees the buffer read in the previous step, which then takes chunk i + 2
-        if (i + 1 < i1) __builtin_amdgcn_s_waitcnt(kVmcntChunk<OPC>());
+        // chunk i (buffer q) has landed once only the chunks after it are outstanding (loads complete in order; a
+        // store issued in between only makes the wait stricter); the barrier makes every wave's share of the
+        // activations visible and frees the buffer read in the previous step, which then takes chunk i + B - 1
+        if (B > 2 && i + 1 < i1) __builtin_amdgcn_s_waitcnt(kVmcntChunk<OPC>());
         else __builtin_amdgcn_s_waitcnt(kVmcntChunk<0>());
         barrier_lds();
-        if (i + kSkBufs - 1 < i1) issue(i + kSkBufs - 1, (q + kSkBufs - 1) % kSkBufs);
+        if (i + B - 1 < i1) issue(i + B - 1, (q + B - 1) % B);
         const int qd = i / nck;
         if (qd != cur) {
           flush(cur);
           cur = qd;
         }
         const unsigned char* t0 = mine + (q * 2) * kSkTileBytes + r16 * 256;
-        const unsigned char* av = act + q * kSkActBytes + lane * 16;
+        const unsigned char* av = act + q * ACT + lane * 16;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int at = 16 * ((4 * s + hq) ^ r16);
+        for (int st = 0; st < 4; ++st) {
+          const int at = 16 * ((4 * st + hq) ^ r16);
           const bf16x8 A0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(t0 + at));
           const bf16x8 A1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(t0 + kSkTileBytes + at));
-          const bf16x8 BH = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(av + 1024 * s));
-          const bf16x8 BL = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(av + 1024 * (4 + s)));
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BH, acc0, 0, 0, 0);
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BL, acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BH, acc1, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BL, acc1, 0, 0, 0);
+#pragma unroll
+          for (int c = 0; c < NT; ++c) {
+            const bf16x8 BH = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(av + 1024 * (st * NT + c)));
+            const bf16x8 BL =
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(av + 1024 * (4 * NT + st * NT + c)));
+            acc0[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BH, acc0[c], 0, 0, 0);
+            acc0[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BL, acc0[c], 0, 0, 0);
+            acc1[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BH, acc1[c], 0, 0, 0);
+            acc1[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BL, acc1[c], 0, 0, 0);
+          }
         }
       }
     }
@@ -555,7 +584,7 @@ __global__ void __launch_bounds__(64 * kSkWaves) sk_gemm_kernel(SkGemmParams p) 
   flush(cur);
 }
 
-// grid = (ceil(D / kPrepSpan), 16 rows), one wave per block, 8 inputs per lane.
+// grid = (ceil(D / kPrepSpan), 16 nt rows), one wave per block, 8 inputs per lane.
 __global__ void __launch_bounds__(64) sk_prep_kernel(SkPrepParams p) {
   const int r = blockIdx.y, lane = threadIdx.x;
   const int k0 = blockIdx.x * kPrepSpan + 8 * lane;
@@ -566,7 +595,7 @@ __global__ void __launch_bounds__(64) sk_prep_kernel(SkPrepParams p) {
     float4 a = *reinterpret_cast<const float4*>(x);
     float4 b = *reinterpret_cast<const float4*>(x + 4);
     if (p.part) {
-      const f32x4 pa = sk_sum4(p.part, p.plan, k0, r), pb = sk_sum4(p.part, p.plan, k0 + 4, r);
+      const f32x4 pa = sk_sum4(p.part, p.plan, p.nt, k0, r), pb = sk_sum4(p.part, p.plan, p.nt, k0 + 4, r);
       a.x += pa[0]; a.y += pa[1]; a.z += pa[2]; a.w += pa[3];
       b.x += pb[0]; b.y += pb[1]; b.z += pb[2]; b.w += pb[3];
       *reinterpret_cast<float4*>(x) = a;
@@ -578,14 +607,14 @@ __global__ void __launch_bounds__(64) sk_prep_kernel(SkPrepParams p) {
 #pragma unroll
   for (int e = 0; e < 8; e += 2) ss += v[e] * v[e] + v[e + 1] * v[e + 1];
   ss = wave_total(ss);
-  if (lane == 0) p.ss[blockIdx.x * kMfmaRows + r] = ss;
+  if (lane == 0) p.ss[blockIdx.x * kSsRows + r] = ss;
   if (!in) return;
   if (live) {
     const float4 ga = *reinterpret_cast<const float4*>(p.gain + k0);
     const float4 gb = *reinterpret_cast<const float4*>(p.gain + k0 + 4);
     v[0] *= ga.x; v[1] *= ga.y; v[2] *= ga.z; v[3] *= ga.w; v[4] *= gb.x; v[5] *= gb.y; v[6] *= gb.z; v[7] *= gb.w;
   }
-  store_frag8(p.hi, p.lo, r, k0, v);
+  store_frag8(p.hi, p.lo, p.nt, r, k0, v);
 }
 
 // grid = (ceil(N / 4 / kBlock), rows): a thread takes output rows n .. n + 3 (n = 4 x index) of activation row r;
@@ -607,7 +636,7 @@ __global__ void __launch_bounds__(kBlock) sk_qkv_kernel(SkQkvParams p) {
     pos = 0;
   }
   const float sc = sk_row_scale(p.ss, p.ss_blocks, r, p.D, p.eps);
-  const f32x4 a = sk_sum4(p.part, p.plan, n, r) * sc;
+  const f32x4 a = sk_sum4(p.part, p.plan, p.nt, n, r) * sc;
   int loc = pos;
   if (seg != 0) {
     if (!ok) return;
@@ -626,7 +655,7 @@ __global__ void __launch_bounds__(kBlock) sk_qkv_kernel(SkQkvParams p) {
     for (int e = 0; e < 4; ++e) store_kv(base + kv_at(p.kv, true, r, p.nkv, head, hd, loc, idx + e), a[e]);
     return;
   }
-  const f32x4 b = sk_sum4(p.part, p.plan, n + half, r) * sc;
+  const f32x4 b = sk_sum4(p.part, p.plan, p.nt, n + half, r) * sc;
   float va[4], vb[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -652,7 +681,7 @@ __global__ void __launch_bounds__(kBlock) sk_qkv_kernel(SkQkvParams p) {
   }
 }
 
-// grid = (ceil(F / kPrepSpan), 16 rows), one wave per block: silu(gate) * up of 8 consecutive j -> fragments.
+// grid = (ceil(F / kPrepSpan), 16 nt rows), one wave per block: silu(gate) * up of 8 consecutive j -> fragments.
 __global__ void __launch_bounds__(64) sk_swiglu_kernel(SkActParams p) {
   const int r = blockIdx.y;
   const int j0 = blockIdx.x * kPrepSpan + 8 * threadIdx.x;
@@ -662,13 +691,13 @@ __global__ void __launch_bounds__(64) sk_swiglu_kernel(SkActParams p) {
     const float sc = sk_row_scale(p.ss, p.ss_blocks, r, p.D, p.eps);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const f32x4 g = sk_sum4(p.part, p.plan, j0 + 4 * h, r) * sc;
-      const f32x4 u = sk_sum4(p.part, p.plan, p.F + j0 + 4 * h, r) * sc;
+      const f32x4 g = sk_sum4(p.part, p.plan, p.nt, j0 + 4 * h, r) * sc;
+      const f32x4 u = sk_sum4(p.part, p.plan, p.nt, p.F + j0 + 4 * h, r) * sc;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[4 * h + e] = g[e] / (1.0f + expf(-g[e])) * u[e];
     }
   }
-  store_frag8(p.hi, p.lo, r, j0, v);
+  store_frag8(p.hi, p.lo, p.nt, r, j0, v);
 }
 
 // ----------------------------------------------------------------------------------------------------------
@@ -750,7 +779,7 @@ __global__ void __launch_bounds__(128) attn_combine_kernel(AttnParams p) {
     v[0] = o;
 #pragma unroll
     for (int k = 1; k < 8; ++k) v[k] = __shfl_down(o, k, 64);
-    if ((d & 7) == 0) store_frag8(p.frag_hi, p.frag_lo, r, h * HD + d, v);
+    if ((d & 7) == 0) store_frag8(p.frag_hi, p.frag_lo, p.nt, r, h * HD + d, v);
   }
 }
 
@@ -2299,25 +2328,28 @@ hipError_t launch_sk_gemm(const SkGemmParams& p, bool head, hipStream_t s) {
   if (p.K % kSkChunk || pl.nck != p.K / kSkChunk || pl.groups < kSkQuad || pl.groups % kSkQuad || pl.nck < 1 || pl.nb < 1)
     return hipErrorInvalidValue;
   if (!head && pl.cmax < 1) return hipErrorInvalidValue;
-  if (head && (p.rows < 1 || p.rows > kMfmaRows || p.n_out != pl.groups * kSkRows || p.n_out % 4)) return hipErrorInvalidValue;
+  if (p.nt != sk_tiles(p.rows) || p.rows < 1 || p.rows > kMfmaRows * p.nt) return hipErrorInvalidValue;
+  if (head && (p.n_out != pl.groups * kSkRows || p.n_out % 4)) return hipErrorInvalidValue;
   if (!head && !p.part) return hipErrorInvalidValue;
-  auto* f = head ? sk_gemm_kernel<true> : sk_gemm_kernel<false>;
-  hipError_t e = set_lds(f, kSkLds);
+  auto* f = p.nt == 1 ? (head ? sk_gemm_kernel<true, 1> : sk_gemm_kernel<false, 1>)
+                      : (head ? sk_gemm_kernel<true, 4> : sk_gemm_kernel<false, 4>);
+  const size_t lds = p.nt == 1 ? kSkLds<1> : kSkLds<4>;
+  hipError_t e = set_lds(f, lds);
   if (e != hipSuccess) return e;
-  f<<<pl.nb, 64 * kSkWaves, kSkLds, s>>>(p);
+  f<<<pl.nb, 64 * kSkWaves, lds, s>>>(p);
   return hipGetLastError();
 }
 
 hipError_t launch_sk_prep(const SkPrepParams& p, hipStream_t s) {
-  if (p.D % 8 || p.rows < 1 || p.rows > kMfmaRows) return hipErrorInvalidValue;
-  const dim3 grid((p.D + kPrepSpan - 1) / kPrepSpan, kMfmaRows);
+  if (p.D % 8 || p.rows < 1 || p.nt != sk_tiles(p.rows) || p.rows > kMfmaRows * p.nt) return hipErrorInvalidValue;
+  const dim3 grid((p.D + kPrepSpan - 1) / kPrepSpan, kMfmaRows * p.nt);
   sk_prep_kernel<<<grid, 64, 0, s>>>(p);
   return hipGetLastError();
 }
 
 hipError_t launch_sk_qkv(const SkQkvParams& p, int kv_dtype, hipStream_t s) {
   const int n4 = (p.nq + 2 * p.nkv) * p.hd / 4;
-  if (p.hd % 8 || p.rows < 1 || p.rows > kMfmaRows) return hipErrorInvalidValue;
+  if (p.hd % 8 || p.rows < 1 || p.nt != sk_tiles(p.rows) || p.rows > kMfmaRows * p.nt) return hipErrorInvalidValue;
   const dim3 grid((n4 + kBlock - 1) / kBlock, p.rows);
   if (kv_dtype == 1) sk_qkv_kernel<uint16_t><<<grid, kBlock, 0, s>>>(p);
   else sk_qkv_kernel<float><<<grid, kBlock, 0, s>>>(p);
@@ -2325,8 +2357,8 @@ hipError_t launch_sk_qkv(const SkQkvParams& p, int kv_dtype, hipStream_t s) {
 }
 
 hipError_t launch_sk_swiglu(const SkActParams& p, hipStream_t s) {
-  if (p.F % 8 || p.rows < 1 || p.rows > kMfmaRows) return hipErrorInvalidValue;
-  const dim3 grid((p.F + kPrepSpan - 1) / kPrepSpan, kMfmaRows);
+  if (p.F % 8 || p.rows < 1 || p.nt != sk_tiles(p.rows) || p.rows > kMfmaRows * p.nt) return hipErrorInvalidValue;
+  const dim3 grid((p.F + kPrepSpan - 1) / kPrepSpan, kMfmaRows * p.nt);
   sk_swiglu_kernel<<<grid, 64, 0, s>>>(p);
   return hipGetLastError();
 }

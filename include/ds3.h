@@ -90,7 +90,7 @@ typedef struct {
   uint32_t timeout_ms;
   int32_t kernel_plan;         /* DS3_PLAN_*; FUSED where it does not apply -> DS3_E_UNSUPPORTED */
   int32_t trace;               /* DS3_TRACE_*: fused plan, what every step records for ds3_phase_trace */
-  int32_t prefill_rows;        /* 0: no prefill step; 1..16: ds3_prefill takes this many tokens per launch */
+  int32_t prefill_rows;        /* 0: no prefill step; 1..64: ds3_prefill takes this many tokens per launch */
 } ds3_config;
 
 /* Device buffers the caller allocates for ds3_create, in this id order. */
@@ -267,7 +267,9 @@ ds3_status ds3_step_sample(ds3_engine* e, const int32_t* tokens, const int32_t* 
  * t of the chunk at position pos0 + k prefill_rows + t, so its attention sees the K/V of the chunk's earlier tokens
  * (written by the same step before the attention runs) and nothing after its own position -- the causal mask
  * inside the chunk is the position mask of the decode step. Chunks run their projections on the matrix cores
- * under the same rule as decode rows (see the rows field of ds3_config). The rows after the last token of the last chunk repeat that token at its position. logits_host (float32
+ * under the same rule as decode rows (see the rows field of ds3_config); a chunk of 17..64 rows takes four
+ * 16-row activation tiles per weight tile, so its weights stream once for up to 64 tokens. The rows after the
+ * last token of the last chunk repeat that token at its position. logits_host (float32
  * [vocab], may be NULL) receives the last token's logits, from which the first decode step's token is picked;
  * flags (may be NULL) bit 0: some logit of the prefill was NaN or infinite. n in 1..DS3_MAX_PREFILL; pos0 + n must
  * not pass cap; paged layout: the page table must be set. DS3_E_UNSUPPORTED when the engine was created with

@@ -2,7 +2,8 @@
 configuration bench.py times (HIP-graph replay, the engine's own kernel plan and split plan):
 
 * the 1B-shaped decoder (16 layers, vocab 32000, cap 4096): the 512-token random prompt through ds3_prefill in
-  16-token chunks (matrix-core projections), checked against a causal forward of the whole prompt (last-token
+  64-token chunks (matrix-core projections, four activation tiles), checked against a causal forward of the whole
+  prompt (last-token
   logits, the K/V of every prompt position at the first and last layer), then greedy decode steps on the fused
   step kernel, teacher-forced by the oracle's pick;
 * the 8B-shaped decoder with 8 rows of contiguous K/V at cap 32768 and seeded start positions in [1024, 32000];
@@ -51,7 +52,7 @@ def _decode(ls, eng, tok, pos, steps, visible_from):
 def test_llama1b_prompt_prefill_then_greedy_full_depth():
     w = synth.workload("llama1b-bf16")
     ws = weights(w.model)
-    eng = make_engine(w, ws, prefill_rows=16)
+    eng = make_engine(w, ws, prefill_rows=64)
     try:
         n = w.prefill_len
         ls = Lockstep(w, ws, eng, n_alloc=n + 16)

@@ -2,8 +2,9 @@
 of a chunk an activation row of the same K/V row. Against the oracle fed the same tokens one decode step at a
 time (a prefill is steps at consecutive absolute positions): the last token's logits within
 the stated tolerance and its greedy id outside the margin, the K/V of every prompt position, and decoding after
-the prefill staying in parity. Chunks of 16 tokens run the projections on the matrix cores, chunks of up to 4 on
-the GEMV kernels; the last chunk may be partial.
+the prefill staying in parity. Chunks of 16 tokens run the projections on the matrix cores with one 16-row
+activation tile, chunks of 17..64 with four (a 40-token chunk pads 24 rows), chunks of up to 4 on the GEMV kernels;
+the last chunk may be partial, and a chunk may sweep the whole capacity or only the visible positions.
 """
 from dataclasses import replace
 
@@ -28,12 +29,15 @@ def _check_last(w, got, ref):
     return err
 
 
-@pytest.mark.parametrize("case", ["1b-mfma16", "tiny-gemv3", "1b-paged16"])
+@pytest.mark.parametrize("case", ["1b-mfma16", "1b-mfma64", "1b-mfma64-visible", "1b-mfma40", "tiny-gemv3",
+                                  "1b-paged16", "8b-paged64"])
 def test_prefill_matches_oracle_then_decodes(case):
-    if case == "1b-mfma16":
+    sweep = "visible" if case.endswith("visible") else "full"
+    if case.startswith("1b-mfma"):
         base = synth.workload("llama1b-bf16")
         w = replace(synth.small_variant(base, n_layers=2, vocab=4096), name="llama1b-2l-prefill")
-        T, row, pos0, n = 16, 0, 0, 40
+        T, row, pos0, n = {"1b-mfma16": (16, 0, 0, 40), "1b-mfma64": (64, 0, 0, 150),
+                           "1b-mfma64-visible": (64, 0, 0, 150), "1b-mfma40": (40, 0, 30, 90)}[case]
     elif case == "tiny-gemv3":
         w = synth.workload("tiny-fp32")
         T, row, pos0, n = 3, 0, 5, 20
@@ -41,10 +45,11 @@ def test_prefill_matches_oracle_then_decodes(case):
         base = synth.workload("llama8b-bf16-r16-paged")
         w = replace(synth.small_variant(base, n_layers=1, vocab=4096, rows=2, cap=1024, pool_pages=256),
                     name="llama8b-r2-paged-prefill")
-        T, row, pos0, n = 16, 1, 100, 37
+        T, row, pos0, n = (16, 1, 100, 37) if case == "1b-paged16" else (64, 1, 100, 100)
     ws = synth.make_weights(w.model)
     eng = make_engine(w, ws, prefill_rows=T)
     try:
+        eng.set_kv_sweep(sweep)
         ls = Lockstep(w, ws, eng)
         if w.kv_layout == "paged":
             eng.set_slot_map(synth.page_table(w))
