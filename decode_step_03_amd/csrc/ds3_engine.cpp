@@ -160,6 +160,7 @@ struct ds3_engine {
     float* logits = nullptr;
     bool mfma = false;            // projections on the matrix cores (rows_on_mfma)
     const int* row_map = nullptr; // K/V row of each activation row (null: the row itself)
+    int splits = 0, split_len = 0;  // attention split plan of a step of `rows` rows
   };
   RunCtx dec, pre, cur;
   std::vector<Launch> pre_sequence;
@@ -189,7 +190,7 @@ ds3_status poison(ds3_engine* e, ds3_status st, const std::string& msg) {
       return poison((e), DS3_E_DEVICE_LOST, std::string(#call) + ": " + hipGetErrorString(_h));         \
   } while (0)
 
-void plan_splits(const ds3_config& c, int* splits, int* split_len);
+void plan_splits(const ds3_config& c, int rows, int* splits, int* split_len);
 
 // Why the fused step kernel cannot run this configuration ("" if it can, device aside).
 std::string fused_refusal(const ds3_config& c) {
@@ -256,9 +257,10 @@ std::string check_config(const ds3_config* c) {
                                   : (int64_t)c->rows * c->n_kv_heads * c->cap * c->head_dim;
     if (per_layer > INT32_MAX) return "cap / pool_pages: one layer's K must hold fewer than 2^31 elements";
   }
-  {
+  for (const int R : {c->rows, c->prefill_rows}) {
+    if (R < 1) continue;
     int splits = 0, split_len = 0;
-    plan_splits(*c, &splits, &split_len);
+    plan_splits(*c, R, &splits, &split_len);
     if (attn_lds_bytes(c->n_q_heads, c->n_kv_heads, c->head_dim, split_len, c->kv_dtype,
                        c->kv_layout == DS3_KV_PAGED ? c->page_size : 0) > 160 * 1024)
       return "cap / page_size: the attention page table of a split does not fit the 160 KB LDS";
@@ -292,14 +294,15 @@ std::string check_config(const ds3_config* c) {
   return "";
 }
 
-// Attention split plan: about kAttnBlocks blocks over rows x kv heads x splits (measured best among 256..1024 on
-// MI355X). A split is a whole number of LDS chunks, and there are no more splits than the in-kernel merge takes.
-// The plan is a function of the configuration alone, so one configuration always reduces in the same order.
+// Attention split plan of a step of `rows` rows (the decode rows, or a prefill chunk's tokens): about kAttnBlocks
+// blocks over rows x kv heads x splits (measured best among 256..1024 on MI355X). A split is a whole number of LDS
+// chunks, and there are no more splits than the in-kernel merge takes. The plan is a function of the configuration
+// and the step alone, so a step always reduces in the same order.
 constexpr int kAttnBlocks = 512;
-void plan_splits(const ds3_config& c, int* splits, int* split_len) {
+void plan_splits(const ds3_config& c, int rows, int* splits, int* split_len) {
   const int chunk = attn_positions_per_pass(c.head_dim, c.kv_dtype);
   const int units = (c.cap + chunk - 1) / chunk;
-  int s = std::max(1, kAttnBlocks / (c.rows * c.n_kv_heads));
+  int s = std::max(1, kAttnBlocks / (rows * c.n_kv_heads));
   s = std::min(s, units);
   s = std::min(s, attn_max_splits(c.n_q_heads, c.n_kv_heads, c.head_dim));
   const int per = (units + s - 1) / s;
@@ -324,7 +327,13 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
   w.q = take(RA * c.n_q_heads * c.head_dim * 4);
   w.attn = take(RA * c.n_q_heads * c.head_dim * 4);
   w.act = take(RA * c.ffn_dim * 4);
-  w.part = take(RA * c.n_kv_heads * std::max(splits, kFusedBlocks / c.n_kv_heads) * G * (c.head_dim + 4) * 4);
+  size_t row_splits = RA * std::max(splits, kFusedBlocks / c.n_kv_heads);   // attention partials: rows x splits
+  if (c.prefill_rows > 0) {
+    int ps = 0, pl = 0;
+    plan_splits(c, c.prefill_rows, &ps, &pl);
+    row_splits = std::max(row_splits, (size_t)c.prefill_rows * ps);
+  }
+  w.part = take(row_splits * c.n_kv_heads * G * (c.head_dim + 4) * 4);
   w.pre_slots = take(c.prefill_rows ? (size_t)(SlotLayout{c.prefill_rows}.words() + c.prefill_rows) * 4 : 4);
   w.pre_logits = take(c.prefill_rows ? (size_t)c.prefill_rows * c.vocab * 4 : 4);
   w.kvnew = take((size_t)c.n_kv_heads * 2 * c.head_dim * 4);
@@ -671,8 +680,8 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.nq = c.n_q_heads;
       p.nkv = c.n_kv_heads;
       p.hd = c.head_dim;
-      p.splits = e->splits;
-      p.split_len = e->split_len;
+      p.splits = e->cur.splits;
+      p.split_len = e->cur.split_len;
       p.scale = (float)(1.0 / std::sqrt((double)c.head_dim));
       p.slots = e->cur.slots;
       p.status = e->status;
@@ -776,7 +785,7 @@ ds3_status ds3_query_buffers(const ds3_config* cfg, ds3_buffer_req* out, int32_t
   if (!why.empty()) return fail(nullptr, cfg ? DS3_E_UNSUPPORTED : DS3_E_INVALID, why);
   if (!out || !n_inout || *n_inout < DS3_NUM_BUFFERS) return fail(nullptr, DS3_E_INVALID, "need room for 4 buffers");
   int splits, split_len;
-  plan_splits(*cfg, &splits, &split_len);
+  plan_splits(*cfg, cfg->rows, &splits, &split_len);
   const size_t sizes[DS3_NUM_BUFFERS] = {plan_weights(*cfg).total, kv_state_bytes(*cfg),
                                          plan_work(*cfg, splits).total,
                                          (size_t)cfg->rows * cfg->vocab * sizeof(float)};
@@ -821,7 +830,7 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   // the allocation-free staging array of this device, looked up once per device while it is current
   h = scratch_device_ptr(e->device, &e->scratch);
   if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("scratch array: ") + hipGetErrorString(h));
-  plan_splits(c, &e->splits, &e->split_len);
+  plan_splits(c, c.rows, &e->splits, &e->split_len);
   const WorkPlan wp = plan_work(c, e->splits);
   char* work = reinterpret_cast<char*>(e->buf[DS3_BUF_WORK]);
   e->slots = reinterpret_cast<int*>(work + wp.slots);
@@ -939,6 +948,8 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
                       hipHostMallocDefault);
   if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("hipHostMalloc: ") + hipGetErrorString(h));
   e->dec.rows = c.rows;
+  e->dec.splits = e->splits;
+  e->dec.split_len = e->split_len;
   e->dec.slots = e->slots;
   e->dec.logits = e->logits;
   e->dec.mfma = e->mfma;
@@ -946,6 +957,7 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   if (c.prefill_rows > 0) {
     const int T = c.prefill_rows;
     e->pre.rows = T;
+    plan_splits(c, T, &e->pre.splits, &e->pre.split_len);   // (the partials buffer holds either plan)
     e->pre.slots = reinterpret_cast<int*>(work + wp.pre_slots);
     e->pre.logits = reinterpret_cast<float*>(work + wp.pre_logits);
     e->pre.mfma = rows_on_mfma(c, T);
