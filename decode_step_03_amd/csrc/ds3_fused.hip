@@ -58,6 +58,9 @@ struct Shape {
   static constexpr int QW = NQ * HD;                 // q width, the o-projection's input
   static constexpr int S = kFusedBlocks / NKV;       // attention splits per kv head: one (kv head, split) per block
   static constexpr int KB = TC * HD * 2;             // bytes of one staged K chunk (and of its V^T chunk)
+  // the stage area: the K and V^T chunks, and between the sweep and the next staging two gate/up batches of every
+  // wave (8 rows x 1 KB each): at least 128 KB
+  static constexpr int SB = 2 * KB > 128 * 1024 ? 2 * KB : 128 * 1024;
   static constexpr int WST = kFW * G * (HD + 2);     // attention wave states
   static constexpr int UNI = WST > kFW * 520 ? WST : kFW * 520;
   static constexpr int QU = (G + 2) * HD / 2;        // QKV units (rotary / v row pairs) of one kv-head group
@@ -88,11 +91,18 @@ struct Geo {
   static constexpr int RBP = RB <= 1 ? 1 : RB <= 2 ? 2 : RB <= 4 ? 4 : RB <= 8 ? 8 : 16;
   static constexpr int LOG = RBP == 1 ? 0 : RBP == 2 ? 1 : RBP == 4 ? 2 : RBP == 8 ? 3 : 4;
   // gate/up: batches 2 .. 2 + NLB - 1 of every wave travel through the LDS stage area (free between the attention
-  // sweep and the next layer's K/V staging), loaded while the attention and o-projection phases wait on their
-  // barriers, when HBM would otherwise idle. 1 KB slots; wave w's in slots w, w + 8, w + 16, ...
-  static constexpr int SLOTS_PER_WAVE = 2 * SH::KB / 1024 / kFW;
-  static constexpr int NLB = (PH == PH_GU && CW == 1) ? (SLOTS_PER_WAVE / RB < 2 ? SLOTS_PER_WAVE / RB : 2) : 0;
-  static_assert(NLB == 0 || NBT >= 2 + NLB + 1, "LDS batches leave streamed batches");
+  // sweep and the next layer's K/V staging; at least 128 KB, so two batches fit at both shapes), loaded while the
+  // attention and o-projection phases wait on their barriers, when HBM would otherwise idle (1B shape: 599 -> 586 us
+  // per step on MI355X). 1 KB slots; wave w's in slots w, w + 8, w + 16, ...
+  static constexpr int SLOTS_PER_WAVE = SH::SB / 1024 / kFW;
+  // (the loop then runs 1 + ceil((NBT - 2 - NLB) / 2) iterations, and the next layer's K/V staging takes one per
+  // two of its NIW instructions per wave: fewer LDS batches where that would not fit)
+  static constexpr int NIW = SH::KB / 1024 / kFW;
+  static constexpr int NLB0 = (PH == PH_GU && CW == 1) ? (SLOTS_PER_WAVE / RB < 2 ? SLOTS_PER_WAVE / RB : 2) : 0;
+  static constexpr int fit(int n) { return n <= 0 ? 0 : (1 + (NBT - 1 - n) / 2 >= NIW / 2 ? n : fit(n - 1)); }
+  static constexpr int NLB = fit(NLB0);
+  static_assert(NLB == 0 || (NBT >= 2 + NLB && 1 + (NBT - 1 - NLB) / 2 >= NIW / 2),
+                "the batches after the LDS ones leave a loop iteration for every K/V staging step");
   static_assert(C * 512 == K && KS * CW == C, "input width must be whole 512-element chunks");
   static_assert(NL >= 1 && NL <= kNL && RB <= 16, "a batch is at most kNL loads per lane");
   static_assert(PH == PH_HEAD || UNITS % kFusedBlocks == 0, "units split evenly over the blocks");
@@ -1046,7 +1056,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedParams p_in) {
     p.trace = nullptr;
     p.trace2 = nullptr;
   }
-  __shared__ __attribute__((aligned(16))) unsigned char s_stage[2 * SH::KB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_stage[SH::SB];
   __shared__ __attribute__((aligned(16))) float s_uni[SH::UNI];
   __shared__ float s_ssq[kFW];
   __shared__ int s_flags[3];
