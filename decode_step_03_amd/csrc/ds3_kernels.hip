@@ -411,14 +411,14 @@ __global__ void __launch_bounds__(kBlock) gemv_kernel(GemvParams p) {
 constexpr int kSkTileBytes = 16 * kSkChunk * 2;  // one 16-row weight tile of one chunk: 4 KB
 constexpr int kSkActTileBytes = kSkChunk / 32 * 2 * 1024;   // a chunk's fragments of one activation tile, hi and lo: 8 KB
 constexpr int kSkNt = 2;                         // cache policy of the weight loads: streamed once
-// chunk buffers: three (two load while one is consumed) with one activation tile; two with four, whose fragments
-// take four times the LDS (weights 64 KB + activations 64 KB)
+// chunk buffers: three of weights (two load while one is consumed); three of activation fragments with one
+// activation tile, two with four, whose fragments take four times the LDS (weights 96 KB + activations 24 / 64 KB)
+constexpr int kSkBufsW = 3;
 template <int NT>
-constexpr int kSkBufs = NT == 1 ? 3 : 2;
+constexpr int kSkBufsA = NT == 1 ? 3 : 2;
+constexpr size_t kSkRingBytes = (size_t)kSkWaves * kSkBufsW * 2 * kSkTileBytes;   // weights: 96 KB
 template <int NT>
-constexpr size_t kSkRingBytes = (size_t)kSkWaves * kSkBufs<NT> * 2 * kSkTileBytes;   // weights: 96 / 64 KB
-template <int NT>
-constexpr size_t kSkLds = kSkRingBytes<NT> + (size_t)kSkBufs<NT> * NT * kSkActTileBytes;   // + 24 / 64 KB
+constexpr size_t kSkLds = kSkRingBytes + (size_t)kSkBufsA<NT> * NT * kSkActTileBytes;
 
 // sum of the partial products of weight rows n .. n + 3 (n % 4 == 0) for activation row r, in block order; the
 // loads of up to eight contributors are issued before their adds
@@ -455,8 +455,9 @@ __device__ __forceinline__ float sk_row_scale(const float* ss, int nblk, int r, 
 template <bool HEAD, int NT>
 __global__ void __launch_bounds__(64 * kSkWaves) sk_gemm_kernel(SkGemmParams p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char sk_lds[];
-  constexpr int B = kSkBufs<NT>;
-  constexpr int OPC = 8 + 2 * NT;   // vector-memory operations per chunk and wave: 8 weight (2 tiles x 4), 2 NT activation
+  constexpr int B = kSkBufsW;
+  constexpr int OPW = 8;                // vector-memory operations per chunk and wave: 8 weight (2 tiles x 4) ...
+  constexpr int OPC = OPW + 2 * NT;     // ... and 2 NT activation
   constexpr int ACT = NT * kSkActTileBytes;   // a chunk's activation fragments
   const int lane = threadIdx.x & 63, r16 = lane & 15, hq = lane >> 4;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -473,13 +474,13 @@ __global__ void __launch_bounds__(64 * kSkWaves) sk_gemm_kernel(SkGemmParams p) 
   if (i0 >= i1) return;   // (block-uniform)
   unsigned char* mine = sk_lds + (size_t)wid * B * 2 * kSkTileBytes;
   // activations: [buffer][hi k-steps 0..3 x tiles, lo k-steps 0..3 x tiles][64 lanes][16 B]
-  unsigned char* act = sk_lds + kSkRingBytes<NT>;
+  unsigned char* act = sk_lds + kSkRingBytes;
   const int K = p.K, nck = pl.nck;
 
   // chunk i into buffer bf: the wave's own two weight tiles (tile t's row r lands at byte 256 r, its 16-byte piece
   // c at position c ^ r; instruction j covers rows 4j .. 4j + 3) and its share of the activation fragments
   // (1 KB pieces m = part x 4 NT + k-step x NT + tile, wave w taking pieces 2 NT w .. 2 NT w + 2 NT - 1)
-  auto issue = [&](int i, int bf) {
+  auto issue_w = [&](int i, int bf) {
     const int q = i / nck, ck = i - q * nck;
     const int g = kSkQuad * q + wid;
 #pragma unroll
@@ -492,12 +493,19 @@ __global__ void __launch_bounds__(64 * kSkWaves) sk_gemm_kernel(SkGemmParams p) 
                                          (lds_ptr)(mine + (bf * 2 + t) * kSkTileBytes + 1024 * j), 16, 0, kSkNt);
       }
     }
+  };
+  auto issue_a = [&](int i, int bf) {
+    const int ck = i % nck;
 #pragma unroll
     for (int m = 2 * NT * wid; m < 2 * NT * wid + 2 * NT; ++m) {
       const int part = m / (4 * NT), st = (m / NT) % 4, ct = m % NT;
       const uint16_t* src = (part == 0 ? p.hi : p.lo) + (((size_t)(ck * 4 + st) * NT + ct) * 64 + lane) * 8;
       __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(act + bf * ACT + 1024 * m), 16, 0, 0);
     }
+  };
+  auto issue = [&](int i, int bf) {
+    issue_w(i, bf);
+    issue_a(i, bf);
   };
 
   f32x4 acc0[NT], acc1[NT];
@@ -540,43 +548,69 @@ __global__ void __launch_bounds__(64 * kSkWaves) sk_gemm_kernel(SkGemmParams p) 
     }
   };
 
+  // chunk i's products from weight buffer qw and activation buffer qa
+  auto compute = [&](int i, int qw, int qa) {
+    const int qd = i / nck;
+    if (qd != cur) {
+      flush(cur);
+      cur = qd;
+    }
+    const unsigned char* t0 = mine + (qw * 2) * kSkTileBytes + r16 * 256;
+    const unsigned char* av = act + qa * ACT + lane * 16;
 #pragma unroll
-  for (int q = 0; q < B - 1; ++q)
-    if (i0 + q < i1) issue(i0 + q, q);
-  for (int base = i0; base < i1; base += B) {
+    for (int st = 0; st < 4; ++st) {
+      const int at = 16 * ((4 * st + hq) ^ r16);
+      const bf16x8 A0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(t0 + at));
+      const bf16x8 A1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(t0 + kSkTileBytes + at));
 #pragma unroll
-    for (int q = 0; q < B; ++q) {
-      const int i = base + q;
-      if (i < i1) {
-        // chunk i (buffer q) has landed once only the chunks after it are outstanding (loads complete in order; a
-        // store issued in between only makes the wait stricter); the barrier makes every wave's share of the
-        // activations visible and frees the buffer read in the previous step, which then takes chunk i + B - 1
-        if (B > 2 && i + 1 < i1) __builtin_amdgcn_s_waitcnt(kVmcntChunk<OPC>());
-        else __builtin_amdgcn_s_waitcnt(kVmcntChunk<0>());
-        barrier_lds();
-        if (i + B - 1 < i1) issue(i + B - 1, (q + B - 1) % B);
-        const int qd = i / nck;
-        if (qd != cur) {
-          flush(cur);
-          cur = qd;
+      for (int c = 0; c < NT; ++c) {
+        const bf16x8 BH = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(av + 1024 * (st * NT + c)));
+        const bf16x8 BL =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(av + 1024 * (4 * NT + st * NT + c)));
+        acc0[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BH, acc0[c], 0, 0, 0);
+        acc0[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BL, acc0[c], 0, 0, 0);
+        acc1[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BH, acc1[c], 0, 0, 0);
+        acc1[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BL, acc1[c], 0, 0, 0);
+      }
+    }
+  };
+
+  if constexpr (kSkBufsA<NT> == B) {   // one ring: chunk i's weights and activations share buffer i mod 3
+#pragma unroll
+    for (int q = 0; q < B - 1; ++q)
+      if (i0 + q < i1) issue(i0 + q, q);
+    for (int base = i0; base < i1; base += B) {
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        const int i = base + q;
+        if (i < i1) {
+          // chunk i (buffer q) has landed once only the chunks after it are outstanding (loads complete in order;
+          // a store issued in between only makes the wait stricter); the barrier makes every wave's share of the
+          // activations visible and frees the buffer read in the previous step, which then takes chunk i + B - 1
+          if (i + 1 < i1) __builtin_amdgcn_s_waitcnt(kVmcntChunk<OPC>());
+          else __builtin_amdgcn_s_waitcnt(kVmcntChunk<0>());
+          barrier_lds();
+          if (i + B - 1 < i1) issue(i + B - 1, (q + B - 1) % B);
+          compute(i, q, q);
         }
-        const unsigned char* t0 = mine + (q * 2) * kSkTileBytes + r16 * 256;
-        const unsigned char* av = act + q * ACT + lane * 16;
+      }
+    }
+  } else {   // weights three deep, activations two: the issue order W(i0), A(i0), W(i0 + 1), then per chunk i
+             // A(i + 1), W(i + 2), so chunk i has landed once only W(i + 1) is outstanding
+    issue_w(i0, 0);
+    issue_a(i0, 0);
+    if (i0 + 1 < i1) issue_w(i0 + 1, 1);
+    for (int base = i0; base < i1; base += 6) {   // (buffers i mod 3 and i mod 2 repeat every 6 chunks)
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int at = 16 * ((4 * st + hq) ^ r16);
-          const bf16x8 A0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(t0 + at));
-          const bf16x8 A1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(t0 + kSkTileBytes + at));
-#pragma unroll
-          for (int c = 0; c < NT; ++c) {
-            const bf16x8 BH = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(av + 1024 * (st * NT + c)));
-            const bf16x8 BL =
-                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(av + 1024 * (4 * NT + st * NT + c)));
-            acc0[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BH, acc0[c], 0, 0, 0);
-            acc0[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, BL, acc0[c], 0, 0, 0);
-            acc1[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BH, acc1[c], 0, 0, 0);
-            acc1[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, BL, acc1[c], 0, 0, 0);
-          }
+      for (int q = 0; q < 6; ++q) {
+        const int i = base + q;
+        if (i < i1) {
+          if (i + 1 < i1) __builtin_amdgcn_s_waitcnt(kVmcntChunk<OPW>());
+          else __builtin_amdgcn_s_waitcnt(kVmcntChunk<0>());
+          barrier_lds();
+          if (i + 1 < i1) issue_a(i + 1, (q + 1) % 2);
+          if (i + 2 < i1) issue_w(i + 2, (q + 2) % 3);
+          compute(i, q % 3, q % 2);
         }
       }
     }
@@ -2333,7 +2367,7 @@ hipError_t launch_sk_gemm(const SkGemmParams& p, bool head, hipStream_t s) {
   if (!head && !p.part) return hipErrorInvalidValue;
   auto* f = p.nt == 1 ? (head ? sk_gemm_kernel<true, 1> : sk_gemm_kernel<false, 1>)
                       : (head ? sk_gemm_kernel<true, 4> : sk_gemm_kernel<false, 4>);
-  const size_t lds = p.nt == 1 ? kSkLds<1> : kSkLds<4>;
+  const size_t lds = p.nt == 1 ? kSkLds<1> : kSkLds<4>;   // 120 KB, 160 KB
   hipError_t e = set_lds(f, lds);
   if (e != hipSuccess) return e;
   f<<<pl.nb, 64 * kSkWaves, lds, s>>>(p);
