@@ -633,6 +633,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       p.lp_ids = e->lp_ids;
       p.max_chain = kMaxChain;
       p.status = e->status;
+      p.done = e->pick_done;   // (the pick and the sampler never run in the same step; both leave it at zero)
       return launch_sample(p, e->stream);
     }
     case K_PICK: {

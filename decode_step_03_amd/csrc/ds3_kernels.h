@@ -170,6 +170,7 @@ struct SampleParams {
   int32_t* lp_ids;          // [max_chain][rows][kMaxLogprobs]
   int max_chain;
   StatusWords* status;
+  uint32_t* done;           // [1] the row blocks' ticket: the last one closes the step (zero between launches)
 };
 
 struct EmbedParams {

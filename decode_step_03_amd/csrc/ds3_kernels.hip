@@ -1429,6 +1429,7 @@ struct SampleShared {
   float fv[kSampleWaves];
   int fi[kSampleWaves];
   unsigned long long bcast[2];
+  float lse;
 };
 
 // 64-bit lane exchanges as two 32-bit ones
@@ -1644,11 +1645,57 @@ __device__ __forceinline__ float adjust_logit(float x, int c, float bias_v, cons
   return x;
 }
 
+// The selection over a top-k list of n <= 64 entries (index order) in one wave, lane i on entry i: top-p keeps an
+// entry while the weight of the entries ranked before it (key descending, index ascending) stays below p of the
+// list's total, which is the shortest ranked prefix reaching it; min-p then drops the entries below min_p of the top
+// token's weight; the draw takes the first kept entry in index order whose running weight reaches u times the kept
+// total, plus one. The weights are integers, so every sum is exact in any order and the result is the one the
+// block-wide passes find. Returns the drawn entry, or -1 if no weight is kept.
+template <class KEY, class WT>
+__device__ __forceinline__ int wave_select(const float* lx, int n, KEY&& key, WT&& wt, float top_p, float inv_t,
+                                           float smax, float lmin, double u) {
+  const int i = threadIdx.x & 63;
+  const bool live = i < n;
+  const float x = live ? lx[i] : -INFINITY;
+  const uint32_t k = live ? key(x) : 0u;
+  const unsigned long long w = live ? wt(x) : 0ull;
+  bool kept = live;
+  if (top_p < 1.f) {
+    const unsigned long long tw = wave_sum_u64(w);
+    unsigned long long target = (unsigned long long)((double)top_p * (double)tw);
+    if (target < 1) target = 1;
+    unsigned long long before = 0;
+    for (int j = 0; j < n; ++j) {
+      // (the builtin returns a signed int: each half goes through unsigned before it is widened)
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane(k, j);
+      const unsigned long long wj =
+          ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((unsigned)(w >> 32), j) << 32) |
+          (unsigned long long)(uint32_t)__builtin_amdgcn_readlane((unsigned)w, j);
+      if (kj > k || (kj == k && j < i)) before += wj;
+    }
+    kept = kept && before < target;
+  }
+  kept = kept && x * inv_t - smax >= lmin;
+  const unsigned long long kw = kept ? w : 0ull;
+  const unsigned long long tw = wave_sum_u64(kw);
+  if (tw == 0) return -1;
+  unsigned long long target = (unsigned long long)(u * (double)tw) + 1ull;
+  if (target > tw) target = tw;
+  const unsigned long long hit = __ballot(wave_scan_u64(kw) >= target);
+  return hit ? (int)__builtin_ctzll(hit) : n - 1;
+}
+
 // Whether a row's draw takes the candidate path: a temperature draw whose top-k (below the vocabulary) is at most
 // kSampFastK, with at most kSampCand candidates over at most kSampLpSeg segments.
 __host__ __device__ __forceinline__ bool samp_fast(const SampleRow& prm, int V) {
   return prm.temperature > 0.f && prm.top_k >= 1 && prm.top_k <= kSampFastK && prm.top_k < V &&
          samp_segments(V) * prm.top_k <= kSampCand && samp_segments(V) <= kSampLpSeg;
+}
+
+// Whether the log-probabilities' top n come from the candidate path's top-k list: the n best by rank all lie in
+// the row's top-k set when n <= k, so the segments need not keep top-n lists of their own.
+__host__ __device__ __forceinline__ bool samp_lp_listed(const SampleRow& prm, int V, int nl) {
+  return samp_fast(prm, V) && nl <= prm.top_k;
 }
 
 constexpr int kPartThreads = 256;
@@ -1822,8 +1869,9 @@ __global__ void __launch_bounds__(kPartThreads) sample_part_kernel(SampleParams 
       out.m = m;
       out.l = l;
     }
-    // the top nl by rank: each wave's own (its lanes' PT tokens each), then wave 0 over the waves' lists
-    {
+    // the top nl by rank: each wave's own (its lanes' PT tokens each), then wave 0 over the waves' lists (unless
+    // the per-row kernel takes them from its top-k list)
+    if (!samp_lp_listed(prm, V, nl)) {
       float x[PT];
       int v[PT];
 #pragma unroll
@@ -1936,6 +1984,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
   int token = bi < V ? bi : 0;
   const float T = prm.temperature;
   const float inv_t = T > 0.f ? 1.f / T : 1.f;
+  int n_list = 0;   // the top-k list's length (sh.lv, sh.lx), when one is gathered
 
   if (T > 0.f && zmax > -INFINITY) {
     auto key = [&](float x) __attribute__((always_inline)) { return order_key(x * inv_t); };
@@ -2013,6 +2062,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
       });
       __syncthreads();
       n = min(sh.nlist, kSampleList);
+      n_list = n;
       for (int i = tid; i < n; i += kSampleThreads) {   // index order: a token's rank among the gathered ones
         const int v = sh.gv[i];
         int rank = 0;
@@ -2064,7 +2114,14 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
       if (target > tw) target = tw;
       return tw > 0 ? index_scan(sh, zs, Vs, kept, wt, target, true) : -1;
     };
-    if (listed) {
+    if (listed && n <= 64) {   // (the bench's top-k of 40, say: no block-wide passes)
+      if (tid < 64) {
+        const int i = wave_select(sh.lx, n, key, wt, prm.top_p, inv_t, smax, lmin, u);
+        if (tid == 0) sh.nlist = i;
+      }
+      __syncthreads();
+      if (sh.nlist >= 0) token = sh.lv[sh.nlist];
+    } else if (listed) {
       const float* lx = sh.lx;
       const int i = select(lx, n, [](int, float) __attribute__((always_inline)) { return true; });
       if (i >= 0) token = sh.lv[i];
@@ -2076,7 +2133,8 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
   }
 
   // ---- logprobs of the adjusted distribution (temperature 1 for greedy): the drawn token's and the top n by rank,
-  // from the segments' log-sum-exp partials (merged in segment order) and their top-n lists
+  // from the segments' log-sum-exp partials (merged in segment order) and, unless they come from the top-k list,
+  // the segments' top-n lists
   const SlotLayout sl{p.rows};
   const int step = p.slots[sl.chain()];
   const int slot = step % p.max_chain;
@@ -2084,6 +2142,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
   int32_t* lpi = p.lp_ids + ((size_t)slot * p.rows + r) * kMaxLogprobs;
   const int nl = min(max(prm.n_logprobs, 0), kMaxLogprobs);
   if (nl > 0) {
+    const bool from_list = samp_lp_listed(prm, V, nl);
     // the segment records, staged in LDS by all threads (read from global memory past kSampLpSeg segments)
     const bool staged = NB <= kSampLpSeg;
     if (staged) {
@@ -2091,10 +2150,12 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
         sh.seg_m[b] = pr[b].m;
         sh.seg_l[b] = pr[b].l;
       }
-      for (int i = tid; i < NB * kMaxLogprobs; i += kSampleThreads) {   // (stride kMaxLogprobs per segment)
-        const int b = i / kMaxLogprobs, q = i % kMaxLogprobs;
-        sh.seg_tv[i] = q < nl ? pr[b].top_v[q] : -INFINITY;
-        sh.seg_ti[i] = q < nl ? pr[b].top_i[q] : 0x7fffffff;
+      if (!from_list) {
+        for (int i = tid; i < NB * kMaxLogprobs; i += kSampleThreads) {   // (stride kMaxLogprobs per segment)
+          const int b = i / kMaxLogprobs, q = i % kMaxLogprobs;
+          sh.seg_tv[i] = q < nl ? pr[b].top_v[q] : -INFINITY;
+          sh.seg_ti[i] = q < nl ? pr[b].top_i[q] : 0x7fffffff;
+        }
       }
     }
     __syncthreads();
@@ -2110,10 +2171,30 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
         if (m > -INFINITY) L += (staged ? sh.seg_l[b] : pr[b].l) * __expf(m - M);
       }
       lse = M + __logf(wave_total(L));
+      if (tid == 0) sh.lse = lse;
     }
-    // the top n by rank over the segments' top-n lists, by wave 0: chunks of 64 EL entries, each merged with the
-    // running top n (lane j < n offers running entry j)
-    if (tid < 64) {
+    if (from_list) {
+      // the top n by rank (s descending, index ascending) are the list entries of rank < n: each entry's rank is
+      // the number of list entries ranked before it (the list is in index order). With no list (every adjusted
+      // logit -inf) the ranks fall to the lowest indices.
+      __syncthreads();
+      const float lb = sh.lse;
+      for (int i = tid; i < n_list; i += kSampleThreads) {
+        const float si = sh.lx[i] * inv_t;
+        int rank = 0;
+        for (int j = 0; j < n_list; ++j) rank += pick_better(sh.lx[j] * inv_t, j, si, i);
+        if (rank < nl) {
+          lpi[rank] = sh.lv[i];
+          lpo[1 + rank] = si - lb;
+        }
+      }
+      if (n_list == 0 && tid < nl) {
+        lpi[tid] = tid < V ? tid : -1;
+        lpo[1 + tid] = -INFINITY - lb;
+      }
+    } else if (tid < 64) {
+      // the top n by rank over the segments' top-n lists, by wave 0: chunks of 64 EL entries, each merged with the
+      // running top n (lane j < n offers running entry j)
       constexpr int EL = kSampLpSeg * kMaxLogprobs / 64;
       float tv[kMaxLogprobs];
       int ti[kMaxLogprobs];
@@ -2172,15 +2253,19 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleParams p) 
       p.slots[sl.write_map() + r] = p.page_table[(size_t)r * ppr + np / p.page_size] * p.page_size + np % p.page_size;
     }
   }
-}
 
-// after every row's sampler: the step's non-finite flag and the chain counter (one thread)
-__global__ void sample_close_kernel(SampleParams p) {
-  const SlotLayout sl{p.rows};
-  const int step = p.slots[sl.chain()];
-  p.flags[step % p.max_chain] = p.status->nonfinite ? 1u : 0u;
-  p.status->nonfinite = 0;
-  p.slots[sl.chain()] = step + 1;
+  // ---- the last row's block to finish closes the step: the non-finite flag and the chain counter (every thread
+  // of every block has read the counter before its block takes a ticket); the ticket word is back at zero after
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == (unsigned)p.rows - 1u) {
+      p.flags[step % p.max_chain] = p.status->nonfinite ? 1u : 0u;
+      p.status->nonfinite = 0;
+      p.slots[sl.chain()] = step + 1;
+      __hip_atomic_store(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------------------------------------
@@ -2420,14 +2505,11 @@ hipError_t launch_pick(const PickParams& p, hipStream_t s) {
 }
 
 hipError_t launch_sample(const SampleParams& p, hipStream_t s) {
-  if (p.rows < 1 || p.vocab < 1 || p.max_chain < 1 || !p.part) return hipErrorInvalidValue;
+  if (p.rows < 1 || p.vocab < 1 || p.max_chain < 1 || !p.part || !p.done) return hipErrorInvalidValue;
   sample_part_kernel<<<dim3(samp_segments(p.vocab), p.rows), kPartThreads, 0, s>>>(p);
   hipError_t h0 = hipGetLastError();
   if (h0 != hipSuccess) return h0;
   sample_kernel<<<p.rows, kSampleThreads, 0, s>>>(p);
-  hipError_t h = hipGetLastError();
-  if (h != hipSuccess) return h;
-  sample_close_kernel<<<1, 1, 0, s>>>(p);
   return hipGetLastError();
 }
 

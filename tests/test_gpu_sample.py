@@ -27,6 +27,8 @@ PARAMS = [   # one row each: (temperature, top_k, top_p, min_p, rep, presence, f
     (0.8, 1500, 0.7, 0.0, 1.0, 0.0, 0.0, 0),    # top-k above the gathered-set limit: the whole-vocabulary path
     (0.8, 40, 0.95, 0.02, 1.1, 0.0, 0.0, 5),    # the parameters bench.py times
     (1.0, 5000, 0.98, 0.0, 1.0, 0.1, 0.0, 1),   # a large top-k with top-p
+    (0.9, 100, 0.9, 0.0, 1.0, 0.0, 0.0, 6),     # a candidate-path top-k above one wave's lanes, logprobs from it
+    (1.0, 3, 1.0, 0.0, 1.0, 0.0, 0.1, 8),       # more logprobs than top-k: the segments' own top-n lists
 ]
 
 
@@ -64,7 +66,8 @@ def _set(eng, w, rng, shift=0):
 
 @pytest.mark.parametrize("name,shift", [("tiny-fp32", 1), ("tiny-fp32", 2), ("8b-fused", 0), ("8b-fused", 2),
                                         ("8b-fused", 3), ("8b-fused", 4), ("8b-fused", 5), ("8b-r8", 0),
-                                        ("8b-fullvocab", 6), ("8b-fullvocab", 7), ("8b-fullvocab", 5)])
+                                        ("8b-fullvocab", 6), ("8b-fullvocab", 7), ("8b-fullvocab", 5),
+                                        ("8b-fullvocab", 8), ("8b-fullvocab", 9)])
 def test_sampler_follows_oracle(name, shift):
     w = _workload(name)
     ws = weights(w.model)
