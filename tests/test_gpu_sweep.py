@@ -11,7 +11,7 @@ import pytest
 import bench
 import synth
 from decode_step_03_amd import DS3Error, _ds3 as C
-from tests.ds3_testlib import log, make_engine
+from tests.ds3_testlib import Lockstep, log, make_engine
 
 pytestmark = pytest.mark.gpu
 
@@ -68,3 +68,30 @@ def test_visible_sweep_is_bit_identical(name):
     finally:
         full.close()
         vis.close()
+
+
+@pytest.mark.parametrize("name", ["8b-fused", "8b-r8", "8b-r16-paged"])
+def test_visible_sweep_follows_oracle(name):
+    """The visible sweep against the oracle itself (not only against the GPU's full sweep): teacher-forced steps of
+    the fused, matrix-core contiguous and paged engines with the sweep set to VISIBLE, every logit within the
+    tolerance, greedy ids outside the margin, and this step's K/V in the cache."""
+    w = _workload(name)
+    ws = synth.make_weights(w.model)
+    eng = make_engine(w, ws)
+    try:
+        eng.set_kv_sweep("visible")
+        sp = np.minimum(synth.start_positions(w), 1500).astype(np.int32)
+        n = 3
+        ls = Lockstep(w, ws, eng, n_alloc=[int(p) + n for p in sp])
+        if w.kv_layout == "paged":
+            eng.set_slot_map(synth.page_table(w))
+        ls.prefill_random_kv([int(p) for p in sp])
+        t = synth.start_tokens(w)
+        for i in range(n):
+            _, ref, _ = ls.step(t, sp + i)
+            t = ref.argmax(axis=1).astype(np.int32)
+        for r in range(w.rows):
+            ls.check_kv(0, r, int(sp[r]), n)
+        log(name, "plan", eng.stats()["kernel_plan"], "visible-sweep max err", ls.max_err)
+    finally:
+        eng.close()
