@@ -54,7 +54,6 @@ template <int D_, int F_, int HD_, int NQ_, int NKV_, int TC_, bool MC_ = false>
 struct Shape {
   static constexpr int D = D_, F = F_, HD = HD_, NQ = NQ_, NKV = NKV_, G = NQ_ / NKV_, TC = TC_;
   static constexpr bool MC = MC_;
-  static constexpr bool ONE_HOP = D >= 4096;         // grid barrier form (arrive_and_wait)
   static constexpr int QW = NQ * HD;                 // q width, the o-projection's input
   static constexpr int S = kFusedBlocks / NKV;       // attention splits per kv head: one (kv head, split) per block
   static constexpr int KB = TC * HD * 2;             // bytes of one staged K chunk (and of its V^T chunk)
@@ -440,47 +439,33 @@ __device__ __forceinline__ bool spin_until(const FusedParams& p, int* flags, F&&
 // this wave's first batches of the next phase and wait for every block. (Wave 0 polls with vector loads, and a
 // wave can only wait for its oldest loads first, so its polls also wait for those batches.)
 //
-// ONE_HOP: every block polls all 256 arrival flags itself (four per lane), and a flag already at a later
-// generation (its block has passed this barrier and reached the next) counts as arrived. Otherwise block 0 alone
-// polls the arrival flags and then raises one release flag per XCD, which the other blocks poll: two hops, but
-// 8 x 32 pollers on single cache lines instead of 256 on the whole array. On MI355X the one-hop form measured
-// 1.1-1.9% faster per step at the 4096-wide shape and 1.4-3% slower at the 2048-wide one (whose phases are
-// short); the shape picks it. (Block 0 as the collector issues its batches only after the barrier.)
-template <bool ONE_HOP, class PF>
+// Every block polls all 256 arrival flags itself (four per lane, one hop), and a flag already at a later
+// generation (its block has passed this barrier and reached the next) counts as arrived. (A collector block that
+// polls the arrivals and raises one release flag per XCD -- two hops, 8 x 32 pollers on single cache lines --
+// measured 2.3% slower per step at the 2048-wide shape and 1.1-1.9% slower at the 4096-wide one.)
+template <class PF>
 __device__ __forceinline__ void arrive_and_wait(const FusedParams& p, unsigned gen0, int bar, int lane, int* flags,
                                                 PF&& prefetch) {
   wait_all();
   const long long t0 = wall_clock64();
   const unsigned gen = gen0 + (unsigned)bar + 1u;
-  const bool col = !ONE_HOP && blockIdx.x == 0;   // the collector
-  const bool early = !col && !flags[0];
   if (!flags[0]) {
     if (lane == 0) st_dev(&p.sync[kSyncArrive + blockIdx.x], gen);
     // (the weights go out first: the polls then wait for them too, but the release rarely comes sooner)
-    if (early) prefetch();
-    if constexpr (ONE_HOP) {
-      const auto rf = make_rsrc(p.sync + kSyncArrive);
-      spin_until(p, flags, [&]() __attribute__((always_inline)) {
-        const u32x4 v = ld_dev16(rf, lane * 16);
-        return __all((int)(v.x - gen) >= 0 && (int)(v.y - gen) >= 0 && (int)(v.z - gen) >= 0 &&
-                     (int)(v.w - gen) >= 0) != 0;
-      });
-    } else {
-      // the collector polls every block's arrival flag (four per lane), the others their XCD's release flag
-      const auto rf = make_rsrc(p.sync + (col ? kSyncArrive : kSyncRelease + 32 * (blockIdx.x & 7)));
-      const int off = col ? lane * 16 : 0;
-      const bool ok = spin_until(p, flags, [&]() __attribute__((always_inline)) {
-        const u32x4 v = ld_dev16(rf, off);
-        return __all(v.x == gen && (!col || (v.y == gen && v.z == gen && v.w == gen))) != 0;
-      });
-      if (col && ok && lane < 8) st_dev(&p.sync[kSyncRelease + 32 * lane], gen);
-    }
+    prefetch();
+    const auto rf = make_rsrc(p.sync + kSyncArrive);
+    spin_until(p, flags, [&]() __attribute__((always_inline)) {
+      const u32x4 v = ld_dev16(rf, lane * 16);
+      return __all((int)(v.x - gen) >= 0 && (int)(v.y - gen) >= 0 && (int)(v.z - gen) >= 0 &&
+                   (int)(v.w - gen) >= 0) != 0;
+    });
+  } else {
+    prefetch();
   }
   if (lane == 0 && p.trace) {   // this block's arrival and release times at barrier `bar`
     p.trace[((size_t)bar * kFusedBlocks + blockIdx.x) * 2] = (unsigned long long)t0;
     p.trace[((size_t)bar * kFusedBlocks + blockIdx.x) * 2 + 1] = (unsigned long long)wall_clock64();
   }
-  if (!early) prefetch();
 }
 
 // End of the QKV phase, wave 0 only (after its epilogue stores): wait for them and raise this block's arrival flag
@@ -767,7 +752,7 @@ __device__ __forceinline__ void run_gemv(const FusedParams& p, const GemvPhase<S
     if constexpr (PH == PH_QKV) {
       group_arrive(p, gen0, kFusedPhases * layer, lane, sm.flags);
     } else if constexpr (PH != PH_HEAD) {
-      arrive_and_wait<SH::ONE_HOP>(p, gen0, kFusedPhases * layer + (PH == PH_O ? 2 : PH == PH_GU ? 3 : 4), lane, sm.flags,
+      arrive_and_wait(p, gen0, kFusedPhases * layer + (PH == PH_O ? 2 : PH == PH_GU ? 3 : 4), lane, sm.flags,
                       [&]() __attribute__((always_inline)) {
                         nx.issue(0, A);
                         nx.issue(1, B);
@@ -1036,7 +1021,7 @@ __device__ __forceinline__ void run_attn(const FusedParams& p, const NX& nx, con
       st_dev(opaque_p(p.attn) + (g * G + hh) * HD + d0 + (lane >> (6 - LOGO)), o / Lt);
     if (st) st[5] = (unsigned long long)wall_clock64();
     if (lane == 0) __hip_atomic_store(&sm.flags[1], (int)gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    arrive_and_wait<SH::ONE_HOP>(p, gen0, kFusedPhases * layer + 1, lane, sm.flags, [&]() __attribute__((always_inline)) {
+    arrive_and_wait(p, gen0, kFusedPhases * layer + 1, lane, sm.flags, [&]() __attribute__((always_inline)) {
       nx.issue(0, A);
       nx.issue(1, B);
     });

@@ -322,10 +322,9 @@ struct FusedParams {
 constexpr long long kFusedSpinTicks = 200000000LL;   // default grid-barrier wait limit: 2 s of the 100 MHz clock
 
 // The fused kernel's sync region (32-bit words): [0] launch epoch, [1] abort flag, [kSyncArrive..+256) each
-// block's barrier arrival flag, [kSyncRelease + 32 x] the release flag seen by XCD x (one 128-byte line each),
-// [kSyncSplit + 32 g + s] split s of kv head g has written its attention partial. No flag is ever reset: each
-// holds the generation (epoch x (5 L + 1) + barrier + 1) it last signalled.
-constexpr int kSyncArrive = 256, kSyncRelease = 512, kSyncSplit = 1024;
+// block's barrier arrival flag, [kSyncSplit + 32 g + s] split s of kv head g has written its attention partial.
+// No flag is ever reset: each holds the generation (epoch x (5 L + 1) + barrier + 1) it last signalled.
+constexpr int kSyncArrive = 256, kSyncSplit = 1024;
 inline size_t fused_sync_words(int n_layers, int nkv) { (void)n_layers; return (size_t)kSyncSplit + 32 * (size_t)nkv; }
 
 // Host launchers (defined in ds3_kernels.hip). Each returns the launch error, if any.
