@@ -19,10 +19,9 @@
 //
 // Grid barrier i, with flags and no atomics (device-scope atomics on one address serialize at close to a
 // microsecond each on this GPU): wave 0 of every block finishes its epilogue stores, waits for them (vmcnt 0)
-// and stores the barrier's generation into its arrival flag; then either every block polls all 256 flags (one
-// 16-byte load per lane; the 4096-wide shape), or block 0 alone does and stores the generation into one release
-// flag per XCD, which the other blocks poll (the 2048-wide shape). The generation is epoch x (5 L + 1) + i + 1, with the epoch read at the start and advanced by block 0 at the end,
-// so flags never need clearing and a recorded graph replays without host work. A block that waits longer than the
+// and stores the barrier's generation into its arrival flag; then every block polls all 256 flags (one 16-byte
+// load per lane). The generation is epoch x (5 L + 1) + i + 1, with the epoch read at the start and advanced by
+// block 0 at the end, so flags never need clearing and a recorded graph replays without host work. A block that waits longer than the
 // limit (a slot word; 2 s by default) raises ERR_BARRIER and the abort flag; from then on no block waits, so
 // every wave exits (the step's results are then void).
 //
