@@ -8,7 +8,8 @@ default). Weights are seeded N(0, 0.02) draws rounded to bf16; nothing is traine
 
 One step = one HIP-graph replay of every kernel of the step (the slot buffers hold token and position). By default
 the greedy token is picked on the device and fed to the next step, and the host waits once per --chain steps
-(reading back the ids); `value` is decode tokens/s over the timed steps (rows x steps / wall time). Beside it,
+(reading back the ids; fewer when the timed steps would give under five waits, so the wall-time percentiles have
+samples); `value` is decode tokens/s over the timed steps (rows x steps / wall time). Beside it,
 `step.per_token_readback` times the same engine with one host wait per step, the logits copied back and the greedy
 token picked on the host (--chain 0 makes that the headline).
 
@@ -409,14 +410,16 @@ def main() -> int:
         total = args.warmup + args.steps
         log(f"steps limited to {args.steps} by the KV capacity")
     wall, gpu_us, submit_us = [], [], []
+    # steps per host wait: --chain, or fewer so that the timed steps give at least five wall-time samples
+    chain = min(args.chain, max(1, -(-args.steps // 5))) if args.chain > 0 else 0
     torch.cuda.synchronize()
-    if args.chain > 0:
+    if chain > 0:
         # chained greedy steps: the device picks each token; one host wait per `chain` steps
         def run(n_total, timed):
             nonlocal tok, pos
             done = 0
             while done < n_total:
-                n = min(args.chain, n_total - done)
+                n = min(chain, n_total - done)
                 ts = time.perf_counter()
                 ids, flags = eng.step_greedy(tok, pos, n)
                 tok, pos, done = ids[-1].copy(), pos + n, done + n
@@ -606,8 +609,8 @@ def main() -> int:
                  "wall_samples": len(wall), "per_token_readback": readback,
                  "kernel_plan": stats["kernel_plan"],
                  "kernels_per_step": stats["kernels_per_step"], "graph_replays_per_step": 1,
-                 "steps_per_host_wait": args.chain if args.chain > 0 else 1,
-                 "token_pick": "device (greedy, chained)" if args.chain > 0 else "host argmax of copied logits",
+                 "steps_per_host_wait": chain if chain > 0 else 1,
+                 "token_pick": "device (greedy, chained)" if chain > 0 else "host argmax of copied logits",
                  "host_submit_us_graph": round(float(np.median(submit_us)), 1),
                  "per_op_graph": per_op.get("graph", {}), "eager": per_op.get("eager", {}),
                  "attn_splits": stats["attn_splits"], "visible_sweep": visible, "sampled": sampled, "prompt_prefill": prefill.last},
