@@ -345,6 +345,12 @@ def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 5) -> int:
     return 0
 
 
+def steps_per_host_wait(chain: int, steps: int) -> int:
+    """Steps per host wait of the chained greedy run: `chain`, or fewer so that the timed steps give at least five
+    wall-time samples (0: no chaining, the host picks every token)."""
+    return min(chain, max(1, steps // 5)) if chain > 0 else 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -410,8 +416,7 @@ def main() -> int:
         total = args.warmup + args.steps
         log(f"steps limited to {args.steps} by the KV capacity")
     wall, gpu_us, submit_us = [], [], []
-    # steps per host wait: --chain, or fewer so that the timed steps give at least five wall-time samples
-    chain = min(args.chain, max(1, -(-args.steps // 5))) if args.chain > 0 else 0
+    chain = steps_per_host_wait(args.chain, args.steps)
     torch.cuda.synchronize()
     if chain > 0:
         # chained greedy steps: the device picks each token; one host wait per `chain` steps

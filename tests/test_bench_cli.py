@@ -1,5 +1,5 @@
 """bench.py's host-side contract, without a GPU: the one-GPU refusal, the algorithmic byte count of the headline
-workload, and the stale-profile rule for the reported HBM traffic."""
+workload, the stale-profile rule for the reported HBM traffic, and the steps per host wait of the chained run."""
 import os
 import subprocess
 import sys
@@ -33,3 +33,13 @@ def test_traffic_is_withheld_when_the_kernel_sources_changed(monkeypatch):
     real = bench.sources_sha256("decode_step_fused")
     monkeypatch.setattr(bench, "sources_sha256", lambda kind: "0" * 64 if kind == "decode_step_fused" else real)
     assert bench.pmc_traffic("decode_step_fused", "llama8b-bf16-cap8192") is None
+
+
+def test_chained_run_keeps_several_wall_samples():
+    assert bench.steps_per_host_wait(32, 504) == 32      # the default run: 16 waits
+    assert bench.steps_per_host_wait(32, 20) == 4        # a short run still gives five wall-time samples
+    assert bench.steps_per_host_wait(32, 3) == 1
+    assert bench.steps_per_host_wait(0, 504) == 0        # --chain 0: one host pick per step
+    for steps in range(1, 200):
+        c = bench.steps_per_host_wait(32, steps)
+        assert 1 <= c <= 32 and (-(-steps // c) >= 5 or c == 1)
