@@ -166,6 +166,10 @@ struct ds3_engine {
   std::vector<Launch> pre_sequence;
   hipGraph_t pre_graph = nullptr;
   hipGraphExec_t pre_exec = nullptr;
+  // the prefill step without its final norm and LM head, for every chunk but the last (their logits are not used)
+  size_t pre_body = 0;   // launches of pre_sequence before the final norm / head
+  hipGraph_t pre_body_graph = nullptr;
+  hipGraphExec_t pre_body_exec = nullptr;
   bool pre_captured = false;
   int32_t* h_pre = nullptr;   // pinned: the slot words of every chunk of one ds3_prefill call
 };
@@ -964,6 +968,7 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
     e->pre.mfma = rows_on_mfma(c, T);
     e->pre.row_map = e->pre.slots + SlotLayout{T}.words();
     per_op(e->pre_sequence, e->pre.mfma, false);
+    e->pre_body = e->pre_sequence.size() - (e->pre.mfma ? 2 : 1);   // (the final norm prep, then the head)
     h = hipHostMalloc(reinterpret_cast<void**>(&e->h_pre),
                       (size_t)(kMaxPrefill / T + 1) * (SlotLayout{T}.words() + T) * 4, hipHostMallocDefault);
     if (h != hipSuccess) return bail(DS3_E_DEVICE_LOST, std::string("hipHostMalloc: ") + hipGetErrorString(h));
@@ -1336,36 +1341,40 @@ ds3_status ds3_prefill(ds3_engine* e, int32_t row, const int32_t* tokens, int32_
   HIP_OR_POISON(e, hipMemcpyAsync(e->status, e->h_status, sizeof(StatusWords), hipMemcpyHostToDevice, e->stream));
   e->cur = e->pre;
   hipError_t h = hipSuccess;
-  if (c.exec_mode == DS3_GRAPH && !e->pre_captured) {
-    h = hipStreamBeginCapture(e->stream, hipStreamCaptureModeThreadLocal);
-    if (h == hipSuccess) {
-      hipError_t h1 = hipSuccess;
-      for (const Launch& l : e->pre_sequence)
-        if (h1 == hipSuccess) h1 = enqueue_kernel(e, l);
-      hipGraph_t g = nullptr;
-      h = hipStreamEndCapture(e->stream, &g);
-      if (h == hipSuccess) h = h1;
-      if (h == hipSuccess) {
-        e->pre_graph = g;
-        h = hipGraphInstantiate(&e->pre_exec, g, nullptr, nullptr, 0);
-        if (h == hipSuccess) {
-          e->pre_captured = true;
-          e->stats.captures++;
-        }
-      } else if (g) {
-        (void)hipGraphDestroy(g);
-      }
+  // two graphs: the whole prefill step (the last chunk) and the step without its final norm and head
+  auto capture = [&](size_t n_launch, hipGraph_t* graph, hipGraphExec_t* exec) {
+    hipError_t hc = hipStreamBeginCapture(e->stream, hipStreamCaptureModeThreadLocal);
+    if (hc != hipSuccess) return hc;
+    hipError_t h1 = hipSuccess;
+    for (size_t i = 0; i < n_launch; ++i)
+      if (h1 == hipSuccess) h1 = enqueue_kernel(e, e->pre_sequence[i]);
+    hipGraph_t g = nullptr;
+    hc = hipStreamEndCapture(e->stream, &g);
+    if (hc == hipSuccess) hc = h1;
+    if (hc != hipSuccess) {
+      if (g) (void)hipGraphDestroy(g);
+      return hc;
     }
+    *graph = g;
+    hc = hipGraphInstantiate(exec, g, nullptr, nullptr, 0);
+    if (hc == hipSuccess) e->stats.captures++;
+    return hc;
+  };
+  if (c.exec_mode == DS3_GRAPH && !e->pre_captured) {
+    h = capture(e->pre_sequence.size(), &e->pre_graph, &e->pre_exec);
+    if (h == hipSuccess) h = capture(e->pre_body, &e->pre_body_graph, &e->pre_body_exec);
+    if (h == hipSuccess) e->pre_captured = true;
   }
   if (h == hipSuccess) h = hipEventRecord(e->ev0, e->stream);
   for (int k = 0; k < chunks && h == hipSuccess; ++k) {
+    const bool last = k == chunks - 1;
     h = hipMemcpyAsync(e->pre.slots, e->h_pre + (size_t)k * words, (size_t)words * 4, hipMemcpyHostToDevice, e->stream);
     if (h != hipSuccess) break;
     if (c.exec_mode == DS3_GRAPH) {
-      h = hipGraphLaunch(e->pre_exec, e->stream);
+      h = hipGraphLaunch(last ? e->pre_exec : e->pre_body_exec, e->stream);
     } else {
-      for (const Launch& l : e->pre_sequence)
-        if (h == hipSuccess) h = enqueue_kernel(e, l);
+      const size_t n_launch = last ? e->pre_sequence.size() : e->pre_body;
+      for (size_t i = 0; i < n_launch && h == hipSuccess; ++i) h = enqueue_kernel(e, e->pre_sequence[i]);
     }
   }
   e->cur = e->dec;
@@ -1712,6 +1721,8 @@ void ds3_destroy(ds3_engine* e) {
   if (e->h_lp) (void)hipHostFree(e->h_lp);
   if (e->pre_exec) (void)hipGraphExecDestroy(e->pre_exec);
   if (e->pre_graph) (void)hipGraphDestroy(e->pre_graph);
+  if (e->pre_body_exec) (void)hipGraphExecDestroy(e->pre_body_exec);
+  if (e->pre_body_graph) (void)hipGraphDestroy(e->pre_body_graph);
   if (e->h_pre) (void)hipHostFree(e->h_pre);
   for (hipEvent_t ev : {e->ev0, e->ev1, e->ev_done})
     if (ev) (void)hipEventDestroy(ev);

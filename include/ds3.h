@@ -140,7 +140,7 @@ typedef struct {
 typedef struct {
   uint64_t steps;            /* successful ds3_step calls */
   uint64_t replays;          /* graph launches */
-  uint64_t captures;         /* graph captures (1 per engine in graph mode) */
+  uint64_t captures;         /* graph captures (graph mode: 1 for the step, 2 more at the first ds3_prefill) */
   int32_t kernels_per_step;  /* kernel launches (eager) or kernel nodes (graph) per step */
   int32_t state;             /* 0 ready, 1 not loaded, 2 needs reset, 3 poisoned */
   double last_host_us;       /* host time of the last ds3_step, slot write to logits ready */
@@ -271,7 +271,9 @@ ds3_status ds3_step_sample(ds3_engine* e, const int32_t* tokens, const int32_t* 
  * 16-row activation tiles per weight tile, so its weights stream once for up to 64 tokens. The rows after the
  * last token of the last chunk repeat that token at its position. logits_host (float32
  * [vocab], may be NULL) receives the last token's logits, from which the first decode step's token is picked;
- * flags (may be NULL) bit 0: some logit of the prefill was NaN or infinite. n in 1..DS3_MAX_PREFILL; pos0 + n must
+ * only the last chunk runs the final norm and the LM head (the other chunks' logits are never used, so their
+ * launch sequence, a graph of its own, stops after the last layer). flags (may be NULL) bit 0: some logit of the
+ * last chunk was NaN or infinite. n in 1..DS3_MAX_PREFILL; pos0 + n must
  * not pass cap; paged layout: the page table must be set. DS3_E_UNSUPPORTED when the engine was created with
  * prefill_rows = 0; other errors as ds3_step. */
 #define DS3_MAX_PREFILL 8192

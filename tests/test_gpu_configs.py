@@ -69,7 +69,7 @@ def test_llama1b_prompt_prefill_then_greedy_full_depth():
         assert st["kernel_plan"] == "fused" and st["prefill_tokens"] == n
         tok = np.array([int(np.argmax(ref[-1]))], np.int32)
         _decode(ls, eng, tok, np.array([n], np.int32), steps=8, visible_from=6)
-        assert eng.stats()["captures"] == 2   # the decode graph and the prefill graph
+        assert eng.stats()["captures"] == 3   # the decode graph and the prefill graphs (with and without the head)
     finally:
         eng.close()
         _release()
