@@ -923,14 +923,15 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
   }
   // the per-operation sequence of R rows (above 4 rows: the matrix-core GEMMs and the kernels that consume their
   // partial products)
-  auto per_op = [&](std::vector<Launch>& seq, bool mfma, bool pick) {
+  // (a plan of one attention split needs no combine: the attention writes the merged output itself)
+  auto per_op = [&](std::vector<Launch>& seq, bool mfma, bool combine, bool pick) {
     seq.push_back({K_EMBED, -1, 0});
     for (int l = 0; l < c.n_layers; ++l) {
       if (mfma) seq.push_back({K_SPLIT, l, S_ATTN_NORM});
       seq.push_back({K_QKV, l, 0});
       if (mfma) seq.push_back({K_QKVFIN, l, 0});
       seq.push_back({K_ATTN, l, 0});
-      seq.push_back({K_COMBINE, l, 0});
+      if (combine) seq.push_back({K_COMBINE, l, 0});
       seq.push_back({K_OPROJ, l, 0});
       if (mfma) seq.push_back({K_SPLIT, l, S_FFN_NORM});
       seq.push_back({K_GATEUP, l, 0});
@@ -942,7 +943,7 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
     if (pick) seq.push_back({K_PICK, -1, 0});
   };
   if (e->fused) e->sequence.push_back({K_FUSED, -1, 0});   // (the fused kernel picks in its own last phase)
-  else per_op(e->sequence, e->mfma, true);
+  else per_op(e->sequence, e->mfma, e->splits > 1, true);
   e->samp_sequence = e->sequence;   // the same step, the sampler as its pick
   if (e->fused) e->samp_sequence.push_back({K_SAMPLE, -1, 0});
   else e->samp_sequence.back() = {K_SAMPLE, -1, 0};
@@ -967,7 +968,7 @@ ds3_status ds3_create(const ds3_config* cfg, void* const* dev_ptrs, int32_t n, v
     e->pre.logits = reinterpret_cast<float*>(work + wp.pre_logits);
     e->pre.mfma = rows_on_mfma(c, T);
     e->pre.row_map = e->pre.slots + SlotLayout{T}.words();
-    per_op(e->pre_sequence, e->pre.mfma, false);
+    per_op(e->pre_sequence, e->pre.mfma, e->pre.splits > 1, false);
     e->pre_body = e->pre_sequence.size() - (e->pre.mfma ? 2 : 1);   // (the final norm prep, then the head)
     h = hipHostMalloc(reinterpret_cast<void**>(&e->h_pre),
                       (size_t)(kMaxPrefill / T + 1) * (SlotLayout{T}.words() + T) * 4, hipHostMallocDefault);

@@ -758,9 +758,40 @@ __global__ void __launch_bounds__(64) sk_swiglu_kernel(SkActParams p) {
 // The end of an attention block: `wst` holds each wave's state [4 waves][G][HD + 2] (weighted value sums, then the
 // running max and the weight sum, maxima in the log2 domain). The 4 waves are merged in wave order into this
 // split's partial, stored with plain coalesced stores at part[row][kv head][split][G][HD + 2]; the combine kernel
-// that follows merges the splits (the kernel boundary makes the partials visible to every XCD).
+// that follows merges the splits (the kernel boundary makes the partials visible to every XCD). A plan of one split
+// (a 64-token prefill chunk: one block per row and kv head) has nothing to merge: the block writes the normalized
+// output, and the o-projection's fragments, itself -- the values the combine would form from its one split
+// (weight 2^0 = 1 and the split's own sum).
 template <int G, int HD>
 __device__ __forceinline__ void attn_write_partial(const AttnParams& p, const float* wst, int r, int g, int s) {
+  if (p.splits == 1) {
+    for (int i = threadIdx.x; i < G * HD / 8; i += kBlock) {
+      const int hh = i / (HD / 8), d0 = i % (HD / 8) * 8;
+      float mm = wst[hh * (HD + 2) + HD];
+      float ll = wst[hh * (HD + 2) + HD + 1];
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = wst[hh * (HD + 2) + d0 + e];
+#pragma unroll
+      for (int w = 1; w < kBlock / 64; ++w) {
+        const float* ws2 = wst + (w * G + hh) * (HD + 2);
+        float M, w1, w2;
+        Lse::weights(mm, ws2[HD], M, w1, w2);
+        ll = ll * w1 + ws2[HD + 1] * w2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = v[e] * w1 + ws2[d0 + e] * w2;
+        mm = M;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = v[e] / ll;
+      const int h = g * G + hh;
+      float* o = p.out + ((size_t)r * p.nq + h) * HD + d0;
+      *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      if (p.frag_hi) store_frag8(p.frag_hi, p.frag_lo, p.nt, r, h * HD + d0, v);
+    }
+    return;
+  }
   float* part = p.part + (((size_t)r * p.nkv + g) * p.splits + s) * (size_t)(G * (HD + 2));
   for (int i = threadIdx.x; i < G * (HD + 2); i += kBlock) {
     const int hh = i / (HD + 2), dd = i % (HD + 2);
