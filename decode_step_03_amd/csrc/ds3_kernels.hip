@@ -651,12 +651,14 @@ __global__ void __launch_bounds__(64) sk_prep_kernel(SkPrepParams p) {
   store_frag8(p.hi, p.lo, p.nt, r, k0, v);
 }
 
-// grid = (ceil(N / 4 / kBlock), rows): a thread takes output rows n .. n + 3 (n = 4 x index) of activation row r;
-// the first rotary half of a q or k head also takes its partners n + hd/2 .. + 3.
+// grid = (ceil(N / 4 / 64), rows), one wave per block (the latency-bound sums then spread over every CU): a thread
+// takes output rows n .. n + 3 (n = 4 x index) of activation row r; the first rotary half of a q or k head also
+// takes its partners n + hd/2 .. + 3.
+constexpr int kQkvBlock = 64;
 template <typename KT>
-__global__ void __launch_bounds__(kBlock) sk_qkv_kernel(SkQkvParams p) {
+__global__ void __launch_bounds__(kQkvBlock) sk_qkv_kernel(SkQkvParams p) {
   const int r = blockIdx.y;
-  const int n = 4 * (blockIdx.x * kBlock + threadIdx.x);
+  const int n = 4 * (blockIdx.x * kQkvBlock + threadIdx.x);
   const int hd = p.hd, half = hd / 2;
   if (n >= (p.nq + 2 * p.nkv) * hd) return;
   const int hh = n / hd, idx = n % hd;
@@ -2504,9 +2506,9 @@ hipError_t launch_sk_prep(const SkPrepParams& p, hipStream_t s) {
 hipError_t launch_sk_qkv(const SkQkvParams& p, int kv_dtype, hipStream_t s) {
   const int n4 = (p.nq + 2 * p.nkv) * p.hd / 4;
   if (p.hd % 8 || p.rows < 1 || p.nt != sk_tiles(p.rows) || p.rows > kMfmaRows * p.nt) return hipErrorInvalidValue;
-  const dim3 grid((n4 + kBlock - 1) / kBlock, p.rows);
-  if (kv_dtype == 1) sk_qkv_kernel<uint16_t><<<grid, kBlock, 0, s>>>(p);
-  else sk_qkv_kernel<float><<<grid, kBlock, 0, s>>>(p);
+  const dim3 grid((n4 + kQkvBlock - 1) / kQkvBlock, p.rows);
+  if (kv_dtype == 1) sk_qkv_kernel<uint16_t><<<grid, kQkvBlock, 0, s>>>(p);
+  else sk_qkv_kernel<float><<<grid, kQkvBlock, 0, s>>>(p);
   return hipGetLastError();
 }
 
