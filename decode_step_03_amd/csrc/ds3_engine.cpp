@@ -373,7 +373,7 @@ WorkPlan plan_work(const ds3_config& c, int splits) {
       skp = std::max(skp, sk_partial_floats(sp, nt_max) * 4);
   }
   w.skpart = take(skp);
-  w.skss = take((size_t)((c.d_model + kPrepSpan - 1) / kPrepSpan) * kSsRows * 4);
+  w.skss = take((size_t)((c.d_model + kNormSpan - 1) / kNormSpan) * kSsRows * 4);
   w.total = off;
   return w;
 }
@@ -485,7 +485,7 @@ hipError_t run_projection(ds3_engine* e, const GemvParams& p, int mode, int kind
   g.nt = sk_tiles(p.rows);
   g.n_out = 2 * p.n_pairs;
   g.ss = e->skss;
-  g.ss_blocks = (c.d_model + kPrepSpan - 1) / kPrepSpan;
+  g.ss_blocks = (c.d_model + kNormSpan - 1) / kNormSpan;
   g.norm_dim = c.d_model;
   g.eps = c.rms_eps;
   g.status = e->status;
@@ -585,7 +585,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       qp.part = e->skpart;
       qp.plan = plan_of(c, K_QKV);
       qp.ss = e->skss;
-      qp.ss_blocks = (c.d_model + kPrepSpan - 1) / kPrepSpan;
+      qp.ss_blocks = (c.d_model + kNormSpan - 1) / kNormSpan;
       qp.D = c.d_model;
       qp.eps = c.rms_eps;
       qp.q = e->q;
@@ -606,7 +606,7 @@ hipError_t enqueue_kernel(ds3_engine* e, const Launch& l) {
       ap.part = e->skpart;
       ap.plan = plan_of(c, K_GATEUP);
       ap.ss = e->skss;
-      ap.ss_blocks = (c.d_model + kPrepSpan - 1) / kPrepSpan;
+      ap.ss_blocks = (c.d_model + kNormSpan - 1) / kNormSpan;
       ap.D = c.d_model;
       ap.eps = c.rms_eps;
       ap.F = c.ffn_dim;

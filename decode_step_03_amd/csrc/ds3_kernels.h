@@ -208,7 +208,8 @@ constexpr int kSkQuad = 4;         // groups per quad = waves per block
 constexpr int kSkChunk = 128;      // inputs per chunk
 constexpr int kSkWaves = kSkQuad;  // waves per block (one block per CU: its LDS takes 120 KB)
 constexpr int kSkMaxBlocks = 256;
-constexpr int kPrepSpan = 512;     // consumer kernels: inputs per block (one wave, 8 per lane)
+constexpr int kPrepSpan = 512;     // SwiGLU consumer: outputs per block (one wave, 8 per lane)
+constexpr int kNormSpan = 256;     // norm prep: inputs per block (one wave, 4 per lane), one sum of squares each
 struct SkPlan {
   int groups;   // N / kSkRows
   int nck;      // K / kSkChunk
@@ -251,7 +252,7 @@ struct SkPrepParams {
   const float* gain;     // [D]
   uint16_t* hi;
   uint16_t* lo;
-  float* ss;             // [ceil(D / kPrepSpan)][kSsRows]
+  float* ss;             // [ceil(D / kNormSpan)][kSsRows]
   int D, rows, nt;       // (nt: activation tiles of the partials and the fragments)
 };
 

@@ -48,6 +48,15 @@ __device__ __forceinline__ void store_frag8(uint16_t* hi, uint16_t* lo, int nt, 
   *reinterpret_cast<bf16x8*>(hi + idx) = h;
   *reinterpret_cast<bf16x8*>(lo + idx) = l;
 }
+// the same for 4 inputs k0 .. k0 + 3 (k0 % 4 == 0): one half of the 16-byte fragment word of k0 & ~7, split alike
+__device__ __forceinline__ void store_frag4(uint16_t* hi, uint16_t* lo, int nt, int r, int k0, const float (&v)[4]) {
+  const uint32_t h0 = cvt_pk_bf16(v[0], v[1]), h1 = cvt_pk_bf16(v[2], v[3]);
+  const uint32_t l0 = cvt_pk_bf16(v[0] - __uint_as_float(h0 << 16), v[1] - __uint_as_float(h0 & 0xffff0000u));
+  const uint32_t l1 = cvt_pk_bf16(v[2] - __uint_as_float(h1 << 16), v[3] - __uint_as_float(h1 & 0xffff0000u));
+  const size_t idx = (((size_t)(k0 >> 5) * nt + (r >> 4)) * 64 + ((k0 >> 3) & 3) * 16 + (r & 15)) * 8 + (k0 & 4);
+  *reinterpret_cast<uint2*>(hi + idx) = make_uint2(h0, h1);
+  *reinterpret_cast<uint2*>(lo + idx) = make_uint2(l0, l1);
+}
 
 
 // ----------------------------------------------------------------------------------------------------------
@@ -618,37 +627,33 @@ __global__ void __launch_bounds__(64 * kSkWaves) sk_gemm_kernel(SkGemmParams p) 
   flush(cur);
 }
 
-// grid = (ceil(D / kPrepSpan), 16 nt rows), one wave per block, 8 inputs per lane.
+// grid = (ceil(D / kNormSpan), 16 nt rows), one wave per block, 4 inputs per lane (twice the waves of 8 per lane:
+// the partial sums are latency-bound, so more of them in flight at once).
 __global__ void __launch_bounds__(64) sk_prep_kernel(SkPrepParams p) {
   const int r = blockIdx.y, lane = threadIdx.x;
-  const int k0 = blockIdx.x * kPrepSpan + 8 * lane;
+  const int k0 = blockIdx.x * kNormSpan + 4 * lane;
   const bool in = k0 < p.D, live = in && r < p.rows;
-  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
   if (live) {
     float* x = p.x + (size_t)r * p.D + k0;
     float4 a = *reinterpret_cast<const float4*>(x);
-    float4 b = *reinterpret_cast<const float4*>(x + 4);
     if (p.part) {
-      const f32x4 pa = sk_sum4(p.part, p.plan, p.nt, k0, r), pb = sk_sum4(p.part, p.plan, p.nt, k0 + 4, r);
+      const f32x4 pa = sk_sum4(p.part, p.plan, p.nt, k0, r);
       a.x += pa[0]; a.y += pa[1]; a.z += pa[2]; a.w += pa[3];
-      b.x += pb[0]; b.y += pb[1]; b.z += pb[2]; b.w += pb[3];
       *reinterpret_cast<float4*>(x) = a;
-      *reinterpret_cast<float4*>(x + 4) = b;
     }
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   }
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) ss += v[e] * v[e] + v[e + 1] * v[e + 1];
+  float ss = v[0] * v[0] + v[1] * v[1];
+  ss += v[2] * v[2] + v[3] * v[3];
   ss = wave_total(ss);
   if (lane == 0) p.ss[blockIdx.x * kSsRows + r] = ss;
   if (!in) return;
   if (live) {
     const float4 ga = *reinterpret_cast<const float4*>(p.gain + k0);
-    const float4 gb = *reinterpret_cast<const float4*>(p.gain + k0 + 4);
-    v[0] *= ga.x; v[1] *= ga.y; v[2] *= ga.z; v[3] *= ga.w; v[4] *= gb.x; v[5] *= gb.y; v[6] *= gb.z; v[7] *= gb.w;
+    v[0] *= ga.x; v[1] *= ga.y; v[2] *= ga.z; v[3] *= ga.w;
   }
-  store_frag8(p.hi, p.lo, p.nt, r, k0, v);
+  store_frag4(p.hi, p.lo, p.nt, r, k0, v);
 }
 
 // grid = (ceil(N / 4 / 64), rows), one wave per block (the latency-bound sums then spread over every CU): a thread
@@ -2498,7 +2503,7 @@ hipError_t launch_sk_gemm(const SkGemmParams& p, bool head, hipStream_t s) {
 
 hipError_t launch_sk_prep(const SkPrepParams& p, hipStream_t s) {
   if (p.D % 8 || p.rows < 1 || p.nt != sk_tiles(p.rows) || p.rows > kMfmaRows * p.nt) return hipErrorInvalidValue;
-  const dim3 grid((p.D + kPrepSpan - 1) / kPrepSpan, kMfmaRows * p.nt);
+  const dim3 grid((p.D + kNormSpan - 1) / kNormSpan, kMfmaRows * p.nt);
   sk_prep_kernel<<<grid, 64, 0, s>>>(p);
   return hipGetLastError();
 }
