@@ -208,7 +208,7 @@ constexpr int kSkQuad = 4;         // groups per quad = waves per block
 constexpr int kSkChunk = 128;      // inputs per chunk
 constexpr int kSkWaves = kSkQuad;  // waves per block (one block per CU: its LDS takes 120 KB)
 constexpr int kSkMaxBlocks = 256;
-constexpr int kPrepSpan = 512;     // SwiGLU consumer: outputs per block (one wave, 8 per lane)
+constexpr int kActSpan = 256;      // SwiGLU consumer: outputs per block (one wave, 4 per lane)
 constexpr int kNormSpan = 256;     // norm prep: inputs per block (one wave, 4 per lane), one sum of squares each
 struct SkPlan {
   int groups;   // N / kSkRows

@@ -722,23 +722,21 @@ __global__ void __launch_bounds__(kQkvBlock) sk_qkv_kernel(SkQkvParams p) {
   }
 }
 
-// grid = (ceil(F / kPrepSpan), 16 nt rows), one wave per block: silu(gate) * up of 8 consecutive j -> fragments.
+// grid = (ceil(F / kActSpan), 16 nt rows), one wave per block: silu(gate) * up of 4 consecutive j per lane ->
+// fragments (4 per lane, not 8: twice the waves for the latency-bound partial sums).
 __global__ void __launch_bounds__(64) sk_swiglu_kernel(SkActParams p) {
   const int r = blockIdx.y;
-  const int j0 = blockIdx.x * kPrepSpan + 8 * threadIdx.x;
+  const int j0 = blockIdx.x * kActSpan + 4 * threadIdx.x;
   if (j0 >= p.F) return;
-  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
   if (r < p.rows) {
     const float sc = sk_row_scale(p.ss, p.ss_blocks, r, p.D, p.eps);
+    const f32x4 g = sk_sum4(p.part, p.plan, p.nt, j0, r) * sc;
+    const f32x4 u = sk_sum4(p.part, p.plan, p.nt, p.F + j0, r) * sc;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const f32x4 g = sk_sum4(p.part, p.plan, p.nt, j0 + 4 * h, r) * sc;
-      const f32x4 u = sk_sum4(p.part, p.plan, p.nt, p.F + j0 + 4 * h, r) * sc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * h + e] = g[e] / (1.0f + expf(-g[e])) * u[e];
-    }
+    for (int e = 0; e < 4; ++e) v[e] = g[e] / (1.0f + expf(-g[e])) * u[e];
   }
-  store_frag8(p.hi, p.lo, p.nt, r, j0, v);
+  store_frag4(p.hi, p.lo, p.nt, r, j0, v);
 }
 
 // ----------------------------------------------------------------------------------------------------------
@@ -2519,7 +2517,7 @@ hipError_t launch_sk_qkv(const SkQkvParams& p, int kv_dtype, hipStream_t s) {
 
 hipError_t launch_sk_swiglu(const SkActParams& p, hipStream_t s) {
   if (p.F % 8 || p.rows < 1 || p.nt != sk_tiles(p.rows) || p.rows > kMfmaRows * p.nt) return hipErrorInvalidValue;
-  const dim3 grid((p.F + kPrepSpan - 1) / kPrepSpan, kMfmaRows * p.nt);
+  const dim3 grid((p.F + kActSpan - 1) / kActSpan, kMfmaRows * p.nt);
   sk_swiglu_kernel<<<grid, 64, 0, s>>>(p);
   return hipGetLastError();
 }
