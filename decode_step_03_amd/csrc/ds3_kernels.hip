@@ -821,7 +821,8 @@ __device__ __forceinline__ void attn_write_partial(const AttnParams& p, const fl
 // has m_s = -inf and weight 0). Lane s of each wave loads split s's max and weight sum, so every load of the
 // kernel is a vector load issued up front (uniform addresses would become serialized scalar loads); the weights
 // reach every lane by readlane, and the value sum runs in split order.
-template <int G, int HD>
+// NS: the plan's splits rounded up to 4, 8, 16 or 32 (the loads and the weighted sum run over NS, not kMaxSplits).
+template <int G, int HD, int NS>
 __global__ void __launch_bounds__(128) attn_combine_kernel(AttnParams p) {
   const int h = blockIdx.x, r = blockIdx.y, d = threadIdx.x, lane = d & 63;
   const int g = h / G, hh = h % G, S = p.splits;
@@ -830,15 +831,15 @@ __global__ void __launch_bounds__(128) attn_combine_kernel(AttnParams p) {
   const int sl = min(lane, S - 1);
   const float ms = part[(size_t)sl * stride + HD];
   const float ls = part[(size_t)sl * stride + HD + 1];
-  float ov[kMaxSplits];
+  float ov[NS];
 #pragma unroll
-  for (int k = 0; k < kMaxSplits; ++k) ov[k] = part[(size_t)min(k, S - 1) * stride + d];
+  for (int k = 0; k < NS; ++k) ov[k] = part[(size_t)min(k, S - 1) * stride + d];
   const float M = wave_max(lane < S ? ms : -INFINITY);
   const float w = (lane < S && ms != -INFINITY) ? fast_exp2(ms - M) : 0.f;
   const float L = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum(w * (lane < S ? ls : 0.f))), 0));
   float acc = 0.f;
 #pragma unroll
-  for (int k = 0; k < kMaxSplits; ++k) {
+  for (int k = 0; k < NS; ++k) {
     const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));   // 0 for k >= S
     acc = fmaf(wk, k < S ? ov[k] : 0.f, acc);   // a padded split adds an exact zero, never 0 * garbage
   }
@@ -2436,17 +2437,25 @@ static hipError_t attn_g(const AttnParams& p, int rows, hipStream_t s) {
   }
 }
 
-template <int HD>
-static hipError_t combine_g(const AttnParams& p, int rows, hipStream_t s) {
+template <int HD, int NS>
+static hipError_t combine_gs(const AttnParams& p, int rows, hipStream_t s) {
   const dim3 grid(p.nq, rows);
   switch (p.nq / p.nkv) {
-    case 1: attn_combine_kernel<1, HD><<<grid, HD, 0, s>>>(p); break;
-    case 2: attn_combine_kernel<2, HD><<<grid, HD, 0, s>>>(p); break;
-    case 4: attn_combine_kernel<4, HD><<<grid, HD, 0, s>>>(p); break;
-    case 8: attn_combine_kernel<8, HD><<<grid, HD, 0, s>>>(p); break;
+    case 1: attn_combine_kernel<1, HD, NS><<<grid, HD, 0, s>>>(p); break;
+    case 2: attn_combine_kernel<2, HD, NS><<<grid, HD, 0, s>>>(p); break;
+    case 4: attn_combine_kernel<4, HD, NS><<<grid, HD, 0, s>>>(p); break;
+    case 8: attn_combine_kernel<8, HD, NS><<<grid, HD, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+template <int HD>
+static hipError_t combine_g(const AttnParams& p, int rows, hipStream_t s) {
+  static_assert(kMaxSplits == 32, "split classes 4, 8, 16, 32");
+  if (p.splits <= 4) return combine_gs<HD, 4>(p, rows, s);
+  if (p.splits <= 8) return combine_gs<HD, 8>(p, rows, s);
+  if (p.splits <= 16) return combine_gs<HD, 16>(p, rows, s);
+  return combine_gs<HD, 32>(p, rows, s);
 }
 
 hipError_t launch_attention_combine(const AttnParams& p, int rows, hipStream_t s) {
