@@ -1370,9 +1370,16 @@ __global__ void __launch_bounds__(kPickThreads) pick_kernel(PickParams p) {
   const float* lg = p.logits + (size_t)r * p.vocab;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int i = lo + (int)threadIdx.x; i < hi; i += kPickThreads) {
-    const float v = lg[i];
-    if (pick_better(v, i, bv, bi)) { bv = v; bi = i; }
+  // eight loads in flight per thread before any comparison (the maximum does not depend on the order)
+  for (int i0 = lo + (int)threadIdx.x; i0 < hi; i0 += 8 * kPickThreads) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = i0 + u * kPickThreads < hi ? lg[i0 + u * kPickThreads] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kPickThreads;
+      if (i < hi && pick_better(v[u], i, bv, bi)) { bv = v[u]; bi = i; }
+    }
   }
   // wave, then block: the order-independent (value, index) maximum
 #pragma unroll
