@@ -656,28 +656,41 @@ __global__ void __launch_bounds__(64) sk_prep_kernel(SkPrepParams p) {
   store_frag4(p.hi, p.lo, p.nt, r, k0, v);
 }
 
-// grid = (ceil(N / 4 / 64), rows), one wave per block (the latency-bound sums then spread over every CU): a thread
-// takes output rows n .. n + 3 (n = 4 x index) of activation row r; the first rotary half of a q or k head also
-// takes its partners n + hd/2 .. + 3.
+// grid = (ceil(N / 4 / 64), rows), one wave per block (the latency-bound sums then spread over every CU): a lane
+// takes output rows n .. n + 3 (n = 4 x index) of activation row r, one partial sum each, and a q or k lane gets its
+// rotary partners n +- hd/2 .. + 3 from the lane hd/8 away (a wave holds 256 consecutive outputs: whole heads).
 constexpr int kQkvBlock = 64;
 template <typename KT>
 __global__ void __launch_bounds__(kQkvBlock) sk_qkv_kernel(SkQkvParams p) {
-  const int r = blockIdx.y;
-  const int n = 4 * (blockIdx.x * kQkvBlock + threadIdx.x);
+  const int r = blockIdx.y, lane = threadIdx.x & 63;
   const int hd = p.hd, half = hd / 2;
-  if (n >= (p.nq + 2 * p.nkv) * hd) return;
+  const int n4 = 4 * (blockIdx.x * kQkvBlock + threadIdx.x);
+  if (blockIdx.x * kQkvBlock * 4 >= (p.nq + 2 * p.nkv) * hd) return;   // (wave-uniform: N is whole heads)
+  const bool act = n4 < (p.nq + 2 * p.nkv) * hd;
+  const int n = act ? n4 : 0;   // (an idle lane's whole head is idle, partner included)
   const int hh = n / hd, idx = n % hd;
   const int seg = hh < p.nq ? 0 : (hh < p.nq + p.nkv ? 1 : 2);   // q, k, v
-  if (seg != 2 && idx >= half) return;
   const SlotLayout sl{p.rows};
   int pos = p.slots[sl.pos() + r];
   const bool ok = pos >= 0 && pos < p.kv.cap;
   if (!ok) {
-    raise_error(p.status, ERR_POS);
+    if (act) raise_error(p.status, ERR_POS);
     pos = 0;
   }
+  const bool first = idx < half;   // first rotary half of its head
+  const int ri = first ? idx : idx - half;
+  float2 cs[4];
+  if (seg != 2)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cs[e] = reinterpret_cast<const float2*>(p.rope)[(size_t)pos * half + ri + e];
   const float sc = sk_row_scale(p.ss, p.ss_blocks, r, p.D, p.eps);
-  const f32x4 a = sk_sum4(p.part, p.plan, p.nt, n, r) * sc;
+  const f32x4 own = sk_sum4(p.part, p.plan, p.nt, n, r) * sc;
+  // the rotary partner's sums, by lane shuffle before any lane leaves
+  const int mate = first ? lane + half / 4 : lane - half / 4;
+  f32x4 oth;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) oth[e] = __shfl(own[e], mate, 64);
+  if (!act) return;
   int loc = pos;
   if (seg != 0) {
     if (!ok) return;
@@ -693,33 +706,25 @@ __global__ void __launch_bounds__(kQkvBlock) sk_qkv_kernel(SkQkvParams p) {
     const int head = hh - p.nq - p.nkv;
     KT* base = reinterpret_cast<KT*>(p.kv.v) + (size_t)p.layer * p.kv.layer_stride;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) store_kv(base + kv_at(p.kv, true, r, p.nkv, head, hd, loc, idx + e), a[e]);
+    for (int e = 0; e < 4; ++e) store_kv(base + kv_at(p.kv, true, r, p.nkv, head, hd, loc, idx + e), own[e]);
     return;
   }
-  const f32x4 b = sk_sum4(p.part, p.plan, p.nt, n + half, r) * sc;
-  float va[4], vb[4];
+  // (x1, x2) = (first half, second half): x1 c - x2 s for the first, x1 s + x2 c for the second
+  float v[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float2 cs = reinterpret_cast<const float2*>(p.rope)[(size_t)pos * half + idx + e];
-    va[e] = a[e] * cs.x - b[e] * cs.y;
-    vb[e] = a[e] * cs.y + b[e] * cs.x;
+    const float x1 = first ? own[e] : oth[e], x2 = first ? oth[e] : own[e];
+    v[e] = first ? x1 * cs[e].x - x2 * cs[e].y : x1 * cs[e].y + x2 * cs[e].x;
   }
   if (seg == 0) {
     float* q = p.q + ((size_t)r * p.nq + hh) * hd + idx;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      q[e] = va[e];
-      q[e + half] = vb[e];
-    }
+    *reinterpret_cast<float4*>(q) = make_float4(v[0], v[1], v[2], v[3]);
     return;
   }
   const int head = hh - p.nq;
   KT* base = reinterpret_cast<KT*>(p.kv.k) + (size_t)p.layer * p.kv.layer_stride;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    store_kv(base + kv_at(p.kv, false, r, p.nkv, head, hd, loc, idx + e), va[e]);
-    store_kv(base + kv_at(p.kv, false, r, p.nkv, head, hd, loc, idx + e + half), vb[e]);
-  }
+  for (int e = 0; e < 4; ++e) store_kv(base + kv_at(p.kv, false, r, p.nkv, head, hd, loc, idx + e), v[e]);
 }
 
 // grid = (ceil(F / kActSpan), 16 nt rows), one wave per block: silu(gate) * up of 4 consecutive j per lane ->
