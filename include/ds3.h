@@ -50,8 +50,8 @@ typedef enum {
 enum { DS3_F32 = 0, DS3_BF16 = 1 };                  /* weight and KV storage types */
 enum { DS3_KV_CONTIGUOUS = 0, DS3_KV_PAGED = 1 };    /* KV layouts */
 enum { DS3_GRAPH = 0, DS3_EAGER = 1 };               /* replay one captured graph, or launch every kernel */
-/* Kernel plan. PER_OP: one kernel per operation (embed, then per layer QKV, attention, split combine, o-proj,
- * gate/up, down; then the LM head). FUSED: the whole step as one persistent kernel whose phases are those
+/* Kernel plan. PER_OP: one kernel per operation (embed, then per layer QKV, attention, split combine (absent when
+ * the attention takes one split), o-proj, gate/up, down; then the LM head). FUSED: the whole step as one persistent kernel whose phases are those
  * operations, separated by grid barriers (one block per compute unit; one row, bf16 weights and K/V, contiguous
  * layout, the 1B and 8B model shapes, cap a multiple of 32 x 128 positions per 8 kv heads, a 256-CU device).
  * AUTO picks FUSED where it applies (the faster of the two on MI355X) and PER_OP elsewhere. Both compute the same
